@@ -1,0 +1,355 @@
+"""Python binding of libturboquant (TurboQuant KV-cache path on MI355X).
+
+A thin ctypes layer over the C ABI declared in include/turboquant.h. It only
+marshals arguments: torch tensors supply device memory and the stream, and
+every step of quantization and attention runs in the library's HIP kernels.
+The functions carry the C names (tq_build_codebook, tq_quantize,
+tq_attn_decode, ...). If the shared library has not been built, loading it
+raises immediately; there is no fallback path.
+
+Helpers:
+  Quantizer  -- device copies of a quantizer instance (rotation, sketch,
+                folded sketch, float32 codebook) assembled from its parts.
+  Cache      -- caller-owned compressed-cache tensors for one record format.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libturboquant.so")
+
+TQ_OK = 0
+TQ_ERR_INVALID = -1
+TQ_ERR_UNSUPPORTED = -2
+TQ_ERR_NOCONVERGE = -3
+TQ_ERR_WORKSPACE = -4
+TQ_ERR_DEVICE = -5
+TQ_F32 = 0
+TQ_BF16 = 1
+TQ_TOKEN_MAJOR = 0
+TQ_BLOCK32 = 1
+
+SYMBOLS = ("tq_abi_version", "tq_status_string", "tq_build_codebook", "tq_record_layout",
+           "tq_fold_sketch", "tq_quantize", "tq_attn_decode_workspace_bytes", "tq_attn_decode")
+
+
+class TQError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {tq_status_string(status)} ({status})")
+        self.status = status
+
+
+class tq_layout(C.Structure):
+    _fields_ = [("d", C.c_int32), ("n_groups", C.c_int32), ("group_dim", C.c_int32 * 2),
+                ("mse_bits", C.c_int32 * 2)]
+
+
+class tq_quantizer(C.Structure):
+    _fields_ = [("layout", tq_layout), ("rot", C.c_void_p), ("sketch", C.c_void_p),
+                ("sketch_rot", C.c_void_p), ("centroids", C.c_void_p), ("boundaries", C.c_void_p)]
+
+
+class tq_cache(C.Structure):
+    _fields_ = [("codes", C.c_void_p), ("signs", C.c_void_p), ("norms", C.c_void_p),
+                ("n_rows", C.c_int64)]
+
+
+class tq_record_info(C.Structure):
+    _fields_ = [("code_words", C.c_int32), ("sign_words", C.c_int32), ("norm_floats", C.c_int32),
+                ("block_code_words", C.c_int32), ("block_sign_words", C.c_int32),
+                ("record_bits", C.c_int32)]
+
+
+class tq_rows(C.Structure):
+    _fields_ = [("dst_rows", C.c_void_p), ("seg_len", C.c_int64), ("seg_stride", C.c_int64),
+                ("seg_offset", C.c_int64)]
+
+
+class tq_decode_shape(C.Structure):
+    _fields_ = [("batch", C.c_int32), ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32),
+                ("n_split", C.c_int32), ("n_ctx", C.c_int64), ("cache_capacity", C.c_int64),
+                ("scale", C.c_float)]
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """The loaded shared library (loads it on first use; raises if absent)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libturboquant is not built ({LIB_PATH} missing); run "
+                              "python -m kv_cache_vector_rotation_amd.build")
+        L = C.CDLL(LIB_PATH)
+        L.tq_abi_version.restype = C.c_int
+        L.tq_status_string.restype = C.c_char_p
+        L.tq_status_string.argtypes = [C.c_int]
+        L.tq_build_codebook.restype = C.c_int
+        L.tq_build_codebook.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.c_double,
+                                        C.POINTER(C.c_double), C.POINTER(C.c_double),
+                                        C.POINTER(C.c_double)]
+        L.tq_record_layout.restype = C.c_int
+        L.tq_record_layout.argtypes = [C.POINTER(tq_layout), C.POINTER(tq_record_info)]
+        L.tq_fold_sketch.restype = C.c_int
+        L.tq_fold_sketch.argtypes = [C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]
+        L.tq_quantize.restype = C.c_int
+        L.tq_quantize.argtypes = [C.POINTER(tq_quantizer), C.c_int, C.c_void_p, C.c_int, C.c_int64,
+                                  C.c_int64, C.POINTER(tq_rows), C.POINTER(tq_cache), C.c_void_p]
+        L.tq_attn_decode_workspace_bytes.restype = C.c_int
+        L.tq_attn_decode_workspace_bytes.argtypes = [C.POINTER(tq_quantizer), C.POINTER(tq_quantizer),
+                                                     C.POINTER(tq_decode_shape), C.POINTER(C.c_size_t)]
+        L.tq_attn_decode.restype = C.c_int
+        L.tq_attn_decode.argtypes = [C.POINTER(tq_quantizer), C.POINTER(tq_quantizer),
+                                     C.POINTER(tq_decode_shape), C.c_void_p, C.c_int,
+                                     C.POINTER(tq_cache), C.POINTER(tq_cache), C.c_void_p, C.c_void_p,
+                                     C.c_void_p, C.c_size_t, C.c_void_p]
+        _lib = L
+    return _lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != TQ_OK:
+        raise TQError(status, where)
+
+
+def make_layout(dims: Sequence[int], mse_bits: Sequence[int]) -> tq_layout:
+    l = tq_layout()
+    l.d = int(sum(dims))
+    l.n_groups = len(dims)
+    for g, (d, m) in enumerate(zip(dims, mse_bits)):
+        l.group_dim[g] = int(d)
+        l.mse_bits[g] = int(m)
+    return l
+
+
+# ---------------------------------------------------------------------------
+# Host-only entry points
+# ---------------------------------------------------------------------------
+
+def tq_abi_version() -> int:
+    return int(lib().tq_abi_version())
+
+
+def tq_status_string(status: int) -> str:
+    return lib().tq_status_string(int(status)).decode()
+
+
+def tq_build_codebook(d: int, mse_bits: int, max_iter: int = 0, tol: float = 0.0):
+    """(centroids [2^m] float64, boundaries [2^m - 1] float64, mse_per_coord)."""
+    L = 1 << mse_bits if 1 <= mse_bits <= 4 else 1
+    c = (C.c_double * L)()
+    t = (C.c_double * max(L - 1, 1))()
+    mse = C.c_double()
+    _check(lib().tq_build_codebook(d, mse_bits, max_iter, tol, c, t, C.byref(mse)),
+           "tq_build_codebook")
+    return np.array(c[:L]), np.array(t[:L - 1]), float(mse.value)
+
+
+def tq_record_layout(layout: tq_layout) -> tq_record_info:
+    info = tq_record_info()
+    _check(lib().tq_record_layout(C.byref(layout), C.byref(info)), "tq_record_layout")
+    return info
+
+
+def tq_fold_sketch(rot: np.ndarray, sketch: np.ndarray) -> np.ndarray:
+    rot = np.ascontiguousarray(rot, dtype=np.float32)
+    sketch = np.ascontiguousarray(sketch, dtype=np.float32)
+    d = rot.shape[0]
+    out = np.empty((d, d), dtype=np.float32)
+    _check(lib().tq_fold_sketch(d, rot.ctypes.data, sketch.ctypes.data, out.ctypes.data),
+           "tq_fold_sketch")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Device objects
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def _stream(stream) -> Optional[int]:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+@dataclass
+class Quantizer:
+    """Device copies of one quantizer instance plus its ABI struct."""
+    layout: tq_layout
+    dims: tuple
+    mse_bits: tuple
+    rot: "object"
+    sketch: "object"
+    sketch_rot: "object"
+    centroids: "object"
+    boundaries: "object"
+
+    @staticmethod
+    def from_parts(rotations: Sequence[np.ndarray], sketches: Sequence[np.ndarray],
+                   mse_bits: Sequence[int], perm: Optional[np.ndarray] = None,
+                   device: str = "cuda") -> "Quantizer":
+        """Assemble rot = blockdiag(Pi_g) P and sketch = blockdiag(S_g) P (P the
+        channel permutation x -> x[perm]), fold sketch rot^T on the host, and
+        build the float32 codebooks with tq_build_codebook."""
+        torch = _torch()
+        dims = [int(r.shape[0]) for r in rotations]
+        d = sum(dims)
+        perm = np.arange(d) if perm is None else np.asarray(perm, dtype=np.int64)
+        bd_r = np.zeros((d, d), dtype=np.float64)
+        bd_s = np.zeros((d, d), dtype=np.float64)
+        o = 0
+        for r, s in zip(rotations, sketches):
+            g = r.shape[0]
+            bd_r[o:o + g, o:o + g] = r
+            bd_s[o:o + g, o:o + g] = s
+            o += g
+        rot = np.zeros((d, d), dtype=np.float32)
+        sk = np.zeros((d, d), dtype=np.float32)
+        rot[:, perm] = bd_r.astype(np.float32)
+        sk[:, perm] = bd_s.astype(np.float32)
+        skr = tq_fold_sketch(rot, sk)
+        cents, bnds = [], []
+        for g, m in zip(dims, mse_bits):
+            c, t, _ = tq_build_codebook(g, int(m))
+            cents.append(c.astype(np.float32))
+            bnds.append(t.astype(np.float32))
+        to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
+        return Quantizer(layout=make_layout(dims, mse_bits), dims=tuple(dims),
+                         mse_bits=tuple(int(m) for m in mse_bits), rot=to(rot), sketch=to(sk),
+                         sketch_rot=to(skr), centroids=to(np.concatenate(cents)),
+                         boundaries=to(np.concatenate(bnds)))
+
+    def struct(self) -> tq_quantizer:
+        q = tq_quantizer()
+        q.layout = self.layout
+        q.rot = _ptr(self.rot)
+        q.sketch = _ptr(self.sketch)
+        q.sketch_rot = _ptr(self.sketch_rot)
+        q.centroids = _ptr(self.centroids)
+        q.boundaries = _ptr(self.boundaries)
+        return q
+
+
+@dataclass
+class Cache:
+    """Compressed-cache tensors (caller-owned device memory)."""
+    fmt: int
+    n_rows: int
+    codes: "object"
+    signs: "object"
+    norms: "object"
+
+    @staticmethod
+    def empty(quantizer: Quantizer, n_rows: int, fmt: int, device: str = "cuda") -> "Cache":
+        torch = _torch()
+        info = tq_record_layout(quantizer.layout)
+        if fmt == TQ_BLOCK32:
+            if n_rows % 32:
+                raise ValueError("TQ_BLOCK32 needs a multiple of 32 rows")
+            nb = n_rows // 32
+            codes = torch.zeros(nb * info.block_code_words, dtype=torch.int32, device=device)
+            signs = torch.zeros(nb * info.block_sign_words, dtype=torch.int32, device=device)
+        else:
+            codes = torch.zeros(n_rows * info.code_words, dtype=torch.int32, device=device)
+            signs = torch.zeros(n_rows * info.sign_words, dtype=torch.int32, device=device)
+        norms = torch.zeros(n_rows * info.norm_floats, dtype=torch.float32, device=device)
+        return Cache(fmt=fmt, n_rows=n_rows, codes=codes, signs=signs, norms=norms)
+
+    def struct(self) -> tq_cache:
+        c = tq_cache()
+        c.codes = _ptr(self.codes)
+        c.signs = _ptr(self.signs)
+        c.norms = _ptr(self.norms)
+        c.n_rows = int(self.n_rows)
+        return c
+
+    def clone(self) -> "Cache":
+        return Cache(self.fmt, self.n_rows, self.codes.clone(), self.signs.clone(), self.norms.clone())
+
+
+def decode_shape(batch: int, n_q_heads: int, n_kv_heads: int, n_ctx: int, capacity: int,
+                 scale: float, n_split: int = 0) -> tq_decode_shape:
+    s = tq_decode_shape()
+    s.batch, s.n_q_heads, s.n_kv_heads, s.n_split = batch, n_q_heads, n_kv_heads, n_split
+    s.n_ctx, s.cache_capacity, s.scale = n_ctx, capacity, scale
+    return s
+
+
+# ---------------------------------------------------------------------------
+# Device entry points
+# ---------------------------------------------------------------------------
+
+def tq_quantize(quantizer: Quantizer, fmt: int, x, cache: Cache, dst_rows=None, seg_len: int = 1,
+                seg_stride: int = 1, seg_offset: int = 0, stream=None) -> None:
+    """Quantize the rows of x ([n_vec, >= d], float32 or bfloat16, on the GPU)
+    into ``cache``. Rows: dst_rows (int64 device tensor) if given, else
+    (i // seg_len) * seg_stride + seg_offset + i % seg_len."""
+    torch = _torch()
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D tensor with unit stride along the channels")
+    dt = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}[x.dtype]
+    rows = tq_rows()
+    rows.dst_rows = _ptr(dst_rows)
+    rows.seg_len, rows.seg_stride, rows.seg_offset = seg_len, seg_stride, seg_offset
+    q = quantizer.struct()
+    c = cache.struct()
+    _check(lib().tq_quantize(C.byref(q), fmt, _ptr(x), dt, x.shape[0], x.stride(0), C.byref(rows),
+                             C.byref(c), _stream(stream)), "tq_quantize")
+
+
+def tq_attn_decode_workspace_bytes(kq: Quantizer, vq: Optional[Quantizer], shape: tq_decode_shape) -> int:
+    n = C.c_size_t()
+    kqs = kq.struct()
+    vqs = vq.struct() if vq is not None else None
+    _check(lib().tq_attn_decode_workspace_bytes(C.byref(kqs), C.byref(vqs) if vqs is not None else None,
+                                                C.byref(shape), C.byref(n)),
+           "tq_attn_decode_workspace_bytes")
+    return int(n.value)
+
+
+def tq_attn_decode(kq: Quantizer, vq: Optional[Quantizer], shape: tq_decode_shape, q,
+                   k_cache: Cache, v_cache: Optional[Cache], logits=None, out=None, workspace=None,
+                   stream=None) -> None:
+    """One decode step (see include/turboquant.h). q: [batch, n_q_heads, d]
+    float32/bfloat16 contiguous on the GPU; logits / out: float32 device
+    tensors or None; workspace: uint8 device tensor (allocated here if None)."""
+    torch = _torch()
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    dt = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}[q.dtype]
+    if workspace is None:
+        workspace = torch.empty(tq_attn_decode_workspace_bytes(kq, vq, shape), dtype=torch.uint8,
+                                device=q.device)
+    kqs = kq.struct()
+    vqs = vq.struct() if vq is not None else None
+    kc = k_cache.struct()
+    vc = v_cache.struct() if v_cache is not None else None
+    _check(lib().tq_attn_decode(C.byref(kqs), C.byref(vqs) if vqs is not None else None,
+                                C.byref(shape), _ptr(q), dt, C.byref(kc),
+                                C.byref(vc) if vc is not None else None, _ptr(logits), _ptr(out),
+                                _ptr(workspace), workspace.numel(), _stream(stream)),
+           "tq_attn_decode")
+
+
+__all__ = [
+    "LIB_PATH", "SYMBOLS", "lib", "TQError", "Quantizer", "Cache", "make_layout", "decode_shape",
+    "tq_abi_version", "tq_status_string", "tq_build_codebook", "tq_record_layout", "tq_fold_sketch",
+    "tq_quantize", "tq_attn_decode_workspace_bytes", "tq_attn_decode",
+    "TQ_OK", "TQ_ERR_INVALID", "TQ_ERR_UNSUPPORTED", "TQ_ERR_NOCONVERGE", "TQ_ERR_WORKSPACE",
+    "TQ_ERR_DEVICE", "TQ_F32", "TQ_BF16", "TQ_TOKEN_MAJOR", "TQ_BLOCK32",
+]

@@ -1,0 +1,182 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads and
+exports every function include/turboquant.h declares; the C++ Lloyd-Max
+codebook agrees with the independent numpy/scipy oracle; record sizes; the
+sketch folding; and argument validation, which must reject bad calls before
+any HIP call is made (the device pointers passed here are never touched)."""
+import ctypes as C
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "turboquant.h")
+
+
+@pytest.fixture(scope="module")
+def tq():
+    import kv_cache_vector_rotation_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from kv_cache_vector_rotation_amd import build
+        build.build()
+    m.lib()
+    return m
+
+
+def test_header_symbols_exported(tq):
+    text = open(HEADER).read()
+    declared = sorted(set(re.findall(r"^\s*(?:tq_status|int|const char\*)\s+(tq_\w+)\s*\(", text, re.M)))
+    assert len(declared) == 8
+    lib = C.CDLL(tq.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(tq.SYMBOLS) == declared
+    version = int(re.search(r"#define TQ_ABI_VERSION (\d+)", text).group(1))
+    assert tq.tq_abi_version() == version
+
+
+@pytest.mark.parametrize("d", [3, 8, 64, 128, 200, 1024])
+@pytest.mark.parametrize("m", [1, 2, 3, 4])
+def test_codebook_matches_oracle(tq, d, m):
+    c, t, mse = tq.tq_build_codebook(d, m)
+    ref = oracle.lloyd_max(d, m)
+    assert np.max(np.abs(c - ref.centroids)) <= 1e-10 / math.sqrt(d)
+    assert np.max(np.abs(t - ref.boundaries)) <= 1e-10 / math.sqrt(d)
+    assert abs(mse - ref.mse_per_coord) <= 1e-13
+    assert np.array_equal(c, -c[::-1])
+    assert np.array_equal(t, 0.5 * (c[:-1] + c[1:]))
+
+
+def test_codebook_errors(tq):
+    for d, m in [(2, 2), (128, 0), (128, 5), (-1, 1)]:
+        with pytest.raises(tq.TQError) as e:
+            tq.tq_build_codebook(d, m)
+        assert e.value.status == tq.TQ_ERR_INVALID
+    with pytest.raises(tq.TQError) as e:
+        tq.tq_build_codebook(128, 3, max_iter=1)
+    assert e.value.status == tq.TQ_ERR_NOCONVERGE
+    lib = tq.lib()
+    c = (C.c_double * 8)()
+    assert lib.tq_build_codebook(128, 3, 0, 0.0, c, None, None) == tq.TQ_ERR_INVALID
+    assert lib.tq_build_codebook(128, 3, 0, -1.0, c, c, None) == tq.TQ_ERR_INVALID
+
+
+@pytest.mark.parametrize("dims,bits", [([128], [2]), ([128], [3]), ([64, 64], [3, 2]),
+                                       ([64, 64], [2, 1]), ([200], [3]), ([40, 24], [4, 1])])
+def test_record_layout(tq, dims, bits):
+    info = tq.tq_record_layout(tq.make_layout(dims, bits))
+    cw, sw, nf, bcw, bsw = oracle.record_words(dims, bits)
+    assert (info.code_words, info.sign_words, info.norm_floats, info.block_code_words,
+            info.block_sign_words) == (cw, sw, nf, bcw, bsw)
+    assert info.record_bits == 8 * oracle.record_bytes(dims, bits)
+
+
+def test_layout_validation(tq):
+    bad = [([2], [2]), ([300], [2]), ([128], [0]), ([128], [5]), ([64, 2], [2, 2])]
+    for dims, bits in bad:
+        with pytest.raises(tq.TQError):
+            tq.tq_record_layout(tq.make_layout(dims, bits))
+    l = tq.make_layout([64, 64], [2, 2])
+    l.d = 100
+    with pytest.raises(tq.TQError):
+        tq.tq_record_layout(l)
+
+
+def test_fold_sketch(tq):
+    rng = np.random.default_rng(1)
+    rot = rng.standard_normal((48, 48)).astype(np.float32)
+    sk = rng.standard_normal((48, 48)).astype(np.float32)
+    got = tq.tq_fold_sketch(rot, sk)
+    ref = (sk.astype(np.float64) @ rot.astype(np.float64).T).astype(np.float32)
+    assert np.array_equal(got, ref)
+
+
+# ---- validation of device entry points (nothing is dereferenced) ----
+FAKE = 1 << 20  # a 16-byte aligned address that is never accessed
+
+
+def _fake_quantizer(tq, dims=(128,), bits=(3,)):
+    q = tq.tq_quantizer()
+    q.layout = tq.make_layout(dims, bits)
+    q.rot = q.sketch = q.sketch_rot = q.centroids = q.boundaries = FAKE
+    return q
+
+
+def _fake_cache(tq, n_rows):
+    c = tq.tq_cache()
+    c.codes = c.signs = c.norms = FAKE
+    c.n_rows = n_rows
+    return c
+
+
+def test_quantize_validation(tq):
+    lib = tq.lib()
+    q = _fake_quantizer(tq)
+    cache = _fake_cache(tq, 1024)
+    rows = tq.tq_rows()
+    rows.dst_rows, rows.seg_len, rows.seg_stride, rows.seg_offset = None, 1024, 1024, 0
+    call = lambda **kw: lib.tq_quantize(C.byref(kw.get("q", q)), kw.get("fmt", 0), kw.get("x", FAKE),
+                                        kw.get("dt", 0), kw.get("n", 100), kw.get("stride", 128),
+                                        C.byref(kw.get("rows", rows)), C.byref(kw.get("cache", cache)),
+                                        None)
+    assert call(n=-1) == tq.TQ_ERR_INVALID
+    assert call(fmt=7) == tq.TQ_ERR_INVALID
+    assert call(dt=9) == tq.TQ_ERR_INVALID
+    assert call(stride=127) == tq.TQ_ERR_INVALID
+    assert call(n=1025) == tq.TQ_ERR_INVALID                 # rows beyond the cache
+    assert call(x=FAKE + 2) == tq.TQ_ERR_INVALID             # misaligned input
+    assert call(n=0) == tq.TQ_OK                              # no-op, nothing launched
+    small = _fake_cache(tq, 1000)
+    assert call(fmt=1, cache=small) == tq.TQ_ERR_INVALID      # block records need 32-row blocks
+    overlap = tq.tq_rows()
+    overlap.dst_rows, overlap.seg_len, overlap.seg_stride, overlap.seg_offset = None, 10, 5, 0
+    assert call(rows=overlap) == tq.TQ_ERR_INVALID
+    bad_q = _fake_quantizer(tq)
+    bad_q.rot = None
+    assert call(q=bad_q) == tq.TQ_ERR_INVALID
+    mis = _fake_quantizer(tq)
+    mis.centroids = FAKE + 4
+    assert call(q=mis) == tq.TQ_ERR_INVALID
+    split = _fake_quantizer(tq, dims=(72, 56), bits=(3, 2))
+    assert call(q=split) == tq.TQ_ERR_UNSUPPORTED            # group edge not a multiple of 16
+    odd = _fake_quantizer(tq, dims=(100,), bits=(3,))
+    assert call(q=odd, fmt=1, stride=100) == tq.TQ_ERR_UNSUPPORTED
+
+
+def test_decode_validation(tq):
+    lib = tq.lib()
+    kq, vq = _fake_quantizer(tq), _fake_quantizer(tq)
+    kc = _fake_cache(tq, 2 * 8 * 1024)
+    vc = _fake_cache(tq, 2 * 8 * 1024)
+
+    def call(shape, **kw):
+        return lib.tq_attn_decode(C.byref(kw.get("kq", kq)), kw.get("vq", C.byref(vq)), C.byref(shape),
+                                  kw.get("q", FAKE), kw.get("dt", 1), C.byref(kw.get("kc", kc)),
+                                  C.byref(kw.get("vc", vc)), kw.get("logits", None), kw.get("out", FAKE),
+                                  kw.get("ws", FAKE), kw.get("wsb", 1 << 40), None)
+
+    good = tq.decode_shape(2, 32, 8, 1000, 1024, 0.088)
+    for bad in [tq.decode_shape(2, 30, 8, 1000, 1024, 0.1), tq.decode_shape(2, 32, 8, 0, 1024, 0.1),
+                tq.decode_shape(2, 32, 8, 1025, 1024, 0.1), tq.decode_shape(2, 32, 8, 1000, 1000, 0.1),
+                tq.decode_shape(0, 32, 8, 1000, 1024, 0.1), tq.decode_shape(2, 32, 8, 1000, 1024, math.inf),
+                tq.decode_shape(2, 32, 8, 1000, 1024, 0.1, n_split=-1)]:
+        assert call(bad) == tq.TQ_ERR_INVALID
+    assert call(good, dt=5) == tq.TQ_ERR_INVALID
+    assert call(good, out=None) == tq.TQ_ERR_INVALID                       # V given, no output
+    assert call(good, vq=None, out=FAKE, logits=FAKE) == tq.TQ_ERR_INVALID  # logits-only with out
+    assert call(good, vq=None, out=None) == tq.TQ_ERR_INVALID              # logits-only without logits
+    assert call(good, kc=_fake_cache(tq, 100)) == tq.TQ_ERR_INVALID        # cache too small
+    assert call(good, q=FAKE + 8) == tq.TQ_ERR_INVALID
+    assert call(good, wsb=10) == tq.TQ_ERR_WORKSPACE
+    other = _fake_quantizer(tq, bits=(2,))
+    assert call(good, vq=C.byref(other)) == tq.TQ_ERR_UNSUPPORTED          # K and V layouts differ
+    d64 = _fake_quantizer(tq, dims=(64,), bits=(3,))
+    assert call(good, kq=d64, vq=C.byref(_fake_quantizer(tq, dims=(64,), bits=(3,)))) == tq.TQ_ERR_UNSUPPORTED
+    # the workspace query agrees with what the call requires
+    need = C.c_size_t()
+    assert lib.tq_attn_decode_workspace_bytes(C.byref(kq), C.byref(vq), C.byref(good), C.byref(need)) == 0
+    assert call(good, wsb=need.value - 1) == tq.TQ_ERR_WORKSPACE

@@ -1,0 +1,163 @@
+"""GPU parity of tq_attn_decode against the CPU oracle (through the C ABI).
+
+The compressed caches are written by the oracle (its own codes, signs and
+norms, packed by its own packers) and uploaded, so the device and the oracle
+decode the identical cache. Logits and outputs must agree within 2e-3
+normwise per (batch, head): max |got - ref| <= 2e-3 max |ref|.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import gpu_common as gc
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tq():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import kv_cache_vector_rotation_amd as m
+    m.lib()
+    return m
+
+
+def _oracle_side(wl, n_ctx, cap, with_v=True):
+    """Quantize the K (and V) streams with the oracle, return oracle quantizers,
+    specs, per-(b,h) dequantized caches and packed arrays."""
+    ks, vs = synth.draw_quantizer(wl, "K"), synth.draw_quantizer(wl, "V")
+    okq = oracle.Quantizer.from_spec(ks)
+    ovq = oracle.Quantizer.from_spec(vs)
+    B, H = wl.batch, wl.n_kv_heads
+    dims = [g.dim for g in ks.groups]
+    bits = [g.mse_bits for g in ks.groups]
+    kx = np.concatenate([synth.draw_kv_slab(wl, "K", b, h, 0, n_ctx) for b in range(B) for h in range(H)])
+    qk = oracle.quantize(kx, okq)
+    k_t = oracle.dequantize(qk.idx, qk.bits, qk.norm, qk.gamma, okq).reshape(B, H, n_ctx, wl.d)
+    rows = np.concatenate([(b * H + h) * cap + np.arange(n_ctx) for b in range(B) for h in range(H)])
+    karr = gc.oracle_cache_arrays(qk, dims, bits, 0, B * H * cap, rows)
+    out = dict(ks=ks, vs=vs, k_t=k_t, karr=karr, dims=dims, bits=bits)
+    if with_v:
+        # block records need whole blocks: quantize up to the block boundary
+        nb = ((n_ctx + 31) // 32) * 32
+        vx = np.concatenate([synth.draw_kv_slab(wl, "V", b, h, 0, nb) for b in range(B) for h in range(H)])
+        qvv = oracle.quantize(vx, ovq)
+        v_full = oracle.dequantize(qvv.idx, qvv.bits, qvv.norm, qvv.gamma, ovq).reshape(B, H, nb, wl.d)
+        vrows = np.concatenate([(b * H + h) * cap + np.arange(nb) for b in range(B) for h in range(H)])
+        out["varr"] = gc.oracle_cache_arrays(qvv, dims, bits, 1, B * H * cap, vrows)
+        out["v_t"] = v_full[:, :, :n_ctx]
+    return out
+
+
+def _device_decode(tq, wl, o, n_ctx, cap, with_v=True, want_logits=True, n_split=0, q=None):
+    import torch
+    kq = tq.Quantizer.from_parts(o["ks"].rotations, o["ks"].sketches, o["bits"], perm=o["ks"].perm)
+    vq = tq.Quantizer.from_parts(o["vs"].rotations, o["vs"].sketches, o["bits"], perm=o["vs"].perm)
+    B, H = wl.batch, wl.n_kv_heads
+    kc = gc.to_device_cache(kq, tq.TQ_TOKEN_MAJOR, B * H * cap, o["karr"])
+    vc = gc.to_device_cache(vq, tq.TQ_BLOCK32, B * H * cap, o["varr"]) if with_v else None
+    if q is None:
+        q = synth.draw_queries(wl)
+    qt = torch.from_numpy(q).cuda()
+    if wl.dtype == "bf16":
+        qt = qt.to(torch.bfloat16)
+    shape = tq.decode_shape(B, wl.n_q_heads, H, n_ctx, cap, wl.scale, n_split)
+    logits = torch.full((B, wl.n_q_heads, n_ctx), float("nan"), device="cuda") if want_logits else None
+    out = torch.full((B, wl.n_q_heads, wl.d), float("nan"), device="cuda") if with_v else None
+    tq.tq_attn_decode(kq, vq if with_v else None, shape, qt, kc, vc, logits=logits, out=out)
+    torch.cuda.synchronize()
+    return (None if logits is None else logits.cpu().numpy().astype(np.float64),
+            None if out is None else out.cpu().numpy().astype(np.float64), q)
+
+
+def _reference(wl, o, q, with_v=True):
+    B = wl.batch
+    lg, ot = [], []
+    for b in range(B):
+        l, out = oracle.attention_decode(q[b].astype(np.float64), o["k_t"][b],
+                                         o["v_t"][b] if with_v else None, wl.scale)
+        lg.append(l)
+        ot.append(out)
+    return np.stack(lg), (np.stack(ot) if with_v else None)
+
+
+def test_tiny_logits_only(tq):
+    # 64 fp32 queries x 4096 fp32 keys, 3 bits, raw inner products (scale 1)
+    wl = synth.workload("tiny")
+    o = _oracle_side(wl, 4096, 4096, with_v=False)
+    got, _, q = _device_decode(tq, wl, o, 4096, 4096, with_v=False)
+    ref, _ = _reference(wl, o, q, with_v=False)
+    ok, worst = gc.normwise_close(got, ref)
+    print("tiny logits worst", worst)
+    assert ok, worst
+
+
+CASES = [
+    # name, overrides, n_ctx, cap
+    ("llama8b_decode", dict(batch=2, n_q_heads=8, n_kv_heads=2), 1000, 1024),
+    ("llama8b_decode", dict(batch=1, n_q_heads=8, n_kv_heads=1), 1, 32),
+    ("llama8b_decode", dict(batch=1, n_q_heads=4, n_kv_heads=2), 33, 64),
+    ("llama8b_decode", dict(batch=1, n_q_heads=16, n_kv_heads=2), 2048, 2048),
+    ("llama70b_long", dict(batch=2, n_q_heads=16, n_kv_heads=2), 1500, 1536),
+    ("llama70b_long", dict(batch=1, n_q_heads=40, n_kv_heads=2), 300, 320),
+    ("mixed_3p5", dict(batch=2, n_q_heads=8, n_kv_heads=2), 777, 800),
+    ("mixed_2p5", dict(batch=2, n_q_heads=8, n_kv_heads=2), 777, 800),
+    ("llama8b_decode", dict(batch=1, n_q_heads=4, n_kv_heads=1, groups=((128, 1),)), 500, 512),
+    ("llama8b_decode", dict(batch=1, n_q_heads=4, n_kv_heads=1, groups=((128, 4),)), 500, 512),
+]
+
+
+@pytest.mark.parametrize("name,over,n_ctx,cap", CASES)
+def test_decode_matches_oracle(tq, name, over, n_ctx, cap):
+    wl = synth.workload(name, **over)
+    o = _oracle_side(wl, n_ctx, cap)
+    lg, out, q = _device_decode(tq, wl, o, n_ctx, cap)
+    rl, ro = _reference(wl, o, q)
+    ok_l, wl_ = gc.normwise_close(lg, rl)
+    ok_o, wo = gc.normwise_close(out, ro)
+    print(name, over, n_ctx, "logits", wl_, "out", wo)
+    assert ok_l and ok_o, (wl_, wo)
+
+
+def test_split_count_does_not_change_result(tq):
+    wl = synth.workload("llama8b_decode", batch=1, n_q_heads=8, n_kv_heads=2)
+    o = _oracle_side(wl, 3000, 3008)
+    outs = []
+    for ns in (1, 3, 7, 0):
+        _, out, q = _device_decode(tq, wl, o, 3000, 3008, want_logits=False, n_split=ns)
+        outs.append(out)
+    _, ro = _reference(wl, o, q)
+    for out in outs:
+        assert gc.normwise_close(out, ro)[0]
+    for out in outs[1:]:
+        assert np.max(np.abs(out - outs[0])) <= 1e-4 * np.max(np.abs(outs[0]))
+
+
+def test_gqa_equals_repeated_heads(tq):
+    # G query heads sharing one KV head give the same outputs as the same
+    # queries each against its own copy of that KV head
+    import torch
+    wl = synth.workload("llama8b_decode", batch=1, n_q_heads=4, n_kv_heads=1)
+    o = _oracle_side(wl, 200, 224)
+    _, out_gqa, q = _device_decode(tq, wl, o, 200, 224, want_logits=False)
+    wl4 = synth.workload("llama8b_decode", batch=1, n_q_heads=4, n_kv_heads=4)
+    o4 = dict(o)
+    kc, ks_, kn = o["karr"]
+    vc, vs_, vn = o["varr"]
+    o4["karr"] = (np.tile(kc, 4), np.tile(ks_, 4), np.tile(kn, 4))
+    o4["varr"] = (np.tile(vc, 4), np.tile(vs_, 4), np.tile(vn, 4))
+    _, out_mha, _ = _device_decode(tq, wl4, o4, 200, 224, want_logits=False, q=q)
+    assert np.max(np.abs(out_gqa - out_mha)) <= 1e-5 * np.max(np.abs(out_gqa))
+
+
+def test_single_token_returns_its_value(tq):
+    wl = synth.workload("llama8b_decode", batch=1, n_q_heads=4, n_kv_heads=1)
+    o = _oracle_side(wl, 1, 32)
+    _, out, _ = _device_decode(tq, wl, o, 1, 32, want_logits=False)
+    ref = np.repeat(o["v_t"][0, :, 0], 4, axis=0)
+    assert gc.normwise_close(out[0], ref)[0]

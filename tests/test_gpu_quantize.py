@@ -1,0 +1,138 @@
+"""GPU parity of tq_quantize against the CPU oracle (through the C ABI).
+
+Inputs are the seeded synthetic workloads; the oracle quantizes the same
+arrays in float64. Codes and sign bits must be bit-exact except within 1e-6
+of a decision boundary (fewer than 1e-5 of all coordinates), norms to 1e-6.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import gpu_common as gc
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tq():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import kv_cache_vector_rotation_amd as m
+    m.lib()
+    return m
+
+
+def _run(tq, spec, x, fmt, n_rows, rows=None, seg=(1, 1, 0), dtype="f32"):
+    import torch
+    oq, dq = gc.quantizers(spec)
+    cache = tq.Cache.empty(dq, n_rows, fmt)
+    xt = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    if dtype == "bf16":
+        xt = xt.to(torch.bfloat16)
+    dr = None if rows is None else torch.from_numpy(np.asarray(rows, np.int64)).cuda()
+    tq.tq_quantize(dq, fmt, xt, cache, dst_rows=dr, seg_len=seg[0], seg_stride=seg[1], seg_offset=seg[2])
+    torch.cuda.synchronize()
+    return oq, dq, cache
+
+
+def _check(tq, spec, x, fmt, n_rows, rows, dtype="f32", seg=None, pass_rows=True):
+    oq, dq, cache = _run(tq, spec, x, fmt, n_rows, rows if pass_rows else None,
+                         seg if seg else (1, 1, 0), dtype)
+    qv = oracle.quantize(x.astype(np.float64), oq)
+    got = gc.select_rows(gc.read_cache(cache, dq), np.asarray(rows))
+    return gc.compare_records(x.astype(np.float64), oq, qv, got)
+
+
+@pytest.mark.parametrize("fmt_name", ["TQ_TOKEN_MAJOR", "TQ_BLOCK32"])
+def test_tiny_workload_fp32(tq, fmt_name):
+    # d = 128, 4096 iid N(0,1) fp32 keys, 3 bits (2 + 1), seed 0
+    wl = synth.workload("tiny")
+    spec = synth.draw_quantizer(wl, "K")
+    x = synth.draw_kv_slab(wl, "K", 0, 0, 0, 4096)
+    stats = _check(tq, spec, x, getattr(tq, fmt_name), 4096, np.arange(4096), pass_rows=False,
+                   seg=(4096, 4096, 0))
+    print(stats)
+
+
+@pytest.mark.parametrize("fmt_name", ["TQ_TOKEN_MAJOR", "TQ_BLOCK32"])
+def test_bf16_outliers_4bit_ragged(tq, fmt_name):
+    # 1000 vectors (not a multiple of the 64-vector tile), bf16 with x10 outlier channels
+    wl = synth.workload("llama8b_decode")
+    spec = synth.draw_quantizer(wl, "V")
+    x = synth.draw_kv_slab(wl, "V", 0, 3, 100, 1100)
+    x[17] = 0.0  # a zero vector
+    _check(tq, spec, x, getattr(tq, fmt_name), 1024, np.arange(1000), dtype="bf16")
+
+
+@pytest.mark.parametrize("name", ["mixed_3p5", "mixed_2p5"])
+@pytest.mark.parametrize("fmt_name", ["TQ_TOKEN_MAJOR", "TQ_BLOCK32"])
+def test_two_group_fractional_bits(tq, name, fmt_name):
+    wl = synth.workload(name)
+    spec = synth.draw_quantizer(wl, "K")
+    x = synth.draw_kv_slab(wl, "K", 2, 5, 0, 333)
+    _check(tq, spec, x, getattr(tq, fmt_name), 352, np.arange(333), dtype="bf16")
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 4])
+def test_every_bit_width_d64(tq, m):
+    wl = synth.workload("llama8b_decode", d=64, groups=((64, m),), n_outliers=0)
+    spec = synth.draw_quantizer(wl, "K")
+    x = synth.draw_kv_slab(wl, "K", 0, 0, 0, 256)
+    _check(tq, spec, x, tq.TQ_TOKEN_MAJOR, 256, np.arange(256), dtype="bf16")
+
+
+def test_d200_unit_vectors(tq):
+    # nearest-neighbour database shape: d = 200, L2-normalised mixture vectors, 4 bits
+    wl = synth.workload("nn_search")
+    spec = synth.draw_quantizer(wl, "K")
+    x = synth.draw_mixture_vectors(wl, 500, "db")
+    for fmt in (tq.TQ_TOKEN_MAJOR, tq.TQ_BLOCK32):
+        _check(tq, spec, x, fmt, 512, np.arange(500))
+
+
+def test_scattered_rows_and_partial_blocks(tq):
+    # rows given explicitly in a random order: every block is partial and is
+    # updated in place; rows not written keep their previous contents
+    import torch
+    wl = synth.workload("llama8b_decode")
+    spec = synth.draw_quantizer(wl, "V")
+    x = synth.draw_kv_slab(wl, "V", 0, 1, 0, 200)
+    rows = np.random.default_rng(0).permutation(256)[:200]
+    oq, dq = gc.quantizers(spec)
+    cache = tq.Cache.empty(dq, 256, tq.TQ_BLOCK32)
+    # pre-fill with ones: untouched bits must stay, written fields must be replaced
+    cache.codes.fill_(-1)
+    cache.signs.fill_(-1)
+    xt = torch.from_numpy(x).cuda().to(torch.bfloat16)
+    tq.tq_quantize(dq, tq.TQ_BLOCK32, xt, cache, dst_rows=torch.from_numpy(rows).cuda())
+    torch.cuda.synchronize()
+    got_all = gc.read_cache(cache, dq)
+    qv = oracle.quantize(x.astype(np.float64), oq)
+    gc.compare_records(x.astype(np.float64), oq, qv, gc.select_rows(got_all, rows))
+    untouched = np.setdiff1d(np.arange(256), rows)
+    L = 2 ** dq.mse_bits[0] - 1
+    assert np.all(got_all[0][0][untouched] == L) and np.all(got_all[1][0][untouched])
+
+
+def test_append_rows_by_segments(tq):
+    # one new token per (batch, head) slice: vector i -> row i * capacity + 777
+    wl = synth.workload("llama8b_decode")
+    spec = synth.draw_quantizer(wl, "K")
+    x = np.stack([synth.draw_kv_slab(wl, "K", 0, h, 777, 778)[0] for h in range(8)])
+    cap = 1024
+    rows = np.arange(8) * cap + 777
+    for fmt in (tq.TQ_TOKEN_MAJOR, tq.TQ_BLOCK32):
+        _check(tq, spec, x, fmt, 8 * cap, rows, dtype="bf16", seg=(1, cap, 777), pass_rows=False)
+
+
+def test_empty_call_is_noop(tq):
+    import torch
+    wl = synth.workload("tiny")
+    spec = synth.draw_quantizer(wl, "K")
+    oq, dq = gc.quantizers(spec)
+    cache = tq.Cache.empty(dq, 64, tq.TQ_TOKEN_MAJOR)
+    tq.tq_quantize(dq, tq.TQ_TOKEN_MAJOR, torch.zeros((0, 128), device="cuda"), cache)
+    torch.cuda.synchronize()
+    assert int(cache.codes.abs().sum()) == 0
