@@ -1,0 +1,338 @@
+#!/usr/bin/env python3
+"""Throughput of the TurboQuant compressed-KV decode step on one MI355X.
+
+One step = quantize-on-append of the new token(s) of every (batch, KV head)
+for K (token-major records) and V (32-token block records), then one decode
+step over the whole compressed cache (query prep, split-K pass, combine).
+Inputs are seeded synthetic tensors already resident in HBM; the cache is
+built (untimed) by the library's own quantize kernel from synthetic K/V.
+
+To measure HBM rather than the 256 MB Infinity Cache, each step uses the
+next of several copies of the compressed cache (at least 1 GiB in total).
+
+Prints one JSON line: cached tokens/s (batch * context / step time), the
+split-K kernel against the HBM roofline (HIP events around that kernel on
+its stream), a secondary quantize throughput on a 524,288-vector chunk, and
+the CPU oracle timed on a bounded sample as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, vendor figure
+PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 matrix, vendor figure
+DECODE_WORKLOADS = ("llama8b_decode", "llama70b_long", "mixed_3p5", "mixed_2p5")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_kernel_traffic.json")
+DECODE_SOURCE = os.path.join(ROOT, "kv_cache_vector_rotation_amd", "csrc", "tq_decode.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama8b_decode", choices=DECODE_WORKLOADS)
+    ap.add_argument("--copies", type=int, default=0, help="cache copies (0: enough for 1 GiB)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-quantize-bench", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="launch every step from Python")
+    return ap.parse_args()
+
+
+def record_bytes(dims, bits):
+    return sum((m + 1) * d for d, m in zip(dims, bits)) / 8 + 8 * len(dims)
+
+
+def _threads():
+    try:
+        return max(1, min(16, len(os.sched_getaffinity(0))))
+    except AttributeError:
+        return 8
+
+
+def build_caches(tq, torch, wl, kq, vq, prefix, cap):
+    """Quantize tokens [0, prefix) of every (b, h) into fresh caches (untimed)."""
+    B, H = wl.batch, wl.n_kv_heads
+    kc = tq.Cache.empty(kq, B * H * cap, tq.TQ_TOKEN_MAJOR)
+    vc = tq.Cache.empty(vq, B * H * cap, tq.TQ_BLOCK32)
+    if prefix == 0:
+        return kc, vc
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    pairs = [(b, h) for b in range(B) for h in range(H)]
+    per = max(1, min(len(pairs), int(2e9 // (prefix * wl.d * 8))))
+    with ThreadPoolExecutor(_threads()) as ex:
+        for i in range(0, len(pairs), per):
+            chunk = pairs[i:i + per]
+            ks = list(ex.map(lambda p: synth.draw_kv_slab(wl, "K", p[0], p[1], 0, prefix), chunk))
+            vs = list(ex.map(lambda p: synth.draw_kv_slab(wl, "V", p[0], p[1], 0, prefix), chunk))
+            for (b, h), kx, vx in zip(chunk, ks, vs):
+                row0 = (b * H + h) * cap
+                for x, qz, cache, fmt in ((kx, kq, kc, tq.TQ_TOKEN_MAJOR), (vx, vq, vc, tq.TQ_BLOCK32)):
+                    xt = torch.from_numpy(x).cuda().to(dt)
+                    tq.tq_quantize(qz, fmt, xt, cache, seg_len=prefix, seg_stride=cap, seg_offset=row0)
+            torch.cuda.synchronize()
+    return kc, vc
+
+
+def new_tokens(torch, wl, prefix):
+    B, H = wl.batch, wl.n_kv_heads
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    pairs = [(b, h) for b in range(B) for h in range(H)]
+    with ThreadPoolExecutor(_threads()) as ex:
+        ks = list(ex.map(lambda p: synth.draw_kv_slab(wl, "K", p[0], p[1], prefix, wl.n_ctx), pairs))
+        vs = list(ex.map(lambda p: synth.draw_kv_slab(wl, "V", p[0], p[1], prefix, wl.n_ctx), pairs))
+    k = torch.from_numpy(np.concatenate(ks)).cuda().to(dt)
+    v = torch.from_numpy(np.concatenate(vs)).cuda().to(dt)
+    return k, v
+
+
+def traffic_record():
+    """HBM traffic of the split-K kernel from rocprofv3 counters, if they were
+    taken on the current kernel source (else None)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = json.load(open(TRAFFIC_FILE))
+    sha = hashlib.sha256(open(DECODE_SOURCE, "rb").read()).hexdigest()
+    return rec if rec.get("source_sha256") == sha else None
+
+
+def quantize_bench(tq, torch, wl, kq, n_vec=524288, launches=20):
+    """Secondary figure: vectors/s of one quantize launch over a chunk of
+    n_vec vectors (the 70B-shaped prefill chunk: 4 x 8 heads x 8192 tokens x K,V)."""
+    rng_x = synth.standard_normal(synth.rng_for(wl.seed, 99), (n_vec, wl.d))
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    x = torch.from_numpy(synth.to_bf16_exact(rng_x) if wl.dtype == "bf16" else rng_x).cuda().to(dt)
+    cache = tq.Cache.empty(kq, n_vec, tq.TQ_TOKEN_MAJOR)
+    for _ in range(3):
+        tq.tq_quantize(kq, tq.TQ_TOKEN_MAJOR, x, cache, seg_len=n_vec, seg_stride=n_vec)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(launches):
+        tq.tq_quantize(kq, tq.TQ_TOKEN_MAJOR, x, cache, seg_len=n_vec, seg_stride=n_vec)
+    e1.record()
+    torch.cuda.synchronize()
+    s = e0.elapsed_time(e1) / 1e3 / launches
+    flops = 4.0 * wl.d * wl.d * n_vec  # two d x d products per vector
+    return {"vectors": n_vec, "us_per_launch": round(s * 1e6, 2), "vectors_per_s": n_vec / s,
+            "bound": "mfma", "achieved_tflops": flops / s / 1e12, "peak_tflops": PEAK_FP32_MFMA_TFLOPS,
+            "frac": flops / s / 1e12 / PEAK_FP32_MFMA_TFLOPS, "dtype": "f32"}
+
+
+def cpu_baseline(wl, budget_s):
+    """The oracle (plain float64 numpy) on a bounded sample of the same step:
+    for (b, h) pairs in order, untimed: quantize the prefix; timed: quantize
+    the appended token(s), dequantize the K and V caches and attend with the
+    pair's query heads. The mean time per pair is scaled to the whole step."""
+    import oracle  # the baseline leg is the only bench code that uses the oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    okq = oracle.Quantizer.from_spec(synth.draw_quantizer(wl, "K"))
+    ovq = oracle.Quantizer.from_spec(synth.draw_quantizer(wl, "V"))
+    q = synth.draw_queries(wl).astype(np.float64)
+    G = wl.group_size
+    prefix = wl.n_ctx - wl.n_new
+    times, pairs_done, started = [], 0, time.perf_counter()
+    for b in range(wl.batch):
+        for h in range(wl.n_kv_heads):
+            kx = synth.draw_kv_slab(wl, "K", b, h, 0, wl.n_ctx)
+            vx = synth.draw_kv_slab(wl, "V", b, h, 0, wl.n_ctx)
+            kp, vp = oracle.quantize(kx[:prefix], okq), oracle.quantize(vx[:prefix], ovq)
+            t0 = time.perf_counter()
+            kn, vn = oracle.quantize(kx[prefix:], okq), oracle.quantize(vx[prefix:], ovq)
+            cat = lambda a, c: [np.concatenate([u, w]) for u, w in zip(a, c)]
+            kt = oracle.dequantize(cat(kp.idx, kn.idx), cat(kp.bits, kn.bits), cat(kp.norm, kn.norm),
+                                   cat(kp.gamma, kn.gamma), okq)
+            vt = oracle.dequantize(cat(vp.idx, vn.idx), cat(vp.bits, vn.bits), cat(vp.norm, vn.norm),
+                                   cat(vp.gamma, vn.gamma), ovq)
+            oracle.attention_decode(q[b, h * G:(h + 1) * G], kt[None], vt[None], wl.scale)
+            times.append(time.perf_counter() - t0)
+            pairs_done += 1
+            if sum(times) >= budget_s or time.perf_counter() - started > 4 * budget_s:
+                break
+        else:
+            continue
+        break
+    per_step = float(np.mean(times)) * wl.batch * wl.n_kv_heads
+    return {"value": wl.batch * wl.n_ctx / per_step, "unit": "cached tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{pairs_done} of {wl.batch * wl.n_kv_heads} (batch, KV head) pairs: append "
+                      f"{wl.n_new} token(s) K+V, dequantize {wl.n_ctx} K+V records, attend with {G} "
+                      f"query heads; {sum(times):.1f} s timed, scaled to the full step",
+            "seconds_per_step": per_step}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU layout "
+              "(head-sharded decode, no collective) is described in DESIGN.md and is not built here.")
+        sys.exit(2)
+    import torch
+    import kv_cache_vector_rotation_amd as tq
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    tq.lib()
+    wl = synth.workload(args.workload)
+    B, HQ, H, d, N = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.d, wl.n_ctx
+    cap = wl.capacity
+    prefix = N - wl.n_new
+    ks, vs = synth.draw_quantizer(wl, "K"), synth.draw_quantizer(wl, "V")
+    bits = [g.mse_bits for g in ks.groups]
+    dims = [g.dim for g in ks.groups]
+    kq = tq.Quantizer.from_parts(ks.rotations, ks.sketches, bits, perm=ks.perm)
+    vq = tq.Quantizer.from_parts(vs.rotations, vs.sketches, bits, perm=vs.perm)
+
+    t_setup = time.perf_counter()
+    kc0, vc0 = build_caches(tq, torch, wl, kq, vq, prefix, cap)
+    k_new, v_new = new_tokens(torch, wl, prefix)
+    rb = record_bytes(dims, bits)
+    cache_bytes = B * H * cap * 2 * rb
+    n_copies = args.copies or max(1, math.ceil((1 << 30) / cache_bytes))
+    caches = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(n_copies - 1)]
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    q = torch.from_numpy(synth.draw_queries(wl)).cuda().to(dt)
+    shape = tq.decode_shape(B, HQ, H, N, cap, wl.scale)
+    ws = torch.empty(tq.tq_attn_decode_workspace_bytes(kq, vq, shape), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, HQ, d), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    log(f"setup {time.perf_counter() - t_setup:.1f}s: {args.workload} B={B} Hq={HQ} Hkv={H} d={d} "
+        f"N={N} bits={bits} dims={dims} copies={n_copies} ({n_copies * cache_bytes / 2**30:.2f} GiB)")
+
+    def step(i, ev=None):
+        kc, vc = caches[i % n_copies]
+        tq.tq_quantize(kq, tq.TQ_TOKEN_MAJOR, k_new, kc, seg_len=wl.n_new, seg_stride=cap, seg_offset=prefix)
+        tq.tq_quantize(vq, tq.TQ_BLOCK32, v_new, vc, seg_len=wl.n_new, seg_stride=cap, seg_offset=prefix)
+        tq.tq_attn_decode_phases(tq.TQ_PHASE_PREP, kq, vq, shape, q, kc, vc, out=out, workspace=ws)
+        if ev is not None:
+            ev[0].record()
+        tq.tq_attn_decode_phases(tq.TQ_PHASE_SPLIT, kq, vq, shape, q, kc, vc, out=out, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+        tq.tq_attn_decode_phases(tq.TQ_PHASE_COMBINE, kq, vq, shape, q, kc, vc, out=out, workspace=ws)
+
+    for i in range(max(args.warmup, n_copies)):
+        step(i)
+    torch.cuda.synchronize()
+
+    # One graph holds a full cycle of steps (one per cache copy); replaying it
+    # removes the host launch cost from the step time. (Event timestamps are
+    # not available inside a captured graph on ROCm, so the split-K kernel is
+    # then timed in its own event-bracketed loop right after.)
+    graph, evs = None, None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(n_copies):
+                step(i)
+        for _ in range(max(1, args.warmup // n_copies)):
+            graph.replay()
+        torch.cuda.synchronize()
+    t_begin, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = max(1, math.ceil(args.steps / n_copies)) if graph is not None else 0
+    n_steps = reps * n_copies if graph is not None else args.steps
+    split_ms = []
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_begin.record()
+    if graph is not None:
+        for _ in range(reps):
+            graph.replay()
+    else:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n_steps)]
+        for i in range(n_steps):
+            step(args.warmup + i, evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_begin.elapsed_time(t_end) / n_steps
+    if evs is not None:
+        timing_source = "events around the split-K launch in the timed steps"
+        split_ms = [a.elapsed_time(b) for a, b in evs]
+    else:
+        # The split-K pass alone: a graph of one launch per cache copy (the
+        # prepared query in the workspace is the same for every copy), replayed
+        # between two events on the launch stream; the mean is per launch.
+        timing_source = "events around replays of a graph of split-K launches, one per cache copy"
+        split_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(split_graph):
+            for i in range(n_copies):
+                kc, vc = caches[i]
+                tq.tq_attn_decode_phases(tq.TQ_PHASE_SPLIT, kq, vq, shape, q, kc, vc, out=out, workspace=ws)
+        split_graph.replay()
+        torch.cuda.synchronize()
+        split_reps = max(1, math.ceil(200 / n_copies))
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(split_reps):
+                split_graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            split_ms.append(e0.elapsed_time(e1) / (split_reps * n_copies))
+    split_s = float(np.mean(split_ms)) / 1e3
+    log(f"step {ms_step * 1e3:.2f} us over {n_steps} steps (wall {wall / n_steps * 1e6:.2f} us); "
+        f"split-K kernel mean {split_s * 1e6:.2f} us, median {np.median(split_ms) * 1e3:.2f} us, "
+        f"min {np.min(split_ms) * 1e3:.2f} us "
+        f"[{timing_source}]")
+
+    algo_bytes = B * H * N * 2 * rb  # K and V records of every cached token read by the split-K pass
+    achieved = algo_bytes / split_s / 1e9
+    tr = traffic_record()
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": tr["bytes_per_launch"] if tr and tr.get("workload") == args.workload else None,
+                "kernel": "decode_kernel (split-K pass)", "kernel_us": round(split_s * 1e6, 2),
+                "kernel_timing": timing_source,
+                "algorithmic_bytes": int(algo_bytes)}
+    result = {
+        "metric": "compressed-KV decode throughput (cached tokens/s; split-K kernel vs HBM roofline)",
+        "value": B * N / (ms_step / 1e3),
+        "unit": "cached tokens/s",
+        "n_gpus": 1, "steps": n_steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": B, "n_q_heads": HQ, "n_kv_heads": H, "d": d,
+                   "n_ctx": N, "appended_tokens": wl.n_new, "bits_per_channel": [m + 1 for m in bits],
+                   "group_dims": dims, "record_bytes_per_token": rb, "cache_copies": n_copies,
+                   "input_dtype": wl.dtype, "hip_graph": graph is not None},
+        "roofline": roofline,
+    }
+    if not args.no_quantize_bench:
+        result["quantize"] = quantize_bench(tq, torch, wl, kq)
+        log(f"quantize: {result['quantize']}")
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        log(f"cpu baseline: {result['cpu_baseline']}")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

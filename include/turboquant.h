@@ -265,6 +265,24 @@ tq_status tq_attn_decode(const tq_quantizer* kq, const tq_quantizer* vq,
                          const tq_cache* k_cache, const tq_cache* v_cache, float* logits,
                          float* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* The three stages of tq_attn_decode, for callers that schedule or time them
+ * separately (e.g. to bracket the split-K kernel with events):
+ *   TQ_PHASE_PREP    q_rot = rot q, q_sk = sketch q into the workspace,
+ *   TQ_PHASE_SPLIT   the split-K pass over the cache (logits; partial softmax
+ *                    sums and accumulators into the workspace),
+ *   TQ_PHASE_COMBINE merge of the splits and back-transform into `out`.
+ * A stage reads what the earlier stages left in the same workspace, so
+ * stages must run in this order on one stream with identical arguments. */
+enum { TQ_PHASE_PREP = 1, TQ_PHASE_SPLIT = 2, TQ_PHASE_COMBINE = 4, TQ_PHASE_ALL = 7 };
+
+/* tq_attn_decode restricted to the stages in `phases` (a non-zero subset of
+ * TQ_PHASE_ALL); arguments, validation and errors as tq_attn_decode, plus
+ * TQ_ERR_INVALID for an empty or unknown phase mask. */
+tq_status tq_attn_decode_phases(unsigned phases, const tq_quantizer* kq, const tq_quantizer* vq,
+                                const tq_decode_shape* shape, const void* q, tq_dtype q_dtype,
+                                const tq_cache* k_cache, const tq_cache* v_cache, float* logits,
+                                float* out, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

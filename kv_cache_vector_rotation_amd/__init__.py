@@ -35,8 +35,14 @@ TQ_BF16 = 1
 TQ_TOKEN_MAJOR = 0
 TQ_BLOCK32 = 1
 
+TQ_PHASE_PREP = 1
+TQ_PHASE_SPLIT = 2
+TQ_PHASE_COMBINE = 4
+TQ_PHASE_ALL = 7
+
 SYMBOLS = ("tq_abi_version", "tq_status_string", "tq_build_codebook", "tq_record_layout",
-           "tq_fold_sketch", "tq_quantize", "tq_attn_decode_workspace_bytes", "tq_attn_decode")
+           "tq_fold_sketch", "tq_quantize", "tq_attn_decode_workspace_bytes", "tq_attn_decode",
+           "tq_attn_decode_phases")
 
 
 class TQError(RuntimeError):
@@ -87,6 +93,14 @@ def lib() -> C.CDLL:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"libturboquant is not built ({LIB_PATH} missing); run "
                               "python -m kv_cache_vector_rotation_amd.build")
+        try:
+            import torch
+            if torch.cuda.is_available():
+                # let torch bring up the HIP runtime before the library's
+                # kernels are registered with it
+                torch.cuda.init()
+        except ImportError:
+            pass
         L = C.CDLL(LIB_PATH)
         L.tq_abi_version.restype = C.c_int
         L.tq_status_string.restype = C.c_char_p
@@ -110,6 +124,8 @@ def lib() -> C.CDLL:
                                      C.POINTER(tq_decode_shape), C.c_void_p, C.c_int,
                                      C.POINTER(tq_cache), C.POINTER(tq_cache), C.c_void_p, C.c_void_p,
                                      C.c_void_p, C.c_size_t, C.c_void_p]
+        L.tq_attn_decode_phases.restype = C.c_int
+        L.tq_attn_decode_phases.argtypes = [C.c_uint] + L.tq_attn_decode.argtypes
         _lib = L
     return _lib
 
@@ -328,6 +344,15 @@ def tq_attn_decode(kq: Quantizer, vq: Optional[Quantizer], shape: tq_decode_shap
     """One decode step (see include/turboquant.h). q: [batch, n_q_heads, d]
     float32/bfloat16 contiguous on the GPU; logits / out: float32 device
     tensors or None; workspace: uint8 device tensor (allocated here if None)."""
+    tq_attn_decode_phases(TQ_PHASE_ALL, kq, vq, shape, q, k_cache, v_cache, logits, out, workspace,
+                          stream)
+
+
+def tq_attn_decode_phases(phases: int, kq: Quantizer, vq: Optional[Quantizer], shape: tq_decode_shape,
+                          q, k_cache: Cache, v_cache: Optional[Cache], logits=None, out=None,
+                          workspace=None, stream=None) -> None:
+    """The stages of tq_attn_decode selected by ``phases`` (TQ_PHASE_* bits);
+    stages share state through ``workspace``, which must then be given."""
     torch = _torch()
     if not q.is_contiguous():
         raise ValueError("q must be contiguous")
@@ -339,17 +364,18 @@ def tq_attn_decode(kq: Quantizer, vq: Optional[Quantizer], shape: tq_decode_shap
     vqs = vq.struct() if vq is not None else None
     kc = k_cache.struct()
     vc = v_cache.struct() if v_cache is not None else None
-    _check(lib().tq_attn_decode(C.byref(kqs), C.byref(vqs) if vqs is not None else None,
-                                C.byref(shape), _ptr(q), dt, C.byref(kc),
-                                C.byref(vc) if vc is not None else None, _ptr(logits), _ptr(out),
-                                _ptr(workspace), workspace.numel(), _stream(stream)),
+    _check(lib().tq_attn_decode_phases(phases, C.byref(kqs), C.byref(vqs) if vqs is not None else None,
+                                       C.byref(shape), _ptr(q), dt, C.byref(kc),
+                                       C.byref(vc) if vc is not None else None, _ptr(logits), _ptr(out),
+                                       _ptr(workspace), workspace.numel(), _stream(stream)),
            "tq_attn_decode")
 
 
 __all__ = [
     "LIB_PATH", "SYMBOLS", "lib", "TQError", "Quantizer", "Cache", "make_layout", "decode_shape",
     "tq_abi_version", "tq_status_string", "tq_build_codebook", "tq_record_layout", "tq_fold_sketch",
-    "tq_quantize", "tq_attn_decode_workspace_bytes", "tq_attn_decode",
+    "tq_quantize", "tq_attn_decode_workspace_bytes", "tq_attn_decode", "tq_attn_decode_phases",
+    "TQ_PHASE_PREP", "TQ_PHASE_SPLIT", "TQ_PHASE_COMBINE", "TQ_PHASE_ALL",
     "TQ_OK", "TQ_ERR_INVALID", "TQ_ERR_UNSUPPORTED", "TQ_ERR_NOCONVERGE", "TQ_ERR_WORKSPACE",
     "TQ_ERR_DEVICE", "TQ_F32", "TQ_BF16", "TQ_TOKEN_MAJOR", "TQ_BLOCK32",
 ]

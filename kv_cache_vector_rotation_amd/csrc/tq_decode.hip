@@ -8,38 +8,43 @@
 //   logit = scale * sum_g ( n_g <(rot q)_g, c[idx]> + alpha_g gamma_g <(sketch q)_g, z> ).
 //
 // Three kernels on the caller's stream:
-//  1. prep:    q_rot = rot q and q_sk = sketch q per query head (fp32 sums,
-//              stored as fp16 hi/lo pairs).
-//  2. decode:  split-K over the context. A workgroup takes one (batch, KV head,
-//              16-query-head block) and a range of 32-token tiles; its four
-//              waves take alternate tiles. Per tile a wave
-//              - expands the K codes through LDS pair tables (two fp16
-//                centroids per lookup) and the K sign bits into fp16 +-1,
+//  1. prep:    q_rot = rot q and q_sk = sketch q per query head (fp32 sums;
+//              q_rot stored as an fp16 hi/lo pair, q_sk as fp16).
+//  2. split:   split-K over the context. A workgroup takes one (batch, KV
+//              head, 16-query-head block) and a range of 32-token tiles; its
+//              four waves take alternate tiles. Per tile a wave
+//              - expands the K codes through LDS tables (two fp16 centroids
+//                and, from a second table, their fp16 rounding remainders
+//                per lookup) and the K sign bits through a nibble table into
+//                fp16 +-1,
 //              - forms both logit parts on v_mfma_f32_16x16x32_f16 (tokens x
-//                channels times channels x heads), with centroids and
-//                queries split into fp16 hi + lo parts so the products keep
-//                fp32 accuracy, scales them by the token's norms, and runs
-//                the online softmax,
-//              - expands the V codes/signs the same way and accumulates
-//                sum_t p_t n_t c[idx_t] and sum_t p_t gamma_t z_t on MFMA
-//                (channels x tokens times tokens x heads): V is summed in the
-//                rotated and sketch domains, never dequantized per token.
+//                channels times channels x heads); the MSE part uses the
+//                hi/lo splits of centroids and queries so its products keep
+//                fp32 accuracy; scales them by the tokens' norms and runs
+//                the online softmax (accumulators are rescaled only when a
+//                head's running maximum moves),
+//              - expands the V codes four at a time and the V signs, and
+//                accumulates sum_t p_t n_t c[idx_t] and sum_t p_t gamma_t z_t
+//                on MFMA (channels x tokens times tokens x heads): V is
+//                summed in the rotated and sketch domains, never
+//                dequantized per token.
 //              The MFMA output layout of the logits (lane = head, 8 tokens)
 //              is exactly the operand layout the V product needs, so the
 //              softmax weights never leave registers. The four waves merge
 //              through LDS into one partial (max, sum, accumulators).
 //  3. combine: log-sum-exp merge of the splits, then out = (rot^T acc_rot +
-//              sketch^T (alpha acc_sk)) / sum: the back-transform runs once
+//              sketch^T (alpha_g acc_sk)) / sum: the back-transform runs once
 //              per head, which is valid because dequantization is linear.
 //
-// Record formats: K rows are token-major (a token's codes for 8 consecutive
-// channels are one 8m-bit field); V is stored in 32-token blocks where each
+// Record formats: K rows are token-major (a lane's 8 codes of one token are
+// one 8m-bit field of the row); V is stored in 32-token blocks where each
 // octet of tokens keeps its 8 codes of a channel in one 8m-bit field. Both
 // fields feed one lane's eight MFMA operand slots directly.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "tq_internal.h"
 #include "turboquant.h"
@@ -49,16 +54,14 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2a4 __attribute__((ext_vector_type(2))) __attribute__((aligned(4)));
-typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x2a8 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
-// Low parts of the split fp16 operands are stored times 2^11 (kLoScale) so
-// they stay in the normal fp16 range; their products are scaled back by 2^-11.
+// Low parts of the split fp16 operands are stored times 2^11 so they stay in
+// the normal fp16 range; their products are scaled back by 2^-11.
 constexpr float kLoScale = 2048.0f;
 constexpr float kLoInv = 1.0f / 2048.0f;
-constexpr int lowbit(int v) { return v & (-v); }
 constexpr int kWaves = 4;
 constexpr int kTile = 32;
 
@@ -67,7 +70,7 @@ struct DArgs {
   int n_split;
   int64_t n_ctx, cap;
   float scale;
-  const _Float16* qprep;  // [batch*hq][4d]: q_rot hi, q_rot lo*2^11, q_sk hi, q_sk lo*2^11
+  const _Float16* qprep;  // [batch*hq][3d]: q_rot hi, q_rot lo * 2^11, q_sk
   const uint32_t* kc;
   const uint32_t* ks;
   const float* kn;
@@ -85,45 +88,6 @@ __device__ __forceinline__ uint32_t h2bits(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-// 8 sign bits -> 8 fp16 values +1 (bit set) / -1 (bit clear), two per dword.
-__device__ __forceinline__ u32x4 signs_to_pm1(uint32_t byte) {
-  const uint32_t x = (~byte) & 0xFFu;
-  const uint32_t x2 = x | (x << 16);
-  u32x4 r;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    // bit 2p to bit 15 of the low half, bit 2p+1 to bit 15 of the high half
-    const u16x2 sh = {(uint16_t)(15 - 2 * p), (uint16_t)(14 - 2 * p)};
-    const u16x2 y = __builtin_bit_cast(u16x2, x2) << sh;
-    r[p] = (__builtin_bit_cast(uint32_t, y) & 0x80008000u) | 0x3C003C00u;
-  }
-  return r;
-}
-
-// 8 codes of M bits (one 8M-bit field, code s at bits [M s, M s + M)) ->
-// 8 fp16 centroids through a pair table (entry = code_a | code_b << M).
-template <int M>
-__device__ __forceinline__ u32x4 codes_to_f16(uint32_t field, const uint32_t* lut) {
-  u32x4 r;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) r[p] = lut[(field >> (2 * M * p)) & ((1u << (2 * M)) - 1u)];
-  return r;
-}
-
-// Same as codes_to_f16 from a split table: entry e holds the fp16 pair of the
-// centroids (hi) and the fp16 pair of their rounding remainders times 2^11
-// (lo), so that hi + 2^-11 lo reproduces the fp32 centroid.
-template <int M>
-__device__ __forceinline__ void codes_to_f16_split(uint32_t field, const u32x2a8* lut, u32x4& hi,
-                                                   u32x4& lo) {
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const u32x2a8 v = lut[(field >> (2 * M * p)) & ((1u << (2 * M)) - 1u)];
-    hi[p] = v[0];
-    lo[p] = v[1];
-  }
-}
-
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
@@ -131,43 +95,89 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 
 __device__ __forceinline__ float xor_max(float v, int m) { return fmaxf(v, __shfl_xor(v, m, 64)); }
 
-// Load NW consecutive 32-bit words starting at p, with p known to be aligned
-// to ALIGN bytes.
-template <int NW, int ALIGN>
-__device__ __forceinline__ void load_words(const uint32_t* p, uint32_t* out) {
-  if constexpr (ALIGN >= 16 && NW % 4 == 0) {
-#pragma unroll
-    for (int i = 0; i < NW / 4; ++i) {
-      const u32x4 v = reinterpret_cast<const u32x4*>(p)[i];
-      out[4 * i] = v[0];
-      out[4 * i + 1] = v[1];
-      out[4 * i + 2] = v[2];
-      out[4 * i + 3] = v[3];
+// ---------------------------------------------------------------------------
+// Lookup tables in LDS. A table of E entries of W bytes keeps each entry
+// replicated across one 256-byte LDS row (entry e, replica r at byte
+// e * 256 + W * r, 256 / W replicas); lane l reads replica l mod (256 / W),
+// so the lanes served together in one LDS cycle hit distinct banks whatever
+// entries they look up. Tables with more than 64 entries are stored plainly.
+// ---------------------------------------------------------------------------
+template <int E, int W>
+struct Tab {
+  static constexpr bool REP = E <= 64;
+  static constexpr int BYTES = REP ? E * 256 : E * W;
+};
+
+template <int E, int W>
+__device__ __forceinline__ uint32_t tab_addr(uint32_t e, uint32_t lane_off) {
+  if constexpr (Tab<E, W>::REP)
+    return (e << 8) | lane_off;
+  else
+    return e * W;
+}
+
+template <int E, int W, typename F>
+__device__ void tab_build(unsigned char* base, int tid, F entry) {
+  if constexpr (Tab<E, W>::REP) {
+    constexpr int R = 256 / W;
+    for (int i = tid; i < E * R; i += 256) {
+      const int e = i / R, r = i % R;
+      entry(e, base + e * 256 + W * r);
     }
-  } else if constexpr (ALIGN >= 8 && NW % 2 == 0) {
+  } else {
+    for (int e = tid; e < E; e += 256) entry(e, base + e * W);
+  }
+}
+
+// 8 sign bits (bit s -> slot s) -> 8 fp16 values, +1 where set, -1 where clear.
+__device__ __forceinline__ u32x4 signs8(uint32_t byte, const unsigned char* stab, uint32_t off8) {
+  const u32x2 lo = *reinterpret_cast<const u32x2*>(stab + tab_addr<16, 8>(byte & 15u, off8));
+  const u32x2 hi = *reinterpret_cast<const u32x2*>(stab + tab_addr<16, 8>((byte >> 4) & 15u, off8));
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// 8 K codes of M bits -> fp16 centroids (hi) and their rounding remainders
+// x 2^11 (lo): one address per pair, two 4-byte reads (lo table at +LO).
+template <int M, int LO>
+__device__ __forceinline__ void kcodes8(uint32_t field, const unsigned char* tab, uint32_t off4,
+                                        u32x4& hi, u32x4& lo) {
+  constexpr int E = 1 << (2 * M);
 #pragma unroll
-    for (int i = 0; i < NW / 2; ++i) {
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t e = (field >> (2 * M * p)) & (E - 1u);
+    const unsigned char* ad = tab + tab_addr<E, 4>(e, off4);
+    hi[p] = *reinterpret_cast<const uint32_t*>(ad);
+    lo[p] = *reinterpret_cast<const uint32_t*>(ad + LO);
+  }
+}
+
+// 8 codes of M bits (code s at bits [M s, M s + M) of field) -> 8 fp16
+// centroids, one 4-byte lookup per pair.
+template <int M>
+__device__ __forceinline__ u32x4 codes8(uint32_t field, const unsigned char* tab, uint32_t off4) {
+  constexpr int E = 1 << (2 * M);
+  u32x4 r;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t e = (field >> (2 * M * p)) & (E - 1u);
+    r[p] = *reinterpret_cast<const uint32_t*>(tab + tab_addr<E, 4>(e, off4));
+  }
+  return r;
+}
+
+// Loads N consecutive words from a 4-byte aligned address.
+template <int N>
+__device__ __forceinline__ void load_w(const uint32_t* p, uint32_t* out) {
+  if constexpr (N % 2 == 0) {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
       const u32x2a4 v = reinterpret_cast<const u32x2a4*>(p)[i];
       out[2 * i] = v[0];
       out[2 * i + 1] = v[1];
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < NW; ++i) out[i] = p[i];
-  }
-}
-
-// Norms (n_g, gamma_g) of 8 consecutive rows; p is 16-byte aligned.
-template <int NG>
-__device__ __forceinline__ void load_norms(const float* p, float (&out)[8][2 * NG]) {
-#pragma unroll
-  for (int i = 0; i < 4 * NG; ++i) {
-    const f32x4 v = reinterpret_cast<const f32x4*>(p)[i];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int flat = 4 * i + e;
-      out[flat / (2 * NG)][flat % (2 * NG)] = v[e];
-    }
+    for (int i = 0; i < N; ++i) out[i] = p[i];
   }
 }
 
@@ -181,76 +191,170 @@ __device__ __forceinline__ uint32_t field_at(const uint32_t* w, int pos, int wid
   return v;
 }
 
-// One group's V contribution for one 32-token tile. The lane (row ln, octet
-// lg) owns channels RUN ln + u, u < RUN, of the group; for each u it expands
-// the 8 codes and 8 sign bits of its octet's tokens at that channel and adds
-// (V tile MT0 + u) += codes^T x P'_rot and signs^T x P'_sketch.
-template <int M, int RUN, int MT0, int NMT>
-__device__ __forceinline__ void v_accumulate(const uint32_t* cw, const uint32_t* sw,
-                                             const uint32_t* lut, u32x4 pr, u32x4 pz,
-                                             f32x4 (&acc_r)[NMT], f32x4 (&acc_s)[NMT]) {
+// Norms (n_g, gamma_g) of 8 consecutive tokens from the wave's LDS staging.
+template <int NG>
+__device__ __forceinline__ void load_norms(const float* p, float (&out)[8][2 * NG]) {
 #pragma unroll
-  for (int u = 0; u < RUN; ++u) {
-    const uint32_t field = field_at(cw, 8 * M * u, 8 * M);
-    const u32x4 av = codes_to_f16<M>(field, lut);
-    const uint32_t sbyte = (sw[u >> 2] >> (8 * (u & 3))) & 0xFFu;
-    const u32x4 az = signs_to_pm1(sbyte);
-    acc_r[MT0 + u] = mfma16(av, pr, acc_r[MT0 + u]);
-    acc_s[MT0 + u] = mfma16(az, pz, acc_s[MT0 + u]);
+  for (int i = 0; i < 4 * NG; ++i) {
+    const f32x4 v = reinterpret_cast<const f32x4*>(p)[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int flat = 4 * i + e;
+      out[flat / (2 * NG)][flat % (2 * NG)] = v[e];
+    }
   }
 }
 
-// Loads the lane's V code and sign words of one group and accumulates.
-template <int M, int RUN, int DG, int MT0, int NMT>
-__device__ __forceinline__ void v_group(const uint32_t* cb, const uint32_t* sb, int lg, int ln,
-                                        const uint32_t* lut, u32x4 pr, u32x4 pz,
-                                        f32x4 (&acc_r)[NMT], f32x4 (&acc_s)[NMT]) {
-  constexpr int NWC = (RUN * M) / 4;  // 8 tokens x RUN channels x M bits / 32
-  constexpr int ALC = lowbit(RUN * M) < 16 ? lowbit(RUN * M) : 16;
-  constexpr int NWS = RUN / 4;
-  constexpr int ALS = lowbit(RUN) < 16 ? lowbit(RUN) : 16;
-  uint32_t cw[NWC + 1];
-  load_words<NWC, ALC>(cb + (M * (lg * DG + RUN * ln)) / 4, cw);
-  cw[NWC] = 0u;
-  uint32_t swv[NWS];
-  load_words<NWS, ALS>(sb + (lg * DG + RUN * ln) / 4, swv);
-  v_accumulate<M, RUN, MT0, NMT>(cw, swv, lut, pr, pz, acc_r, acc_s);
+constexpr int max_lane_shift(int kb) {
+  int m = 0;
+  for (int g = 0; g < 4; ++g) m = (kb * g) % 32 > m ? (kb * g) % 32 : m;
+  return m;
+}
+
+// Compile-time geometry of one decode instantiation.
+//
+// Logit product: chunk c of 32 k-slots lies in quantizer group g = c / CPG
+// (local chunk cl = c % CPG); lane group lg, slot s holds channel
+// 8 CPG lg + 8 cl + s of that group, so a lane's channels of one token form a
+// single contiguous run of 8 CPG codes (8 M CPG bits) of the row.
+// V product: tile v of 16 rows lies in group g = v / MTPG; row r holds channel
+// RUN r + v % MTPG of the group, so a lane's channels are one run of RUN.
+template <int D, int NG, int M0, int M1>
+struct Geo {
+  static constexpr int DG = D / NG, CPG = DG / 32, NC = D / 32, NMT = D / 16, MTPG = NMT / NG,
+                       RUN = DG / 16;
+  static constexpr int MB[2] = {M0, M1};
+  static constexpr int CWG[2] = {(M0 * DG + 31) / 32, NG > 1 ? (M1 * DG + 31) / 32 : 0};
+  static constexpr int CW = CWG[0] + CWG[1];
+  static constexpr int CWOFF[2] = {0, CWG[0]};
+  static constexpr int SWG = (DG + 31) / 32;
+  static constexpr int SW = SWG * NG;
+  static constexpr int SWOFF[2] = {0, SWG};
+  static constexpr int BCW = M0 * DG + (NG > 1 ? M1 * DG : 0);
+  static constexpr int BCWOFF[2] = {0, M0 * DG};
+  static constexpr int BSW = D;
+  static constexpr int BSWOFF[2] = {0, DG};
+  // per lane and token: K code bits, words loaded, offset in the lane's K words
+  static constexpr int KB[2] = {8 * M0 * CPG, 8 * M1 * CPG};
+  static constexpr int KSH[2] = {max_lane_shift(KB[0]), max_lane_shift(KB[1])};
+  static constexpr int KNW[2] = {(KB[0] + KSH[0] + 31) / 32, NG > 1 ? (KB[1] + KSH[1] + 31) / 32 : 0};
+  static constexpr int KOFF[2] = {0, KNW[0]};
+  static constexpr int KNWT = KNW[0] + KNW[1];
+  // per lane: V code words and sign words of each group
+  static constexpr int VNW[2] = {RUN * M0 / 4, NG > 1 ? RUN * M1 / 4 : 0};
+  static constexpr int VOFF[2] = {0, VNW[0]};
+  static constexpr int VNWT = VNW[0] + VNW[1];
+  static constexpr int VNS = RUN / 4;
+  // table sizes
+  static constexpr int KE[2] = {1 << (2 * M0), 1 << (2 * M1)};
+  static constexpr int KTB[2] = {Tab<KE[0], 4>::BYTES, NG > 1 ? Tab<KE[1], 4>::BYTES : 0};
+  static constexpr int VTB[2] = {Tab<KE[0], 4>::BYTES, NG > 1 ? Tab<KE[1], 4>::BYTES : 0};
+  static constexpr int STB = Tab<16, 8>::BYTES;
+};
+
+// Raw record data of one 32-token tile for one lane (what it loads from HBM).
+template <int D, int NG, int M0, int M1>
+struct Raw {
+  using G = Geo<D, NG, M0, M1>;
+  uint32_t kc[2][G::KNWT];  // K code words of the lane's token in each half-tile
+  uint32_t ks[2][NG];       // K sign word holding the lane's sign bits, per group
+  float kn[NG];             // the lane's share of the tile's K norms
+  float vn[NG];             // and of the V norms
+  uint32_t vc[G::VNWT];     // V code words (octet lg, channels RUN ln ..)
+  uint32_t vs[G::VNS * NG]; // V sign words
+};
+
+// Per-lane word offsets of a tile's data, relative to the tile's first row
+// (K, norms) or block (V); the same for every tile.
+template <int D, int NG, int M0, int M1>
+struct LaneOff {
+  uint32_t kc[2][NG];
+  uint32_t ks[2][NG];
+  uint32_t vc[NG];
+  uint32_t vs[NG];
+};
+
+template <int D, int NG, int M0, int M1>
+__device__ __forceinline__ LaneOff<D, NG, M0, M1> lane_offsets(int ln, int lg) {
+  using G = Geo<D, NG, M0, M1>;
+  LaneOff<D, NG, M0, M1> o;
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau) {
+    // logit-product row ln <-> token 8 (ln / 4) + 4 tau + ln % 4 of the tile
+    const uint32_t row = 8 * (ln >> 2) + 4 * tau + (ln & 3);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      o.kc[tau][g] = row * G::CW + G::CWOFF[g] + ((G::KB[g] * lg) >> 5);
+      o.ks[tau][g] = row * G::SW + G::SWOFF[g] + ((8 * G::CPG * lg) >> 5);
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    o.vc[g] = G::BCWOFF[g] + (G::MB[g] * (lg * G::DG + G::RUN * ln)) / 4;
+    o.vs[g] = G::BSWOFF[g] + (lg * G::DG + G::RUN * ln) / 4;
+  }
+  return o;
+}
+
+// Loads one 32-token tile whose first cache row is row0 (wave-uniform, a
+// multiple of 32): the base addresses are scalar, the lanes add their offsets.
+template <int D, int NG, int M0, int M1, bool WV>
+__device__ __forceinline__ void load_tile(const DArgs& a, int64_t row0, int lane,
+                                          const LaneOff<D, NG, M0, M1>& o, Raw<D, NG, M0, M1>& r) {
+  using G = Geo<D, NG, M0, M1>;
+  const uint32_t* kc = a.kc + row0 * G::CW;
+  const uint32_t* ks = a.ks + row0 * G::SW;
+  auto k_rows = [&](auto gc) {
+    constexpr int g = decltype(gc)::value;
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      load_w<G::KNW[g]>(kc + o.kc[tau][g], &r.kc[tau][G::KOFF[g]]);
+      r.ks[tau][g] = ks[o.ks[tau][g]];
+    }
+  };
+  k_rows(std::integral_constant<int, 0>{});
+  if constexpr (NG > 1) k_rows(std::integral_constant<int, 1>{});
+  const float* kn = a.kn + row0 * (2 * NG);
+#pragma unroll
+  for (int e = 0; e < NG; ++e) r.kn[e] = kn[lane * NG + e];
+  if constexpr (WV) {
+    const float* vn = a.vn + row0 * (2 * NG);
+#pragma unroll
+    for (int e = 0; e < NG; ++e) r.vn[e] = vn[lane * NG + e];
+    const int64_t blk = row0 / 32;
+    const uint32_t* vc = a.vc + blk * G::BCW;
+    const uint32_t* vs = a.vs + blk * G::BSW;
+    auto v_words = [&](auto gc) {
+      constexpr int g = decltype(gc)::value;
+      load_w<G::VNW[g]>(vc + o.vc[g], &r.vc[G::VOFF[g]]);
+      load_w<G::VNS>(vs + o.vs[g], &r.vs[G::VNS * g]);
+    };
+    v_words(std::integral_constant<int, 0>{});
+    if constexpr (NG > 1) v_words(std::integral_constant<int, 1>{});
+  }
 }
 
 template <int D, int NG, int M0, int M1, bool WV>
-__global__ __launch_bounds__(256) void decode_kernel(DArgs a) {
-  constexpr int DG = D / NG;     // channels per group
-  constexpr int NC = D / 32;     // 32-channel chunks of the logit product
-  constexpr int CPG = NC / NG;   // chunks per group
-  constexpr int NMT = D / 16;    // 16-channel tiles of the V product
-  constexpr int MTPG = NMT / NG; // V tiles per group
-  constexpr int RUN = DG / 16;   // channels per lane in each group (V operand)
-  constexpr int MB[2] = {M0, M1};
-  // token-major word offsets of each group's codes / signs
-  constexpr int CW0 = (M0 * DG + 31) / 32;
-  constexpr int CW = CW0 + (NG > 1 ? (M1 * DG + 31) / 32 : 0);
-  constexpr int SW0 = (DG + 31) / 32;
-  constexpr int SW = SW0 * NG;
-  constexpr int CWOFF[2] = {0, CW0};
-  constexpr int SWOFF[2] = {0, SW0};
-  // block-record word offsets
-  constexpr int BCW = M0 * DG + (NG > 1 ? M1 * DG : 0);
-  constexpr int BCWOFF[2] = {0, M0 * DG};
-  constexpr int BSW = D;
-  constexpr int BSWOFF[2] = {0, DG};
-  constexpr int LUT0 = 1 << (2 * M0);
-  constexpr int LUT1 = NG > 1 ? 1 << (2 * M1) : 0;
-  constexpr int LUTOFF[2] = {0, LUT0};
-
-  __shared__ u32x2a8 klut[LUT0 + LUT1];
-  __shared__ uint32_t vlut[WV ? LUT0 + LUT1 : 1];
+__global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
+  using G = Geo<D, NG, M0, M1>;
+  constexpr int NC = G::NC, CPG = G::CPG, NMT = G::NMT, MTPG = G::MTPG, RUN = G::RUN, DG = G::DG;
+  constexpr int KT1 = G::KTB[0], VT0 = KT1 + G::KTB[1], VT1 = VT0 + G::VTB[0];
+  constexpr int ST = VT1 + G::VTB[1];
+  // K lo tables (fp16 rounding remainders x 2^11) after the sign table, skewed
+  // by 128 bytes so that a hi/lo pair of reads is never fused into one
+  // two-register read (whose registers would then need moving into place)
+  constexpr int KLO0 = ST + G::STB + 128, KLO1 = KLO0 + G::KTB[0];
+  constexpr int TAB_BYTES = KLO1 + G::KTB[1];
+  constexpr int ACC_BYTES = WV ? 2 * (2 * 4 * NMT * 64) * 4 : 0;  // two merge regions
+  constexpr int SMEM = TAB_BYTES > ACC_BYTES ? TAB_BYTES : ACC_BYTES;
+  __shared__ __align__(16) unsigned char s_tab[SMEM];  // tables; after the loop: merge buffer
+  __shared__ __align__(16) float s_nrm[kWaves][2][64 * NG];  // per-wave norm staging (K, V)
   __shared__ float s_m[kWaves][16];
-  __shared__ float s_l[16];
-  __shared__ float s_acc[WV ? 16 * 2 * D : 1];
+  __shared__ float s_lw[kWaves][16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int ln = lane & 15;
   const int lg = lane >> 4;
   const int split = blockIdx.x;
@@ -258,52 +362,92 @@ __global__ __launch_bounds__(256) void decode_kernel(DArgs a) {
   const int hblk = blockIdx.z;
   const int b = bh / a.hkv;
   const int kvh = bh % a.hkv;
+  const uint32_t off8 = 8u * (lane & 31), off4 = 4u * lane;
 
-  // ---- pair tables: entry e -> (c[e & (L-1)], c[e >> M]) as two fp16 ----
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    const int m = MB[g];
-    const int L = 1 << m;
-    const int coff = g == 0 ? 0 : (1 << M0);
-    for (int e = tid; e < (1 << (2 * m)); e += 256) {
-      const float c0 = a.kcent[coff + (e & (L - 1))], c1 = a.kcent[coff + (e >> m)];
-      const _Float16 h0 = (_Float16)c0, h1 = (_Float16)c1;
-      klut[LUTOFF[g] + e] = u32x2a8{h2bits(c0, c1),
-                                    h2bits((c0 - (float)h0) * kLoScale, (c1 - (float)h1) * kLoScale)};
-      if constexpr (WV) vlut[LUTOFF[g] + e] = h2bits(a.vcent[coff + (e & (L - 1))], a.vcent[coff + (e >> m)]);
-    }
-  }
-  if constexpr (WV) {
-    for (int e = tid; e < 16 * 2 * D; e += 256) s_acc[e] = 0.f;
-    if (tid < 16) s_l[tid] = 0.f;
-  }
-
-  // ---- this lane's head and its query operands (B operand: channels x heads) ----
-  const int hloc = hblk * 16 + ln;  // head index within the KV group
-  const bool hvalid = hloc < a.group;
-  const int hq = kvh * a.group + hloc;
-  u32x4 qr[NC], qrl[NC], qs[NC], qsl[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    if (hvalid) {
-      const _Float16* qp = a.qprep + ((int64_t)b * a.hq + hq) * (4 * D) + 32 * c + 8 * lg;
-      qr[c] = *reinterpret_cast<const u32x4*>(qp);
-      qrl[c] = *reinterpret_cast<const u32x4*>(qp + D);
-      qs[c] = *reinterpret_cast<const u32x4*>(qp + 2 * D);
-      qsl[c] = *reinterpret_cast<const u32x4*>(qp + 3 * D);
-    } else {
-      qr[c] = qrl[c] = qs[c] = qsl[c] = u32x4{0, 0, 0, 0};
-    }
-  }
-  __syncthreads();
-
-  const float alpha[2] = {sqrtf(0.5f * (float)M_PI) / (float)DG, sqrtf(0.5f * (float)M_PI) / (float)DG};
+  // ---- this wave's tiles; the first one is loaded before the tables are
+  // built, so its memory latency overlaps the table setup ----
   const int64_t N = a.n_ctx;
   const int64_t n_tiles = (N + kTile - 1) / kTile;
   const int64_t tps = (n_tiles + a.n_split - 1) / a.n_split;
   const int64_t t_begin = split * tps;
   const int64_t t_end = t_begin + tps < n_tiles ? t_begin + tps : n_tiles;
   const int64_t rowbase = (int64_t)bh * a.cap;
+  const LaneOff<D, NG, M0, M1> lo = lane_offsets<D, NG, M0, M1>(ln, lg);
+
+  // ---- tables (built from an LDS copy of the centroids) ----
+  __shared__ float s_cent[2][32];
+  float cent_k = 0.f, cent_v = 0.f;
+  if (tid < 32) {
+    const int nc = (1 << M0) + (NG > 1 ? (1 << M1) : 0);
+    cent_k = a.kcent[tid < nc ? tid : nc - 1];
+    if constexpr (WV) cent_v = a.vcent[tid < nc ? tid : nc - 1];
+  }
+  Raw<D, NG, M0, M1> ra, rb, rc;
+  int64_t tile = t_begin + wv;
+  // (unconditional, so the wait for the centroids below need not drain it;
+  // a wave without tiles loads tile 0, which always exists, and drops it)
+  load_tile<D, NG, M0, M1, WV>(a, rowbase + (tile < t_end ? tile : 0) * kTile, lane, lo, ra);
+  if (tid < 32) {
+    s_cent[0][tid] = cent_k;
+    s_cent[1][tid] = cent_v;
+  }
+  __syncthreads();
+  {
+    auto kentry = [&](const float* cent, int m, int lo_off) {
+      return [=](int e, unsigned char* dst) {
+        const int L = 1 << m;
+        const float c0 = cent[e & (L - 1)], c1 = cent[e >> m];
+        const _Float16 h0 = (_Float16)c0, h1 = (_Float16)c1;
+        *reinterpret_cast<uint32_t*>(dst) = h2bits(c0, c1);
+        *reinterpret_cast<uint32_t*>(dst + lo_off) =
+            h2bits((c0 - (float)h0) * kLoScale, (c1 - (float)h1) * kLoScale);
+      };
+    };
+    auto entry = [&](const float* cent, int m) {
+      return [=](int e, unsigned char* dst) {
+        const int L = 1 << m;
+        *reinterpret_cast<uint32_t*>(dst) = h2bits(cent[e & (L - 1)], cent[e >> m]);
+      };
+    };
+    tab_build<G::KE[0], 4>(s_tab, tid, kentry(s_cent[0], M0, KLO0));
+    if constexpr (NG > 1)
+      tab_build<G::KE[1], 4>(s_tab + KT1, tid, kentry(s_cent[0] + (1 << M0), M1, KLO1 - KT1));
+    if constexpr (WV) {
+      tab_build<G::KE[0], 4>(s_tab + VT0, tid, entry(s_cent[1], M0));
+      if constexpr (NG > 1) tab_build<G::KE[1], 4>(s_tab + VT1, tid, entry(s_cent[1] + (1 << M0), M1));
+    }
+    // nibble -> four fp16 values, +1 where the bit is set, -1 where clear
+    tab_build<16, 8>(s_tab + ST, tid, [](int e, unsigned char* dst) {
+      uint32_t w[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        w[h] = (((e >> (2 * h)) & 1) ? 0x3C00u : 0xBC00u) | (((e >> (2 * h + 1)) & 1) ? 0x3C000000u : 0xBC000000u);
+      *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
+    });
+  }
+
+  // ---- this lane's head and its query operands (B operand: channels x heads) ----
+  const int hloc = hblk * 16 + ln;  // head index within the KV group
+  const bool hvalid = hloc < a.group;
+  const int hq = kvh * a.group + hloc;
+  u32x4 qr[NC], qrl[NC], qs[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int g = c / CPG, cl = c % CPG;
+    if (hvalid) {
+      const _Float16* qp =
+          a.qprep + ((int64_t)b * a.hq + hq) * (3 * D) + g * DG + 8 * CPG * lg + 8 * cl;
+      qr[c] = *reinterpret_cast<const u32x4*>(qp);
+      qrl[c] = *reinterpret_cast<const u32x4*>(qp + D);
+      qs[c] = *reinterpret_cast<const u32x4*>(qp + 2 * D);
+    } else {
+      qr[c] = qrl[c] = qs[c] = u32x4{0, 0, 0, 0};
+    }
+  }
+  __syncthreads();
+
+  constexpr float kAlpha = 1.2533141373155003f / (float)DG;  // sqrt(pi/2) / d_g
+  const unsigned char* stab = s_tab + ST;
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 acc_r[WV ? NMT : 1], acc_s[WV ? NMT : 1];
@@ -313,53 +457,65 @@ __global__ __launch_bounds__(256) void decode_kernel(DArgs a) {
     acc_s[v] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  for (int64_t tile = t_begin + wv; tile < t_end; tile += kWaves) {
-    const int64_t T0 = tile * kTile;
-    // ---------------- K: logits ----------------
-    // hi and lo (x 2^11) accumulators of the MSE part and of the sketch part
-    f32x4 lr[2][NG], lrl[2][NG], ls[2][NG], lsl[2][NG];
+  auto compute = [&](const Raw<D, NG, M0, M1>& r, int64_t T0) {
+    // tokens past n_ctx (only in the last tile): norms staged as 0 (rows past
+    // the context may hold anything) and logits masked to -inf below
+    const bool full = T0 + kTile <= N;
+    // stage this tile's norms for the head-major lanes
+    {
+      // lane l holds float l NG + e of the tile's [32][2 NG] norms
+      const bool nok = full || T0 + (lane * NG) / (2 * NG) < N;
 #pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-      // A operand row ln <-> token 8 (ln / 4) + 4 tau + ln % 4 of the tile
-      const int64_t row = rowbase + T0 + 8 * (ln >> 2) + 4 * tau + (ln & 3);
-      const uint32_t* crow = a.kc + row * CW;
-      const uint32_t* srow = a.ks + row * SW;
-      uint32_t sw[SW];
-      load_words<SW, (SW * 4) % 16 == 0 ? 16 : 4>(srow, sw);
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        lr[tau][g] = lrl[tau][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-        ls[tau][g] = lsl[tau][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int e = 0; e < NG; ++e) {
+        s_nrm[wv][0][lane * NG + e] = nok ? r.kn[e] : 0.f;
+        if constexpr (WV) s_nrm[wv][1][lane * NG + e] = nok ? r.vn[e] : 0.f;
       }
+    }
+    // LDS operations of one wave execute in order; the wave barrier only keeps
+    // the compiler from moving the reads above the writes (a memory fence here
+    // would also wait for the next tile's loads in flight)
+    __builtin_amdgcn_wave_barrier();
+    // ---------------- K: logits ----------------
+    f32x4 lr[2][NG], lrl[2][NG], ls[2][NG];
+    auto k_group = [&](auto gc, int tau) {
+      constexpr int g = decltype(gc)::value;
+      constexpr int M = G::MB[g];
+      lr[tau][g] = lrl[tau][g] = ls[tau][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // the lane's K code bits of this group start at bit (KB lg) mod 32 of its words
+      uint32_t w[G::KNW[g] + 1];
+      const int sh = (G::KB[g] * lg) & 31;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const int g = c / CPG;
-        const int m = MB[g];
-        // channels 32 (c % CPG) + 8 lg .. + 7 of group g: 8m bits at this bit offset
-        const int bit = 32 * CWOFF[g] + m * (32 * (c % CPG) + 8 * lg);
-        const uint32_t* wp = crow + (bit >> 5);
-        const int sh = bit & 31;
-        uint32_t field = wp[0] >> sh;
-        if (sh + 8 * m > 32) field |= wp[1] << (32 - sh);
+      for (int i = 0; i < G::KNW[g]; ++i) {
+        const uint32_t lo = r.kc[tau][G::KOFF[g] + i];
+        const uint32_t hi = i + 1 < G::KNW[g] ? r.kc[tau][G::KOFF[g] + i + 1] : 0u;
+        w[i] = G::KSH[g] ? __builtin_amdgcn_alignbit(hi, lo, sh) : lo;
+      }
+      w[G::KNW[g]] = 0u;
+      const uint32_t sword = r.ks[tau][g] >> ((8 * CPG * lg) & 31);
+      const unsigned char* kt = g == 0 ? s_tab : s_tab + KT1;
+#pragma unroll
+      for (int cl = 0; cl < CPG; ++cl) {
+        const int c = g * CPG + cl;
+        constexpr int LO = g == 0 ? KLO0 : KLO1 - KT1;
         u32x4 ak, akl;
-        if (g == 0)
-          codes_to_f16_split<M0>(field, klut, ak, akl);
-        else
-          codes_to_f16_split<M1>(field, klut + LUT0, ak, akl);
-        const uint32_t sbyte = (sw[SWOFF[g] + (c % CPG)] >> (8 * lg)) & 0xFFu;
-        const u32x4 az = signs_to_pm1(sbyte);
-        // c q = c_hi q_hi + 2^-11 (c_lo' q_hi + c_hi q_lo'), products exact, fp32 sums
+        kcodes8<M, LO>(field_at(w, 8 * M * cl, 8 * M), kt, off4, ak, akl);
+        const u32x4 az = signs8((sword >> (8 * cl)) & 0xFFu, stab, off8);
+        // c q = c_hi q_hi + 2^-11 (c_lo' q_hi + c_hi q_lo'); products exact, fp32 sums
         lr[tau][g] = mfma16(ak, qr[c], lr[tau][g]);
         lrl[tau][g] = mfma16(akl, qr[c], lrl[tau][g]);
         lrl[tau][g] = mfma16(ak, qrl[c], lrl[tau][g]);
         ls[tau][g] = mfma16(az, qs[c], ls[tau][g]);
-        lsl[tau][g] = mfma16(az, qsl[c], lsl[tau][g]);
       }
+    };
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      k_group(std::integral_constant<int, 0>{}, tau);
+      if constexpr (NG > 1) k_group(std::integral_constant<int, 1>{}, tau);
     }
     // lane (head ln, lg) now holds tokens 8 lg + j, j = 4 tau + i
     const int64_t tok0 = T0 + 8 * lg;
     float kn[8][2 * NG];
-    load_norms<NG>(a.kn + (rowbase + tok0) * (2 * NG), kn);
+    load_norms<NG>(&s_nrm[wv][0][8 * lg * 2 * NG], kn);
     float l2[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -368,12 +524,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DArgs a) {
 #pragma unroll
       for (int g = 0; g < NG; ++g)
         s += kn[j][2 * g] * fmaf(kLoInv, lrl[tau][g][i], lr[tau][g][i]) +
-             alpha[g] * kn[j][2 * g + 1] * fmaf(kLoInv, lsl[tau][g][i], ls[tau][g][i]);
+             kAlpha * kn[j][2 * g + 1] * ls[tau][g][i];
       const float lg_val = a.scale * s;
-      const bool ok = tok0 + j < N;
-      if (a.logits && hvalid && ok)
+      if (a.logits && hvalid && (full || tok0 + j < N))
         a.logits[((int64_t)b * a.hq + hq) * N + tok0 + j] = lg_val;
-      l2[j] = ok ? lg_val * kLog2e : -INFINITY;
+      l2[j] = lg_val * kLog2e;
+    }
+    if (!full) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) l2[j] = tok0 + j < N ? l2[j] : -INFINITY;
     }
     if constexpr (WV) {
       // ---------------- online softmax ----------------
@@ -383,51 +542,98 @@ __global__ __launch_bounds__(256) void decode_kernel(DArgs a) {
       mx = xor_max(mx, 16);
       mx = xor_max(mx, 32);
       const float m_new = fmaxf(m_run, mx);
-      const float corr = exp2f(m_run - m_new);
-      m_run = m_new;
+      if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+        // some head's maximum moved: rescale (factor 1 for the others)
+        const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= corr;
+#pragma unroll
+        for (int v = 0; v < NMT; ++v) {
+          acc_r[v] *= corr;
+          acc_s[v] *= corr;
+        }
+        m_run = m_new;
+      }
       float p[8], psum = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        p[j] = exp2f(l2[j] - m_new);
+        p[j] = __builtin_amdgcn_exp2f(l2[j] - m_run);
         psum += p[j];
       }
-      l_run = l_run * corr + psum;
-#pragma unroll
-      for (int v = 0; v < NMT; ++v) {
-        acc_r[v] *= corr;
-        acc_s[v] *= corr;
-      }
+      l_run += psum;
       // B operands of the V product: slot j <-> token 8 lg + j
       float vn[8][2 * NG];
-      load_norms<NG>(a.vn + (rowbase + tok0) * (2 * NG), vn);
+      load_norms<NG>(&s_nrm[wv][1][8 * lg * 2 * NG], vn);
       u32x4 pr[NG], pz[NG];
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int j0 = 2 * q, j1 = 2 * q + 1;
-          const bool ok0 = tok0 + j0 < N, ok1 = tok0 + j1 < N;
-          const float r0 = ok0 ? p[j0] * vn[j0][2 * g] : 0.f;
-          const float r1 = ok1 ? p[j1] * vn[j1][2 * g] : 0.f;
-          // alpha_g is applied once per head in the combine, not here
-          const float z0 = ok0 ? p[j0] * vn[j0][2 * g + 1] : 0.f;
-          const float z1 = ok1 ? p[j1] * vn[j1][2 * g + 1] : 0.f;
-          pr[g][q] = h2bits(r0, r1);
-          pz[g][q] = h2bits(z0, z1);
+          // (alpha_g is applied once per head in the combine; past n_ctx p = 0
+          // and the staged norms are 0)
+          pr[g][q] = h2bits(p[j0] * vn[j0][2 * g], p[j1] * vn[j1][2 * g]);
+          pz[g][q] = h2bits(p[j0] * vn[j0][2 * g + 1], p[j1] * vn[j1][2 * g + 1]);
         }
       }
       // ---------------- V: accumulate in the rotated / sketch domains ----------------
-      const int64_t blk = (rowbase + T0) / 32;
-      v_group<M0, RUN, DG, 0, NMT>(a.vc + blk * BCW + BCWOFF[0], a.vs + blk * BSW + BSWOFF[0], lg,
-                                   ln, vlut, pr[0], pz[0], acc_r, acc_s);
-      if constexpr (NG > 1)
-        v_group<M1, RUN, DG, MTPG, NMT>(a.vc + blk * BCW + BCWOFF[1], a.vs + blk * BSW + BSWOFF[1],
-                                        lg, ln, vlut + LUT0, pr[1], pz[1], acc_r, acc_s);
+      auto v_group = [&](auto gc) {
+        constexpr int g = decltype(gc)::value;
+        constexpr int M = G::MB[g];
+        uint32_t cw[G::VNW[g] + 1];
+#pragma unroll
+        for (int i = 0; i < G::VNW[g]; ++i) cw[i] = r.vc[G::VOFF[g] + i];
+        cw[G::VNW[g]] = 0u;
+        const unsigned char* vt = g == 0 ? s_tab + VT0 : s_tab + VT1;
+#pragma unroll
+        for (int u = 0; u < RUN; ++u) {
+          const u32x4 av = codes8<M>(field_at(cw, 8 * M * u, 8 * M), vt, off4);
+          const u32x4 az = signs8((r.vs[G::VNS * g + (u >> 2)] >> (8 * (u & 3))) & 0xFFu, stab, off8);
+          acc_r[g * MTPG + u] = mfma16(av, pr[g], acc_r[g * MTPG + u]);
+          acc_s[g * MTPG + u] = mfma16(az, pz[g], acc_s[g * MTPG + u]);
+        }
+      };
+      v_group(std::integral_constant<int, 0>{});
+      if constexpr (NG > 1) v_group(std::integral_constant<int, 1>{});
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  // ---- software-pipelined loop: tile t + 4 is loaded while tile t is computed ----
+  // (the prefetch is unconditional: on the last tile it reloads that tile, an
+  // in-bounds cache hit, so the compiler sees one straight-line load stream)
+  // Two tiles stay in flight while one is computed: three register buffers
+  // in rotation (the loop is unrolled three times so no data is copied).
+  // Prefetches past the wave's last tile reload that tile (in bounds,
+  // dropped).
+  if (tile < t_end) {
+    const int64_t last = t_end - 1 - ((t_end - 1 - tile) % kWaves);  // this wave's last tile
+    auto next = [&](int64_t t, int k) { return t + k * kWaves <= last ? t + k * kWaves : last; };
+    load_tile<D, NG, M0, M1, WV>(a, rowbase + next(tile, 1) * kTile, lane, lo, rb);
+    for (;;) {
+      load_tile<D, NG, M0, M1, WV>(a, rowbase + next(tile, 2) * kTile, lane, lo, rc);
+      compute(ra, tile * kTile);
+      if (tile == last) break;
+      tile += kWaves;
+      load_tile<D, NG, M0, M1, WV>(a, rowbase + next(tile, 2) * kTile, lane, lo, ra);
+      compute(rb, tile * kTile);
+      if (tile == last) break;
+      tile += kWaves;
+      load_tile<D, NG, M0, M1, WV>(a, rowbase + next(tile, 2) * kTile, lane, lo, rb);
+      compute(rc, tile * kTile);
+      if (tile == last) break;
+      tile += kWaves;
     }
   }
 
   if constexpr (WV) {
-    // ---- merge the four waves into one partial ----
+    // ---- merge the four waves into one partial (the table space is reused) ----
+    // Region r (r = 0, 1) holds, for every accumulator register (part, i, v)
+    // and lane (lg, ln), the sum of the values of waves r and r + 2 scaled to
+    // the workgroup maximum; the index is register-major so that every store
+    // writes 64 consecutive floats. Waves 0 and 1 store, then waves 2 and 3 add.
+    float* s_red = reinterpret_cast<float*>(s_tab);
+    constexpr int REG = 2 * 4 * NMT * 64;  // floats per region
+    __syncthreads();  // tables are no longer read
     l_run += __shfl_xor(l_run, 16, 64);
     l_run += __shfl_xor(l_run, 32, 64);
     if (lg == 0) s_m[wv][ln] = m_run;
@@ -436,76 +642,153 @@ __global__ __launch_bounds__(256) void decode_kernel(DArgs a) {
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][ln]);
     const float e = (m_run == -INFINITY) ? 0.f : exp2f(m_run - M);
-    if (lg == 0) atomicAdd(&s_l[ln], l_run * e);
+    if (lg == 0) s_lw[wv][ln] = l_run * e;
+    float* reg = s_red + (wv & 1) * REG + lane;
+    if (wv < 2) {
 #pragma unroll
-    for (int v = 0; v < NMT; ++v) {
-      const int g = v / MTPG;
+      for (int v = 0; v < NMT; ++v)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // accumulator row 4 lg + i of V tile v <-> channel of group g
-        const int ch = g * DG + RUN * (4 * lg + i) + (v % MTPG);
-        atomicAdd(&s_acc[ln * 2 * D + ch], acc_r[v][i] * e);
-        atomicAdd(&s_acc[ln * 2 * D + D + ch], acc_s[v][i] * e);
-      }
+        for (int i = 0; i < 4; ++i) {
+          reg[((0 * 4 + i) * NMT + v) * 64] = acc_r[v][i] * e;
+          reg[((1 * 4 + i) * NMT + v) * 64] = acc_s[v][i] * e;
+        }
+    }
+    __syncthreads();
+    if (wv >= 2) {
+#pragma unroll
+      for (int v = 0; v < NMT; ++v)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          reg[((0 * 4 + i) * NMT + v) * 64] += acc_r[v][i] * e;
+          reg[((1 * 4 + i) * NMT + v) * 64] += acc_s[v][i] * e;
+        }
     }
     __syncthreads();
     // write the partial of every valid head: [max (log2 domain), sum, acc_rot[D], acc_sk[D]]
     const int nh = a.group - hblk * 16 < 16 ? a.group - hblk * 16 : 16;
     for (int e2 = tid; e2 < nh * (2 + 2 * D); e2 += 256) {
       const int h = e2 / (2 + 2 * D), k = e2 % (2 + 2 * D);
-      float Mh = s_m[0][h];
+      float val;
+      if (k < 2) {
+        float Mh = s_m[0][h];
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) Mh = fmaxf(Mh, s_m[w][h]);
-      const float val = k == 0 ? Mh : (k == 1 ? s_l[h] : s_acc[h * 2 * D + k - 2]);
+        for (int w = 1; w < kWaves; ++w) Mh = fmaxf(Mh, s_m[w][h]);
+        val = k == 0 ? Mh : s_lw[0][h] + s_lw[1][h] + s_lw[2][h] + s_lw[3][h];
+      } else {
+        // channel ch of part pt <-> register (pt, i, v), lane (lg, ln = h):
+        // ch = g DG + RUN (4 lg + i) + u, v = g MTPG + u
+        const int pt = (k - 2) / D, ch = (k - 2) % D;
+        const int g = ch / DG, local = ch % DG, u = local % RUN, row = local / RUN;
+        const int idx = (((pt * 4 + (row & 3)) * NMT + g * MTPG + u) * 4 + (row >> 2)) * 16 + h;
+        val = s_red[idx] + s_red[REG + idx];
+      }
       const int hq2 = kvh * a.group + hblk * 16 + h;
       a.part[(((int64_t)b * a.hq + hq2) * a.n_split + split) * (2 + 2 * D) + k] = val;
     }
   }
 }
 
-
 // ---------------------------------------------------------------------------
-// Query preparation: q_rot = rot q, q_sk = sketch q (fp32 sums), each stored
-// as an fp16 pair (hi, (q - hi) * 2^11) so the logit products keep fp32 accuracy.
-// Thread t computes output channel t % D of matrix t / D for kPrepHeads heads.
+// Query preparation: q_rot = rot q (stored as fp16 hi and (q - hi) * 2^11)
+// and q_sk = sketch q (fp16), fp32 sums in ascending k. A workgroup takes 16
+// rows of the stacked [rot; sketch] matrix and kPrepHeads heads; both are
+// staged in LDS by coalesced 16-byte loads, then thread (i, hq) forms the
+// dot products of row i with heads hq, hq + 16, ...
 // ---------------------------------------------------------------------------
-constexpr int kPrepHeads = 4;
+constexpr int kPrepHeads = 64;
+constexpr int kPrepRows = 16;
 
 template <int D>
-__global__ __launch_bounds__(2 * D) void prep_kernel(const void* q, int q_bf16, int n_heads,
-                                                     const float* rot, const float* sketch,
-                                                     _Float16* qprep) {
-  __shared__ float sq[kPrepHeads][D];
-  const int h0 = blockIdx.x * kPrepHeads;
+__global__ __launch_bounds__(256) void prep_kernel(const void* q, int q_bf16, int n_heads,
+                                                   const float* rot, const float* sketch,
+                                                   _Float16* qprep) {
+  constexpr int QS = D + 4;  // LDS row stride (floats)
+  constexpr int HPT = kPrepHeads / 16;  // heads per thread
+  __shared__ __align__(16) float sm[kPrepRows][QS];
+  __shared__ __align__(16) float sq[kPrepHeads][QS];
   const int t = threadIdx.x;
-  for (int e = t; e < kPrepHeads * D; e += 2 * D) {
-    const int h = h0 + e / D, k = e % D;
-    float v = 0.f;
-    if (h < n_heads) {
-      const int64_t off = (int64_t)h * D + k;
-      v = q_bf16 ? __uint_as_float(((uint32_t) reinterpret_cast<const uint16_t*>(q)[off]) << 16)
-                 : reinterpret_cast<const float*>(q)[off];
+  const int r0 = blockIdx.x * kPrepRows;  // first row of [rot; sketch]
+  const int h0 = blockIdx.y * kPrepHeads;
+  const float* mat = r0 < D ? rot + (int64_t)r0 * D : sketch + (int64_t)(r0 - D) * D;
+  {
+    constexpr int C4 = D / 4;  // 16-byte chunks per matrix row
+    f32x4 mb[kPrepRows * C4 / 256];
+#pragma unroll
+    for (int i = 0; i < kPrepRows * C4 / 256; ++i) {
+      const int c = t + 256 * i;
+      mb[i] = *reinterpret_cast<const f32x4*>(mat + (c / C4) * D + (c % C4) * 4);
     }
-    sq[e / D][k] = v;
+#pragma unroll
+    for (int i = 0; i < kPrepRows * C4 / 256; ++i) {
+      const int c = t + 256 * i;
+      *reinterpret_cast<f32x4*>(&sm[c / C4][(c % C4) * 4]) = mb[i];
+    }
+  }
+  if (q_bf16) {
+    constexpr int C8 = D / 8;  // 16-byte chunks per bf16 query row
+    constexpr int NC = kPrepHeads * C8 / 256;
+    u32x4 qb[NC];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c = t + 256 * i, h = h0 + c / C8;
+      const int hc = h < n_heads ? h : n_heads - 1;
+      qb[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(q) + (int64_t)hc * D +
+                                              (c % C8) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c = t + 256 * i;
+      float* dst = &sq[c / C8][(c % C8) * 8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dst[2 * e] = __uint_as_float(qb[i][e] << 16);
+        dst[2 * e + 1] = __uint_as_float(qb[i][e] & 0xFFFF0000u);
+      }
+    }
+  } else {
+    constexpr int C4 = D / 4;
+    constexpr int NC = kPrepHeads * C4 / 256;
+    f32x4 qb[NC];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c = t + 256 * i, h = h0 + c / C4;
+      const int hc = h < n_heads ? h : n_heads - 1;
+      qb[i] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(q) + (int64_t)hc * D +
+                                              (c % C4) * 4);
+    }
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c = t + 256 * i;
+      *reinterpret_cast<f32x4*>(&sq[c / C4][(c % C4) * 4]) = qb[i];
+    }
   }
   __syncthreads();
-  const int half = t / D, i = t % D;
-  const float* row = (half == 0 ? rot : sketch) + (int64_t)i * D;
-  float acc[kPrepHeads] = {};
-  for (int k = 0; k < D; ++k) {
-    const float mk = row[k];
+  const int i = t % kPrepRows, hq = t / kPrepRows;
+  float acc[HPT] = {};
+#pragma unroll 4
+  for (int k = 0; k < D; k += 4) {
+    const f32x4 m4 = *reinterpret_cast<const f32x4*>(&sm[i][k]);
 #pragma unroll
-    for (int h = 0; h < kPrepHeads; ++h) acc[h] = fmaf(mk, sq[h][k], acc[h]);
-  }
+    for (int r = 0; r < HPT; ++r) {
+      const f32x4 q4 = *reinterpret_cast<const f32x4*>(&sq[hq + 16 * r][k]);
 #pragma unroll
-  for (int h = 0; h < kPrepHeads; ++h)
-    if (h0 + h < n_heads) {
-      const _Float16 hi = (_Float16)acc[h];
-      const _Float16 lo = (_Float16)((acc[h] - (float)hi) * kLoScale);
-      _Float16* dst = qprep + (int64_t)(h0 + h) * 4 * D + half * 2 * D + i;
-      dst[0] = hi;
-      dst[D] = lo;
+      for (int j = 0; j < 4; ++j) acc[r] = fmaf(m4[j], q4[j], acc[r]);
     }
+  }
+  const int row = r0 + i;
+#pragma unroll
+  for (int r = 0; r < HPT; ++r) {
+    const int h = h0 + hq + 16 * r;
+    if (h >= n_heads) continue;
+    _Float16* dst = qprep + (int64_t)h * 3 * D;
+    const _Float16 hi = (_Float16)acc[r];
+    if (row < D) {
+      dst[row] = hi;
+      dst[D + row] = (_Float16)((acc[r] - (float)hi) * kLoScale);
+    } else {
+      dst[D + row] = hi;  // q_sk at [2 D, 3 D)
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -553,11 +836,12 @@ __global__ __launch_bounds__(2 * D) void combine_kernel(const float* part, int n
   // merged accumulators; alpha_g is applied to the sketch half here
   {
     float acc = 0.f;
+#pragma unroll 16
     for (int s = 0; s < n_split; ++s) acc = fmaf(s_w[s], P[(int64_t)s * (2 + 2 * D) + 2 + t], acc);
     if (t >= D) {
       const int j = t - D;
       const int dg = j < group_dim0 ? group_dim0 : D - group_dim0;
-      acc *= sqrtf(0.5f * (float)M_PI) / (float)dg;
+      acc *= 1.2533141373155003f / (float)dg;
     }
     s_acc[t] = acc;
   }
@@ -568,6 +852,7 @@ __global__ __launch_bounds__(2 * D) void combine_kernel(const float* part, int n
     const float* mat = half == 0 ? rot : sketch;
     const float* av = s_acc + half * D;
     float o = 0.f;
+#pragma unroll 16
     for (int j = 0; j < D; ++j) o = fmaf(mat[(int64_t)j * D + i], av[j], o);
     s_o[t] = o;
   }
@@ -620,13 +905,14 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 size_t workspace_for(const tq_decode_shape* s, int d, bool with_v, int n_split) {
   const size_t heads = (size_t)s->batch * s->n_q_heads;
-  size_t bytes = align256(heads * 4 * d * sizeof(_Float16));
+  size_t bytes = align256(heads * 3 * d * sizeof(_Float16));
   if (with_v) bytes += align256(heads * (size_t)n_split * (2 + 2 * d) * sizeof(float));
   return bytes;
 }
 
 template <int D, int NG, int M0, int M1, bool WV>
 hipError_t launch_decode(const DArgs& a, int n_hblk, hipStream_t st) {
+  (void)hipGetLastError();  // a launch error is reported below, not an older one
   hipLaunchKernelGGL((decode_kernel<D, NG, M0, M1, WV>),
                      dim3((unsigned)a.n_split, (unsigned)(a.batch * a.hkv), (unsigned)n_hblk), dim3(256),
                      0, st, a);
@@ -673,11 +959,12 @@ extern "C" tq_status tq_attn_decode_workspace_bytes(const tq_quantizer* kq, cons
   return TQ_OK;
 }
 
-extern "C" tq_status tq_attn_decode(const tq_quantizer* kq, const tq_quantizer* vq,
-                                    const tq_decode_shape* shape, const void* q, tq_dtype q_dtype,
-                                    const tq_cache* k_cache, const tq_cache* v_cache, float* logits,
-                                    float* out, void* workspace, size_t workspace_bytes,
-                                    void* stream) {
+extern "C" tq_status tq_attn_decode_phases(unsigned phases, const tq_quantizer* kq,
+                                           const tq_quantizer* vq, const tq_decode_shape* shape,
+                                           const void* q, tq_dtype q_dtype, const tq_cache* k_cache,
+                                           const tq_cache* v_cache, float* logits, float* out,
+                                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (phases == 0 || (phases & ~(unsigned)TQ_PHASE_ALL) != 0) return TQ_ERR_INVALID;
   if (!tq::quantizer_pointers_valid(kq) || !shape_valid(shape)) return TQ_ERR_INVALID;
   if (vq && !tq::quantizer_pointers_valid(vq)) return TQ_ERR_INVALID;
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_ERR_INVALID;
@@ -711,12 +998,15 @@ extern "C" tq_status tq_attn_decode(const tq_quantizer* kq, const tq_quantizer* 
   const int n_heads = shape->batch * shape->n_q_heads;
   _Float16* qprep = reinterpret_cast<_Float16*>(workspace);
   float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
-                                         align256((size_t)n_heads * 4 * D * sizeof(_Float16)));
+                                         align256((size_t)n_heads * 3 * D * sizeof(_Float16)));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
 
-  hipLaunchKernelGGL((prep_kernel<D>), dim3((n_heads + kPrepHeads - 1) / kPrepHeads), dim3(2 * D), 0,
-                     st, q, (int)(q_dtype == TQ_BF16), n_heads, kq->rot, kq->sketch, qprep);
-  if (hipGetLastError() != hipSuccess) return TQ_ERR_DEVICE;
+  if (phases & TQ_PHASE_PREP) {
+    (void)hipGetLastError();  // a launch error is reported below, not an older one
+    hipLaunchKernelGGL((prep_kernel<D>), dim3(2 * D / kPrepRows, (n_heads + kPrepHeads - 1) / kPrepHeads),
+                       dim3(256), 0, st, q, (int)(q_dtype == TQ_BF16), n_heads, kq->rot, kq->sketch, qprep);
+    if (hipGetLastError() != hipSuccess) return TQ_ERR_DEVICE;
+  }
 
   DArgs a{};
   a.batch = shape->batch;
@@ -740,18 +1030,30 @@ extern "C" tq_status tq_attn_decode(const tq_quantizer* kq, const tq_quantizer* 
   }
   a.logits = logits;
   a.part = part;
-  hipError_t e;
-  if (l.n_groups == 1)
-    e = with_v ? dispatch_m0<D, 1, true>(a, l.mse_bits[0], 0, n_hblk, st)
-               : dispatch_m0<D, 1, false>(a, l.mse_bits[0], 0, n_hblk, st);
-  else
-    e = with_v ? dispatch_m0<D, 2, true>(a, l.mse_bits[0], l.mse_bits[1], n_hblk, st)
-               : dispatch_m0<D, 2, false>(a, l.mse_bits[0], l.mse_bits[1], n_hblk, st);
-  if (e != hipSuccess) return TQ_ERR_DEVICE;
-  if (with_v) {
+  if (phases & TQ_PHASE_SPLIT) {
+    hipError_t e;
+    if (l.n_groups == 1)
+      e = with_v ? dispatch_m0<D, 1, true>(a, l.mse_bits[0], 0, n_hblk, st)
+                 : dispatch_m0<D, 1, false>(a, l.mse_bits[0], 0, n_hblk, st);
+    else
+      e = with_v ? dispatch_m0<D, 2, true>(a, l.mse_bits[0], l.mse_bits[1], n_hblk, st)
+                 : dispatch_m0<D, 2, false>(a, l.mse_bits[0], l.mse_bits[1], n_hblk, st);
+    if (e != hipSuccess) return TQ_ERR_DEVICE;
+  }
+  if (with_v && (phases & TQ_PHASE_COMBINE)) {
+    (void)hipGetLastError();  // a launch error is reported below, not an older one
     hipLaunchKernelGGL((combine_kernel<D>), dim3(n_heads), dim3(2 * D), 0, st, part, n_split, vq->rot,
                        vq->sketch, l.n_groups == 2 ? l.group_dim[0] : D, out);
     if (hipGetLastError() != hipSuccess) return TQ_ERR_DEVICE;
   }
   return TQ_OK;
+}
+
+extern "C" tq_status tq_attn_decode(const tq_quantizer* kq, const tq_quantizer* vq,
+                                    const tq_decode_shape* shape, const void* q, tq_dtype q_dtype,
+                                    const tq_cache* k_cache, const tq_cache* v_cache, float* logits,
+                                    float* out, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  return tq_attn_decode_phases(TQ_PHASE_ALL, kq, vq, shape, q, q_dtype, k_cache, v_cache, logits, out,
+                               workspace, workspace_bytes, stream);
 }

@@ -30,12 +30,15 @@ namespace {
 constexpr int QT = 64;  // vectors per tile
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct QArgs {
   const void* x;
   int64_t n_vec;
   int64_t x_stride;
   int x_bf16;
+  int x_vec;  // rows 16-byte aligned and d a multiple of the 16-byte vector width
+  int m_vec;  // rot and sketch_rot 16-byte aligned and d a multiple of 4
   const float* rot;
   const float* skr;
   const float* centroids;
@@ -61,16 +64,73 @@ struct QArgs {
   int64_t seg_stride;
   int64_t seg_offset;
   int64_t n_rows;
+  // Block-owned tiling (block records, segment rows, seg_stride % 32 == 0):
+  // tile = (segment, pair of 32-row blocks); the workgroup owning the tile is
+  // the only writer of those blocks, so partial blocks are read-modify-written.
+  int blk_owned;
+  int pk_zero;  // token-major: some record word is only partly covered by the waves' fields
+  int64_t pairs_per_seg;
+  int64_t n_tiles;
   uint32_t* codes;
   uint32_t* signs;
   float* norms;
 };
 
-__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+// Sum over each row of 16 lanes, result in every lane of the row, with DPP
+// lane moves (no LDS round trip): swap neighbours, swap pairs, then mirror
+// within 8 and within 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t row16_or(uint32_t s) {
+  s |= dpp_u<0xB1>(s);
+  s |= dpp_u<0x4E>(s);
+  s |= dpp_u<0x141>(s);
+  s |= dpp_u<0x140>(s);
+  return s;
+}
+__device__ __forceinline__ float row16_sum(float s) {
+  s += dpp_f<0xB1>(s);   // quad_perm [1, 0, 3, 2]
+  s += dpp_f<0x4E>(s);   // quad_perm [2, 3, 0, 1]
+  s += dpp_f<0x141>(s);  // row_half_mirror
+  s += dpp_f<0x140>(s);  // row_mirror
+  return s;
+}
 
 __device__ __forceinline__ int64_t dest_row(const QArgs& a, int64_t i) {
   if (a.dst_rows) return a.dst_rows[i];
   return (i / a.seg_len) * a.seg_stride + a.seg_offset + (i % a.seg_len);
+}
+
+// acc[mt] = A[16 mt .. 16 mt + 15][:] x B for the first NMT 16-vector tiles
+// (the rest are zeroed). A is the fp32 tile in LDS (row stride XS); B is this
+// wave's register fragment. Step (q, j) of lane group lg takes k = 16 q + 4 lg
+// + j, so a lane's four k of one q are adjacent in memory on both sides (one
+// 16-byte read each) and the four lane groups of a row cover 64 contiguous
+// bytes. The NMT accumulator chains are interleaved so consecutive MFMAs are
+// independent.
+template <int NMT, int KPG, int XS>
+__device__ __forceinline__ void mfma_tiles(const float* xr, const float (&b)[KPG], int ln, int lg,
+                                           f32x4 (&acc)[4]) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < KPG / 4; ++q) {
+    f32x4 a4[NMT];
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+      a4[mt] = *reinterpret_cast<const f32x4*>(xr + (mt * 16 + ln) * XS + 16 * q + 4 * lg);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[mt][j], b[4 * q + j], acc[mt], 0, 0, 0);
+  }
 }
 
 // LDS layout (bytes), KP = padded K, NT = number of 16-wide coordinate tiles.
@@ -87,7 +147,11 @@ struct Lds {
   static constexpr int off_cb = off_nrm + 2 * QT * 4;               // float [64]
   static constexpr int off_rows = off_cb + 64 * 4;                  // int64 [QT]
   static constexpr int off_flags = off_rows + QT * 8;               // int [4]
-  static constexpr int bytes = off_flags + 16;
+  // packed token-major records: codes (at most 4 bits x KP) then signs, plus
+  // slack for per-group rounding and for the last wave's bits past the end
+  static constexpr int PKW = KP * 4 / 32 + KP / 32 + 4;
+  static constexpr int off_pk = off_flags + 16;                     // u32 [QT][PKW]
+  static constexpr int bytes = off_pk + QT * PKW * 4;
 };
 
 template <int KP, int NT>
@@ -107,6 +171,9 @@ __global__ __launch_bounds__(NT * 64) void quantize_kernel(QArgs a) {
   float* cbk = reinterpret_cast<float*>(smem + L::off_cb);  // [0,32): centroids, [32,64): boundaries
   int64_t* rows = reinterpret_cast<int64_t*>(smem + L::off_rows);
   int* flags = reinterpret_cast<int*>(smem + L::off_flags);
+  uint32_t* pk = reinterpret_cast<uint32_t*>(smem + L::off_pk);
+  uint16_t* pk16 = reinterpret_cast<uint16_t*>(smem + L::off_pk);
+  constexpr int PKW = L::PKW;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -115,84 +182,201 @@ __global__ __launch_bounds__(NT * 64) void quantize_kernel(QArgs a) {
   const int lg = lane >> 4;
   const int d = a.d;
 
-  // codebooks of both groups into LDS (centroids at their concatenated offsets)
-  if (tid < 32) {
-    int ncent = (1 << a.gbits[0]) + (a.n_groups > 1 ? (1 << a.gbits[1]) : 0);
-    int nbnd = ((1 << a.gbits[0]) - 1) + (a.n_groups > 1 ? (1 << a.gbits[1]) - 1 : 0);
-    cbk[tid] = tid < ncent ? a.centroids[tid] : 0.f;
-    cbk[32 + tid] = tid < nbnd ? a.boundaries[tid] : 0.f;
+  // Every global load of the prologue and of the first tile is issued before
+  // the first wait, so the kernel pays one memory latency up front.
+  // Centroids of both groups (concatenated), kept in a register until the
+  // tile's LDS stores.
+  float cent_reg = 0.f;
+  {
+    const int ncent = (1 << a.gbits[0]) + (a.n_groups > 1 ? (1 << a.gbits[1]) : 0);
+    cent_reg = a.centroids[tid < ncent ? tid : ncent - 1];
   }
 
-  // This wave's rows of rot and sketch_rot: B[k][n] = M[16 w + n][k] with the
-  // lane group lg covering k in [lg*KPG, lg*KPG + KPG).
+  // This wave's rows of rot and sketch_rot: B[k][n] = M[16 w + n][k], with k
+  // assigned to steps as in mfma_tiles. The loads are unconditional (indices
+  // clamped into the matrix) so they issue back to back; out-of-range entries
+  // are zeroed afterwards.
   const int ocoord = w * 16 + ln;  // output coordinate of this lane
   float brot[KPG], bskr[KPG];
+  {
+    const int64_t rb = (int64_t)(ocoord < d ? ocoord : d - 1) * d;
+    if (a.m_vec) {
+      // d is a multiple of 4 and the matrices are 16-byte aligned
 #pragma unroll
-  for (int kk = 0; kk < KPG; ++kk) {
-    const int k = lg * KPG + kk;
-    const bool ok = ocoord < d && k < d;
-    brot[kk] = ok ? a.rot[(int64_t)ocoord * d + k] : 0.f;
-    bskr[kk] = ok ? a.skr[(int64_t)ocoord * d + k] : 0.f;
+      for (int q = 0; q < KPG / 4; ++q) {
+        const int k = 16 * q + 4 * lg;
+        const int kc = k < d ? k : d - 4;
+        const f32x4 r4 = *reinterpret_cast<const f32x4*>(a.rot + rb + kc);
+        const f32x4 s4 = *reinterpret_cast<const f32x4*>(a.skr + rb + kc);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          brot[4 * q + j] = r4[j];
+          bskr[4 * q + j] = s4[j];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KPG; ++kk) {
+        const int k = 16 * (kk / 4) + 4 * lg + kk % 4;
+        const int kc = k < d ? k : d - 1;
+        brot[kk] = a.rot[rb + kc];
+        bskr[kk] = a.skr[rb + kc];
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < KPG; ++kk) {
+      const bool ok = ocoord < d && 16 * (kk / 4) + 4 * lg + kk % 4 < d;
+      brot[kk] = ok ? brot[kk] : 0.f;
+      bskr[kk] = ok ? bskr[kk] : 0.f;
+    }
   }
-  // group of this wave's coordinates (group boundaries are multiples of 16)
-  const int grp = (a.n_groups > 1 && w * 16 >= a.choff[1]) ? 1 : 0;
+  // group of this wave's coordinates (group boundaries are multiples of 16);
+  // everything derived from it is wave-uniform
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int grp = (a.n_groups > 1 && wu * 16 >= a.choff[1]) ? 1 : 0;
   const int nb = (1 << a.gbits[grp]) - 1;
   const int coff = a.coff[grp];
   const int boff = a.boff[grp];
+  const int mg = a.gbits[grp];
+  const int wig = wu - a.choff[grp] / 16;  // wave index within its group
+  // halfword offsets, in a packed token-major row, of this wave's 16 codes
+  // (2 mg bytes) and of its 16 sign bits
+  const int pk_code_h = 2 * a.cwoff[grp] + mg * wig;
+  const int pk_sign_h = 2 * (a.code_words + a.swoff[grp]) + wig;
+  const bool tok = a.fmt == TQ_TOKEN_MAJOR;
+  // decision boundaries of both groups (concatenated), like the centroids
+  float bnd_reg = 0.f;
+  {
+    const int nbt = ((1 << a.gbits[0]) - 1) + (a.n_groups > 1 ? (1 << a.gbits[1]) - 1 : 0);
+    bnd_reg = a.boundaries[tid < nbt ? tid : nbt - 1];
+  }
 
-  const int64_t n_tiles = (a.n_vec + QT - 1) / QT;
-  for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
-    const int64_t v0 = tile * QT;
-    const int nvalid = (int)((a.n_vec - v0) < QT ? (a.n_vec - v0) : QT);
+  for (int64_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
+    // Tile = input vectors [v0, v0 + nvalid). With block-owned tiling the
+    // vectors are those of one segment falling in one aligned pair of
+    // blocks, whose first row is rowbase; slot_lo is the first vector's
+    // position in the pair.
+    int64_t v0, rowbase = 0;
+    int nvalid, slot_lo = 0;
+    if (a.blk_owned) {
+      const int64_t sg = tile / a.pairs_per_seg, pr = tile % a.pairs_per_seg;
+      const int o32 = (int)(a.seg_offset % 32);
+      const int64_t rem = a.n_vec - sg * a.seg_len;
+      const int64_t len = rem < a.seg_len ? rem : a.seg_len;
+      const int64_t lo = 64 * pr - o32 > 0 ? 64 * pr - o32 : 0;      // segment-relative
+      const int64_t hi = 64 * pr + 64 - o32 < len ? 64 * pr + 64 - o32 : len;
+      if (hi <= lo) continue;  // uniform across the workgroup
+      v0 = sg * a.seg_len + lo;
+      nvalid = (int)(hi - lo);
+      rowbase = sg * a.seg_stride + (a.seg_offset - o32) + 64 * pr;
+      slot_lo = (int)(lo + o32 - 64 * pr);
+    } else {
+      v0 = tile * QT;
+      nvalid = (int)((a.n_vec - v0) < QT ? (a.n_vec - v0) : QT);
+    }
 
     // ---- stage the input tile (fp32, zero padded) and destination rows ----
-    for (int e = tid; e < QT * KP; e += NT * 64) {
-      const int v = e / KP, k = e % KP;
-      float val = 0.f;
-      if (v < nvalid && k < d) {
-        const int64_t off = (v0 + v) * a.x_stride + k;
-        if (a.x_bf16) {
-          const uint16_t h = reinterpret_cast<const uint16_t*>(a.x)[off];
-          val = __uint_as_float(((uint32_t)h) << 16);
-        } else {
-          val = reinterpret_cast<const float*>(a.x)[off];
+    // All of a thread's loads are issued before any LDS store, so the tile
+    // costs one memory latency rather than one per element.
+    if (tok && a.pk_zero)
+      for (int e = tid; e < QT * PKW; e += NT * 64) pk[e] = 0u;
+    // (destination row of vector tid: loaded now, stored to LDS with the tile)
+    int64_t my_row = -1;
+    if (tid < nvalid) my_row = a.blk_owned ? rowbase + slot_lo + tid : dest_row(a, v0 + tid);
+    if (a.x_vec) {
+      // rows are 16-byte aligned and d is a multiple of the vector width:
+      // 16-byte loads, 8 bf16 or 4 fp32 values each
+      if (a.x_bf16) {
+        constexpr int CPR = KP / 8, NCH = QT * CPR / (NT * 64);  // chunks per row, per thread
+        u32x4 buf[NCH];
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          const int c = tid + i * NT * 64, v = c / CPR, k = (c % CPR) * 8;
+          buf[i] = (v < nvalid && k < d)
+                       ? *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.x) +
+                                                         (v0 + v) * a.x_stride + k)
+                       : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          const int c = tid + i * NT * 64, v = c / CPR, k = (c % CPR) * 8;
+          f32x4 lo, hi;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t w = buf[i][e];
+            const float f0 = __uint_as_float(w << 16), f1 = __uint_as_float(w & 0xFFFF0000u);
+            if (e < 2) {
+              lo[2 * e] = f0;
+              lo[2 * e + 1] = f1;
+            } else {
+              hi[2 * e - 4] = f0;
+              hi[2 * e - 3] = f1;
+            }
+          }
+          *reinterpret_cast<f32x4*>(xr + v * XS + k) = lo;
+          *reinterpret_cast<f32x4*>(xr + v * XS + k + 4) = hi;
+        }
+      } else {
+        constexpr int CPR = KP / 4, NCH = QT * CPR / (NT * 64);
+        f32x4 buf[NCH];
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          const int c = tid + i * NT * 64, v = c / CPR, k = (c % CPR) * 4;
+          buf[i] = (v < nvalid && k < d)
+                       ? *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(a.x) +
+                                                         (v0 + v) * a.x_stride + k)
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          const int c = tid + i * NT * 64, v = c / CPR, k = (c % CPR) * 4;
+          *reinterpret_cast<f32x4*>(xr + v * XS + k) = buf[i];
         }
       }
-      xr[v * XS + k] = val;
-    }
-    if (tid < QT) {
-      int64_t r = -1;
-      if (tid < nvalid) {
-        r = dest_row(a, v0 + tid);
-        if (r < 0 || r >= a.n_rows) r = -1;
+    } else {
+      constexpr int PER = QT * KP / (NT * 64);
+      float buf[PER];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int e = tid + i * NT * 64, v = e / KP, k = e % KP;
+        float val = 0.f;
+        if (v < nvalid && k < d) {
+          const int64_t off = (v0 + v) * a.x_stride + k;
+          val = a.x_bf16 ? __uint_as_float(((uint32_t) reinterpret_cast<const uint16_t*>(a.x)[off]) << 16)
+                         : reinterpret_cast<const float*>(a.x)[off];
+        }
+        buf[i] = val;
       }
-      rows[tid] = r;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int e = tid + i * NT * 64;
+        xr[(e / KP) * XS + e % KP] = buf[i];
+      }
+    }
+    if (tid < QT) rows[tid] = (my_row < 0 || my_row >= a.n_rows) ? -1 : my_row;
+    if (tid < 32) {
+      cbk[tid] = cent_reg;
+      cbk[32 + tid] = bnd_reg;
     }
     __syncthreads();
 
     // ---- y = rot x (fp32 MFMA), four 16-vector tiles ----
+    // (a tile with at most 16 vectors, e.g. an append, runs only its first
+    // 16-vector tile)
+    const int n_mt = (nvalid + 15) / 16;
     f32x4 yacc[4];
+    if (n_mt == 1)
+      mfma_tiles<1, KPG, XS>(xr, brot, ln, lg, yacc);
+    else
+      mfma_tiles<4, KPG, XS>(xr, brot, ln, lg, yacc);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const float* arow = xr + (mt * 16 + ln) * XS + lg * KPG;
-#pragma unroll
-      for (int q = 0; q < KPG / 4; ++q) {
-        const f32x4 a4 = *reinterpret_cast<const f32x4*>(arow + 4 * q);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[0], brot[4 * q + 0], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[1], brot[4 * q + 1], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[2], brot[4 * q + 2], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[3], brot[4 * q + 3], acc, 0, 0, 0);
-      }
-      yacc[mt] = acc;
+      if (mt >= n_mt) break;
       // lane (ln, lg) holds y[vector 16 mt + 4 lg + i][coordinate 16 w + ln]
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float s = acc[i] * acc[i];
-        s += shfl_xor_f(s, 1);
-        s += shfl_xor_f(s, 2);
-        s += shfl_xor_f(s, 4);
-        s += shfl_xor_f(s, 8);
+        float s = yacc[mt][i] * yacc[mt][i];
+        s = row16_sum(s);
         if (ln == 0) npart[w * QT + mt * 16 + lg * 4 + i] = s;
       }
     }
@@ -208,8 +392,15 @@ __global__ __launch_bounds__(NT * 64) void quantize_kernel(QArgs a) {
     __syncthreads();
 
     // ---- cells, residual in the rotated domain, residual norm partials ----
+    // (this group's boundaries, wave-uniform LDS reads; +inf past the last)
+    float tb[15];
+#pragma unroll
+    for (int k = 0; k < 15; ++k)
+      tb[k] = k < nb ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(cbk[32 + boff + k])))
+                     : INFINITY;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
+      if (mt >= n_mt) break;  // tiles past the last vector: their rows stay zero
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int v = mt * 16 + lg * 4 + i;
@@ -218,28 +409,35 @@ __global__ __launch_bounds__(NT * 64) void quantize_kernel(QArgs a) {
         int idx;
         float r;
         if (n > 0.f) {
-          const float u = y * (1.0f / n);
+          // cell = number of boundaries below u (the +inf entries past the
+          // group's count never are); fully unrolled so tb stays in SGPRs
+          const float u = y * __builtin_amdgcn_rcpf(n);
           idx = 0;
-          float cval = cbk[coff];
-          for (int k = 0; k < nb; ++k) {
-            if (u > cbk[32 + boff + k]) {
-              idx = k + 1;
-              cval = cbk[coff + k + 1];
-            }
-          }
-          r = fmaf(-n, cval, y);
+#pragma unroll
+          for (int k = 0; k < 15; ++k) idx += u > tb[k] ? 1 : 0;
+          r = fmaf(-n, cbk[coff + idx], y);
         } else {
           idx = (nb + 1) / 2 - 1;
           r = 0.f;
         }
-        if (ocoord >= d) r = 0.f;
+        if (ocoord >= d) {
+          r = 0.f;
+          idx = 0;
+        }
         code_b[v * DP + ocoord] = (uint8_t)idx;
+        if (tok) {
+          // the row's 16 codes of this wave, OR-combined across the row of
+          // lanes, are 2 mg bytes of the packed record
+          const uint64_t f = (uint64_t)(uint32_t)idx << (mg * ln);
+          const uint32_t lo = row16_or((uint32_t)f);
+          const uint32_t hi = mg > 2 ? row16_or((uint32_t)(f >> 32)) : 0u;
+          if (ln == 0)
+            for (int k = 0; k < mg; ++k)
+              pk16[v * 2 * PKW + pk_code_h + k] = (uint16_t)((k < 2 ? lo : hi) >> (16 * (k & 1)));
+        }
         xr[v * XS + ocoord] = r;  // A operand of the sketch product (k = rotated coordinate)
         float s = r * r;
-        s += shfl_xor_f(s, 1);
-        s += shfl_xor_f(s, 2);
-        s += shfl_xor_f(s, 4);
-        s += shfl_xor_f(s, 8);
+        s = row16_sum(s);
         if (ln == 0) gpart[w * QT + v] = s;
       }
     }
@@ -248,22 +446,23 @@ __global__ __launch_bounds__(NT * 64) void quantize_kernel(QArgs a) {
     __syncthreads();
 
     // ---- s = (S Pi^T) r (fp32 MFMA); sign bit = [s >= 0] ----
+    f32x4 sacc[4];
+    if (n_mt == 1)
+      mfma_tiles<1, KPG, XS>(xr, bskr, ln, lg, sacc);
+    else
+      mfma_tiles<4, KPG, XS>(xr, bskr, ln, lg, sacc);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const float* arow = xr + (mt * 16 + ln) * XS + lg * KPG;
-#pragma unroll
-      for (int q = 0; q < KPG / 4; ++q) {
-        const f32x4 a4 = *reinterpret_cast<const f32x4*>(arow + 4 * q);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[0], bskr[4 * q + 0], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[1], bskr[4 * q + 1], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[2], bskr[4 * q + 2], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[3], bskr[4 * q + 3], acc, 0, 0, 0);
-      }
+      if (mt >= n_mt) break;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int v = mt * 16 + lg * 4 + i;
-        sign_b[v * DP + ocoord] = acc[i] >= 0.f ? 1 : 0;
+        const bool bit = sacc[mt][i] >= 0.f && ocoord < d;
+        sign_b[v * DP + ocoord] = bit ? 1 : 0;
+        // the wave's 16 channels for vector 16 mt + 4 q + i are ballot bits [16 q, 16 q + 16)
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(bit);
+        if (tok && lane < 4)
+          pk16[(mt * 16 + lane * 4 + i) * 2 * PKW + pk_sign_h] = (uint16_t)(bal >> (16 * lane));
       }
     }
     // full aligned 32-row blocks of this tile (block records only)
@@ -292,45 +491,79 @@ __global__ __launch_bounds__(NT * 64) void quantize_kernel(QArgs a) {
         a.norms[row * (2 * a.n_groups) + 2 * g + 1] = sqrtf(s);
       }
     }
-    if (a.fmt == TQ_TOKEN_MAJOR) {
-      const int cw = a.code_words;
-      for (int e = tid; e < QT * cw; e += NT * 64) {
-        const int v = e / cw, wd = e % cw;
+    if (tok) {
+      // packed records: code words then sign words, copied word by word
+      const int cw = a.code_words, sw = a.sign_words, rw = cw + sw;
+      for (int e = tid; e < QT * rw; e += NT * 64) {
+        const int v = e / rw, wd = e % rw;
         const int64_t row = rows[v];
         if (row < 0) continue;
-        const int g = (a.n_groups > 1 && wd >= a.cwoff[1]) ? 1 : 0;
-        const int m = a.gbits[g], dg = a.gdim[g];
-        const int lw = wd - a.cwoff[g];
-        const int b0 = 32 * lw;
-        int j0 = b0 / m - 1;
-        if (j0 < 0) j0 = 0;
-        int j1 = (b0 + 31) / m;
-        if (j1 > dg - 1) j1 = dg - 1;
-        uint64_t acc = 0;
-        for (int j = j0; j <= j1; ++j) {
-          const int pos = m * j - b0;
-          const uint64_t c = code_b[v * DP + a.choff[g] + j];
-          if (pos >= 0)
-            acc |= c << pos;
-          else
-            acc |= c >> (-pos);
-        }
-        a.codes[row * cw + wd] = (uint32_t)acc;
+        if (wd < cw)
+          a.codes[row * cw + wd] = pk[v * PKW + wd];
+        else
+          a.signs[row * sw + wd - cw] = pk[v * PKW + wd];
       }
-      const int sw = a.sign_words;
-      for (int e = tid; e < QT * sw; e += NT * 64) {
-        const int v = e / sw, wd = e % sw;
-        const int64_t row = rows[v];
-        if (row < 0) continue;
-        const int g = (a.n_groups > 1 && wd >= a.swoff[1]) ? 1 : 0;
-        const int dg = a.gdim[g];
-        const int lw = wd - a.swoff[g];
-        uint32_t word = 0;
-        for (int b = 0; b < 32; ++b) {
-          const int j = 32 * lw + b;
-          if (j < dg) word |= (uint32_t)sign_b[v * DP + a.choff[g] + j] << b;
+    } else if (a.blk_owned) {
+      // block records, tile = one aligned pair of blocks owned by this
+      // workgroup: each word is assembled from the tile's fields; a word
+      // that also holds rows outside the tile is read, merged and written
+      // back (no other workgroup writes these blocks in this call)
+      for (int h = 0; h < 2; ++h) {
+        const int vlo = slot_lo > 32 * h ? slot_lo : 32 * h;
+        const int vhi = slot_lo + nvalid < 32 * h + 32 ? slot_lo + nvalid : 32 * h + 32;
+        if (vhi <= vlo) continue;
+        const int64_t blk = rowbase / 32 + h;
+        const int bcw = a.blk_code_words;
+        for (int wd = tid; wd < bcw; wd += NT * 64) {
+          const int g = (a.n_groups > 1 && wd >= a.bcwoff[1]) ? 1 : 0;
+          const int m = a.gbits[g], dg = a.gdim[g];
+          const int lw = wd - a.bcwoff[g];
+          const int b0 = 32 * lw;
+          const int u0 = b0 / (8 * m), u1 = (b0 + 31) / (8 * m);
+          const uint64_t fm = (1u << m) - 1u;
+          uint64_t word = 0, mask = 0;
+          for (int u = u0; u <= u1 && u < 4 * dg; ++u) {
+            const int o = u / dg, j = u % dg;
+            uint64_t unit = 0, umask = 0;
+            for (int sl = 0; sl < 8; ++sl) {
+              const int t = 32 * h + 8 * o + sl;
+              if (t < vlo || t >= vhi) continue;
+              unit |= (uint64_t)code_b[(t - slot_lo) * DP + a.choff[g] + j] << (m * sl);
+              umask |= fm << (m * sl);
+            }
+            const int pos = 8 * m * u - b0;
+            word |= pos >= 0 ? unit << pos : unit >> (-pos);
+            mask |= pos >= 0 ? umask << pos : umask >> (-pos);
+          }
+          uint32_t* dst = a.codes + blk * bcw + wd;
+          const uint32_t m32 = (uint32_t)mask;
+          if (m32 == 0xFFFFFFFFu)
+            *dst = (uint32_t)word;
+          else if (m32 != 0)
+            *dst = (*dst & ~m32) | ((uint32_t)word & m32);
         }
-        a.signs[row * sw + wd] = word;
+        const int bsw = a.blk_sign_words;
+        for (int wd = tid; wd < bsw; wd += NT * 64) {
+          const int g = (a.n_groups > 1 && wd >= a.bswoff[1]) ? 1 : 0;
+          const int dg = a.gdim[g];
+          const int lw = wd - a.bswoff[g];
+          uint32_t word = 0, mask = 0;
+          for (int q = 0; q < 4; ++q) {
+            const int u = 4 * lw + q;
+            const int o = u / dg, j = u % dg;
+            for (int sl = 0; sl < 8; ++sl) {
+              const int t = 32 * h + 8 * o + sl;
+              if (t < vlo || t >= vhi) continue;
+              word |= (uint32_t)sign_b[(t - slot_lo) * DP + a.choff[g] + j] << (8 * q + sl);
+              mask |= 1u << (8 * q + sl);
+            }
+          }
+          uint32_t* dst = a.signs + blk * bsw + wd;
+          if (mask == 0xFFFFFFFFu)
+            *dst = word;
+          else if (mask != 0)
+            *dst = (*dst & ~mask) | (word & mask);
+        }
       }
     } else {
       // block records: whole blocks are written word by word
@@ -416,7 +649,7 @@ tq_status launch_quantize(const QArgs& a, hipStream_t stream) {
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(&quantize_kernel<KP, NT>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, L::bytes) != hipSuccess)
     return TQ_ERR_DEVICE;
-  const int64_t n_tiles = (a.n_vec + QT - 1) / QT;
+  const int64_t n_tiles = a.n_tiles;
   int dev = 0, n_cu = 256;
   if (hipGetDevice(&dev) == hipSuccess) {
     int v = 0;
@@ -425,6 +658,7 @@ tq_status launch_quantize(const QArgs& a, hipStream_t stream) {
   }
   const int64_t per_cu = L::bytes <= 80 * 1024 ? 2 : 1;
   const int64_t grid = n_tiles < per_cu * n_cu ? n_tiles : per_cu * n_cu;
+  (void)hipGetLastError();  // a launch error is reported below, not an older one
   hipLaunchKernelGGL((quantize_kernel<KP, NT>), dim3((unsigned)grid), dim3(NT * 64), L::bytes, stream,
                      a);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_DEVICE;
@@ -467,8 +701,14 @@ extern "C" tq_status tq_quantize(const tq_quantizer* qz, tq_format fmt, const vo
   a.n_vec = n_vec;
   a.x_stride = x_row_stride;
   a.x_bf16 = x_dtype == TQ_BF16;
+  {
+    const int64_t esz = a.x_bf16 ? 2 : 4, per = 16 / esz;
+    a.x_vec = reinterpret_cast<uintptr_t>(x) % 16 == 0 && (x_row_stride * esz) % 16 == 0 && l.d % per == 0;
+  }
   a.rot = qz->rot;
   a.skr = qz->sketch_rot;
+  a.m_vec = l.d % 4 == 0 && reinterpret_cast<uintptr_t>(qz->rot) % 16 == 0 &&
+            reinterpret_cast<uintptr_t>(qz->sketch_rot) % 16 == 0;
   a.centroids = qz->centroids;
   a.boundaries = qz->boundaries;
   a.d = l.d;
@@ -495,6 +735,21 @@ extern "C" tq_status tq_quantize(const tq_quantizer* qz, tq_format fmt, const vo
   a.seg_stride = rows->seg_stride;
   a.seg_offset = rows->seg_offset;
   a.n_rows = cache->n_rows;
+  a.pk_zero = 0;
+  for (int g = 0; g < l.n_groups; ++g) {
+    const int waves = (geo.dim[g] + 15) / 16;
+    if ((waves * geo.bits[g]) % 2 != 0 || waves % 2 != 0) a.pk_zero = 1;
+  }
+  a.blk_owned = fmt == TQ_BLOCK32 && !rows->dst_rows &&
+                (n_vec <= rows->seg_len || rows->seg_stride % 32 == 0);
+  if (a.blk_owned) {
+    const int64_t n_seg = (n_vec + a.seg_len - 1) / a.seg_len;
+    a.pairs_per_seg = (a.seg_offset % 32 + a.seg_len + 63) / 64;
+    a.n_tiles = n_seg * a.pairs_per_seg;
+  } else {
+    a.pairs_per_seg = 1;
+    a.n_tiles = (n_vec + QT - 1) / QT;
+  }
   a.codes = cache->codes;
   a.signs = cache->signs;
   a.norms = cache->norms;

@@ -30,7 +30,7 @@ def tq():
 def test_header_symbols_exported(tq):
     text = open(HEADER).read()
     declared = sorted(set(re.findall(r"^\s*(?:tq_status|int|const char\*)\s+(tq_\w+)\s*\(", text, re.M)))
-    assert len(declared) == 8
+    assert len(declared) == 9
     lib = C.CDLL(tq.LIB_PATH)
     for name in declared:
         assert hasattr(lib, name), name
@@ -180,3 +180,16 @@ def test_decode_validation(tq):
     need = C.c_size_t()
     assert lib.tq_attn_decode_workspace_bytes(C.byref(kq), C.byref(vq), C.byref(good), C.byref(need)) == 0
     assert call(good, wsb=need.value - 1) == tq.TQ_ERR_WORKSPACE
+
+
+def test_phase_mask_validation(tq):
+    lib = tq.lib()
+    kq, vq = _fake_quantizer(tq), _fake_quantizer(tq)
+    kc, vc = _fake_cache(tq, 8 * 1024), _fake_cache(tq, 8 * 1024)
+    shape = tq.decode_shape(1, 32, 8, 1000, 1024, 0.088)
+    for mask in (0, 8, 15):
+        assert lib.tq_attn_decode_phases(mask, C.byref(kq), C.byref(vq), C.byref(shape), FAKE, 1,
+                                         C.byref(kc), C.byref(vc), None, FAKE, FAKE, 10, None) == tq.TQ_ERR_INVALID
+    # a valid mask reaches the workspace check
+    assert lib.tq_attn_decode_phases(2, C.byref(kq), C.byref(vq), C.byref(shape), FAKE, 1, C.byref(kc),
+                                     C.byref(vc), None, FAKE, FAKE, 10, None) == tq.TQ_ERR_WORKSPACE

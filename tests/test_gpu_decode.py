@@ -134,8 +134,10 @@ def test_split_count_does_not_change_result(tq):
     _, ro = _reference(wl, o, q)
     for out in outs:
         assert gc.normwise_close(out, ro)[0]
+    # splits change only where the fp16 softmax weights are rounded (relative
+    # to each split's running maximum): a few fp16 ulps per head
     for out in outs[1:]:
-        assert np.max(np.abs(out - outs[0])) <= 1e-4 * np.max(np.abs(outs[0]))
+        assert gc.normwise_close(out, outs[0], tol=5e-4)[0]
 
 
 def test_gqa_equals_repeated_heads(tq):

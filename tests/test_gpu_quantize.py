@@ -127,6 +127,35 @@ def test_append_rows_by_segments(tq):
         _check(tq, spec, x, fmt, 8 * cap, rows, dtype="bf16", seg=(1, cap, 777), pass_rows=False)
 
 
+@pytest.mark.parametrize("seg_len,offset,n_vec", [(150, 45, 677), (32, 0, 96), (7, 30, 40), (300, 1, 300)])
+def test_segments_partial_blocks_keep_other_rows(tq, seg_len, offset, n_vec):
+    # segments of seg_len rows at offset within 256-row slices (the last one
+    # ragged), over a cache pre-filled with ones: block records are merged
+    # word by word, rows outside the segments keep every bit
+    import torch
+    wl = synth.workload("llama8b_decode")
+    spec = synth.draw_quantizer(wl, "V")
+    cap = 512
+    n_seg = (n_vec + seg_len - 1) // seg_len
+    x = synth.draw_kv_slab(wl, "V", 0, 2, 0, n_vec)
+    i = np.arange(n_vec)
+    rows = (i // seg_len) * cap + offset + i % seg_len
+    oq, dq = gc.quantizers(spec)
+    qv = oracle.quantize(x.astype(np.float64), oq)
+    for fmt in (tq.TQ_BLOCK32, tq.TQ_TOKEN_MAJOR):
+        cache = tq.Cache.empty(dq, n_seg * cap, fmt)
+        cache.codes.fill_(-1)
+        cache.signs.fill_(-1)
+        xt = torch.from_numpy(x).cuda().to(torch.bfloat16)
+        tq.tq_quantize(dq, fmt, xt, cache, seg_len=seg_len, seg_stride=cap, seg_offset=offset)
+        torch.cuda.synchronize()
+        got_all = gc.read_cache(cache, dq)
+        gc.compare_records(x.astype(np.float64), oq, qv, gc.select_rows(got_all, rows))
+        untouched = np.setdiff1d(np.arange(n_seg * cap), rows)
+        L = 2 ** dq.mse_bits[0] - 1
+        assert np.all(got_all[0][0][untouched] == L) and np.all(got_all[1][0][untouched])
+
+
 def test_empty_call_is_noop(tq):
     import torch
     wl = synth.workload("tiny")
