@@ -247,8 +247,11 @@ tq_status tq_attn_decode_workspace_bytes(const tq_quantizer* kq, const tq_quanti
  * The estimate is evaluated in factored form: scale * sum_g (n_g <rot q,
  * c[idx]>_g + alpha_g gamma_g <sketch q, z>_g); V is accumulated in the
  * rotated and sketch domains and mapped back once per head with rot^T and
- * sketch^T. Operand precision: fp16 products, fp32 accumulation; stored
- * norms must be below 65504.
+ * sketch^T. Operand precision: fp16 products, fp32 accumulation (queries
+ * as an fp16 hi/lo pair; K centroids tabulated as fp16(s c) with a scale
+ * s in [1, 2) chosen per codebook so that the rounding is far below fp16's
+ * own, and 1/s applied with the norm); stored norms must be below 65504,
+ * and scale * |rot q| below about 4.5e4.
  *   q        device [batch, n_q_heads, d], f32 or bf16.
  *   k_cache  K records, TQ_TOKEN_MAJOR. v_cache: V records, TQ_BLOCK32
  *            (ignored when vq is NULL).
@@ -267,7 +270,8 @@ tq_status tq_attn_decode(const tq_quantizer* kq, const tq_quantizer* vq,
 
 /* The three stages of tq_attn_decode, for callers that schedule or time them
  * separately (e.g. to bracket the split-K kernel with events):
- *   TQ_PHASE_PREP    q_rot = rot q, q_sk = sketch q into the workspace,
+ *   TQ_PHASE_PREP    q_rot = rot q, q_sk = sketch q and the K codebook
+ *                    scales into the workspace,
  *   TQ_PHASE_SPLIT   the split-K pass over the cache (logits; partial softmax
  *                    sums and accumulators into the workspace),
  *   TQ_PHASE_COMBINE merge of the splits and back-transform into `out`.

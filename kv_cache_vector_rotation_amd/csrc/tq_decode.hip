@@ -9,7 +9,8 @@
 //
 // Three kernels on the caller's stream:
 //  1. prep:    q_rot = rot q and q_sk = sketch q per query head (fp32 sums;
-//              q_rot stored as an fp16 hi/lo pair, q_sk as fp16).
+//              q_rot stored as an fp16 hi/lo pair, q_sk as fp16), both
+//              scaled by scale * log2(e) and q_sk also by alpha_g.
 //  2. split:   split-K over the context. A workgroup takes one (batch, KV
 //              head, 16-query-head block) and a range of 32-token tiles; its
 //              four waves take alternate tiles. Per tile a wave
@@ -53,11 +54,13 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2a4 __attribute__((ext_vector_type(2))) __attribute__((aligned(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 // Low parts of the split fp16 operands are stored times 2^11 so they stay in
 // the normal fp16 range; their products are scaled back by 2^-11.
 constexpr float kLoScale = 2048.0f;
@@ -71,6 +74,7 @@ struct DArgs {
   int64_t n_ctx, cap;
   float scale;
   const _Float16* qprep;  // [batch*hq][3d]: q_rot hi, q_rot lo * 2^11, q_sk
+  const float* kscale;    // per K group: the fp16 table holds c * kscale
   const uint32_t* kc;
   const uint32_t* ks;
   const float* kn;
@@ -83,9 +87,10 @@ struct DArgs {
   float* part;    // [batch*hq][n_split][2 + 2d]
 };
 
+// two floats -> packed fp16 pair (round to nearest even; one v_cvt_pk_f16_f32)
 __device__ __forceinline__ uint32_t h2bits(float lo, float hi) {
-  const _Float16 a = (_Float16)lo, b = (_Float16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  const f16x2 v = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
@@ -93,7 +98,20 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float xor_max(float v, int m) { return fmaxf(v, __shfl_xor(v, m, 64)); }
+// max over the four 16-lane rows (lanes l, l ^ 16, l ^ 32, l ^ 48): swap the
+// 32-lane halves, then odd and even rows, with v_permlane{32,16}_swap
+__device__ __forceinline__ float rows4_max(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows4_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 // ---------------------------------------------------------------------------
 // Lookup tables in LDS. A table of E entries of W bytes keeps each entry
@@ -116,16 +134,31 @@ __device__ __forceinline__ uint32_t tab_addr(uint32_t e, uint32_t lane_off) {
     return e * W;
 }
 
+// Fills a table from value(e) (a uint32_t for W = 4, a u32x2 for W = 8). A
+// replicated entry's 256-byte row is written as 16 16-byte stores, each by
+// its own thread, with the value computed once per store.
 template <int E, int W, typename F>
-__device__ void tab_build(unsigned char* base, int tid, F entry) {
+__device__ void tab_build(unsigned char* base, int tid, F value) {
   if constexpr (Tab<E, W>::REP) {
-    constexpr int R = 256 / W;
-    for (int i = tid; i < E * R; i += 256) {
-      const int e = i / R, r = i % R;
-      entry(e, base + e * 256 + W * r);
+    for (int i = tid; i < E * 16; i += 256) {
+      const int e = i >> 4, k = i & 15;
+      u32x4 v;
+      if constexpr (W == 4) {
+        const uint32_t x = value(e);
+        v = u32x4{x, x, x, x};
+      } else {
+        const u32x2 x = value(e);
+        v = u32x4{x[0], x[1], x[0], x[1]};
+      }
+      *reinterpret_cast<u32x4*>(base + e * 256 + 16 * k) = v;
     }
   } else {
-    for (int e = tid; e < E; e += 256) entry(e, base + e * W);
+    for (int e = tid; e < E; e += 256) {
+      if constexpr (W == 4)
+        *reinterpret_cast<uint32_t*>(base + e * W) = value(e);
+      else
+        *reinterpret_cast<u32x2*>(base + e * W) = value(e);
+    }
   }
 }
 
@@ -134,21 +167,6 @@ __device__ __forceinline__ u32x4 signs8(uint32_t byte, const unsigned char* stab
   const u32x2 lo = *reinterpret_cast<const u32x2*>(stab + tab_addr<16, 8>(byte & 15u, off8));
   const u32x2 hi = *reinterpret_cast<const u32x2*>(stab + tab_addr<16, 8>((byte >> 4) & 15u, off8));
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
-}
-
-// 8 K codes of M bits -> fp16 centroids (hi) and their rounding remainders
-// x 2^11 (lo): one address per pair, two 4-byte reads (lo table at +LO).
-template <int M, int LO>
-__device__ __forceinline__ void kcodes8(uint32_t field, const unsigned char* tab, uint32_t off4,
-                                        u32x4& hi, u32x4& lo) {
-  constexpr int E = 1 << (2 * M);
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint32_t e = (field >> (2 * M * p)) & (E - 1u);
-    const unsigned char* ad = tab + tab_addr<E, 4>(e, off4);
-    hi[p] = *reinterpret_cast<const uint32_t*>(ad);
-    lo[p] = *reinterpret_cast<const uint32_t*>(ad + LO);
-  }
 }
 
 // 8 codes of M bits (code s at bits [M s, M s + M) of field) -> 8 fp16
@@ -340,12 +358,9 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
   constexpr int NC = G::NC, CPG = G::CPG, NMT = G::NMT, MTPG = G::MTPG, RUN = G::RUN, DG = G::DG;
   constexpr int KT1 = G::KTB[0], VT0 = KT1 + G::KTB[1], VT1 = VT0 + G::VTB[0];
   constexpr int ST = VT1 + G::VTB[1];
-  // K lo tables (fp16 rounding remainders x 2^11) after the sign table, skewed
-  // by 128 bytes so that a hi/lo pair of reads is never fused into one
-  // two-register read (whose registers would then need moving into place)
-  constexpr int KLO0 = ST + G::STB + 128, KLO1 = KLO0 + G::KTB[0];
-  constexpr int TAB_BYTES = KLO1 + G::KTB[1];
-  constexpr int ACC_BYTES = WV ? 2 * (2 * 4 * NMT * 64) * 4 : 0;  // two merge regions
+  constexpr int TAB_BYTES = ST + G::STB;
+  // two merge regions of 16 heads x (2 (D + 16 D / 64) + 1) floats
+  constexpr int ACC_BYTES = WV ? 2 * 16 * (2 * (D + 16 * (D / 64)) + 1) * 4 : 0;
   constexpr int SMEM = TAB_BYTES > ACC_BYTES ? TAB_BYTES : ACC_BYTES;
   __shared__ __align__(16) unsigned char s_tab[SMEM];  // tables; after the loop: merge buffer
   __shared__ __align__(16) float s_nrm[kWaves][2][64 * NG];  // per-wave norm staging (K, V)
@@ -373,14 +388,24 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
   const int64_t t_end = t_begin + tps < n_tiles ? t_begin + tps : n_tiles;
   const int64_t rowbase = (int64_t)bh * a.cap;
   const LaneOff<D, NG, M0, M1> lo = lane_offsets<D, NG, M0, M1>(ln, lg);
+  // lane l stages floats l NG + e of a tile's K norms [32][n_0, gamma_0, ..]:
+  // an n_g is divided by the group's codebook scale s_g
+  float kn_mul[NG];
+#pragma unroll
+  for (int e = 0; e < NG; ++e) {
+    const int f = (lane * NG + e) % (2 * NG);
+    kn_mul[e] = (f & 1) ? 1.0f : 1.0f / a.kscale[f >> 1];
+  }
 
   // ---- tables (built from an LDS copy of the centroids) ----
   __shared__ float s_cent[2][32];
   float cent_k = 0.f, cent_v = 0.f;
   if (tid < 32) {
+    // K centroids are tabulated as fp16(s_g c): scaled here by the group's s_g
     const int nc = (1 << M0) + (NG > 1 ? (1 << M1) : 0);
-    cent_k = a.kcent[tid < nc ? tid : nc - 1];
-    if constexpr (WV) cent_v = a.vcent[tid < nc ? tid : nc - 1];
+    const int tc = tid < nc ? tid : nc - 1;
+    cent_k = a.kcent[tc] * a.kscale[NG > 1 && tc >= (1 << M0) ? 1 : 0];
+    if constexpr (WV) cent_v = a.vcent[tc];
   }
   Raw<D, NG, M0, M1> ra, rb, rc;
   int64_t tile = t_begin + wv;
@@ -393,36 +418,23 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
   }
   __syncthreads();
   {
-    auto kentry = [&](const float* cent, int m, int lo_off) {
-      return [=](int e, unsigned char* dst) {
-        const int L = 1 << m;
-        const float c0 = cent[e & (L - 1)], c1 = cent[e >> m];
-        const _Float16 h0 = (_Float16)c0, h1 = (_Float16)c1;
-        *reinterpret_cast<uint32_t*>(dst) = h2bits(c0, c1);
-        *reinterpret_cast<uint32_t*>(dst + lo_off) =
-            h2bits((c0 - (float)h0) * kLoScale, (c1 - (float)h1) * kLoScale);
-      };
+    // pair entry e = (code e mod L, code e div L): two fp16 centroids
+    auto hi_val = [](const float* cent, int m) {
+      return [=](int e) { return h2bits(cent[e & ((1 << m) - 1)], cent[e >> m]); };
     };
-    auto entry = [&](const float* cent, int m) {
-      return [=](int e, unsigned char* dst) {
-        const int L = 1 << m;
-        *reinterpret_cast<uint32_t*>(dst) = h2bits(cent[e & (L - 1)], cent[e >> m]);
-      };
-    };
-    tab_build<G::KE[0], 4>(s_tab, tid, kentry(s_cent[0], M0, KLO0));
-    if constexpr (NG > 1)
-      tab_build<G::KE[1], 4>(s_tab + KT1, tid, kentry(s_cent[0] + (1 << M0), M1, KLO1 - KT1));
+    tab_build<G::KE[0], 4>(s_tab, tid, hi_val(s_cent[0], M0));
+    if constexpr (NG > 1) tab_build<G::KE[1], 4>(s_tab + KT1, tid, hi_val(s_cent[0] + (1 << M0), M1));
     if constexpr (WV) {
-      tab_build<G::KE[0], 4>(s_tab + VT0, tid, entry(s_cent[1], M0));
-      if constexpr (NG > 1) tab_build<G::KE[1], 4>(s_tab + VT1, tid, entry(s_cent[1] + (1 << M0), M1));
+      tab_build<G::KE[0], 4>(s_tab + VT0, tid, hi_val(s_cent[1], M0));
+      if constexpr (NG > 1) tab_build<G::KE[1], 4>(s_tab + VT1, tid, hi_val(s_cent[1] + (1 << M0), M1));
     }
     // nibble -> four fp16 values, +1 where the bit is set, -1 where clear
-    tab_build<16, 8>(s_tab + ST, tid, [](int e, unsigned char* dst) {
+    tab_build<16, 8>(s_tab + ST, tid, [](int e) {
       uint32_t w[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h)
         w[h] = (((e >> (2 * h)) & 1) ? 0x3C00u : 0xBC00u) | (((e >> (2 * h + 1)) & 1) ? 0x3C000000u : 0xBC000000u);
-      *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
+      return u32x2{w[0], w[1]};
     });
   }
 
@@ -446,7 +458,6 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
   }
   __syncthreads();
 
-  constexpr float kAlpha = 1.2533141373155003f / (float)DG;  // sqrt(pi/2) / d_g
   const unsigned char* stab = s_tab + ST;
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -467,7 +478,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
       const bool nok = full || T0 + (lane * NG) / (2 * NG) < N;
 #pragma unroll
       for (int e = 0; e < NG; ++e) {
-        s_nrm[wv][0][lane * NG + e] = nok ? r.kn[e] : 0.f;
+        s_nrm[wv][0][lane * NG + e] = nok ? r.kn[e] * kn_mul[e] : 0.f;
         if constexpr (WV) s_nrm[wv][1][lane * NG + e] = nok ? r.vn[e] : 0.f;
       }
     }
@@ -496,13 +507,11 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
 #pragma unroll
       for (int cl = 0; cl < CPG; ++cl) {
         const int c = g * CPG + cl;
-        constexpr int LO = g == 0 ? KLO0 : KLO1 - KT1;
-        u32x4 ak, akl;
-        kcodes8<M, LO>(field_at(w, 8 * M * cl, 8 * M), kt, off4, ak, akl);
+        const u32x4 ak = codes8<M>(field_at(w, 8 * M * cl, 8 * M), kt, off4);
         const u32x4 az = signs8((sword >> (8 * cl)) & 0xFFu, stab, off8);
-        // c q = c_hi q_hi + 2^-11 (c_lo' q_hi + c_hi q_lo'); products exact, fp32 sums
+        // (s c) q = (s c)16 (q_hi + 2^-11 q_lo'): products exact, fp32 sums;
+        // 1 / s is applied with the token's norm
         lr[tau][g] = mfma16(ak, qr[c], lr[tau][g]);
-        lrl[tau][g] = mfma16(akl, qr[c], lrl[tau][g]);
         lrl[tau][g] = mfma16(ak, qrl[c], lrl[tau][g]);
         ls[tau][g] = mfma16(az, qs[c], ls[tau][g]);
       }
@@ -520,15 +529,15 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int tau = j >> 2, i = j & 3;
+      // (the prepared queries carry scale * log2(e), and alpha_g on the
+      // sketch part, so this is the logit in the log2 domain)
       float s = 0.f;
 #pragma unroll
       for (int g = 0; g < NG; ++g)
-        s += kn[j][2 * g] * fmaf(kLoInv, lrl[tau][g][i], lr[tau][g][i]) +
-             kAlpha * kn[j][2 * g + 1] * ls[tau][g][i];
-      const float lg_val = a.scale * s;
+        s += kn[j][2 * g] * fmaf(kLoInv, lrl[tau][g][i], lr[tau][g][i]) + kn[j][2 * g + 1] * ls[tau][g][i];
       if (a.logits && hvalid && (full || tok0 + j < N))
-        a.logits[((int64_t)b * a.hq + hq) * N + tok0 + j] = lg_val;
-      l2[j] = lg_val * kLog2e;
+        a.logits[((int64_t)b * a.hq + hq) * N + tok0 + j] = s * kLn2;
+      l2[j] = s;
     }
     if (!full) {
 #pragma unroll
@@ -539,9 +548,12 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
       float mx = l2[0];
 #pragma unroll
       for (int j = 1; j < 8; ++j) mx = fmaxf(mx, l2[j]);
-      mx = xor_max(mx, 16);
-      mx = xor_max(mx, 32);
-      const float m_new = fmaxf(m_run, mx);
+      mx = rows4_max(mx);
+      // The reference is kept at an integer (log2 domain): every weight and
+      // every rescale is then an exact power of two times the same mantissa,
+      // so the fp16 weights, and hence the result, do not depend on how the
+      // context is split.
+      const float m_new = fmaxf(m_run, ceilf(mx));
       if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
         // some head's maximum moved: rescale (factor 1 for the others)
         const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -627,30 +639,36 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
 
   if constexpr (WV) {
     // ---- merge the four waves into one partial (the table space is reused) ----
-    // Region r (r = 0, 1) holds, for every accumulator register (part, i, v)
-    // and lane (lg, ln), the sum of the values of waves r and r + 2 scaled to
-    // the workgroup maximum; the index is register-major so that every store
-    // writes 64 consecutive floats. Waves 0 and 1 store, then waves 2 and 3 add.
+    // Region r (r = 0, 1) holds, head-major, the sum of the accumulators of
+    // waves r and r + 2 scaled to the workgroup maximum: waves 0 and 1 store,
+    // then waves 2 and 3 add. Head h, part pt, channel ch sits at
+    // h HS + pt DP + ch + 16 (ch / 64): the odd head stride and the skew of
+    // every 64 channels keep both the register-order stores and the
+    // channel-order reads free of bank conflicts.
+    constexpr int DP = D + 16 * (D / 64), HS = 2 * DP + 1, REG = 16 * HS;
     float* s_red = reinterpret_cast<float*>(s_tab);
-    constexpr int REG = 2 * 4 * NMT * 64;  // floats per region
     __syncthreads();  // tables are no longer read
-    l_run += __shfl_xor(l_run, 16, 64);
-    l_run += __shfl_xor(l_run, 32, 64);
+    l_run = rows4_sum(l_run);
     if (lg == 0) s_m[wv][ln] = m_run;
     __syncthreads();
     float M = s_m[0][ln];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][ln]);
-    const float e = (m_run == -INFINITY) ? 0.f : exp2f(m_run - M);
+    const float e = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
     if (lg == 0) s_lw[wv][ln] = l_run * e;
-    float* reg = s_red + (wv & 1) * REG + lane;
+    float* reg = s_red + (wv & 1) * REG + ln * HS;
+    auto slot = [&](int pt, int v, int i) {
+      const int g = v / MTPG, u = v % MTPG;
+      const int ch = g * DG + RUN * (4 * lg + i) + u;
+      return pt * DP + ch + 16 * (ch >> 6);
+    };
     if (wv < 2) {
 #pragma unroll
       for (int v = 0; v < NMT; ++v)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          reg[((0 * 4 + i) * NMT + v) * 64] = acc_r[v][i] * e;
-          reg[((1 * 4 + i) * NMT + v) * 64] = acc_s[v][i] * e;
+          reg[slot(0, v, i)] = acc_r[v][i] * e;
+          reg[slot(1, v, i)] = acc_s[v][i] * e;
         }
     }
     __syncthreads();
@@ -659,8 +677,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
       for (int v = 0; v < NMT; ++v)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          reg[((0 * 4 + i) * NMT + v) * 64] += acc_r[v][i] * e;
-          reg[((1 * 4 + i) * NMT + v) * 64] += acc_s[v][i] * e;
+          reg[slot(0, v, i)] += acc_r[v][i] * e;
+          reg[slot(1, v, i)] += acc_s[v][i] * e;
         }
     }
     __syncthreads();
@@ -675,11 +693,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
         for (int w = 1; w < kWaves; ++w) Mh = fmaxf(Mh, s_m[w][h]);
         val = k == 0 ? Mh : s_lw[0][h] + s_lw[1][h] + s_lw[2][h] + s_lw[3][h];
       } else {
-        // channel ch of part pt <-> register (pt, i, v), lane (lg, ln = h):
-        // ch = g DG + RUN (4 lg + i) + u, v = g MTPG + u
         const int pt = (k - 2) / D, ch = (k - 2) % D;
-        const int g = ch / DG, local = ch % DG, u = local % RUN, row = local / RUN;
-        const int idx = (((pt * 4 + (row & 3)) * NMT + g * MTPG + u) * 4 + (row >> 2)) * 16 + h;
+        const int idx = h * HS + pt * DP + ch + 16 * (ch >> 6);
         val = s_red[idx] + s_red[REG + idx];
       }
       const int hq2 = kvh * a.group + hblk * 16 + h;
@@ -689,8 +704,10 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Query preparation: q_rot = rot q (stored as fp16 hi and (q - hi) * 2^11)
-// and q_sk = sketch q (fp16), fp32 sums in ascending k. A workgroup takes 16
+// Query preparation: q_rot = f rot q (stored as fp16 hi and (q - hi) * 2^11)
+// and q_sk = f alpha_g sketch q (fp16), with f = scale * log2(e) so that the
+// split pass forms log2-domain logits directly; fp32 sums in ascending k,
+// scaled after the sum. A workgroup takes 16
 // rows of the stacked [rot; sketch] matrix and kPrepHeads heads; both are
 // staged in LDS by coalesced 16-byte loads, then thread (i, hq) forms the
 // dot products of row i with heads hq, hq + 16, ...
@@ -698,10 +715,60 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
 constexpr int kPrepHeads = 64;
 constexpr int kPrepRows = 16;
 
+// Scale s in [1, 2) for which the fp16 roundings of s |c_k| are closest to
+// exact (smallest largest relative error over the centroids; 2048
+// candidates s = 1 + i / 2048, ties to the smaller i). The decode tables
+// hold fp16(s c) and the logits divide by s, so the centroids enter the
+// products with a few 1e-5 relative error instead of fp16's ~2.4e-4.
+__device__ void search_fp16_scale(const float* cent, int L, float* out, int tid) {
+  __shared__ float s_err[256];
+  __shared__ int s_idx[256];
+  float best = INFINITY;
+  int bi = 0;
+  for (int i = tid; i < 2048; i += 256) {
+    const float sc = 1.0f + (float)i * (1.0f / 2048.0f);
+    float worst = 0.f;
+    for (int k = 0; k < L; ++k) {
+      const float x = fabsf(cent[k]) * sc;
+      const float r = fabsf((float)(_Float16)x - x) / x;
+      worst = fmaxf(worst, r);
+    }
+    if (worst < best) {
+      best = worst;
+      bi = i;
+    }
+  }
+  s_err[tid] = best;
+  s_idx[tid] = bi;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) {
+      const float e2 = s_err[tid + w];
+      const int i2 = s_idx[tid + w];
+      if (e2 < s_err[tid] || (e2 == s_err[tid] && i2 < s_idx[tid])) {
+        s_err[tid] = e2;
+        s_idx[tid] = i2;
+      }
+    }
+    __syncthreads();
+  }
+  if (tid == 0) *out = 1.0f + (float)s_idx[0] * (1.0f / 2048.0f);
+  __syncthreads();
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void prep_kernel(const void* q, int q_bf16, int n_heads,
                                                    const float* rot, const float* sketch,
-                                                   _Float16* qprep) {
+                                                   float scale_l2, int group_dim0,
+                                                   _Float16* qprep, const float* kcent, int n_groups,
+                                                   int m0, int m1, float* kscale) {
+  if (blockIdx.x == 2 * D / kPrepRows) {
+    if (blockIdx.y == 0) {
+      search_fp16_scale(kcent, 1 << m0, kscale, threadIdx.x);
+      if (n_groups > 1) search_fp16_scale(kcent + (1 << m0), 1 << m1, kscale + 1, threadIdx.x);
+    }
+    return;
+  }
   constexpr int QS = D + 4;  // LDS row stride (floats)
   constexpr int HPT = kPrepHeads / 16;  // heads per thread
   __shared__ __align__(16) float sm[kPrepRows][QS];
@@ -776,11 +843,19 @@ __global__ __launch_bounds__(256) void prep_kernel(const void* q, int q_bf16, in
     }
   }
   const int row = r0 + i;
+  // logits in the log2 domain: both parts carry scale * log2(e); the sketch
+  // part also alpha_g = sqrt(pi / 2) / d_g of the row's group
+  float f = scale_l2;
+  if (row >= D) {
+    const int dg = row - D < group_dim0 ? group_dim0 : D - group_dim0;
+    f *= 1.2533141373155003f / (float)dg;
+  }
 #pragma unroll
   for (int r = 0; r < HPT; ++r) {
     const int h = h0 + hq + 16 * r;
     if (h >= n_heads) continue;
     _Float16* dst = qprep + (int64_t)h * 3 * D;
+    acc[r] *= f;
     const _Float16 hi = (_Float16)acc[r];
     if (row < D) {
       dst[row] = hi;
@@ -903,9 +978,10 @@ bool decode_supported(const tq_layout& l) {
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// workspace: [prepared queries][K codebook scales, 2 floats][split partials]
 size_t workspace_for(const tq_decode_shape* s, int d, bool with_v, int n_split) {
   const size_t heads = (size_t)s->batch * s->n_q_heads;
-  size_t bytes = align256(heads * 3 * d * sizeof(_Float16));
+  size_t bytes = align256(heads * 3 * d * sizeof(_Float16)) + 256;
   if (with_v) bytes += align256(heads * (size_t)n_split * (2 + 2 * d) * sizeof(float));
   return bytes;
 }
@@ -997,14 +1073,18 @@ extern "C" tq_status tq_attn_decode_phases(unsigned phases, const tq_quantizer* 
   constexpr int D = 128;
   const int n_heads = shape->batch * shape->n_q_heads;
   _Float16* qprep = reinterpret_cast<_Float16*>(workspace);
-  float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
-                                         align256((size_t)n_heads * 3 * D * sizeof(_Float16)));
+  float* kscale = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
+                                           align256((size_t)n_heads * 3 * D * sizeof(_Float16)));
+  float* part = kscale + 64;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
 
   if (phases & TQ_PHASE_PREP) {
     (void)hipGetLastError();  // a launch error is reported below, not an older one
-    hipLaunchKernelGGL((prep_kernel<D>), dim3(2 * D / kPrepRows, (n_heads + kPrepHeads - 1) / kPrepHeads),
-                       dim3(256), 0, st, q, (int)(q_dtype == TQ_BF16), n_heads, kq->rot, kq->sketch, qprep);
+    // (one extra workgroup searches the K codebook scales)
+    hipLaunchKernelGGL((prep_kernel<D>), dim3(2 * D / kPrepRows + 1, (n_heads + kPrepHeads - 1) / kPrepHeads),
+                       dim3(256), 0, st, q, (int)(q_dtype == TQ_BF16), n_heads, kq->rot, kq->sketch,
+                       shape->scale * kLog2e, l.n_groups == 2 ? l.group_dim[0] : D, qprep, kq->centroids,
+                       l.n_groups, l.mse_bits[0], l.n_groups == 2 ? l.mse_bits[1] : 0, kscale);
     if (hipGetLastError() != hipSuccess) return TQ_ERR_DEVICE;
   }
 
@@ -1018,6 +1098,7 @@ extern "C" tq_status tq_attn_decode_phases(unsigned phases, const tq_quantizer* 
   a.cap = shape->cache_capacity;
   a.scale = shape->scale;
   a.qprep = qprep;
+  a.kscale = kscale;
   a.kc = k_cache->codes;
   a.ks = k_cache->signs;
   a.kn = k_cache->norms;

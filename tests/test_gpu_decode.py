@@ -128,16 +128,17 @@ def test_split_count_does_not_change_result(tq):
     wl = synth.workload("llama8b_decode", batch=1, n_q_heads=8, n_kv_heads=2)
     o = _oracle_side(wl, 3000, 3008)
     outs = []
-    for ns in (1, 3, 7, 0):
+    for ns in (1, 3, 7, 0, 16):
         _, out, q = _device_decode(tq, wl, o, 3000, 3008, want_logits=False, n_split=ns)
         outs.append(out)
     _, ro = _reference(wl, o, q)
     for out in outs:
         assert gc.normwise_close(out, ro)[0]
-    # splits change only where the fp16 softmax weights are rounded (relative
-    # to each split's running maximum): a few fp16 ulps per head
+    # the softmax reference is an integer in the log2 domain, so a token's
+    # fp16 weight is the same whatever the split (up to a power of two); only
+    # the order of the fp32 sums changes
     for out in outs[1:]:
-        assert gc.normwise_close(out, outs[0], tol=5e-4)[0]
+        assert gc.normwise_close(out, outs[0], tol=5e-5)[0]
 
 
 def test_gqa_equals_repeated_heads(tq):
