@@ -39,6 +39,7 @@ PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 matrix, vendor figure
 DECODE_WORKLOADS = ("llama8b_decode", "llama70b_long", "mixed_3p5", "mixed_2p5")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_kernel_traffic.json")
 DECODE_SOURCE = os.path.join(ROOT, "kv_cache_vector_rotation_amd", "csrc", "tq_decode.hip")
+COPY_PROBE_BYTES = 256 << 20
 
 
 def log(*a):
@@ -56,6 +57,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quantize-bench", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch every step from Python")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 256 MiB device copy (the reference for scaling "
+                         "the FETCH_SIZE / WRITE_SIZE counters of a profiled run)")
     return ap.parse_args()
 
 
@@ -325,6 +329,14 @@ def main():
                    "input_dtype": wl.dtype, "hip_graph": graph is not None},
         "roofline": roofline,
     }
+    if args.copy_probe:
+        src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: 3 device copies of {COPY_PROBE_BYTES} bytes")
+        del src, dst
     if not args.no_quantize_bench:
         result["quantize"] = quantize_bench(tq, torch, wl, kq)
         log(f"quantize: {result['quantize']}")
