@@ -114,6 +114,28 @@ __device__ __forceinline__ int64_t dest_row(const QArgs& a, int64_t i) {
 // 16-byte read each) and the four lane groups of a row cover 64 contiguous
 // bytes. The NMT accumulator chains are interleaved so consecutive MFMAs are
 // independent.
+// The same product with the B fragment read from LDS: b4 points at this
+// lane's f32x4 of step q = 0; step q is 64 f32x4 further.
+template <int NMT, int KPG, int XS>
+__device__ __forceinline__ void mfma_tiles_lds(const float* xr, const f32x4* b4, int ln, int lg,
+                                               f32x4 (&acc)[4]) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < KPG / 4; ++q) {
+    f32x4 a4[NMT];
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+      a4[mt] = *reinterpret_cast<const f32x4*>(xr + (mt * 16 + ln) * XS + 16 * q + 4 * lg);
+    const f32x4 b = b4[64 * q];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[mt][j], b[j], acc[mt], 0, 0, 0);
+  }
+}
+
 template <int NMT, int KPG, int XS>
 __device__ __forceinline__ void mfma_tiles(const float* xr, const float (&b)[KPG], int ln, int lg,
                                            f32x4 (&acc)[4]) {
@@ -151,7 +173,11 @@ struct Lds {
   // slack for per-group rounding and for the last wave's bits past the end
   static constexpr int PKW = KP * 4 / 32 + KP / 32 + 4;
   static constexpr int off_pk = off_flags + 16;                     // u32 [QT][PKW]
-  static constexpr int bytes = off_pk + QT * PKW * 4;
+  // every wave's slice of sketch_rot, in MFMA operand order: [NT][KP/16][64 lanes]
+  // f32x4 (d <= 128; larger d keeps it in registers)
+  static constexpr bool SKR_LDS = KP <= 128;
+  static constexpr int off_skr = (off_pk + QT * PKW * 4 + 15) / 16 * 16;
+  static constexpr int bytes = off_skr + (SKR_LDS ? NT * KP * 64 : 0);
 };
 
 template <int KP, int NT>
@@ -197,8 +223,15 @@ __global__ __launch_bounds__(NT * 64) void quantize_kernel(QArgs a) {
   // clamped into the matrix) so they issue back to back; out-of-range entries
   // are zeroed afterwards.
   const int ocoord = w * 16 + ln;  // output coordinate of this lane
-  float brot[KPG], bskr[KPG];
+  constexpr bool SKR_LDS = L::SKR_LDS;
+  // For d <= 128 the sketch slice lives in LDS (read once per product), which
+  // leaves the register file to the rotation slice and the tile's values;
+  // larger d keeps both slices in registers.
+  float brot[KPG];
+  float bskr[SKR_LDS ? 1 : KPG];
+  f32x4* skr_lds = reinterpret_cast<f32x4*>(smem + L::off_skr);
   {
+    float bs[KPG];
     const int64_t rb = (int64_t)(ocoord < d ? ocoord : d - 1) * d;
     if (a.m_vec) {
       // d is a multiple of 4 and the matrices are 16-byte aligned
@@ -211,7 +244,7 @@ __global__ __launch_bounds__(NT * 64) void quantize_kernel(QArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           brot[4 * q + j] = r4[j];
-          bskr[4 * q + j] = s4[j];
+          bs[4 * q + j] = s4[j];
         }
       }
     } else {
@@ -220,14 +253,22 @@ __global__ __launch_bounds__(NT * 64) void quantize_kernel(QArgs a) {
         const int k = 16 * (kk / 4) + 4 * lg + kk % 4;
         const int kc = k < d ? k : d - 1;
         brot[kk] = a.rot[rb + kc];
-        bskr[kk] = a.skr[rb + kc];
+        bs[kk] = a.skr[rb + kc];
       }
     }
 #pragma unroll
     for (int kk = 0; kk < KPG; ++kk) {
       const bool ok = ocoord < d && 16 * (kk / 4) + 4 * lg + kk % 4 < d;
       brot[kk] = ok ? brot[kk] : 0.f;
-      bskr[kk] = ok ? bskr[kk] : 0.f;
+      bs[kk] = ok ? bs[kk] : 0.f;
+    }
+    if constexpr (SKR_LDS) {
+#pragma unroll
+      for (int q = 0; q < KPG / 4; ++q)
+        skr_lds[(w * (KPG / 4) + q) * 64 + lane] = f32x4{bs[4 * q], bs[4 * q + 1], bs[4 * q + 2], bs[4 * q + 3]};
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KPG; ++kk) bskr[kk] = bs[kk];
     }
   }
   // group of this wave's coordinates (group boundaries are multiples of 16);
@@ -447,10 +488,17 @@ __global__ __launch_bounds__(NT * 64) void quantize_kernel(QArgs a) {
 
     // ---- s = (S Pi^T) r (fp32 MFMA); sign bit = [s >= 0] ----
     f32x4 sacc[4];
-    if (n_mt == 1)
-      mfma_tiles<1, KPG, XS>(xr, bskr, ln, lg, sacc);
-    else
-      mfma_tiles<4, KPG, XS>(xr, bskr, ln, lg, sacc);
+    if constexpr (SKR_LDS) {
+      if (n_mt == 1)
+        mfma_tiles_lds<1, KPG, XS>(xr, skr_lds + w * (KPG / 4) * 64 + lane, ln, lg, sacc);
+      else
+        mfma_tiles_lds<4, KPG, XS>(xr, skr_lds + w * (KPG / 4) * 64 + lane, ln, lg, sacc);
+    } else {
+      if (n_mt == 1)
+        mfma_tiles<1, KPG, XS>(xr, bskr, ln, lg, sacc);
+      else
+        mfma_tiles<4, KPG, XS>(xr, bskr, ln, lg, sacc);
+    }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       if (mt >= n_mt) break;
