@@ -3,7 +3,8 @@
 
 One step = quantize-on-append of the new token(s) of every (batch, KV head)
 for K (token-major records) and V (32-token block records), then one decode
-step over the whole compressed cache (query prep, split-K pass, combine).
+step over the whole compressed cache: tq_attn_decode_append, i.e. one launch
+for both appends and the query prep, then the split-K pass and the combine.
 Inputs are seeded synthetic tensors already resident in HBM; the cache is
 built (untimed) by the library's own quantize kernel from synthetic K/V.
 
@@ -227,16 +228,25 @@ def main():
     log(f"setup {time.perf_counter() - t_setup:.1f}s: {args.workload} B={B} Hq={HQ} Hkv={H} d={d} "
         f"N={N} bits={bits} dims={dims} copies={n_copies} ({n_copies * cache_bytes / 2**30:.2f} GiB)")
 
+    k_app = tq.append_spec(k_new, seg_len=wl.n_new, seg_stride=cap, seg_offset=prefix)
+    v_app = tq.append_spec(v_new, seg_len=wl.n_new, seg_stride=cap, seg_offset=prefix)
+
     def step(i, ev=None):
+        # append the new K/V tokens and decode over the whole cache: one
+        # launch for both appends and the query preparation, then the
+        # split-K pass and the combine
         kc, vc = caches[i % n_copies]
+        if ev is None:
+            tq.tq_attn_decode_append(kq, vq, shape, q, kc, vc, k_new=k_app, v_new=v_app, out=out,
+                                     workspace=ws)
+            return
+        # (the per-phase form, to put events around the split-K pass)
         tq.tq_quantize(kq, tq.TQ_TOKEN_MAJOR, k_new, kc, seg_len=wl.n_new, seg_stride=cap, seg_offset=prefix)
         tq.tq_quantize(vq, tq.TQ_BLOCK32, v_new, vc, seg_len=wl.n_new, seg_stride=cap, seg_offset=prefix)
         tq.tq_attn_decode_phases(tq.TQ_PHASE_PREP, kq, vq, shape, q, kc, vc, out=out, workspace=ws)
-        if ev is not None:
-            ev[0].record()
+        ev[0].record()
         tq.tq_attn_decode_phases(tq.TQ_PHASE_SPLIT, kq, vq, shape, q, kc, vc, out=out, workspace=ws)
-        if ev is not None:
-            ev[1].record()
+        ev[1].record()
         tq.tq_attn_decode_phases(tq.TQ_PHASE_COMBINE, kq, vq, shape, q, kc, vc, out=out, workspace=ws)
 
     for i in range(max(args.warmup, n_copies)):

@@ -287,6 +287,35 @@ tq_status tq_attn_decode_phases(unsigned phases, const tq_quantizer* kq, const t
                                 const tq_cache* k_cache, const tq_cache* v_cache, float* logits,
                                 float* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Vectors to append to a cache within a decode step (see
+ * tq_attn_decode_append): x, dtype, n_vec, x_row_stride and rows as for
+ * tq_quantize. */
+typedef struct {
+  const void* x;
+  tq_dtype dtype;
+  int64_t n_vec;
+  int64_t x_row_stride;
+  tq_rows rows;
+} tq_append;
+
+/* One decode step with its appends ([ZB] paragraph 2: each new token is
+ * quantized as it enters the cache; [WD] introduction: attention logits from
+ * the compressed cache; R14: the new tokens are attended to). Equivalent to
+ *   tq_quantize(kq, TQ_TOKEN_MAJOR, k_new..., k_cache);
+ *   tq_quantize(vq, TQ_BLOCK32, v_new..., v_cache);
+ *   tq_attn_decode(kq, vq, shape, q, ...);
+ * on the same stream, but the two appends and the query preparation run as
+ * one launch (they are independent), followed by the split-K pass and the
+ * combine. k_new / v_new may be NULL (nothing appended; v_new requires vq).
+ * Same arguments, validation and errors as those calls; everything is
+ * validated before anything is launched. Supported for d = 128 (as
+ * tq_attn_decode), otherwise TQ_ERR_UNSUPPORTED. */
+tq_status tq_attn_decode_append(const tq_quantizer* kq, const tq_quantizer* vq,
+                                const tq_decode_shape* shape, const tq_append* k_new,
+                                const tq_append* v_new, const void* q, tq_dtype q_dtype,
+                                const tq_cache* k_cache, const tq_cache* v_cache, float* logits,
+                                float* out, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

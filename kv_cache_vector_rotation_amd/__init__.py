@@ -42,7 +42,7 @@ TQ_PHASE_ALL = 7
 
 SYMBOLS = ("tq_abi_version", "tq_status_string", "tq_build_codebook", "tq_record_layout",
            "tq_fold_sketch", "tq_quantize", "tq_attn_decode_workspace_bytes", "tq_attn_decode",
-           "tq_attn_decode_phases")
+           "tq_attn_decode_phases", "tq_attn_decode_append")
 
 
 class TQError(RuntimeError):
@@ -75,6 +75,11 @@ class tq_record_info(C.Structure):
 class tq_rows(C.Structure):
     _fields_ = [("dst_rows", C.c_void_p), ("seg_len", C.c_int64), ("seg_stride", C.c_int64),
                 ("seg_offset", C.c_int64)]
+
+
+class tq_append(C.Structure):
+    _fields_ = [("x", C.c_void_p), ("dtype", C.c_int), ("n_vec", C.c_int64), ("x_row_stride", C.c_int64),
+                ("rows", tq_rows)]
 
 
 class tq_decode_shape(C.Structure):
@@ -126,6 +131,10 @@ def lib() -> C.CDLL:
                                      C.c_void_p, C.c_size_t, C.c_void_p]
         L.tq_attn_decode_phases.restype = C.c_int
         L.tq_attn_decode_phases.argtypes = [C.c_uint] + L.tq_attn_decode.argtypes
+        L.tq_attn_decode_append.restype = C.c_int
+        L.tq_attn_decode_append.argtypes = (L.tq_attn_decode.argtypes[:3] +
+                                            [C.POINTER(tq_append), C.POINTER(tq_append)] +
+                                            L.tq_attn_decode.argtypes[3:])
         _lib = L
     return _lib
 
@@ -371,10 +380,56 @@ def tq_attn_decode_phases(phases: int, kq: Quantizer, vq: Optional[Quantizer], s
            "tq_attn_decode")
 
 
+def append_spec(x, dst_rows=None, seg_len: int = 1, seg_stride: int = 1, seg_offset: int = 0) -> tq_append:
+    """Vectors to append within tq_attn_decode_append: the rows of x ([n_vec,
+    >= d] float32/bfloat16 on the GPU) go to dst_rows, or by segments as in
+    tq_quantize. The returned struct keeps a reference to its tensors."""
+    torch = _torch()
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D tensor with unit stride along the channels")
+    a = tq_append()
+    a.x = _ptr(x)
+    a.dtype = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}[x.dtype]
+    a.n_vec = x.shape[0]
+    a.x_row_stride = x.stride(0)
+    a.rows.dst_rows = _ptr(dst_rows)
+    a.rows.seg_len, a.rows.seg_stride, a.rows.seg_offset = seg_len, seg_stride, seg_offset
+    a._keep = (x, dst_rows)
+    return a
+
+
+def tq_attn_decode_append(kq: Quantizer, vq: Optional[Quantizer], shape: tq_decode_shape, q,
+                          k_cache: Cache, v_cache: Optional[Cache], k_new: Optional[tq_append] = None,
+                          v_new: Optional[tq_append] = None, logits=None, out=None, workspace=None,
+                          stream=None) -> None:
+    """Appends k_new / v_new (append_spec structs, or None) to the caches and
+    runs the decode step over them, as one launch for the appends and the
+    query preparation followed by the split-K pass and the combine."""
+    torch = _torch()
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    dt = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}[q.dtype]
+    if workspace is None:
+        workspace = torch.empty(tq_attn_decode_workspace_bytes(kq, vq, shape), dtype=torch.uint8,
+                                device=q.device)
+    kqs = kq.struct()
+    vqs = vq.struct() if vq is not None else None
+    kc = k_cache.struct()
+    vc = v_cache.struct() if v_cache is not None else None
+    _check(lib().tq_attn_decode_append(C.byref(kqs), C.byref(vqs) if vqs is not None else None,
+                                       C.byref(shape), C.byref(k_new) if k_new is not None else None,
+                                       C.byref(v_new) if v_new is not None else None, _ptr(q), dt,
+                                       C.byref(kc), C.byref(vc) if vc is not None else None,
+                                       _ptr(logits), _ptr(out), _ptr(workspace), workspace.numel(),
+                                       _stream(stream)),
+           "tq_attn_decode_append")
+
+
 __all__ = [
     "LIB_PATH", "SYMBOLS", "lib", "TQError", "Quantizer", "Cache", "make_layout", "decode_shape",
     "tq_abi_version", "tq_status_string", "tq_build_codebook", "tq_record_layout", "tq_fold_sketch",
     "tq_quantize", "tq_attn_decode_workspace_bytes", "tq_attn_decode", "tq_attn_decode_phases",
+    "tq_attn_decode_append", "append_spec", "tq_append",
     "TQ_PHASE_PREP", "TQ_PHASE_SPLIT", "TQ_PHASE_COMBINE", "TQ_PHASE_ALL",
     "TQ_OK", "TQ_ERR_INVALID", "TQ_ERR_UNSUPPORTED", "TQ_ERR_NOCONVERGE", "TQ_ERR_WORKSPACE",
     "TQ_ERR_DEVICE", "TQ_F32", "TQ_BF16", "TQ_TOKEN_MAJOR", "TQ_BLOCK32",

@@ -48,6 +48,8 @@
 #include <type_traits>
 
 #include "tq_internal.h"
+#include "tq_prep_dev.h"
+#include "tq_quantize_dev.h"
 #include "turboquant.h"
 
 namespace {
@@ -704,166 +706,12 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Query preparation: q_rot = f rot q (stored as fp16 hi and (q - hi) * 2^11)
-// and q_sk = f alpha_g sketch q (fp16), with f = scale * log2(e) so that the
-// split pass forms log2-domain logits directly; fp32 sums in ascending k,
-// scaled after the sum. A workgroup takes 16
-// rows of the stacked [rot; sketch] matrix and kPrepHeads heads; both are
-// staged in LDS by coalesced 16-byte loads, then thread (i, hq) forms the
-// dot products of row i with heads hq, hq + 16, ...
+// Query preparation (see tq_prep_dev.h), 256 threads per block.
 // ---------------------------------------------------------------------------
-constexpr int kPrepHeads = 64;
-constexpr int kPrepRows = 16;
-
-// Scale s in [1, 2) for which the fp16 roundings of s |c_k| are closest to
-// exact (smallest largest relative error over the centroids; 2048
-// candidates s = 1 + i / 2048, ties to the smaller i). The decode tables
-// hold fp16(s c) and the logits divide by s, so the centroids enter the
-// products with a few 1e-5 relative error instead of fp16's ~2.4e-4.
-__device__ void search_fp16_scale(const float* cent, int L, float* out, int tid) {
-  __shared__ float s_err[256];
-  __shared__ int s_idx[256];
-  float best = INFINITY;
-  int bi = 0;
-  for (int i = tid; i < 2048; i += 256) {
-    const float sc = 1.0f + (float)i * (1.0f / 2048.0f);
-    float worst = 0.f;
-    for (int k = 0; k < L; ++k) {
-      const float x = fabsf(cent[k]) * sc;
-      const float r = fabsf((float)(_Float16)x - x) / x;
-      worst = fmaxf(worst, r);
-    }
-    if (worst < best) {
-      best = worst;
-      bi = i;
-    }
-  }
-  s_err[tid] = best;
-  s_idx[tid] = bi;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) {
-      const float e2 = s_err[tid + w];
-      const int i2 = s_idx[tid + w];
-      if (e2 < s_err[tid] || (e2 == s_err[tid] && i2 < s_idx[tid])) {
-        s_err[tid] = e2;
-        s_idx[tid] = i2;
-      }
-    }
-    __syncthreads();
-  }
-  if (tid == 0) *out = 1.0f + (float)s_idx[0] * (1.0f / 2048.0f);
-  __syncthreads();
-}
-
 template <int D>
-__global__ __launch_bounds__(256) void prep_kernel(const void* q, int q_bf16, int n_heads,
-                                                   const float* rot, const float* sketch,
-                                                   float scale_l2, int group_dim0,
-                                                   _Float16* qprep, const float* kcent, int n_groups,
-                                                   int m0, int m1, float* kscale) {
-  if (blockIdx.x == 2 * D / kPrepRows) {
-    if (blockIdx.y == 0) {
-      search_fp16_scale(kcent, 1 << m0, kscale, threadIdx.x);
-      if (n_groups > 1) search_fp16_scale(kcent + (1 << m0), 1 << m1, kscale + 1, threadIdx.x);
-    }
-    return;
-  }
-  constexpr int QS = D + 4;  // LDS row stride (floats)
-  constexpr int HPT = kPrepHeads / 16;  // heads per thread
-  __shared__ __align__(16) float sm[kPrepRows][QS];
-  __shared__ __align__(16) float sq[kPrepHeads][QS];
-  const int t = threadIdx.x;
-  const int r0 = blockIdx.x * kPrepRows;  // first row of [rot; sketch]
-  const int h0 = blockIdx.y * kPrepHeads;
-  const float* mat = r0 < D ? rot + (int64_t)r0 * D : sketch + (int64_t)(r0 - D) * D;
-  {
-    constexpr int C4 = D / 4;  // 16-byte chunks per matrix row
-    f32x4 mb[kPrepRows * C4 / 256];
-#pragma unroll
-    for (int i = 0; i < kPrepRows * C4 / 256; ++i) {
-      const int c = t + 256 * i;
-      mb[i] = *reinterpret_cast<const f32x4*>(mat + (c / C4) * D + (c % C4) * 4);
-    }
-#pragma unroll
-    for (int i = 0; i < kPrepRows * C4 / 256; ++i) {
-      const int c = t + 256 * i;
-      *reinterpret_cast<f32x4*>(&sm[c / C4][(c % C4) * 4]) = mb[i];
-    }
-  }
-  if (q_bf16) {
-    constexpr int C8 = D / 8;  // 16-byte chunks per bf16 query row
-    constexpr int NC = kPrepHeads * C8 / 256;
-    u32x4 qb[NC];
-#pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      const int c = t + 256 * i, h = h0 + c / C8;
-      const int hc = h < n_heads ? h : n_heads - 1;
-      qb[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(q) + (int64_t)hc * D +
-                                              (c % C8) * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      const int c = t + 256 * i;
-      float* dst = &sq[c / C8][(c % C8) * 8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        dst[2 * e] = __uint_as_float(qb[i][e] << 16);
-        dst[2 * e + 1] = __uint_as_float(qb[i][e] & 0xFFFF0000u);
-      }
-    }
-  } else {
-    constexpr int C4 = D / 4;
-    constexpr int NC = kPrepHeads * C4 / 256;
-    f32x4 qb[NC];
-#pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      const int c = t + 256 * i, h = h0 + c / C4;
-      const int hc = h < n_heads ? h : n_heads - 1;
-      qb[i] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(q) + (int64_t)hc * D +
-                                              (c % C4) * 4);
-    }
-#pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      const int c = t + 256 * i;
-      *reinterpret_cast<f32x4*>(&sq[c / C4][(c % C4) * 4]) = qb[i];
-    }
-  }
-  __syncthreads();
-  const int i = t % kPrepRows, hq = t / kPrepRows;
-  float acc[HPT] = {};
-#pragma unroll 4
-  for (int k = 0; k < D; k += 4) {
-    const f32x4 m4 = *reinterpret_cast<const f32x4*>(&sm[i][k]);
-#pragma unroll
-    for (int r = 0; r < HPT; ++r) {
-      const f32x4 q4 = *reinterpret_cast<const f32x4*>(&sq[hq + 16 * r][k]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[r] = fmaf(m4[j], q4[j], acc[r]);
-    }
-  }
-  const int row = r0 + i;
-  // logits in the log2 domain: both parts carry scale * log2(e); the sketch
-  // part also alpha_g = sqrt(pi / 2) / d_g of the row's group
-  float f = scale_l2;
-  if (row >= D) {
-    const int dg = row - D < group_dim0 ? group_dim0 : D - group_dim0;
-    f *= 1.2533141373155003f / (float)dg;
-  }
-#pragma unroll
-  for (int r = 0; r < HPT; ++r) {
-    const int h = h0 + hq + 16 * r;
-    if (h >= n_heads) continue;
-    _Float16* dst = qprep + (int64_t)h * 3 * D;
-    acc[r] *= f;
-    const _Float16 hi = (_Float16)acc[r];
-    if (row < D) {
-      dst[row] = hi;
-      dst[D + row] = (_Float16)((acc[r] - (float)hi) * kLoScale);
-    } else {
-      dst[D + row] = hi;  // q_sk at [2 D, 3 D)
-    }
-  }
+__global__ __launch_bounds__(256) void prep_kernel(tqp::PrepArgs p) {
+  __shared__ __align__(16) unsigned char smem[tqp::prep_lds_bytes<D>()];
+  tqp::prep_block<D, 256>(p, blockIdx.x, blockIdx.y, threadIdx.x, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -1035,12 +883,24 @@ extern "C" tq_status tq_attn_decode_workspace_bytes(const tq_quantizer* kq, cons
   return TQ_OK;
 }
 
-extern "C" tq_status tq_attn_decode_phases(unsigned phases, const tq_quantizer* kq,
-                                           const tq_quantizer* vq, const tq_decode_shape* shape,
-                                           const void* q, tq_dtype q_dtype, const tq_cache* k_cache,
-                                           const tq_cache* v_cache, float* logits, float* out,
-                                           void* workspace, size_t workspace_bytes, void* stream) {
-  if (phases == 0 || (phases & ~(unsigned)TQ_PHASE_ALL) != 0) return TQ_ERR_INVALID;
+namespace {
+
+// Everything a decode call launches, validated and laid out in the workspace.
+struct Plan {
+  DArgs a;
+  tqp::PrepArgs prep;
+  int n_hblk, prep_grid_y, n_heads, n_groups, m0, m1, group_dim0;
+  bool with_v;
+  const float* vrot;
+  const float* vsketch;
+  float* out;
+};
+
+constexpr int kD = 128;  // the decode kernels' dimension
+
+tq_status plan_decode(const tq_quantizer* kq, const tq_quantizer* vq, const tq_decode_shape* shape,
+                      const void* q, tq_dtype q_dtype, const tq_cache* k_cache, const tq_cache* v_cache,
+                      float* logits, float* out, void* workspace, size_t workspace_bytes, Plan* pl) {
   if (!tq::quantizer_pointers_valid(kq) || !shape_valid(shape)) return TQ_ERR_INVALID;
   if (vq && !tq::quantizer_pointers_valid(vq)) return TQ_ERR_INVALID;
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_ERR_INVALID;
@@ -1060,8 +920,8 @@ extern "C" tq_status tq_attn_decode_phases(unsigned phases, const tq_quantizer* 
                         with_v ? (const void*)v_cache->codes : nullptr,
                         with_v ? (const void*)v_cache->signs : nullptr,
                         with_v ? (const void*)v_cache->norms : nullptr};
-  for (const void* p : ptrs)
-    if (p && reinterpret_cast<uintptr_t>(p) % 16 != 0) return TQ_ERR_INVALID;
+  for (const void* ptr : ptrs)
+    if (ptr && reinterpret_cast<uintptr_t>(ptr) % 16 != 0) return TQ_ERR_INVALID;
   if (!decode_supported(kq->layout)) return TQ_ERR_UNSUPPORTED;
   const tq_layout& l = kq->layout;
   const int group = shape->n_q_heads / shape->n_kv_heads;
@@ -1070,25 +930,39 @@ extern "C" tq_status tq_attn_decode_phases(unsigned phases, const tq_quantizer* 
   const size_t need = workspace_for(shape, l.d, with_v, n_split);
   if (!workspace || workspace_bytes < need) return TQ_ERR_WORKSPACE;
 
-  constexpr int D = 128;
+  constexpr int D = kD;
   const int n_heads = shape->batch * shape->n_q_heads;
   _Float16* qprep = reinterpret_cast<_Float16*>(workspace);
   float* kscale = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
                                            align256((size_t)n_heads * 3 * D * sizeof(_Float16)));
   float* part = kscale + 64;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
 
-  if (phases & TQ_PHASE_PREP) {
-    (void)hipGetLastError();  // a launch error is reported below, not an older one
-    // (one extra workgroup searches the K codebook scales)
-    hipLaunchKernelGGL((prep_kernel<D>), dim3(2 * D / kPrepRows + 1, (n_heads + kPrepHeads - 1) / kPrepHeads),
-                       dim3(256), 0, st, q, (int)(q_dtype == TQ_BF16), n_heads, kq->rot, kq->sketch,
-                       shape->scale * kLog2e, l.n_groups == 2 ? l.group_dim[0] : D, qprep, kq->centroids,
-                       l.n_groups, l.mse_bits[0], l.n_groups == 2 ? l.mse_bits[1] : 0, kscale);
-    if (hipGetLastError() != hipSuccess) return TQ_ERR_DEVICE;
-  }
+  *pl = Plan{};
+  pl->n_hblk = n_hblk;
+  pl->n_heads = n_heads;
+  pl->n_groups = l.n_groups;
+  pl->m0 = l.mse_bits[0];
+  pl->m1 = l.n_groups == 2 ? l.mse_bits[1] : 0;
+  pl->group_dim0 = l.n_groups == 2 ? l.group_dim[0] : D;
+  pl->with_v = with_v;
+  pl->out = out;
+  pl->prep_grid_y = (n_heads + tqp::kPrepHeads - 1) / tqp::kPrepHeads;
+  tqp::PrepArgs& pp = pl->prep;
+  pp.q = q;
+  pp.q_bf16 = q_dtype == TQ_BF16;
+  pp.n_heads = n_heads;
+  pp.rot = kq->rot;
+  pp.sketch = kq->sketch;
+  pp.scale_l2 = shape->scale * kLog2e;
+  pp.group_dim0 = pl->group_dim0;
+  pp.qprep = qprep;
+  pp.kcent = kq->centroids;
+  pp.n_groups = l.n_groups;
+  pp.m0 = pl->m0;
+  pp.m1 = pl->m1;
+  pp.kscale = kscale;
 
-  DArgs a{};
+  DArgs& a = pl->a;
   a.batch = shape->batch;
   a.hq = shape->n_q_heads;
   a.hkv = shape->n_kv_heads;
@@ -1108,26 +982,128 @@ extern "C" tq_status tq_attn_decode_phases(unsigned phases, const tq_quantizer* 
     a.vs = v_cache->signs;
     a.vn = v_cache->norms;
     a.vcent = vq->centroids;
+    pl->vrot = vq->rot;
+    pl->vsketch = vq->sketch;
   }
   a.logits = logits;
   a.part = part;
+  return TQ_OK;
+}
+
+tq_status run_phases(const Plan& pl, unsigned phases, hipStream_t st) {
+  constexpr int D = kD;
+  if (phases & TQ_PHASE_PREP) {
+    (void)hipGetLastError();  // a launch error is reported below, not an older one
+    hipLaunchKernelGGL((prep_kernel<D>), dim3(tqp::prep_blocks_x<D>(), pl.prep_grid_y), dim3(256), 0, st,
+                       pl.prep);
+    if (hipGetLastError() != hipSuccess) return TQ_ERR_DEVICE;
+  }
   if (phases & TQ_PHASE_SPLIT) {
     hipError_t e;
-    if (l.n_groups == 1)
-      e = with_v ? dispatch_m0<D, 1, true>(a, l.mse_bits[0], 0, n_hblk, st)
-                 : dispatch_m0<D, 1, false>(a, l.mse_bits[0], 0, n_hblk, st);
+    if (pl.n_groups == 1)
+      e = pl.with_v ? dispatch_m0<D, 1, true>(pl.a, pl.m0, 0, pl.n_hblk, st)
+                    : dispatch_m0<D, 1, false>(pl.a, pl.m0, 0, pl.n_hblk, st);
     else
-      e = with_v ? dispatch_m0<D, 2, true>(a, l.mse_bits[0], l.mse_bits[1], n_hblk, st)
-                 : dispatch_m0<D, 2, false>(a, l.mse_bits[0], l.mse_bits[1], n_hblk, st);
+      e = pl.with_v ? dispatch_m0<D, 2, true>(pl.a, pl.m0, pl.m1, pl.n_hblk, st)
+                    : dispatch_m0<D, 2, false>(pl.a, pl.m0, pl.m1, pl.n_hblk, st);
     if (e != hipSuccess) return TQ_ERR_DEVICE;
   }
-  if (with_v && (phases & TQ_PHASE_COMBINE)) {
+  if (pl.with_v && (phases & TQ_PHASE_COMBINE)) {
     (void)hipGetLastError();  // a launch error is reported below, not an older one
-    hipLaunchKernelGGL((combine_kernel<D>), dim3(n_heads), dim3(2 * D), 0, st, part, n_split, vq->rot,
-                       vq->sketch, l.n_groups == 2 ? l.group_dim[0] : D, out);
+    hipLaunchKernelGGL((combine_kernel<D>), dim3(pl.n_heads), dim3(2 * D), 0, st, pl.a.part, pl.a.n_split,
+                       pl.vrot, pl.vsketch, pl.group_dim0, pl.out);
     if (hipGetLastError() != hipSuccess) return TQ_ERR_DEVICE;
   }
   return TQ_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Fused appends + query preparation: the blocks of one launch quantize the
+// new K vectors, then the new V vectors, then run the query preparation (the
+// three are independent, so their latencies overlap).
+// ---------------------------------------------------------------------------
+constexpr int kStepKP = 128, kStepNT = 8;  // quantize shape for d = 128
+
+struct StepArgs {
+  tqq::QArgs k, v;
+  int nk, nv;  // blocks given to the K and V appends (0 = none)
+  tqp::PrepArgs prep;
+  int prep_x;  // prep blocks along x; the prep blocks are laid out x-major
+};
+
+__global__ __launch_bounds__(kStepNT * 64) void step_kernel(StepArgs s) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int b = blockIdx.x;
+  if (b < s.nk + s.nv) {
+    const bool is_k = b < s.nk;
+    tqq::quantize_tiles<kStepKP, kStepNT>(is_k ? s.k : s.v, is_k ? b : b - s.nk, is_k ? s.nk : s.nv, smem);
+  } else {
+    const int pb = b - s.nk - s.nv;
+    tqp::prep_block<kD, kStepNT * 64>(s.prep, pb % s.prep_x, pb / s.prep_x, threadIdx.x, smem);
+  }
+}
+
+}  // namespace
+
+extern "C" tq_status tq_attn_decode_phases(unsigned phases, const tq_quantizer* kq,
+                                           const tq_quantizer* vq, const tq_decode_shape* shape,
+                                           const void* q, tq_dtype q_dtype, const tq_cache* k_cache,
+                                           const tq_cache* v_cache, float* logits, float* out,
+                                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (phases == 0 || (phases & ~(unsigned)TQ_PHASE_ALL) != 0) return TQ_ERR_INVALID;
+  Plan pl;
+  const tq_status st = plan_decode(kq, vq, shape, q, q_dtype, k_cache, v_cache, logits, out, workspace,
+                                   workspace_bytes, &pl);
+  if (st != TQ_OK) return st;
+  return run_phases(pl, phases, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" tq_status tq_attn_decode_append(const tq_quantizer* kq, const tq_quantizer* vq,
+                                           const tq_decode_shape* shape, const tq_append* k_new,
+                                           const tq_append* v_new, const void* q, tq_dtype q_dtype,
+                                           const tq_cache* k_cache, const tq_cache* v_cache,
+                                           float* logits, float* out, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  Plan pl;
+  tq_status st = plan_decode(kq, vq, shape, q, q_dtype, k_cache, v_cache, logits, out, workspace,
+                             workspace_bytes, &pl);
+  if (st != TQ_OK) return st;
+  if (v_new && !vq) return TQ_ERR_INVALID;
+  StepArgs sa{};
+  bool k_empty = true, v_empty = true;
+  if (k_new) {
+    st = tqq::make_qargs(kq, TQ_TOKEN_MAJOR, k_new->x, k_new->dtype, k_new->n_vec, k_new->x_row_stride,
+                         &k_new->rows, k_cache, &sa.k, &k_empty);
+    if (st != TQ_OK) return st;
+  }
+  if (v_new) {
+    st = tqq::make_qargs(vq, TQ_BLOCK32, v_new->x, v_new->dtype, v_new->n_vec, v_new->x_row_stride,
+                         &v_new->rows, v_cache, &sa.v, &v_empty);
+    if (st != TQ_OK) return st;
+  }
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (tqq::quantize_kp(kq->layout.d) != kStepKP) return TQ_ERR_UNSUPPORTED;
+  // blocks per append: every tile of an append gets its own block, up to one
+  // round of the machine
+  int dev = 0, n_cu = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) n_cu = v;
+  }
+  sa.nk = k_empty ? 0 : (int)(sa.k.n_tiles < n_cu ? sa.k.n_tiles : n_cu);
+  sa.nv = v_empty ? 0 : (int)(sa.v.n_tiles < n_cu ? sa.v.n_tiles : n_cu);
+  sa.prep = pl.prep;
+  sa.prep_x = tqp::prep_blocks_x<kD>();
+  const int grid = sa.nk + sa.nv + sa.prep_x * pl.prep_grid_y;
+  using L = tqq::Lds<kStepKP, kStepNT>;
+  constexpr int lds = L::bytes > tqp::prep_lds_bytes<kD>() ? L::bytes : tqp::prep_lds_bytes<kD>();
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&step_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          lds) != hipSuccess)
+    return TQ_ERR_DEVICE;
+  (void)hipGetLastError();  // a launch error is reported below, not an older one
+  hipLaunchKernelGGL(step_kernel, dim3(grid), dim3(kStepNT * 64), lds, hs, sa);
+  if (hipGetLastError() != hipSuccess) return TQ_ERR_DEVICE;
+  return run_phases(pl, TQ_PHASE_SPLIT | TQ_PHASE_COMBINE, hs);
 }
 
 extern "C" tq_status tq_attn_decode(const tq_quantizer* kq, const tq_quantizer* vq,

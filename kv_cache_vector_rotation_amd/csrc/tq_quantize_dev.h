@@ -1,0 +1,802 @@
+// Quantize kernel body and argument set-up, shared by the quantize entry
+// point and the fused append + query-prep launch of a decode step.
+//
+// [ZB] paragraph 2 and [WD] "Como o TurboQuant funciona": rotate each vector
+// by a random orthogonal matrix, give every rotated coordinate its Lloyd-Max
+// cell, take the residual of that MSE quantizer, keep the signs of a Gaussian
+// sketch of the residual, and store codes, sign bits and the norms.
+//
+// Work decomposition. A workgroup owns a tile of 64 vectors at a time and
+// loops over tiles (grid-stride). It has one wave per 16 output coordinates
+// (d rounded up to 16), so a wave's slice of the d x d matrices stays in
+// registers for the whole kernel, as the B operand of
+// v_mfma_f32_16x16x4_f32. The input tile and later the rotated residual sit
+// in LDS as the A operand shared by all waves. Both contractions are fp32
+// MFMA with fp32 accumulation: the codes are decided by comparing rotated
+// coordinates with the decision boundaries, which needs fp32-grade
+// products (bf16-rounded operands would move coordinates by ~1e-4 of a
+// cell). Between the two contractions each lane finishes its coordinates:
+// group norms (cross-wave sums through LDS), cells, residual, residual norm.
+// After the second contraction the sign bits and codes are packed from LDS
+// bytes into the record format and stored.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "tq_internal.h"
+#include "turboquant.h"
+
+namespace tqq {
+
+
+constexpr int QT = 64;  // vectors per tile
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct QArgs {
+  const void* x;
+  int64_t n_vec;
+  int64_t x_stride;
+  int x_bf16;
+  int x_vec;  // rows 16-byte aligned and d a multiple of the 16-byte vector width
+  int m_vec;  // rot and sketch_rot 16-byte aligned and d a multiple of 4
+  const float* rot;
+  const float* skr;
+  const float* centroids;
+  const float* boundaries;
+  int d;
+  int n_groups;
+  int gdim[2];
+  int gbits[2];
+  int choff[2];
+  int cwoff[2];
+  int swoff[2];
+  int bcwoff[2];
+  int bswoff[2];
+  int coff[2];
+  int boff[2];
+  int code_words;
+  int sign_words;
+  int blk_code_words;
+  int blk_sign_words;
+  int fmt;
+  const int64_t* dst_rows;
+  int64_t seg_len;
+  int64_t seg_stride;
+  int64_t seg_offset;
+  int64_t n_rows;
+  // Block-owned tiling (block records, segment rows, seg_stride % 32 == 0):
+  // tile = (segment, pair of 32-row blocks); the workgroup owning the tile is
+  // the only writer of those blocks, so partial blocks are read-modify-written.
+  int blk_owned;
+  int pk_zero;  // token-major: some record word is only partly covered by the waves' fields
+  int64_t pairs_per_seg;
+  int64_t n_tiles;
+  uint32_t* codes;
+  uint32_t* signs;
+  float* norms;
+};
+
+// Sum over each row of 16 lanes, result in every lane of the row, with DPP
+// lane moves (no LDS round trip): swap neighbours, swap pairs, then mirror
+// within 8 and within 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t row16_or(uint32_t s) {
+  s |= dpp_u<0xB1>(s);
+  s |= dpp_u<0x4E>(s);
+  s |= dpp_u<0x141>(s);
+  s |= dpp_u<0x140>(s);
+  return s;
+}
+__device__ __forceinline__ float row16_sum(float s) {
+  s += dpp_f<0xB1>(s);   // quad_perm [1, 0, 3, 2]
+  s += dpp_f<0x4E>(s);   // quad_perm [2, 3, 0, 1]
+  s += dpp_f<0x141>(s);  // row_half_mirror
+  s += dpp_f<0x140>(s);  // row_mirror
+  return s;
+}
+
+__device__ __forceinline__ int64_t dest_row(const QArgs& a, int64_t i) {
+  if (a.dst_rows) return a.dst_rows[i];
+  return (i / a.seg_len) * a.seg_stride + a.seg_offset + (i % a.seg_len);
+}
+
+// acc[mt] = A[16 mt .. 16 mt + 15][:] x B for the first NMT 16-vector tiles
+// (the rest are zeroed). A is the fp32 tile in LDS (row stride XS); B is this
+// wave's register fragment. Step (q, j) of lane group lg takes k = 16 q + 4 lg
+// + j, so a lane's four k of one q are adjacent in memory on both sides (one
+// 16-byte read each) and the four lane groups of a row cover 64 contiguous
+// bytes. The NMT accumulator chains are interleaved so consecutive MFMAs are
+// independent.
+// The same product with the B fragment read from LDS: b4 points at this
+// lane's f32x4 of step q = 0; step q is 64 f32x4 further.
+template <int NMT, int KPG, int XS>
+__device__ __forceinline__ void mfma_tiles_lds(const float* xr, const f32x4* b4, int ln, int lg,
+                                               f32x4 (&acc)[4]) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < KPG / 4; ++q) {
+    f32x4 a4[NMT];
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+      a4[mt] = *reinterpret_cast<const f32x4*>(xr + (mt * 16 + ln) * XS + 16 * q + 4 * lg);
+    const f32x4 b = b4[64 * q];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[mt][j], b[j], acc[mt], 0, 0, 0);
+  }
+}
+
+template <int NMT, int KPG, int XS>
+__device__ __forceinline__ void mfma_tiles(const float* xr, const float (&b)[KPG], int ln, int lg,
+                                           f32x4 (&acc)[4]) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < KPG / 4; ++q) {
+    f32x4 a4[NMT];
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+      a4[mt] = *reinterpret_cast<const f32x4*>(xr + (mt * 16 + ln) * XS + 16 * q + 4 * lg);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[mt][j], b[4 * q + j], acc[mt], 0, 0, 0);
+  }
+}
+
+// LDS layout (bytes), KP = padded K, NT = number of 16-wide coordinate tiles.
+template <int KP, int NT>
+struct Lds {
+  static constexpr int XS = KP + 4;  // row stride of the fp32 tile, in floats
+  static constexpr int DP = NT * 16;
+  static constexpr int off_x = 0;                                   // float [QT][XS]
+  static constexpr int off_code = off_x + QT * XS * 4;              // u8 [QT][DP]
+  static constexpr int off_sign = off_code + QT * DP;               // u8 [QT][DP]
+  static constexpr int off_npart = off_sign + QT * DP;              // float [NT][QT]
+  static constexpr int off_gpart = off_npart + NT * QT * 4;         // float [NT][QT]
+  static constexpr int off_nrm = off_gpart + NT * QT * 4;           // float [2][QT]
+  static constexpr int off_cb = off_nrm + 2 * QT * 4;               // float [64]
+  static constexpr int off_rows = off_cb + 64 * 4;                  // int64 [QT]
+  static constexpr int off_flags = off_rows + QT * 8;               // int [4]
+  // packed token-major records: codes (at most 4 bits x KP) then signs, plus
+  // slack for per-group rounding and for the last wave's bits past the end
+  static constexpr int PKW = KP * 4 / 32 + KP / 32 + 4;
+  static constexpr int off_pk = off_flags + 16;                     // u32 [QT][PKW]
+  // every wave's slice of sketch_rot, in MFMA operand order: [NT][KP/16][64 lanes]
+  // f32x4 (d <= 128; larger d keeps it in registers)
+  static constexpr bool SKR_LDS = KP <= 128;
+  static constexpr int off_skr = (off_pk + QT * PKW * 4 + 15) / 16 * 16;
+  static constexpr int bytes = off_skr + (SKR_LDS ? NT * KP * 64 : 0);
+};
+
+// The kernel body: this workgroup quantizes tiles first_tile,
+// first_tile + tile_stride, ... of `a`, with NT * 64 threads and the dynamic
+// LDS block `smem` (Lds<KP, NT>::bytes).
+template <int KP, int NT>
+__device__ __forceinline__ void quantize_tiles(const QArgs& a, int64_t first_tile, int64_t tile_stride,
+                                               unsigned char* smem) {
+  using L = Lds<KP, NT>;
+  constexpr int XS = L::XS;
+  constexpr int DP = L::DP;
+  constexpr int KPG = KP / 4;  // k values per lane group
+  static_assert(KP == NT * 16 && KPG % 4 == 0, "tile shape");
+  float* xr = reinterpret_cast<float*>(smem + L::off_x);
+  uint8_t* code_b = smem + L::off_code;
+  uint8_t* sign_b = smem + L::off_sign;
+  float* npart = reinterpret_cast<float*>(smem + L::off_npart);
+  float* gpart = reinterpret_cast<float*>(smem + L::off_gpart);
+  float* nrm = reinterpret_cast<float*>(smem + L::off_nrm);
+  float* cbk = reinterpret_cast<float*>(smem + L::off_cb);  // [0,32): centroids, [32,64): boundaries
+  int64_t* rows = reinterpret_cast<int64_t*>(smem + L::off_rows);
+  int* flags = reinterpret_cast<int*>(smem + L::off_flags);
+  uint32_t* pk = reinterpret_cast<uint32_t*>(smem + L::off_pk);
+  uint16_t* pk16 = reinterpret_cast<uint16_t*>(smem + L::off_pk);
+  constexpr int PKW = L::PKW;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;  // wave = coordinate tile
+  const int ln = lane & 15;
+  const int lg = lane >> 4;
+  const int d = a.d;
+
+  // Every global load of the prologue and of the first tile is issued before
+  // the first wait, so the kernel pays one memory latency up front.
+  // Centroids of both groups (concatenated), kept in a register until the
+  // tile's LDS stores.
+  float cent_reg = 0.f;
+  {
+    const int ncent = (1 << a.gbits[0]) + (a.n_groups > 1 ? (1 << a.gbits[1]) : 0);
+    cent_reg = a.centroids[tid < ncent ? tid : ncent - 1];
+  }
+
+  // This wave's rows of rot and sketch_rot: B[k][n] = M[16 w + n][k], with k
+  // assigned to steps as in mfma_tiles. The loads are unconditional (indices
+  // clamped into the matrix) so they issue back to back; out-of-range entries
+  // are zeroed afterwards.
+  const int ocoord = w * 16 + ln;  // output coordinate of this lane
+  constexpr bool SKR_LDS = L::SKR_LDS;
+  // For d <= 128 the sketch slice lives in LDS (read once per product), which
+  // leaves the register file to the rotation slice and the tile's values;
+  // larger d keeps both slices in registers.
+  float brot[KPG];
+  float bskr[SKR_LDS ? 1 : KPG];
+  f32x4* skr_lds = reinterpret_cast<f32x4*>(smem + L::off_skr);
+  {
+    float bs[KPG];
+    const int64_t rb = (int64_t)(ocoord < d ? ocoord : d - 1) * d;
+    if (a.m_vec) {
+      // d is a multiple of 4 and the matrices are 16-byte aligned
+#pragma unroll
+      for (int q = 0; q < KPG / 4; ++q) {
+        const int k = 16 * q + 4 * lg;
+        const int kc = k < d ? k : d - 4;
+        const f32x4 r4 = *reinterpret_cast<const f32x4*>(a.rot + rb + kc);
+        const f32x4 s4 = *reinterpret_cast<const f32x4*>(a.skr + rb + kc);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          brot[4 * q + j] = r4[j];
+          bs[4 * q + j] = s4[j];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KPG; ++kk) {
+        const int k = 16 * (kk / 4) + 4 * lg + kk % 4;
+        const int kc = k < d ? k : d - 1;
+        brot[kk] = a.rot[rb + kc];
+        bs[kk] = a.skr[rb + kc];
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < KPG; ++kk) {
+      const bool ok = ocoord < d && 16 * (kk / 4) + 4 * lg + kk % 4 < d;
+      brot[kk] = ok ? brot[kk] : 0.f;
+      bs[kk] = ok ? bs[kk] : 0.f;
+    }
+    if constexpr (SKR_LDS) {
+#pragma unroll
+      for (int q = 0; q < KPG / 4; ++q)
+        skr_lds[(w * (KPG / 4) + q) * 64 + lane] = f32x4{bs[4 * q], bs[4 * q + 1], bs[4 * q + 2], bs[4 * q + 3]};
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KPG; ++kk) bskr[kk] = bs[kk];
+    }
+  }
+  // group of this wave's coordinates (group boundaries are multiples of 16);
+  // everything derived from it is wave-uniform
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int grp = (a.n_groups > 1 && wu * 16 >= a.choff[1]) ? 1 : 0;
+  const int nb = (1 << a.gbits[grp]) - 1;
+  const int coff = a.coff[grp];
+  const int boff = a.boff[grp];
+  const int mg = a.gbits[grp];
+  const int wig = wu - a.choff[grp] / 16;  // wave index within its group
+  // halfword offsets, in a packed token-major row, of this wave's 16 codes
+  // (2 mg bytes) and of its 16 sign bits
+  const int pk_code_h = 2 * a.cwoff[grp] + mg * wig;
+  const int pk_sign_h = 2 * (a.code_words + a.swoff[grp]) + wig;
+  const bool tok = a.fmt == TQ_TOKEN_MAJOR;
+  // decision boundaries of both groups (concatenated), like the centroids
+  float bnd_reg = 0.f;
+  {
+    const int nbt = ((1 << a.gbits[0]) - 1) + (a.n_groups > 1 ? (1 << a.gbits[1]) - 1 : 0);
+    bnd_reg = a.boundaries[tid < nbt ? tid : nbt - 1];
+  }
+
+  for (int64_t tile = first_tile; tile < a.n_tiles; tile += tile_stride) {
+    // Tile = input vectors [v0, v0 + nvalid). With block-owned tiling the
+    // vectors are those of one segment falling in one aligned pair of
+    // blocks, whose first row is rowbase; slot_lo is the first vector's
+    // position in the pair.
+    int64_t v0, rowbase = 0;
+    int nvalid, slot_lo = 0;
+    if (a.blk_owned) {
+      const int64_t sg = tile / a.pairs_per_seg, pr = tile % a.pairs_per_seg;
+      const int o32 = (int)(a.seg_offset % 32);
+      const int64_t rem = a.n_vec - sg * a.seg_len;
+      const int64_t len = rem < a.seg_len ? rem : a.seg_len;
+      const int64_t lo = 64 * pr - o32 > 0 ? 64 * pr - o32 : 0;      // segment-relative
+      const int64_t hi = 64 * pr + 64 - o32 < len ? 64 * pr + 64 - o32 : len;
+      if (hi <= lo) continue;  // uniform across the workgroup
+      v0 = sg * a.seg_len + lo;
+      nvalid = (int)(hi - lo);
+      rowbase = sg * a.seg_stride + (a.seg_offset - o32) + 64 * pr;
+      slot_lo = (int)(lo + o32 - 64 * pr);
+    } else {
+      v0 = tile * QT;
+      nvalid = (int)((a.n_vec - v0) < QT ? (a.n_vec - v0) : QT);
+    }
+
+    // ---- stage the input tile (fp32, zero padded) and destination rows ----
+    // All of a thread's loads are issued before any LDS store, so the tile
+    // costs one memory latency rather than one per element.
+    if (tok && a.pk_zero)
+      for (int e = tid; e < QT * PKW; e += NT * 64) pk[e] = 0u;
+    // (destination row of vector tid: loaded now, stored to LDS with the tile)
+    int64_t my_row = -1;
+    if (tid < nvalid) my_row = a.blk_owned ? rowbase + slot_lo + tid : dest_row(a, v0 + tid);
+    if (a.x_vec) {
+      // rows are 16-byte aligned and d is a multiple of the vector width:
+      // 16-byte loads, 8 bf16 or 4 fp32 values each
+      if (a.x_bf16) {
+        constexpr int CPR = KP / 8, NCH = QT * CPR / (NT * 64);  // chunks per row, per thread
+        u32x4 buf[NCH];
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          const int c = tid + i * NT * 64, v = c / CPR, k = (c % CPR) * 8;
+          buf[i] = (v < nvalid && k < d)
+                       ? *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.x) +
+                                                         (v0 + v) * a.x_stride + k)
+                       : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          const int c = tid + i * NT * 64, v = c / CPR, k = (c % CPR) * 8;
+          f32x4 lo, hi;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t w = buf[i][e];
+            const float f0 = __uint_as_float(w << 16), f1 = __uint_as_float(w & 0xFFFF0000u);
+            if (e < 2) {
+              lo[2 * e] = f0;
+              lo[2 * e + 1] = f1;
+            } else {
+              hi[2 * e - 4] = f0;
+              hi[2 * e - 3] = f1;
+            }
+          }
+          *reinterpret_cast<f32x4*>(xr + v * XS + k) = lo;
+          *reinterpret_cast<f32x4*>(xr + v * XS + k + 4) = hi;
+        }
+      } else {
+        constexpr int CPR = KP / 4, NCH = QT * CPR / (NT * 64);
+        f32x4 buf[NCH];
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          const int c = tid + i * NT * 64, v = c / CPR, k = (c % CPR) * 4;
+          buf[i] = (v < nvalid && k < d)
+                       ? *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(a.x) +
+                                                         (v0 + v) * a.x_stride + k)
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          const int c = tid + i * NT * 64, v = c / CPR, k = (c % CPR) * 4;
+          *reinterpret_cast<f32x4*>(xr + v * XS + k) = buf[i];
+        }
+      }
+    } else {
+      constexpr int PER = QT * KP / (NT * 64);
+      float buf[PER];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int e = tid + i * NT * 64, v = e / KP, k = e % KP;
+        float val = 0.f;
+        if (v < nvalid && k < d) {
+          const int64_t off = (v0 + v) * a.x_stride + k;
+          val = a.x_bf16 ? __uint_as_float(((uint32_t) reinterpret_cast<const uint16_t*>(a.x)[off]) << 16)
+                         : reinterpret_cast<const float*>(a.x)[off];
+        }
+        buf[i] = val;
+      }
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int e = tid + i * NT * 64;
+        xr[(e / KP) * XS + e % KP] = buf[i];
+      }
+    }
+    if (tid < QT) rows[tid] = (my_row < 0 || my_row >= a.n_rows) ? -1 : my_row;
+    if (tid < 32) {
+      cbk[tid] = cent_reg;
+      cbk[32 + tid] = bnd_reg;
+    }
+    __syncthreads();
+
+    // ---- y = rot x (fp32 MFMA), four 16-vector tiles ----
+    // (a tile with at most 16 vectors, e.g. an append, runs only its first
+    // 16-vector tile)
+    const int n_mt = (nvalid + 15) / 16;
+    f32x4 yacc[4];
+    if (n_mt == 1)
+      mfma_tiles<1, KPG, XS>(xr, brot, ln, lg, yacc);
+    else
+      mfma_tiles<4, KPG, XS>(xr, brot, ln, lg, yacc);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      if (mt >= n_mt) break;
+      // lane (ln, lg) holds y[vector 16 mt + 4 lg + i][coordinate 16 w + ln]
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float s = yacc[mt][i] * yacc[mt][i];
+        s = row16_sum(s);
+        if (ln == 0) npart[w * QT + mt * 16 + lg * 4 + i] = s;
+      }
+    }
+    __syncthreads();
+    // group norms n_g = sqrt(sum of the partial sums of the group's waves)
+    if (tid < QT * a.n_groups) {
+      const int g = tid / QT, v = tid % QT;
+      const int w0 = a.choff[g] / 16, w1 = (a.choff[g] + a.gdim[g] + 15) / 16;
+      float s = 0.f;
+      for (int ww = w0; ww < w1; ++ww) s += npart[ww * QT + v];
+      nrm[g * QT + v] = sqrtf(s);
+    }
+    __syncthreads();
+
+    // ---- cells, residual in the rotated domain, residual norm partials ----
+    // (this group's boundaries, wave-uniform LDS reads; +inf past the last)
+    float tb[15];
+#pragma unroll
+    for (int k = 0; k < 15; ++k)
+      tb[k] = k < nb ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(cbk[32 + boff + k])))
+                     : INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      if (mt >= n_mt) break;  // tiles past the last vector: their rows stay zero
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int v = mt * 16 + lg * 4 + i;
+        const float y = yacc[mt][i];
+        const float n = nrm[grp * QT + v];
+        int idx;
+        float r;
+        if (n > 0.f) {
+          // cell = number of boundaries below u (the +inf entries past the
+          // group's count never are); fully unrolled so tb stays in SGPRs
+          const float u = y * __builtin_amdgcn_rcpf(n);
+          idx = 0;
+#pragma unroll
+          for (int k = 0; k < 15; ++k) idx += u > tb[k] ? 1 : 0;
+          r = fmaf(-n, cbk[coff + idx], y);
+        } else {
+          idx = (nb + 1) / 2 - 1;
+          r = 0.f;
+        }
+        if (ocoord >= d) {
+          r = 0.f;
+          idx = 0;
+        }
+        code_b[v * DP + ocoord] = (uint8_t)idx;
+        if (tok) {
+          // the row's 16 codes of this wave, OR-combined across the row of
+          // lanes, are 2 mg bytes of the packed record
+          const uint64_t f = (uint64_t)(uint32_t)idx << (mg * ln);
+          const uint32_t lo = row16_or((uint32_t)f);
+          const uint32_t hi = mg > 2 ? row16_or((uint32_t)(f >> 32)) : 0u;
+          if (ln == 0)
+            for (int k = 0; k < mg; ++k)
+              pk16[v * 2 * PKW + pk_code_h + k] = (uint16_t)((k < 2 ? lo : hi) >> (16 * (k & 1)));
+        }
+        xr[v * XS + ocoord] = r;  // A operand of the sketch product (k = rotated coordinate)
+        float s = r * r;
+        s = row16_sum(s);
+        if (ln == 0) gpart[w * QT + v] = s;
+      }
+    }
+    // (every k < KP is a coordinate owned by some wave, so the residual tile
+    // is fully written, with zeros past d)
+    __syncthreads();
+
+    // ---- s = (S Pi^T) r (fp32 MFMA); sign bit = [s >= 0] ----
+    f32x4 sacc[4];
+    if constexpr (SKR_LDS) {
+      if (n_mt == 1)
+        mfma_tiles_lds<1, KPG, XS>(xr, skr_lds + w * (KPG / 4) * 64 + lane, ln, lg, sacc);
+      else
+        mfma_tiles_lds<4, KPG, XS>(xr, skr_lds + w * (KPG / 4) * 64 + lane, ln, lg, sacc);
+    } else {
+      if (n_mt == 1)
+        mfma_tiles<1, KPG, XS>(xr, bskr, ln, lg, sacc);
+      else
+        mfma_tiles<4, KPG, XS>(xr, bskr, ln, lg, sacc);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      if (mt >= n_mt) break;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int v = mt * 16 + lg * 4 + i;
+        const bool bit = sacc[mt][i] >= 0.f && ocoord < d;
+        sign_b[v * DP + ocoord] = bit ? 1 : 0;
+        // the wave's 16 channels for vector 16 mt + 4 q + i are ballot bits [16 q, 16 q + 16)
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(bit);
+        if (tok && lane < 4)
+          pk16[(mt * 16 + lane * 4 + i) * 2 * PKW + pk_sign_h] = (uint16_t)(bal >> (16 * lane));
+      }
+    }
+    // full aligned 32-row blocks of this tile (block records only)
+    if (tid < 2) {
+      int full = 0;
+      if (a.fmt == TQ_BLOCK32) {
+        const int base = tid * 32;
+        const int64_t r0 = rows[base];
+        full = (base + 32 <= nvalid) && r0 >= 0 && (r0 % 32 == 0);
+        for (int t = 1; t < 32 && full; ++t) full = rows[base + t] == r0 + t;
+      }
+      flags[tid] = full;
+    }
+    __syncthreads();
+
+    // ---- pack and store ----
+    // norms (both formats): (n_g, gamma_g) per row
+    if (tid < QT * a.n_groups) {
+      const int g = tid / QT, v = tid % QT;
+      const int64_t row = rows[v];
+      if (row >= 0) {
+        const int w0 = a.choff[g] / 16, w1 = (a.choff[g] + a.gdim[g] + 15) / 16;
+        float s = 0.f;
+        for (int ww = w0; ww < w1; ++ww) s += gpart[ww * QT + v];
+        a.norms[row * (2 * a.n_groups) + 2 * g] = nrm[g * QT + v];
+        a.norms[row * (2 * a.n_groups) + 2 * g + 1] = sqrtf(s);
+      }
+    }
+    if (tok) {
+      // packed records: code words then sign words, copied word by word
+      const int cw = a.code_words, sw = a.sign_words, rw = cw + sw;
+      for (int e = tid; e < QT * rw; e += NT * 64) {
+        const int v = e / rw, wd = e % rw;
+        const int64_t row = rows[v];
+        if (row < 0) continue;
+        if (wd < cw)
+          a.codes[row * cw + wd] = pk[v * PKW + wd];
+        else
+          a.signs[row * sw + wd - cw] = pk[v * PKW + wd];
+      }
+    } else if (a.blk_owned) {
+      // block records, tile = one aligned pair of blocks owned by this
+      // workgroup: each word is assembled from the tile's fields; a word
+      // that also holds rows outside the tile is read, merged and written
+      // back (no other workgroup writes these blocks in this call)
+      for (int h = 0; h < 2; ++h) {
+        const int vlo = slot_lo > 32 * h ? slot_lo : 32 * h;
+        const int vhi = slot_lo + nvalid < 32 * h + 32 ? slot_lo + nvalid : 32 * h + 32;
+        if (vhi <= vlo) continue;
+        const int64_t blk = rowbase / 32 + h;
+        const int bcw = a.blk_code_words;
+        for (int wd = tid; wd < bcw; wd += NT * 64) {
+          const int g = (a.n_groups > 1 && wd >= a.bcwoff[1]) ? 1 : 0;
+          const int m = a.gbits[g], dg = a.gdim[g];
+          const int lw = wd - a.bcwoff[g];
+          const int b0 = 32 * lw;
+          const int u0 = b0 / (8 * m), u1 = (b0 + 31) / (8 * m);
+          const uint64_t fm = (1u << m) - 1u;
+          uint64_t word = 0, mask = 0;
+          for (int u = u0; u <= u1 && u < 4 * dg; ++u) {
+            const int o = u / dg, j = u % dg;
+            uint64_t unit = 0, umask = 0;
+            for (int sl = 0; sl < 8; ++sl) {
+              const int t = 32 * h + 8 * o + sl;
+              if (t < vlo || t >= vhi) continue;
+              unit |= (uint64_t)code_b[(t - slot_lo) * DP + a.choff[g] + j] << (m * sl);
+              umask |= fm << (m * sl);
+            }
+            const int pos = 8 * m * u - b0;
+            word |= pos >= 0 ? unit << pos : unit >> (-pos);
+            mask |= pos >= 0 ? umask << pos : umask >> (-pos);
+          }
+          uint32_t* dst = a.codes + blk * bcw + wd;
+          const uint32_t m32 = (uint32_t)mask;
+          if (m32 == 0xFFFFFFFFu)
+            *dst = (uint32_t)word;
+          else if (m32 != 0)
+            *dst = (*dst & ~m32) | ((uint32_t)word & m32);
+        }
+        const int bsw = a.blk_sign_words;
+        for (int wd = tid; wd < bsw; wd += NT * 64) {
+          const int g = (a.n_groups > 1 && wd >= a.bswoff[1]) ? 1 : 0;
+          const int dg = a.gdim[g];
+          const int lw = wd - a.bswoff[g];
+          uint32_t word = 0, mask = 0;
+          for (int q = 0; q < 4; ++q) {
+            const int u = 4 * lw + q;
+            const int o = u / dg, j = u % dg;
+            for (int sl = 0; sl < 8; ++sl) {
+              const int t = 32 * h + 8 * o + sl;
+              if (t < vlo || t >= vhi) continue;
+              word |= (uint32_t)sign_b[(t - slot_lo) * DP + a.choff[g] + j] << (8 * q + sl);
+              mask |= 1u << (8 * q + sl);
+            }
+          }
+          uint32_t* dst = a.signs + blk * bsw + wd;
+          if (mask == 0xFFFFFFFFu)
+            *dst = word;
+          else if (mask != 0)
+            *dst = (*dst & ~mask) | (word & mask);
+        }
+      }
+    } else {
+      // block records: whole blocks are written word by word
+      for (int h = 0; h < 2; ++h) {
+        if (!flags[h]) continue;
+        const int64_t blk = rows[h * 32] / 32;
+        const int bcw = a.blk_code_words;
+        for (int wd = tid; wd < bcw; wd += NT * 64) {
+          const int g = (a.n_groups > 1 && wd >= a.bcwoff[1]) ? 1 : 0;
+          const int m = a.gbits[g], dg = a.gdim[g];
+          const int lw = wd - a.bcwoff[g];
+          const int b0 = 32 * lw;
+          const int u0 = b0 / (8 * m), u1 = (b0 + 31) / (8 * m);
+          uint64_t word = 0;
+          for (int u = u0; u <= u1 && u < 4 * dg; ++u) {
+            const int o = u / dg, j = u % dg;
+            uint64_t unit = 0;
+            for (int s = 0; s < 8; ++s)
+              unit |= (uint64_t)code_b[(h * 32 + 8 * o + s) * DP + a.choff[g] + j] << (m * s);
+            const int pos = 8 * m * u - b0;
+            if (pos >= 0)
+              word |= unit << pos;
+            else
+              word |= unit >> (-pos);
+          }
+          a.codes[blk * bcw + wd] = (uint32_t)word;
+        }
+        const int bsw = a.blk_sign_words;
+        for (int wd = tid; wd < bsw; wd += NT * 64) {
+          const int g = (a.n_groups > 1 && wd >= a.bswoff[1]) ? 1 : 0;
+          const int dg = a.gdim[g];
+          const int lw = wd - a.bswoff[g];
+          uint32_t word = 0;
+          for (int q = 0; q < 4; ++q) {
+            const int u = 4 * lw + q;
+            const int o = u / dg, j = u % dg;
+            uint32_t unit = 0;
+            for (int s = 0; s < 8; ++s)
+              unit |= (uint32_t)sign_b[(h * 32 + 8 * o + s) * DP + a.choff[g] + j] << s;
+            word |= unit << (8 * q);
+          }
+          a.signs[blk * bsw + wd] = word;
+        }
+      }
+      // rows outside full blocks: update their bits in place
+      for (int e = tid; e < QT * d; e += NT * 64) {
+        const int v = e / d, ch = e % d;
+        if (flags[v / 32]) continue;
+        const int64_t row = rows[v];
+        if (row < 0) continue;
+        const int g = (a.n_groups > 1 && ch >= a.choff[1]) ? 1 : 0;
+        const int m = a.gbits[g], dg = a.gdim[g];
+        const int j = ch - a.choff[g];
+        const int64_t blk = row / 32;
+        const int t = (int)(row % 32), o = t / 8, s = t % 8;
+        const uint32_t code = code_b[v * DP + ch];
+        const int pos = 8 * m * (o * dg + j) + m * s;
+        uint32_t* base = a.codes + blk * a.blk_code_words + a.bcwoff[g];
+        const int wi = pos / 32, bi = pos % 32;
+        const uint32_t fmask = (1u << m) - 1u;
+        atomicAnd(base + wi, ~(fmask << bi));
+        atomicOr(base + wi, code << bi);
+        if (bi + m > 32) {
+          const int spill = bi + m - 32;
+          atomicAnd(base + wi + 1, ~((1u << spill) - 1u));
+          atomicOr(base + wi + 1, code >> (32 - bi));
+        }
+        const int spos = 8 * (o * dg + j) + s;
+        uint32_t* sbase = a.signs + blk * a.blk_sign_words + a.bswoff[g];
+        const uint32_t sbit = sign_b[v * DP + ch];
+        atomicAnd(sbase + spos / 32, ~(1u << (spos % 32)));
+        atomicOr(sbase + spos / 32, sbit << (spos % 32));
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Validates the arguments of one quantize call and fills its kernel
+// arguments. Returns TQ_OK with *empty = true for n_vec == 0.
+inline tq_status make_qargs(const tq_quantizer* qz, tq_format fmt, const void* x, tq_dtype x_dtype,
+                            int64_t n_vec, int64_t x_row_stride, const tq_rows* rows,
+                            const tq_cache* cache, QArgs* out, bool* empty) {
+  *empty = false;
+  if (!tq::quantizer_pointers_valid(qz) || !rows || !cache) return TQ_ERR_INVALID;
+  if (fmt != TQ_TOKEN_MAJOR && fmt != TQ_BLOCK32) return TQ_ERR_INVALID;
+  if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return TQ_ERR_INVALID;
+  const tq_layout& l = qz->layout;
+  if (n_vec < 0 || x_row_stride < l.d) return TQ_ERR_INVALID;
+  if (!cache->codes || !cache->signs || !cache->norms || cache->n_rows < 0) return TQ_ERR_INVALID;
+  if (fmt == TQ_BLOCK32 && cache->n_rows % 32 != 0) return TQ_ERR_INVALID;
+  if (!rows->dst_rows) {
+    if (rows->seg_len < 1 || rows->seg_stride < 0 || rows->seg_offset < 0) return TQ_ERR_INVALID;
+    if (n_vec > 0) {
+      // rows grow with the segment index when segments do not overlap, so the
+      // largest row is the last vector's
+      const int64_t last = n_vec - 1;
+      const int64_t nseg = last / rows->seg_len;
+      if (nseg > 0 && rows->seg_stride < rows->seg_len) return TQ_ERR_INVALID;  // overlapping rows
+      const int64_t hi = nseg * rows->seg_stride + rows->seg_offset + last % rows->seg_len;
+      if (hi >= cache->n_rows) return TQ_ERR_INVALID;
+    }
+  }
+  const tq::GroupGeom geo = tq::geometry(&l);
+  if (l.n_groups == 2 && l.group_dim[0] % 16 != 0) return TQ_ERR_UNSUPPORTED;
+  if (fmt == TQ_BLOCK32)
+    for (int g = 0; g < l.n_groups; ++g)
+      if (l.group_dim[g] % 8 != 0) return TQ_ERR_UNSUPPORTED;
+  if (n_vec == 0) {
+    *empty = true;
+    return TQ_OK;
+  }
+  if (!x || reinterpret_cast<uintptr_t>(x) % 4 != 0) return TQ_ERR_INVALID;
+
+  QArgs& a = *out;
+  a = QArgs{};
+  a.x = x;
+  a.n_vec = n_vec;
+  a.x_stride = x_row_stride;
+  a.x_bf16 = x_dtype == TQ_BF16;
+  {
+    const int64_t esz = a.x_bf16 ? 2 : 4, per = 16 / esz;
+    a.x_vec = reinterpret_cast<uintptr_t>(x) % 16 == 0 && (x_row_stride * esz) % 16 == 0 && l.d % per == 0;
+  }
+  a.rot = qz->rot;
+  a.skr = qz->sketch_rot;
+  a.m_vec = l.d % 4 == 0 && reinterpret_cast<uintptr_t>(qz->rot) % 16 == 0 &&
+            reinterpret_cast<uintptr_t>(qz->sketch_rot) % 16 == 0;
+  a.centroids = qz->centroids;
+  a.boundaries = qz->boundaries;
+  a.d = l.d;
+  a.n_groups = l.n_groups;
+  for (int g = 0; g < 2; ++g) {
+    a.gdim[g] = geo.dim[g];
+    a.gbits[g] = geo.bits[g];
+    a.choff[g] = geo.ch_off[g];
+    a.cwoff[g] = geo.code_word_off[g];
+    a.swoff[g] = geo.sign_word_off[g];
+    a.bcwoff[g] = geo.blk_code_off[g];
+    a.bswoff[g] = geo.blk_sign_off[g];
+    a.coff[g] = geo.centroid_off[g];
+    a.boff[g] = geo.boundary_off[g];
+  }
+  if (l.n_groups == 1) a.choff[1] = 1 << 30;  // never reached
+  a.code_words = geo.info.code_words;
+  a.sign_words = geo.info.sign_words;
+  a.blk_code_words = geo.info.block_code_words;
+  a.blk_sign_words = geo.info.block_sign_words;
+  a.fmt = fmt;
+  a.dst_rows = rows->dst_rows;
+  a.seg_len = rows->seg_len < 1 ? 1 : rows->seg_len;
+  a.seg_stride = rows->seg_stride;
+  a.seg_offset = rows->seg_offset;
+  a.n_rows = cache->n_rows;
+  a.pk_zero = 0;
+  for (int g = 0; g < l.n_groups; ++g) {
+    const int waves = (geo.dim[g] + 15) / 16;
+    if ((waves * geo.bits[g]) % 2 != 0 || waves % 2 != 0) a.pk_zero = 1;
+  }
+  a.blk_owned = fmt == TQ_BLOCK32 && !rows->dst_rows &&
+                (n_vec <= rows->seg_len || rows->seg_stride % 32 == 0);
+  if (a.blk_owned) {
+    const int64_t n_seg = (n_vec + a.seg_len - 1) / a.seg_len;
+    a.pairs_per_seg = (a.seg_offset % 32 + a.seg_len + 63) / 64;
+    a.n_tiles = n_seg * a.pairs_per_seg;
+  } else {
+    a.pairs_per_seg = 1;
+    a.n_tiles = (n_vec + QT - 1) / QT;
+  }
+  a.codes = cache->codes;
+  a.signs = cache->signs;
+  a.norms = cache->norms;
+  return TQ_OK;
+}
+
+// Kernel shape for a dimension: KP = d rounded up to 16, NT = KP / 16 waves.
+inline int quantize_kp(int d) {
+  const int dpad = (d + 15) / 16;
+  return dpad <= 4 ? 64 : dpad <= 8 ? 128 : dpad <= 13 ? 208 : 256;
+}
+
+}  // namespace tqq

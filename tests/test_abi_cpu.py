@@ -30,7 +30,7 @@ def tq():
 def test_header_symbols_exported(tq):
     text = open(HEADER).read()
     declared = sorted(set(re.findall(r"^\s*(?:tq_status|int|const char\*)\s+(tq_\w+)\s*\(", text, re.M)))
-    assert len(declared) == 9
+    assert len(declared) == 10
     lib = C.CDLL(tq.LIB_PATH)
     for name in declared:
         assert hasattr(lib, name), name
@@ -193,3 +193,34 @@ def test_phase_mask_validation(tq):
     # a valid mask reaches the workspace check
     assert lib.tq_attn_decode_phases(2, C.byref(kq), C.byref(vq), C.byref(shape), FAKE, 1, C.byref(kc),
                                      C.byref(vc), None, FAKE, FAKE, 10, None) == tq.TQ_ERR_WORKSPACE
+
+
+def test_decode_append_validation(tq):
+    # every error is found before any launch (no GPU here)
+    lib = tq.lib()
+    kq, vq = _fake_quantizer(tq), _fake_quantizer(tq)
+    kc, vc = _fake_cache(tq, 8 * 1024), _fake_cache(tq, 8 * 1024)
+    shape = tq.decode_shape(1, 32, 8, 1000, 1024, 0.088)
+    need = C.c_size_t()
+    assert lib.tq_attn_decode_workspace_bytes(C.byref(kq), C.byref(vq), C.byref(shape), C.byref(need)) == 0
+
+    def app(n_vec=8, stride=128, dtype=1, x=FAKE, seg=(1, 1024, 999)):
+        a = tq.tq_append()
+        a.x, a.dtype, a.n_vec, a.x_row_stride = x, dtype, n_vec, stride
+        a.rows.dst_rows = None
+        a.rows.seg_len, a.rows.seg_stride, a.rows.seg_offset = seg
+        return a
+
+    def call(k_new, v_new, vq_=C.byref(vq), wsb=need.value):
+        return lib.tq_attn_decode_append(C.byref(kq), vq_, C.byref(shape),
+                                         C.byref(k_new) if k_new is not None else None,
+                                         C.byref(v_new) if v_new is not None else None, FAKE, 1,
+                                         C.byref(kc), C.byref(vc), None, FAKE, FAKE, wsb, None)
+
+    assert call(app(), app(), wsb=need.value - 1) == tq.TQ_ERR_WORKSPACE  # decode checks first
+    assert call(app(dtype=7), app()) == tq.TQ_ERR_INVALID                  # bad K dtype
+    assert call(app(), app(stride=64)) == tq.TQ_ERR_INVALID                # V row stride < d
+    assert call(app(seg=(1, 1024, 1024)), app()) == tq.TQ_ERR_INVALID      # K rows past the cache
+    assert call(app(n_vec=-1), None) == tq.TQ_ERR_INVALID
+    assert lib.tq_attn_decode_append(C.byref(kq), None, C.byref(shape), None, C.byref(app()), FAKE, 1,
+                                     C.byref(kc), None, FAKE, None, FAKE, need.value, None) == tq.TQ_ERR_INVALID
