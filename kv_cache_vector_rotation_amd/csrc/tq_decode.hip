@@ -721,47 +721,63 @@ __global__ __launch_bounds__(256) void prep_kernel(tqp::PrepArgs p) {
 // ---------------------------------------------------------------------------
 constexpr int kMaxSplit = 1024;
 
+// 1024 threads per head: the split sums and the back-transform are each cut
+// four ways across thread groups and finished through LDS, so every thread
+// has only a few independent loads in flight.
+constexpr int kCombThreads = 1024;
+
 template <int D>
-__global__ __launch_bounds__(2 * D) void combine_kernel(const float* part, int n_split,
-                                                        const float* rot, const float* sketch,
-                                                        int group_dim0, float* out) {
+__global__ __launch_bounds__(kCombThreads) void combine_kernel(const float* part, int n_split,
+                                                               const float* rot, const float* sketch,
+                                                               int group_dim0, float* out) {
+  constexpr int NW = kCombThreads / 64, NG = kCombThreads / (2 * D);  // waves, groups
+  constexpr int PS = 2 + 2 * D;                                      // floats per partial
   __shared__ float s_w[kMaxSplit];
+  __shared__ float s_part[NG][2 * D];
   __shared__ float s_acc[2 * D];
-  __shared__ float s_o[2 * D];
-  __shared__ float s_red[2 * D / 64];
+  __shared__ float s_red[NW];
   const int head = blockIdx.x;
   const int t = threadIdx.x;
   const int lane = t & 63, wv = t >> 6;
-  constexpr int NW = 2 * D / 64;
-  const float* P = part + (int64_t)head * n_split * (2 + 2 * D);
-  // max over splits
+  const float* P = part + (int64_t)head * n_split * PS;
+  // max over splits (log2 domain)
   float mx = -INFINITY;
-  for (int s = t; s < n_split; s += 2 * D) mx = fmaxf(mx, P[(int64_t)s * (2 + 2 * D)]);
+  for (int s = t; s < n_split; s += kCombThreads) mx = fmaxf(mx, P[(int64_t)s * PS]);
   for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
   if (lane == 0) s_red[wv] = mx;
   __syncthreads();
   float M = s_red[0];
+#pragma unroll
   for (int w = 1; w < NW; ++w) M = fmaxf(M, s_red[w]);
   __syncthreads();
-  // weights and the total sum
+  // split weights and the total sum
   float lsum = 0.f;
-  for (int s = t; s < n_split; s += 2 * D) {
-    const float ms = P[(int64_t)s * (2 + 2 * D)];
+  for (int s = t; s < n_split; s += kCombThreads) {
+    const float ms = P[(int64_t)s * PS];
     const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
     s_w[s] = w;
-    lsum += w * P[(int64_t)s * (2 + 2 * D) + 1];
+    lsum += w * P[(int64_t)s * PS + 1];
   }
   for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o, 64);
   if (lane == 0) s_red[wv] = lsum;
   __syncthreads();
   float L = 0.f;
+#pragma unroll
   for (int w = 0; w < NW; ++w) L += s_red[w];
-  // merged accumulators; alpha_g is applied to the sketch half here
+  // merged accumulators: group g sums the splits s = g (mod NG)
   {
+    const int c = t % (2 * D), g = t / (2 * D);
     float acc = 0.f;
-#pragma unroll 16
-    for (int s = 0; s < n_split; ++s) acc = fmaf(s_w[s], P[(int64_t)s * (2 + 2 * D) + 2 + t], acc);
-    if (t >= D) {
+#pragma unroll 8
+    for (int s = g; s < n_split; s += NG) acc = fmaf(s_w[s], P[(int64_t)s * PS + 2 + c], acc);
+    s_part[g][c] = acc;
+  }
+  __syncthreads();
+  if (t < 2 * D) {
+    float acc = 0.f;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) acc += s_part[g][t];
+    if (t >= D) {  // alpha_g on the sketch half
       const int j = t - D;
       const int dg = j < group_dim0 ? group_dim0 : D - group_dim0;
       acc *= 1.2533141373155003f / (float)dg;
@@ -769,18 +785,27 @@ __global__ __launch_bounds__(2 * D) void combine_kernel(const float* part, int n
     s_acc[t] = acc;
   }
   __syncthreads();
-  // back-transform: o_half[i] = sum_j M_half[j][i] acc_half[j]
+  // back-transform: out[i] = sum_j rot[j][i] acc_rot[j] + sum_j sketch[j][i] acc_sk[j];
+  // the 2 NG groups of D threads are (half, part of the j range) pairs
   {
-    const int half = t / D, i = t % D;
+    const int i = t % D, hq = t / D;  // hq = half * NG + part, 0 <= hq < 2 NG
+    const int half = hq / NG, qtr = hq % NG;
+    constexpr int JN = D / NG;
     const float* mat = half == 0 ? rot : sketch;
     const float* av = s_acc + half * D;
     float o = 0.f;
 #pragma unroll 16
-    for (int j = 0; j < D; ++j) o = fmaf(mat[(int64_t)j * D + i], av[j], o);
-    s_o[t] = o;
+    for (int j = qtr * JN; j < qtr * JN + JN; ++j) o = fmaf(mat[(int64_t)j * D + i], av[j], o);
+    __syncthreads();  // s_part is reused
+    s_part[hq / 2][(hq % 2) * D + i] = o;
   }
   __syncthreads();
-  if (t < D) out[(int64_t)head * D + t] = (s_o[t] + s_o[D + t]) / L;
+  if (t < D) {
+    float o = 0.f;
+#pragma unroll
+    for (int k = 0; k < NG * 2; ++k) o += s_part[k / 2][(k % 2) * D + t];
+    out[(int64_t)head * D + t] = o / L;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1010,7 +1035,7 @@ tq_status run_phases(const Plan& pl, unsigned phases, hipStream_t st) {
   }
   if (pl.with_v && (phases & TQ_PHASE_COMBINE)) {
     (void)hipGetLastError();  // a launch error is reported below, not an older one
-    hipLaunchKernelGGL((combine_kernel<D>), dim3(pl.n_heads), dim3(2 * D), 0, st, pl.a.part, pl.a.n_split,
+    hipLaunchKernelGGL((combine_kernel<D>), dim3(pl.n_heads), dim3(kCombThreads), 0, st, pl.a.part, pl.a.n_split,
                        pl.vrot, pl.vsketch, pl.group_dim0, pl.out);
     if (hipGetLastError() != hipSuccess) return TQ_ERR_DEVICE;
   }
