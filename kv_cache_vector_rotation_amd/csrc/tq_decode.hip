@@ -100,6 +100,17 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+// value of another lane of the same 16-lane row (DPP control CTRL; lanes
+// whose source falls outside the row read 0)
+// DPP row move in which a lane whose source lies outside its 16-lane row keeps
+// its own value. Every lane uses the result, so the move is never placed
+// under a lane mask (a DPP read from a masked-off lane returns nothing).
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float v) {
+  const int x = __float_as_int(v);
+  return __int_as_float(__builtin_amdgcn_update_dpp(x, x, CTRL, 0xF, 0xF, false));
+}
+
 // max over the four 16-lane rows (lanes l, l ^ 16, l ^ 32, l ^ 48): swap the
 // 32-lane halves, then odd and even rows, with v_permlane{32,16}_swap
 __device__ __forceinline__ float rows4_max(float v) {
@@ -354,9 +365,15 @@ __device__ __forceinline__ void load_tile(const DArgs& a, int64_t row0, int lane
   }
 }
 
-template <int D, int NG, int M0, int M1, bool WV>
+// HB = query heads per workgroup and MFMA column block: 16, or 4 ("packed",
+// for KV groups of at most 4 query heads). Packed, the 16 MFMA columns hold
+// [q_rot hi | q_rot lo | q_sk | unused] x 4 heads for the logits and
+// [p n | p gamma | 0 | 0] x 4 heads for the V sums, so one accumulator
+// serves all three logit parts and one serves both V parts.
+template <int D, int NG, int M0, int M1, bool WV, int HB>
 __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
   using G = Geo<D, NG, M0, M1>;
+  constexpr bool PK = HB == 4;
   constexpr int NC = G::NC, CPG = G::CPG, NMT = G::NMT, MTPG = G::MTPG, RUN = G::RUN, DG = G::DG;
   constexpr int KT1 = G::KTB[0], VT0 = KT1 + G::KTB[1], VT1 = VT0 + G::VTB[0];
   constexpr int ST = VT1 + G::VTB[1];
@@ -441,21 +458,31 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
   }
 
   // ---- this lane's head and its query operands (B operand: channels x heads) ----
-  const int hloc = hblk * 16 + ln;  // head index within the KV group
+  // packed: column ln = (role, head) with role = ln / 4: 0 q_rot hi / rot
+  // weights, 1 q_rot lo / sketch weights, 2 q_sk, 3 unused
+  const int role = PK ? ln >> 2 : 0;
+  const int hcol = PK ? ln & 3 : ln;  // head of this lane's column within the block
+  const int hloc = hblk * HB + hcol;  // head index within the KV group
   const bool hvalid = hloc < a.group;
   const int hq = kvh * a.group + hloc;
-  u32x4 qr[NC], qrl[NC], qs[NC];
+  u32x4 qr[NC], qrl[PK ? 1 : NC], qs[NC];  // packed: qr = B of the code product, qs = B of the sign product
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int g = c / CPG, cl = c % CPG;
-    if (hvalid) {
-      const _Float16* qp =
-          a.qprep + ((int64_t)b * a.hq + hq) * (3 * D) + g * DG + 8 * CPG * lg + 8 * cl;
-      qr[c] = *reinterpret_cast<const u32x4*>(qp);
-      qrl[c] = *reinterpret_cast<const u32x4*>(qp + D);
-      qs[c] = *reinterpret_cast<const u32x4*>(qp + 2 * D);
+    const _Float16* qp = a.qprep + ((int64_t)b * a.hq + (hvalid ? hq : 0)) * (3 * D) + g * DG + 8 * CPG * lg + 8 * cl;
+    if constexpr (PK) {
+      const u32x4 z{0, 0, 0, 0};
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qp + (role == 0 ? 0 : role == 1 ? D : 2 * D));
+      qr[c] = hvalid && role < 2 ? v : z;
+      qs[c] = hvalid && role == 2 ? v : z;
     } else {
-      qr[c] = qrl[c] = qs[c] = u32x4{0, 0, 0, 0};
+      if (hvalid) {
+        qr[c] = *reinterpret_cast<const u32x4*>(qp);
+        qrl[c] = *reinterpret_cast<const u32x4*>(qp + D);
+        qs[c] = *reinterpret_cast<const u32x4*>(qp + 2 * D);
+      } else {
+        qr[c] = qrl[c] = qs[c] = u32x4{0, 0, 0, 0};
+      }
     }
   }
   __syncthreads();
@@ -463,12 +490,11 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
   const unsigned char* stab = s_tab + ST;
 
   float m_run = -INFINITY, l_run = 0.f;
-  f32x4 acc_r[WV ? NMT : 1], acc_s[WV ? NMT : 1];
+  f32x4 acc_r[WV ? NMT : 1], acc_s[WV && !PK ? NMT : 1];  // packed: acc_r holds both
 #pragma unroll
-  for (int v = 0; v < (WV ? NMT : 1); ++v) {
-    acc_r[v] = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc_s[v] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int v = 0; v < (WV ? NMT : 1); ++v) acc_r[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int v = 0; v < (WV && !PK ? NMT : 1); ++v) acc_s[v] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](const Raw<D, NG, M0, M1>& r, int64_t T0) {
     // tokens past n_ctx (only in the last tile): norms staged as 0 (rows past
@@ -489,11 +515,12 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
     // would also wait for the next tile's loads in flight)
     __builtin_amdgcn_wave_barrier();
     // ---------------- K: logits ----------------
-    f32x4 lr[2][NG], lrl[2][NG], ls[2][NG];
+    f32x4 lr[2][NG], lrl[PK ? 1 : 2][NG], ls[PK ? 1 : 2][NG];  // packed: lr holds all three parts
     auto k_group = [&](auto gc, int tau) {
       constexpr int g = decltype(gc)::value;
       constexpr int M = G::MB[g];
-      lr[tau][g] = lrl[tau][g] = ls[tau][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+      lr[tau][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (!PK) lrl[tau][g] = ls[tau][g] = f32x4{0.f, 0.f, 0.f, 0.f};
       // the lane's K code bits of this group start at bit (KB lg) mod 32 of its words
       uint32_t w[G::KNW[g] + 1];
       const int sh = (G::KB[g] * lg) & 31;
@@ -513,9 +540,14 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
         const u32x4 az = signs8((sword >> (8 * cl)) & 0xFFu, stab, off8);
         // (s c) q = (s c)16 (q_hi + 2^-11 q_lo'): products exact, fp32 sums;
         // 1 / s is applied with the token's norm
-        lr[tau][g] = mfma16(ak, qr[c], lr[tau][g]);
-        lrl[tau][g] = mfma16(ak, qrl[c], lrl[tau][g]);
-        ls[tau][g] = mfma16(az, qs[c], ls[tau][g]);
+        if constexpr (PK) {
+          lr[tau][g] = mfma16(ak, qr[c], lr[tau][g]);
+          lr[tau][g] = mfma16(az, qs[c], lr[tau][g]);
+        } else {
+          lr[tau][g] = mfma16(ak, qr[c], lr[tau][g]);
+          lrl[tau][g] = mfma16(ak, qrl[c], lrl[tau][g]);
+          ls[tau][g] = mfma16(az, qs[c], ls[tau][g]);
+        }
       }
     };
 #pragma unroll
@@ -535,9 +567,19 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
       // sketch part, so this is the logit in the log2 domain)
       float s = 0.f;
 #pragma unroll
-      for (int g = 0; g < NG; ++g)
-        s += kn[j][2 * g] * fmaf(kLoInv, lrl[tau][g][i], lr[tau][g][i]) + kn[j][2 * g + 1] * ls[tau][g][i];
-      if (a.logits && hvalid && (full || tok0 + j < N))
+      for (int g = 0; g < NG; ++g) {
+        if constexpr (PK) {
+          // this lane's column is q_rot hi; q_rot lo and q_sk are 4 and 8 lanes up
+          const float v = lr[tau][g][i];
+          const float vl = dpp_row<0x104>(v), vs = dpp_row<0x108>(v);  // row_shl:4, row_shl:8
+          s += kn[j][2 * g] * fmaf(kLoInv, vl, v) + kn[j][2 * g + 1] * vs;
+        } else {
+          s += kn[j][2 * g] * fmaf(kLoInv, lrl[tau][g][i], lr[tau][g][i]) + kn[j][2 * g + 1] * ls[tau][g][i];
+        }
+      }
+      // (packed: only the role-0 columns are logits; the other columns carry
+      // finite values that no result uses)
+      if (a.logits && hvalid && role == 0 && (full || tok0 + j < N))
         a.logits[((int64_t)b * a.hq + hq) * N + tok0 + j] = s * kLn2;
       l2[j] = s;
     }
@@ -560,10 +602,18 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
         // some head's maximum moved: rescale (factor 1 for the others)
         const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= corr;
+        if constexpr (PK) {
+          // the sketch column of a head (role 1) takes its head's factor
+          // from 4 lanes down; the role 2 and 3 columns are zero
+          const float cc = dpp_row<0x114>(corr);  // row_shr:4
 #pragma unroll
-        for (int v = 0; v < NMT; ++v) {
-          acc_r[v] *= corr;
-          acc_s[v] *= corr;
+          for (int v = 0; v < NMT; ++v) acc_r[v] *= cc;
+        } else {
+#pragma unroll
+          for (int v = 0; v < NMT; ++v) {
+            acc_r[v] *= corr;
+            acc_s[v] *= corr;
+          }
         }
         m_run = m_new;
       }
@@ -578,15 +628,34 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
       float vn[8][2 * NG];
       load_norms<NG>(&s_nrm[wv][1][8 * lg * 2 * NG], vn);
       u32x4 pr[NG], pz[NG];
+      if constexpr (PK) {
+        // column role 0 carries p n (code product), role 1 carries p gamma of
+        // the head 4 lanes down (sign product); the other columns are 0
+        float pp[8];
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
+        for (int j = 0; j < 8; ++j) pp[j] = dpp_row<0x114>(p[j]);  // row_shr:4; role 0 keeps its own
+        const u32x4 z{0, 0, 0, 0};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int j0 = 2 * q, j1 = 2 * q + 1;
-          // (alpha_g is applied once per head in the combine; past n_ctx p = 0
-          // and the staged norms are 0)
-          pr[g][q] = h2bits(p[j0] * vn[j0][2 * g], p[j1] * vn[j1][2 * g]);
-          pz[g][q] = h2bits(p[j0] * vn[j0][2 * g + 1], p[j1] * vn[j1][2 * g + 1]);
+        for (int g = 0; g < NG; ++g) {
+          u32x4 w;
+          const int sel = role == 1 ? 1 : 0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            w[q] = h2bits(pp[2 * q] * vn[2 * q][2 * g + sel], pp[2 * q + 1] * vn[2 * q + 1][2 * g + sel]);
+          pr[g] = role == 0 ? w : z;
+          pz[g] = role == 1 ? w : z;
+        }
+      } else {
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int j0 = 2 * q, j1 = 2 * q + 1;
+            // (alpha_g is applied once per head in the combine; past n_ctx p = 0
+            // and the staged norms are 0)
+            pr[g][q] = h2bits(p[j0] * vn[j0][2 * g], p[j1] * vn[j1][2 * g]);
+            pz[g][q] = h2bits(p[j0] * vn[j0][2 * g + 1], p[j1] * vn[j1][2 * g + 1]);
+          }
         }
       }
       // ---------------- V: accumulate in the rotated / sketch domains ----------------
@@ -603,7 +672,10 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
           const u32x4 av = codes8<M>(field_at(cw, 8 * M * u, 8 * M), vt, off4);
           const u32x4 az = signs8((r.vs[G::VNS * g + (u >> 2)] >> (8 * (u & 3))) & 0xFFu, stab, off8);
           acc_r[g * MTPG + u] = mfma16(av, pr[g], acc_r[g * MTPG + u]);
-          acc_s[g * MTPG + u] = mfma16(az, pz[g], acc_s[g * MTPG + u]);
+          if constexpr (PK)
+            acc_r[g * MTPG + u] = mfma16(az, pz[g], acc_r[g * MTPG + u]);
+          else
+            acc_s[g * MTPG + u] = mfma16(az, pz[g], acc_s[g * MTPG + u]);
         }
       };
       v_group(std::integral_constant<int, 0>{});
@@ -651,14 +723,17 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
     float* s_red = reinterpret_cast<float*>(s_tab);
     __syncthreads();  // tables are no longer read
     l_run = rows4_sum(l_run);
-    if (lg == 0) s_m[wv][ln] = m_run;
+    // (packed: the role-0 lanes own a head's maximum and sum; the role-1
+    // lanes, which hold its sketch sums, read the maximum back from LDS)
+    if (lg == 0 && role == 0) s_m[wv][hcol] = m_run;
     __syncthreads();
-    float M = s_m[0][ln];
+    float M = s_m[0][hcol];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][ln]);
-    const float e = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
-    if (lg == 0) s_lw[wv][ln] = l_run * e;
-    float* reg = s_red + (wv & 1) * REG + ln * HS;
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][hcol]);
+    const float m_own = PK ? s_m[wv][hcol] : m_run;
+    const float e = (m_own == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_own - M);
+    if (lg == 0 && role == 0) s_lw[wv][hcol] = l_run * e;
+    float* reg = s_red + (wv & 1) * REG + hcol * HS;
     auto slot = [&](int pt, int v, int i) {
       const int g = v / MTPG, u = v % MTPG;
       const int ch = g * DG + RUN * (4 * lg + i) + u;
@@ -669,8 +744,12 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
       for (int v = 0; v < NMT; ++v)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          reg[slot(0, v, i)] = acc_r[v][i] * e;
-          reg[slot(1, v, i)] = acc_s[v][i] * e;
+          if constexpr (PK) {
+            if (role < 2) reg[slot(role, v, i)] = acc_r[v][i] * e;
+          } else {
+            reg[slot(0, v, i)] = acc_r[v][i] * e;
+            reg[slot(1, v, i)] = acc_s[v][i] * e;
+          }
         }
     }
     __syncthreads();
@@ -679,13 +758,17 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
       for (int v = 0; v < NMT; ++v)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          reg[slot(0, v, i)] += acc_r[v][i] * e;
-          reg[slot(1, v, i)] += acc_s[v][i] * e;
+          if constexpr (PK) {
+            if (role < 2) reg[slot(role, v, i)] += acc_r[v][i] * e;
+          } else {
+            reg[slot(0, v, i)] += acc_r[v][i] * e;
+            reg[slot(1, v, i)] += acc_s[v][i] * e;
+          }
         }
     }
     __syncthreads();
     // write the partial of every valid head: [max (log2 domain), sum, acc_rot[D], acc_sk[D]]
-    const int nh = a.group - hblk * 16 < 16 ? a.group - hblk * 16 : 16;
+    const int nh = a.group - hblk * HB < HB ? a.group - hblk * HB : HB;
     for (int e2 = tid; e2 < nh * (2 + 2 * D); e2 += 256) {
       const int h = e2 / (2 + 2 * D), k = e2 % (2 + 2 * D);
       float val;
@@ -699,7 +782,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
         const int idx = h * HS + pt * DP + ch + 16 * (ch >> 6);
         val = s_red[idx] + s_red[REG + idx];
       }
-      const int hq2 = kvh * a.group + hblk * 16 + h;
+      const int hq2 = kvh * a.group + hblk * HB + h;
       a.part[(((int64_t)b * a.hq + hq2) * a.n_split + split) * (2 + 2 * D) + k] = val;
     }
   }
@@ -859,12 +942,22 @@ size_t workspace_for(const tq_decode_shape* s, int d, bool with_v, int n_split) 
   return bytes;
 }
 
+// heads per workgroup: 4 (packed columns) for KV groups of at most 4 query
+// heads with V, else 16
+inline int heads_per_block(int group, bool with_v) { return with_v && group <= 4 ? 4 : 16; }
+
 template <int D, int NG, int M0, int M1, bool WV>
 hipError_t launch_decode(const DArgs& a, int n_hblk, hipStream_t st) {
   (void)hipGetLastError();  // a launch error is reported below, not an older one
-  hipLaunchKernelGGL((decode_kernel<D, NG, M0, M1, WV>),
-                     dim3((unsigned)a.n_split, (unsigned)(a.batch * a.hkv), (unsigned)n_hblk), dim3(256),
-                     0, st, a);
+  const dim3 grid((unsigned)a.n_split, (unsigned)(a.batch * a.hkv), (unsigned)n_hblk);
+  if constexpr (WV) {
+    if (heads_per_block(a.group, WV) == 4)
+      hipLaunchKernelGGL((decode_kernel<D, NG, M0, M1, WV, 4>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<D, NG, M0, M1, WV, 16>), grid, dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((decode_kernel<D, NG, M0, M1, WV, 16>), grid, dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 
@@ -903,7 +996,9 @@ extern "C" tq_status tq_attn_decode_workspace_bytes(const tq_quantizer* kq, cons
                                                     const tq_decode_shape* shape, size_t* bytes) {
   if (!kq || !tq::layout_valid(&kq->layout) || !shape_valid(shape) || !bytes) return TQ_ERR_INVALID;
   if (vq && !tq::layout_valid(&vq->layout)) return TQ_ERR_INVALID;
-  const int n_hblk = (shape->n_q_heads / shape->n_kv_heads + 15) / 16;
+  const int grp = shape->n_q_heads / shape->n_kv_heads;
+  const int hb = heads_per_block(grp, vq != nullptr);
+  const int n_hblk = (grp + hb - 1) / hb;
   *bytes = workspace_for(shape, kq->layout.d, vq != nullptr, choose_split(shape, n_hblk));
   return TQ_OK;
 }
@@ -950,7 +1045,8 @@ tq_status plan_decode(const tq_quantizer* kq, const tq_quantizer* vq, const tq_d
   if (!decode_supported(kq->layout)) return TQ_ERR_UNSUPPORTED;
   const tq_layout& l = kq->layout;
   const int group = shape->n_q_heads / shape->n_kv_heads;
-  const int n_hblk = (group + 15) / 16;
+  const int hb = heads_per_block(group, with_v);
+  const int n_hblk = (group + hb - 1) / hb;
   const int n_split = choose_split(shape, n_hblk);
   const size_t need = workspace_for(shape, l.d, with_v, n_split);
   if (!workspace || workspace_bytes < need) return TQ_ERR_WORKSPACE;
