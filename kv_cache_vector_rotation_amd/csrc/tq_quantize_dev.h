@@ -183,6 +183,142 @@ struct Lds {
   static constexpr int bytes = off_skr + (SKR_LDS ? NT * KP * 64 : 0);
 };
 
+// Vectors of one tile: [v0, v0 + nvalid). With block-owned tiling they are
+// those of one segment falling in one aligned pair of blocks, whose first row
+// is rowbase; slot_lo is the first vector's position in the pair.
+struct TileGeo {
+  int64_t v0, rowbase;
+  int nvalid, slot_lo;
+};
+
+// Geometry of `tile`; false when it holds no vector (block-owned tiling).
+__device__ __forceinline__ bool tile_geo(const QArgs& a, int64_t tile, TileGeo& g) {
+  g.rowbase = 0;
+  g.slot_lo = 0;
+  if (a.blk_owned) {
+    const int64_t sg = tile / a.pairs_per_seg, pr = tile % a.pairs_per_seg;
+    const int o32 = (int)(a.seg_offset % 32);
+    const int64_t rem = a.n_vec - sg * a.seg_len;
+    const int64_t len = rem < a.seg_len ? rem : a.seg_len;
+    const int64_t lo = 64 * pr - o32 > 0 ? 64 * pr - o32 : 0;  // segment-relative
+    const int64_t hi = 64 * pr + 64 - o32 < len ? 64 * pr + 64 - o32 : len;
+    if (hi <= lo) return false;
+    g.v0 = sg * a.seg_len + lo;
+    g.nvalid = (int)(hi - lo);
+    g.rowbase = sg * a.seg_stride + (a.seg_offset - o32) + 64 * pr;
+    g.slot_lo = (int)(lo + o32 - 64 * pr);
+  } else {
+    g.v0 = tile * QT;
+    g.nvalid = (int)((a.n_vec - g.v0) < QT ? (a.n_vec - g.v0) : QT);
+  }
+  return true;
+}
+
+// The first tile at or after `tile` (in steps of `stride`) that holds
+// vectors, or n_tiles. Uniform across the workgroup.
+__device__ __forceinline__ int64_t next_live_tile(const QArgs& a, int64_t tile, int64_t stride, TileGeo& g) {
+  for (; tile < a.n_tiles; tile += stride)
+    if (tile_geo(a, tile, g)) return tile;
+  return a.n_tiles;
+}
+
+// A thread's share of one input tile (QT KP / (64 NT) = 16 values) and the
+// destination row of vector tid, held in registers between the global loads
+// and the LDS stores.
+struct XStage {
+  u32x4 v[4];
+  int64_t row;
+};
+
+template <int KP, int NT>
+__device__ __forceinline__ void load_x(const QArgs& a, const TileGeo& g, int tid, XStage& st) {
+  static_assert(QT * KP / (NT * 64) == 16, "16 values per thread");
+  const int d = a.d;
+  st.row = -1;
+  if (tid < g.nvalid) st.row = a.blk_owned ? g.rowbase + g.slot_lo + tid : dest_row(a, g.v0 + tid);
+  if (a.x_vec) {
+    // rows are 16-byte aligned and d is a multiple of the vector width:
+    // 16-byte loads, 8 bf16 or 4 fp32 values each
+    if (a.x_bf16) {
+      constexpr int CPR = KP / 8, NCH = QT * CPR / (NT * 64);  // chunks per row, per thread
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int c = tid + i * NT * 64, v = c / CPR, k = (c % CPR) * 8;
+        st.v[i] = (v < g.nvalid && k < d)
+                      ? *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.x) +
+                                                        (g.v0 + v) * a.x_stride + k)
+                      : u32x4{0u, 0u, 0u, 0u};
+      }
+    } else {
+      constexpr int CPR = KP / 4, NCH = QT * CPR / (NT * 64);
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int c = tid + i * NT * 64, v = c / CPR, k = (c % CPR) * 4;
+        st.v[i] = (v < g.nvalid && k < d)
+                      ? *reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(a.x) +
+                                                        (g.v0 + v) * a.x_stride + k)
+                      : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int e = tid + i * NT * 64, v = e / KP, k = e % KP;
+      uint32_t val = 0u;
+      if (v < g.nvalid && k < d) {
+        const int64_t off = (g.v0 + v) * a.x_stride + k;
+        val = a.x_bf16 ? ((uint32_t) reinterpret_cast<const uint16_t*>(a.x)[off]) << 16
+                       : __float_as_uint(reinterpret_cast<const float*>(a.x)[off]);
+      }
+      st.v[i / 4][i % 4] = val;
+    }
+  }
+}
+
+// The tile as fp32 in LDS (row stride XS), zero padded.
+template <int KP, int NT, int XS>
+__device__ __forceinline__ void store_x(const QArgs& a, const XStage& st, int tid, float* xr) {
+  if (a.x_vec) {
+    if (a.x_bf16) {
+      constexpr int CPR = KP / 8, NCH = QT * CPR / (NT * 64);
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int c = tid + i * NT * 64, v = c / CPR, k = (c % CPR) * 8;
+        f32x4 lo, hi;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t w = st.v[i][e];
+          const float f0 = __uint_as_float(w << 16), f1 = __uint_as_float(w & 0xFFFF0000u);
+          if (e < 2) {
+            lo[2 * e] = f0;
+            lo[2 * e + 1] = f1;
+          } else {
+            hi[2 * e - 4] = f0;
+            hi[2 * e - 3] = f1;
+          }
+        }
+        *reinterpret_cast<f32x4*>(xr + v * XS + k) = lo;
+        *reinterpret_cast<f32x4*>(xr + v * XS + k + 4) = hi;
+      }
+    } else {
+      constexpr int CPR = KP / 4, NCH = QT * CPR / (NT * 64);
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int c = tid + i * NT * 64, v = c / CPR, k = (c % CPR) * 4;
+        const u32x4 w = st.v[i];
+        *reinterpret_cast<f32x4*>(xr + v * XS + k) =
+            f32x4{__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]), __uint_as_float(w[3])};
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int e = tid + i * NT * 64;
+      xr[(e / KP) * XS + e % KP] = __uint_as_float(st.v[i / 4][i % 4]);
+    }
+  }
+}
+
 // The kernel body: this workgroup quantizes tiles first_tile,
 // first_tile + tile_stride, ... of `a`, with NT * 64 threads and the dynamic
 // LDS block `smem` (Lds<KP, NT>::bytes).
@@ -223,6 +359,12 @@ __device__ __forceinline__ void quantize_tiles(const QArgs& a, int64_t first_til
     const int ncent = (1 << a.gbits[0]) + (a.n_groups > 1 ? (1 << a.gbits[1]) : 0);
     cent_reg = a.centroids[tid < ncent ? tid : ncent - 1];
   }
+  // the first tile's vectors and destination rows (the next tile's are
+  // loaded at the end of each pass)
+  TileGeo g;
+  int64_t tile = next_live_tile(a, first_tile, tile_stride, g);
+  XStage st;
+  if (tile < a.n_tiles) load_x<KP, NT>(a, g, tid, st);
 
   // This wave's rows of rot and sketch_rot: B[k][n] = M[16 w + n][k], with k
   // assigned to steps as in mfma_tiles. The loads are unconditional (indices
@@ -298,109 +440,15 @@ __device__ __forceinline__ void quantize_tiles(const QArgs& a, int64_t first_til
     bnd_reg = a.boundaries[tid < nbt ? tid : nbt - 1];
   }
 
-  for (int64_t tile = first_tile; tile < a.n_tiles; tile += tile_stride) {
-    // Tile = input vectors [v0, v0 + nvalid). With block-owned tiling the
-    // vectors are those of one segment falling in one aligned pair of
-    // blocks, whose first row is rowbase; slot_lo is the first vector's
-    // position in the pair.
-    int64_t v0, rowbase = 0;
-    int nvalid, slot_lo = 0;
-    if (a.blk_owned) {
-      const int64_t sg = tile / a.pairs_per_seg, pr = tile % a.pairs_per_seg;
-      const int o32 = (int)(a.seg_offset % 32);
-      const int64_t rem = a.n_vec - sg * a.seg_len;
-      const int64_t len = rem < a.seg_len ? rem : a.seg_len;
-      const int64_t lo = 64 * pr - o32 > 0 ? 64 * pr - o32 : 0;      // segment-relative
-      const int64_t hi = 64 * pr + 64 - o32 < len ? 64 * pr + 64 - o32 : len;
-      if (hi <= lo) continue;  // uniform across the workgroup
-      v0 = sg * a.seg_len + lo;
-      nvalid = (int)(hi - lo);
-      rowbase = sg * a.seg_stride + (a.seg_offset - o32) + 64 * pr;
-      slot_lo = (int)(lo + o32 - 64 * pr);
-    } else {
-      v0 = tile * QT;
-      nvalid = (int)((a.n_vec - v0) < QT ? (a.n_vec - v0) : QT);
-    }
+  while (tile < a.n_tiles) {
+    const int64_t rowbase = g.rowbase;
+    const int nvalid = g.nvalid, slot_lo = g.slot_lo;
 
     // ---- stage the input tile (fp32, zero padded) and destination rows ----
-    // All of a thread's loads are issued before any LDS store, so the tile
-    // costs one memory latency rather than one per element.
     if (tok && a.pk_zero)
       for (int e = tid; e < QT * PKW; e += NT * 64) pk[e] = 0u;
-    // (destination row of vector tid: loaded now, stored to LDS with the tile)
-    int64_t my_row = -1;
-    if (tid < nvalid) my_row = a.blk_owned ? rowbase + slot_lo + tid : dest_row(a, v0 + tid);
-    if (a.x_vec) {
-      // rows are 16-byte aligned and d is a multiple of the vector width:
-      // 16-byte loads, 8 bf16 or 4 fp32 values each
-      if (a.x_bf16) {
-        constexpr int CPR = KP / 8, NCH = QT * CPR / (NT * 64);  // chunks per row, per thread
-        u32x4 buf[NCH];
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-          const int c = tid + i * NT * 64, v = c / CPR, k = (c % CPR) * 8;
-          buf[i] = (v < nvalid && k < d)
-                       ? *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.x) +
-                                                         (v0 + v) * a.x_stride + k)
-                       : u32x4{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-          const int c = tid + i * NT * 64, v = c / CPR, k = (c % CPR) * 8;
-          f32x4 lo, hi;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t w = buf[i][e];
-            const float f0 = __uint_as_float(w << 16), f1 = __uint_as_float(w & 0xFFFF0000u);
-            if (e < 2) {
-              lo[2 * e] = f0;
-              lo[2 * e + 1] = f1;
-            } else {
-              hi[2 * e - 4] = f0;
-              hi[2 * e - 3] = f1;
-            }
-          }
-          *reinterpret_cast<f32x4*>(xr + v * XS + k) = lo;
-          *reinterpret_cast<f32x4*>(xr + v * XS + k + 4) = hi;
-        }
-      } else {
-        constexpr int CPR = KP / 4, NCH = QT * CPR / (NT * 64);
-        f32x4 buf[NCH];
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-          const int c = tid + i * NT * 64, v = c / CPR, k = (c % CPR) * 4;
-          buf[i] = (v < nvalid && k < d)
-                       ? *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(a.x) +
-                                                         (v0 + v) * a.x_stride + k)
-                       : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-          const int c = tid + i * NT * 64, v = c / CPR, k = (c % CPR) * 4;
-          *reinterpret_cast<f32x4*>(xr + v * XS + k) = buf[i];
-        }
-      }
-    } else {
-      constexpr int PER = QT * KP / (NT * 64);
-      float buf[PER];
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const int e = tid + i * NT * 64, v = e / KP, k = e % KP;
-        float val = 0.f;
-        if (v < nvalid && k < d) {
-          const int64_t off = (v0 + v) * a.x_stride + k;
-          val = a.x_bf16 ? __uint_as_float(((uint32_t) reinterpret_cast<const uint16_t*>(a.x)[off]) << 16)
-                         : reinterpret_cast<const float*>(a.x)[off];
-        }
-        buf[i] = val;
-      }
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const int e = tid + i * NT * 64;
-        xr[(e / KP) * XS + e % KP] = buf[i];
-      }
-    }
-    if (tid < QT) rows[tid] = (my_row < 0 || my_row >= a.n_rows) ? -1 : my_row;
+    store_x<KP, NT, XS>(a, st, tid, xr);
+    if (tid < QT) rows[tid] = (st.row < 0 || st.row >= a.n_rows) ? -1 : st.row;
     if (tid < 32) {
       cbk[tid] = cent_reg;
       cbk[32 + tid] = bnd_reg;
@@ -445,47 +493,69 @@ __device__ __forceinline__ void quantize_tiles(const QArgs& a, int64_t first_til
     for (int k = 0; k < 15; ++k)
       tb[k] = k < nb ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(cbk[32 + boff + k])))
                      : INFINITY;
+    // In phases over a lane's four vectors of a 16-vector tile: LDS reads,
+    // arithmetic, then LDS stores and row reductions, so no store sits
+    // between two reads (the reads of one phase are in flight together).
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       if (mt >= n_mt) break;  // tiles past the last vector: their rows stay zero
+      float nv[4], cv[4], rr[4];
+      int idx[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) nv[i] = nrm[grp * QT + mt * 16 + lg * 4 + i];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // cell = number of boundaries below u (the +inf entries past the
+        // group's count never are); fully unrolled so tb stays in SGPRs.
+        // A zero vector takes the middle cell and a zero residual.
+        const float u = yacc[mt][i] * __builtin_amdgcn_rcpf(nv[i]);
+        int c = 0;
+#pragma unroll
+        for (int k = 0; k < 15; ++k) c += u > tb[k] ? 1 : 0;
+        idx[i] = nv[i] > 0.f ? c : (nb + 1) / 2 - 1;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cv[i] = cbk[coff + idx[i]];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        rr[i] = nv[i] > 0.f ? fmaf(-nv[i], cv[i], yacc[mt][i]) : 0.f;
+        if (ocoord >= d) {
+          rr[i] = 0.f;
+          idx[i] = 0;
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int v = mt * 16 + lg * 4 + i;
-        const float y = yacc[mt][i];
-        const float n = nrm[grp * QT + v];
-        int idx;
-        float r;
-        if (n > 0.f) {
-          // cell = number of boundaries below u (the +inf entries past the
-          // group's count never are); fully unrolled so tb stays in SGPRs
-          const float u = y * __builtin_amdgcn_rcpf(n);
-          idx = 0;
+        code_b[v * DP + ocoord] = (uint8_t)idx[i];
+        xr[v * XS + ocoord] = rr[i];  // A operand of the sketch product (k = rotated coordinate)
+      }
+      if (tok) {
+        // the row's 16 codes of this wave, OR-combined across the row of
+        // lanes, are 2 mg bytes of the packed record
+        uint32_t lo[4], hi[4];
 #pragma unroll
-          for (int k = 0; k < 15; ++k) idx += u > tb[k] ? 1 : 0;
-          r = fmaf(-n, cbk[coff + idx], y);
-        } else {
-          idx = (nb + 1) / 2 - 1;
-          r = 0.f;
+        for (int i = 0; i < 4; ++i) {
+          const uint64_t f = (uint64_t)(uint32_t)idx[i] << (mg * ln);
+          lo[i] = row16_or((uint32_t)f);
+          hi[i] = mg > 2 ? row16_or((uint32_t)(f >> 32)) : 0u;
         }
-        if (ocoord >= d) {
-          r = 0.f;
-          idx = 0;
+        if (ln == 0) {
+          // (one base address; the vector and halfword offsets are constants)
+          uint16_t* row = pk16 + lg * 4 * 2 * PKW + pk_code_h;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              if (k < mg) row[(mt * 16 + i) * 2 * PKW + k] = (uint16_t)((k < 2 ? lo[i] : hi[i]) >> (16 * (k & 1)));
         }
-        code_b[v * DP + ocoord] = (uint8_t)idx;
-        if (tok) {
-          // the row's 16 codes of this wave, OR-combined across the row of
-          // lanes, are 2 mg bytes of the packed record
-          const uint64_t f = (uint64_t)(uint32_t)idx << (mg * ln);
-          const uint32_t lo = row16_or((uint32_t)f);
-          const uint32_t hi = mg > 2 ? row16_or((uint32_t)(f >> 32)) : 0u;
-          if (ln == 0)
-            for (int k = 0; k < mg; ++k)
-              pk16[v * 2 * PKW + pk_code_h + k] = (uint16_t)((k < 2 ? lo : hi) >> (16 * (k & 1)));
-        }
-        xr[v * XS + ocoord] = r;  // A operand of the sketch product (k = rotated coordinate)
-        float s = r * r;
-        s = row16_sum(s);
-        if (ln == 0) gpart[w * QT + v] = s;
+      }
+      float ss[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ss[i] = row16_sum(rr[i] * rr[i]);
+      if (ln == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gpart[w * QT + mt * 16 + lg * 4 + i] = ss[i];
       }
     }
     // (every k < KP is a coordinate owned by some wave, so the residual tile
@@ -559,9 +629,10 @@ __device__ __forceinline__ void quantize_tiles(const QArgs& a, int64_t first_til
       }
     } else if (a.blk_owned) {
       // block records, tile = one aligned pair of blocks owned by this
-      // workgroup: each word is assembled from the tile's fields; a word
-      // that also holds rows outside the tile is read, merged and written
-      // back (no other workgroup writes these blocks in this call)
+      // workgroup: each word is assembled from the tile's fields; in a word
+      // that also holds rows outside the tile, the tile's bits are cleared
+      // and then set by two atomics, which need no read round trip (no other
+      // workgroup writes these blocks in this call)
       for (int h = 0; h < 2; ++h) {
         const int vlo = slot_lo > 32 * h ? slot_lo : 32 * h;
         const int vhi = slot_lo + nvalid < 32 * h + 32 ? slot_lo + nvalid : 32 * h + 32;
@@ -591,10 +662,12 @@ __device__ __forceinline__ void quantize_tiles(const QArgs& a, int64_t first_til
           }
           uint32_t* dst = a.codes + blk * bcw + wd;
           const uint32_t m32 = (uint32_t)mask;
-          if (m32 == 0xFFFFFFFFu)
+          if (m32 == 0xFFFFFFFFu) {
             *dst = (uint32_t)word;
-          else if (m32 != 0)
-            *dst = (*dst & ~m32) | ((uint32_t)word & m32);
+          } else if (m32 != 0) {
+            atomicAnd(dst, ~m32);
+            atomicOr(dst, (uint32_t)word & m32);
+          }
         }
         const int bsw = a.blk_sign_words;
         for (int wd = tid; wd < bsw; wd += NT * 64) {
@@ -613,10 +686,12 @@ __device__ __forceinline__ void quantize_tiles(const QArgs& a, int64_t first_til
             }
           }
           uint32_t* dst = a.signs + blk * bsw + wd;
-          if (mask == 0xFFFFFFFFu)
+          if (mask == 0xFFFFFFFFu) {
             *dst = word;
-          else if (mask != 0)
-            *dst = (*dst & ~mask) | (word & mask);
+          } else if (mask != 0) {
+            atomicAnd(dst, ~mask);
+            atomicOr(dst, word & mask);
+          }
         }
       }
     } else {
@@ -693,6 +768,8 @@ __device__ __forceinline__ void quantize_tiles(const QArgs& a, int64_t first_til
       }
     }
     __syncthreads();
+    tile = next_live_tile(a, tile + tile_stride, tile_stride, g);
+    if (tile < a.n_tiles) load_x<KP, NT>(a, g, tid, st);
   }
 }
 
