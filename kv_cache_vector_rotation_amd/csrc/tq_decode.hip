@@ -110,6 +110,13 @@ __device__ __forceinline__ float dpp_row(float v) {
   const int x = __float_as_int(v);
   return __int_as_float(__builtin_amdgcn_update_dpp(x, x, CTRL, 0xF, 0xF, false));
 }
+// The same move with 0 where the source lies outside the row (the compiler
+// can fold it into the consuming multiply); only for results that every lane
+// uses unconditionally.
+template <int CTRL>
+__device__ __forceinline__ float dpp_row_z(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
 
 // max over the four 16-lane rows (lanes l, l ^ 16, l ^ 32, l ^ 48): swap the
 // 32-lane halves, then odd and even rows, with v_permlane{32,16}_swap
@@ -175,24 +182,49 @@ __device__ void tab_build(unsigned char* base, int tid, F value) {
   }
 }
 
-// 8 sign bits (bit s -> slot s) -> 8 fp16 values, +1 where set, -1 where clear.
-__device__ __forceinline__ u32x4 signs8(uint32_t byte, const unsigned char* stab, uint32_t off8) {
-  const u32x2 lo = *reinterpret_cast<const u32x2*>(stab + tab_addr<16, 8>(byte & 15u, off8));
-  const u32x2 hi = *reinterpret_cast<const u32x2*>(stab + tab_addr<16, 8>((byte >> 4) & 15u, off8));
+constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
+
+// Address of the table entry whose index is the ilog2(E)-bit field at bit
+// pos of the word array w (pos is a constant once the callers' loops are
+// unrolled; a field may run into the next word, which must exist). The
+// field is brought to its position in the address by one shift, or one
+// funnel shift where it crosses a word, and masked into the lane's replica
+// offset by one v_and_or.
+template <int E, int W>
+__device__ __forceinline__ uint32_t tab_addr_at(const uint32_t* w, int pos, uint32_t lane_off) {
+  constexpr int NB = ilog2(E), P = Tab<E, W>::REP ? 8 : ilog2(W);
+  const int wi = pos >> 5, b = pos & 31;
+  const uint32_t mask = (uint32_t)(E - 1) << P;
+  uint32_t t;
+  if (b + NB > 32)
+    t = __builtin_amdgcn_alignbit(w[wi + 1], w[wi], b - P);
+  else if (b >= P)
+    t = w[wi] >> (b - P);
+  else
+    t = w[wi] << (P - b);
+  if constexpr (Tab<E, W>::REP)
+    return (t & mask) | lane_off;
+  else
+    return t & mask;
+}
+
+// 8 sign bits at bit pos of w (bit s -> slot s) -> 8 fp16 values, +1 where
+// set, -1 where clear.
+__device__ __forceinline__ u32x4 signs8(const uint32_t* w, int pos, const unsigned char* stab, uint32_t off8) {
+  const u32x2 lo = *reinterpret_cast<const u32x2*>(stab + tab_addr_at<16, 8>(w, pos, off8));
+  const u32x2 hi = *reinterpret_cast<const u32x2*>(stab + tab_addr_at<16, 8>(w, pos + 4, off8));
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
-// 8 codes of M bits (code s at bits [M s, M s + M) of field) -> 8 fp16
-// centroids, one 4-byte lookup per pair.
+// 8 codes of M bits at bit pos of w (code s at bits [pos + M s, pos + M s + M))
+// -> 8 fp16 centroids, one 4-byte lookup per pair.
 template <int M>
-__device__ __forceinline__ u32x4 codes8(uint32_t field, const unsigned char* tab, uint32_t off4) {
+__device__ __forceinline__ u32x4 codes8(const uint32_t* w, int pos, const unsigned char* tab, uint32_t off4) {
   constexpr int E = 1 << (2 * M);
   u32x4 r;
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint32_t e = (field >> (2 * M * p)) & (E - 1u);
-    r[p] = *reinterpret_cast<const uint32_t*>(tab + tab_addr<E, 4>(e, off4));
-  }
+  for (int p = 0; p < 4; ++p)
+    r[p] = *reinterpret_cast<const uint32_t*>(tab + tab_addr_at<E, 4>(w, pos + 2 * M * p, off4));
   return r;
 }
 
@@ -210,16 +242,6 @@ __device__ __forceinline__ void load_w(const uint32_t* p, uint32_t* out) {
 #pragma unroll
     for (int i = 0; i < N; ++i) out[i] = p[i];
   }
-}
-
-// bits [pos, pos + width) of a word array; pos and width are compile-time
-// constants after unrolling (width <= 32)
-__device__ __forceinline__ uint32_t field_at(const uint32_t* w, int pos, int width) {
-  const int wi = pos >> 5, sh = pos & 31;
-  uint32_t v = w[wi] >> sh;
-  if (sh + width > 32) v |= w[wi + 1] << (32 - sh);
-  if (width < 32) v &= (1u << width) - 1u;
-  return v;
 }
 
 // Norms (n_g, gamma_g) of 8 consecutive tokens from the wave's LDS staging.
@@ -366,12 +388,13 @@ __device__ __forceinline__ void load_tile(const DArgs& a, int64_t row0, int lane
 }
 
 // HB = query heads per workgroup and MFMA column block: 16, or 4 ("packed",
-// for KV groups of at most 4 query heads). Packed, the 16 MFMA columns hold
+// for KV groups of at most 4 query heads; with one quantizer group it fits
+// three waves per SIMD). Packed, the 16 MFMA columns hold
 // [q_rot hi | q_rot lo | q_sk | unused] x 4 heads for the logits and
 // [p n | p gamma | 0 | 0] x 4 heads for the V sums, so one accumulator
 // serves all three logit parts and one serves both V parts.
 template <int D, int NG, int M0, int M1, bool WV, int HB>
-__global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
+__global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel(DArgs a) {
   using G = Geo<D, NG, M0, M1>;
   constexpr bool PK = HB == 4;
   constexpr int NC = G::NC, CPG = G::CPG, NMT = G::NMT, MTPG = G::MTPG, RUN = G::RUN, DG = G::DG;
@@ -426,11 +449,57 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
     cent_k = a.kcent[tc] * a.kscale[NG > 1 && tc >= (1 << M0) ? 1 : 0];
     if constexpr (WV) cent_v = a.vcent[tc];
   }
-  Raw<D, NG, M0, M1> ra, rb, rc;
+  // ---- this lane's head and its query operands (B operand: channels x heads) ----
+  // (loaded before the first tile: loads complete in issue order, so using
+  // them then does not wait for the tile)
+  // packed: column ln = (role, head) with role = ln / 4: 0 q_rot hi / rot
+  // weights, 1 q_rot lo / sketch weights, 2 q_sk, 3 unused
+  const int role = PK ? ln >> 2 : 0;
+  const int hcol = PK ? ln & 3 : ln;  // head of this lane's column within the block
+  const int hloc = hblk * HB + hcol;  // head index within the KV group
+  const bool hvalid = hloc < a.group;
+  const int hq = kvh * a.group + hloc;
+  u32x4 qr[NC], qrl[PK ? 1 : NC], qs[NC];  // packed: qr = B of the code product, qs = B of the sign product
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int g = c / CPG, cl = c % CPG;
+    const _Float16* qp = a.qprep + ((int64_t)b * a.hq + (hvalid ? hq : 0)) * (3 * D) + g * DG + 8 * CPG * lg + 8 * cl;
+    if constexpr (PK) {
+      const u32x4 z{0, 0, 0, 0};
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qp + (role == 0 ? 0 : role == 1 ? D : 2 * D));
+      qr[c] = hvalid && role < 2 ? v : z;
+      qs[c] = hvalid && role == 2 ? v : z;
+    } else {
+      const u32x4 z{0, 0, 0, 0};
+      const u32x4 vr = *reinterpret_cast<const u32x4*>(qp);
+      const u32x4 vl = *reinterpret_cast<const u32x4*>(qp + D);
+      const u32x4 vs = *reinterpret_cast<const u32x4*>(qp + 2 * D);
+      qr[c] = hvalid ? vr : z;
+      qrl[c] = hvalid ? vl : z;
+      qs[c] = hvalid ? vs : z;
+    }
+  }
+  // register buffers: NBUF - 1 tiles in flight while one is computed. One
+  // tile ahead measures faster than two or three: every workgroup starts at
+  // once, and a smaller initial burst of loads brings each wave's first tile
+  // sooner.
+  constexpr int NBUF = 2;
+  Raw<D, NG, M0, M1> rb0, rb1, rb2, rb3;  // (the first NBUF are used)
+  auto rbuf = [&](auto kc) __attribute__((always_inline)) -> Raw<D, NG, M0, M1>& {
+    constexpr int k = decltype(kc)::value % NBUF;
+    if constexpr (k == 0) return rb0;
+    else if constexpr (k == 1) return rb1;
+    else if constexpr (k == 2) return rb2;
+    else return rb3;
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
   int64_t tile = t_begin + wv;
   // (unconditional, so the wait for the centroids below need not drain it;
   // a wave without tiles loads tile 0, which always exists, and drops it)
-  load_tile<D, NG, M0, M1, WV>(a, rowbase + (tile < t_end ? tile : 0) * kTile, lane, lo, ra);
+  load_tile<D, NG, M0, M1, WV>(a, rowbase + (tile < t_end ? tile : 0) * kTile, lane, lo, rb0);
   if (tid < 32) {
     s_cent[0][tid] = cent_k;
     s_cent[1][tid] = cent_v;
@@ -457,34 +526,6 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
     });
   }
 
-  // ---- this lane's head and its query operands (B operand: channels x heads) ----
-  // packed: column ln = (role, head) with role = ln / 4: 0 q_rot hi / rot
-  // weights, 1 q_rot lo / sketch weights, 2 q_sk, 3 unused
-  const int role = PK ? ln >> 2 : 0;
-  const int hcol = PK ? ln & 3 : ln;  // head of this lane's column within the block
-  const int hloc = hblk * HB + hcol;  // head index within the KV group
-  const bool hvalid = hloc < a.group;
-  const int hq = kvh * a.group + hloc;
-  u32x4 qr[NC], qrl[PK ? 1 : NC], qs[NC];  // packed: qr = B of the code product, qs = B of the sign product
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int g = c / CPG, cl = c % CPG;
-    const _Float16* qp = a.qprep + ((int64_t)b * a.hq + (hvalid ? hq : 0)) * (3 * D) + g * DG + 8 * CPG * lg + 8 * cl;
-    if constexpr (PK) {
-      const u32x4 z{0, 0, 0, 0};
-      const u32x4 v = *reinterpret_cast<const u32x4*>(qp + (role == 0 ? 0 : role == 1 ? D : 2 * D));
-      qr[c] = hvalid && role < 2 ? v : z;
-      qs[c] = hvalid && role == 2 ? v : z;
-    } else {
-      if (hvalid) {
-        qr[c] = *reinterpret_cast<const u32x4*>(qp);
-        qrl[c] = *reinterpret_cast<const u32x4*>(qp + D);
-        qs[c] = *reinterpret_cast<const u32x4*>(qp + 2 * D);
-      } else {
-        qr[c] = qrl[c] = qs[c] = u32x4{0, 0, 0, 0};
-      }
-    }
-  }
   __syncthreads();
 
   const unsigned char* stab = s_tab + ST;
@@ -496,7 +537,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
 #pragma unroll
   for (int v = 0; v < (WV && !PK ? NMT : 1); ++v) acc_s[v] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const Raw<D, NG, M0, M1>& r, int64_t T0) {
+  auto compute = [&](const Raw<D, NG, M0, M1>& r, int64_t T0) __attribute__((always_inline)) {
     // tokens past n_ctx (only in the last tile): norms staged as 0 (rows past
     // the context may hold anything) and logits masked to -inf below
     const bool full = T0 + kTile <= N;
@@ -531,13 +572,13 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
         w[i] = G::KSH[g] ? __builtin_amdgcn_alignbit(hi, lo, sh) : lo;
       }
       w[G::KNW[g]] = 0u;
-      const uint32_t sword = r.ks[tau][g] >> ((8 * CPG * lg) & 31);
+      const uint32_t sword[1] = {r.ks[tau][g] >> ((8 * CPG * lg) & 31)};
       const unsigned char* kt = g == 0 ? s_tab : s_tab + KT1;
 #pragma unroll
       for (int cl = 0; cl < CPG; ++cl) {
         const int c = g * CPG + cl;
-        const u32x4 ak = codes8<M>(field_at(w, 8 * M * cl, 8 * M), kt, off4);
-        const u32x4 az = signs8((sword >> (8 * cl)) & 0xFFu, stab, off8);
+        const u32x4 ak = codes8<M>(w, 8 * M * cl, kt, off4);
+        const u32x4 az = signs8(sword, 8 * cl, stab, off8);
         // (s c) q = (s c)16 (q_hi + 2^-11 q_lo'): products exact, fp32 sums;
         // 1 / s is applied with the token's norm
         if constexpr (PK) {
@@ -565,27 +606,37 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
       const int tau = j >> 2, i = j & 3;
       // (the prepared queries carry scale * log2(e), and alpha_g on the
       // sketch part, so this is the logit in the log2 domain)
-      float s = 0.f;
+      float s;
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
+        float t;
         if constexpr (PK) {
           // this lane's column is q_rot hi; q_rot lo and q_sk are 4 and 8 lanes up
           const float v = lr[tau][g][i];
-          const float vl = dpp_row<0x104>(v), vs = dpp_row<0x108>(v);  // row_shl:4, row_shl:8
-          s += kn[j][2 * g] * fmaf(kLoInv, vl, v) + kn[j][2 * g + 1] * vs;
+          const float vl = dpp_row_z<0x104>(v), vs = dpp_row_z<0x108>(v);  // row_shl:4, row_shl:8
+          t = kn[j][2 * g] * fmaf(kLoInv, vl, v) + kn[j][2 * g + 1] * vs;
         } else {
-          s += kn[j][2 * g] * fmaf(kLoInv, lrl[tau][g][i], lr[tau][g][i]) + kn[j][2 * g + 1] * ls[tau][g][i];
+          t = kn[j][2 * g] * fmaf(kLoInv, lrl[tau][g][i], lr[tau][g][i]) + kn[j][2 * g + 1] * ls[tau][g][i];
         }
+        s = g == 0 ? t : s + t;
       }
-      // (packed: only the role-0 columns are logits; the other columns carry
-      // finite values that no result uses)
-      if (a.logits && hvalid && role == 0 && (full || tok0 + j < N))
-        a.logits[((int64_t)b * a.hq + hq) * N + tok0 + j] = s * kLn2;
       l2[j] = s;
+    }
+    // tokens of the tile before n_ctx (32 except in the last tile)
+    const int nvt = full ? kTile : (int)(N - T0);
+    // (packed: only the role-0 columns are logits; the other columns carry
+    // finite values that no result uses)
+    if (a.logits) {
+      if (hvalid && role == 0) {
+        float* lp = a.logits + ((int64_t)b * a.hq + hq) * N + tok0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (8 * lg + j < nvt) lp[j] = l2[j] * kLn2;
+      }
     }
     if (!full) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) l2[j] = tok0 + j < N ? l2[j] : -INFINITY;
+      for (int j = 0; j < 8; ++j) l2[j] = 8 * lg + j < nvt ? l2[j] : -INFINITY;
     }
     if constexpr (WV) {
       // ---------------- online softmax ----------------
@@ -617,11 +668,11 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
         }
         m_run = m_new;
       }
-      float p[8], psum = 0.f;
+      float p[8], psum;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         p[j] = __builtin_amdgcn_exp2f(l2[j] - m_run);
-        psum += p[j];
+        psum = j == 0 ? p[j] : psum + p[j];
       }
       l_run += psum;
       // B operands of the V product: slot j <-> token 8 lg + j
@@ -669,8 +720,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
         const unsigned char* vt = g == 0 ? s_tab + VT0 : s_tab + VT1;
 #pragma unroll
         for (int u = 0; u < RUN; ++u) {
-          const u32x4 av = codes8<M>(field_at(cw, 8 * M * u, 8 * M), vt, off4);
-          const u32x4 az = signs8((r.vs[G::VNS * g + (u >> 2)] >> (8 * (u & 3))) & 0xFFu, stab, off8);
+          const u32x4 av = codes8<M>(cw, 8 * M * u, vt, off4);
+          const u32x4 az = signs8(&r.vs[G::VNS * g], 8 * u, stab, off8);
           acc_r[g * MTPG + u] = mfma16(av, pr[g], acc_r[g * MTPG + u]);
           if constexpr (PK)
             acc_r[g * MTPG + u] = mfma16(az, pz[g], acc_r[g * MTPG + u]);
@@ -684,30 +735,34 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DArgs a) {
     __builtin_amdgcn_wave_barrier();
   };
 
-  // ---- software-pipelined loop: tile t + 4 is loaded while tile t is computed ----
-  // (the prefetch is unconditional: on the last tile it reloads that tile, an
-  // in-bounds cache hit, so the compiler sees one straight-line load stream)
-  // Two tiles stay in flight while one is computed: three register buffers
-  // in rotation (the loop is unrolled three times so no data is copied).
-  // Prefetches past the wave's last tile reload that tile (in bounds,
-  // dropped).
+  // ---- software-pipelined loop ----
+  // NBUF - 1 tiles stay in flight while one is computed: NBUF register
+  // buffers in rotation (the loop is unrolled NBUF times so no data is
+  // copied). The prefetch is unconditional: past the wave's last tile it
+  // reloads that tile (in bounds, a cache hit, dropped), so the compiler sees
+  // one straight-line load stream.
   if (tile < t_end) {
     const int64_t last = t_end - 1 - ((t_end - 1 - tile) % kWaves);  // this wave's last tile
     auto next = [&](int64_t t, int k) { return t + k * kWaves <= last ? t + k * kWaves : last; };
-    load_tile<D, NG, M0, M1, WV>(a, rowbase + next(tile, 1) * kTile, lane, lo, rb);
+    if constexpr (NBUF > 2) load_tile<D, NG, M0, M1, WV>(a, rowbase + next(tile, 1) * kTile, lane, lo, rb1);
+    if constexpr (NBUF > 3) load_tile<D, NG, M0, M1, WV>(a, rowbase + next(tile, 2) * kTile, lane, lo, rb2);
+    // one pass of the rotation: true after the wave's last tile
+    auto stage = [&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      load_tile<D, NG, M0, M1, WV>(a, rowbase + next(tile, NBUF - 1) * kTile, lane, lo,
+                                   rbuf(std::integral_constant<int, k + NBUF - 1>{}));
+      compute(rbuf(kc), tile * kTile);
+      if (tile == last) return true;
+      tile += kWaves;
+      return false;
+    };
     for (;;) {
-      load_tile<D, NG, M0, M1, WV>(a, rowbase + next(tile, 2) * kTile, lane, lo, rc);
-      compute(ra, tile * kTile);
-      if (tile == last) break;
-      tile += kWaves;
-      load_tile<D, NG, M0, M1, WV>(a, rowbase + next(tile, 2) * kTile, lane, lo, ra);
-      compute(rb, tile * kTile);
-      if (tile == last) break;
-      tile += kWaves;
-      load_tile<D, NG, M0, M1, WV>(a, rowbase + next(tile, 2) * kTile, lane, lo, rb);
-      compute(rc, tile * kTile);
-      if (tile == last) break;
-      tile += kWaves;
+      if (stage(I0{})) break;
+      if (stage(I1{})) break;
+      if constexpr (NBUF > 2)
+        if (stage(I2{})) break;
+      if constexpr (NBUF > 3)
+        if (stage(I3{})) break;
     }
   }
 
