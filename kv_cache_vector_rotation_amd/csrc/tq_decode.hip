@@ -65,7 +65,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // Low parts of the split fp16 operands are stored times 2^11 so they stay in
 // the normal fp16 range; their products are scaled back by 2^-11.
-constexpr float kLoScale = 2048.0f;
 constexpr float kLoInv = 1.0f / 2048.0f;
 constexpr int kWaves = 4;
 constexpr int kTile = 32;

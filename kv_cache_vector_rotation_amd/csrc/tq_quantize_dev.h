@@ -319,6 +319,72 @@ __device__ __forceinline__ void store_x(const QArgs& a, const XStage& st, int ti
   }
 }
 
+// Code word wd of block blk = block h of a block-owned tile's pair: the
+// fields of the pair's rows [vlo, vhi) (row t is the tile's vector
+// t - slot_lo; its codes are LDS bytes [vector][DP]). A word that also holds
+// rows outside the tile has the tile's bits cleared and then set by two
+// atomics, which need no read round trip (no other workgroup writes these
+// blocks in the call).
+template <int DP>
+__device__ __forceinline__ void store_blk_code_word(const QArgs& a, const uint8_t* code_b, int64_t blk, int wd,
+                                                    int h, int vlo, int vhi, int slot_lo) {
+  const int g = (a.n_groups > 1 && wd >= a.bcwoff[1]) ? 1 : 0;
+  const int m = a.gbits[g], dg = a.gdim[g];
+  const int lw = wd - a.bcwoff[g];
+  const int b0 = 32 * lw;
+  const int u0 = b0 / (8 * m), u1 = (b0 + 31) / (8 * m);
+  const uint64_t fm = (1u << m) - 1u;
+  uint64_t word = 0, mask = 0;
+  for (int u = u0; u <= u1 && u < 4 * dg; ++u) {
+    const int o = u / dg, j = u % dg;
+    uint64_t unit = 0, umask = 0;
+    const int base = 32 * h + 8 * o;  // row of slot 0 of the unit
+    const int s0 = vlo > base ? vlo - base : 0, s1 = vhi < base + 8 ? vhi - base : 8;
+    for (int sl = s0; sl < s1; ++sl) {
+      unit |= (uint64_t)code_b[(base + sl - slot_lo) * DP + a.choff[g] + j] << (m * sl);
+      umask |= fm << (m * sl);
+    }
+    const int pos = 8 * m * u - b0;
+    word |= pos >= 0 ? unit << pos : unit >> (-pos);
+    mask |= pos >= 0 ? umask << pos : umask >> (-pos);
+  }
+  uint32_t* dst = a.codes + blk * a.blk_code_words + wd;
+  const uint32_t m32 = (uint32_t)mask;
+  if (m32 == 0xFFFFFFFFu) {
+    *dst = (uint32_t)word;
+  } else if (m32 != 0) {
+    atomicAnd(dst, ~m32);
+    atomicOr(dst, (uint32_t)word & m32);
+  }
+}
+
+// Sign word wd of the same block, from the LDS sign bytes.
+template <int DP>
+__device__ __forceinline__ void store_blk_sign_word(const QArgs& a, const uint8_t* sign_b, int64_t blk, int wd,
+                                                    int h, int vlo, int vhi, int slot_lo) {
+  const int g = (a.n_groups > 1 && wd >= a.bswoff[1]) ? 1 : 0;
+  const int dg = a.gdim[g];
+  const int lw = wd - a.bswoff[g];
+  uint32_t word = 0, mask = 0;
+  for (int q = 0; q < 4; ++q) {
+    const int u = 4 * lw + q;
+    const int o = u / dg, j = u % dg;
+    const int base = 32 * h + 8 * o;
+    const int s0 = vlo > base ? vlo - base : 0, s1 = vhi < base + 8 ? vhi - base : 8;
+    for (int sl = s0; sl < s1; ++sl) {
+      word |= (uint32_t)sign_b[(base + sl - slot_lo) * DP + a.choff[g] + j] << (8 * q + sl);
+      mask |= 1u << (8 * q + sl);
+    }
+  }
+  uint32_t* dst = a.signs + blk * a.blk_sign_words + wd;
+  if (mask == 0xFFFFFFFFu) {
+    *dst = word;
+  } else if (mask != 0) {
+    atomicAnd(dst, ~mask);
+    atomicOr(dst, word & mask);
+  }
+}
+
 // The kernel body: this workgroup quantizes tiles first_tile,
 // first_tile + tile_stride, ... of `a`, with NT * 64 threads and the dynamic
 // LDS block `smem` (Lds<KP, NT>::bytes).
@@ -638,61 +704,10 @@ __device__ __forceinline__ void quantize_tiles(const QArgs& a, int64_t first_til
         const int vhi = slot_lo + nvalid < 32 * h + 32 ? slot_lo + nvalid : 32 * h + 32;
         if (vhi <= vlo) continue;
         const int64_t blk = rowbase / 32 + h;
-        const int bcw = a.blk_code_words;
-        for (int wd = tid; wd < bcw; wd += NT * 64) {
-          const int g = (a.n_groups > 1 && wd >= a.bcwoff[1]) ? 1 : 0;
-          const int m = a.gbits[g], dg = a.gdim[g];
-          const int lw = wd - a.bcwoff[g];
-          const int b0 = 32 * lw;
-          const int u0 = b0 / (8 * m), u1 = (b0 + 31) / (8 * m);
-          const uint64_t fm = (1u << m) - 1u;
-          uint64_t word = 0, mask = 0;
-          for (int u = u0; u <= u1 && u < 4 * dg; ++u) {
-            const int o = u / dg, j = u % dg;
-            uint64_t unit = 0, umask = 0;
-            for (int sl = 0; sl < 8; ++sl) {
-              const int t = 32 * h + 8 * o + sl;
-              if (t < vlo || t >= vhi) continue;
-              unit |= (uint64_t)code_b[(t - slot_lo) * DP + a.choff[g] + j] << (m * sl);
-              umask |= fm << (m * sl);
-            }
-            const int pos = 8 * m * u - b0;
-            word |= pos >= 0 ? unit << pos : unit >> (-pos);
-            mask |= pos >= 0 ? umask << pos : umask >> (-pos);
-          }
-          uint32_t* dst = a.codes + blk * bcw + wd;
-          const uint32_t m32 = (uint32_t)mask;
-          if (m32 == 0xFFFFFFFFu) {
-            *dst = (uint32_t)word;
-          } else if (m32 != 0) {
-            atomicAnd(dst, ~m32);
-            atomicOr(dst, (uint32_t)word & m32);
-          }
-        }
-        const int bsw = a.blk_sign_words;
-        for (int wd = tid; wd < bsw; wd += NT * 64) {
-          const int g = (a.n_groups > 1 && wd >= a.bswoff[1]) ? 1 : 0;
-          const int dg = a.gdim[g];
-          const int lw = wd - a.bswoff[g];
-          uint32_t word = 0, mask = 0;
-          for (int q = 0; q < 4; ++q) {
-            const int u = 4 * lw + q;
-            const int o = u / dg, j = u % dg;
-            for (int sl = 0; sl < 8; ++sl) {
-              const int t = 32 * h + 8 * o + sl;
-              if (t < vlo || t >= vhi) continue;
-              word |= (uint32_t)sign_b[(t - slot_lo) * DP + a.choff[g] + j] << (8 * q + sl);
-              mask |= 1u << (8 * q + sl);
-            }
-          }
-          uint32_t* dst = a.signs + blk * bsw + wd;
-          if (mask == 0xFFFFFFFFu) {
-            *dst = word;
-          } else if (mask != 0) {
-            atomicAnd(dst, ~mask);
-            atomicOr(dst, word & mask);
-          }
-        }
+        for (int wd = tid; wd < a.blk_code_words; wd += NT * 64)
+          store_blk_code_word<DP>(a, code_b, blk, wd, h, vlo, vhi, slot_lo);
+        for (int wd = tid; wd < a.blk_sign_words; wd += NT * 64)
+          store_blk_sign_word<DP>(a, sign_b, blk, wd, h, vlo, vhi, slot_lo);
       }
     } else {
       // block records: whole blocks are written word by word

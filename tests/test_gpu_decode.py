@@ -166,52 +166,108 @@ def test_single_token_returns_its_value(tq):
     assert gc.normwise_close(out[0], ref)[0]
 
 
-@pytest.mark.parametrize("n_ctx,cap", [(1000, 1024), (64, 64)])
-def test_append_step_equals_separate_calls(tq, n_ctx, cap):
+@pytest.mark.parametrize("n_ctx,cap,n_new", [(1000, 1024, 1), (64, 64, 1), (700, 768, 40), (1500, 1536, 300)])
+def test_append_step_equals_separate_calls(tq, n_ctx, cap, n_new):
     # one launch for the K/V appends and the query preparation, then the
     # decode: the same caches and the same results, bit for bit, as
-    # tq_quantize (K), tq_quantize (V) and tq_attn_decode in a row
+    # tq_quantize (K), tq_quantize (V) and tq_attn_decode in a row; one new
+    # token per head, and 40 and 300 (several tiles, ragged blocks). Two
+    # steps in a row on one workspace, with different tokens.
     import torch
     wl = synth.workload("llama8b_decode", batch=2, n_q_heads=8, n_kv_heads=2)
     o = _oracle_side(wl, n_ctx, cap)
     kq = tq.Quantizer.from_parts(o["ks"].rotations, o["ks"].sketches, o["bits"], perm=o["ks"].perm)
     vq = tq.Quantizer.from_parts(o["vs"].rotations, o["vs"].sketches, o["bits"], perm=o["vs"].perm)
     B, H = wl.batch, wl.n_kv_heads
-    t = n_ctx - 1  # the appended token of every (batch, kv head)
-    kx = np.stack([synth.draw_kv_slab(wl, "K", b, h, t, t + 1)[0] for b in range(B) for h in range(H)])
-    vx = np.stack([synth.draw_kv_slab(wl, "V", b, h, t, t + 1)[0] for b in range(B) for h in range(H)])
-    kx_t = torch.from_numpy(kx).cuda().to(torch.bfloat16)
-    vx_t = torch.from_numpy(vx).cuda().to(torch.bfloat16)
+    t0 = n_ctx - n_new  # the appended tokens [t0, n_ctx) of every (batch, kv head)
+    kx = np.concatenate([synth.draw_kv_slab(wl, "K", b, h, t0, n_ctx) for b in range(B) for h in range(H)])
+    vx = np.concatenate([synth.draw_kv_slab(wl, "V", b, h, t0, n_ctx) for b in range(B) for h in range(H)])
     q = torch.from_numpy(synth.draw_queries(wl)).cuda().to(torch.bfloat16)
     shape = tq.decode_shape(B, wl.n_q_heads, H, n_ctx, cap, wl.scale)
-    results = []
-    for fused in (False, True):
-        kc = gc.to_device_cache(kq, tq.TQ_TOKEN_MAJOR, B * H * cap, o["karr"])
-        vc = gc.to_device_cache(vq, tq.TQ_BLOCK32, B * H * cap, o["varr"])
-        logits = torch.full((B, wl.n_q_heads, n_ctx), float("nan"), device="cuda")
-        out = torch.full((B, wl.n_q_heads, wl.d), float("nan"), device="cuda")
-        if fused:
-            tq.tq_attn_decode_append(kq, vq, shape, q, kc, vc,
-                                     k_new=tq.append_spec(kx_t, seg_len=1, seg_stride=cap, seg_offset=t),
-                                     v_new=tq.append_spec(vx_t, seg_len=1, seg_stride=cap, seg_offset=t),
-                                     logits=logits, out=out)
-        else:
-            tq.tq_quantize(kq, tq.TQ_TOKEN_MAJOR, kx_t, kc, seg_len=1, seg_stride=cap, seg_offset=t)
-            tq.tq_quantize(vq, tq.TQ_BLOCK32, vx_t, vc, seg_len=1, seg_stride=cap, seg_offset=t)
-            tq.tq_attn_decode(kq, vq, shape, q, kc, vc, logits=logits, out=out)
-        torch.cuda.synchronize()
-        results.append([x.cpu().numpy() for x in (kc.codes, kc.signs, kc.norms, vc.codes, vc.signs, vc.norms,
-                                                  logits, out)])
-    for a, b in zip(*results):
-        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
-    # and the step agrees with the oracle on the appended caches
+    ws = torch.zeros(tq.tq_attn_decode_workspace_bytes(kq, vq, shape), dtype=torch.uint8, device="cuda")
+    for sign in (1.0, -1.0):
+        kx_t = torch.from_numpy(sign * kx).cuda().to(torch.bfloat16)
+        vx_t = torch.from_numpy(sign * vx).cuda().to(torch.bfloat16)
+        results = []
+        for fused in (False, True):
+            kc = gc.to_device_cache(kq, tq.TQ_TOKEN_MAJOR, B * H * cap, o["karr"])
+            vc = gc.to_device_cache(vq, tq.TQ_BLOCK32, B * H * cap, o["varr"])
+            logits = torch.full((B, wl.n_q_heads, n_ctx), float("nan"), device="cuda")
+            out = torch.full((B, wl.n_q_heads, wl.d), float("nan"), device="cuda")
+            if fused:
+                tq.tq_attn_decode_append(kq, vq, shape, q, kc, vc,
+                                         k_new=tq.append_spec(kx_t, seg_len=n_new, seg_stride=cap, seg_offset=t0),
+                                         v_new=tq.append_spec(vx_t, seg_len=n_new, seg_stride=cap, seg_offset=t0),
+                                         logits=logits, out=out, workspace=ws)
+            else:
+                tq.tq_quantize(kq, tq.TQ_TOKEN_MAJOR, kx_t, kc, seg_len=n_new, seg_stride=cap, seg_offset=t0)
+                tq.tq_quantize(vq, tq.TQ_BLOCK32, vx_t, vc, seg_len=n_new, seg_stride=cap, seg_offset=t0)
+                tq.tq_attn_decode(kq, vq, shape, q, kc, vc, logits=logits, out=out)
+            torch.cuda.synchronize()
+            results.append([x.cpu().numpy() for x in (kc.codes, kc.signs, kc.norms, vc.codes, vc.signs,
+                                                      vc.norms, logits, out)])
+        for a, b in zip(*results):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+    # and the step (of the second, negated tokens) agrees with the oracle
     kt, vt = o["k_t"].copy(), o["v_t"].copy()
     okq, ovq = oracle.Quantizer.from_spec(o["ks"]), oracle.Quantizer.from_spec(o["vs"])
     for arr, x, qz in ((kt, kx, okq), (vt, vx, ovq)):
-        qv = oracle.quantize(x.astype(np.float64), qz)
-        arr[:, :, t] = oracle.dequantize(qv.idx, qv.bits, qv.norm, qv.gamma, qz).reshape(B, H, wl.d)
+        # (the appended inputs went through bf16)
+        xb = torch.from_numpy(-x).to(torch.bfloat16).to(torch.float64).numpy()
+        qv = oracle.quantize(xb, qz)
+        arr[:, :, t0:n_ctx] = oracle.dequantize(qv.idx, qv.bits, qv.norm, qv.gamma, qz).reshape(B, H, n_new, wl.d)
     q64 = synth.draw_queries(wl)
     for b in range(B):
         rl, ro = oracle.attention_decode(q64[b].astype(np.float64), kt[b], vt[b], wl.scale)
         assert gc.normwise_close(results[1][6][b].astype(np.float64), rl)[0]
         assert gc.normwise_close(results[1][7][b].astype(np.float64), ro)[0]
+
+
+def test_append_step_in_a_captured_graph(tq):
+    # the fused step captured in a graph replays to the eager results, every
+    # time (eager work and synchronizations between the replays)
+    import torch
+    wl = synth.workload("llama8b_decode", batch=2, n_q_heads=8, n_kv_heads=2)
+    n_ctx, cap, n_new = 1000, 1024, 1
+    o = _oracle_side(wl, n_ctx, cap)
+    kq = tq.Quantizer.from_parts(o["ks"].rotations, o["ks"].sketches, o["bits"], perm=o["ks"].perm)
+    vq = tq.Quantizer.from_parts(o["vs"].rotations, o["vs"].sketches, o["bits"], perm=o["vs"].perm)
+    B, H = wl.batch, wl.n_kv_heads
+    t0 = n_ctx - n_new
+    kx = np.concatenate([synth.draw_kv_slab(wl, "K", b, h, t0, n_ctx) for b in range(B) for h in range(H)])
+    vx = np.concatenate([synth.draw_kv_slab(wl, "V", b, h, t0, n_ctx) for b in range(B) for h in range(H)])
+    kx_t = torch.from_numpy(kx).cuda().to(torch.bfloat16)
+    vx_t = torch.from_numpy(vx).cuda().to(torch.bfloat16)
+    q = torch.from_numpy(synth.draw_queries(wl)).cuda().to(torch.bfloat16)
+    shape = tq.decode_shape(B, wl.n_q_heads, H, n_ctx, cap, wl.scale)
+    ws = torch.zeros(tq.tq_attn_decode_workspace_bytes(kq, vq, shape), dtype=torch.uint8, device="cuda")
+    kc = gc.to_device_cache(kq, tq.TQ_TOKEN_MAJOR, B * H * cap, o["karr"])
+    vc = gc.to_device_cache(vq, tq.TQ_BLOCK32, B * H * cap, o["varr"])
+    logits = torch.zeros((B, wl.n_q_heads, n_ctx), device="cuda")
+    out = torch.zeros((B, wl.n_q_heads, wl.d), device="cuda")
+    k_app = tq.append_spec(kx_t, seg_len=n_new, seg_stride=cap, seg_offset=t0)
+    v_app = tq.append_spec(vx_t, seg_len=n_new, seg_stride=cap, seg_offset=t0)
+
+    def step():
+        tq.tq_attn_decode_append(kq, vq, shape, q, kc, vc, k_new=k_app, v_new=v_app, logits=logits, out=out,
+                                 workspace=ws, stream=torch.cuda.current_stream())
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in (kc.codes, kc.signs, kc.norms, vc.codes, vc.signs, vc.norms, logits, out)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        logits.fill_(float("nan"))
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (kc.codes, kc.signs, kc.norms, vc.codes, vc.signs, vc.norms, logits, out)
+        for a, b in zip(ref, got):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
