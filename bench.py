@@ -13,7 +13,8 @@ next of several copies of the compressed cache (at least 1 GiB in total).
 
 Prints one JSON line: cached tokens/s (batch * context / step time), the
 split-K kernel against the HBM roofline (HIP events around that kernel on
-its stream), a secondary quantize throughput on a 524,288-vector chunk, and
+its stream), the same decode over uncompressed bf16 K/V caches for
+comparison, a secondary quantize throughput on a 524,288-vector chunk, and
 the CPU oracle timed on a bounded sample as a baseline.
 """
 from __future__ import annotations
@@ -57,6 +58,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quantize-bench", action="store_true")
+    ap.add_argument("--no-bf16-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch every step from Python")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (the reference for scaling "
@@ -142,6 +144,61 @@ def quantize_bench(tq, torch, wl, kq, n_vec=524288, launches=20):
     return {"vectors": n_vec, "us_per_launch": round(s * 1e6, 2), "vectors_per_s": n_vec / s,
             "bound": "mfma", "achieved_tflops": flops / s / 1e12, "peak_tflops": PEAK_FP32_MFMA_TFLOPS,
             "frac": flops / s / 1e12 / PEAK_FP32_MFMA_TFLOPS, "dtype": "f32"}
+
+
+def bf16_baseline(tq, torch, wl, q, step_ms, launches=200):
+    """Secondary figure: the same decode over uncompressed bf16 K/V caches
+    (tq_attn_decode_bf16: split-K pass and combine), on copies of the cache
+    totalling at least 1 GiB so that it streams from HBM. Returns its time
+    per decode, its bandwidth against the HBM roofline and the ratio to the
+    compressed step time (which also includes the appends)."""
+    B, HQ, H, d, N = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.d, wl.n_ctx
+    cap = wl.capacity
+    pairs = [(b, h) for b in range(B) for h in range(H)]
+    k = torch.empty((B * H * cap, d), dtype=torch.bfloat16, device="cuda")
+    vt = torch.empty((B * H * cap, d), dtype=torch.bfloat16, device="cuda")
+    per = max(1, min(len(pairs), int(2e9 // (N * d * 8))))
+    with ThreadPoolExecutor(_threads()) as ex:
+        for i in range(0, len(pairs), per):
+            chunk = pairs[i:i + per]
+            ks = list(ex.map(lambda p: synth.draw_kv_slab(wl, "K", p[0], p[1], 0, N), chunk))
+            vs = list(ex.map(lambda p: synth.draw_kv_slab(wl, "V", p[0], p[1], 0, N), chunk))
+            for (b, h), kx, vx in zip(chunk, ks, vs):
+                r0 = (b * H + h) * cap
+                k[r0:r0 + N] = torch.from_numpy(kx).cuda().to(torch.bfloat16)
+                vt[r0:r0 + N] = torch.from_numpy(vx).cuda().to(torch.bfloat16)
+    v = vt.reshape(B * H * cap // 32, 32, d).transpose(1, 2).contiguous()
+    del vt
+    cache_bytes = 2 * k.numel() * 2
+    n_copies = max(1, math.ceil((1 << 30) / cache_bytes))
+    caches = [(k, v)] + [(k.clone(), v.clone()) for _ in range(n_copies - 1)]
+    shape = tq.decode_shape(B, HQ, H, N, cap, wl.scale)
+    ws = torch.empty(tq.tq_attn_decode_bf16_workspace_bytes(shape, d), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, HQ, d), dtype=torch.float32, device="cuda")
+    for i in range(n_copies):
+        tq.tq_attn_decode_bf16(shape, q, caches[i][0], caches[i][1], out, workspace=ws)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(n_copies):
+            tq.tq_attn_decode_bf16(shape, q, caches[i][0], caches[i][1], out, workspace=ws)
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, math.ceil(launches / n_copies))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * n_copies)
+    algo = B * H * N * d * 2 * 2  # bf16 K and V of every cached token
+    gbs = algo / (ms / 1e3) / 1e9
+    del caches, k, v
+    return {"kernel": "bf16_split_kernel + bf16_combine_kernel", "us_per_decode": round(ms * 1e3, 2),
+            "cached_tokens_per_s": B * N / (ms / 1e3), "algorithmic_bytes": int(algo),
+            "achieved_gbs": round(gbs, 1), "peak_gbs": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "cache_copies": n_copies, "compressed_step_speedup": round(ms / step_ms, 3)}
 
 
 def cpu_baseline(wl, budget_s):
@@ -347,6 +404,9 @@ def main():
         torch.cuda.synchronize()
         log(f"copy probe: 3 device copies of {COPY_PROBE_BYTES} bytes")
         del src, dst
+    if not args.no_bf16_baseline:
+        result["bf16_baseline"] = bf16_baseline(tq, torch, wl, q, ms_step)
+        log(f"bf16 baseline: {result['bf16_baseline']}")
     if not args.no_quantize_bench:
         result["quantize"] = quantize_bench(tq, torch, wl, kq)
         log(f"quantize: {result['quantize']}")

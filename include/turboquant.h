@@ -316,6 +316,31 @@ tq_status tq_attn_decode_append(const tq_quantizer* kq, const tq_quantizer* vq,
                                 const tq_cache* k_cache, const tq_cache* v_cache, float* logits,
                                 float* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Uncompressed decode baseline: the same decode step over bf16 K/V caches,
+ * for comparison with tq_attn_decode ([WD] "Os numeros que importam": the
+ * reported speed-ups are against unquantized keys). For each batch b and
+ * query head h over KV head h_kv:
+ *   logits[b, h, t] = scale * <q[b, h], k[b, h_kv, t]>  for t < n_ctx,
+ *   out[b, h]       = sum_t softmax(logits[b, h])_t v[b, h_kv, t],
+ * with fp32 accumulation (the scaled query and the softmax weights enter the
+ * bf16 products as hi + lo bf16 pairs).
+ *   shape    as tq_attn_decode (n_split 0 = automatic); d = 128.
+ *   q        device [batch, n_q_heads, d], f32 or bf16, 16-byte aligned.
+ *   k        device bf16 [batch * n_kv_heads * cache_capacity, d], token-major
+ *            (KV head bh owns rows [bh * cache_capacity, (bh + 1) * cache_capacity)).
+ *   v        device bf16 [batch * n_kv_heads * cache_capacity / 32, d, 32]: the
+ *            rows in blocks of 32, channel-major inside a block.
+ *   logits   device fp32 [batch, n_q_heads, n_ctx], or NULL.
+ *   out      device fp32 [batch, n_q_heads, d].
+ *   workspace device scratch of at least tq_attn_decode_bf16_workspace_bytes().
+ * Rows past n_ctx inside the last 32-row block are ignored, whatever they
+ * hold. Errors: TQ_ERR_INVALID (shape, null or misaligned pointers, dtype),
+ * TQ_ERR_UNSUPPORTED (d != 128), TQ_ERR_WORKSPACE, TQ_ERR_DEVICE. */
+tq_status tq_attn_decode_bf16_workspace_bytes(const tq_decode_shape* shape, int d, size_t* bytes);
+tq_status tq_attn_decode_bf16(const tq_decode_shape* shape, int d, const void* q, tq_dtype q_dtype,
+                              const void* k, const void* v, float* logits, float* out, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

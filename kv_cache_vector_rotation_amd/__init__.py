@@ -42,7 +42,8 @@ TQ_PHASE_ALL = 7
 
 SYMBOLS = ("tq_abi_version", "tq_status_string", "tq_build_codebook", "tq_record_layout",
            "tq_fold_sketch", "tq_quantize", "tq_attn_decode_workspace_bytes", "tq_attn_decode",
-           "tq_attn_decode_phases", "tq_attn_decode_append")
+           "tq_attn_decode_phases", "tq_attn_decode_append", "tq_attn_decode_bf16_workspace_bytes",
+           "tq_attn_decode_bf16")
 
 
 class TQError(RuntimeError):
@@ -135,6 +136,13 @@ def lib() -> C.CDLL:
         L.tq_attn_decode_append.argtypes = (L.tq_attn_decode.argtypes[:3] +
                                             [C.POINTER(tq_append), C.POINTER(tq_append)] +
                                             L.tq_attn_decode.argtypes[3:])
+        L.tq_attn_decode_bf16_workspace_bytes.restype = C.c_int
+        L.tq_attn_decode_bf16_workspace_bytes.argtypes = [C.POINTER(tq_decode_shape), C.c_int,
+                                                          C.POINTER(C.c_size_t)]
+        L.tq_attn_decode_bf16.restype = C.c_int
+        L.tq_attn_decode_bf16.argtypes = [C.POINTER(tq_decode_shape), C.c_int, C.c_void_p, C.c_int, C.c_void_p,
+                                          C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
+                                          C.c_void_p]
         _lib = L
     return _lib
 
@@ -425,11 +433,37 @@ def tq_attn_decode_append(kq: Quantizer, vq: Optional[Quantizer], shape: tq_deco
            "tq_attn_decode_append")
 
 
+def tq_attn_decode_bf16_workspace_bytes(shape: tq_decode_shape, d: int = 128) -> int:
+    n = C.c_size_t()
+    _check(lib().tq_attn_decode_bf16_workspace_bytes(C.byref(shape), d, C.byref(n)),
+           "tq_attn_decode_bf16_workspace_bytes")
+    return int(n.value)
+
+
+def tq_attn_decode_bf16(shape: tq_decode_shape, q, k, v, out, logits=None, workspace=None, stream=None) -> None:
+    """Uncompressed baseline decode (see include/turboquant.h): q [batch,
+    n_q_heads, d] float32/bfloat16; k bf16 [batch*n_kv_heads*capacity, d];
+    v bf16 [batch*n_kv_heads*capacity/32, d, 32]; out / logits float32 device
+    tensors; workspace: uint8 device tensor (allocated here if None)."""
+    torch = _torch()
+    for t in (q, k, v, out):
+        if not t.is_contiguous():
+            raise ValueError("q, k, v and out must be contiguous")
+    dt = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}[q.dtype]
+    d = int(q.shape[-1])
+    if workspace is None:
+        workspace = torch.empty(tq_attn_decode_bf16_workspace_bytes(shape, d), dtype=torch.uint8, device=q.device)
+    _check(lib().tq_attn_decode_bf16(C.byref(shape), d, _ptr(q), dt, _ptr(k), _ptr(v), _ptr(logits), _ptr(out),
+                                     _ptr(workspace), workspace.numel(), _stream(stream)),
+           "tq_attn_decode_bf16")
+
+
 __all__ = [
     "LIB_PATH", "SYMBOLS", "lib", "TQError", "Quantizer", "Cache", "make_layout", "decode_shape",
     "tq_abi_version", "tq_status_string", "tq_build_codebook", "tq_record_layout", "tq_fold_sketch",
     "tq_quantize", "tq_attn_decode_workspace_bytes", "tq_attn_decode", "tq_attn_decode_phases",
-    "tq_attn_decode_append", "append_spec", "tq_append",
+    "tq_attn_decode_append", "append_spec", "tq_append", "tq_attn_decode_bf16_workspace_bytes",
+    "tq_attn_decode_bf16",
     "TQ_PHASE_PREP", "TQ_PHASE_SPLIT", "TQ_PHASE_COMBINE", "TQ_PHASE_ALL",
     "TQ_OK", "TQ_ERR_INVALID", "TQ_ERR_UNSUPPORTED", "TQ_ERR_NOCONVERGE", "TQ_ERR_WORKSPACE",
     "TQ_ERR_DEVICE", "TQ_F32", "TQ_BF16", "TQ_TOKEN_MAJOR", "TQ_BLOCK32",

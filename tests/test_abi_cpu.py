@@ -30,7 +30,7 @@ def tq():
 def test_header_symbols_exported(tq):
     text = open(HEADER).read()
     declared = sorted(set(re.findall(r"^\s*(?:tq_status|int|const char\*)\s+(tq_\w+)\s*\(", text, re.M)))
-    assert len(declared) == 10
+    assert len(declared) == 12
     lib = C.CDLL(tq.LIB_PATH)
     for name in declared:
         assert hasattr(lib, name), name
@@ -224,3 +224,26 @@ def test_decode_append_validation(tq):
     assert call(app(n_vec=-1), None) == tq.TQ_ERR_INVALID
     assert lib.tq_attn_decode_append(C.byref(kq), None, C.byref(shape), None, C.byref(app()), FAKE, 1,
                                      C.byref(kc), None, FAKE, None, FAKE, need.value, None) == tq.TQ_ERR_INVALID
+
+
+def test_bf16_baseline_validation(tq):
+    # the uncompressed baseline: sizing and every argument error before any launch
+    lib = tq.lib()
+    shape = tq.decode_shape(2, 32, 8, 1000, 1024, 0.088)
+    need = C.c_size_t()
+    assert lib.tq_attn_decode_bf16_workspace_bytes(C.byref(shape), 128, C.byref(need)) == 0
+    # 2 * 32 heads x n_split x (2 + 128) floats, n_split for about 512 workgroups
+    n_split = min(512 // 16, (32 + 3) // 4)
+    assert need.value == 2 * 32 * n_split * 130 * 4
+    assert lib.tq_attn_decode_bf16_workspace_bytes(C.byref(shape), 64, C.byref(need)) == tq.TQ_ERR_UNSUPPORTED
+
+    def call(shape=shape, d=128, q=FAKE, dt=1, k=FAKE, v=FAKE, out=FAKE, ws=FAKE, wsb=need.value):
+        return lib.tq_attn_decode_bf16(C.byref(shape), d, q, dt, k, v, None, out, ws, wsb, None)
+
+    assert call(wsb=need.value - 1) == tq.TQ_ERR_WORKSPACE
+    assert call(dt=7) == tq.TQ_ERR_INVALID
+    assert call(out=None) == tq.TQ_ERR_INVALID
+    assert call(k=FAKE + 2) == tq.TQ_ERR_INVALID  # misaligned
+    assert call(d=64) == tq.TQ_ERR_UNSUPPORTED
+    assert call(shape=tq.decode_shape(2, 30, 8, 1000, 1024, 0.088)) == tq.TQ_ERR_INVALID  # heads not a multiple
+    assert call(shape=tq.decode_shape(2, 32, 8, 1000, 1000, 0.088)) == tq.TQ_ERR_INVALID  # capacity % 32
