@@ -1202,6 +1202,7 @@ constexpr int kStepKP = 128, kStepNT = 8;  // quantize shape for d = 128
 struct StepArgs {
   tqq::QArgs k, v;
   int nk, nv;  // blocks given to the K and V appends (0 = none)
+  int k_small, v_small;  // append takes the one-block-per-vector path
   tqp::PrepArgs prep;
   int prep_x;  // prep blocks along x; the prep blocks are laid out x-major
 };
@@ -1211,7 +1212,10 @@ __global__ __launch_bounds__(kStepNT * 64) void step_kernel(StepArgs s) {
   const int b = blockIdx.x;
   if (b < s.nk + s.nv) {
     const bool is_k = b < s.nk;
-    tqq::quantize_tiles<kStepKP, kStepNT>(is_k ? s.k : s.v, is_k ? b : b - s.nk, is_k ? s.nk : s.nv, smem);
+    if (is_k ? s.k_small : s.v_small)
+      tqq::quantize_small<kStepNT * 64>(is_k ? s.k : s.v, is_k ? b : b - s.nk, smem);
+    else
+      tqq::quantize_tiles<kStepKP, kStepNT>(is_k ? s.k : s.v, is_k ? b : b - s.nk, is_k ? s.nk : s.nv, smem);
   } else {
     const int pb = b - s.nk - s.nv;
     tqp::prep_block<kD, kStepNT * 64>(s.prep, pb % s.prep_x, pb / s.prep_x, threadIdx.x, smem);
@@ -1265,13 +1269,17 @@ extern "C" tq_status tq_attn_decode_append(const tq_quantizer* kq, const tq_quan
     int v = 0;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) n_cu = v;
   }
-  sa.nk = k_empty ? 0 : (int)(sa.k.n_tiles < n_cu ? sa.k.n_tiles : n_cu);
-  sa.nv = v_empty ? 0 : (int)(sa.v.n_tiles < n_cu ? sa.v.n_tiles : n_cu);
+  // (a few vectors: one block per vector, as tq_quantize does for them)
+  sa.k_small = !k_empty && tqq::small_path_ok(sa.k);
+  sa.v_small = !v_empty && tqq::small_path_ok(sa.v);
+  sa.nk = k_empty ? 0 : sa.k_small ? (int)sa.k.n_vec : (int)(sa.k.n_tiles < n_cu ? sa.k.n_tiles : n_cu);
+  sa.nv = v_empty ? 0 : sa.v_small ? (int)sa.v.n_vec : (int)(sa.v.n_tiles < n_cu ? sa.v.n_tiles : n_cu);
   sa.prep = pl.prep;
   sa.prep_x = tqp::prep_blocks_x<kD>();
   const int grid = sa.nk + sa.nv + sa.prep_x * pl.prep_grid_y;
   using L = tqq::Lds<kStepKP, kStepNT>;
-  constexpr int lds = L::bytes > tqp::prep_lds_bytes<kD>() ? L::bytes : tqp::prep_lds_bytes<kD>();
+  constexpr int lds0 = L::bytes > tqp::prep_lds_bytes<kD>() ? L::bytes : tqp::prep_lds_bytes<kD>();
+  constexpr int lds = lds0 > tqq::SmallLds<kStepNT * 64>::bytes ? lds0 : tqq::SmallLds<kStepNT * 64>::bytes;
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(&step_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
                           lds) != hipSuccess)
     return TQ_ERR_DEVICE;

@@ -5,7 +5,9 @@
 // cell, take the residual of that MSE quantizer, keep the signs of a Gaussian
 // sketch of the residual, and store codes, sign bits and the norms.
 //
-// Work decomposition. A workgroup owns a tile of 64 vectors at a time and
+// Work decomposition (calls with more than a few vectors; a few vectors take
+// the one-workgroup-per-vector latency path described with quantize_small).
+// A workgroup owns a tile of 64 vectors at a time and
 // loops over tiles (grid-stride). It has one wave per 16 output coordinates
 // (d rounded up to 16), so a wave's slice of the d x d matrices stays in
 // registers for the whole kernel, as the B operand of
@@ -35,6 +37,18 @@ template <int KP, int NT>
 __global__ __launch_bounds__(NT * 64) void quantize_kernel(QArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   tqq::quantize_tiles<KP, NT>(a, blockIdx.x, gridDim.x, smem);
+}
+
+__global__ __launch_bounds__(tqq::kSmallThreads) void quantize_small_kernel(QArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  tqq::quantize_small<tqq::kSmallThreads>(a, blockIdx.x, smem);
+}
+
+tq_status launch_quantize_small(const QArgs& a, hipStream_t stream) {
+  (void)hipGetLastError();  // a launch error is reported below, not an older one
+  hipLaunchKernelGGL(quantize_small_kernel, dim3((unsigned)a.n_vec), dim3(tqq::kSmallThreads),
+                     tqq::SmallLds<tqq::kSmallThreads>::bytes, stream, a);
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_DEVICE;
 }
 
 template <int KP, int NT>
@@ -69,6 +83,8 @@ extern "C" tq_status tq_quantize(const tq_quantizer* qz, tq_format fmt, const vo
   const tq_status st = tqq::make_qargs(qz, fmt, x, x_dtype, n_vec, x_row_stride, rows, cache, &a, &empty);
   if (st != TQ_OK || empty) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // a few vectors (an append): one workgroup per vector, for latency
+  if (tqq::small_path_ok(a)) return launch_quantize_small(a, s);
   switch (tqq::quantize_kp(a.d)) {
     case 64: return launch_quantize<64, 4>(a, s);
     case 128: return launch_quantize<128, 8>(a, s);

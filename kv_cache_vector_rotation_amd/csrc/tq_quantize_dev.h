@@ -788,6 +788,294 @@ __device__ __forceinline__ void quantize_tiles(const QArgs& a, int64_t first_til
   }
 }
 
+// ---------------------------------------------------------------------------
+// Latency path for a few vectors (the appends of a decode step): one
+// workgroup of 512 threads per vector and no tiles. Thread t owns output
+// coordinate o = t / 4 and a quarter of the inner index (h = t % 4: the
+// 16-byte chunks 16 i + 4 h). Its pieces of rot and sketch_rot (8 x 16
+// bytes each) and the matching entries of the vector are loaded at once,
+// each product is four fp32 FMA chains summed within the lane quad, and
+// three barriers separate the group norms, the cells and residual, and the
+// sign bits. Codes and signs are
+// assembled into record words in LDS. A token-major record belongs to its
+// row alone and is stored word by word; a block record shares its words with
+// the block's other tokens (possibly written by other workgroups of the same
+// call), so each touched word takes this vector's bits by an atomic AND
+// (clear) and an atomic OR (set) on exactly those bits.
+// ---------------------------------------------------------------------------
+constexpr int kSmallMaxVec = 64;    // calls with at most this many vectors take this path
+constexpr int kSmallThreads = 512;
+constexpr int kSmallWords = 768;    // record words assembled in LDS
+
+template <int NTHR>
+struct SmallLds {
+  static constexpr int off_np = 0;                        // float [8]: per-wave sums of y^2
+  static constexpr int off_gp = off_np + 8 * 4;           // float [8]: per-wave sums of r^2
+  static constexpr int off_r = off_gp + 8 * 4;            // float [128]: rotated residual
+  static constexpr int off_bits = off_r + 128 * 4;        // u32 [kSmallWords]
+  static constexpr int off_mask = off_bits + kSmallWords * 4;
+  static constexpr int bytes = off_mask + kSmallWords * 4;
+};
+
+// Whether a call (already validated by make_qargs) takes the latency path.
+inline bool small_path_ok(const QArgs& a) {
+  const int words = a.fmt == TQ_TOKEN_MAJOR ? a.code_words + a.sign_words : a.blk_code_words + a.blk_sign_words;
+  return a.n_vec <= kSmallMaxVec && a.d <= 128 && a.d >= 4 && a.m_vec && words <= kSmallWords;
+}
+
+// Sum over the whole wave, the same value in every lane (lane moves only:
+// DPP within rows of 16, then swaps of the 32-lane halves and of the 16-lane
+// rows inside each half).
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Sum of the per-wave partials p[w0 .. w1) (in that order) from LDS, read as
+// two 16-byte words.
+__device__ __forceinline__ float wave_range_sum(const float* p, int w0, int w1) {
+  const f32x4 lo = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 hi = *reinterpret_cast<const f32x4*>(p + 4);
+  const float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) s += (k >= w0 && k < w1) ? v[k] : 0.f;
+  return s;
+}
+
+// ORs an m-bit field at bit position pos of the LDS words into bits / mask.
+__device__ __forceinline__ void or_field(uint32_t* bits, uint32_t* mask, int pos, uint32_t val, int m) {
+  const int wi = pos >> 5, bi = pos & 31;
+  const uint32_t fm = (1u << m) - 1u;
+  atomicOr(bits + wi, val << bi);
+  atomicOr(mask + wi, fm << bi);
+  if (bi + m > 32) {
+    atomicOr(bits + wi + 1, val >> (32 - bi));
+    atomicOr(mask + wi + 1, fm >> (32 - bi));
+  }
+}
+
+template <int NTHR>
+__device__ __forceinline__ void quantize_small(const QArgs& a, int64_t vec, unsigned char* smem) {
+  static_assert(NTHR == 512, "four threads per output coordinate, d <= 128");
+  using L = SmallLds<NTHR>;
+  float* s_np = reinterpret_cast<float*>(smem + L::off_np);
+  float* s_gp = reinterpret_cast<float*>(smem + L::off_gp);
+  float* s_r = reinterpret_cast<float*>(smem + L::off_r);
+  uint32_t* s_bits = reinterpret_cast<uint32_t*>(smem + L::off_bits);
+  uint32_t* s_mask = reinterpret_cast<uint32_t*>(smem + L::off_mask);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int o = tid >> 2, h = tid & 3;
+  const int d = a.d;
+  const bool tok = a.fmt == TQ_TOKEN_MAJOR;
+
+  // ---- loads, all issued before the first use: rows o of rot and
+  // sketch_rot (indices clamped into the matrix, out-of-range entries zeroed
+  // afterwards), the matching entries of the vector, the codebook (lane k of
+  // every 16 holds centroid k and boundary k). Thread h of a coordinate takes
+  // the 16-byte chunks k = 16 i + 4 h, i = 0 .. 7, so the four threads of a
+  // row read 64 contiguous bytes per load instruction ----
+  const int oc = o < d ? o : d - 1;
+  f32x4 rq[8], sq[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int k = 16 * i + 4 * h, kc = k < d ? k : d - 4;
+    rq[i] = *reinterpret_cast<const f32x4*>(a.rot + (int64_t)oc * d + kc);
+    sq[i] = *reinterpret_cast<const f32x4*>(a.skr + (int64_t)oc * d + kc);
+  }
+  float xv[32];  // xv[4 i + e] = x[16 i + 4 h + e]
+  if (a.x_vec && a.x_bf16) {
+    const uint16_t* xp = reinterpret_cast<const uint16_t*>(a.x) + vec * a.x_stride;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int k = 16 * i + 4 * h, kc = k < d ? k : d - 4;
+      const uint2 v = *reinterpret_cast<const uint2*>(xp + kc);
+      xv[4 * i] = __uint_as_float(v.x << 16);
+      xv[4 * i + 1] = __uint_as_float(v.x & 0xFFFF0000u);
+      xv[4 * i + 2] = __uint_as_float(v.y << 16);
+      xv[4 * i + 3] = __uint_as_float(v.y & 0xFFFF0000u);
+    }
+  } else if (a.x_vec) {
+    const float* xp = reinterpret_cast<const float*>(a.x) + vec * a.x_stride;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int k = 16 * i + 4 * h, kc = k < d ? k : d - 4;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(xp + kc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xv[4 * i + e] = v[e];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int k = 16 * (i / 4) + 4 * h + i % 4, kc = k < d ? k : d - 1;
+      xv[i] = a.x_bf16 ? __uint_as_float((uint32_t) reinterpret_cast<const uint16_t*>(a.x)[vec * a.x_stride + kc]
+                                         << 16)
+                       : reinterpret_cast<const float*>(a.x)[vec * a.x_stride + kc];
+    }
+  }
+  // The group of this wave's 16 coordinates (group boundaries are multiples
+  // of 16) and its parameters, chosen by selects rather than indexed reads of
+  // the argument block, and the destination row (a row index list is read
+  // through an always-valid address): every scalar argument is fetched here,
+  // in one round trip, instead of at its first use further down.
+  const int grp = (a.n_groups > 1 && 16 * w >= a.choff[1]) ? 1 : 0;
+  int mg = grp ? a.gbits[1] : a.gbits[0];
+  int choff = grp ? a.choff[1] : a.choff[0];
+  int gdim = grp ? a.gdim[1] : a.gdim[0];
+  int coff = grp ? a.coff[1] : a.coff[0];
+  int boff = grp ? a.boff[1] : a.boff[0];
+  int code_pos = tok ? 32 * (grp ? a.cwoff[1] : a.cwoff[0]) : 32 * (grp ? a.bcwoff[1] : a.bcwoff[0]);
+  int sign_pos = tok ? 32 * (a.code_words + (grp ? a.swoff[1] : a.swoff[0]))
+                     : 32 * (a.blk_code_words + (grp ? a.bswoff[1] : a.bswoff[0]));
+  int n_words = tok ? a.code_words + a.sign_words : a.blk_code_words + a.blk_sign_words;
+  int n_groups = a.n_groups, cw = a.code_words, sw = a.sign_words, bcw = a.blk_code_words,
+      bsw = a.blk_sign_words;
+  int c0 = a.choff[0], c1 = a.choff[1], g0 = a.gdim[0], g1 = a.gdim[1];
+  int64_t seg_len = a.seg_len, seg_stride = a.seg_stride, seg_offset = a.seg_offset, n_rows = a.n_rows;
+  uint32_t* codes = a.codes;
+  uint32_t* signs = a.signs;
+  float* norms = a.norms;
+  const int64_t* dst_rows = a.dst_rows;
+  int64_t row_listed = *(dst_rows ? dst_rows + vec : reinterpret_cast<const int64_t*>(a.rot));
+  // (opaque to the compiler from here on, so it keeps them in registers
+  // rather than reading the argument block again at each use)
+  asm volatile("" : "+s"(mg), "+s"(choff), "+s"(gdim), "+s"(coff), "+s"(boff), "+s"(code_pos), "+s"(sign_pos),
+               "+s"(n_words), "+s"(n_groups), "+s"(cw), "+s"(sw), "+s"(bcw), "+s"(bsw));
+  asm volatile("" : "+s"(c0), "+s"(c1), "+s"(g0), "+s"(g1), "+s"(seg_len), "+s"(seg_stride), "+s"(seg_offset),
+               "+s"(n_rows), "+s"(codes), "+s"(signs), "+s"(norms), "+s"(dst_rows));
+  const int nb = (1 << mg) - 1;
+  const int kc = (lane & 15) < nb ? (lane & 15) : nb - 1;
+  const float bnd_l = a.boundaries[boff + kc];
+  const float cen_l = a.centroids[coff + kc + ((lane & 15) == nb ? 1 : 0)];
+  for (int e = tid; e < n_words; e += NTHR) {
+    s_bits[e] = 0u;
+    s_mask[e] = 0u;
+  }
+  const bool live = o < d;
+  if (d < 128) {  // (uniform) entries past d were loaded from clamped indices
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bool ok = live && 16 * i + 4 * h < d;
+      if (!ok) {
+        rq[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sq[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+      if (16 * (i / 4) + 4 * h + i % 4 >= d) xv[i] = 0.f;
+  }
+
+  // ---- y_o = rot[o] . x: four FMA chains, then the lane quad ----
+  float y;
+  {
+    float c4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) c4[j] = fmaf(rq[i][j], xv[4 * i + j], c4[j]);
+    y = (c4[0] + c4[1]) + (c4[2] + c4[3]);
+    y += dpp_f<0xB1>(y);
+    y += dpp_f<0x4E>(y);
+  }
+  {
+    const float t = wave_sum(h == 0 ? y * y : 0.f);
+    if (lane == 0) s_np[w] = t;
+  }
+  __syncthreads();
+
+  // ---- group norm, cell, residual (rotated domain), code field ----
+  // (the destination row is formed here, off the path of the loads; a row
+  // outside the cache, the same for the whole workgroup, stores nothing)
+  // (vec < kSmallMaxVec here, so a segment length clamped to kSmallMaxVec
+  // gives the same quotient and remainder in 32-bit arithmetic)
+  const int seg = seg_len < kSmallMaxVec ? (int)seg_len : kSmallMaxVec;
+  const int64_t row = dst_rows ? row_listed : (int64_t)((int)vec / seg) * seg_stride + seg_offset + (int)vec % seg;
+  const bool row_ok = row >= 0 && row < n_rows;
+  const int w0 = choff / 16, w1 = (choff + gdim + 15) / 16;
+  const float nv = sqrtf(wave_range_sum(s_np, w0, w1));
+  int idx;
+  {
+    const float u = y * __builtin_amdgcn_rcpf(nv);
+    int c = 0;
+#pragma unroll
+    for (int k = 0; k < 15; ++k) {
+      const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bnd_l), k));
+      c += (k < nb && u > b) ? 1 : 0;
+    }
+    idx = nv > 0.f ? c : (nb + 1) / 2 - 1;
+  }
+  const float cv = __shfl(cen_l, idx, 64);  // centroid idx (lanes 0 .. 15 hold them)
+  float rr = nv > 0.f ? fmaf(-nv, cv, y) : 0.f;
+  if (!live) {
+    rr = 0.f;
+    idx = 0;
+  }
+  if (h == 0) s_r[o] = rr;
+  {
+    const float t = wave_sum(h == 0 ? rr * rr : 0.f);
+    if (lane == 0) s_gp[w] = t;
+  }
+  const int j = o - choff;  // channel within the group
+  const int slot = (int)(row & 31), quarter = slot >> 3, sl = slot & 7;
+  if (h == 0 && live && row_ok) {
+    const int pos = tok ? code_pos + mg * j : code_pos + 8 * mg * (quarter * gdim + j) + mg * sl;
+    or_field(s_bits, s_mask, pos, (uint32_t)idx, mg);
+  }
+  __syncthreads();
+
+  // ---- s_o = sketch_rot[o] . r; sign bit = [s >= 0] ----
+  {
+    float c4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const f32x4 r4 = *reinterpret_cast<const f32x4*>(s_r + 16 * i + 4 * h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c4[e] = fmaf(sq[i][e], r4[e], c4[e]);
+    }
+    float sv = (c4[0] + c4[1]) + (c4[2] + c4[3]);
+    sv += dpp_f<0xB1>(sv);
+    sv += dpp_f<0x4E>(sv);
+    if (h == 0 && live && row_ok) {
+      const int pos = tok ? sign_pos + j : sign_pos + 8 * (quarter * gdim + j) + sl;
+      or_field(s_bits, s_mask, pos, sv >= 0.f ? 1u : 0u, 1);
+    }
+  }
+  __syncthreads();
+
+  // ---- store: norms (n_g, gamma_g), then the record words ----
+  if (!row_ok) return;
+  if (tid < n_groups) {
+    const int g = tid;
+    const int cg = g ? c1 : c0, dg = g ? g1 : g0;
+    const int v0 = cg / 16, v1 = (cg + dg + 15) / 16;
+    norms[row * (2 * n_groups) + 2 * g] = sqrtf(wave_range_sum(s_np, v0, v1));
+    norms[row * (2 * n_groups) + 2 * g + 1] = sqrtf(wave_range_sum(s_gp, v0, v1));
+  }
+  if (tok) {
+    for (int e = tid; e < n_words; e += NTHR) {
+      if (e < cw)
+        codes[row * cw + e] = s_bits[e];
+      else
+        signs[row * sw + e - cw] = s_bits[e];
+    }
+  } else {
+    const int64_t blk = row >> 5;
+    for (int e = tid; e < n_words; e += NTHR) {
+      const uint32_t m = s_mask[e];
+      if (m == 0u) continue;
+      uint32_t* dst = e < bcw ? codes + blk * bcw + e : signs + blk * bsw + (e - bcw);
+      atomicAnd(dst, ~m);
+      atomicOr(dst, s_bits[e] & m);
+    }
+  }
+}
+
 // Validates the arguments of one quantize call and fills its kernel
 // arguments. Returns TQ_OK with *empty = true for n_vec == 0.
 inline tq_status make_qargs(const tq_quantizer* qz, tq_format fmt, const void* x, tq_dtype x_dtype,

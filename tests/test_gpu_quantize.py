@@ -165,3 +165,91 @@ def test_empty_call_is_noop(tq):
     tq.tq_quantize(dq, tq.TQ_TOKEN_MAJOR, torch.zeros((0, 128), device="cuda"), cache)
     torch.cuda.synchronize()
     assert int(cache.codes.abs().sum()) == 0
+
+
+# Calls with at most 64 vectors take the one-workgroup-per-vector path.
+SMALL_CASES = [
+    # name, overrides, kind, format, dtype, n_vec
+    ("llama8b_decode", {}, "K", "TQ_TOKEN_MAJOR", "bf16", 1),
+    ("llama8b_decode", {}, "V", "TQ_BLOCK32", "bf16", 64),
+    ("mixed_3p5", {}, "K", "TQ_TOKEN_MAJOR", "bf16", 17),
+    ("mixed_3p5", {}, "V", "TQ_BLOCK32", "bf16", 17),
+    ("mixed_2p5", {}, "V", "TQ_BLOCK32", "bf16", 5),
+    ("tiny", {}, "K", "TQ_BLOCK32", "f32", 40),
+    ("llama8b_decode", dict(d=64, groups=((64, 1),), n_outliers=0), "K", "TQ_TOKEN_MAJOR", "bf16", 33),
+    ("llama8b_decode", dict(d=64, groups=((64, 4),), n_outliers=0), "V", "TQ_BLOCK32", "bf16", 33),
+    ("tiny", dict(d=100, groups=((100, 2),)), "K", "TQ_TOKEN_MAJOR", "f32", 9),
+    ("tiny", dict(d=120, groups=((120, 3),)), "K", "TQ_BLOCK32", "f32", 9),
+]
+
+
+@pytest.mark.parametrize("name,over,kind,fmt_name,dtype,n_vec", SMALL_CASES)
+def test_few_vectors_path(tq, name, over, kind, fmt_name, dtype, n_vec):
+    # a handful of vectors, one per 32-row block or packed into a block,
+    # into a cache pre-filled with ones: the records of the written rows
+    # against the oracle, every bit of the other rows kept
+    import torch
+    wl = synth.workload(name, **over)
+    spec = synth.draw_quantizer(wl, kind)
+    x = synth.draw_kv_slab(wl, kind, 1, 0, 0, n_vec).copy()
+    x[n_vec // 2] = 0.0  # a zero vector
+    rows = np.random.default_rng(n_vec).permutation(128)[:n_vec] * (3 if n_vec < 40 else 1)
+    n_rows = 384
+    oq, dq = gc.quantizers(spec)
+    fmt = getattr(tq, fmt_name)
+    cache = tq.Cache.empty(dq, n_rows, fmt)
+    cache.codes.fill_(-1)
+    cache.signs.fill_(-1)
+    xt = torch.from_numpy(x).cuda()
+    if dtype == "bf16":
+        xt = xt.to(torch.bfloat16)
+    tq.tq_quantize(dq, fmt, xt, cache, dst_rows=torch.from_numpy(rows.astype(np.int64)).cuda())
+    torch.cuda.synchronize()
+    got_all = gc.read_cache(cache, dq)
+    qv = oracle.quantize(x.astype(np.float64), oq)
+    gc.compare_records(x.astype(np.float64), oq, qv, gc.select_rows(got_all, rows))
+    untouched = np.setdiff1d(np.arange(n_rows), rows)
+    for g in range(len(dq.mse_bits)):
+        assert np.all(got_all[0][g][untouched] == 2 ** dq.mse_bits[g] - 1)
+        assert np.all(got_all[1][g][untouched])
+
+
+def test_few_vectors_unaligned_rows(tq):
+    # fp32 rows with a stride of d + 1 floats (no 16-byte loads), by segments
+    import torch
+    wl = synth.workload("tiny")
+    spec = synth.draw_quantizer(wl, "K")
+    x = synth.draw_kv_slab(wl, "K", 0, 0, 0, 12)
+    xs = torch.zeros((12, 129), device="cuda")
+    xs[:, :128] = torch.from_numpy(x).cuda()
+    oq, dq = gc.quantizers(spec)
+    for fmt in (tq.TQ_TOKEN_MAJOR, tq.TQ_BLOCK32):
+        cache = tq.Cache.empty(dq, 12 * 64, fmt)
+        tq.tq_quantize(dq, fmt, xs[:, :128], cache, seg_len=1, seg_stride=64, seg_offset=37)
+        torch.cuda.synchronize()
+        qv = oracle.quantize(x.astype(np.float64), oq)
+        gc.compare_records(x.astype(np.float64), oq, qv,
+                           gc.select_rows(gc.read_cache(cache, dq), np.arange(12) * 64 + 37))
+
+
+def test_few_vectors_agree_with_tiles(tq):
+    # the same 64 vectors through the few-vector path (one call) and the tile
+    # path (inside a 65-vector call): equal records up to the boundary rule
+    import torch
+    wl = synth.workload("llama8b_decode")
+    spec = synth.draw_quantizer(wl, "K")
+    x = synth.draw_kv_slab(wl, "K", 0, 4, 0, 65)
+    oq, dq = gc.quantizers(spec)
+    xt = torch.from_numpy(x).cuda().to(torch.bfloat16)
+    a = tq.Cache.empty(dq, 96, tq.TQ_TOKEN_MAJOR)
+    b = tq.Cache.empty(dq, 96, tq.TQ_TOKEN_MAJOR)
+    tq.tq_quantize(dq, tq.TQ_TOKEN_MAJOR, xt[:64], a, seg_len=64, seg_stride=64)
+    tq.tq_quantize(dq, tq.TQ_TOKEN_MAJOR, xt, b, seg_len=65, seg_stride=65)
+    torch.cuda.synchronize()
+    ca, cb = (c.codes.cpu().numpy().reshape(96, -1)[:64] for c in (a, b))
+    sa, sb = (c.signs.cpu().numpy().reshape(96, -1)[:64] for c in (a, b))
+    na, nb = (c.norms.cpu().numpy().reshape(96, -1)[:64] for c in (a, b))
+    assert np.mean(np.all(ca == cb, axis=1) & np.all(sa == sb, axis=1)) >= 0.95
+    # norms n to 1e-6 relative, residual norms gamma to 2e-6 n (the record rule)
+    assert np.all(np.abs(na[:, 0] - nb[:, 0]) <= 1e-6 * nb[:, 0])
+    assert np.all(np.abs(na[:, 1] - nb[:, 1]) <= 2e-6 * nb[:, 0])
