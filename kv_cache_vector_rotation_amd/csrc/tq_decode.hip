@@ -99,8 +99,6 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// value of another lane of the same 16-lane row (DPP control CTRL; lanes
-// whose source falls outside the row read 0)
 // DPP row move in which a lane whose source lies outside its 16-lane row keeps
 // its own value. Every lane uses the result, so the move is never placed
 // under a lane mask (a DPP read from a masked-off lane returns nothing).
@@ -1207,14 +1205,17 @@ struct StepArgs {
   int prep_x;  // prep blocks along x; the prep blocks are laid out x-major
 };
 
+// SMALL: every append takes the few-vector path (a smaller kernel without the
+// tile path, which is the usual decode step of one token per head).
+template <bool SMALL>
 __global__ __launch_bounds__(kStepNT * 64) void step_kernel(StepArgs s) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int b = blockIdx.x;
   if (b < s.nk + s.nv) {
     const bool is_k = b < s.nk;
-    if (is_k ? s.k_small : s.v_small)
+    if (SMALL || (is_k ? s.k_small : s.v_small))
       tqq::quantize_small<kStepNT * 64>(is_k ? s.k : s.v, is_k ? b : b - s.nk, smem);
-    else
+    else if constexpr (!SMALL)
       tqq::quantize_tiles<kStepKP, kStepNT>(is_k ? s.k : s.v, is_k ? b : b - s.nk, is_k ? s.nk : s.nv, smem);
   } else {
     const int pb = b - s.nk - s.nv;
@@ -1278,13 +1279,21 @@ extern "C" tq_status tq_attn_decode_append(const tq_quantizer* kq, const tq_quan
   sa.prep_x = tqp::prep_blocks_x<kD>();
   const int grid = sa.nk + sa.nv + sa.prep_x * pl.prep_grid_y;
   using L = tqq::Lds<kStepKP, kStepNT>;
-  constexpr int lds0 = L::bytes > tqp::prep_lds_bytes<kD>() ? L::bytes : tqp::prep_lds_bytes<kD>();
-  constexpr int lds = lds0 > tqq::SmallLds<kStepNT * 64>::bytes ? lds0 : tqq::SmallLds<kStepNT * 64>::bytes;
-  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&step_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                          lds) != hipSuccess)
+  constexpr int lds_small = tqp::prep_lds_bytes<kD>() > tqq::SmallLds<kStepNT * 64>::bytes
+                                ? tqp::prep_lds_bytes<kD>()
+                                : tqq::SmallLds<kStepNT * 64>::bytes;
+  constexpr int lds = L::bytes > lds_small ? L::bytes : lds_small;
+  const bool all_small = (k_empty || sa.k_small) && (v_empty || sa.v_small);
+  const void* fn = all_small ? reinterpret_cast<const void*>(&step_kernel<true>)
+                             : reinterpret_cast<const void*>(&step_kernel<false>);
+  const int lds_use = all_small ? lds_small : lds;
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds_use) != hipSuccess)
     return TQ_ERR_DEVICE;
   (void)hipGetLastError();  // a launch error is reported below, not an older one
-  hipLaunchKernelGGL(step_kernel, dim3(grid), dim3(kStepNT * 64), lds, hs, sa);
+  if (all_small)
+    hipLaunchKernelGGL(step_kernel<true>, dim3(grid), dim3(kStepNT * 64), lds_use, hs, sa);
+  else
+    hipLaunchKernelGGL(step_kernel<false>, dim3(grid), dim3(kStepNT * 64), lds_use, hs, sa);
   if (hipGetLastError() != hipSuccess) return TQ_ERR_DEVICE;
   return run_phases(pl, TQ_PHASE_SPLIT | TQ_PHASE_COMBINE, hs);
 }
