@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quantize-bench", action="store_true")
     ap.add_argument("--no-bf16-baseline", action="store_true")
+    ap.add_argument("--ctx-sweep", default="",
+                    help="comma-separated context lengths: also time the compressed step and the bf16 "
+                         "decode of the llama8b_decode shape at each (reported under ctx_sweep)")
     ap.add_argument("--no-graph", action="store_true", help="launch every step from Python")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (the reference for scaling "
@@ -146,7 +149,7 @@ def quantize_bench(tq, torch, wl, kq, n_vec=524288, launches=20):
             "frac": flops / s / 1e12 / PEAK_FP32_MFMA_TFLOPS, "dtype": "f32"}
 
 
-def bf16_baseline(tq, torch, wl, q, step_ms, launches=200):
+def bf16_baseline(tq, torch, wl, q, step_ms, launches=200, min_bytes=1 << 30, max_copies=None):
     """Secondary figure: the same decode over uncompressed bf16 K/V caches
     (tq_attn_decode_bf16: split-K pass and combine), on copies of the cache
     totalling at least 1 GiB so that it streams from HBM. Returns its time
@@ -170,7 +173,9 @@ def bf16_baseline(tq, torch, wl, q, step_ms, launches=200):
     v = vt.reshape(B * H * cap // 32, 32, d).transpose(1, 2).contiguous()
     del vt
     cache_bytes = 2 * k.numel() * 2
-    n_copies = max(1, math.ceil((1 << 30) / cache_bytes))
+    n_copies = max(1, math.ceil(min_bytes / cache_bytes))
+    if max_copies:
+        n_copies = min(n_copies, max_copies)
     caches = [(k, v)] + [(k.clone(), v.clone()) for _ in range(n_copies - 1)]
     shape = tq.decode_shape(B, HQ, H, N, cap, wl.scale)
     ws = torch.empty(tq.tq_attn_decode_bf16_workspace_bytes(shape, d), dtype=torch.uint8, device="cuda")
@@ -199,6 +204,68 @@ def bf16_baseline(tq, torch, wl, q, step_ms, launches=200):
             "cached_tokens_per_s": B * N / (ms / 1e3), "algorithmic_bytes": int(algo),
             "achieved_gbs": round(gbs, 1), "peak_gbs": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4),
             "cache_copies": n_copies, "compressed_step_speedup": round(ms / step_ms, 3)}
+
+
+def compressed_step_us(tq, torch, wl, kq, vq, n_copies, reps=20):
+    """Mean time of tq_attn_decode_append steps (graph of one step per cache
+    copy, replayed), in microseconds."""
+    B, HQ, H, N, cap = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.n_ctx, wl.capacity
+    prefix = N - wl.n_new
+    kc0, vc0 = build_caches(tq, torch, wl, kq, vq, prefix, cap)
+    caches = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(n_copies - 1)]
+    k_new, v_new = new_tokens(torch, wl, prefix)
+    q = torch.from_numpy(synth.draw_queries(wl)).cuda().to(torch.bfloat16)
+    shape = tq.decode_shape(B, HQ, H, N, cap, wl.scale)
+    ws = torch.empty(tq.tq_attn_decode_workspace_bytes(kq, vq, shape), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, HQ, wl.d), dtype=torch.float32, device="cuda")
+    k_app = tq.append_spec(k_new, seg_len=wl.n_new, seg_stride=cap, seg_offset=prefix)
+    v_app = tq.append_spec(v_new, seg_len=wl.n_new, seg_stride=cap, seg_offset=prefix)
+
+    def step(i):
+        tq.tq_attn_decode_append(kq, vq, shape, q, caches[i][0], caches[i][1], k_new=k_app, v_new=v_app,
+                                 out=out, workspace=ws)
+    for i in range(n_copies):
+        step(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(n_copies):
+            step(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * n_copies)
+
+
+def ctx_sweep(tq, torch, contexts):
+    """Compressed step against the bf16 baseline decode at several context
+    lengths of the llama8b_decode shape (both over rotated cache copies of at
+    least 256 MiB, at most 64 copies)."""
+    rows = []
+    base = synth.workload("llama8b_decode")
+    ks, vs = synth.draw_quantizer(base, "K"), synth.draw_quantizer(base, "V")
+    bits = [g.mse_bits for g in ks.groups]
+    kq = tq.Quantizer.from_parts(ks.rotations, ks.sketches, bits, perm=ks.perm)
+    vq = tq.Quantizer.from_parts(vs.rotations, vs.sketches, bits, perm=vs.perm)
+    for n in contexts:
+        wl = synth.workload("llama8b_decode", n_ctx=n)
+        rb = record_bytes([g for g, _ in wl.groups], [m for _, m in wl.groups])
+        comp_bytes = wl.batch * wl.n_kv_heads * wl.capacity * 2 * rb
+        copies = max(1, min(64, math.ceil((256 << 20) / comp_bytes)))
+        step_us = compressed_step_us(tq, torch, wl, kq, vq, copies)
+        q = torch.from_numpy(synth.draw_queries(wl)).cuda().to(torch.bfloat16)
+        b = bf16_baseline(tq, torch, wl, q, step_us / 1e3, min_bytes=256 << 20, max_copies=64)
+        rows.append({"n_ctx": n, "compressed_step_us": round(step_us, 2), "compressed_copies": copies,
+                     "bf16_decode_us": b["us_per_decode"], "bf16_copies": b["cache_copies"],
+                     "compressed_step_speedup": b["compressed_step_speedup"]})
+        log(f"ctx {n}: compressed step {step_us:.2f} us, bf16 decode {b['us_per_decode']:.2f} us")
+        torch.cuda.empty_cache()
+    return rows
 
 
 def cpu_baseline(wl, budget_s):
@@ -410,6 +477,8 @@ def main():
     if not args.no_quantize_bench:
         result["quantize"] = quantize_bench(tq, torch, wl, kq)
         log(f"quantize: {result['quantize']}")
+    if args.ctx_sweep:
+        result["ctx_sweep"] = ctx_sweep(tq, torch, [int(v) for v in args.ctx_sweep.split(",")])
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
         log(f"cpu baseline: {result['cpu_baseline']}")

@@ -850,16 +850,21 @@ __global__ __launch_bounds__(256) void prep_kernel(tqp::PrepArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// Split merge and back-transform, one block per query head:
+// Split merge and back-transform, kCombCols blocks per query head:
 //   M = max_s m_s, w_s = 2^(m_s - M), L = sum_s w_s l_s, acc = sum_s w_s acc_s,
 //   out = (rot^T acc_rot + sketch^T (alpha_g acc_sk)) / L.
+// Every block of a head forms the whole merged accumulator (the partials are
+// read by each of them) and back-transforms one slice of D / kCombCols
+// outputs, so a block pulls only that slice's columns of rot and sketch
+// through its compute unit (the matrices are the larger part of the bytes).
 // ---------------------------------------------------------------------------
 constexpr int kMaxSplit = 1024;
 
-// 1024 threads per head: the split sums and the back-transform are each cut
-// four ways across thread groups and finished through LDS, so every thread
-// has only a few independent loads in flight.
+// 1024 threads per block: the split sums are cut four ways across thread
+// groups and the back-transform 32 ways (rows of [rot; sketch]), both
+// finished through LDS.
 constexpr int kCombThreads = 1024;
+constexpr int kCombCols = 4;
 
 template <int D>
 __global__ __launch_bounds__(kCombThreads) void combine_kernel(const float* part, int n_split,
@@ -867,14 +872,30 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const float* part
                                                                int group_dim0, float* out) {
   constexpr int NW = kCombThreads / 64, NG = kCombThreads / (2 * D);  // waves, groups
   constexpr int PS = 2 + 2 * D;                                      // floats per partial
+  constexpr int OC = D / kCombCols;                                  // outputs per block
+  constexpr int RP = kCombThreads / OC;                              // row parts of [rot; sketch]
+  constexpr int JR = 2 * D / RP;                                     // rows per part
+  static_assert(JR * RP == 2 * D && D % JR == 0, "combine shape");
   __shared__ float s_w[kMaxSplit];
   __shared__ float s_part[NG][2 * D];
   __shared__ float s_acc[2 * D];
   __shared__ float s_red[NW];
+  __shared__ float s_out[RP][OC + 1];
   const int head = blockIdx.x;
+  const int cs = blockIdx.y;  // output slice
   const int t = threadIdx.x;
   const int lane = t & 63, wv = t >> 6;
   const float* P = part + (int64_t)head * n_split * PS;
+  // this thread's back-transform operands (no dependence on the merge, so
+  // their loads overlap it): output i = cs OC + t % OC, rows
+  // [JR r, JR r + JR) of [rot; sketch] with r = t / OC
+  const int io = t % OC, rp = t / OC;
+  const int i = cs * OC + io;
+  const int j0 = JR * rp;
+  const float* mat = (j0 < D ? rot + (int64_t)j0 * D : sketch + (int64_t)(j0 - D) * D) + i;
+  float mv[JR];
+#pragma unroll
+  for (int j = 0; j < JR; ++j) mv[j] = mat[(int64_t)j * D];
   // max over splits (log2 domain)
   float mx = -INFINITY;
   for (int s = t; s < n_split; s += kCombThreads) mx = fmaxf(mx, P[(int64_t)s * PS]);
@@ -920,26 +941,20 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const float* part
     s_acc[t] = acc;
   }
   __syncthreads();
-  // back-transform: out[i] = sum_j rot[j][i] acc_rot[j] + sum_j sketch[j][i] acc_sk[j];
-  // the 2 NG groups of D threads are (half, part of the j range) pairs
+  // back-transform of this block's outputs: out[i] = sum over the rows j of
+  // [rot; sketch] of M[j][i] acc[j], cut into RP parts of JR rows
   {
-    const int i = t % D, hq = t / D;  // hq = half * NG + part, 0 <= hq < 2 NG
-    const int half = hq / NG, qtr = hq % NG;
-    constexpr int JN = D / NG;
-    const float* mat = half == 0 ? rot : sketch;
-    const float* av = s_acc + half * D;
-    float o = 0.f;
-#pragma unroll 16
-    for (int j = qtr * JN; j < qtr * JN + JN; ++j) o = fmaf(mat[(int64_t)j * D + i], av[j], o);
-    __syncthreads();  // s_part is reused
-    s_part[hq / 2][(hq % 2) * D + i] = o;
-  }
-  __syncthreads();
-  if (t < D) {
     float o = 0.f;
 #pragma unroll
-    for (int k = 0; k < NG * 2; ++k) o += s_part[k / 2][(k % 2) * D + t];
-    out[(int64_t)head * D + t] = o / L;
+    for (int j = 0; j < JR; ++j) o = fmaf(mv[j], s_acc[j0 + j], o);
+    s_out[rp][io] = o;
+  }
+  __syncthreads();
+  if (t < OC) {
+    float o = 0.f;
+#pragma unroll 8
+    for (int r = 0; r < RP; ++r) o += s_out[r][t];
+    out[(int64_t)head * D + cs * OC + t] = o / L;
   }
 }
 
@@ -1183,7 +1198,8 @@ tq_status run_phases(const Plan& pl, unsigned phases, hipStream_t st) {
   }
   if (pl.with_v && (phases & TQ_PHASE_COMBINE)) {
     (void)hipGetLastError();  // a launch error is reported below, not an older one
-    hipLaunchKernelGGL((combine_kernel<D>), dim3(pl.n_heads), dim3(kCombThreads), 0, st, pl.a.part, pl.a.n_split,
+    hipLaunchKernelGGL((combine_kernel<D>), dim3(pl.n_heads, kCombCols), dim3(kCombThreads), 0, st, pl.a.part,
+                       pl.a.n_split,
                        pl.vrot, pl.vsketch, pl.group_dim0, pl.out);
     if (hipGetLastError() != hipSuccess) return TQ_ERR_DEVICE;
   }
