@@ -14,8 +14,10 @@ next of several copies of the compressed cache (at least 1 GiB in total).
 Prints one JSON line: cached tokens/s (batch * context / step time), the
 split-K kernel against the HBM roofline (HIP events around that kernel on
 its stream), the same decode over uncompressed bf16 K/V caches for
-comparison, a secondary quantize throughput on a 524,288-vector chunk, and
-the CPU oracle timed on a bounded sample as a baseline.
+comparison, a secondary quantize throughput on a 524,288-vector chunk, the
+nearest-neighbour search workload (10,000 queries over 1,000,000 compressed
+vectors, top 10, with its recall), and the CPU oracle timed on a bounded
+sample as a baseline.
 """
 from __future__ import annotations
 
@@ -59,6 +61,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quantize-bench", action="store_true")
     ap.add_argument("--no-bf16-baseline", action="store_true")
+    ap.add_argument("--no-search", action="store_true")
     ap.add_argument("--ctx-sweep", default="",
                     help="comma-separated context lengths: also time the compressed step and the bf16 "
                          "decode of the llama8b_decode shape at each (reported under ctx_sweep)")
@@ -204,6 +207,51 @@ def bf16_baseline(tq, torch, wl, q, step_ms, launches=200, min_bytes=1 << 30, ma
             "cached_tokens_per_s": B * N / (ms / 1e3), "algorithmic_bytes": int(algo),
             "achieved_gbs": round(gbs, 1), "peak_gbs": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4),
             "cache_copies": n_copies, "compressed_step_speedup": round(ms / step_ms, 3)}
+
+
+PEAK_FP16_MFMA_TFLOPS = 2500.0  # MI355X dense fp16 matrix, vendor figure
+
+
+def search_bench(tq, torch, reps=5):
+    """Secondary figure: nearest-neighbour search on the nn_search workload
+    (1,000,000 database vectors, d = 200, 4 bits; 10,000 queries; top 10):
+    the database is quantized on the device, then tq_search is timed with HIP
+    events. Reports queries/s, the dense-equivalent fp16 TFLOP/s of the scan
+    (2 flop x n_q x n_db x d for each of the rotated and the sketch products)
+    against the dense fp16 MFMA peak, and recall@10 against exact fp32 brute
+    force (torch matmul and top-k, query chunks)."""
+    wl = synth.workload("nn_search")
+    n_db, n_q, k = wl.n_ctx, 10_000, 10
+    spec = synth.draw_quantizer(wl, "K")
+    qz = tq.Quantizer.from_parts(spec.rotations, spec.sketches, [g.mse_bits for g in spec.groups], perm=spec.perm)
+    x = torch.from_numpy(synth.draw_mixture_vectors(wl, n_db, "db")).cuda()
+    q = torch.from_numpy(synth.draw_mixture_vectors(wl, n_q, "query")).cuda()
+    db = tq.Cache.empty(qz, n_db, tq.TQ_TOKEN_MAJOR)
+    tq.tq_quantize(qz, tq.TQ_TOKEN_MAJOR, x, db, seg_len=n_db, seg_stride=n_db)
+    ws = torch.empty(tq.tq_search_workspace_bytes(qz, n_db, n_q, k), dtype=torch.uint8, device="cuda")
+    oi = torch.empty((n_q, k), dtype=torch.int64, device="cuda")
+    osc = torch.empty((n_q, k), dtype=torch.float32, device="cuda")
+    tq.tq_search(qz, db, n_db, q, k, out_idx=oi, out_score=osc, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        tq.tq_search(qz, db, n_db, q, k, out_idx=oi, out_score=osc, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    hits = 0
+    for s0 in range(0, n_q, 1000):
+        ex = torch.topk(q[s0:s0 + 1000] @ x.T, k, dim=1).indices
+        got = oi[s0:s0 + 1000]
+        hits += int((got[:, :, None] == ex[:, None, :]).any(dim=2).sum())
+    flop = 2.0 * 2 * n_q * n_db * wl.d
+    tf = flop / (ms / 1e3) / 1e12
+    del x, db, ws
+    return {"workload": "nn_search", "n_db": n_db, "n_q": n_q, "d": wl.d, "k": k, "bits_per_channel": 4,
+            "ms_per_search": round(ms, 3), "queries_per_s": n_q / (ms / 1e3),
+            "bound": "mfma", "dense_equiv_tflops": round(tf, 1), "peak_tflops": PEAK_FP16_MFMA_TFLOPS,
+            "frac": round(tf / PEAK_FP16_MFMA_TFLOPS, 4), "recall_at_10": hits / (n_q * k)}
 
 
 def compressed_step_us(tq, torch, wl, kq, vq, n_copies, reps=20):
@@ -477,6 +525,9 @@ def main():
     if not args.no_quantize_bench:
         result["quantize"] = quantize_bench(tq, torch, wl, kq)
         log(f"quantize: {result['quantize']}")
+    if not args.no_search:
+        result["search"] = search_bench(tq, torch)
+        log(f"search: {result['search']}")
     if args.ctx_sweep:
         result["ctx_sweep"] = ctx_sweep(tq, torch, [int(v) for v in args.ctx_sweep.split(",")])
     if not args.no_cpu_baseline:

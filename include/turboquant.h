@@ -341,6 +341,29 @@ tq_status tq_attn_decode_bf16(const tq_decode_shape* shape, int d, const void* q
                               const void* k, const void* v, float* logits, float* out, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/* Nearest-neighbour search with the compressed codes ([WD] "Os numeros que
+ * importam": the method also serves vector search). Every query is scored
+ * against database rows [0, n_db) of a token-major cache with the
+ * inner-product estimator of tq_attn_decode at scale 1,
+ *   score(q, i) = n_i <Pi q, c[idx_i]> + alpha gamma_i <S q, z_i>,
+ * and its k best rows are returned in decreasing score order; equal scores
+ * go to the lower row index.
+ *   qz         the database's quantizer: one group, d = 128 or 200, m <= 3.
+ *   db         token-major cache holding the database records (n_rows >= n_db).
+ *   q          [n_q, d] fp32 or bf16, row-major, 16-byte aligned rows.
+ *   k          1 <= k <= 10.
+ *   out_idx    [n_q, k] int64 (8-byte aligned); -1 where fewer than k rows exist.
+ *   out_score  [n_q, k] fp32 (-inf where out_idx is -1).
+ *   workspace  device scratch of at least tq_search_workspace_bytes() bytes.
+ * Limits: 1 <= n_db < 2^31 - 1, 1 <= n_q <= 2^30.
+ * Errors: TQ_ERR_INVALID (sizes, k, null or misaligned pointers, dtype),
+ * TQ_ERR_UNSUPPORTED (layout outside the limits above), TQ_ERR_WORKSPACE,
+ * TQ_ERR_DEVICE. */
+tq_status tq_search_workspace_bytes(const tq_quantizer* qz, int64_t n_db, int64_t n_q, int k, size_t* bytes);
+tq_status tq_search(const tq_quantizer* qz, const tq_cache* db, int64_t n_db, const void* q, tq_dtype q_dtype,
+                    int64_t n_q, int k, int64_t* out_idx, float* out_score, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

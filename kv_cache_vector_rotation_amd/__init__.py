@@ -43,7 +43,7 @@ TQ_PHASE_ALL = 7
 SYMBOLS = ("tq_abi_version", "tq_status_string", "tq_build_codebook", "tq_record_layout",
            "tq_fold_sketch", "tq_quantize", "tq_attn_decode_workspace_bytes", "tq_attn_decode",
            "tq_attn_decode_phases", "tq_attn_decode_append", "tq_attn_decode_bf16_workspace_bytes",
-           "tq_attn_decode_bf16")
+           "tq_attn_decode_bf16", "tq_search_workspace_bytes", "tq_search")
 
 
 class TQError(RuntimeError):
@@ -143,6 +143,12 @@ def lib() -> C.CDLL:
         L.tq_attn_decode_bf16.argtypes = [C.POINTER(tq_decode_shape), C.c_int, C.c_void_p, C.c_int, C.c_void_p,
                                           C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
                                           C.c_void_p]
+        L.tq_search_workspace_bytes.restype = C.c_int
+        L.tq_search_workspace_bytes.argtypes = [C.POINTER(tq_quantizer), C.c_int64, C.c_int64, C.c_int,
+                                                C.POINTER(C.c_size_t)]
+        L.tq_search.restype = C.c_int
+        L.tq_search.argtypes = [C.POINTER(tq_quantizer), C.POINTER(tq_cache), C.c_int64, C.c_void_p, C.c_int,
+                                C.c_int64, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
         _lib = L
     return _lib
 
@@ -458,12 +464,43 @@ def tq_attn_decode_bf16(shape: tq_decode_shape, q, k, v, out, logits=None, works
            "tq_attn_decode_bf16")
 
 
+def tq_search_workspace_bytes(quantizer: Quantizer, n_db: int, n_q: int, k: int) -> int:
+    n = C.c_size_t()
+    q = quantizer.struct()
+    _check(lib().tq_search_workspace_bytes(C.byref(q), n_db, n_q, k, C.byref(n)), "tq_search_workspace_bytes")
+    return int(n.value)
+
+
+def tq_search(quantizer: Quantizer, db: Cache, n_db: int, q, k: int, out_idx=None, out_score=None,
+              workspace=None, stream=None):
+    """k best database rows per query (see include/turboquant.h): q [n_q, d]
+    float32/bfloat16 device tensor; db a token-major Cache; returns
+    (out_idx int64 [n_q, k], out_score float32 [n_q, k]) device tensors."""
+    torch = _torch()
+    if not q.is_contiguous() or q.dim() != 2:
+        raise ValueError("q must be a contiguous [n_q, d] tensor")
+    dt = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}[q.dtype]
+    n_q = int(q.shape[0])
+    if out_idx is None:
+        out_idx = torch.empty((n_q, k), dtype=torch.int64, device=q.device)
+    if out_score is None:
+        out_score = torch.empty((n_q, k), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(tq_search_workspace_bytes(quantizer, n_db, n_q, k), dtype=torch.uint8,
+                                device=q.device)
+    qs = quantizer.struct()
+    c = db.struct()
+    _check(lib().tq_search(C.byref(qs), C.byref(c), n_db, _ptr(q), dt, n_q, k, _ptr(out_idx), _ptr(out_score),
+                           _ptr(workspace), workspace.numel(), _stream(stream)), "tq_search")
+    return out_idx, out_score
+
+
 __all__ = [
     "LIB_PATH", "SYMBOLS", "lib", "TQError", "Quantizer", "Cache", "make_layout", "decode_shape",
     "tq_abi_version", "tq_status_string", "tq_build_codebook", "tq_record_layout", "tq_fold_sketch",
     "tq_quantize", "tq_attn_decode_workspace_bytes", "tq_attn_decode", "tq_attn_decode_phases",
     "tq_attn_decode_append", "append_spec", "tq_append", "tq_attn_decode_bf16_workspace_bytes",
-    "tq_attn_decode_bf16",
+    "tq_attn_decode_bf16", "tq_search_workspace_bytes", "tq_search",
     "TQ_PHASE_PREP", "TQ_PHASE_SPLIT", "TQ_PHASE_COMBINE", "TQ_PHASE_ALL",
     "TQ_OK", "TQ_ERR_INVALID", "TQ_ERR_UNSUPPORTED", "TQ_ERR_NOCONVERGE", "TQ_ERR_WORKSPACE",
     "TQ_ERR_DEVICE", "TQ_F32", "TQ_BF16", "TQ_TOKEN_MAJOR", "TQ_BLOCK32",

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libturboquant.so")
-SOURCES = ["tq_host.cpp", "tq_quantize.hip", "tq_decode.hip", "tq_decode_bf16.hip"]
+SOURCES = ["tq_host.cpp", "tq_quantize.hip", "tq_decode.hip", "tq_decode_bf16.hip", "tq_search.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -37,9 +37,13 @@ struct PrepArgs {
   float* kscale;  // out: one scale per K group
 };
 
-// blocks along x: the row blocks of [rot; sketch], then the scale search
+// blocks along x: the row blocks of rot, those of sketch (each matrix cut
+// into blocks of kPrepRows rows, the last one partial when kPrepRows does not
+// divide D), then the scale search
 template <int D>
-constexpr int prep_blocks_x() { return 2 * D / kPrepRows + 1; }
+constexpr int prep_row_blocks() { return (D + kPrepRows - 1) / kPrepRows; }
+template <int D>
+constexpr int prep_blocks_x() { return 2 * prep_row_blocks<D>() + 1; }
 
 // LDS bytes a prep block needs (row and head staging, or the search)
 template <int D>
@@ -100,7 +104,8 @@ __device__ void search_fp16_scale(const float* cent, int L, float* out, int tid,
 // Block (bx, by) of the preparation with NTHR threads.
 template <int D, int NTHR>
 __device__ void prep_block(const PrepArgs& p, int bx, int by, int t, unsigned char* smem) {
-  if (bx == 2 * D / kPrepRows) {
+  constexpr int RB = prep_row_blocks<D>();
+  if (bx == 2 * RB) {
     if (by == 0) {
       search_fp16_scale<NTHR>(p.kcent, 1 << p.m0, p.kscale, t, smem);
       if (p.n_groups > 1) search_fp16_scale<NTHR>(p.kcent + (1 << p.m0), 1 << p.m1, p.kscale + 1, t, smem);
@@ -112,9 +117,11 @@ __device__ void prep_block(const PrepArgs& p, int bx, int by, int t, unsigned ch
   constexpr int HPT = kPrepHeads / TPR;                // heads per thread
   float (*sm)[QS] = reinterpret_cast<float (*)[QS]>(smem);
   float (*sq)[QS] = reinterpret_cast<float (*)[QS]>(smem + kPrepRows * QS * 4);
-  const int r0 = bx * kPrepRows;  // first row of [rot; sketch]
+  const bool sk = bx >= RB;
+  const int lr0 = (sk ? bx - RB : bx) * kPrepRows;  // first row of the block in its matrix
+  const int r0 = lr0 + (sk ? D : 0);                // first row of [rot; sketch]
   const int h0 = by * kPrepHeads;
-  const float* mat = r0 < D ? p.rot + (int64_t)r0 * D : p.sketch + (int64_t)(r0 - D) * D;
+  const float* mat = (sk ? p.sketch : p.rot) + (int64_t)lr0 * D;
   {
     constexpr int C4 = D / 4;  // 16-byte chunks per matrix row
     constexpr int NM = (kPrepRows * C4 + NTHR - 1) / NTHR;
@@ -122,8 +129,10 @@ __device__ void prep_block(const PrepArgs& p, int bx, int by, int t, unsigned ch
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       const int c = t + NTHR * i;
+      // (rows past the matrix read its last row; their results are dropped)
       const int cc = c < kPrepRows * C4 ? c : 0;
-      mb[i] = *reinterpret_cast<const f32x4*>(mat + (cc / C4) * D + (cc % C4) * 4);
+      const int rr = lr0 + cc / C4 < D ? cc / C4 : D - 1 - lr0;
+      mb[i] = *reinterpret_cast<const f32x4*>(mat + rr * D + (cc % C4) * 4);
     }
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
@@ -131,20 +140,22 @@ __device__ void prep_block(const PrepArgs& p, int bx, int by, int t, unsigned ch
       if (c < kPrepRows * C4) *reinterpret_cast<f32x4*>(&sm[c / C4][(c % C4) * 4]) = mb[i];
     }
   }
+  // (chunk counts rounded up; chunks past the block's last are skipped)
   if (p.q_bf16) {
     constexpr int C8 = D / 8;  // 16-byte chunks per bf16 query row
-    constexpr int NC = kPrepHeads * C8 / NTHR;
+    constexpr int NC = (kPrepHeads * C8 + NTHR - 1) / NTHR;
     u32x4 qb[NC];
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
-      const int c = t + NTHR * i, h = h0 + c / C8;
+      const int c = t + NTHR * i, cc = c < kPrepHeads * C8 ? c : 0, h = h0 + cc / C8;
       const int hc = h < p.n_heads ? h : p.n_heads - 1;
       qb[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.q) + (int64_t)hc * D +
-                                              (c % C8) * 8);
+                                              (cc % C8) * 8);
     }
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
       const int c = t + NTHR * i;
+      if (c >= kPrepHeads * C8) continue;
       float* dst = &sq[c / C8][(c % C8) * 8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -154,19 +165,19 @@ __device__ void prep_block(const PrepArgs& p, int bx, int by, int t, unsigned ch
     }
   } else {
     constexpr int C4 = D / 4;
-    constexpr int NC = kPrepHeads * C4 / NTHR;
+    constexpr int NC = (kPrepHeads * C4 + NTHR - 1) / NTHR;
     f32x4 qb[NC];
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
-      const int c = t + NTHR * i, h = h0 + c / C4;
+      const int c = t + NTHR * i, cc = c < kPrepHeads * C4 ? c : 0, h = h0 + cc / C4;
       const int hc = h < p.n_heads ? h : p.n_heads - 1;
       qb[i] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p.q) + (int64_t)hc * D +
-                                              (c % C4) * 4);
+                                              (cc % C4) * 4);
     }
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
       const int c = t + NTHR * i;
-      *reinterpret_cast<f32x4*>(&sq[c / C4][(c % C4) * 4]) = qb[i];
+      if (c < kPrepHeads * C4) *reinterpret_cast<f32x4*>(&sq[c / C4][(c % C4) * 4]) = qb[i];
     }
   }
   __syncthreads();
@@ -183,6 +194,7 @@ __device__ void prep_block(const PrepArgs& p, int bx, int by, int t, unsigned ch
     }
   }
   const int row = r0 + i;
+  if (lr0 + i >= D) return;  // a row past the matrix (partial last block)
   // logits in the log2 domain: both parts carry scale * log2(e); the sketch
   // part also alpha_g = sqrt(pi / 2) / d_g of the row's group
   float f = p.scale_l2;

@@ -46,6 +46,7 @@ from .estimate import dequantize, estimate_logits, attention_decode, softmax
 from .records import (
     pack_token_major, pack_block32, record_words, record_bytes,
 )
+from .search import top_k, estimated_scores, search, exact_search, recall_at_k
 
 __all__ = [
     "coordinate_pdf", "coordinate_cdf", "coordinate_ppf", "cell_first_moment",
@@ -53,4 +54,5 @@ __all__ = [
     "Quantizer", "QuantizedVectors", "quantize", "legal_variants",
     "dequantize", "estimate_logits", "attention_decode", "softmax",
     "pack_token_major", "pack_block32", "record_words", "record_bytes",
+    "top_k", "estimated_scores", "search", "exact_search", "recall_at_k",
 ]

@@ -30,7 +30,7 @@ def tq():
 def test_header_symbols_exported(tq):
     text = open(HEADER).read()
     declared = sorted(set(re.findall(r"^\s*(?:tq_status|int|const char\*)\s+(tq_\w+)\s*\(", text, re.M)))
-    assert len(declared) == 12
+    assert len(declared) == 14
     lib = C.CDLL(tq.LIB_PATH)
     for name in declared:
         assert hasattr(lib, name), name
@@ -247,3 +247,38 @@ def test_bf16_baseline_validation(tq):
     assert call(d=64) == tq.TQ_ERR_UNSUPPORTED
     assert call(shape=tq.decode_shape(2, 30, 8, 1000, 1024, 0.088)) == tq.TQ_ERR_INVALID  # heads not a multiple
     assert call(shape=tq.decode_shape(2, 32, 8, 1000, 1000, 0.088)) == tq.TQ_ERR_INVALID  # capacity % 32
+
+
+def test_search_validation(tq):
+    # nearest-neighbour search: sizing and argument errors before any launch
+    lib = tq.lib()
+    q = _fake_quantizer(tq, dims=(200,), bits=(3,))
+    db = _fake_cache(tq, 1000)
+    need = C.c_size_t()
+    assert lib.tq_search_workspace_bytes(C.byref(q), 1000, 50, 10, C.byref(need)) == 0
+    # prepared queries (50 x 3 x 200 fp16, rounded up to 256 B), the codebook
+    # scale (256 B) and two [50][slices][10] lists; 63 tiles of 16 rows give
+    # 16 slices of 4 tiles
+    qprep = (50 * 3 * 200 * 2 + 255) // 256 * 256
+    assert need.value == qprep + 256 + 2 * 50 * 16 * 10 * 4
+    for args in ((0, 50, 10), (1000, 0, 10), (1000, 50, 0), (1000, 50, 11)):
+        assert lib.tq_search_workspace_bytes(C.byref(q), *args, C.byref(need)) == tq.TQ_ERR_INVALID
+    assert lib.tq_search_workspace_bytes(C.byref(q), 1000, 50, 10, C.byref(need)) == 0
+
+    def call(qz=q, db=db, n_db=1000, x=FAKE, dt=0, n_q=50, k=10, oi=FAKE, os_=FAKE, ws=FAKE, wsb=need.value):
+        return lib.tq_search(C.byref(qz), C.byref(db), n_db, x, dt, n_q, k, oi, os_, ws, wsb, None)
+
+    assert call(wsb=need.value - 1) == tq.TQ_ERR_WORKSPACE
+    assert call(dt=5) == tq.TQ_ERR_INVALID
+    assert call(k=11) == tq.TQ_ERR_INVALID
+    assert call(x=None) == tq.TQ_ERR_INVALID
+    assert call(oi=FAKE + 4) == tq.TQ_ERR_INVALID  # misaligned int64 output
+    assert call(n_db=1001) == tq.TQ_ERR_INVALID  # more rows than the cache holds
+    two = _fake_quantizer(tq, dims=(64, 64), bits=(3, 2))
+    assert call(qz=two) == tq.TQ_ERR_UNSUPPORTED
+    four = _fake_quantizer(tq, dims=(128,), bits=(4,))
+    n4 = C.c_size_t()
+    assert lib.tq_search_workspace_bytes(C.byref(four), 1000, 50, 10, C.byref(n4)) == 0
+    assert call(qz=four, wsb=n4.value) == tq.TQ_ERR_UNSUPPORTED
+    odd = _fake_quantizer(tq, dims=(96,), bits=(3,))
+    assert call(qz=odd) == tq.TQ_ERR_UNSUPPORTED
