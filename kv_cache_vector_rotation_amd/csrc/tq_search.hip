@@ -9,13 +9,16 @@
 //
 // Work decomposition. The queries are prepared once (the decode's query
 // preparation with scale 1: Pi q as fp16 hi and lo parts, alpha S q as fp16,
-// and the fp16 codebook scale). A workgroup takes 32 queries and one slice of
+// and the fp16 codebook scale; the search uses the hi part alone: its
+// rounding moves a score by at most 2^-12 sum |q_i c_i| n, far inside the
+// score tolerance, whereas the decode needs the lo part because the softmax
+// amplifies logit errors). A workgroup takes 32 queries and one slice of
 // the database; its four waves take 16-vector tiles of the slice in turn. Per
 // tile a wave expands the codes of its 16 vectors into fp16 centroid pairs
 // through a replicated LDS table (one lookup per two coordinates) and the
 // sign bits into fp16 +-1 through a nibble table, and multiplies them with
-// the 32 queries on v_mfma_f32_16x16x32_f16 (three products per 32
-// coordinates and 16 queries: q hi, q lo, sketch), with the query operands in
+// the 32 queries on v_mfma_f32_16x16x32_f16 (two products per 32
+// coordinates and 16 queries: rotated and sketch), with the query operands in
 // LDS in lane order. The scores of a tile then enter per-lane sorted top-k
 // lists (lane (l, g) owns query l of each 16-query block and database rows
 // 4 g .. 4 g + 3 of every tile, so its candidates arrive in increasing index
@@ -44,7 +47,6 @@ constexpr int kWaves = 4;
 constexpr int kKL = 10;       // list length; k <= kKL
 constexpr int kMaxSlices = 16;
 constexpr int kTargetWorkgroups = 2048;
-constexpr float kLoInv = 1.0f / 2048.0f;  // the prepared query's lo part is scaled by 2^11
 
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
@@ -58,7 +60,7 @@ struct SArgs {
   const uint32_t* codes;
   const uint32_t* signs;
   const float* norms;
-  const _Float16* qprep;  // [n_q][3 D]: q_rot hi, q_rot lo * 2^11, q_sk
+  const _Float16* qprep;  // [n_q][3 D]: q_rot hi, q_rot lo * 2^11 (unused here), q_sk
   const float* kscale;    // fp16 codebook scale s
   const float* centroids;
   float* part_score;      // [n_q][n_slices][kKL]
@@ -71,8 +73,8 @@ struct Geo {
   static constexpr int CW = (M * D + 31) / 32;         // code words per record
   static constexpr int SW = (D + 31) / 32;             // sign words per record
   static constexpr int NPAIR = 1 << (2 * M);           // entries of the pair table
-  static constexpr int B_BYTES = KC * 3 * 2 * 64 * 16; // query operands
-  static constexpr int M_BYTES = kQB * kWaves * 4 * kKL * 8;  // merge lists
+  static constexpr int B_BYTES = KC * 2 * 2 * 64 * 16; // query operands
+  static constexpr int M_BYTES = 16 * kWaves * 4 * kKL * 8;   // merge lists of one column block
   static constexpr int R0 = B_BYTES > M_BYTES ? B_BYTES : M_BYTES;
   static constexpr int off_ctab = R0;                  // u32 [NPAIR][64]
   static constexpr int off_stab = off_ctab + NPAIR * 64 * 4;  // u32x2 [16][64]
@@ -97,7 +99,7 @@ __device__ __forceinline__ void list_insert(float (&sc)[kKL], int (&ix)[kKL], fl
 }
 
 template <int D, int M>
-__global__ __launch_bounds__(256, 2) void search_kernel(SArgs a) {
+__global__ __launch_bounds__(256, 3) void search_kernel(SArgs a) {
   using G = Geo<D, M>;
   constexpr int KC = G::KC, CW = G::CW, SW = G::SW;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -130,15 +132,15 @@ __global__ __launch_bounds__(256, 2) void search_kernel(SArgs a) {
       s_stab[v * 64 + l] = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
     }
   }
-  // ---- query operands in lane order: [chunk][part][column block][lane],
-  // lane (l, g): query 16 cb + l, coordinates 32 c + 8 g .. + 8; zero past
-  // D and past the last query ----
-  for (int e = tid; e < KC * 3 * 2 * 64; e += 256) {
-    const int l = e & 63, cb = (e >> 6) & 1, pt = (e >> 7) % 3, c = (e >> 7) / 3;
+  // ---- query operands in lane order: [chunk][part (rot hi, sketch)][column
+  // block][lane], lane (l, g): query 16 cb + l, coordinates 32 c + 8 g .. + 8;
+  // zero past D and past the last query ----
+  for (int e = tid; e < KC * 2 * 2 * 64; e += 256) {
+    const int l = e & 63, cb = (e >> 6) & 1, pt = (e >> 7) & 1, c = e >> 8;
     const int h = qb * kQB + cb * 16 + (l & 15);
     const int k = 32 * c + 8 * (l >> 4);
     u32x4 v = u32x4{0u, 0u, 0u, 0u};
-    if (h < a.n_q && k < D) v = *reinterpret_cast<const u32x4*>(a.qprep + (int64_t)h * 3 * D + pt * D + k);
+    if (h < a.n_q && k < D) v = *reinterpret_cast<const u32x4*>(a.qprep + (int64_t)h * 3 * D + 2 * pt * D + k);
     s_b[e] = v;
   }
   __syncthreads();
@@ -179,11 +181,11 @@ __global__ __launch_bounds__(256, 2) void search_kernel(SArgs a) {
   };
 
   auto compute = [&](const Rec& r, int64_t t) __attribute__((always_inline)) {
-    f32x4 acc[2][3];
+    f32x4 acc[2][2];
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-      for (int p = 0; p < 3; ++p) acc[cb][p] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int p = 0; p < 2; ++p) acc[cb][p] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       // codes of coordinates 32 c + 8 lg .. + 8: 8 M bits from bit M (32 c + 8 lg)
@@ -212,10 +214,9 @@ __global__ __launch_bounds__(256, 2) void search_kernel(SArgs a) {
       }
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
-        const u32x4* bp = s_b + ((c * 3) * 2 + cb) * 64 + lane;
+        const u32x4* bp = s_b + ((c * 2) * 2 + cb) * 64 + lane;
         acc[cb][0] = mfma16(arot, bp[0], acc[cb][0]);
-        acc[cb][1] = mfma16(arot, bp[2 * 64], acc[cb][1]);
-        acc[cb][2] = mfma16(ask, bp[4 * 64], acc[cb][2]);
+        acc[cb][1] = mfma16(ask, bp[2 * 64], acc[cb][1]);
       }
       // (keeps the next chunk's table and operand reads from being hoisted
       // above this one, which would hold every chunk's operands at once)
@@ -228,8 +229,7 @@ __global__ __launch_bounds__(256, 2) void search_kernel(SArgs a) {
       const float n = __uint_as_float(r.nr[i][0]), gm = __uint_as_float(r.nr[i][1]);
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
-        const float rot = fmaf(acc[cb][1][i], kLoInv, acc[cb][0][i]);
-        float x = fmaf(n * inv_s, rot, gm * acc[cb][2][i]);
+        float x = fmaf(n * inv_s, acc[cb][0][i], gm * acc[cb][1][i]);
         if (row >= a.n_db) x = -INFINITY;
         if (x > sc[cb][kKL - 1]) list_insert(sc[cb], ix[cb], x, (int)row);
       }
@@ -254,23 +254,22 @@ __global__ __launch_bounds__(256, 2) void search_kernel(SArgs a) {
     }
   }
 
-  // ---- merge the 16 lists of each query (4 lane groups x 4 waves) ----
-  __syncthreads();  // the query operands are no longer read
-  float* m_sc = reinterpret_cast<float*>(smem);                      // [kQB][16][kKL]
-  int* m_ix = reinterpret_cast<int*>(smem + kQB * 16 * kKL * 4);     // [kQB][16][kKL]
+  // ---- merge the 16 lists of each query (4 lane groups x 4 waves), one
+  // 16-query column block at a time ----
+  float* m_sc = reinterpret_cast<float*>(smem);                      // [16][16][kKL]
+  int* m_ix = reinterpret_cast<int*>(smem + 16 * 16 * kKL * 4);      // [16][16][kKL]
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
-    const int ql = cb * 16 + ln, li = wv * 4 + lg;
+    __syncthreads();  // the query operands, or the previous block's lists, are no longer read
+    const int li = wv * 4 + lg;
 #pragma unroll
     for (int j = 0; j < kKL; ++j) {
-      m_sc[(ql * 16 + li) * kKL + j] = sc[cb][j];
-      m_ix[(ql * 16 + li) * kKL + j] = ix[cb][j];
+      m_sc[(ln * 16 + li) * kKL + j] = sc[cb][j];
+      m_ix[(ln * 16 + li) * kKL + j] = ix[cb][j];
     }
-  }
-  __syncthreads();
-  if (tid < kQB) {
-    const int qg = qb * kQB + tid;
-    if (qg < a.n_q) {
+    __syncthreads();
+    const int qg = qb * kQB + cb * 16 + tid;
+    if (tid < 16 && qg < a.n_q) {
       int ptr[16];
 #pragma unroll
       for (int l = 0; l < 16; ++l) ptr[l] = 0;
@@ -367,7 +366,7 @@ bool plan_search(const tq_quantizer* qz, int64_t n_db, int64_t n_q, int k, Plan*
 template <int D, int M>
 hipError_t launch_search(const SArgs& a, int n_qblocks, hipStream_t st) {
   using G = Geo<D, M>;
-  static_assert(G::bytes <= 80 * 1024, "two workgroups per compute unit");
+  static_assert(G::bytes <= 53 * 1024, "three workgroups per compute unit");
   static_assert(M <= 3, "pair tables of at most 64 entries");
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&search_kernel<D, M>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, G::bytes);
