@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 1
+#define TQ_ABI_VERSION 2
 
 typedef enum {
   TQ_OK = 0,
@@ -178,7 +178,10 @@ typedef struct {
 
 /* One decode step over a compressed K/V cache. K and V of (batch b, KV head
  * h) occupy rows (b * n_kv_heads + h) * cache_capacity + t for tokens
- * t in [0, n_ctx). */
+ * t in [0, n_ctx). With n_q_tokens = T > 1 the step attends T query tokens
+ * per head at once (a chunk of a prefill): query token i sits at position
+ * n_ctx - T + i of the context (its own K/V already cached) and attends
+ * causally to tokens [0, n_ctx - T + i]. */
 typedef struct {
   int32_t batch;
   int32_t n_q_heads;      /* multiple of n_kv_heads */
@@ -187,6 +190,7 @@ typedef struct {
   int64_t n_ctx;          /* >= 1, <= cache_capacity */
   int64_t cache_capacity; /* rows per (b, h); a multiple of 32 */
   float scale;            /* logit = scale * <q, k~> */
+  int32_t n_q_tokens;     /* T, 1 <= T <= n_ctx (0 is read as 1) */
 } tq_decode_shape;
 
 /* ABI version of the loaded library (TQ_ABI_VERSION). */
@@ -244,6 +248,10 @@ tq_status tq_attn_decode_workspace_bytes(const tq_quantizer* kq, const tq_quanti
  * softmax times the dequantized values). For each batch b and query head h:
  *   logits[b, h, t] = scale * <q[b, h], k~[b, h_kv, t]>  for t < n_ctx,
  *   out[b, h]       = sum_t softmax(logits[b, h])_t v~[b, h_kv, t].
+ * With T = n_q_tokens > 1 (causal chunk): q is [batch, T, n_q_heads, d],
+ * out [batch, T, n_q_heads, d], logits [batch, n_q_heads, T, n_ctx] with
+ * -inf past each query token's causal limit, and query token i attends to
+ * tokens [0, n_ctx - T + i].
  * The estimate is evaluated in factored form: scale * sum_g (n_g <rot q,
  * c[idx]>_g + alpha_g gamma_g <sketch q, z>_g); V is accumulated in the
  * rotated and sketch domains and mapped back once per head with rot^T and
@@ -335,7 +343,8 @@ tq_status tq_attn_decode_append(const tq_quantizer* kq, const tq_quantizer* vq,
  *   workspace device scratch of at least tq_attn_decode_bf16_workspace_bytes().
  * Rows past n_ctx inside the last 32-row block are ignored, whatever they
  * hold. Errors: TQ_ERR_INVALID (shape, null or misaligned pointers, dtype),
- * TQ_ERR_UNSUPPORTED (d != 128), TQ_ERR_WORKSPACE, TQ_ERR_DEVICE. */
+ * TQ_ERR_UNSUPPORTED (d != 128, n_q_tokens > 1), TQ_ERR_WORKSPACE,
+ * TQ_ERR_DEVICE. */
 tq_status tq_attn_decode_bf16_workspace_bytes(const tq_decode_shape* shape, int d, size_t* bytes);
 tq_status tq_attn_decode_bf16(const tq_decode_shape* shape, int d, const void* q, tq_dtype q_dtype,
                               const void* k, const void* v, float* logits, float* out, void* workspace,

@@ -86,7 +86,7 @@ class tq_append(C.Structure):
 class tq_decode_shape(C.Structure):
     _fields_ = [("batch", C.c_int32), ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32),
                 ("n_split", C.c_int32), ("n_ctx", C.c_int64), ("cache_capacity", C.c_int64),
-                ("scale", C.c_float)]
+                ("scale", C.c_float), ("n_q_tokens", C.c_int32)]
 
 
 _lib = None
@@ -322,10 +322,10 @@ class Cache:
 
 
 def decode_shape(batch: int, n_q_heads: int, n_kv_heads: int, n_ctx: int, capacity: int,
-                 scale: float, n_split: int = 0) -> tq_decode_shape:
+                 scale: float, n_split: int = 0, n_q_tokens: int = 1) -> tq_decode_shape:
     s = tq_decode_shape()
     s.batch, s.n_q_heads, s.n_kv_heads, s.n_split = batch, n_q_heads, n_kv_heads, n_split
-    s.n_ctx, s.cache_capacity, s.scale = n_ctx, capacity, scale
+    s.n_ctx, s.cache_capacity, s.scale, s.n_q_tokens = n_ctx, capacity, scale, n_q_tokens
     return s
 
 

@@ -70,8 +70,9 @@ constexpr int kWaves = 4;
 constexpr int kTile = 32;
 
 struct DArgs {
-  int batch, hq, hkv, group;  // group = hq / hkv
+  int batch, hq, hkv, group;  // group = hq / hkv (heads here are (q head, query token) pairs)
   int n_split;
+  int T;  // query tokens per head: column hloc is token hloc % T, causal past n_ctx - T + t
   int64_t n_ctx, cap;
   float scale;
   const _Float16* qprep;  // [batch*hq][3d]: q_rot hi, q_rot lo * 2^11, q_sk
@@ -621,6 +622,12 @@ __global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel
     }
     // tokens of the tile before n_ctx (32 except in the last tile)
     const int nvt = full ? kTile : (int)(N - T0);
+    // a chunk of T query tokens: this column's token t sees [0, N - T + t]
+    if (a.T > 1) {
+      const int64_t lim = N - a.T + hloc % a.T + 1;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) l2[j] = tok0 + j < lim ? l2[j] : -INFINITY;
+    }
     // (packed: only the role-0 columns are logits; the other columns carry
     // finite values that no result uses)
     if (a.logits) {
@@ -647,8 +654,9 @@ __global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel
       // context is split.
       const float m_new = fmaxf(m_run, ceilf(mx));
       if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
-        // some head's maximum moved: rescale (factor 1 for the others)
-        const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+        // some head's maximum moved: rescale (factor 1 for the others; a
+        // head that has seen only masked tokens keeps -inf and factor 1)
+        const float corr = m_new == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= corr;
         if constexpr (PK) {
           // the sketch column of a head (role 1) takes its head's factor
@@ -666,9 +674,11 @@ __global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel
         m_run = m_new;
       }
       float p[8], psum;
+      // (m_run is -inf only while every token seen is masked: then p = 0)
+      const float m_ref = m_run == -INFINITY ? 0.f : m_run;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        p[j] = __builtin_amdgcn_exp2f(l2[j] - m_run);
+        p[j] = __builtin_amdgcn_exp2f(l2[j] - m_ref);
         psum = j == 0 ? p[j] : psum + p[j];
       }
       l_run += psum;
@@ -866,10 +876,12 @@ constexpr int kMaxSplit = 1024;
 constexpr int kCombThreads = 1024;
 constexpr int kCombCols = 4;
 
+// Heads are ordered (batch, q head, query token); out rows are (batch, query
+// token, q head) (the same order when T = 1).
 template <int D>
 __global__ __launch_bounds__(kCombThreads) void combine_kernel(const float* part, int n_split,
                                                                const float* rot, const float* sketch,
-                                                               int group_dim0, float* out) {
+                                                               int group_dim0, int T, int hq, float* out) {
   constexpr int NW = kCombThreads / 64, NG = kCombThreads / (2 * D);  // waves, groups
   constexpr int PS = 2 + 2 * D;                                      // floats per partial
   constexpr int OC = D / kCombCols;                                  // outputs per block
@@ -954,7 +966,8 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const float* part
     float o = 0.f;
 #pragma unroll 8
     for (int r = 0; r < RP; ++r) o += s_out[r][t];
-    out[(int64_t)head * D + cs * OC + t] = o / L;
+    const int64_t orow = T <= 1 ? head : ((int64_t)(head / T / hq) * T + head % T) * hq + (head / T) % hq;
+    out[orow * D + cs * OC + t] = o / L;
   }
 }
 
@@ -983,8 +996,14 @@ bool same_layout(const tq_layout& a, const tq_layout& b) {
   return true;
 }
 
+// query tokens per head of a shape
+inline int q_tokens(const tq_decode_shape* s) { return s->n_q_tokens < 1 ? 1 : s->n_q_tokens; }
+
 bool shape_valid(const tq_decode_shape* s) {
   if (!s) return false;
+  if (s->n_q_tokens < 0 || q_tokens(s) > s->n_ctx) return false;
+  // (prepared heads per launch column of the prep grid: at most 65535 x 64)
+  if ((int64_t)s->batch * s->n_q_heads * q_tokens(s) > (int64_t)65535 * 64) return false;
   if (s->batch < 1 || s->n_kv_heads < 1 || s->n_q_heads < 1) return false;
   if (s->n_q_heads % s->n_kv_heads != 0) return false;
   if (s->n_ctx < 1 || s->cache_capacity < s->n_ctx || s->cache_capacity % 32 != 0) return false;
@@ -1003,7 +1022,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // workspace: [prepared queries][K codebook scales, 2 floats][split partials]
 size_t workspace_for(const tq_decode_shape* s, int d, bool with_v, int n_split) {
-  const size_t heads = (size_t)s->batch * s->n_q_heads;
+  const size_t heads = (size_t)s->batch * s->n_q_heads * q_tokens(s);
   size_t bytes = align256(heads * 3 * d * sizeof(_Float16)) + 256;
   if (with_v) bytes += align256(heads * (size_t)n_split * (2 + 2 * d) * sizeof(float));
   return bytes;
@@ -1063,7 +1082,7 @@ extern "C" tq_status tq_attn_decode_workspace_bytes(const tq_quantizer* kq, cons
                                                     const tq_decode_shape* shape, size_t* bytes) {
   if (!kq || !tq::layout_valid(&kq->layout) || !shape_valid(shape) || !bytes) return TQ_ERR_INVALID;
   if (vq && !tq::layout_valid(&vq->layout)) return TQ_ERR_INVALID;
-  const int grp = shape->n_q_heads / shape->n_kv_heads;
+  const int grp = shape->n_q_heads / shape->n_kv_heads * q_tokens(shape);
   const int hb = heads_per_block(grp, vq != nullptr);
   const int n_hblk = (grp + hb - 1) / hb;
   *bytes = workspace_for(shape, kq->layout.d, vq != nullptr, choose_split(shape, n_hblk));
@@ -1076,7 +1095,7 @@ namespace {
 struct Plan {
   DArgs a;
   tqp::PrepArgs prep;
-  int n_hblk, prep_grid_y, n_heads, n_groups, m0, m1, group_dim0;
+  int n_hblk, prep_grid_y, n_heads, n_groups, m0, m1, group_dim0, T, hq_orig;
   bool with_v;
   const float* vrot;
   const float* vsketch;
@@ -1111,7 +1130,8 @@ tq_status plan_decode(const tq_quantizer* kq, const tq_quantizer* vq, const tq_d
     if (ptr && reinterpret_cast<uintptr_t>(ptr) % 16 != 0) return TQ_ERR_INVALID;
   if (!decode_supported(kq->layout)) return TQ_ERR_UNSUPPORTED;
   const tq_layout& l = kq->layout;
-  const int group = shape->n_q_heads / shape->n_kv_heads;
+  const int T = q_tokens(shape);
+  const int group = shape->n_q_heads / shape->n_kv_heads * T;  // (q head, query token) columns per KV head
   const int hb = heads_per_block(group, with_v);
   const int n_hblk = (group + hb - 1) / hb;
   const int n_split = choose_split(shape, n_hblk);
@@ -1119,7 +1139,7 @@ tq_status plan_decode(const tq_quantizer* kq, const tq_quantizer* vq, const tq_d
   if (!workspace || workspace_bytes < need) return TQ_ERR_WORKSPACE;
 
   constexpr int D = kD;
-  const int n_heads = shape->batch * shape->n_q_heads;
+  const int n_heads = shape->batch * shape->n_q_heads * T;
   _Float16* qprep = reinterpret_cast<_Float16*>(workspace);
   float* kscale = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
                                            align256((size_t)n_heads * 3 * D * sizeof(_Float16)));
@@ -1149,10 +1169,15 @@ tq_status plan_decode(const tq_quantizer* kq, const tq_quantizer* vq, const tq_d
   pp.m0 = pl->m0;
   pp.m1 = pl->m1;
   pp.kscale = kscale;
+  pp.T = T;
+  pp.hq = shape->n_q_heads;
+  pl->T = T;
+  pl->hq_orig = shape->n_q_heads;
 
   DArgs& a = pl->a;
   a.batch = shape->batch;
-  a.hq = shape->n_q_heads;
+  a.hq = shape->n_q_heads * T;
+  a.T = T;
   a.hkv = shape->n_kv_heads;
   a.group = group;
   a.n_split = n_split;
@@ -1200,7 +1225,7 @@ tq_status run_phases(const Plan& pl, unsigned phases, hipStream_t st) {
     (void)hipGetLastError();  // a launch error is reported below, not an older one
     hipLaunchKernelGGL((combine_kernel<D>), dim3(pl.n_heads, kCombCols), dim3(kCombThreads), 0, st, pl.a.part,
                        pl.a.n_split,
-                       pl.vrot, pl.vsketch, pl.group_dim0, pl.out);
+                       pl.vrot, pl.vsketch, pl.group_dim0, pl.T, pl.hq_orig, pl.out);
     if (hipGetLastError() != hipSuccess) return TQ_ERR_DEVICE;
   }
   return TQ_OK;

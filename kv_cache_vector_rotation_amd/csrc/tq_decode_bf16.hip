@@ -376,6 +376,7 @@ bool shape_ok(const tq_decode_shape* s) {
   if (!s) return false;
   if (s->batch < 1 || s->n_kv_heads < 1 || s->n_q_heads < 1 || s->n_q_heads % s->n_kv_heads != 0) return false;
   if (s->n_ctx < 1 || s->cache_capacity < s->n_ctx || s->cache_capacity % 32 != 0 || s->n_split < 0) return false;
+  if (s->n_q_tokens < 0) return false;
   return std::isfinite(s->scale);
 }
 
@@ -392,7 +393,7 @@ int n_hblk_of(const tq_decode_shape* s) {
 
 extern "C" tq_status tq_attn_decode_bf16_workspace_bytes(const tq_decode_shape* shape, int d, size_t* bytes) {
   if (!bytes || !shape_ok(shape)) return TQ_ERR_INVALID;
-  if (d != kD) return TQ_ERR_UNSUPPORTED;
+  if (d != kD || shape->n_q_tokens > 1) return TQ_ERR_UNSUPPORTED;
   *bytes = workspace_for(shape, choose_split(shape, n_hblk_of(shape)));
   return TQ_OK;
 }
@@ -402,7 +403,7 @@ extern "C" tq_status tq_attn_decode_bf16(const tq_decode_shape* shape, int d, co
                                          size_t workspace_bytes, void* stream) {
   if (!shape_ok(shape) || !q || !k || !v || !out) return TQ_ERR_INVALID;
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_ERR_INVALID;
-  if (d != kD) return TQ_ERR_UNSUPPORTED;
+  if (d != kD || shape->n_q_tokens > 1) return TQ_ERR_UNSUPPORTED;
   const void* ptrs[] = {q, k, v, out, workspace};
   for (const void* p : ptrs)
     if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return TQ_ERR_INVALID;

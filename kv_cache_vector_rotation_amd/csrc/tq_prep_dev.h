@@ -35,7 +35,18 @@ struct PrepArgs {
   const float* kcent;
   int n_groups, m0, m1;
   float* kscale;  // out: one scale per K group
+  // query tokens per head (T > 1: heads are ordered (batch, q head, token)
+  // while q rows are (batch, token, q head)), and the q heads per batch
+  int T, hq;
 };
+
+// q row of prepared head h: the identity for T <= 1, else head
+// (b hq + g) T + t reads row (b T + t) hq + g
+__device__ __forceinline__ int64_t prep_q_row(const PrepArgs& p, int h) {
+  if (p.T <= 1) return h;
+  const int t = h % p.T, bh = h / p.T;
+  return ((int64_t)(bh / p.hq) * p.T + t) * p.hq + bh % p.hq;
+}
 
 // blocks along x: the row blocks of rot, those of sketch (each matrix cut
 // into blocks of kPrepRows rows, the last one partial when kPrepRows does not
@@ -149,7 +160,7 @@ __device__ void prep_block(const PrepArgs& p, int bx, int by, int t, unsigned ch
     for (int i = 0; i < NC; ++i) {
       const int c = t + NTHR * i, cc = c < kPrepHeads * C8 ? c : 0, h = h0 + cc / C8;
       const int hc = h < p.n_heads ? h : p.n_heads - 1;
-      qb[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.q) + (int64_t)hc * D +
+      qb[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.q) + prep_q_row(p, hc) * D +
                                               (cc % C8) * 8);
     }
 #pragma unroll
@@ -171,7 +182,7 @@ __device__ void prep_block(const PrepArgs& p, int bx, int by, int t, unsigned ch
     for (int i = 0; i < NC; ++i) {
       const int c = t + NTHR * i, cc = c < kPrepHeads * C4 ? c : 0, h = h0 + cc / C4;
       const int hc = h < p.n_heads ? h : p.n_heads - 1;
-      qb[i] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p.q) + (int64_t)hc * D +
+      qb[i] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p.q) + prep_q_row(p, hc) * D +
                                               (cc % C4) * 4);
     }
 #pragma unroll

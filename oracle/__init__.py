@@ -42,7 +42,7 @@ from .codebook import (
     lloyd_max, Codebook,
 )
 from .quantize import Quantizer, QuantizedVectors, quantize, legal_variants
-from .estimate import dequantize, estimate_logits, attention_decode, softmax
+from .estimate import dequantize, estimate_logits, attention_decode, attention_prefill, softmax
 from .records import (
     pack_token_major, pack_block32, record_words, record_bytes,
 )
@@ -52,7 +52,7 @@ __all__ = [
     "coordinate_pdf", "coordinate_cdf", "coordinate_ppf", "cell_first_moment",
     "lloyd_max", "Codebook",
     "Quantizer", "QuantizedVectors", "quantize", "legal_variants",
-    "dequantize", "estimate_logits", "attention_decode", "softmax",
+    "dequantize", "estimate_logits", "attention_decode", "attention_prefill", "softmax",
     "pack_token_major", "pack_block32", "record_words", "record_bytes",
     "top_k", "estimated_scores", "search", "exact_search", "recall_at_k",
 ]

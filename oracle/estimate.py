@@ -76,3 +76,28 @@ def attention_decode(q: np.ndarray, k_tilde: np.ndarray, v_tilde: np.ndarray | N
             p = softmax(logits[h])
             out[h] = p @ v_tilde[kv]
     return logits, out
+
+
+def attention_prefill(q: np.ndarray, k_tilde: np.ndarray, v_tilde: np.ndarray | None, scale: float):
+    """A chunk of T query tokens for one batch element, attended causally.
+
+    q [T, H_q, d]; k_tilde / v_tilde [H_kv, N, d] (dequantized caches that
+    already hold the chunk's own T tokens as their last rows). Query token i
+    sits at position N - T + i and sees tokens 0 .. N - T + i (reading: a
+    prefill chunk attends to the cached prefix and causally within itself).
+    Returns (logits [H_q, T, N] with -inf past each token's limit,
+    out [T, H_q, d] or None)."""
+    T, hq, d = q.shape
+    hkv, n = k_tilde.shape[0], k_tilde.shape[1]
+    group = hq // hkv
+    logits = np.full((hq, T, n), -np.inf)
+    out = None if v_tilde is None else np.empty((T, hq, d), dtype=np.float64)
+    for i in range(T):
+        lim = n - T + i + 1
+        for h in range(hq):
+            kv = h // group
+            row = estimate_logits(q[i, h][None, :], k_tilde[kv, :lim], scale)[0]
+            logits[h, i, :lim] = row
+            if v_tilde is not None:
+                out[i, h] = softmax(row[None, :])[0] @ v_tilde[kv, :lim]
+    return logits, out

@@ -282,3 +282,22 @@ def test_search_validation(tq):
     assert call(qz=four, wsb=n4.value) == tq.TQ_ERR_UNSUPPORTED
     odd = _fake_quantizer(tq, dims=(96,), bits=(3,))
     assert call(qz=odd) == tq.TQ_ERR_UNSUPPORTED
+
+
+def test_query_token_chunks_validation(tq):
+    # n_q_tokens = T: the workspace holds T prepared queries and partials per
+    # head; T past n_ctx is rejected; the bf16 baseline takes T = 1 only
+    lib = tq.lib()
+    q = _fake_quantizer(tq)
+    need1, needT = C.c_size_t(), C.c_size_t()
+    s1 = tq.decode_shape(1, 8, 2, 1000, 1024, 0.088, n_split=4)
+    sT = tq.decode_shape(1, 8, 2, 1000, 1024, 0.088, n_split=4, n_q_tokens=16)
+    assert lib.tq_attn_decode_workspace_bytes(C.byref(q), C.byref(q), C.byref(s1), C.byref(need1)) == 0
+    assert lib.tq_attn_decode_workspace_bytes(C.byref(q), C.byref(q), C.byref(sT), C.byref(needT)) == 0
+    per_head = lambda heads: (heads * 3 * 128 * 2 + 255) // 256 * 256 + 256 + (heads * 4 * 258 * 4 + 255) // 256 * 256
+    assert need1.value == per_head(8) and needT.value == per_head(8 * 16)
+    bad = tq.decode_shape(1, 8, 2, 10, 32, 0.088, n_q_tokens=11)
+    assert lib.tq_attn_decode_workspace_bytes(C.byref(q), C.byref(q), C.byref(bad), C.byref(needT)) == \
+        tq.TQ_ERR_INVALID
+    nb = C.c_size_t()
+    assert lib.tq_attn_decode_bf16_workspace_bytes(C.byref(sT), 128, C.byref(nb)) == tq.TQ_ERR_UNSUPPORTED

@@ -271,3 +271,114 @@ def test_append_step_in_a_captured_graph(tq):
         got = (kc.codes, kc.signs, kc.norms, vc.codes, vc.signs, vc.norms, logits, out)
         for a, b in zip(ref, got):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+# A chunk of T query tokens attended causally (n_q_tokens = T): q and out
+# are [batch, T, n_q_heads, d], logits [batch, n_q_heads, T, n_ctx].
+CHUNK_CASES = [
+    # name, overrides, n_ctx, cap, T
+    ("llama8b_decode", dict(batch=2, n_q_heads=8, n_kv_heads=2), 1000, 1024, 16),
+    ("llama8b_decode", dict(batch=1, n_q_heads=8, n_kv_heads=2), 300, 320, 3),
+    ("llama8b_decode", dict(batch=2, n_q_heads=2, n_kv_heads=2), 500, 512, 2),   # 2 columns per KV head
+    ("llama8b_decode", dict(batch=1, n_q_heads=4, n_kv_heads=1), 40, 64, 40),    # the whole context
+    ("mixed_3p5", dict(batch=1, n_q_heads=8, n_kv_heads=2), 777, 800, 8),
+    ("llama70b_long", dict(batch=1, n_q_heads=16, n_kv_heads=2), 2000, 2048, 33),
+]
+
+
+def _chunk_queries(wl, T, seed=21):
+    q = synth.standard_normal(synth.rng_for(wl.seed, seed, T), (wl.batch, T, wl.n_q_heads, wl.d))
+    return synth.to_bf16_exact(q) if wl.dtype == "bf16" else q
+
+
+@pytest.mark.parametrize("name,over,n_ctx,cap,T", CHUNK_CASES)
+def test_causal_chunk_matches_oracle(tq, name, over, n_ctx, cap, T):
+    import torch
+    wl = synth.workload(name, **over)
+    o = _oracle_side(wl, n_ctx, cap)
+    kq = tq.Quantizer.from_parts(o["ks"].rotations, o["ks"].sketches, o["bits"], perm=o["ks"].perm)
+    vq = tq.Quantizer.from_parts(o["vs"].rotations, o["vs"].sketches, o["bits"], perm=o["vs"].perm)
+    B, H = wl.batch, wl.n_kv_heads
+    kc = gc.to_device_cache(kq, tq.TQ_TOKEN_MAJOR, B * H * cap, o["karr"])
+    vc = gc.to_device_cache(vq, tq.TQ_BLOCK32, B * H * cap, o["varr"])
+    q = _chunk_queries(wl, T)
+    qt = torch.from_numpy(q).cuda().to(torch.bfloat16)
+    shape = tq.decode_shape(B, wl.n_q_heads, H, n_ctx, cap, wl.scale, n_q_tokens=T)
+    logits = torch.full((B, wl.n_q_heads, T, n_ctx), float("nan"), device="cuda")
+    out = torch.full((B, T, wl.n_q_heads, wl.d), float("nan"), device="cuda")
+    tq.tq_attn_decode(kq, vq, shape, qt, kc, vc, logits=logits, out=out)
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy().astype(np.float64)
+    ot = out.cpu().numpy().astype(np.float64)
+    worst_l = worst_o = 0.0
+    for b in range(B):
+        rl, ro = oracle.attention_prefill(q[b].astype(np.float64), o["k_t"][b], o["v_t"][b], wl.scale)
+        for i in range(T):
+            lim = n_ctx - T + i + 1
+            assert np.all(np.isneginf(lg[b, :, i, lim:]))
+            ok, w = gc.normwise_close(lg[b, :, i, :lim], rl[:, i, :lim])
+            assert ok, ("logits", b, i, w)
+            worst_l = max(worst_l, w)
+        ok, w = gc.normwise_close(ot[b], ro)
+        assert ok, ("out", b, w)
+        worst_o = max(worst_o, w)
+    print(name, over, n_ctx, T, "logits", worst_l, "out", worst_o)
+
+
+def test_causal_chunk_last_token_equals_decode(tq):
+    # the chunk's last token attends to the whole context, like a decode step
+    import torch
+    wl = synth.workload("llama8b_decode", batch=1, n_q_heads=8, n_kv_heads=2)
+    n_ctx, cap, T = 700, 704, 6
+    o = _oracle_side(wl, n_ctx, cap)
+    kq = tq.Quantizer.from_parts(o["ks"].rotations, o["ks"].sketches, o["bits"], perm=o["ks"].perm)
+    vq = tq.Quantizer.from_parts(o["vs"].rotations, o["vs"].sketches, o["bits"], perm=o["vs"].perm)
+    kc = gc.to_device_cache(kq, tq.TQ_TOKEN_MAJOR, 2 * cap, o["karr"])
+    vc = gc.to_device_cache(vq, tq.TQ_BLOCK32, 2 * cap, o["varr"])
+    q = torch.from_numpy(_chunk_queries(wl, T)).cuda().to(torch.bfloat16)
+    out = torch.empty((1, T, 8, 128), device="cuda")
+    tq.tq_attn_decode(kq, vq, tq.decode_shape(1, 8, 2, n_ctx, cap, wl.scale, n_q_tokens=T), q, kc, vc, out=out)
+    out1 = torch.empty((1, 8, 128), device="cuda")
+    tq.tq_attn_decode(kq, vq, tq.decode_shape(1, 8, 2, n_ctx, cap, wl.scale), q[:, -1].contiguous(), kc, vc,
+                      out=out1)
+    torch.cuda.synchronize()
+    a, b1 = out[0, -1].cpu().numpy(), out1[0].cpu().numpy()
+    assert np.max(np.abs(a - b1)) <= 1e-4 * np.max(np.abs(b1))
+
+
+def test_causal_chunk_append_step_equals_separate_calls(tq):
+    # a prefill chunk through tq_attn_decode_append (append T tokens of K and
+    # V, prepare T x 8 queries, attend causally) against tq_quantize twice and
+    # tq_attn_decode: bit for bit
+    import torch
+    wl = synth.workload("llama8b_decode", batch=2, n_q_heads=8, n_kv_heads=2)
+    n_ctx, cap, T = 900, 1024, 24
+    o = _oracle_side(wl, n_ctx, cap)
+    kq = tq.Quantizer.from_parts(o["ks"].rotations, o["ks"].sketches, o["bits"], perm=o["ks"].perm)
+    vq = tq.Quantizer.from_parts(o["vs"].rotations, o["vs"].sketches, o["bits"], perm=o["vs"].perm)
+    B, H = 2, 2
+    t0 = n_ctx - T
+    kx = np.concatenate([synth.draw_kv_slab(wl, "K", b, h, t0, n_ctx) for b in range(B) for h in range(H)])
+    vx = np.concatenate([synth.draw_kv_slab(wl, "V", b, h, t0, n_ctx) for b in range(B) for h in range(H)])
+    kx_t = torch.from_numpy(-kx).cuda().to(torch.bfloat16)
+    vx_t = torch.from_numpy(-vx).cuda().to(torch.bfloat16)
+    q = torch.from_numpy(_chunk_queries(wl, T)).cuda().to(torch.bfloat16)
+    shape = tq.decode_shape(B, 8, H, n_ctx, cap, wl.scale, n_q_tokens=T)
+    res = []
+    for fused in (False, True):
+        kc = gc.to_device_cache(kq, tq.TQ_TOKEN_MAJOR, B * H * cap, o["karr"])
+        vc = gc.to_device_cache(vq, tq.TQ_BLOCK32, B * H * cap, o["varr"])
+        out = torch.full((B, T, 8, 128), float("nan"), device="cuda")
+        if fused:
+            tq.tq_attn_decode_append(kq, vq, shape, q, kc, vc,
+                                     k_new=tq.append_spec(kx_t, seg_len=T, seg_stride=cap, seg_offset=t0),
+                                     v_new=tq.append_spec(vx_t, seg_len=T, seg_stride=cap, seg_offset=t0),
+                                     out=out)
+        else:
+            tq.tq_quantize(kq, tq.TQ_TOKEN_MAJOR, kx_t, kc, seg_len=T, seg_stride=cap, seg_offset=t0)
+            tq.tq_quantize(vq, tq.TQ_BLOCK32, vx_t, vc, seg_len=T, seg_stride=cap, seg_offset=t0)
+            tq.tq_attn_decode(kq, vq, shape, q, kc, vc, out=out)
+        torch.cuda.synchronize()
+        res.append((kc.codes.cpu(), vc.codes.cpu(), out.cpu()))
+    for x, y in zip(res[0], res[1]):
+        assert torch.equal(x, y)

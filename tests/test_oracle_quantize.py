@@ -293,6 +293,36 @@ def test_attention_decode_special_cases():
     assert np.allclose(s.sum(axis=1), 1) and np.allclose(oracle.softmax(logits + 100), s)
 
 
+def test_attention_prefill_causal_chunk():
+    # a chunk of T query tokens: T = 1 is the decode step; a token's output
+    # ignores every later token (change them and it stays); the last token
+    # sees the whole context; the first sees the prefix and itself; brute
+    # force on a tiny case with explicit exponentials
+    rng = np.random.default_rng(6)
+    hkv, g, n, d, T = 2, 2, 12, 4, 5
+    k = rng.standard_normal((hkv, n, d))
+    v = rng.standard_normal((hkv, n, d))
+    q = rng.standard_normal((T, hkv * g, d))
+    lg1, o1 = oracle.attention_prefill(q[-1:], k, v, 0.7)
+    lgd, od = oracle.attention_decode(q[-1], k, v, 0.7)
+    assert np.allclose(o1[0], od, atol=1e-14) and np.allclose(lg1[:, 0], lgd, atol=1e-14)
+    lg, out = oracle.attention_prefill(q, k, v, 0.7)
+    for i in range(T):
+        lim = n - T + i + 1
+        assert np.all(np.isneginf(lg[:, i, lim:])) and np.all(np.isfinite(lg[:, i, :lim]))
+        k2, v2 = k.copy(), v.copy()
+        k2[:, lim:] = rng.standard_normal(k2[:, lim:].shape)
+        v2[:, lim:] = 1e3
+        _, out2 = oracle.attention_prefill(q, k2, v2, 0.7)
+        assert np.allclose(out2[i], out[i], atol=1e-12)
+    for i in range(T):
+        for h in range(hkv * g):
+            lim = n - T + i + 1
+            w = [math.exp(0.7 * sum(q[i, h, e] * k[h // g, t, e] for e in range(d))) for t in range(lim)]
+            ref = [sum(w[t] * v[h // g, t, e] for t in range(lim)) / sum(w) for e in range(d)]
+            assert np.allclose(out[i, h], ref, atol=1e-12)
+
+
 def test_legal_variants_cover_near_boundary_choices():
     d = 16
     qz = _quantizer(d, ((d, 2),), seed=41)
