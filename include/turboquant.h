@@ -295,6 +295,35 @@ tq_status tq_attn_decode_phases(unsigned phases, const tq_quantizer* kq, const t
                                 const tq_cache* k_cache, const tq_cache* v_cache, float* logits,
                                 float* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* A paged cache (a block table with per-sequence lengths). Physical block p
+ * holds 32 consecutive tokens of every KV head: the K and V records of KV
+ * head h at token offset i of block p are row (p * n_kv_heads + h) * 32 + i
+ * of the caches (for TQ_BLOCK32 V caches that is block p * n_kv_heads + h).
+ * Logical block j (tokens [32 j, 32 j + 32)) of batch b lives in physical
+ * block block_table[b * max_blocks + j]. */
+typedef struct {
+  const int32_t* block_table; /* device [batch, max_blocks] physical block ids */
+  const int32_t* seq_lens;    /* device [batch] cached tokens per sequence, clamped
+                                 to [1, n_ctx]; NULL: n_ctx for every sequence */
+  int32_t max_blocks;         /* row length of block_table; 32 * max_blocks must
+                                 equal the shape's cache_capacity */
+} tq_paging;
+
+/* tq_attn_decode over a paged cache (the paged layout is this library's
+ * extension of the decode step for serving with per-sequence lengths; the
+ * arithmetic is that of tq_attn_decode). shape->n_ctx is the longest
+ * sequence: logits rows keep that length and entries past a sequence's own
+ * length are not written; n_q_tokens chunks take their causal limits from
+ * each sequence's length. Block ids outside the caches are clamped into them
+ * (the caller keeps the table valid; nothing is read outside the caches).
+ * Workspace: tq_attn_decode_workspace_bytes(shape). Errors as
+ * tq_attn_decode, plus TQ_ERR_INVALID for a missing or misaligned table or
+ * a capacity other than 32 * max_blocks. */
+tq_status tq_attn_decode_paged(const tq_quantizer* kq, const tq_quantizer* vq, const tq_decode_shape* shape,
+                               const tq_paging* paging, const void* q, tq_dtype q_dtype,
+                               const tq_cache* k_cache, const tq_cache* v_cache, float* logits, float* out,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Vectors to append to a cache within a decode step (see
  * tq_attn_decode_append): x, dtype, n_vec, x_row_stride and rows as for
  * tq_quantize. */

@@ -43,7 +43,7 @@ TQ_PHASE_ALL = 7
 SYMBOLS = ("tq_abi_version", "tq_status_string", "tq_build_codebook", "tq_record_layout",
            "tq_fold_sketch", "tq_quantize", "tq_attn_decode_workspace_bytes", "tq_attn_decode",
            "tq_attn_decode_phases", "tq_attn_decode_append", "tq_attn_decode_bf16_workspace_bytes",
-           "tq_attn_decode_bf16", "tq_search_workspace_bytes", "tq_search")
+           "tq_attn_decode_bf16", "tq_search_workspace_bytes", "tq_search", "tq_attn_decode_paged")
 
 
 class TQError(RuntimeError):
@@ -87,6 +87,10 @@ class tq_decode_shape(C.Structure):
     _fields_ = [("batch", C.c_int32), ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32),
                 ("n_split", C.c_int32), ("n_ctx", C.c_int64), ("cache_capacity", C.c_int64),
                 ("scale", C.c_float), ("n_q_tokens", C.c_int32)]
+
+
+class tq_paging(C.Structure):
+    _fields_ = [("block_table", C.c_void_p), ("seq_lens", C.c_void_p), ("max_blocks", C.c_int32)]
 
 
 _lib = None
@@ -143,6 +147,9 @@ def lib() -> C.CDLL:
         L.tq_attn_decode_bf16.argtypes = [C.POINTER(tq_decode_shape), C.c_int, C.c_void_p, C.c_int, C.c_void_p,
                                           C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
                                           C.c_void_p]
+        L.tq_attn_decode_paged.restype = C.c_int
+        L.tq_attn_decode_paged.argtypes = (L.tq_attn_decode.argtypes[:3] + [C.POINTER(tq_paging)] +
+                                           L.tq_attn_decode.argtypes[3:])
         L.tq_search_workspace_bytes.restype = C.c_int
         L.tq_search_workspace_bytes.argtypes = [C.POINTER(tq_quantizer), C.c_int64, C.c_int64, C.c_int,
                                                 C.POINTER(C.c_size_t)]
@@ -464,6 +471,34 @@ def tq_attn_decode_bf16(shape: tq_decode_shape, q, k, v, out, logits=None, works
            "tq_attn_decode_bf16")
 
 
+def tq_attn_decode_paged(kq: Quantizer, vq: Optional[Quantizer], shape: tq_decode_shape, block_table, q,
+                         k_cache: Cache, v_cache: Optional[Cache], seq_lens=None, logits=None, out=None,
+                         workspace=None, stream=None) -> None:
+    """tq_attn_decode over a paged cache (see include/turboquant.h):
+    block_table int32 device tensor [batch, max_blocks]; seq_lens int32
+    device tensor [batch] or None."""
+    torch = _torch()
+    if not q.is_contiguous() or not block_table.is_contiguous() or block_table.dtype != torch.int32:
+        raise ValueError("q and block_table must be contiguous; block_table int32")
+    dt = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}[q.dtype]
+    if workspace is None:
+        workspace = torch.empty(tq_attn_decode_workspace_bytes(kq, vq, shape), dtype=torch.uint8,
+                                device=q.device)
+    pg = tq_paging()
+    pg.block_table = _ptr(block_table)
+    pg.seq_lens = _ptr(seq_lens)
+    pg.max_blocks = int(block_table.shape[-1])
+    kqs = kq.struct()
+    vqs = vq.struct() if vq is not None else None
+    kc = k_cache.struct()
+    vc = v_cache.struct() if v_cache is not None else None
+    _check(lib().tq_attn_decode_paged(C.byref(kqs), C.byref(vqs) if vqs is not None else None, C.byref(shape),
+                                      C.byref(pg), _ptr(q), dt, C.byref(kc),
+                                      C.byref(vc) if vc is not None else None, _ptr(logits), _ptr(out),
+                                      _ptr(workspace), workspace.numel(), _stream(stream)),
+           "tq_attn_decode_paged")
+
+
 def tq_search_workspace_bytes(quantizer: Quantizer, n_db: int, n_q: int, k: int) -> int:
     n = C.c_size_t()
     q = quantizer.struct()
@@ -500,7 +535,7 @@ __all__ = [
     "tq_abi_version", "tq_status_string", "tq_build_codebook", "tq_record_layout", "tq_fold_sketch",
     "tq_quantize", "tq_attn_decode_workspace_bytes", "tq_attn_decode", "tq_attn_decode_phases",
     "tq_attn_decode_append", "append_spec", "tq_append", "tq_attn_decode_bf16_workspace_bytes",
-    "tq_attn_decode_bf16", "tq_search_workspace_bytes", "tq_search",
+    "tq_attn_decode_bf16", "tq_search_workspace_bytes", "tq_search", "tq_attn_decode_paged", "tq_paging",
     "TQ_PHASE_PREP", "TQ_PHASE_SPLIT", "TQ_PHASE_COMBINE", "TQ_PHASE_ALL",
     "TQ_OK", "TQ_ERR_INVALID", "TQ_ERR_UNSUPPORTED", "TQ_ERR_NOCONVERGE", "TQ_ERR_WORKSPACE",
     "TQ_ERR_DEVICE", "TQ_F32", "TQ_BF16", "TQ_TOKEN_MAJOR", "TQ_BLOCK32",

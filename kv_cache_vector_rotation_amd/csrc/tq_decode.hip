@@ -87,6 +87,13 @@ struct DArgs {
   const float* vcent;
   float* logits;  // [batch, hq, n_ctx] or null
   float* part;    // [batch*hq][n_split][2 + 2d]
+  // paged cache (block_table non-null): logical 32-token block j of batch b
+  // is physical block block_table[b * max_blocks + j], whose rows are
+  // (block * hkv + kv head) * 32 + token; seq_lens[b] (or n_ctx) tokens
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int max_blocks;
+  int64_t n_pblocks;  // physical blocks in the caches (entries are clamped into range)
 };
 
 // two floats -> packed fp16 pair (round to nearest even; one v_cvt_pk_f16_f32)
@@ -421,12 +428,24 @@ __global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel
 
   // ---- this wave's tiles; the first one is loaded before the tables are
   // built, so its memory latency overlaps the table setup ----
-  const int64_t N = a.n_ctx;
+  // tokens of this sequence (a paged call may give each its own length)
+  int64_t N = a.n_ctx;
+  if (a.seq_lens) {
+    const int64_t n = a.seq_lens[b];
+    N = n < 1 ? 1 : (n > a.n_ctx ? a.n_ctx : n);
+  }
   const int64_t n_tiles = (N + kTile - 1) / kTile;
   const int64_t tps = (n_tiles + a.n_split - 1) / a.n_split;
   const int64_t t_begin = split * tps;
   const int64_t t_end = t_begin + tps < n_tiles ? t_begin + tps : n_tiles;
   const int64_t rowbase = (int64_t)bh * a.cap;
+  // first cache row of tile t of this (batch, KV head)
+  auto tile_row = [&](int64_t t) __attribute__((always_inline)) -> int64_t {
+    if (!a.block_table) return rowbase + t * kTile;
+    int64_t pb = a.block_table[(int64_t)b * a.max_blocks + t];
+    pb = pb < 0 ? 0 : (pb >= a.n_pblocks ? a.n_pblocks - 1 : pb);
+    return (pb * a.hkv + kvh) * kTile;
+  };
   const LaneOff<D, NG, M0, M1> lo = lane_offsets<D, NG, M0, M1>(ln, lg);
   // lane l stages floats l NG + e of a tile's K norms [32][n_0, gamma_0, ..]:
   // an n_g is divided by the group's codebook scale s_g
@@ -497,7 +516,7 @@ __global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel
   int64_t tile = t_begin + wv;
   // (unconditional, so the wait for the centroids below need not drain it;
   // a wave without tiles loads tile 0, which always exists, and drops it)
-  load_tile<D, NG, M0, M1, WV>(a, rowbase + (tile < t_end ? tile : 0) * kTile, lane, lo, rb0);
+  load_tile<D, NG, M0, M1, WV>(a, tile_row(tile < t_end ? tile : 0), lane, lo, rb0);
   if (tid < 32) {
     s_cent[0][tid] = cent_k;
     s_cent[1][tid] = cent_v;
@@ -632,7 +651,7 @@ __global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel
     // finite values that no result uses)
     if (a.logits) {
       if (hvalid && role == 0) {
-        float* lp = a.logits + ((int64_t)b * a.hq + hq) * N + tok0;
+        float* lp = a.logits + ((int64_t)b * a.hq + hq) * a.n_ctx + tok0;
 #pragma unroll
         for (int j = 0; j < 8; ++j)
           if (8 * lg + j < nvt) lp[j] = l2[j] * kLn2;
@@ -751,12 +770,12 @@ __global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel
   if (tile < t_end) {
     const int64_t last = t_end - 1 - ((t_end - 1 - tile) % kWaves);  // this wave's last tile
     auto next = [&](int64_t t, int k) { return t + k * kWaves <= last ? t + k * kWaves : last; };
-    if constexpr (NBUF > 2) load_tile<D, NG, M0, M1, WV>(a, rowbase + next(tile, 1) * kTile, lane, lo, rb1);
-    if constexpr (NBUF > 3) load_tile<D, NG, M0, M1, WV>(a, rowbase + next(tile, 2) * kTile, lane, lo, rb2);
+    if constexpr (NBUF > 2) load_tile<D, NG, M0, M1, WV>(a, tile_row(next(tile, 1)), lane, lo, rb1);
+    if constexpr (NBUF > 3) load_tile<D, NG, M0, M1, WV>(a, tile_row(next(tile, 2)), lane, lo, rb2);
     // one pass of the rotation: true after the wave's last tile
     auto stage = [&](auto kc) __attribute__((always_inline)) {
       constexpr int k = decltype(kc)::value;
-      load_tile<D, NG, M0, M1, WV>(a, rowbase + next(tile, NBUF - 1) * kTile, lane, lo,
+      load_tile<D, NG, M0, M1, WV>(a, tile_row(next(tile, NBUF - 1)), lane, lo,
                                    rbuf(std::integral_constant<int, k + NBUF - 1>{}));
       compute(rbuf(kc), tile * kTile);
       if (tile == last) return true;
@@ -1106,13 +1125,21 @@ constexpr int kD = 128;  // the decode kernels' dimension
 
 tq_status plan_decode(const tq_quantizer* kq, const tq_quantizer* vq, const tq_decode_shape* shape,
                       const void* q, tq_dtype q_dtype, const tq_cache* k_cache, const tq_cache* v_cache,
-                      float* logits, float* out, void* workspace, size_t workspace_bytes, Plan* pl) {
+                      float* logits, float* out, void* workspace, size_t workspace_bytes, Plan* pl,
+                      const tq_paging* paging = nullptr) {
   if (!tq::quantizer_pointers_valid(kq) || !shape_valid(shape)) return TQ_ERR_INVALID;
+  if (paging && (!paging->block_table || paging->max_blocks < 1 ||
+                 reinterpret_cast<uintptr_t>(paging->block_table) % 4 != 0 ||
+                 reinterpret_cast<uintptr_t>(paging->seq_lens) % 4 != 0 ||
+                 shape->cache_capacity != (int64_t)kTile * paging->max_blocks))
+    return TQ_ERR_INVALID;
   if (vq && !tq::quantizer_pointers_valid(vq)) return TQ_ERR_INVALID;
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_ERR_INVALID;
   if (!q || reinterpret_cast<uintptr_t>(q) % 16 != 0) return TQ_ERR_INVALID;
   if (!k_cache || !k_cache->codes || !k_cache->signs || !k_cache->norms) return TQ_ERR_INVALID;
-  const int64_t rows_needed = (int64_t)shape->batch * shape->n_kv_heads * shape->cache_capacity;
+  // (paged: at least one physical block of every KV head)
+  const int64_t rows_needed =
+      paging ? (int64_t)shape->n_kv_heads * kTile : (int64_t)shape->batch * shape->n_kv_heads * shape->cache_capacity;
   if (k_cache->n_rows < rows_needed) return TQ_ERR_INVALID;
   const bool with_v = vq != nullptr;
   if (with_v) {
@@ -1200,6 +1227,17 @@ tq_status plan_decode(const tq_quantizer* kq, const tq_quantizer* vq, const tq_d
   }
   a.logits = logits;
   a.part = part;
+  if (paging) {
+    a.block_table = paging->block_table;
+    a.seq_lens = paging->seq_lens;
+    a.max_blocks = paging->max_blocks;
+    int64_t nb = k_cache->n_rows / ((int64_t)kTile * shape->n_kv_heads);
+    if (with_v) {
+      const int64_t nv = v_cache->n_rows / ((int64_t)kTile * shape->n_kv_heads);
+      nb = nv < nb ? nv : nb;
+    }
+    a.n_pblocks = nb;
+  }
   return TQ_OK;
 }
 
@@ -1337,6 +1375,19 @@ extern "C" tq_status tq_attn_decode_append(const tq_quantizer* kq, const tq_quan
     hipLaunchKernelGGL(step_kernel<false>, dim3(grid), dim3(kStepNT * 64), lds_use, hs, sa);
   if (hipGetLastError() != hipSuccess) return TQ_ERR_DEVICE;
   return run_phases(pl, TQ_PHASE_SPLIT | TQ_PHASE_COMBINE, hs);
+}
+
+extern "C" tq_status tq_attn_decode_paged(const tq_quantizer* kq, const tq_quantizer* vq,
+                                          const tq_decode_shape* shape, const tq_paging* paging,
+                                          const void* q, tq_dtype q_dtype, const tq_cache* k_cache,
+                                          const tq_cache* v_cache, float* logits, float* out,
+                                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (!paging) return TQ_ERR_INVALID;
+  Plan pl;
+  const tq_status st = plan_decode(kq, vq, shape, q, q_dtype, k_cache, v_cache, logits, out, workspace,
+                                   workspace_bytes, &pl, paging);
+  if (st != TQ_OK) return st;
+  return run_phases(pl, TQ_PHASE_ALL, reinterpret_cast<hipStream_t>(stream));
 }
 
 extern "C" tq_status tq_attn_decode(const tq_quantizer* kq, const tq_quantizer* vq,

@@ -30,7 +30,7 @@ def tq():
 def test_header_symbols_exported(tq):
     text = open(HEADER).read()
     declared = sorted(set(re.findall(r"^\s*(?:tq_status|int|const char\*)\s+(tq_\w+)\s*\(", text, re.M)))
-    assert len(declared) == 14
+    assert len(declared) == 15
     lib = C.CDLL(tq.LIB_PATH)
     for name in declared:
         assert hasattr(lib, name), name

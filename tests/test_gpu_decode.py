@@ -382,3 +382,99 @@ def test_causal_chunk_append_step_equals_separate_calls(tq):
         res.append((kc.codes.cpu(), vc.codes.cpu(), out.cpu()))
     for x, y in zip(res[0], res[1]):
         assert torch.equal(x, y)
+
+
+def _paged_arrays(tq, o, B, H, cap, n_pblocks, table):
+    """Scatter the contiguous oracle caches of _oracle_side into a paged
+    layout: logical block j of batch b -> physical block table[b, j]."""
+    import kv_cache_vector_rotation_amd as m
+    cw, sw, nf, bcw, bsw = oracle.record_words(o["dims"], o["bits"])
+    kc, ks_, kn = (a.reshape(B * H * cap, -1) for a in o["karr"])
+    vc, vs_, vn = o["varr"]
+    vc = vc.reshape(B * H * cap // 32, bcw)
+    vs_ = vs_.reshape(B * H * cap // 32, bsw)
+    vn = vn.reshape(B * H * cap, nf)
+    rows = n_pblocks * H * 32
+    pk = [np.zeros((rows, a.shape[1]), a.dtype) for a in (kc, ks_, kn)]
+    pv = [np.zeros((n_pblocks * H, bcw), vc.dtype), np.zeros((n_pblocks * H, bsw), vs_.dtype),
+          np.zeros((rows, nf), vn.dtype)]
+    for b in range(B):
+        for j in range(cap // 32):
+            p = table[b, j]
+            for h in range(H):
+                src = (b * H + h) * cap + 32 * j
+                dst = (p * H + h) * 32
+                for a, t in zip((kc, ks_, kn), pk):
+                    t[dst:dst + 32] = a[src:src + 32]
+                pv[0][p * H + h] = vc[src // 32]
+                pv[1][p * H + h] = vs_[src // 32]
+                pv[2][dst:dst + 32] = vn[src:src + 32]
+    return tuple(a.ravel() for a in pk), tuple(a.ravel() for a in pv), rows
+
+
+def _paged_setup(tq, wl, n_ctx, cap, seed=3):
+    B, H = wl.batch, wl.n_kv_heads
+    o = _oracle_side(wl, n_ctx, cap)
+    kq = tq.Quantizer.from_parts(o["ks"].rotations, o["ks"].sketches, o["bits"], perm=o["ks"].perm)
+    vq = tq.Quantizer.from_parts(o["vs"].rotations, o["vs"].sketches, o["bits"], perm=o["vs"].perm)
+    mb = cap // 32
+    n_pblocks = B * mb + 5  # a few physical blocks that no sequence uses
+    table = np.random.default_rng(seed).permutation(n_pblocks)[:B * mb].reshape(B, mb).astype(np.int32)
+    parr_k, parr_v, rows = _paged_arrays(tq, o, B, H, cap, n_pblocks, table)
+    kc = gc.to_device_cache(kq, tq.TQ_TOKEN_MAJOR, rows, parr_k)
+    vc = gc.to_device_cache(vq, tq.TQ_BLOCK32, rows, parr_v)
+    return o, kq, vq, kc, vc, table
+
+
+def test_paged_cache_equals_contiguous(tq):
+    # the same records in a block-table layout give the same outputs and
+    # logits, bit for bit, as the contiguous cache
+    import torch
+    wl = synth.workload("llama8b_decode", batch=3, n_q_heads=8, n_kv_heads=2)
+    n_ctx, cap = 1000, 1024
+    o, kq, vq, kc, vc, table = _paged_setup(tq, wl, n_ctx, cap)
+    q = torch.from_numpy(synth.draw_queries(wl)).cuda().to(torch.bfloat16)
+    shape = tq.decode_shape(3, 8, 2, n_ctx, cap, wl.scale)
+    res = []
+    for paged in (False, True):
+        lg = torch.full((3, 8, n_ctx), float("nan"), device="cuda")
+        out = torch.full((3, 8, 128), float("nan"), device="cuda")
+        if paged:
+            tq.tq_attn_decode_paged(kq, vq, shape, torch.from_numpy(table).cuda(), q, kc, vc, logits=lg, out=out)
+        else:
+            kc0 = gc.to_device_cache(kq, tq.TQ_TOKEN_MAJOR, 3 * 2 * cap, o["karr"])
+            vc0 = gc.to_device_cache(vq, tq.TQ_BLOCK32, 3 * 2 * cap, o["varr"])
+            tq.tq_attn_decode(kq, vq, shape, q, kc0, vc0, logits=lg, out=out)
+        torch.cuda.synchronize()
+        res.append((lg.cpu(), out.cpu()))
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+
+
+@pytest.mark.parametrize("T", [1, 5])
+def test_paged_cache_per_sequence_lengths(tq, T):
+    # sequences of 1000, 517 and 33 tokens in one call (and a causal chunk of
+    # T tokens at the end of each), against the oracle on each sequence's
+    # own prefix
+    import torch
+    wl = synth.workload("llama8b_decode", batch=3, n_q_heads=8, n_kv_heads=2)
+    n_ctx, cap = 1000, 1024
+    lens = np.array([1000, 517, 33], np.int32)
+    o, kq, vq, kc, vc, table = _paged_setup(tq, wl, n_ctx, cap, seed=5)
+    q = _chunk_queries(wl, T)
+    qt = torch.from_numpy(q).cuda().to(torch.bfloat16)
+    shape = tq.decode_shape(3, 8, 2, n_ctx, cap, wl.scale, n_q_tokens=T)
+    lg = torch.full((3, 8, T, n_ctx), float("nan"), device="cuda")
+    out = torch.full((3, T, 8, 128), float("nan"), device="cuda")
+    tq.tq_attn_decode_paged(kq, vq, shape, torch.from_numpy(table).cuda(), qt, kc, vc,
+                            seq_lens=torch.from_numpy(lens).cuda(), logits=lg, out=out)
+    torch.cuda.synchronize()
+    lgn, otn = lg.cpu().numpy().astype(np.float64), out.cpu().numpy().astype(np.float64)
+    for b in range(3):
+        n = int(lens[b])
+        rl, ro = oracle.attention_prefill(q[b].astype(np.float64), o["k_t"][b][:, :n], o["v_t"][b][:, :n],
+                                          wl.scale)
+        assert gc.normwise_close(otn[b], ro)[0], b
+        for i in range(T):
+            lim = n - T + i + 1
+            assert gc.normwise_close(lgn[b, :, i, :lim], rl[:, i, :lim])[0], (b, i)
+        assert np.all(np.isnan(lgn[b, :, :, n:]))  # past the sequence: not written
