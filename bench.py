@@ -62,6 +62,7 @@ def parse():
     ap.add_argument("--no-quantize-bench", action="store_true")
     ap.add_argument("--no-bf16-baseline", action="store_true")
     ap.add_argument("--no-search", action="store_true")
+    ap.add_argument("--no-chunk", action="store_true", help="skip the prefill-chunk and paged-cache legs")
     ap.add_argument("--ctx-sweep", default="",
                     help="comma-separated context lengths: also time the compressed step and the bf16 "
                          "decode of the llama8b_decode shape at each (reported under ctx_sweep)")
@@ -254,18 +255,23 @@ def search_bench(tq, torch, reps=5):
             "frac": round(tf / PEAK_FP16_MFMA_TFLOPS, 4), "recall_at_10": hits / (n_q * k)}
 
 
-def compressed_step_us(tq, torch, wl, kq, vq, n_copies, reps=20):
+def compressed_step_us(tq, torch, wl, kq, vq, n_copies, reps=20, T=1):
     """Mean time of tq_attn_decode_append steps (graph of one step per cache
-    copy, replayed), in microseconds."""
+    copy, replayed), in microseconds. T > 1: a causal chunk of T query tokens
+    per head (the workload's last T tokens are the ones appended)."""
     B, HQ, H, N, cap = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.n_ctx, wl.capacity
     prefix = N - wl.n_new
     kc0, vc0 = build_caches(tq, torch, wl, kq, vq, prefix, cap)
     caches = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(n_copies - 1)]
     k_new, v_new = new_tokens(torch, wl, prefix)
-    q = torch.from_numpy(synth.draw_queries(wl)).cuda().to(torch.bfloat16)
-    shape = tq.decode_shape(B, HQ, H, N, cap, wl.scale)
+    if T == 1:
+        qn = synth.draw_queries(wl)
+    else:
+        qn = synth.to_bf16_exact(synth.standard_normal(synth.rng_for(wl.seed, 21, T), (B, T, HQ, wl.d)))
+    q = torch.from_numpy(qn).cuda().to(torch.bfloat16)
+    shape = tq.decode_shape(B, HQ, H, N, cap, wl.scale, n_q_tokens=T)
     ws = torch.empty(tq.tq_attn_decode_workspace_bytes(kq, vq, shape), dtype=torch.uint8, device="cuda")
-    out = torch.empty((B, HQ, wl.d), dtype=torch.float32, device="cuda")
+    out = torch.empty((B, T, HQ, wl.d), dtype=torch.float32, device="cuda")
     k_app = tq.append_spec(k_new, seg_len=wl.n_new, seg_stride=cap, seg_offset=prefix)
     v_app = tq.append_spec(v_new, seg_len=wl.n_new, seg_stride=cap, seg_offset=prefix)
 
@@ -288,6 +294,93 @@ def compressed_step_us(tq, torch, wl, kq, vq, n_copies, reps=20):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e3 / (reps * n_copies)
+
+
+def _llama8b_quantizers(tq):
+    base = synth.workload("llama8b_decode")
+    ks, vs = synth.draw_quantizer(base, "K"), synth.draw_quantizer(base, "V")
+    bits = [g.mse_bits for g in ks.groups]
+    return (tq.Quantizer.from_parts(ks.rotations, ks.sketches, bits, perm=ks.perm),
+            tq.Quantizer.from_parts(vs.rotations, vs.sketches, bits, perm=vs.perm))
+
+
+def chunk_bench(tq, torch, T=64):
+    """Secondary figure: a prefill chunk on the llama8b_decode shape: T new
+    tokens per KV head appended (K and V) and T x 32 query tokens attended
+    causally over the 32768-token cache, one tq_attn_decode_append call."""
+    wl = synth.workload("llama8b_decode", n_new=T)
+    kq, vq = _llama8b_quantizers(tq)
+    rb = record_bytes([g for g, _ in wl.groups], [m for _, m in wl.groups])
+    copies = max(1, math.ceil((1 << 30) / (wl.batch * wl.n_kv_heads * wl.capacity * 2 * rb)))
+    us = compressed_step_us(tq, torch, wl, kq, vq, copies, T=T)
+    return {"workload": "llama8b_decode", "query_tokens_per_head": T, "n_ctx": wl.n_ctx,
+            "us_per_chunk": round(us, 2), "query_tokens_per_s": wl.batch * T / (us / 1e6),
+            "cache_copies": copies}
+
+
+def paged_bench(tq, torch, n_copies=8, reps=20):
+    """Secondary figure: the llama8b_decode decode (prep, split-K, combine; no
+    append) through tq_attn_decode_paged with a shuffled block table, against
+    tq_attn_decode on the contiguous cache holding the same records; both
+    over n_copies rotated cache copies."""
+    wl = synth.workload("llama8b_decode")
+    kq, vq = _llama8b_quantizers(tq)
+    B, HQ, H, N, cap = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.n_ctx, wl.capacity
+    kc0, vc0 = build_caches(tq, torch, wl, kq, vq, N, cap)
+    mb = cap // 32
+    perm = torch.from_numpy(np.random.default_rng(7).permutation(B * mb).astype(np.int64)).cuda()
+    table = perm.view(B, mb).to(torch.int32).contiguous()
+    # physical block p holds logical block j of batch b where perm[b mb + j] = p
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(B * mb, device="cuda")
+    info = tq.tq_record_layout(kq.layout)
+    b_of = inv // mb
+    j_of = inv % mb
+    hh = torch.arange(H, device="cuda")
+    src_blk = ((b_of[:, None] * H + hh[None, :]) * mb + j_of[:, None]).reshape(-1)  # contiguous 32-row block
+    src_rows = (src_blk[:, None] * 32 + torch.arange(32, device="cuda")[None, :]).reshape(-1)
+    kp = tq.Cache(fmt=tq.TQ_TOKEN_MAJOR, n_rows=kc0.n_rows,
+                  codes=kc0.codes.view(-1, info.code_words)[src_rows].reshape(-1).contiguous(),
+                  signs=kc0.signs.view(-1, info.sign_words)[src_rows].reshape(-1).contiguous(),
+                  norms=kc0.norms.view(-1, info.norm_floats)[src_rows].reshape(-1).contiguous())
+    vp = tq.Cache(fmt=tq.TQ_BLOCK32, n_rows=vc0.n_rows,
+                  codes=vc0.codes.view(-1, info.block_code_words)[src_blk].reshape(-1).contiguous(),
+                  signs=vc0.signs.view(-1, info.block_sign_words)[src_blk].reshape(-1).contiguous(),
+                  norms=vc0.norms.view(-1, info.norm_floats)[src_rows].reshape(-1).contiguous())
+    q = torch.from_numpy(synth.draw_queries(wl)).cuda().to(torch.bfloat16)
+    shape = tq.decode_shape(B, HQ, H, N, cap, wl.scale)
+    ws = torch.empty(tq.tq_attn_decode_workspace_bytes(kq, vq, shape), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, HQ, wl.d), dtype=torch.float32, device="cuda")
+    res = {}
+    for name, pair in (("contiguous", (kc0, vc0)), ("paged", (kp, vp))):
+        copies = [pair] + [(pair[0].clone(), pair[1].clone()) for _ in range(n_copies - 1)]
+
+        def call(i):
+            k, v = copies[i]
+            if name == "paged":
+                tq.tq_attn_decode_paged(kq, vq, shape, table, q, k, v, out=out, workspace=ws)
+            else:
+                tq.tq_attn_decode(kq, vq, shape, q, k, v, out=out, workspace=ws)
+        for i in range(n_copies):
+            call(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n_copies):
+                call(i)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) * 1e3 / (reps * n_copies)
+        del copies
+    return {"workload": "llama8b_decode", "us_per_decode_contiguous": round(res["contiguous"], 2),
+            "us_per_decode_paged": round(res["paged"], 2), "cache_copies": n_copies,
+            "block_table": "shuffled 32-token blocks"}
 
 
 def ctx_sweep(tq, torch, contexts):
@@ -525,6 +618,11 @@ def main():
     if not args.no_quantize_bench:
         result["quantize"] = quantize_bench(tq, torch, wl, kq)
         log(f"quantize: {result['quantize']}")
+    if not args.no_chunk:
+        result["chunk"] = chunk_bench(tq, torch)
+        log(f"chunk: {result['chunk']}")
+        result["paged"] = paged_bench(tq, torch)
+        log(f"paged: {result['paged']}")
     if not args.no_search:
         result["search"] = search_bench(tq, torch)
         log(f"search: {result['search']}")
