@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 2
+#define TQ_ABI_VERSION 3
 
 typedef enum {
   TQ_OK = 0,
@@ -91,6 +91,11 @@ typedef struct {
   int32_t n_groups;     /* 1 or 2 */
   int32_t group_dim[2]; /* d_g >= 3, sum over groups == d */
   int32_t mse_bits[2];  /* m_g in [1, 4]; bits per channel of group g = m_g + 1 */
+  int32_t mse_only;     /* 0: stage two as above (sign bits of the residual sketch);
+                           1: stage one alone (the MSE quantizer): records carry no
+                           sign words, bits per channel = m_g, gamma is stored but
+                           not used, and dequantization is n Pi^T c[idx]. Decode
+                           takes it for V only. */
 } tq_layout;
 
 /* One quantizer instance (one for K, one for V). All pointers are device
@@ -137,7 +142,8 @@ typedef struct {
   int32_t norm_floats;      /* floats per row, both formats: 2 * n_groups */
   int32_t block_code_words; /* TQ_BLOCK32 code words per 32-row block */
   int32_t block_sign_words; /* TQ_BLOCK32 sign words per 32-row block */
-  int32_t record_bits;      /* algorithmic bits per row: sum_g (m_g + 1) d_g + 64 n_groups */
+  int32_t record_bits;      /* algorithmic bits per row: sum_g (m_g + 1) d_g + 64 n_groups
+                               (MSE-only: sum_g m_g d_g + 64 n_groups) */
 } tq_record_info;
 
 /*
@@ -161,6 +167,9 @@ typedef struct {
  *          stream bit 8 (o d_g + j) + s.
  *   norms: as TQ_TOKEN_MAJOR (one row per token).
  * A sign bit is 1 exactly when the sketch coordinate is >= 0.
+ * MSE-only layouts have no sign words (sign_words = block_sign_words = 0);
+ * their norms keep the (n_g, gamma_g) pair, gamma_g being the norm of the
+ * stage-one residual.
  */
 
 /* Rows written by tq_quantize. Vector i goes to row dst_rows[i] when
@@ -267,9 +276,11 @@ tq_status tq_attn_decode_workspace_bytes(const tq_quantizer* kq, const tq_quanti
  *            vq is NULL.
  *   out      device fp32 [batch, n_q_heads, d]; must be NULL when vq is NULL.
  *   workspace device scratch of at least tq_attn_decode_workspace_bytes().
- * Supported: kq and vq with the same layout, every group dimension a
- * multiple of 32, d <= 256 (this build: d = 128), otherwise
- * TQ_ERR_UNSUPPORTED. Errors: TQ_ERR_INVALID, TQ_ERR_WORKSPACE,
+ * Supported: kq and vq with the same group dimensions and bits, every group
+ * dimension a multiple of 32, d <= 256 (this build: d = 128), kq with sign
+ * bits (mse_only = 0), otherwise TQ_ERR_UNSUPPORTED. vq may be MSE-only
+ * (mse_only = 1): then v_cache->signs is not read (it may be NULL) and each
+ * value is dequantized as n Pi^T c[idx], the biased stage-one estimate. Errors: TQ_ERR_INVALID, TQ_ERR_WORKSPACE,
  * TQ_ERR_DEVICE. */
 tq_status tq_attn_decode(const tq_quantizer* kq, const tq_quantizer* vq,
                          const tq_decode_shape* shape, const void* q, tq_dtype q_dtype,
@@ -395,8 +406,8 @@ tq_status tq_attn_decode_bf16(const tq_decode_shape* shape, int d, const void* q
  *   workspace  device scratch of at least tq_search_workspace_bytes() bytes.
  * Limits: 1 <= n_db < 2^31 - 1, 1 <= n_q <= 2^30.
  * Errors: TQ_ERR_INVALID (sizes, k, null or misaligned pointers, dtype),
- * TQ_ERR_UNSUPPORTED (layout outside the limits above), TQ_ERR_WORKSPACE,
- * TQ_ERR_DEVICE. */
+ * TQ_ERR_UNSUPPORTED (layout outside the limits above, or MSE-only records),
+ * TQ_ERR_WORKSPACE, TQ_ERR_DEVICE. */
 tq_status tq_search_workspace_bytes(const tq_quantizer* qz, int64_t n_db, int64_t n_q, int k, size_t* bytes);
 tq_status tq_search(const tq_quantizer* qz, const tq_cache* db, int64_t n_db, const void* q, tq_dtype q_dtype,
                     int64_t n_q, int k, int64_t* out_idx, float* out_score, void* workspace,

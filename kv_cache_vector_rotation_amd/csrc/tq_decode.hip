@@ -356,7 +356,7 @@ __device__ __forceinline__ LaneOff<D, NG, M0, M1> lane_offsets(int ln, int lg) {
 
 // Loads one 32-token tile whose first cache row is row0 (wave-uniform, a
 // multiple of 32): the base addresses are scalar, the lanes add their offsets.
-template <int D, int NG, int M0, int M1, bool WV>
+template <int D, int NG, int M0, int M1, int WV>
 __device__ __forceinline__ void load_tile(const DArgs& a, int64_t row0, int lane,
                                           const LaneOff<D, NG, M0, M1>& o, Raw<D, NG, M0, M1>& r) {
   using G = Geo<D, NG, M0, M1>;
@@ -375,7 +375,7 @@ __device__ __forceinline__ void load_tile(const DArgs& a, int64_t row0, int lane
   const float* kn = a.kn + row0 * (2 * NG);
 #pragma unroll
   for (int e = 0; e < NG; ++e) r.kn[e] = kn[lane * NG + e];
-  if constexpr (WV) {
+  if constexpr (WV != 0) {
     const float* vn = a.vn + row0 * (2 * NG);
 #pragma unroll
     for (int e = 0; e < NG; ++e) r.vn[e] = vn[lane * NG + e];
@@ -385,7 +385,7 @@ __device__ __forceinline__ void load_tile(const DArgs& a, int64_t row0, int lane
     auto v_words = [&](auto gc) {
       constexpr int g = decltype(gc)::value;
       load_w<G::VNW[g]>(vc + o.vc[g], &r.vc[G::VOFF[g]]);
-      load_w<G::VNS>(vs + o.vs[g], &r.vs[G::VNS * g]);
+      if constexpr (WV == 1) load_w<G::VNS>(vs + o.vs[g], &r.vs[G::VNS * g]);
     };
     v_words(std::integral_constant<int, 0>{});
     if constexpr (NG > 1) v_words(std::integral_constant<int, 1>{});
@@ -398,7 +398,9 @@ __device__ __forceinline__ void load_tile(const DArgs& a, int64_t row0, int lane
 // [q_rot hi | q_rot lo | q_sk | unused] x 4 heads for the logits and
 // [p n | p gamma | 0 | 0] x 4 heads for the V sums, so one accumulator
 // serves all three logit parts and one serves both V parts.
-template <int D, int NG, int M0, int M1, bool WV, int HB>
+// WV = 0: logits only; 1: V records with sign bits; 2: MSE-only V records
+// (codes and norms alone; the sign product is skipped).
+template <int D, int NG, int M0, int M1, int WV, int HB>
 __global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel(DArgs a) {
   using G = Geo<D, NG, M0, M1>;
   constexpr bool PK = HB == 4;
@@ -464,7 +466,7 @@ __global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel
     const int nc = (1 << M0) + (NG > 1 ? (1 << M1) : 0);
     const int tc = tid < nc ? tid : nc - 1;
     cent_k = a.kcent[tc] * a.kscale[NG > 1 && tc >= (1 << M0) ? 1 : 0];
-    if constexpr (WV) cent_v = a.vcent[tc];
+    if constexpr (WV != 0) cent_v = a.vcent[tc];
   }
   // ---- this lane's head and its query operands (B operand: channels x heads) ----
   // (loaded before the first tile: loads complete in issue order, so using
@@ -529,7 +531,7 @@ __global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel
     };
     tab_build<G::KE[0], 4>(s_tab, tid, hi_val(s_cent[0], M0));
     if constexpr (NG > 1) tab_build<G::KE[1], 4>(s_tab + KT1, tid, hi_val(s_cent[0] + (1 << M0), M1));
-    if constexpr (WV) {
+    if constexpr (WV != 0) {
       tab_build<G::KE[0], 4>(s_tab + VT0, tid, hi_val(s_cent[1], M0));
       if constexpr (NG > 1) tab_build<G::KE[1], 4>(s_tab + VT1, tid, hi_val(s_cent[1] + (1 << M0), M1));
     }
@@ -565,7 +567,7 @@ __global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel
 #pragma unroll
       for (int e = 0; e < NG; ++e) {
         s_nrm[wv][0][lane * NG + e] = nok ? r.kn[e] * kn_mul[e] : 0.f;
-        if constexpr (WV) s_nrm[wv][1][lane * NG + e] = nok ? r.vn[e] : 0.f;
+        if constexpr (WV != 0) s_nrm[wv][1][lane * NG + e] = nok ? r.vn[e] : 0.f;
       }
     }
     // LDS operations of one wave execute in order; the wave barrier only keeps
@@ -661,7 +663,7 @@ __global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel
 #pragma unroll
       for (int j = 0; j < 8; ++j) l2[j] = 8 * lg + j < nvt ? l2[j] : -INFINITY;
     }
-    if constexpr (WV) {
+    if constexpr (WV != 0) {
       // ---------------- online softmax ----------------
       float mx = l2[0];
 #pragma unroll
@@ -747,12 +749,14 @@ __global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel
 #pragma unroll
         for (int u = 0; u < RUN; ++u) {
           const u32x4 av = codes8<M>(cw, 8 * M * u, vt, off4);
-          const u32x4 az = signs8(&r.vs[G::VNS * g], 8 * u, stab, off8);
           acc_r[g * MTPG + u] = mfma16(av, pr[g], acc_r[g * MTPG + u]);
-          if constexpr (PK)
-            acc_r[g * MTPG + u] = mfma16(az, pz[g], acc_r[g * MTPG + u]);
-          else
-            acc_s[g * MTPG + u] = mfma16(az, pz[g], acc_s[g * MTPG + u]);
+          if constexpr (WV == 1) {  // (MSE-only V: no sign product; the sketch sums stay 0)
+            const u32x4 az = signs8(&r.vs[G::VNS * g], 8 * u, stab, off8);
+            if constexpr (PK)
+              acc_r[g * MTPG + u] = mfma16(az, pz[g], acc_r[g * MTPG + u]);
+            else
+              acc_s[g * MTPG + u] = mfma16(az, pz[g], acc_s[g * MTPG + u]);
+          }
         }
       };
       v_group(std::integral_constant<int, 0>{});
@@ -792,7 +796,7 @@ __global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel
     }
   }
 
-  if constexpr (WV) {
+  if constexpr (WV != 0) {
     // ---- merge the four waves into one partial (the table space is reused) ----
     // Region r (r = 0, 1) holds, head-major, the sum of the accumulators of
     // waves r and r + 2 scaled to the workgroup maximum: waves 0 and 1 store,
@@ -1051,12 +1055,12 @@ size_t workspace_for(const tq_decode_shape* s, int d, bool with_v, int n_split) 
 // heads with V, else 16
 inline int heads_per_block(int group, bool with_v) { return with_v && group <= 4 ? 4 : 16; }
 
-template <int D, int NG, int M0, int M1, bool WV>
+template <int D, int NG, int M0, int M1, int WV>
 hipError_t launch_decode(const DArgs& a, int n_hblk, hipStream_t st) {
   (void)hipGetLastError();  // a launch error is reported below, not an older one
   const dim3 grid((unsigned)a.n_split, (unsigned)(a.batch * a.hkv), (unsigned)n_hblk);
-  if constexpr (WV) {
-    if (heads_per_block(a.group, WV) == 4)
+  if constexpr (WV != 0) {
+    if (heads_per_block(a.group, WV != 0) == 4)
       hipLaunchKernelGGL((decode_kernel<D, NG, M0, M1, WV, 4>), grid, dim3(256), 0, st, a);
     else
       hipLaunchKernelGGL((decode_kernel<D, NG, M0, M1, WV, 16>), grid, dim3(256), 0, st, a);
@@ -1066,7 +1070,7 @@ hipError_t launch_decode(const DArgs& a, int n_hblk, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int D, int NG, int M0, bool WV>
+template <int D, int NG, int M0, int WV>
 hipError_t dispatch_m1(const DArgs& a, int m1, int n_hblk, hipStream_t st) {
   switch (m1) {
     case 1: return launch_decode<D, NG, M0, 1, WV>(a, n_hblk, st);
@@ -1076,7 +1080,7 @@ hipError_t dispatch_m1(const DArgs& a, int m1, int n_hblk, hipStream_t st) {
   }
 }
 
-template <int D, int NG, bool WV>
+template <int D, int NG, int WV>
 hipError_t dispatch_m0(const DArgs& a, int m0, int m1, int n_hblk, hipStream_t st) {
   if constexpr (NG == 1) {
     switch (m0) {
@@ -1115,7 +1119,7 @@ struct Plan {
   DArgs a;
   tqp::PrepArgs prep;
   int n_hblk, prep_grid_y, n_heads, n_groups, m0, m1, group_dim0, T, hq_orig;
-  bool with_v;
+  bool with_v, v_mse;  // V records present; V records without sign bits
   const float* vrot;
   const float* vsketch;
   float* out;
@@ -1137,13 +1141,16 @@ tq_status plan_decode(const tq_quantizer* kq, const tq_quantizer* vq, const tq_d
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_ERR_INVALID;
   if (!q || reinterpret_cast<uintptr_t>(q) % 16 != 0) return TQ_ERR_INVALID;
   if (!k_cache || !k_cache->codes || !k_cache->signs || !k_cache->norms) return TQ_ERR_INVALID;
+  // (keys need the sign bits: the logits are the unbiased two-stage estimate)
+  if (kq->layout.mse_only) return TQ_ERR_UNSUPPORTED;
   // (paged: at least one physical block of every KV head)
   const int64_t rows_needed =
       paging ? (int64_t)shape->n_kv_heads * kTile : (int64_t)shape->batch * shape->n_kv_heads * shape->cache_capacity;
   if (k_cache->n_rows < rows_needed) return TQ_ERR_INVALID;
   const bool with_v = vq != nullptr;
   if (with_v) {
-    if (!v_cache || !v_cache->codes || !v_cache->signs || !v_cache->norms) return TQ_ERR_INVALID;
+    if (!v_cache || !v_cache->codes || (!v_cache->signs && !vq->layout.mse_only) || !v_cache->norms)
+      return TQ_ERR_INVALID;
     if (v_cache->n_rows < rows_needed || !out) return TQ_ERR_INVALID;
     if (!same_layout(kq->layout, vq->layout)) return TQ_ERR_UNSUPPORTED;
   } else {
@@ -1180,6 +1187,7 @@ tq_status plan_decode(const tq_quantizer* kq, const tq_quantizer* vq, const tq_d
   pl->m1 = l.n_groups == 2 ? l.mse_bits[1] : 0;
   pl->group_dim0 = l.n_groups == 2 ? l.group_dim[0] : D;
   pl->with_v = with_v;
+  pl->v_mse = with_v && vq->layout.mse_only;
   pl->out = out;
   pl->prep_grid_y = (n_heads + tqp::kPrepHeads - 1) / tqp::kPrepHeads;
   tqp::PrepArgs& pp = pl->prep;
@@ -1252,11 +1260,13 @@ tq_status run_phases(const Plan& pl, unsigned phases, hipStream_t st) {
   if (phases & TQ_PHASE_SPLIT) {
     hipError_t e;
     if (pl.n_groups == 1)
-      e = pl.with_v ? dispatch_m0<D, 1, true>(pl.a, pl.m0, 0, pl.n_hblk, st)
-                    : dispatch_m0<D, 1, false>(pl.a, pl.m0, 0, pl.n_hblk, st);
+      e = !pl.with_v  ? dispatch_m0<D, 1, 0>(pl.a, pl.m0, 0, pl.n_hblk, st)
+          : pl.v_mse ? dispatch_m0<D, 1, 2>(pl.a, pl.m0, 0, pl.n_hblk, st)
+                     : dispatch_m0<D, 1, 1>(pl.a, pl.m0, 0, pl.n_hblk, st);
     else
-      e = pl.with_v ? dispatch_m0<D, 2, true>(pl.a, pl.m0, pl.m1, pl.n_hblk, st)
-                    : dispatch_m0<D, 2, false>(pl.a, pl.m0, pl.m1, pl.n_hblk, st);
+      e = !pl.with_v  ? dispatch_m0<D, 2, 0>(pl.a, pl.m0, pl.m1, pl.n_hblk, st)
+          : pl.v_mse ? dispatch_m0<D, 2, 2>(pl.a, pl.m0, pl.m1, pl.n_hblk, st)
+                     : dispatch_m0<D, 2, 1>(pl.a, pl.m0, pl.m1, pl.n_hblk, st);
     if (e != hipSuccess) return TQ_ERR_DEVICE;
   }
   if (pl.with_v && (phases & TQ_PHASE_COMBINE)) {

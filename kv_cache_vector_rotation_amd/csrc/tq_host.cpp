@@ -93,6 +93,7 @@ namespace tq {
 
 bool layout_valid(const tq_layout* l) {
   if (!l) return false;
+  if (l->mse_only != 0 && l->mse_only != 1) return false;
   if (l->d < 3 || l->d > 256) return false;
   if (l->n_groups != 1 && l->n_groups != 2) return false;
   int sum = 0;
@@ -121,12 +122,12 @@ GroupGeom geometry(const tq_layout* l) {
     g.boundary_off[i] = bo;
     ch += d;
     cw += (m * d + 31) / 32;
-    sw += (d + 31) / 32;
+    sw += l->mse_only ? 0 : (d + 31) / 32;
     bcw += m * d;  // 32 rows * m * d bits / 32
-    bsw += d;
+    bsw += l->mse_only ? 0 : d;
     co += 1 << m;
     bo += (1 << m) - 1;
-    bits += (m + 1) * d + 64;
+    bits += (l->mse_only ? m : m + 1) * d + 64;
   }
   g.info.code_words = cw;
   g.info.sign_words = sw;

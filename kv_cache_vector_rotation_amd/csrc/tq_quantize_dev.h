@@ -59,6 +59,7 @@ struct QArgs {
   int boff[2];
   int code_words;
   int sign_words;
+  int mse_only;  // stage one alone: no sketch, no sign bits (sign_words = 0)
   int blk_code_words;
   int blk_sign_words;
   int fmt;
@@ -628,31 +629,33 @@ __device__ __forceinline__ void quantize_tiles(const QArgs& a, int64_t first_til
     // is fully written, with zeros past d)
     __syncthreads();
 
-    // ---- s = (S Pi^T) r (fp32 MFMA); sign bit = [s >= 0] ----
-    f32x4 sacc[4];
-    if constexpr (SKR_LDS) {
-      if (n_mt == 1)
-        mfma_tiles_lds<1, KPG, XS>(xr, skr_lds + w * (KPG / 4) * 64 + lane, ln, lg, sacc);
-      else
-        mfma_tiles_lds<4, KPG, XS>(xr, skr_lds + w * (KPG / 4) * 64 + lane, ln, lg, sacc);
-    } else {
-      if (n_mt == 1)
-        mfma_tiles<1, KPG, XS>(xr, bskr, ln, lg, sacc);
-      else
-        mfma_tiles<4, KPG, XS>(xr, bskr, ln, lg, sacc);
-    }
+    // ---- s = (S Pi^T) r (fp32 MFMA); sign bit = [s >= 0] (not for MSE-only records) ----
+    if (!a.mse_only) {
+      f32x4 sacc[4];
+      if constexpr (SKR_LDS) {
+        if (n_mt == 1)
+          mfma_tiles_lds<1, KPG, XS>(xr, skr_lds + w * (KPG / 4) * 64 + lane, ln, lg, sacc);
+        else
+          mfma_tiles_lds<4, KPG, XS>(xr, skr_lds + w * (KPG / 4) * 64 + lane, ln, lg, sacc);
+      } else {
+        if (n_mt == 1)
+          mfma_tiles<1, KPG, XS>(xr, bskr, ln, lg, sacc);
+        else
+          mfma_tiles<4, KPG, XS>(xr, bskr, ln, lg, sacc);
+      }
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      if (mt >= n_mt) break;
+      for (int mt = 0; mt < 4; ++mt) {
+        if (mt >= n_mt) break;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int v = mt * 16 + lg * 4 + i;
-        const bool bit = sacc[mt][i] >= 0.f && ocoord < d;
-        sign_b[v * DP + ocoord] = bit ? 1 : 0;
-        // the wave's 16 channels for vector 16 mt + 4 q + i are ballot bits [16 q, 16 q + 16)
-        const uint64_t bal = __builtin_amdgcn_ballot_w64(bit);
-        if (tok && lane < 4)
-          pk16[(mt * 16 + lane * 4 + i) * 2 * PKW + pk_sign_h] = (uint16_t)(bal >> (16 * lane));
+        for (int i = 0; i < 4; ++i) {
+          const int v = mt * 16 + lg * 4 + i;
+          const bool bit = sacc[mt][i] >= 0.f && ocoord < d;
+          sign_b[v * DP + ocoord] = bit ? 1 : 0;
+          // the wave's 16 channels for vector 16 mt + 4 q + i are ballot bits [16 q, 16 q + 16)
+          const uint64_t bal = __builtin_amdgcn_ballot_w64(bit);
+          if (tok && lane < 4)
+            pk16[(mt * 16 + lane * 4 + i) * 2 * PKW + pk_sign_h] = (uint16_t)(bal >> (16 * lane));
+        }
       }
     }
     // full aligned 32-row blocks of this tile (block records only)
@@ -775,6 +778,7 @@ __device__ __forceinline__ void quantize_tiles(const QArgs& a, int64_t first_til
           atomicAnd(base + wi + 1, ~((1u << spill) - 1u));
           atomicOr(base + wi + 1, code >> (32 - bi));
         }
+        if (a.mse_only) continue;
         const int spos = 8 * (o * dg + j) + s;
         uint32_t* sbase = a.signs + blk * a.blk_sign_words + a.bswoff[g];
         const uint32_t sbit = sign_b[v * DP + ch];
@@ -1029,8 +1033,8 @@ __device__ __forceinline__ void quantize_small(const QArgs& a, int64_t vec, unsi
   }
   __syncthreads();
 
-  // ---- s_o = sketch_rot[o] . r; sign bit = [s >= 0] ----
-  {
+  // ---- s_o = sketch_rot[o] . r; sign bit = [s >= 0] (not for MSE-only records) ----
+  if (!a.mse_only) {
     float c4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -1087,7 +1091,8 @@ inline tq_status make_qargs(const tq_quantizer* qz, tq_format fmt, const void* x
   if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return TQ_ERR_INVALID;
   const tq_layout& l = qz->layout;
   if (n_vec < 0 || x_row_stride < l.d) return TQ_ERR_INVALID;
-  if (!cache->codes || !cache->signs || !cache->norms || cache->n_rows < 0) return TQ_ERR_INVALID;
+  // (MSE-only records have no sign words: their sign pointer is not read and may be null)
+  if (!cache->codes || (!cache->signs && !l.mse_only) || !cache->norms || cache->n_rows < 0) return TQ_ERR_INVALID;
   if (fmt == TQ_BLOCK32 && cache->n_rows % 32 != 0) return TQ_ERR_INVALID;
   if (!rows->dst_rows) {
     if (rows->seg_len < 1 || rows->seg_stride < 0 || rows->seg_offset < 0) return TQ_ERR_INVALID;
@@ -1144,6 +1149,7 @@ inline tq_status make_qargs(const tq_quantizer* qz, tq_format fmt, const void* x
   if (l.n_groups == 1) a.choff[1] = 1 << 30;  // never reached
   a.code_words = geo.info.code_words;
   a.sign_words = geo.info.sign_words;
+  a.mse_only = l.mse_only;
   a.blk_code_words = geo.info.block_code_words;
   a.blk_sign_words = geo.info.block_sign_words;
   a.fmt = fmt;

@@ -395,7 +395,7 @@ extern "C" tq_status tq_search(const tq_quantizer* qz, const tq_cache* db, int64
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_ERR_INVALID;
   if (!db->codes || !db->signs || !db->norms || db->n_rows < n_db) return TQ_ERR_INVALID;
   const tq_layout& l = qz->layout;
-  if (l.n_groups != 1 || l.d % 8 != 0) return TQ_ERR_UNSUPPORTED;
+  if (l.n_groups != 1 || l.d % 8 != 0 || l.mse_only) return TQ_ERR_UNSUPPORTED;
   const void* ptrs[] = {q, workspace, db->norms};
   for (const void* p : ptrs)
     if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return TQ_ERR_INVALID;

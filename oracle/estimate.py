@@ -16,7 +16,10 @@ Readings used here (each listed in the design doc):
 * queries are not quantized: logit = scale * <q, x~>;
 * decode attends over every cached token (no mask); query head h reads KV
   head floor(h / G) with G = n_q_heads / n_kv_heads;
-* V uses the same dequantization as K with its own quantizer.
+* V uses the same dequantization as K with its own quantizer;
+* an MSE-only quantizer (stage one alone) dequantizes to n_g Pi_g^T c[idx]:
+  no sign term. That estimate is biased: over random rotations its mean is
+  (1 - D) x, with D the codebook's mean squared error on unit vectors.
 The norms used are the stored float32 values.
 """
 from __future__ import annotations
@@ -39,6 +42,9 @@ def dequantize(idx, bits, norm, gamma, qz: Quantizer) -> np.ndarray:
         n = np.asarray(norm[g], dtype=np.float64)[:, None]
         gm = np.asarray(gamma[g], dtype=np.float64)[:, None]
         mse_part = n * (c[idx[g]] @ pi)               # n Pi^T c[idx]
+        if qz.mse_only:
+            xp[:, off:off + dg] = mse_part
+            continue
         qjl_part = alpha * gm * (z @ sm)              # alpha gamma S^T z
         xp[:, off:off + dg] = mse_part + qjl_part
     out = np.empty_like(xp)

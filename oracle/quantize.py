@@ -23,7 +23,11 @@ Readings used here (each listed in the design doc):
   sign bits 1;
 * fractional widths (3.5, 2.5 bits) are two independent instances on a
   split of the channels: channels are reordered by ``perm`` and cut into
-  consecutive groups, each with its own rotation, sketch and codebook.
+  consecutive groups, each with its own rotation, sketch and codebook;
+* an MSE-only instance (the first of the two stages alone: [ZB] paragraph
+  2 and [WD] "1. PolarQuant") keeps the same indices and norms but no sign
+  bits: m_g bits per channel. Quantization itself is unchanged (the sign
+  bits are still computed here, for diagnostics, and are simply not stored).
 """
 from __future__ import annotations
 
@@ -46,9 +50,10 @@ class Quantizer:
     rotations: List[np.ndarray]   # float64 d_g x d_g
     sketches: List[np.ndarray]    # float64 d_g x d_g
     codebooks: List[Codebook]
+    mse_only: bool = False        # stage one alone: records carry no sign bits
 
     @staticmethod
-    def from_spec(spec) -> "Quantizer":
+    def from_spec(spec, mse_only: bool = False) -> "Quantizer":
         """Build from a ``synth.QuantizerSpec`` (random inputs) plus this
         oracle's own Lloyd-Max codebooks."""
         dims = [g.dim for g in spec.groups]
@@ -56,7 +61,7 @@ class Quantizer:
         return Quantizer(d=spec.d, perm=np.asarray(spec.perm, dtype=np.int64), dims=dims,
                          rotations=[np.asarray(r, np.float64) for r in spec.rotations],
                          sketches=[np.asarray(s, np.float64) for s in spec.sketches],
-                         codebooks=cbs)
+                         codebooks=cbs, mse_only=bool(mse_only))
 
     @property
     def offsets(self) -> List[int]:

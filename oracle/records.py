@@ -35,18 +35,21 @@ def _words(n_bits: int) -> int:
     return (n_bits + 31) // 32
 
 
-def record_words(dims: Sequence[int], mse_bits: Sequence[int]):
+def record_words(dims: Sequence[int], mse_bits: Sequence[int], mse_only: bool = False):
     """(code words per token-major row, sign words per row, norm floats per
-    row, code words per 32-token block, sign words per 32-token block)."""
+    row, code words per 32-token block, sign words per 32-token block).
+    MSE-only records have no sign words."""
     cw = sum(_words(m * d) for d, m in zip(dims, mse_bits))
-    sw = sum(_words(d) for d in dims)
-    return cw, sw, 2 * len(dims), sum(m * d for d, m in zip(dims, mse_bits)), sum(dims)
+    sw = 0 if mse_only else sum(_words(d) for d in dims)
+    bsw = 0 if mse_only else sum(dims)
+    return cw, sw, 2 * len(dims), sum(m * d for d, m in zip(dims, mse_bits)), bsw
 
 
-def record_bytes(dims: Sequence[int], mse_bits: Sequence[int], include_norms: bool = True) -> float:
-    """Algorithmic bytes per token: index bits + sign bits (+ two float32
-    norms per group)."""
-    bits = sum((m + 1) * d for d, m in zip(dims, mse_bits))
+def record_bytes(dims: Sequence[int], mse_bits: Sequence[int], include_norms: bool = True,
+                 mse_only: bool = False) -> float:
+    """Algorithmic bytes per token: index bits + sign bits (none when
+    MSE-only) (+ two float32 norms per group)."""
+    bits = sum((m if mse_only else m + 1) * d for d, m in zip(dims, mse_bits))
     return bits / 8.0 + (8.0 * len(dims) if include_norms else 0.0)
 
 
@@ -56,9 +59,10 @@ def _bits_to_words(bitarray: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(by).view("<u4")
 
 
-def pack_token_major(idx, bits, norm, gamma, dims, mse_bits):
+def pack_token_major(idx, bits, norm, gamma, dims, mse_bits, mse_only=False):
     """Per-token records from per-group codes/bits/norms (lists over groups).
-    Returns (codes [n, Wc] uint32, signs [n, Ws] uint32, norms [n, 2G] float32)."""
+    Returns (codes [n, Wc] uint32, signs [n, Ws] uint32, norms [n, 2G] float32);
+    MSE-only records have Ws = 0."""
     n = idx[0].shape[0]
     code_parts, sign_parts, norm_cols = [], [], []
     for g, (d, m) in enumerate(zip(dims, mse_bits)):
@@ -66,18 +70,23 @@ def pack_token_major(idx, bits, norm, gamma, dims, mse_bits):
         for p in range(m):                                   # bit p of code j -> m j + p
             stream[:, m * np.arange(d) + p] = (idx[g] >> p) & 1
         code_parts.append(_bits_to_words(stream))
-        sstream = np.zeros((n, _words(d) * 32), dtype=np.uint8)
-        sstream[:, :d] = bits[g]
-        sign_parts.append(_bits_to_words(sstream))
+        if not mse_only:
+            sstream = np.zeros((n, _words(d) * 32), dtype=np.uint8)
+            sstream[:, :d] = bits[g]
+            sign_parts.append(_bits_to_words(sstream))
         norm_cols += [np.asarray(norm[g], np.float32), np.asarray(gamma[g], np.float32)]
-    return (np.concatenate(code_parts, axis=1), np.concatenate(sign_parts, axis=1),
+    return (np.concatenate(code_parts, axis=1), _concat_signs(sign_parts, code_parts[0].shape[0]),
             np.stack(norm_cols, axis=1))
 
 
-def pack_block32(idx, bits, norm, gamma, dims, mse_bits):
+def _concat_signs(parts, n):
+    return np.concatenate(parts, axis=1) if parts else np.zeros((n, 0), np.uint32)
+
+
+def pack_block32(idx, bits, norm, gamma, dims, mse_bits, mse_only=False):
     """Block records for n rows (n a multiple of 32).
     Returns (codes [n/32, sum m_g d_g] uint32, signs [n/32, sum d_g] uint32,
-    norms [n, 2G] float32)."""
+    norms [n, 2G] float32); MSE-only records have no sign words."""
     n = idx[0].shape[0]
     if n % 32:
         raise ValueError("block records need a multiple of 32 rows")
@@ -96,7 +105,8 @@ def pack_block32(idx, bits, norm, gamma, dims, mse_bits):
                 region[:, unit + p] = (codes[:, :, j] >> p) & 1
             sregion[:, 8 * (o * d + j) + s] = sb[:, :, j]
         code_parts.append(_bits_to_words(region))
-        sign_parts.append(_bits_to_words(sregion))
+        if not mse_only:
+            sign_parts.append(_bits_to_words(sregion))
         norm_cols += [np.asarray(norm[g], np.float32), np.asarray(gamma[g], np.float32)]
-    return (np.concatenate(code_parts, axis=1), np.concatenate(sign_parts, axis=1),
+    return (np.concatenate(code_parts, axis=1), _concat_signs(sign_parts, code_parts[0].shape[0]),
             np.stack(norm_cols, axis=1))

@@ -23,20 +23,22 @@ BAND = 1e-6
 FRACTION = 1e-5
 
 
-def quantizers(spec):
+def quantizers(spec, mse_only=False):
     """(oracle.Quantizer, device Quantizer) for one synth.QuantizerSpec."""
     import kv_cache_vector_rotation_amd as tq
-    oq = oracle.Quantizer.from_spec(spec)
+    oq = oracle.Quantizer.from_spec(spec, mse_only=mse_only)
     dq = tq.Quantizer.from_parts(spec.rotations, spec.sketches,
-                                 [g.mse_bits for g in spec.groups], perm=spec.perm)
+                                 [g.mse_bits for g in spec.groups], perm=spec.perm, mse_only=mse_only)
     return oq, dq
 
 
 def compare_records(x, oq, qv, got, check_fraction=True):
     """got = (codes, signs, n, gamma) lists per group (from recfmt), rows aligned
     with x / qv. Returns a dict of counts; raises AssertionError on a
-    violation."""
+    violation. MSE-only records (sign bits None) are checked on codes and
+    norms alone."""
     gc, gs, gn, gg = got
+    mse_only = gs[0] is None
     n_vec = x.shape[0]
     total = n_vec * oq.d
     flips_code = flips_sign = 0
@@ -51,9 +53,10 @@ def compare_records(x, oq, qv, got, check_fraction=True):
         assert np.all(qv.margin[g][code_diff] < BAND), "code differs away from a boundary"
         flips_code += int(code_diff.sum())
         ok_rows = np.setdiff1d(np.arange(n_vec), bad_rows)
-        sdiff = gs[g][ok_rows] != bits[ok_rows]
-        assert np.all(qv.sign_margin[g][ok_rows][sdiff] < BAND), "sign differs away from zero"
-        flips_sign += int(sdiff.sum())
+        if not mse_only:
+            sdiff = gs[g][ok_rows] != bits[ok_rows]
+            assert np.all(qv.sign_margin[g][ok_rows][sdiff] < BAND), "sign differs away from zero"
+            flips_sign += int(sdiff.sum())
         gam_ref = qv.gamma[g][ok_rows].astype(np.float64)
         assert np.all(np.abs(gg[g][ok_rows] - gam_ref) <= 2e-6 * np.maximum(norm_ref[ok_rows], 1e-30)), \
             "residual norm mismatch"
@@ -63,7 +66,7 @@ def compare_records(x, oq, qv, got, check_fraction=True):
             for vidx, vbits, vgam, vmargin in variants:
                 if not np.array_equal(vidx, gc[g][r]):
                     continue
-                sd = vbits != gs[g][r]
+                sd = np.zeros_like(vbits) if mse_only else vbits != gs[g][r]
                 if np.all(vmargin[sd] < BAND) and abs(float(gg[g][r]) - float(vgam)) <= 2e-6 * max(norm_ref[r], 1e-30):
                     match = True
                     flips_sign += int(sd.sum())
@@ -74,15 +77,15 @@ def compare_records(x, oq, qv, got, check_fraction=True):
     return {"code_flips": flips_code, "sign_flips": flips_sign, "coords": total}
 
 
-def oracle_cache_arrays(qv, dims, bits, fmt, n_rows, rows):
+def oracle_cache_arrays(qv, dims, bits, fmt, n_rows, rows, mse_only=False):
     """Pack oracle records and place them at the given rows of an n_rows cache.
     Returns numpy (codes, signs, norms) flat arrays matching the device layout."""
     import kv_cache_vector_rotation_amd as tq
-    info = oracle.record_words(dims, bits)
+    info = oracle.record_words(dims, bits, mse_only)
     cw, sw, nf, bcw, bsw = info
     norms = np.zeros((n_rows, nf), np.float32)
     if fmt == tq.TQ_TOKEN_MAJOR:
-        c, s, nm = oracle.pack_token_major(qv.idx, qv.bits, qv.norm, qv.gamma, dims, bits)
+        c, s, nm = oracle.pack_token_major(qv.idx, qv.bits, qv.norm, qv.gamma, dims, bits, mse_only)
         codes = np.zeros((n_rows, cw), np.uint32)
         signs = np.zeros((n_rows, sw), np.uint32)
         codes[rows], signs[rows], norms[rows] = c, s, nm
@@ -91,7 +94,7 @@ def oracle_cache_arrays(qv, dims, bits, fmt, n_rows, rows):
     rows = np.asarray(rows)
     assert rows.size % 32 == 0 and np.all(rows.reshape(-1, 32)[:, 0] % 32 == 0)
     assert np.all(np.diff(rows.reshape(-1, 32), axis=1) == 1)
-    c, s, nm = oracle.pack_block32(qv.idx, qv.bits, qv.norm, qv.gamma, dims, bits)
+    c, s, nm = oracle.pack_block32(qv.idx, qv.bits, qv.norm, qv.gamma, dims, bits, mse_only)
     codes = np.zeros((n_rows // 32, bcw), np.uint32)
     signs = np.zeros((n_rows // 32, bsw), np.uint32)
     blocks = rows.reshape(-1, 32)[:, 0] // 32
@@ -118,15 +121,16 @@ def read_cache(cache, dq):
     codes = cache.codes.cpu().numpy().view(np.uint32)
     signs = cache.signs.cpu().numpy().view(np.uint32)
     norms = cache.norms.cpu().numpy().reshape(cache.n_rows, info.norm_floats)
+    mse = bool(dq.layout.mse_only)
     if cache.fmt == tq.TQ_TOKEN_MAJOR:
         return recfmt.unpack_token_major(codes.reshape(cache.n_rows, -1), signs.reshape(cache.n_rows, -1),
-                                         norms, dq.dims, dq.mse_bits)
+                                         norms, dq.dims, dq.mse_bits, mse)
     nb = cache.n_rows // 32
-    return recfmt.unpack_block32(codes.reshape(nb, -1), signs.reshape(nb, -1), norms, dq.dims, dq.mse_bits)
+    return recfmt.unpack_block32(codes.reshape(nb, -1), signs.reshape(nb, -1), norms, dq.dims, dq.mse_bits, mse)
 
 
 def select_rows(got, rows):
-    return tuple([a[rows] for a in part] for part in got)
+    return tuple([None if a is None else a[rows] for a in part] for part in got)
 
 
 def normwise_close(got, ref, tol=2e-3):

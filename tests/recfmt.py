@@ -11,9 +11,10 @@ def _bits(words: np.ndarray) -> np.ndarray:
     return np.unpackbits(w.view(np.uint8).reshape(w.shape[0], -1), axis=1, bitorder="little")
 
 
-def unpack_token_major(codes, signs, norms, dims, bits):
+def unpack_token_major(codes, signs, norms, dims, bits, mse_only=False):
     """codes [n, Wc], signs [n, Ws] uint32, norms [n, 2G] -> per group lists of
-    codes [n, d_g] int64, sign bits [n, d_g] bool, n_g [n], gamma_g [n]."""
+    codes [n, d_g] int64, sign bits [n, d_g] bool, n_g [n], gamma_g [n].
+    MSE-only records have no sign words: their sign bits come back None."""
     cb, sb = _bits(codes), _bits(signs)
     out_c, out_s, out_n, out_g = [], [], [], []
     cw = sw = 0
@@ -23,7 +24,7 @@ def unpack_token_major(codes, signs, norms, dims, bits):
         for p in range(m):
             val |= cb[:, 32 * cw + m * j + p].astype(np.int64) << p
         out_c.append(val)
-        out_s.append(sb[:, 32 * sw + j].astype(bool))
+        out_s.append(None if mse_only else sb[:, 32 * sw + j].astype(bool))
         out_n.append(np.asarray(norms)[:, 2 * g])
         out_g.append(np.asarray(norms)[:, 2 * g + 1])
         cw += (m * d + 31) // 32
@@ -31,7 +32,7 @@ def unpack_token_major(codes, signs, norms, dims, bits):
     return out_c, out_s, out_n, out_g
 
 
-def unpack_block32(codes, signs, norms, dims, bits):
+def unpack_block32(codes, signs, norms, dims, bits, mse_only=False):
     """codes [n_blocks, BCW], signs [n_blocks, BSW] uint32, norms [32 n_blocks, 2G]
     -> per group codes [32 n_blocks, d_g], bits, n_g, gamma_g (rows in order)."""
     nb = codes.shape[0]
@@ -48,7 +49,7 @@ def unpack_block32(codes, signs, norms, dims, bits):
             val |= cb[:, 32 * cw + pos + p].astype(np.int64) << p
         spos = 8 * (o[:, None] * d + j[None, :]) + s[:, None]
         out_c.append(val.reshape(nb * 32, d))
-        out_s.append(sb[:, 32 * sw + spos].astype(bool).reshape(nb * 32, d))
+        out_s.append(None if mse_only else sb[:, 32 * sw + spos].astype(bool).reshape(nb * 32, d))
         out_n.append(np.asarray(norms)[:, 2 * g])
         out_g.append(np.asarray(norms)[:, 2 * g + 1])
         cw += m * d

@@ -301,3 +301,47 @@ def test_query_token_chunks_validation(tq):
         tq.TQ_ERR_INVALID
     nb = C.c_size_t()
     assert lib.tq_attn_decode_bf16_workspace_bytes(C.byref(sT), 128, C.byref(nb)) == tq.TQ_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("dims,bits", [([128], [3]), ([64, 64], [3, 2]), ([200], [4])])
+def test_mse_only_record_layout(tq, dims, bits):
+    # stage-one records: no sign words, m_g bits per channel plus the norms
+    info = tq.tq_record_layout(tq.make_layout(dims, bits, mse_only=True))
+    assert (info.code_words, info.sign_words, info.norm_floats, info.block_code_words,
+            info.block_sign_words) == oracle.record_words(dims, bits, mse_only=True)
+    assert info.record_bits == 8 * oracle.record_bytes(dims, bits, mse_only=True)
+    l = tq.make_layout(dims, bits)
+    l.mse_only = 2
+    with pytest.raises(tq.TQError):
+        tq.tq_record_layout(l)
+
+
+def test_mse_only_decode_and_search_validation(tq):
+    # MSE-only V is decoded (its sign pointer may be NULL); MSE-only K and an
+    # MSE-only search database are refused
+    lib = tq.lib()
+    kq = _fake_quantizer(tq)
+    vq_m = _fake_quantizer(tq)
+    vq_m.layout = tq.make_layout((128,), (3,), mse_only=True)
+    kc = _fake_cache(tq, 2 * 8 * 1024)
+    vc = _fake_cache(tq, 2 * 8 * 1024)
+    vc.signs = None
+    shape = tq.decode_shape(2, 32, 8, 1000, 1024, 0.088)
+    need = C.c_size_t()
+    assert lib.tq_attn_decode_workspace_bytes(C.byref(kq), C.byref(vq_m), C.byref(shape), C.byref(need)) == 0
+
+    def call(kq=kq, vq=vq_m, vc=vc, wsb=need.value):
+        # a workspace one byte short: validation passes up to the size check
+        return lib.tq_attn_decode(C.byref(kq), C.byref(vq), C.byref(shape), FAKE, 1, C.byref(kc), C.byref(vc),
+                                  None, FAKE, FAKE, wsb, None)
+
+    assert call(wsb=need.value - 1) == tq.TQ_ERR_WORKSPACE        # V without signs accepted
+    full_v = _fake_quantizer(tq)
+    assert call(vq=full_v, wsb=need.value - 1) == tq.TQ_ERR_INVALID   # its signs are required
+    assert call(kq=vq_m, vq=full_v) == tq.TQ_ERR_UNSUPPORTED         # MSE-only K
+    q = _fake_quantizer(tq, dims=(200,), bits=(3,))
+    q.layout = tq.make_layout((200,), (3,), mse_only=True)
+    db = _fake_cache(tq, 1000)
+    assert lib.tq_search_workspace_bytes(C.byref(q), 1000, 50, 10, C.byref(need)) == 0
+    assert lib.tq_search(C.byref(q), C.byref(db), 1000, FAKE, 0, 50, 10, FAKE, FAKE, FAKE, need.value,
+                         None) == tq.TQ_ERR_UNSUPPORTED

@@ -27,12 +27,13 @@ def tq():
     return m
 
 
-def _oracle_side(wl, n_ctx, cap, with_v=True):
+def _oracle_side(wl, n_ctx, cap, with_v=True, v_mse=False):
     """Quantize the K (and V) streams with the oracle, return oracle quantizers,
-    specs, per-(b,h) dequantized caches and packed arrays."""
+    specs, per-(b,h) dequantized caches and packed arrays (v_mse: MSE-only V
+    records)."""
     ks, vs = synth.draw_quantizer(wl, "K"), synth.draw_quantizer(wl, "V")
     okq = oracle.Quantizer.from_spec(ks)
-    ovq = oracle.Quantizer.from_spec(vs)
+    ovq = oracle.Quantizer.from_spec(vs, mse_only=v_mse)
     B, H = wl.batch, wl.n_kv_heads
     dims = [g.dim for g in ks.groups]
     bits = [g.mse_bits for g in ks.groups]
@@ -41,7 +42,7 @@ def _oracle_side(wl, n_ctx, cap, with_v=True):
     k_t = oracle.dequantize(qk.idx, qk.bits, qk.norm, qk.gamma, okq).reshape(B, H, n_ctx, wl.d)
     rows = np.concatenate([(b * H + h) * cap + np.arange(n_ctx) for b in range(B) for h in range(H)])
     karr = gc.oracle_cache_arrays(qk, dims, bits, 0, B * H * cap, rows)
-    out = dict(ks=ks, vs=vs, k_t=k_t, karr=karr, dims=dims, bits=bits)
+    out = dict(ks=ks, vs=vs, k_t=k_t, karr=karr, dims=dims, bits=bits, v_mse=v_mse)
     if with_v:
         # block records need whole blocks: quantize up to the block boundary
         nb = ((n_ctx + 31) // 32) * 32
@@ -49,7 +50,7 @@ def _oracle_side(wl, n_ctx, cap, with_v=True):
         qvv = oracle.quantize(vx, ovq)
         v_full = oracle.dequantize(qvv.idx, qvv.bits, qvv.norm, qvv.gamma, ovq).reshape(B, H, nb, wl.d)
         vrows = np.concatenate([(b * H + h) * cap + np.arange(nb) for b in range(B) for h in range(H)])
-        out["varr"] = gc.oracle_cache_arrays(qvv, dims, bits, 1, B * H * cap, vrows)
+        out["varr"] = gc.oracle_cache_arrays(qvv, dims, bits, 1, B * H * cap, vrows, v_mse)
         out["v_t"] = v_full[:, :, :n_ctx]
     return out
 
@@ -57,7 +58,8 @@ def _oracle_side(wl, n_ctx, cap, with_v=True):
 def _device_decode(tq, wl, o, n_ctx, cap, with_v=True, want_logits=True, n_split=0, q=None):
     import torch
     kq = tq.Quantizer.from_parts(o["ks"].rotations, o["ks"].sketches, o["bits"], perm=o["ks"].perm)
-    vq = tq.Quantizer.from_parts(o["vs"].rotations, o["vs"].sketches, o["bits"], perm=o["vs"].perm)
+    vq = tq.Quantizer.from_parts(o["vs"].rotations, o["vs"].sketches, o["bits"], perm=o["vs"].perm,
+                                 mse_only=o["v_mse"])
     B, H = wl.batch, wl.n_kv_heads
     kc = gc.to_device_cache(kq, tq.TQ_TOKEN_MAJOR, B * H * cap, o["karr"])
     vc = gc.to_device_cache(vq, tq.TQ_BLOCK32, B * H * cap, o["varr"]) if with_v else None
@@ -478,3 +480,79 @@ def test_paged_cache_per_sequence_lengths(tq, T):
             lim = n - T + i + 1
             assert gc.normwise_close(lgn[b, :, i, :lim], rl[:, i, :lim])[0], (b, i)
         assert np.all(np.isnan(lgn[b, :, :, n:]))  # past the sequence: not written
+
+
+# MSE-only V records (codes and norms, no sign words; the values are
+# dequantized as n Pi^T c[idx]) under two-stage K: the packed layout (at most
+# 4 query heads per KV head), 16-head blocks, two groups, ragged lengths.
+MSE_V_CASES = [
+    ("llama8b_decode", dict(batch=2, n_q_heads=8, n_kv_heads=2), 1000, 1024),
+    ("llama8b_decode", dict(batch=1, n_q_heads=16, n_kv_heads=2), 2048, 2048),
+    ("llama8b_decode", dict(batch=1, n_q_heads=4, n_kv_heads=1), 33, 64),
+    ("mixed_3p5", dict(batch=2, n_q_heads=8, n_kv_heads=2), 777, 800),
+    ("mixed_2p5", dict(batch=1, n_q_heads=40, n_kv_heads=2), 300, 320),
+    ("llama8b_decode", dict(batch=1, n_q_heads=4, n_kv_heads=1, groups=((128, 4),)), 500, 512),
+]
+
+
+@pytest.mark.parametrize("name,over,n_ctx,cap", MSE_V_CASES)
+def test_mse_only_v_matches_oracle(tq, name, over, n_ctx, cap):
+    wl = synth.workload(name, **over)
+    o = _oracle_side(wl, n_ctx, cap, v_mse=True)
+    lg, out, q = _device_decode(tq, wl, o, n_ctx, cap)
+    rl, ro = _reference(wl, o, q)
+    ok_l, wl_ = gc.normwise_close(lg, rl)
+    ok_o, wo = gc.normwise_close(out, ro)
+    print(name, over, n_ctx, "logits", wl_, "out", wo)
+    assert ok_l and ok_o, (wl_, wo)
+
+
+def test_mse_only_v_append_step(tq):
+    # fused K/V append + decode with MSE-only V: the same cache and results,
+    # bit for bit, as tq_quantize (K), tq_quantize (V) and tq_attn_decode
+    import torch
+    wl = synth.workload("llama8b_decode", batch=2, n_q_heads=8, n_kv_heads=2)
+    n_ctx, cap, n_new = 700, 768, 40
+    o = _oracle_side(wl, n_ctx, cap, v_mse=True)
+    kq = tq.Quantizer.from_parts(o["ks"].rotations, o["ks"].sketches, o["bits"], perm=o["ks"].perm)
+    vq = tq.Quantizer.from_parts(o["vs"].rotations, o["vs"].sketches, o["bits"], perm=o["vs"].perm,
+                                 mse_only=True)
+    B, H = wl.batch, wl.n_kv_heads
+    t0 = n_ctx - n_new
+    kx = np.concatenate([synth.draw_kv_slab(wl, "K", b, h, t0, n_ctx) for b in range(B) for h in range(H)])
+    vx = np.concatenate([synth.draw_kv_slab(wl, "V", b, h, t0, n_ctx) for b in range(B) for h in range(H)])
+    q = torch.from_numpy(synth.draw_queries(wl)).cuda().to(torch.bfloat16)
+    shape = tq.decode_shape(B, wl.n_q_heads, H, n_ctx, cap, wl.scale)
+    kx_t = torch.from_numpy(-kx).cuda().to(torch.bfloat16)
+    vx_t = torch.from_numpy(-vx).cuda().to(torch.bfloat16)
+    results = []
+    for fused in (False, True):
+        kc = gc.to_device_cache(kq, tq.TQ_TOKEN_MAJOR, B * H * cap, o["karr"])
+        vc = gc.to_device_cache(vq, tq.TQ_BLOCK32, B * H * cap, o["varr"])
+        logits = torch.full((B, wl.n_q_heads, n_ctx), float("nan"), device="cuda")
+        out = torch.full((B, wl.n_q_heads, wl.d), float("nan"), device="cuda")
+        if fused:
+            tq.tq_attn_decode_append(kq, vq, shape, q, kc, vc,
+                                     k_new=tq.append_spec(kx_t, seg_len=n_new, seg_stride=cap, seg_offset=t0),
+                                     v_new=tq.append_spec(vx_t, seg_len=n_new, seg_stride=cap, seg_offset=t0),
+                                     logits=logits, out=out)
+        else:
+            tq.tq_quantize(kq, tq.TQ_TOKEN_MAJOR, kx_t, kc, seg_len=n_new, seg_stride=cap, seg_offset=t0)
+            tq.tq_quantize(vq, tq.TQ_BLOCK32, vx_t, vc, seg_len=n_new, seg_stride=cap, seg_offset=t0)
+            tq.tq_attn_decode(kq, vq, shape, q, kc, vc, logits=logits, out=out)
+        torch.cuda.synchronize()
+        results.append([x.cpu().numpy() for x in (kc.codes, kc.signs, kc.norms, vc.codes, vc.norms,
+                                                  logits, out)])
+    for a, b in zip(*results):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+    kt, vt = o["k_t"].copy(), o["v_t"].copy()
+    okq, ovq = oracle.Quantizer.from_spec(o["ks"]), oracle.Quantizer.from_spec(o["vs"], mse_only=True)
+    for arr, x, qz in ((kt, kx, okq), (vt, vx, ovq)):
+        xb = torch.from_numpy(-x).to(torch.bfloat16).to(torch.float64).numpy()
+        qv = oracle.quantize(xb, qz)
+        arr[:, :, t0:n_ctx] = oracle.dequantize(qv.idx, qv.bits, qv.norm, qv.gamma, qz).reshape(B, H, n_new, wl.d)
+    q64 = synth.draw_queries(wl)
+    for b in range(B):
+        rl, ro = oracle.attention_decode(q64[b].astype(np.float64), kt[b], vt[b], wl.scale)
+        assert gc.normwise_close(results[1][5][b].astype(np.float64), rl)[0]
+        assert gc.normwise_close(results[1][6][b].astype(np.float64), ro)[0]

@@ -253,3 +253,44 @@ def test_few_vectors_agree_with_tiles(tq):
     # norms n to 1e-6 relative, residual norms gamma to 2e-6 n (the record rule)
     assert np.all(np.abs(na[:, 0] - nb[:, 0]) <= 1e-6 * nb[:, 0])
     assert np.all(np.abs(na[:, 1] - nb[:, 1]) <= 2e-6 * nb[:, 0])
+
+
+# MSE-only records (stage one alone): codes and norms, no sign words; the
+# tile path (more than 64 vectors) and the few-vector path, both formats,
+# scattered rows (partial 32-row blocks) into a cache pre-filled with ones.
+MSE_ONLY_CASES = [
+    # name, kind, format, dtype, n_vec
+    ("llama8b_decode", "V", "TQ_BLOCK32", "bf16", 300),
+    ("llama8b_decode", "V", "TQ_BLOCK32", "bf16", 1),
+    ("mixed_3p5", "V", "TQ_BLOCK32", "bf16", 17),
+    ("mixed_3p5", "V", "TQ_TOKEN_MAJOR", "bf16", 700),
+    ("tiny", "K", "TQ_TOKEN_MAJOR", "f32", 40),
+    ("tiny", "K", "TQ_BLOCK32", "f32", 129),
+]
+
+
+@pytest.mark.parametrize("name,kind,fmt_name,dtype,n_vec", MSE_ONLY_CASES)
+def test_mse_only_records(tq, name, kind, fmt_name, dtype, n_vec):
+    import torch
+    wl = synth.workload(name)
+    spec = synth.draw_quantizer(wl, kind)
+    x = synth.draw_kv_slab(wl, kind, 0, 1, 0, n_vec).copy()
+    x[n_vec // 2] = 0.0
+    n_rows = 32 * ((3 * n_vec + 31) // 32 + 1)
+    rows = np.random.default_rng(n_vec + 5).permutation(n_rows)[:n_vec]
+    oq, dq = gc.quantizers(spec, mse_only=True)
+    fmt = getattr(tq, fmt_name)
+    cache = tq.Cache.empty(dq, n_rows, fmt)
+    assert cache.signs.numel() == 0
+    cache.codes.fill_(-1)
+    xt = torch.from_numpy(x).cuda()
+    if dtype == "bf16":
+        xt = xt.to(torch.bfloat16)
+    tq.tq_quantize(dq, fmt, xt, cache, dst_rows=torch.from_numpy(rows.astype(np.int64)).cuda())
+    torch.cuda.synchronize()
+    got_all = gc.read_cache(cache, dq)
+    qv = oracle.quantize(x.astype(np.float64), oq)
+    print(gc.compare_records(x.astype(np.float64), oq, qv, gc.select_rows(got_all, rows)))
+    untouched = np.setdiff1d(np.arange(n_rows), rows)
+    for g in range(len(dq.mse_bits)):
+        assert np.all(got_all[0][g][untouched] == 2 ** dq.mse_bits[g] - 1)
