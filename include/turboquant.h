@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 3
+#define TQ_ABI_VERSION 4
 
 typedef enum {
   TQ_OK = 0,
@@ -96,6 +96,11 @@ typedef struct {
                            sign words, bits per channel = m_g, gamma is stored but
                            not used, and dequantization is n Pi^T c[idx]. Decode
                            takes it for V only. */
+  int32_t norm_f16;     /* 0: the norms (n_g, gamma_g) are stored as float32;
+                           1: as float16 (rounded to nearest even from float32;
+                           32 bits per group instead of 64). fp16 norms need
+                           every n_g below 65504 and lose relative precision
+                           below 6.1e-5 (subnormals). */
 } tq_layout;
 
 /* One quantizer instance (one for K, one for V). All pointers are device
@@ -139,11 +144,13 @@ typedef struct {
 typedef struct {
   int32_t code_words;       /* TQ_TOKEN_MAJOR code words per row */
   int32_t sign_words;       /* TQ_TOKEN_MAJOR sign words per row */
-  int32_t norm_floats;      /* floats per row, both formats: 2 * n_groups */
+  int32_t norm_floats;      /* norm values per row, both formats: 2 * n_groups
+                               (float32, or float16 when norm_f16) */
   int32_t block_code_words; /* TQ_BLOCK32 code words per 32-row block */
   int32_t block_sign_words; /* TQ_BLOCK32 sign words per 32-row block */
   int32_t record_bits;      /* algorithmic bits per row: sum_g (m_g + 1) d_g + 64 n_groups
-                               (MSE-only: sum_g m_g d_g + 64 n_groups) */
+                               (MSE-only: m_g in place of m_g + 1; fp16 norms:
+                               32 n_groups in place of 64 n_groups) */
 } tq_record_info;
 
 /*
@@ -157,7 +164,8 @@ typedef struct {
  *          channel j (0-based within the group) is stream bits
  *          [m_g j, m_g j + m_g) of the group's words.
  *   signs: for each group, ceil(d_g / 32) words; bit j = sign bit of channel j.
- *   norms: (n_g, gamma_g) as float32 for each group.
+ *   norms: (n_g, gamma_g) as float32 (float16 when norm_f16) for each group;
+ *          tq_cache.norms then points to float16 values.
  * TQ_BLOCK32, per block of 32 rows (row r = 32 b + t, t = 8 o + s with octet
  * o in 0..3 and position s in 0..7):
  *   codes: for each group g, m_g d_g words; the code of slot t at channel j is

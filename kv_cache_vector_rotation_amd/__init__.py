@@ -54,7 +54,8 @@ class TQError(RuntimeError):
 
 class tq_layout(C.Structure):
     _fields_ = [("d", C.c_int32), ("n_groups", C.c_int32), ("group_dim", C.c_int32 * 2),
-                ("mse_bits", C.c_int32 * 2), ("mse_only", C.c_int32)]
+                ("mse_bits", C.c_int32 * 2), ("mse_only", C.c_int32),
+                ("norm_f16", C.c_int32)]
 
 
 class tq_quantizer(C.Structure):
@@ -165,11 +166,13 @@ def _check(status: int, where: str) -> None:
         raise TQError(status, where)
 
 
-def make_layout(dims: Sequence[int], mse_bits: Sequence[int], mse_only: bool = False) -> tq_layout:
+def make_layout(dims: Sequence[int], mse_bits: Sequence[int], mse_only: bool = False,
+                norm_f16: bool = False) -> tq_layout:
     l = tq_layout()
     l.d = int(sum(dims))
     l.n_groups = len(dims)
     l.mse_only = int(bool(mse_only))
+    l.norm_f16 = int(bool(norm_f16))
     for g, (d, m) in enumerate(zip(dims, mse_bits)):
         l.group_dim[g] = int(d)
         l.mse_bits[g] = int(m)
@@ -249,7 +252,7 @@ class Quantizer:
     @staticmethod
     def from_parts(rotations: Sequence[np.ndarray], sketches: Sequence[np.ndarray],
                    mse_bits: Sequence[int], perm: Optional[np.ndarray] = None,
-                   device: str = "cuda", mse_only: bool = False) -> "Quantizer":
+                   device: str = "cuda", mse_only: bool = False, norm_f16: bool = False) -> "Quantizer":
         """Assemble rot = blockdiag(Pi_g) P and sketch = blockdiag(S_g) P (P the
         channel permutation x -> x[perm]), fold sketch rot^T on the host, and
         build the float32 codebooks with tq_build_codebook."""
@@ -276,7 +279,7 @@ class Quantizer:
             cents.append(c.astype(np.float32))
             bnds.append(t.astype(np.float32))
         to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
-        return Quantizer(layout=make_layout(dims, mse_bits, mse_only), dims=tuple(dims),
+        return Quantizer(layout=make_layout(dims, mse_bits, mse_only, norm_f16), dims=tuple(dims),
                          mse_bits=tuple(int(m) for m in mse_bits), rot=to(rot), sketch=to(sk),
                          sketch_rot=to(skr), centroids=to(np.concatenate(cents)),
                          boundaries=to(np.concatenate(bnds)))
@@ -314,7 +317,8 @@ class Cache:
         else:
             codes = torch.zeros(n_rows * info.code_words, dtype=torch.int32, device=device)
             signs = torch.zeros(n_rows * info.sign_words, dtype=torch.int32, device=device)
-        norms = torch.zeros(n_rows * info.norm_floats, dtype=torch.float32, device=device)
+        ndt = torch.float16 if quantizer.layout.norm_f16 else torch.float32
+        norms = torch.zeros(n_rows * info.norm_floats, dtype=ndt, device=device)
         return Cache(fmt=fmt, n_rows=n_rows, codes=codes, signs=signs, norms=norms)
 
     def struct(self) -> tq_cache:

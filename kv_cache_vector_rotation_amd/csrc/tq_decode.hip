@@ -79,10 +79,12 @@ struct DArgs {
   const float* kscale;    // per K group: the fp16 table holds c * kscale
   const uint32_t* kc;
   const uint32_t* ks;
-  const float* kn;
+  const float* kn;  // norm pairs: float32, or float16 when kn_f16 (then read as words)
   const uint32_t* vc;
   const uint32_t* vs;
   const float* vn;
+  int kn_f16, vn_f16;      // norms stored as float16
+  int kn_shift, vn_shift;  // log2 of the norm bytes per row
   const float* kcent;  // K centroids (concatenated over groups)
   const float* vcent;
   float* logits;  // [batch, hq, n_ctx] or null
@@ -316,8 +318,8 @@ struct Raw {
   using G = Geo<D, NG, M0, M1>;
   uint32_t kc[2][G::KNWT];  // K code words of the lane's token in each half-tile
   uint32_t ks[2][NG];       // K sign word holding the lane's sign bits, per group
-  float kn[NG];             // the lane's share of the tile's K norms
-  float vn[NG];             // and of the V norms
+  uint32_t kn[NG];          // the words holding the lane's share of the tile's K norms
+  uint32_t vn[NG];          // and of the V norms
   uint32_t vc[G::VNWT];     // V code words (octet lg, channels RUN ln ..)
   uint32_t vs[G::VNS * NG]; // V sign words
 };
@@ -356,9 +358,23 @@ __device__ __forceinline__ LaneOff<D, NG, M0, M1> lane_offsets(int ln, int lg) {
 
 // Loads one 32-token tile whose first cache row is row0 (wave-uniform, a
 // multiple of 32): the base addresses are scalar, the lanes add their offsets.
+// Byte offsets (from a tile's first row) of the words holding the lane's norm
+// values i = lane NG + e of the tile's [32][2 NG] values, and the shift of a
+// float16 value within its word.
+template <int NG>
+struct NormOff {
+  uint32_t kb[NG], vb[NG], ksh[NG], vsh[NG];
+};
+
+// A stored norm value from the word that holds it.
+__device__ __forceinline__ float norm_value(uint32_t w, uint32_t sh, int f16) {
+  return f16 ? (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> sh)) : __uint_as_float(w);
+}
+
 template <int D, int NG, int M0, int M1, int WV>
 __device__ __forceinline__ void load_tile(const DArgs& a, int64_t row0, int lane,
-                                          const LaneOff<D, NG, M0, M1>& o, Raw<D, NG, M0, M1>& r) {
+                                          const LaneOff<D, NG, M0, M1>& o, const NormOff<NG>& no,
+                                          Raw<D, NG, M0, M1>& r) {
   using G = Geo<D, NG, M0, M1>;
   const uint32_t* kc = a.kc + row0 * G::CW;
   const uint32_t* ks = a.ks + row0 * G::SW;
@@ -372,13 +388,13 @@ __device__ __forceinline__ void load_tile(const DArgs& a, int64_t row0, int lane
   };
   k_rows(std::integral_constant<int, 0>{});
   if constexpr (NG > 1) k_rows(std::integral_constant<int, 1>{});
-  const float* kn = a.kn + row0 * (2 * NG);
+  const unsigned char* kn = reinterpret_cast<const unsigned char*>(a.kn) + (row0 << a.kn_shift);
 #pragma unroll
-  for (int e = 0; e < NG; ++e) r.kn[e] = kn[lane * NG + e];
+  for (int e = 0; e < NG; ++e) r.kn[e] = *reinterpret_cast<const uint32_t*>(kn + no.kb[e]);
   if constexpr (WV != 0) {
-    const float* vn = a.vn + row0 * (2 * NG);
+    const unsigned char* vn = reinterpret_cast<const unsigned char*>(a.vn) + (row0 << a.vn_shift);
 #pragma unroll
-    for (int e = 0; e < NG; ++e) r.vn[e] = vn[lane * NG + e];
+    for (int e = 0; e < NG; ++e) r.vn[e] = *reinterpret_cast<const uint32_t*>(vn + no.vb[e]);
     const int64_t blk = row0 / 32;
     const uint32_t* vc = a.vc + blk * G::BCW;
     const uint32_t* vs = a.vs + blk * G::BSW;
@@ -449,6 +465,15 @@ __global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel
     return (pb * a.hkv + kvh) * kTile;
   };
   const LaneOff<D, NG, M0, M1> lo = lane_offsets<D, NG, M0, M1>(ln, lg);
+  NormOff<NG> no;
+#pragma unroll
+  for (int e = 0; e < NG; ++e) {
+    const uint32_t i = lane * NG + e;
+    no.kb[e] = a.kn_f16 ? 4 * (i >> 1) : 4 * i;
+    no.ksh[e] = a.kn_f16 ? 16 * (i & 1) : 0;
+    no.vb[e] = a.vn_f16 ? 4 * (i >> 1) : 4 * i;
+    no.vsh[e] = a.vn_f16 ? 16 * (i & 1) : 0;
+  }
   // lane l stages floats l NG + e of a tile's K norms [32][n_0, gamma_0, ..]:
   // an n_g is divided by the group's codebook scale s_g
   float kn_mul[NG];
@@ -518,7 +543,7 @@ __global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel
   int64_t tile = t_begin + wv;
   // (unconditional, so the wait for the centroids below need not drain it;
   // a wave without tiles loads tile 0, which always exists, and drops it)
-  load_tile<D, NG, M0, M1, WV>(a, tile_row(tile < t_end ? tile : 0), lane, lo, rb0);
+  load_tile<D, NG, M0, M1, WV>(a, tile_row(tile < t_end ? tile : 0), lane, lo, no, rb0);
   if (tid < 32) {
     s_cent[0][tid] = cent_k;
     s_cent[1][tid] = cent_v;
@@ -566,8 +591,9 @@ __global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel
       const bool nok = full || T0 + (lane * NG) / (2 * NG) < N;
 #pragma unroll
       for (int e = 0; e < NG; ++e) {
-        s_nrm[wv][0][lane * NG + e] = nok ? r.kn[e] * kn_mul[e] : 0.f;
-        if constexpr (WV != 0) s_nrm[wv][1][lane * NG + e] = nok ? r.vn[e] : 0.f;
+        s_nrm[wv][0][lane * NG + e] = nok ? norm_value(r.kn[e], no.ksh[e], a.kn_f16) * kn_mul[e] : 0.f;
+        if constexpr (WV != 0)
+          s_nrm[wv][1][lane * NG + e] = nok ? norm_value(r.vn[e], no.vsh[e], a.vn_f16) : 0.f;
       }
     }
     // LDS operations of one wave execute in order; the wave barrier only keeps
@@ -774,12 +800,12 @@ __global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel
   if (tile < t_end) {
     const int64_t last = t_end - 1 - ((t_end - 1 - tile) % kWaves);  // this wave's last tile
     auto next = [&](int64_t t, int k) { return t + k * kWaves <= last ? t + k * kWaves : last; };
-    if constexpr (NBUF > 2) load_tile<D, NG, M0, M1, WV>(a, tile_row(next(tile, 1)), lane, lo, rb1);
-    if constexpr (NBUF > 3) load_tile<D, NG, M0, M1, WV>(a, tile_row(next(tile, 2)), lane, lo, rb2);
+    if constexpr (NBUF > 2) load_tile<D, NG, M0, M1, WV>(a, tile_row(next(tile, 1)), lane, lo, no, rb1);
+    if constexpr (NBUF > 3) load_tile<D, NG, M0, M1, WV>(a, tile_row(next(tile, 2)), lane, lo, no, rb2);
     // one pass of the rotation: true after the wave's last tile
     auto stage = [&](auto kc) __attribute__((always_inline)) {
       constexpr int k = decltype(kc)::value;
-      load_tile<D, NG, M0, M1, WV>(a, tile_row(next(tile, NBUF - 1)), lane, lo,
+      load_tile<D, NG, M0, M1, WV>(a, tile_row(next(tile, NBUF - 1)), lane, lo, no,
                                    rbuf(std::integral_constant<int, k + NBUF - 1>{}));
       compute(rbuf(kc), tile * kTile);
       if (tile == last) return true;
@@ -1224,11 +1250,15 @@ tq_status plan_decode(const tq_quantizer* kq, const tq_quantizer* vq, const tq_d
   a.kc = k_cache->codes;
   a.ks = k_cache->signs;
   a.kn = k_cache->norms;
+  a.kn_f16 = l.norm_f16;
+  a.kn_shift = (l.n_groups == 2 ? 3 : 2) + (l.norm_f16 ? 0 : 1);  // 2 n_groups values of 2 or 4 bytes
   a.kcent = kq->centroids;
   if (with_v) {
     a.vc = v_cache->codes;
     a.vs = v_cache->signs;
     a.vn = v_cache->norms;
+    a.vn_f16 = vq->layout.norm_f16;
+    a.vn_shift = (l.n_groups == 2 ? 3 : 2) + (vq->layout.norm_f16 ? 0 : 1);
     a.vcent = vq->centroids;
     pl->vrot = vq->rot;
     pl->vsketch = vq->sketch;

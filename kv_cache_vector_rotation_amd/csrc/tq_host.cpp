@@ -94,6 +94,7 @@ namespace tq {
 bool layout_valid(const tq_layout* l) {
   if (!l) return false;
   if (l->mse_only != 0 && l->mse_only != 1) return false;
+  if (l->norm_f16 != 0 && l->norm_f16 != 1) return false;
   if (l->d < 3 || l->d > 256) return false;
   if (l->n_groups != 1 && l->n_groups != 2) return false;
   int sum = 0;
@@ -127,7 +128,7 @@ GroupGeom geometry(const tq_layout* l) {
     bsw += l->mse_only ? 0 : d;
     co += 1 << m;
     bo += (1 << m) - 1;
-    bits += (l->mse_only ? m : m + 1) * d + 64;
+    bits += (l->mse_only ? m : m + 1) * d + (l->norm_f16 ? 32 : 64);
   }
   g.info.code_words = cw;
   g.info.sign_words = sw;

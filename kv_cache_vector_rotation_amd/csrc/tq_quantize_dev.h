@@ -60,6 +60,7 @@ struct QArgs {
   int code_words;
   int sign_words;
   int mse_only;  // stage one alone: no sketch, no sign bits (sign_words = 0)
+  int norm_f16;  // norms stored as float16 pairs (one 32-bit word per row and group)
   int blk_code_words;
   int blk_sign_words;
   int fmt;
@@ -79,6 +80,19 @@ struct QArgs {
   uint32_t* signs;
   float* norms;
 };
+
+// Stores the norm pair (n_g, gamma_g) of record value pair i = row * n_groups
+// + g: two float32, or two float16 (round to nearest even) in one word.
+__device__ __forceinline__ void store_norms(float* norms, int f16, int64_t i, float n, float gam) {
+  if (f16) {
+    typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+    const half2v h = {(_Float16)n, (_Float16)gam};
+    reinterpret_cast<uint32_t*>(norms)[i] = __builtin_bit_cast(uint32_t, h);
+  } else {
+    norms[2 * i] = n;
+    norms[2 * i + 1] = gam;
+  }
+}
 
 // Sum over each row of 16 lanes, result in every lane of the row, with DPP
 // lane moves (no LDS round trip): swap neighbours, swap pairs, then mirror
@@ -680,8 +694,7 @@ __device__ __forceinline__ void quantize_tiles(const QArgs& a, int64_t first_til
         const int w0 = a.choff[g] / 16, w1 = (a.choff[g] + a.gdim[g] + 15) / 16;
         float s = 0.f;
         for (int ww = w0; ww < w1; ++ww) s += gpart[ww * QT + v];
-        a.norms[row * (2 * a.n_groups) + 2 * g] = nrm[g * QT + v];
-        a.norms[row * (2 * a.n_groups) + 2 * g + 1] = sqrtf(s);
+        store_norms(a.norms, a.norm_f16, row * a.n_groups + g, nrm[g * QT + v], sqrtf(s));
       }
     }
     if (tok) {
@@ -1058,8 +1071,8 @@ __device__ __forceinline__ void quantize_small(const QArgs& a, int64_t vec, unsi
     const int g = tid;
     const int cg = g ? c1 : c0, dg = g ? g1 : g0;
     const int v0 = cg / 16, v1 = (cg + dg + 15) / 16;
-    norms[row * (2 * n_groups) + 2 * g] = sqrtf(wave_range_sum(s_np, v0, v1));
-    norms[row * (2 * n_groups) + 2 * g + 1] = sqrtf(wave_range_sum(s_gp, v0, v1));
+    const float nv = sqrtf(wave_range_sum(s_np, v0, v1));
+    store_norms(norms, a.norm_f16, row * n_groups + g, nv, sqrtf(wave_range_sum(s_gp, v0, v1)));
   }
   if (tok) {
     for (int e = tid; e < n_words; e += NTHR) {
@@ -1150,6 +1163,7 @@ inline tq_status make_qargs(const tq_quantizer* qz, tq_format fmt, const void* x
   a.code_words = geo.info.code_words;
   a.sign_words = geo.info.sign_words;
   a.mse_only = l.mse_only;
+  a.norm_f16 = l.norm_f16;
   a.blk_code_words = geo.info.block_code_words;
   a.blk_sign_words = geo.info.block_sign_words;
   a.fmt = fmt;

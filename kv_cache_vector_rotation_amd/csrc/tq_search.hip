@@ -60,6 +60,7 @@ struct SArgs {
   const uint32_t* codes;
   const uint32_t* signs;
   const float* norms;
+  int norm_f16;  // norm pairs stored as float16 (one word per row)
   const _Float16* qprep;  // [n_q][3 D]: q_rot hi, q_rot lo * 2^11 (unused here), q_sk
   const float* kscale;    // fp16 codebook scale s
   const float* centroids;
@@ -176,7 +177,10 @@ __global__ __launch_bounds__(256, 3) void search_kernel(SArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t ri = t * kTV + 4 * lg + i < a.n_db ? t * kTV + 4 * lg + i : a.n_db - 1;
-      r.nr[i] = *reinterpret_cast<const u32x2*>(a.norms + ri * 2);
+      if (a.norm_f16)
+        r.nr[i] = u32x2{reinterpret_cast<const uint32_t*>(a.norms)[ri], 0u};
+      else
+        r.nr[i] = *reinterpret_cast<const u32x2*>(a.norms + ri * 2);
     }
   };
 
@@ -226,7 +230,10 @@ __global__ __launch_bounds__(256, 3) void search_kernel(SArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t row = t * kTV + 4 * lg + i;
-      const float n = __uint_as_float(r.nr[i][0]), gm = __uint_as_float(r.nr[i][1]);
+      const float n = a.norm_f16 ? (float)__builtin_bit_cast(_Float16, (uint16_t)r.nr[i][0])
+                                 : __uint_as_float(r.nr[i][0]);
+      const float gm = a.norm_f16 ? (float)__builtin_bit_cast(_Float16, (uint16_t)(r.nr[i][0] >> 16))
+                                  : __uint_as_float(r.nr[i][1]);
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
         float x = fmaf(n * inv_s, acc[cb][0][i], gm * acc[cb][1][i]);
@@ -444,6 +451,7 @@ extern "C" tq_status tq_search(const tq_quantizer* qz, const tq_cache* db, int64
   a.codes = db->codes;
   a.signs = db->signs;
   a.norms = db->norms;
+  a.norm_f16 = l.norm_f16;
   a.qprep = qprep;
   a.kscale = kscale;
   a.centroids = qz->centroids;

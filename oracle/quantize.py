@@ -27,7 +27,10 @@ Readings used here (each listed in the design doc):
 * an MSE-only instance (the first of the two stages alone: [ZB] paragraph
   2 and [WD] "1. PolarQuant") keeps the same indices and norms but no sign
   bits: m_g bits per channel. Quantization itself is unchanged (the sign
-  bits are still computed here, for diagnostics, and are simply not stored).
+  bits are still computed here, for diagnostics, and are simply not stored);
+* fp16 norm storage (a layout option): n_g and gamma_g are computed exactly
+  as above and rounded to float16 (nearest even) when stored; the residual
+  and the sign bits use the unrounded n_g.
 """
 from __future__ import annotations
 
@@ -51,9 +54,10 @@ class Quantizer:
     sketches: List[np.ndarray]    # float64 d_g x d_g
     codebooks: List[Codebook]
     mse_only: bool = False        # stage one alone: records carry no sign bits
+    norm_f16: bool = False        # norms stored as float16
 
     @staticmethod
-    def from_spec(spec, mse_only: bool = False) -> "Quantizer":
+    def from_spec(spec, mse_only: bool = False, norm_f16: bool = False) -> "Quantizer":
         """Build from a ``synth.QuantizerSpec`` (random inputs) plus this
         oracle's own Lloyd-Max codebooks."""
         dims = [g.dim for g in spec.groups]
@@ -61,7 +65,7 @@ class Quantizer:
         return Quantizer(d=spec.d, perm=np.asarray(spec.perm, dtype=np.int64), dims=dims,
                          rotations=[np.asarray(r, np.float64) for r in spec.rotations],
                          sketches=[np.asarray(s, np.float64) for s in spec.sketches],
-                         codebooks=cbs, mse_only=bool(mse_only))
+                         codebooks=cbs, mse_only=bool(mse_only), norm_f16=bool(norm_f16))
 
     @property
     def offsets(self) -> List[int]:
@@ -120,8 +124,9 @@ def quantize(x: np.ndarray, qz: Quantizer) -> QuantizedVectors:
         margin = np.min(np.abs(y[..., None] - cb.boundaries), axis=-1)
         out.idx.append(idx.astype(np.int64))
         out.bits.append(bits)
-        out.norm.append(n.astype(np.float32))
-        out.gamma.append(gamma.astype(np.float32))
+        stored = np.float16 if qz.norm_f16 else np.float32
+        out.norm.append(n.astype(stored).astype(np.float32))
+        out.gamma.append(gamma.astype(stored).astype(np.float32))
         out.y.append(y)
         out.margin.append(margin)
         out.sign_margin.append(np.abs(s) / safe[:, None])

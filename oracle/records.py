@@ -13,7 +13,8 @@ Token-major records (used for K), one row per token:
           of word floor(b / 32).
   signs : for each group, d_g bits (bit j = sign bit of channel j), padded
           to whole words, same bit order.
-  norms : float32 pairs (n_g, gamma_g) for each group.
+  norms : float32 pairs (n_g, gamma_g) for each group (float16 pairs in the
+          fp16-norm layout).
 
 Block records (used for V): rows are grouped in aligned blocks of 32; inside
 a block, token slot t = 8 o + s (octet o in 0..3, position s in 0..7).
@@ -46,11 +47,11 @@ def record_words(dims: Sequence[int], mse_bits: Sequence[int], mse_only: bool = 
 
 
 def record_bytes(dims: Sequence[int], mse_bits: Sequence[int], include_norms: bool = True,
-                 mse_only: bool = False) -> float:
+                 mse_only: bool = False, norm_f16: bool = False) -> float:
     """Algorithmic bytes per token: index bits + sign bits (none when
-    MSE-only) (+ two float32 norms per group)."""
+    MSE-only) (+ two float32, or float16, norms per group)."""
     bits = sum((m if mse_only else m + 1) * d for d, m in zip(dims, mse_bits))
-    return bits / 8.0 + (8.0 * len(dims) if include_norms else 0.0)
+    return bits / 8.0 + ((4.0 if norm_f16 else 8.0) * len(dims) if include_norms else 0.0)
 
 
 def _bits_to_words(bitarray: np.ndarray) -> np.ndarray:
@@ -59,10 +60,10 @@ def _bits_to_words(bitarray: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(by).view("<u4")
 
 
-def pack_token_major(idx, bits, norm, gamma, dims, mse_bits, mse_only=False):
+def pack_token_major(idx, bits, norm, gamma, dims, mse_bits, mse_only=False, norm_f16=False):
     """Per-token records from per-group codes/bits/norms (lists over groups).
-    Returns (codes [n, Wc] uint32, signs [n, Ws] uint32, norms [n, 2G] float32);
-    MSE-only records have Ws = 0."""
+    Returns (codes [n, Wc] uint32, signs [n, Ws] uint32, norms [n, 2G] float32
+    or float16); MSE-only records have Ws = 0."""
     n = idx[0].shape[0]
     code_parts, sign_parts, norm_cols = [], [], []
     for g, (d, m) in enumerate(zip(dims, mse_bits)):
@@ -76,14 +77,14 @@ def pack_token_major(idx, bits, norm, gamma, dims, mse_bits, mse_only=False):
             sign_parts.append(_bits_to_words(sstream))
         norm_cols += [np.asarray(norm[g], np.float32), np.asarray(gamma[g], np.float32)]
     return (np.concatenate(code_parts, axis=1), _concat_signs(sign_parts, code_parts[0].shape[0]),
-            np.stack(norm_cols, axis=1))
+            np.stack(norm_cols, axis=1).astype(np.float16 if norm_f16 else np.float32))
 
 
 def _concat_signs(parts, n):
     return np.concatenate(parts, axis=1) if parts else np.zeros((n, 0), np.uint32)
 
 
-def pack_block32(idx, bits, norm, gamma, dims, mse_bits, mse_only=False):
+def pack_block32(idx, bits, norm, gamma, dims, mse_bits, mse_only=False, norm_f16=False):
     """Block records for n rows (n a multiple of 32).
     Returns (codes [n/32, sum m_g d_g] uint32, signs [n/32, sum d_g] uint32,
     norms [n, 2G] float32); MSE-only records have no sign words."""
@@ -109,4 +110,4 @@ def pack_block32(idx, bits, norm, gamma, dims, mse_bits, mse_only=False):
             sign_parts.append(_bits_to_words(sregion))
         norm_cols += [np.asarray(norm[g], np.float32), np.asarray(gamma[g], np.float32)]
     return (np.concatenate(code_parts, axis=1), _concat_signs(sign_parts, code_parts[0].shape[0]),
-            np.stack(norm_cols, axis=1))
+            np.stack(norm_cols, axis=1).astype(np.float16 if norm_f16 else np.float32))

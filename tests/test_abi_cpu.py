@@ -345,3 +345,14 @@ def test_mse_only_decode_and_search_validation(tq):
     assert lib.tq_search_workspace_bytes(C.byref(q), 1000, 50, 10, C.byref(need)) == 0
     assert lib.tq_search(C.byref(q), C.byref(db), 1000, FAKE, 0, 50, 10, FAKE, FAKE, FAKE, need.value,
                          None) == tq.TQ_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("mse_only", [False, True])
+def test_norm_f16_record_layout(tq, mse_only):
+    info = tq.tq_record_layout(tq.make_layout([64, 64], [3, 2], mse_only=mse_only, norm_f16=True))
+    assert info.norm_floats == 4
+    assert info.record_bits == 8 * oracle.record_bytes([64, 64], [3, 2], mse_only=mse_only, norm_f16=True)
+    l = tq.make_layout([128], [3])
+    l.norm_f16 = 3
+    with pytest.raises(tq.TQError):
+        tq.tq_record_layout(l)

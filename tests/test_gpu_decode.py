@@ -27,13 +27,13 @@ def tq():
     return m
 
 
-def _oracle_side(wl, n_ctx, cap, with_v=True, v_mse=False):
+def _oracle_side(wl, n_ctx, cap, with_v=True, v_mse=False, k_f16=False, v_f16=False):
     """Quantize the K (and V) streams with the oracle, return oracle quantizers,
     specs, per-(b,h) dequantized caches and packed arrays (v_mse: MSE-only V
-    records)."""
+    records; k_f16, v_f16: fp16 norms)."""
     ks, vs = synth.draw_quantizer(wl, "K"), synth.draw_quantizer(wl, "V")
-    okq = oracle.Quantizer.from_spec(ks)
-    ovq = oracle.Quantizer.from_spec(vs, mse_only=v_mse)
+    okq = oracle.Quantizer.from_spec(ks, norm_f16=k_f16)
+    ovq = oracle.Quantizer.from_spec(vs, mse_only=v_mse, norm_f16=v_f16)
     B, H = wl.batch, wl.n_kv_heads
     dims = [g.dim for g in ks.groups]
     bits = [g.mse_bits for g in ks.groups]
@@ -41,8 +41,8 @@ def _oracle_side(wl, n_ctx, cap, with_v=True, v_mse=False):
     qk = oracle.quantize(kx, okq)
     k_t = oracle.dequantize(qk.idx, qk.bits, qk.norm, qk.gamma, okq).reshape(B, H, n_ctx, wl.d)
     rows = np.concatenate([(b * H + h) * cap + np.arange(n_ctx) for b in range(B) for h in range(H)])
-    karr = gc.oracle_cache_arrays(qk, dims, bits, 0, B * H * cap, rows)
-    out = dict(ks=ks, vs=vs, k_t=k_t, karr=karr, dims=dims, bits=bits, v_mse=v_mse)
+    karr = gc.oracle_cache_arrays(qk, dims, bits, 0, B * H * cap, rows, norm_f16=k_f16)
+    out = dict(ks=ks, vs=vs, k_t=k_t, karr=karr, dims=dims, bits=bits, v_mse=v_mse, k_f16=k_f16, v_f16=v_f16)
     if with_v:
         # block records need whole blocks: quantize up to the block boundary
         nb = ((n_ctx + 31) // 32) * 32
@@ -50,16 +50,17 @@ def _oracle_side(wl, n_ctx, cap, with_v=True, v_mse=False):
         qvv = oracle.quantize(vx, ovq)
         v_full = oracle.dequantize(qvv.idx, qvv.bits, qvv.norm, qvv.gamma, ovq).reshape(B, H, nb, wl.d)
         vrows = np.concatenate([(b * H + h) * cap + np.arange(nb) for b in range(B) for h in range(H)])
-        out["varr"] = gc.oracle_cache_arrays(qvv, dims, bits, 1, B * H * cap, vrows, v_mse)
+        out["varr"] = gc.oracle_cache_arrays(qvv, dims, bits, 1, B * H * cap, vrows, v_mse, v_f16)
         out["v_t"] = v_full[:, :, :n_ctx]
     return out
 
 
 def _device_decode(tq, wl, o, n_ctx, cap, with_v=True, want_logits=True, n_split=0, q=None):
     import torch
-    kq = tq.Quantizer.from_parts(o["ks"].rotations, o["ks"].sketches, o["bits"], perm=o["ks"].perm)
+    kq = tq.Quantizer.from_parts(o["ks"].rotations, o["ks"].sketches, o["bits"], perm=o["ks"].perm,
+                                 norm_f16=o["k_f16"])
     vq = tq.Quantizer.from_parts(o["vs"].rotations, o["vs"].sketches, o["bits"], perm=o["vs"].perm,
-                                 mse_only=o["v_mse"])
+                                 mse_only=o["v_mse"], norm_f16=o["v_f16"])
     B, H = wl.batch, wl.n_kv_heads
     kc = gc.to_device_cache(kq, tq.TQ_TOKEN_MAJOR, B * H * cap, o["karr"])
     vc = gc.to_device_cache(vq, tq.TQ_BLOCK32, B * H * cap, o["varr"]) if with_v else None
@@ -556,3 +557,29 @@ def test_mse_only_v_append_step(tq):
         rl, ro = oracle.attention_decode(q64[b].astype(np.float64), kt[b], vt[b], wl.scale)
         assert gc.normwise_close(results[1][5][b].astype(np.float64), rl)[0]
         assert gc.normwise_close(results[1][6][b].astype(np.float64), ro)[0]
+
+
+# fp16 norms in the K and/or V records (the oracle dequantizes with the same
+# stored float16 values): packed and 16-head blocks, two groups, MSE-only V,
+# logits only, ragged lengths.
+F16_CASES = [
+    # name, overrides, n_ctx, cap, k_f16, v_f16, v_mse, with_v
+    ("llama8b_decode", dict(batch=2, n_q_heads=8, n_kv_heads=2), 1000, 1024, True, True, False, True),
+    ("llama8b_decode", dict(batch=1, n_q_heads=16, n_kv_heads=2), 2048, 2048, True, False, False, True),
+    ("mixed_3p5", dict(batch=2, n_q_heads=8, n_kv_heads=2), 777, 800, False, True, False, True),
+    ("mixed_2p5", dict(batch=1, n_q_heads=40, n_kv_heads=2), 300, 320, True, True, True, True),
+    ("llama8b_decode", dict(batch=1, n_q_heads=4, n_kv_heads=1), 33, 64, True, True, True, True),
+    ("tiny", {}, 4096, 4096, True, False, False, False),
+]
+
+
+@pytest.mark.parametrize("name,over,n_ctx,cap,k_f16,v_f16,v_mse,with_v", F16_CASES)
+def test_fp16_norms_match_oracle(tq, name, over, n_ctx, cap, k_f16, v_f16, v_mse, with_v):
+    wl = synth.workload(name, **over)
+    o = _oracle_side(wl, n_ctx, cap, with_v=with_v, v_mse=v_mse, k_f16=k_f16, v_f16=v_f16)
+    lg, out, q = _device_decode(tq, wl, o, n_ctx, cap, with_v=with_v)
+    rl, ro = _reference(wl, o, q, with_v=with_v)
+    ok_l, wl_ = gc.normwise_close(lg, rl)
+    ok_o, wo = gc.normwise_close(out, ro) if with_v else (True, 0.0)
+    print(name, over, n_ctx, k_f16, v_f16, v_mse, "logits", wl_, "out", wo)
+    assert ok_l and ok_o, (wl_, wo)

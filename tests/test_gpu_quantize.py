@@ -294,3 +294,42 @@ def test_mse_only_records(tq, name, kind, fmt_name, dtype, n_vec):
     untouched = np.setdiff1d(np.arange(n_rows), rows)
     for g in range(len(dq.mse_bits)):
         assert np.all(got_all[0][g][untouched] == 2 ** dq.mse_bits[g] - 1)
+
+
+# fp16 norm storage: codes and signs as in the float32 layout, the norms
+# within one float16 unit of the oracle's (both round to nearest even)
+F16_CASES = [
+    # name, kind, format, dtype, n_vec, mse_only
+    ("llama8b_decode", "K", "TQ_TOKEN_MAJOR", "bf16", 1, False),
+    ("llama8b_decode", "V", "TQ_BLOCK32", "bf16", 300, False),
+    ("mixed_3p5", "K", "TQ_TOKEN_MAJOR", "bf16", 700, False),
+    ("mixed_3p5", "V", "TQ_BLOCK32", "bf16", 17, True),
+    ("tiny", "K", "TQ_BLOCK32", "f32", 129, True),
+]
+
+
+@pytest.mark.parametrize("name,kind,fmt_name,dtype,n_vec,mse_only", F16_CASES)
+def test_fp16_norm_records(tq, name, kind, fmt_name, dtype, n_vec, mse_only):
+    import torch
+    wl = synth.workload(name)
+    spec = synth.draw_quantizer(wl, kind)
+    x = synth.draw_kv_slab(wl, kind, 1, 1, 0, n_vec).copy()
+    x[n_vec // 2] = 0.0
+    n_rows = 32 * ((3 * n_vec + 31) // 32 + 1)
+    rows = np.random.default_rng(n_vec + 9).permutation(n_rows)[:n_vec]
+    oq, dq = gc.quantizers(spec, mse_only=mse_only, norm_f16=True)
+    fmt = getattr(tq, fmt_name)
+    cache = tq.Cache.empty(dq, n_rows, fmt)
+    assert cache.norms.dtype == torch.float16
+    cache.norms.fill_(7.0)
+    xt = torch.from_numpy(x).cuda()
+    if dtype == "bf16":
+        xt = xt.to(torch.bfloat16)
+    tq.tq_quantize(dq, fmt, xt, cache, dst_rows=torch.from_numpy(rows.astype(np.int64)).cuda())
+    torch.cuda.synchronize()
+    got_all = gc.read_cache(cache, dq)
+    qv = oracle.quantize(x.astype(np.float64), oq)
+    print(gc.compare_records(x.astype(np.float64), oq, qv, gc.select_rows(got_all, rows)))
+    untouched = np.setdiff1d(np.arange(n_rows), rows)
+    for g in range(len(dq.mse_bits)):
+        assert np.all(got_all[2][g][untouched] == 7.0) and np.all(got_all[3][g][untouched] == 7.0)

@@ -35,11 +35,11 @@ def tq():
     return m
 
 
-def _db(tq, spec, x, n_rows=None, chunk=100_000):
+def _db(tq, spec, x, n_rows=None, chunk=100_000, norm_f16=False):
     """Oracle-quantized database uploaded as a token-major cache; returns the
     device cache and the oracle's (idx, bits, norm, gamma), quantized and
     packed in chunks."""
-    oq, dq = gc.quantizers(spec)
+    oq, dq = gc.quantizers(spec, norm_f16=norm_f16)
     n = x.shape[0]
     n_rows = n_rows or n
     dims = [g.dim for g in spec.groups]
@@ -47,11 +47,11 @@ def _db(tq, spec, x, n_rows=None, chunk=100_000):
     cw, sw, nf, _, _ = oracle.record_words(dims, bits)
     codes = np.zeros((n_rows, cw), np.uint32)
     signs = np.zeros((n_rows, sw), np.uint32)
-    norms = np.zeros((n_rows, nf), np.float32)
+    norms = np.zeros((n_rows, nf), np.float16 if norm_f16 else np.float32)
     idx, bts, nrm, gam = [], [], [], []
     for s in range(0, n, chunk):
         qv = oracle.quantize(x[s:s + chunk].astype(np.float64), oq)
-        c, sg, nm = oracle.pack_token_major(qv.idx, qv.bits, qv.norm, qv.gamma, dims, bits)
+        c, sg, nm = oracle.pack_token_major(qv.idx, qv.bits, qv.norm, qv.gamma, dims, bits, False, norm_f16)
         codes[s:s + chunk], signs[s:s + chunk], norms[s:s + chunk] = c, sg, nm
         idx.append(qv.idx[0].astype(np.int8))
         bts.append(qv.bits[0])
@@ -154,3 +154,15 @@ def test_full_size_sampled_queries(tq):
 
 
 test_full_size_sampled_queries = pytest.mark.timeout(900)(test_full_size_sampled_queries)
+
+
+@pytest.mark.parametrize("d,m", [(200, 3), (128, 2)])
+def test_search_fp16_norms(tq, d, m):
+    # a database whose records store the norms as float16
+    wl = synth.workload("nn_search", d=d, groups=((d, m),))
+    spec = synth.draw_quantizer(wl, "K")
+    x = synth.draw_mixture_vectors(wl, 2500, "db")
+    q = synth.draw_mixture_vectors(wl, 30, "query")
+    oq, dq, cache, rec = _db(tq, spec, x, norm_f16=True)
+    gi, gs = _search(tq, dq, cache, 2500, q, 10)
+    _check(gi, gs, oracle.estimated_scores(q, *rec, oq), 10)
