@@ -63,7 +63,8 @@ def parse():
     ap.add_argument("--no-bf16-baseline", action="store_true")
     ap.add_argument("--no-search", action="store_true")
     ap.add_argument("--no-chunk", action="store_true", help="skip the prefill-chunk and paged-cache legs")
-    ap.add_argument("--no-mse-v", action="store_true", help="skip the MSE-only V leg")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the record-variant legs (MSE-only V, fp16 norms)")
     ap.add_argument("--ctx-sweep", default="",
                     help="comma-separated context lengths: also time the compressed step and the bf16 "
                          "decode of the llama8b_decode shape at each (reported under ctx_sweep)")
@@ -305,24 +306,29 @@ def _llama8b_quantizers(tq):
             tq.Quantizer.from_parts(vs.rotations, vs.sketches, bits, perm=vs.perm))
 
 
-def mse_v_bench(tq, torch):
-    """Secondary figure: the llama8b_decode step (append + decode) with
-    MSE-only V records (stage one alone: the same code bits, no sign bits)
-    under two-stage K, over enough cache copies for 1 GiB."""
+def variants_bench(tq, torch):
+    """Secondary figures: the llama8b_decode step (append + decode) with the
+    record variants: MSE-only V records (stage one alone: the same code bits,
+    no sign bits) under two-stage K; fp16 norms in both caches; both. Each
+    over enough cache copies for 1 GiB."""
     wl = synth.workload("llama8b_decode")
-    base = synth.workload("llama8b_decode")
-    ks, vs = synth.draw_quantizer(base, "K"), synth.draw_quantizer(base, "V")
+    ks, vs = synth.draw_quantizer(wl, "K"), synth.draw_quantizer(wl, "V")
     bits = [g.mse_bits for g in ks.groups]
     dims = [g.dim for g in ks.groups]
-    kq = tq.Quantizer.from_parts(ks.rotations, ks.sketches, bits, perm=ks.perm)
-    vq = tq.Quantizer.from_parts(vs.rotations, vs.sketches, bits, perm=vs.perm, mse_only=True)
-    rb_k = record_bytes(dims, bits)
-    rb_v = rb_k - sum(dims) / 8
-    copies = max(1, math.ceil((1 << 30) / (wl.batch * wl.n_kv_heads * wl.capacity * (rb_k + rb_v))))
-    us = compressed_step_us(tq, torch, wl, kq, vq, copies)
-    return {"workload": "llama8b_decode", "v_records": "MSE-only", "us_per_step": round(us, 2),
-            "cached_tokens_per_s": wl.batch * wl.n_ctx / (us / 1e6),
-            "record_bytes_per_token": {"K": rb_k, "V": rb_v}, "cache_copies": copies}
+    out = {"workload": "llama8b_decode"}
+    for name, v_mse, f16 in (("mse_only_v", True, False), ("fp16_norms", False, True),
+                             ("mse_only_v_fp16_norms", True, True)):
+        kq = tq.Quantizer.from_parts(ks.rotations, ks.sketches, bits, perm=ks.perm, norm_f16=f16)
+        vq = tq.Quantizer.from_parts(vs.rotations, vs.sketches, bits, perm=vs.perm, mse_only=v_mse,
+                                     norm_f16=f16)
+        nb = (4 if f16 else 8) * len(dims)
+        rb_k = sum((m + 1) * d for d, m in zip(dims, bits)) / 8 + nb
+        rb_v = sum((m if v_mse else m + 1) * d for d, m in zip(dims, bits)) / 8 + nb
+        copies = max(1, math.ceil((1 << 30) / (wl.batch * wl.n_kv_heads * wl.capacity * (rb_k + rb_v))))
+        us = compressed_step_us(tq, torch, wl, kq, vq, copies)
+        out[name] = {"us_per_step": round(us, 2), "cached_tokens_per_s": wl.batch * wl.n_ctx / (us / 1e6),
+                     "record_bytes_per_token": {"K": rb_k, "V": rb_v}, "cache_copies": copies}
+    return out
 
 
 def chunk_bench(tq, torch, T=64):
@@ -644,9 +650,9 @@ def main():
         log(f"chunk: {result['chunk']}")
         result["paged"] = paged_bench(tq, torch)
         log(f"paged: {result['paged']}")
-    if not args.no_mse_v:
-        result["mse_only_v"] = mse_v_bench(tq, torch)
-        log(f"MSE-only V: {result['mse_only_v']}")
+    if not args.no_variants:
+        result["variants"] = variants_bench(tq, torch)
+        log(f"variants: {result['variants']}")
     if not args.no_search:
         result["search"] = search_bench(tq, torch)
         log(f"search: {result['search']}")

@@ -99,7 +99,8 @@ __device__ __forceinline__ void list_insert(float (&sc)[kKL], int (&ix)[kKL], fl
   }
 }
 
-template <int D, int M>
+// H: the database stores its norms as float16 pairs
+template <int D, int M, bool H>
 __global__ __launch_bounds__(256, 3) void search_kernel(SArgs a) {
   using G = Geo<D, M>;
   constexpr int KC = G::KC, CW = G::CW, SW = G::SW;
@@ -177,7 +178,7 @@ __global__ __launch_bounds__(256, 3) void search_kernel(SArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t ri = t * kTV + 4 * lg + i < a.n_db ? t * kTV + 4 * lg + i : a.n_db - 1;
-      if (a.norm_f16)
+      if constexpr (H)
         r.nr[i] = u32x2{reinterpret_cast<const uint32_t*>(a.norms)[ri], 0u};
       else
         r.nr[i] = *reinterpret_cast<const u32x2*>(a.norms + ri * 2);
@@ -230,10 +231,9 @@ __global__ __launch_bounds__(256, 3) void search_kernel(SArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t row = t * kTV + 4 * lg + i;
-      const float n = a.norm_f16 ? (float)__builtin_bit_cast(_Float16, (uint16_t)r.nr[i][0])
-                                 : __uint_as_float(r.nr[i][0]);
-      const float gm = a.norm_f16 ? (float)__builtin_bit_cast(_Float16, (uint16_t)(r.nr[i][0] >> 16))
-                                  : __uint_as_float(r.nr[i][1]);
+      const float n = H ? (float)__builtin_bit_cast(_Float16, (uint16_t)r.nr[i][0]) : __uint_as_float(r.nr[i][0]);
+      const float gm =
+          H ? (float)__builtin_bit_cast(_Float16, (uint16_t)(r.nr[i][0] >> 16)) : __uint_as_float(r.nr[i][1]);
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
         float x = fmaf(n * inv_s, acc[cb][0][i], gm * acc[cb][1][i]);
@@ -370,18 +370,23 @@ bool plan_search(const tq_quantizer* qz, int64_t n_db, int64_t n_q, int k, Plan*
   return true;
 }
 
-template <int D, int M>
-hipError_t launch_search(const SArgs& a, int n_qblocks, hipStream_t st) {
+template <int D, int M, bool H>
+hipError_t launch_search_h(const SArgs& a, int n_qblocks, hipStream_t st) {
   using G = Geo<D, M>;
   static_assert(G::bytes <= 53 * 1024, "three workgroups per compute unit");
   static_assert(M <= 3, "pair tables of at most 64 entries");
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&search_kernel<D, M>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&search_kernel<D, M, H>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, G::bytes);
   if (e != hipSuccess) return e;
   (void)hipGetLastError();  // a launch error is reported below, not an older one
-  hipLaunchKernelGGL((search_kernel<D, M>), dim3((unsigned)n_qblocks, (unsigned)a.n_slices), dim3(256), G::bytes,
-                     st, a);
+  hipLaunchKernelGGL((search_kernel<D, M, H>), dim3((unsigned)n_qblocks, (unsigned)a.n_slices), dim3(256),
+                     G::bytes, st, a);
   return hipGetLastError();
+}
+
+template <int D, int M>
+hipError_t launch_search(const SArgs& a, int n_qblocks, hipStream_t st) {
+  return a.norm_f16 ? launch_search_h<D, M, true>(a, n_qblocks, st) : launch_search_h<D, M, false>(a, n_qblocks, st);
 }
 
 }  // namespace
