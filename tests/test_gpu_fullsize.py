@@ -3,7 +3,8 @@
 - llama8b_decode, in the launch configuration bench.py times (batch 1, 32
   query heads over 8 KV heads, d = 128, 4 bits, 32768 cached tokens, the
   last one appended by tq_attn_decode_append, default split count): every
-  output, every logit and the appended records against the oracle.
+  output, every logit and the appended records against the oracle; again
+  with MSE-only V records and fp16 norms.
 - llama70b_long (batch 4, 64 query heads over 8 KV heads, 131072 tokens,
   3 bits): the 8192-token prefill chunk of every head quantized at once
   (sampled rows against the oracle), then a decode step over the full cache,
@@ -80,21 +81,27 @@ def _read_rows(tq, cache, dq, rows):
     info = tq.tq_record_layout(dq.layout)
     rows = np.asarray(rows, np.int64)
     nf = info.norm_floats
+    mse = bool(dq.layout.mse_only)
+
+    def sign_words(idx, w):  # (MSE-only records have none)
+        if w == 0:
+            return np.zeros((len(idx), 0), np.uint32)
+        return cache.signs.view(-1, w)[idx].cpu().numpy().view(np.uint32)
     if cache.fmt == tq.TQ_TOKEN_MAJOR:
         idx = torch.from_numpy(rows).cuda()
         codes = cache.codes.view(-1, info.code_words)[idx].cpu().numpy().view(np.uint32)
-        signs = cache.signs.view(-1, info.sign_words)[idx].cpu().numpy().view(np.uint32)
+        signs = sign_words(idx, info.sign_words)
         norms = cache.norms.view(-1, nf)[idx].cpu().numpy()
-        return recfmt.unpack_token_major(codes, signs, norms, dq.dims, dq.mse_bits)
+        return recfmt.unpack_token_major(codes, signs, norms, dq.dims, dq.mse_bits, mse)
     blocks = np.unique(rows // 32)
     bidx = torch.from_numpy(blocks).cuda()
     codes = cache.codes.view(-1, info.block_code_words)[bidx].cpu().numpy().view(np.uint32)
-    signs = cache.signs.view(-1, info.block_sign_words)[bidx].cpu().numpy().view(np.uint32)
+    signs = sign_words(bidx, info.block_sign_words)
     brows = (blocks[:, None] * 32 + np.arange(32)[None, :]).ravel()
     norms = cache.norms.view(-1, nf)[torch.from_numpy(brows).cuda()].cpu().numpy()
-    got = recfmt.unpack_block32(codes, signs, norms, dq.dims, dq.mse_bits)
+    got = recfmt.unpack_block32(codes, signs, norms, dq.dims, dq.mse_bits, mse)
     pos = np.searchsorted(blocks, rows // 32) * 32 + rows % 32
-    return tuple([a[pos] for a in part] for part in got)
+    return tuple([None if a is None else a[pos] for a in part] for part in got)
 
 
 def _random_fill(tq, cache, dq, n_rows, seed):
@@ -117,15 +124,19 @@ def _reference(wl, q64, b, h, k_deq, v_deq):
                                    wl.scale)
 
 
-def test_llama8b_decode_step_full_size(tq):
+@pytest.mark.parametrize("v_mse,f16", [(False, False), (True, True)])
+def test_llama8b_decode_step_full_size(tq, v_mse, f16):
+    # (v_mse, f16): MSE-only V records and fp16 norms in both caches, the
+    # record variants bench.py also times
     import torch
     from tests.test_gpu_decode import _oracle_side
     wl = synth.workload("llama8b_decode")
     B, HQ, H, d, N, cap = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.d, wl.n_ctx, wl.capacity
     assert (B, HQ, H, d, N) == (1, 32, 8, 128, 32768)
-    o = _oracle_side(wl, N, cap)
-    kq = tq.Quantizer.from_parts(o["ks"].rotations, o["ks"].sketches, o["bits"], perm=o["ks"].perm)
-    vq = tq.Quantizer.from_parts(o["vs"].rotations, o["vs"].sketches, o["bits"], perm=o["vs"].perm)
+    o = _oracle_side(wl, N, cap, v_mse=v_mse, k_f16=f16, v_f16=f16)
+    kq = tq.Quantizer.from_parts(o["ks"].rotations, o["ks"].sketches, o["bits"], perm=o["ks"].perm, norm_f16=f16)
+    vq = tq.Quantizer.from_parts(o["vs"].rotations, o["vs"].sketches, o["bits"], perm=o["vs"].perm,
+                                 mse_only=v_mse, norm_f16=f16)
     kc = gc.to_device_cache(kq, tq.TQ_TOKEN_MAJOR, B * H * cap, o["karr"])
     vc = gc.to_device_cache(vq, tq.TQ_BLOCK32, B * H * cap, o["varr"])
     t = N - 1  # the appended token of every (batch, kv head)
@@ -148,7 +159,8 @@ def test_llama8b_decode_step_full_size(tq):
     tq.tq_attn_decode(kq, vq, shape, q, kc, vc, logits=logits, out=out2)
     torch.cuda.synchronize()
     assert torch.equal(out, out2)
-    okq, ovq = oracle.Quantizer.from_spec(o["ks"]), oracle.Quantizer.from_spec(o["vs"])
+    okq = oracle.Quantizer.from_spec(o["ks"], norm_f16=f16)
+    ovq = oracle.Quantizer.from_spec(o["vs"], mse_only=v_mse, norm_f16=f16)
     kt, vt = o["k_t"].copy(), o["v_t"].copy()
     rows = np.arange(B * H) * cap + t
     for arr, x, qz, cache, dq in ((kt, kx, okq, kc, kq), (vt, vx, ovq, vc, vq)):
