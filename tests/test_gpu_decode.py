@@ -583,3 +583,25 @@ def test_fp16_norms_match_oracle(tq, name, over, n_ctx, cap, k_f16, v_f16, v_mse
     ok_o, wo = gc.normwise_close(out, ro) if with_v else (True, 0.0)
     print(name, over, n_ctx, k_f16, v_f16, v_mse, "logits", wl_, "out", wo)
     assert ok_l and ok_o, (wl_, wo)
+
+
+@pytest.mark.parametrize("v_mse", [False, True])
+def test_fp16_norm_reads_equal_float32_layout(tq, v_mse):
+    # records whose norms are float16 numbers, stored once as float16 and once
+    # as float32: the decode must give identical logits and outputs (the
+    # float16 read path only changes where the values come from)
+    import torch
+    wl = synth.workload("llama8b_decode", batch=2, n_q_heads=8, n_kv_heads=2)
+    n_ctx, cap = 3000, 3008
+    o = _oracle_side(wl, n_ctx, cap, v_mse=v_mse, k_f16=True, v_f16=True)
+    q = synth.draw_queries(wl)
+    res = []
+    for f16 in (True, False):
+        o2 = dict(o, k_f16=f16, v_f16=f16)
+        if not f16:
+            o2["karr"] = (o["karr"][0], o["karr"][1], o["karr"][2].astype(np.float32))
+            o2["varr"] = (o["varr"][0], o["varr"][1], o["varr"][2].astype(np.float32))
+        lg, out, _ = _device_decode(tq, wl, o2, n_ctx, cap, q=q)
+        res.append((lg, out))
+    assert np.array_equal(res[0][0], res[1][0])
+    assert np.array_equal(res[0][1], res[1][1])
