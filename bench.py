@@ -486,7 +486,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU layout "
-              "(head-sharded decode, no collective) is described in DESIGN.md and is not built here.")
+              "(head-sharded decode, no collective) is not built here.")
         sys.exit(2)
     import torch
     import kv_cache_vector_rotation_amd as tq

@@ -30,8 +30,8 @@ Sources, cited by title and section (the pages are web articles):
       stages, the second being a 1-bit QJL correction).
 
 Where the pages are silent the oracle takes a stated reading; each reading
-is listed in the design doc of the repository and cited in the function that
-relies on it.
+is stated in the module header and cited in the function that relies on
+it.
 
 Pins: every public function here is checked by ``tests/test_oracle_*.py``
 against closed forms, textbook limits, invariants, statistics or brute

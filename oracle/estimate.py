@@ -6,7 +6,7 @@ used to compute attention logits; [WD] "2. QJL Residual": the 1-bit sketch
 of the residual removes the bias of the inner product. The decode step then
 takes softmax(logits) times the dequantized values.
 
-Readings used here (each listed in the design doc):
+Readings used here (where the pages leave a step open; each is cited where it is used):
 * dequantized vector, per group:
       x~_g = n_g Pi_g^T c[idx] + alpha_g gamma_g S_g^T z,
   with z = 2 bit - 1 and alpha_g = sqrt(pi/2) / d_g. For S_g with iid

@@ -7,7 +7,7 @@ keeps one bit per coordinate of a Johnson-Lindenstrauss (Gaussian) sketch
 of it ([WD] "2. QJL Residual"); the stored record is the indices, the sign
 bits and the norm(s).
 
-Readings used here (each listed in the design doc):
+Readings used here (where the pages leave a step open; each is cited where it is used):
 * the rotation is a dense d_g x d_g orthogonal matrix Pi_g given as input;
 * the quantizer acts on the unit vector y = Pi_g x_g / ||x_g|| and the norm
   n_g = ||x_g|| is stored (the Beta law is a law of unit vectors);

@@ -7,7 +7,7 @@ codebooks). A query is compared with every database vector through the
 same inner-product estimator that gives the attention logits, and the best
 matches are kept.
 
-Readings used here (each listed in the design doc):
+Readings used here (where the pages leave a step open; each is cited where it is used):
 * score(q, i) = <q, x~_i>, with x~_i the dequantized database vector
   (``estimate.dequantize``; no scale factor);
 * the k best of a query are the k largest scores in decreasing order, equal
