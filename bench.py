@@ -63,6 +63,7 @@ def parse():
     ap.add_argument("--no-bf16-baseline", action="store_true")
     ap.add_argument("--no-search", action="store_true")
     ap.add_argument("--no-chunk", action="store_true", help="skip the prefill-chunk and paged-cache legs")
+    ap.add_argument("--no-mixed", action="store_true", help="skip the fractional-width (batch 16) legs")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the record-variant legs (MSE-only V, fp16 norms)")
     ap.add_argument("--ctx-sweep", default="",
@@ -86,12 +87,23 @@ def _threads():
         return 8
 
 
-def build_caches(tq, torch, wl, kq, vq, prefix, cap):
-    """Quantize tokens [0, prefix) of every (b, h) into fresh caches (untimed)."""
+def build_caches(tq, torch, wl, kq, vq, prefix, cap, device_fill=False):
+    """Quantize tokens [0, prefix) of every (b, h) into fresh caches (untimed);
+    device_fill: the tokens are N(0, 1) bf16 vectors drawn on the device (for
+    large batches, where drawing the synthetic slabs on the host is slow)."""
     B, H = wl.batch, wl.n_kv_heads
     kc = tq.Cache.empty(kq, B * H * cap, tq.TQ_TOKEN_MAJOR)
     vc = tq.Cache.empty(vq, B * H * cap, tq.TQ_BLOCK32)
     if prefix == 0:
+        return kc, vc
+    if device_fill:
+        g = torch.Generator(device="cuda")
+        g.manual_seed(wl.seed)
+        for b in range(B):
+            for qz, cache, fmt in ((kq, kc, tq.TQ_TOKEN_MAJOR), (vq, vc, tq.TQ_BLOCK32)):
+                x = torch.randn((H * prefix, wl.d), generator=g, device="cuda").to(torch.bfloat16)
+                tq.tq_quantize(qz, fmt, x, cache, seg_len=prefix, seg_stride=cap, seg_offset=b * H * cap)
+        torch.cuda.synchronize()
         return kc, vc
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     pairs = [(b, h) for b in range(B) for h in range(H)]
@@ -257,13 +269,13 @@ def search_bench(tq, torch, reps=5):
             "frac": round(tf / PEAK_FP16_MFMA_TFLOPS, 4), "recall_at_10": hits / (n_q * k)}
 
 
-def compressed_step_us(tq, torch, wl, kq, vq, n_copies, reps=20, T=1):
+def compressed_step_us(tq, torch, wl, kq, vq, n_copies, reps=20, T=1, device_fill=False):
     """Mean time of tq_attn_decode_append steps (graph of one step per cache
     copy, replayed), in microseconds. T > 1: a causal chunk of T query tokens
     per head (the workload's last T tokens are the ones appended)."""
     B, HQ, H, N, cap = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.n_ctx, wl.capacity
     prefix = N - wl.n_new
-    kc0, vc0 = build_caches(tq, torch, wl, kq, vq, prefix, cap)
+    kc0, vc0 = build_caches(tq, torch, wl, kq, vq, prefix, cap, device_fill)
     caches = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(n_copies - 1)]
     k_new, v_new = new_tokens(torch, wl, prefix)
     if T == 1:
@@ -328,6 +340,32 @@ def variants_bench(tq, torch):
         us = compressed_step_us(tq, torch, wl, kq, vq, copies)
         out[name] = {"us_per_step": round(us, 2), "cached_tokens_per_s": wl.batch * wl.n_ctx / (us / 1e6),
                      "record_bytes_per_token": {"K": rb_k, "V": rb_v}, "cache_copies": copies}
+    return out
+
+
+def mixed_bench(tq, torch):
+    """Secondary figures: the fused decode step of the fractional-width
+    workloads (batch 16, 32 query / 8 KV heads, 32768 tokens, two channel
+    groups of 64 with their own codebooks), over at least 1 GiB of cache
+    copies; the step's algorithmic bytes (every K and V record once) over its
+    time, against the HBM peak."""
+    out = {}
+    for name in ("mixed_3p5", "mixed_2p5"):
+        wl = synth.workload(name)
+        ks, vs = synth.draw_quantizer(wl, "K"), synth.draw_quantizer(wl, "V")
+        bits = [g.mse_bits for g in ks.groups]
+        dims = [g.dim for g in ks.groups]
+        kq = tq.Quantizer.from_parts(ks.rotations, ks.sketches, bits, perm=ks.perm)
+        vq = tq.Quantizer.from_parts(vs.rotations, vs.sketches, bits, perm=vs.perm)
+        rb = record_bytes(dims, bits)
+        step_bytes = wl.batch * wl.n_kv_heads * wl.n_ctx * 2 * rb
+        copies = max(1, math.ceil((1 << 30) / (wl.batch * wl.n_kv_heads * wl.capacity * 2 * rb)))
+        us = compressed_step_us(tq, torch, wl, kq, vq, copies, device_fill=True)
+        out[name] = {"us_per_step": round(us, 2), "cached_tokens_per_s": wl.batch * wl.n_ctx / (us / 1e6),
+                     "record_bytes_per_token": rb, "step_gbs": round(step_bytes / us / 1e3, 1),
+                     "frac_of_hbm_peak": round(step_bytes / us / 1e3 / PEAK_HBM_GBS, 4), "cache_copies": copies,
+                     "cache_fill": "device-drawn N(0,1) bf16 tokens"}
+        torch.cuda.empty_cache()
     return out
 
 
@@ -650,6 +688,9 @@ def main():
         log(f"chunk: {result['chunk']}")
         result["paged"] = paged_bench(tq, torch)
         log(f"paged: {result['paged']}")
+    if not args.no_mixed:
+        result["mixed"] = mixed_bench(tq, torch)
+        log(f"mixed: {result['mixed']}")
     if not args.no_variants:
         result["variants"] = variants_bench(tq, torch)
         log(f"variants: {result['variants']}")

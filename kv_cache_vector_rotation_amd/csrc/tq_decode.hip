@@ -743,10 +743,15 @@ __global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
           u32x4 w;
-          const int sel = role == 1 ? 1 : 0;
+          // (a select of two constant indices: an index that depends on the
+          // lane would be lowered to a search over the whole array)
+          const bool r1 = role == 1;
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            w[q] = h2bits(pp[2 * q] * vn[2 * q][2 * g + sel], pp[2 * q + 1] * vn[2 * q + 1][2 * g + sel]);
+          for (int q = 0; q < 4; ++q) {
+            const float n0 = r1 ? vn[2 * q][2 * g + 1] : vn[2 * q][2 * g];
+            const float n1 = r1 ? vn[2 * q + 1][2 * g + 1] : vn[2 * q + 1][2 * g];
+            w[q] = h2bits(pp[2 * q] * n0, pp[2 * q + 1] * n1);
+          }
           pr[g] = role == 0 ? w : z;
           pz[g] = role == 1 ? w : z;
         }
