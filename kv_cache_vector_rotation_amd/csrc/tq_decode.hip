@@ -924,24 +924,28 @@ __global__ __launch_bounds__(256) void prep_kernel(tqp::PrepArgs p) {
 // ---------------------------------------------------------------------------
 constexpr int kMaxSplit = 1024;
 
-// 1024 threads per block: the split sums are cut four ways across thread
-// groups and the back-transform 32 ways (rows of [rot; sketch]), both
-// finished through LDS.
+// NTHR threads per block: 1024 for a few heads (the split sums cut four ways
+// across thread groups and the back-transform 32 ways, rows of [rot;
+// sketch], both finished through LDS), 256 for many heads (chunks of query
+// tokens, large batches), where more blocks resident per compute unit
+// overlap more heads' chains of dependent reductions.
 constexpr int kCombThreads = 1024;
+constexpr int kCombThreadsMany = 256;
+constexpr int kCombManyHeads = 128;  // more heads than this: the 256-thread blocks
 constexpr int kCombCols = 4;
 
 // Heads are ordered (batch, q head, query token); out rows are (batch, query
 // token, q head) (the same order when T = 1).
-template <int D>
-__global__ __launch_bounds__(kCombThreads) void combine_kernel(const float* part, int n_split,
+template <int D, int NTHR>
+__global__ __launch_bounds__(NTHR) void combine_kernel(const float* part, int n_split,
                                                                const float* rot, const float* sketch,
                                                                int group_dim0, int T, int hq, float* out) {
-  constexpr int NW = kCombThreads / 64, NG = kCombThreads / (2 * D);  // waves, groups
+  constexpr int NW = NTHR / 64, NG = NTHR / (2 * D);  // waves, groups
   constexpr int PS = 2 + 2 * D;                                      // floats per partial
   constexpr int OC = D / kCombCols;                                  // outputs per block
-  constexpr int RP = kCombThreads / OC;                              // row parts of [rot; sketch]
+  constexpr int RP = NTHR / OC;                              // row parts of [rot; sketch]
   constexpr int JR = 2 * D / RP;                                     // rows per part
-  static_assert(JR * RP == 2 * D && D % JR == 0, "combine shape");
+  static_assert(JR * RP == 2 * D && D % JR == 0 && NG >= 1, "combine shape");
   __shared__ float s_w[kMaxSplit];
   __shared__ float s_part[NG][2 * D];
   __shared__ float s_acc[2 * D];
@@ -964,7 +968,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const float* part
   for (int j = 0; j < JR; ++j) mv[j] = mat[(int64_t)j * D];
   // max over splits (log2 domain)
   float mx = -INFINITY;
-  for (int s = t; s < n_split; s += kCombThreads) mx = fmaxf(mx, P[(int64_t)s * PS]);
+  for (int s = t; s < n_split; s += NTHR) mx = fmaxf(mx, P[(int64_t)s * PS]);
   for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
   if (lane == 0) s_red[wv] = mx;
   __syncthreads();
@@ -974,7 +978,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const float* part
   __syncthreads();
   // split weights and the total sum
   float lsum = 0.f;
-  for (int s = t; s < n_split; s += kCombThreads) {
+  for (int s = t; s < n_split; s += NTHR) {
     const float ms = P[(int64_t)s * PS];
     const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
     s_w[s] = w;
@@ -1306,9 +1310,12 @@ tq_status run_phases(const Plan& pl, unsigned phases, hipStream_t st) {
   }
   if (pl.with_v && (phases & TQ_PHASE_COMBINE)) {
     (void)hipGetLastError();  // a launch error is reported below, not an older one
-    hipLaunchKernelGGL((combine_kernel<D>), dim3(pl.n_heads, kCombCols), dim3(kCombThreads), 0, st, pl.a.part,
-                       pl.a.n_split,
-                       pl.vrot, pl.vsketch, pl.group_dim0, pl.T, pl.hq_orig, pl.out);
+    if (pl.n_heads > kCombManyHeads)
+      hipLaunchKernelGGL((combine_kernel<D, kCombThreadsMany>), dim3(pl.n_heads, kCombCols), dim3(kCombThreadsMany),
+                         0, st, pl.a.part, pl.a.n_split, pl.vrot, pl.vsketch, pl.group_dim0, pl.T, pl.hq_orig, pl.out);
+    else
+      hipLaunchKernelGGL((combine_kernel<D, kCombThreads>), dim3(pl.n_heads, kCombCols), dim3(kCombThreads), 0, st,
+                         pl.a.part, pl.a.n_split, pl.vrot, pl.vsketch, pl.group_dim0, pl.T, pl.hq_orig, pl.out);
     if (hipGetLastError() != hipSuccess) return TQ_ERR_DEVICE;
   }
   return TQ_OK;
