@@ -820,7 +820,7 @@ __device__ __forceinline__ void quantize_tiles(const QArgs& a, int64_t first_til
 // call), so each touched word takes this vector's bits by an atomic AND
 // (clear) and an atomic OR (set) on exactly those bits.
 // ---------------------------------------------------------------------------
-constexpr int kSmallMaxVec = 64;    // calls with at most this many vectors take this path
+constexpr int kSmallMaxVec = 512;   // calls with at most this many vectors take this path
 constexpr int kSmallThreads = 512;
 constexpr int kSmallWords = 768;    // record words assembled in LDS
 

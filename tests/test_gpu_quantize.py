@@ -167,7 +167,8 @@ def test_empty_call_is_noop(tq):
     assert int(cache.codes.abs().sum()) == 0
 
 
-# Calls with at most 64 vectors take the one-workgroup-per-vector path.
+# Calls with at most SMALL_MAX vectors take the one-workgroup-per-vector path.
+SMALL_MAX = 512
 SMALL_CASES = [
     # name, overrides, kind, format, dtype, n_vec
     ("llama8b_decode", {}, "K", "TQ_TOKEN_MAJOR", "bf16", 1),
@@ -233,22 +234,24 @@ def test_few_vectors_unaligned_rows(tq):
 
 
 def test_few_vectors_agree_with_tiles(tq):
-    # the same 64 vectors through the few-vector path (one call) and the tile
-    # path (inside a 65-vector call): equal records up to the boundary rule
+    # the same SMALL_MAX vectors through the few-vector path (one call) and the
+    # tile path (inside a call with one vector more): equal records up to the
+    # boundary rule
     import torch
     wl = synth.workload("llama8b_decode")
     spec = synth.draw_quantizer(wl, "K")
-    x = synth.draw_kv_slab(wl, "K", 0, 4, 0, 65)
+    n = SMALL_MAX
+    x = synth.draw_kv_slab(wl, "K", 0, 4, 0, n + 1)
     oq, dq = gc.quantizers(spec)
     xt = torch.from_numpy(x).cuda().to(torch.bfloat16)
-    a = tq.Cache.empty(dq, 96, tq.TQ_TOKEN_MAJOR)
-    b = tq.Cache.empty(dq, 96, tq.TQ_TOKEN_MAJOR)
-    tq.tq_quantize(dq, tq.TQ_TOKEN_MAJOR, xt[:64], a, seg_len=64, seg_stride=64)
-    tq.tq_quantize(dq, tq.TQ_TOKEN_MAJOR, xt, b, seg_len=65, seg_stride=65)
+    a = tq.Cache.empty(dq, n + 32, tq.TQ_TOKEN_MAJOR)
+    b = tq.Cache.empty(dq, n + 32, tq.TQ_TOKEN_MAJOR)
+    tq.tq_quantize(dq, tq.TQ_TOKEN_MAJOR, xt[:n], a, seg_len=n, seg_stride=n)
+    tq.tq_quantize(dq, tq.TQ_TOKEN_MAJOR, xt, b, seg_len=n + 1, seg_stride=n + 1)
     torch.cuda.synchronize()
-    ca, cb = (c.codes.cpu().numpy().reshape(96, -1)[:64] for c in (a, b))
-    sa, sb = (c.signs.cpu().numpy().reshape(96, -1)[:64] for c in (a, b))
-    na, nb = (c.norms.cpu().numpy().reshape(96, -1)[:64] for c in (a, b))
+    ca, cb = (c.codes.cpu().numpy().reshape(n + 32, -1)[:n] for c in (a, b))
+    sa, sb = (c.signs.cpu().numpy().reshape(n + 32, -1)[:n] for c in (a, b))
+    na, nb = (c.norms.cpu().numpy().reshape(n + 32, -1)[:n] for c in (a, b))
     assert np.mean(np.all(ca == cb, axis=1) & np.all(sa == sb, axis=1)) >= 0.95
     # norms n to 1e-6 relative, residual norms gamma to 2e-6 n (the record rule)
     assert np.all(np.abs(na[:, 0] - nb[:, 0]) <= 1e-6 * nb[:, 0])
@@ -256,16 +259,18 @@ def test_few_vectors_agree_with_tiles(tq):
 
 
 # MSE-only records (stage one alone): codes and norms, no sign words; the
-# tile path (more than 64 vectors) and the few-vector path, both formats,
+# tile path (more than SMALL_MAX vectors) and the few-vector path, both formats,
 # scattered rows (partial 32-row blocks) into a cache pre-filled with ones.
 MSE_ONLY_CASES = [
     # name, kind, format, dtype, n_vec
+    ("llama8b_decode", "V", "TQ_BLOCK32", "bf16", 600),
     ("llama8b_decode", "V", "TQ_BLOCK32", "bf16", 300),
     ("llama8b_decode", "V", "TQ_BLOCK32", "bf16", 1),
     ("mixed_3p5", "V", "TQ_BLOCK32", "bf16", 17),
     ("mixed_3p5", "V", "TQ_TOKEN_MAJOR", "bf16", 700),
     ("tiny", "K", "TQ_TOKEN_MAJOR", "f32", 40),
     ("tiny", "K", "TQ_BLOCK32", "f32", 129),
+    ("tiny", "K", "TQ_BLOCK32", "f32", 1029),
 ]
 
 
@@ -302,6 +307,7 @@ F16_CASES = [
     # name, kind, format, dtype, n_vec, mse_only
     ("llama8b_decode", "K", "TQ_TOKEN_MAJOR", "bf16", 1, False),
     ("llama8b_decode", "V", "TQ_BLOCK32", "bf16", 300, False),
+    ("llama8b_decode", "V", "TQ_BLOCK32", "bf16", 600, False),
     ("mixed_3p5", "K", "TQ_TOKEN_MAJOR", "bf16", 700, False),
     ("mixed_3p5", "V", "TQ_BLOCK32", "bf16", 17, True),
     ("tiny", "K", "TQ_BLOCK32", "f32", 129, True),
