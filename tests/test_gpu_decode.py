@@ -391,7 +391,7 @@ def _paged_arrays(tq, o, B, H, cap, n_pblocks, table):
     """Scatter the contiguous oracle caches of _oracle_side into a paged
     layout: logical block j of batch b -> physical block table[b, j]."""
     import kv_cache_vector_rotation_amd as m
-    cw, sw, nf, bcw, bsw = oracle.record_words(o["dims"], o["bits"])
+    cw, sw, nf, bcw, bsw = oracle.record_words(o["dims"], o["bits"], o["v_mse"])
     kc, ks_, kn = (a.reshape(B * H * cap, -1) for a in o["karr"])
     vc, vs_, vn = o["varr"]
     vc = vc.reshape(B * H * cap // 32, bcw)
@@ -415,11 +415,12 @@ def _paged_arrays(tq, o, B, H, cap, n_pblocks, table):
     return tuple(a.ravel() for a in pk), tuple(a.ravel() for a in pv), rows
 
 
-def _paged_setup(tq, wl, n_ctx, cap, seed=3):
+def _paged_setup(tq, wl, n_ctx, cap, seed=3, v_mse=False, f16=False):
     B, H = wl.batch, wl.n_kv_heads
-    o = _oracle_side(wl, n_ctx, cap)
-    kq = tq.Quantizer.from_parts(o["ks"].rotations, o["ks"].sketches, o["bits"], perm=o["ks"].perm)
-    vq = tq.Quantizer.from_parts(o["vs"].rotations, o["vs"].sketches, o["bits"], perm=o["vs"].perm)
+    o = _oracle_side(wl, n_ctx, cap, v_mse=v_mse, k_f16=f16, v_f16=f16)
+    kq = tq.Quantizer.from_parts(o["ks"].rotations, o["ks"].sketches, o["bits"], perm=o["ks"].perm, norm_f16=f16)
+    vq = tq.Quantizer.from_parts(o["vs"].rotations, o["vs"].sketches, o["bits"], perm=o["vs"].perm,
+                                 mse_only=v_mse, norm_f16=f16)
     mb = cap // 32
     n_pblocks = B * mb + 5  # a few physical blocks that no sequence uses
     table = np.random.default_rng(seed).permutation(n_pblocks)[:B * mb].reshape(B, mb).astype(np.int32)
@@ -429,13 +430,15 @@ def _paged_setup(tq, wl, n_ctx, cap, seed=3):
     return o, kq, vq, kc, vc, table
 
 
-def test_paged_cache_equals_contiguous(tq):
+@pytest.mark.parametrize("v_mse,f16", [(False, False), (True, True)])
+def test_paged_cache_equals_contiguous(tq, v_mse, f16):
     # the same records in a block-table layout give the same outputs and
-    # logits, bit for bit, as the contiguous cache
+    # logits, bit for bit, as the contiguous cache (also with MSE-only V
+    # records and fp16 norms)
     import torch
     wl = synth.workload("llama8b_decode", batch=3, n_q_heads=8, n_kv_heads=2)
     n_ctx, cap = 1000, 1024
-    o, kq, vq, kc, vc, table = _paged_setup(tq, wl, n_ctx, cap)
+    o, kq, vq, kc, vc, table = _paged_setup(tq, wl, n_ctx, cap, v_mse=v_mse, f16=f16)
     q = torch.from_numpy(synth.draw_queries(wl)).cuda().to(torch.bfloat16)
     shape = tq.decode_shape(3, 8, 2, n_ctx, cap, wl.scale)
     res = []
