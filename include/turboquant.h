@@ -100,7 +100,8 @@ typedef struct {
                            1: as float16 (rounded to nearest even from float32;
                            32 bits per group instead of 64). fp16 norms need
                            every n_g below 65504 and lose relative precision
-                           below 6.1e-5 (subnormals). */
+                           below 6.1e-5 (subnormals). Every entry point takes
+                           either form, for K and V independently. */
 } tq_layout;
 
 /* One quantizer instance (one for K, one for V). All pointers are device
