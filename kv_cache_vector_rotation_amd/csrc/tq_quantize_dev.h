@@ -177,7 +177,10 @@ __device__ __forceinline__ void mfma_tiles(const float* xr, const float (&b)[KPG
 template <int KP, int NT>
 struct Lds {
   static constexpr int XS = KP + 4;  // row stride of the fp32 tile, in floats
-  static constexpr int DP = NT * 16;
+  // row stride of the code and sign bytes: 4 bytes of padding put the rows
+  // that one byte store spans (four vectors, 4 DP bytes apart) in different
+  // LDS banks
+  static constexpr int DP = NT * 16 + 4;
   static constexpr int off_x = 0;                                   // float [QT][XS]
   static constexpr int off_code = off_x + QT * XS * 4;              // u8 [QT][DP]
   static constexpr int off_sign = off_code + QT * DP;               // u8 [QT][DP]
