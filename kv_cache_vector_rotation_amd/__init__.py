@@ -231,6 +231,53 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else int(t.data_ptr())
 
 
+def _dev(t, name: str, dtypes, device=None, numel: Optional[int] = None,
+         min_numel: Optional[int] = None, optional: bool = False) -> Optional[int]:
+    """Device address of tensor ``t`` after checking what the C ABI cannot:
+    its dtype, contiguity and size, that it lives on the GPU, and that it is
+    on ``device`` (the call's device). Raises ValueError otherwise."""
+    torch = _torch()
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    dts = dtypes if isinstance(dtypes, (tuple, list)) else (dtypes,)
+    if t.dtype not in dts:
+        raise ValueError(f"{name} must have dtype {' or '.join(str(d) for d in dts)}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements, got {t.numel()}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name} must hold at least {min_numel} elements, got {t.numel()}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the call's tensors are on {device}")
+    return int(t.data_ptr())
+
+
+def _call_device(t, name: str):
+    """The device of the call's leading tensor, which must be the current
+    device (kernels are launched there)."""
+    torch = _torch()
+    if t is None or not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}, but the current device is cuda:{torch.cuda.current_device()}")
+    return t.device
+
+
+def _qdtype(t, name: str) -> int:
+    torch = _torch()
+    dt = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}.get(getattr(t, "dtype", None))
+    if dt is None:
+        raise ValueError(f"{name} must be float32 or bfloat16")
+    return dt
+
+
 def _stream(stream) -> Optional[int]:
     torch = _torch()
     s = torch.cuda.current_stream() if stream is None else stream
@@ -284,14 +331,24 @@ class Quantizer:
                          sketch_rot=to(skr), centroids=to(np.concatenate(cents)),
                          boundaries=to(np.concatenate(bnds)))
 
-    def struct(self) -> tq_quantizer:
+    def struct(self, device=None) -> tq_quantizer:
+        """The ABI struct; with ``device`` the tensors are checked first
+        (float32, contiguous, sizes of the layout, on that device)."""
         q = tq_quantizer()
         q.layout = self.layout
-        q.rot = _ptr(self.rot)
-        q.sketch = _ptr(self.sketch)
-        q.sketch_rot = _ptr(self.sketch_rot)
-        q.centroids = _ptr(self.centroids)
-        q.boundaries = _ptr(self.boundaries)
+        if device is None:
+            q.rot, q.sketch, q.sketch_rot = _ptr(self.rot), _ptr(self.sketch), _ptr(self.sketch_rot)
+            q.centroids, q.boundaries = _ptr(self.centroids), _ptr(self.boundaries)
+            return q
+        torch = _torch()
+        d = int(self.layout.d)
+        nc = sum(1 << m for m in self.mse_bits)
+        q.rot = _dev(self.rot, "quantizer.rot", torch.float32, device, numel=d * d)
+        q.sketch = _dev(self.sketch, "quantizer.sketch", torch.float32, device, numel=d * d)
+        q.sketch_rot = _dev(self.sketch_rot, "quantizer.sketch_rot", torch.float32, device, numel=d * d)
+        q.centroids = _dev(self.centroids, "quantizer.centroids", torch.float32, device, numel=nc)
+        q.boundaries = _dev(self.boundaries, "quantizer.boundaries", torch.float32, device,
+                            numel=nc - len(self.mse_bits))
         return q
 
 
@@ -321,12 +378,28 @@ class Cache:
         norms = torch.zeros(n_rows * info.norm_floats, dtype=ndt, device=device)
         return Cache(fmt=fmt, n_rows=n_rows, codes=codes, signs=signs, norms=norms)
 
-    def struct(self) -> tq_cache:
+    def struct(self, quantizer: Optional["Quantizer"] = None, device=None) -> tq_cache:
+        """The ABI struct; with ``quantizer`` and ``device`` the tensors are
+        checked first (int32 words and float32 / float16 norms as the layout
+        says, large enough for n_rows records, on that device)."""
         c = tq_cache()
-        c.codes = _ptr(self.codes)
-        c.signs = _ptr(self.signs)
-        c.norms = _ptr(self.norms)
         c.n_rows = int(self.n_rows)
+        if quantizer is None:
+            c.codes, c.signs, c.norms = _ptr(self.codes), _ptr(self.signs), _ptr(self.norms)
+            return c
+        torch = _torch()
+        info = tq_record_layout(quantizer.layout)
+        if self.fmt == TQ_BLOCK32:
+            if self.n_rows % 32:
+                raise ValueError("a TQ_BLOCK32 cache needs a multiple of 32 rows")
+            nw_c, nw_s = self.n_rows // 32 * info.block_code_words, self.n_rows // 32 * info.block_sign_words
+        else:
+            nw_c, nw_s = self.n_rows * info.code_words, self.n_rows * info.sign_words
+        ndt = torch.float16 if quantizer.layout.norm_f16 else torch.float32
+        c.codes = _dev(self.codes, "cache.codes", torch.int32, device, min_numel=nw_c)
+        c.signs = (_dev(self.signs, "cache.signs", torch.int32, device, min_numel=nw_s) if nw_s
+                   else (None if self.signs is None or self.signs.numel() == 0 else _ptr(self.signs)))
+        c.norms = _dev(self.norms, "cache.norms", ndt, device, min_numel=self.n_rows * info.norm_floats)
         return c
 
     def clone(self) -> "Cache":
@@ -345,22 +418,42 @@ def decode_shape(batch: int, n_q_heads: int, n_kv_heads: int, n_ctx: int, capaci
 # Device entry points
 # ---------------------------------------------------------------------------
 
+def _x_rows(x, name: str, d: int, device=None):
+    """(address, dtype code, n_vec, row stride) of a [n_vec, >= d] input."""
+    torch = _torch()
+    if not isinstance(x, torch.Tensor) or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D tensor with unit stride along the channels")
+    dt = _qdtype(x, name)
+    if x.shape[1] < d or (x.shape[0] > 1 and x.stride(0) < d):
+        raise ValueError(f"{name} rows must hold at least d = {d} channels")
+    if not x.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and x.device != device:
+        raise ValueError(f"{name} is on {x.device}, the call's tensors are on {device}")
+    return int(x.data_ptr()), dt, int(x.shape[0]), int(x.stride(0))
+
+
+def _rows_ptr(dst_rows, n_vec: int, device):
+    torch = _torch()
+    return _dev(dst_rows, "dst_rows", torch.int64, device, numel=n_vec, optional=True)
+
+
 def tq_quantize(quantizer: Quantizer, fmt: int, x, cache: Cache, dst_rows=None, seg_len: int = 1,
                 seg_stride: int = 1, seg_offset: int = 0, stream=None) -> None:
     """Quantize the rows of x ([n_vec, >= d], float32 or bfloat16, on the GPU)
-    into ``cache``. Rows: dst_rows (int64 device tensor) if given, else
+    into ``cache``. Rows: dst_rows (int64 device tensor [n_vec]) if given, else
     (i // seg_len) * seg_stride + seg_offset + i % seg_len."""
-    torch = _torch()
-    if x.dim() != 2 or x.stride(1) != 1:
-        raise ValueError("x must be a 2-D tensor with unit stride along the channels")
-    dt = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}[x.dtype]
+    dev = _call_device(x, "x")
+    xp, dt, n_vec, stride = _x_rows(x, "x", int(quantizer.layout.d), dev)
+    if cache.fmt != fmt:
+        raise ValueError("cache.fmt differs from fmt")
     rows = tq_rows()
-    rows.dst_rows = _ptr(dst_rows)
+    rows.dst_rows = _rows_ptr(dst_rows, n_vec, dev)
     rows.seg_len, rows.seg_stride, rows.seg_offset = seg_len, seg_stride, seg_offset
-    q = quantizer.struct()
-    c = cache.struct()
-    _check(lib().tq_quantize(C.byref(q), fmt, _ptr(x), dt, x.shape[0], x.stride(0), C.byref(rows),
-                             C.byref(c), _stream(stream)), "tq_quantize")
+    q = quantizer.struct(dev)
+    c = cache.struct(quantizer, dev)
+    _check(lib().tq_quantize(C.byref(q), fmt, xp, dt, n_vec, stride, C.byref(rows), C.byref(c),
+                             _stream(stream)), "tq_quantize")
 
 
 def tq_attn_decode_workspace_bytes(kq: Quantizer, vq: Optional[Quantizer], shape: tq_decode_shape) -> int:
@@ -371,6 +464,41 @@ def tq_attn_decode_workspace_bytes(kq: Quantizer, vq: Optional[Quantizer], shape
                                                 C.byref(shape), C.byref(n)),
            "tq_attn_decode_workspace_bytes")
     return int(n.value)
+
+
+def _decode_args(kq: Quantizer, vq: Optional[Quantizer], shape: tq_decode_shape, q, k_cache: Cache,
+                 v_cache: Optional[Cache], logits, out):
+    """Checked ABI arguments shared by the decode wrappers: (device, q address,
+    q dtype, kq struct, vq struct or None, K cache struct, V cache struct or
+    None, logits address, out address)."""
+    torch = _torch()
+    dev = _call_device(q, "q")
+    T = max(1, int(shape.n_q_tokens))
+    B, HQ, d = int(shape.batch), int(shape.n_q_heads), int(kq.layout.d)
+    dt = _qdtype(q, "q")
+    qp = _dev(q, "q", (torch.float32, torch.bfloat16), dev, numel=B * T * HQ * d)
+    if k_cache.fmt != TQ_TOKEN_MAJOR:
+        raise ValueError("k_cache must be a TQ_TOKEN_MAJOR cache")
+    kqs, kc = kq.struct(dev), k_cache.struct(kq, dev)
+    vqs = vc = None
+    if vq is not None:
+        if v_cache is None or v_cache.fmt != TQ_BLOCK32:
+            raise ValueError("v_cache must be a TQ_BLOCK32 cache when vq is given")
+        vqs, vc = vq.struct(dev), v_cache.struct(vq, dev)
+    lp = _dev(logits, "logits", torch.float32, dev, numel=B * HQ * T * int(shape.n_ctx), optional=True)
+    op = _dev(out, "out", torch.float32, dev, numel=B * T * HQ * d, optional=True)
+    return dev, qp, dt, kqs, vqs, kc, vc, lp, op
+
+
+def _workspace(workspace, kq, vq, shape, dev):
+    torch = _torch()
+    if workspace is None:
+        workspace = torch.empty(tq_attn_decode_workspace_bytes(kq, vq, shape), dtype=torch.uint8, device=dev)
+    return _dev(workspace, "workspace", torch.uint8, dev), workspace.numel()
+
+
+def _ref(x):
+    return C.byref(x) if x is not None else None
 
 
 def tq_attn_decode(kq: Quantizer, vq: Optional[Quantizer], shape: tq_decode_shape, q,
@@ -388,40 +516,42 @@ def tq_attn_decode_phases(phases: int, kq: Quantizer, vq: Optional[Quantizer], s
                           workspace=None, stream=None) -> None:
     """The stages of tq_attn_decode selected by ``phases`` (TQ_PHASE_* bits);
     stages share state through ``workspace``, which must then be given."""
-    torch = _torch()
-    if not q.is_contiguous():
-        raise ValueError("q must be contiguous")
-    dt = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}[q.dtype]
-    if workspace is None:
-        workspace = torch.empty(tq_attn_decode_workspace_bytes(kq, vq, shape), dtype=torch.uint8,
-                                device=q.device)
-    kqs = kq.struct()
-    vqs = vq.struct() if vq is not None else None
-    kc = k_cache.struct()
-    vc = v_cache.struct() if v_cache is not None else None
-    _check(lib().tq_attn_decode_phases(phases, C.byref(kqs), C.byref(vqs) if vqs is not None else None,
-                                       C.byref(shape), _ptr(q), dt, C.byref(kc),
-                                       C.byref(vc) if vc is not None else None, _ptr(logits), _ptr(out),
-                                       _ptr(workspace), workspace.numel(), _stream(stream)),
+    dev, qp, dt, kqs, vqs, kc, vc, lp, op = _decode_args(kq, vq, shape, q, k_cache, v_cache, logits, out)
+    wp, wn = _workspace(workspace, kq, vq, shape, dev)
+    _check(lib().tq_attn_decode_phases(phases, C.byref(kqs), _ref(vqs), C.byref(shape), qp, dt, C.byref(kc),
+                                       _ref(vc), lp, op, wp, wn, _stream(stream)),
            "tq_attn_decode")
 
 
 def append_spec(x, dst_rows=None, seg_len: int = 1, seg_stride: int = 1, seg_offset: int = 0) -> tq_append:
     """Vectors to append within tq_attn_decode_append: the rows of x ([n_vec,
-    >= d] float32/bfloat16 on the GPU) go to dst_rows, or by segments as in
-    tq_quantize. The returned struct keeps a reference to its tensors."""
+    >= d] float32/bfloat16 on the GPU) go to dst_rows (int64 [n_vec]), or by
+    segments as in tq_quantize. The returned struct keeps a reference to its
+    tensors; tq_attn_decode_append checks them against its quantizers."""
     torch = _torch()
-    if x.dim() != 2 or x.stride(1) != 1:
+    if not isinstance(x, torch.Tensor) or x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be a 2-D tensor with unit stride along the channels")
     a = tq_append()
     a.x = _ptr(x)
-    a.dtype = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}[x.dtype]
+    a.dtype = _qdtype(x, "x")
     a.n_vec = x.shape[0]
     a.x_row_stride = x.stride(0)
     a.rows.dst_rows = _ptr(dst_rows)
     a.rows.seg_len, a.rows.seg_stride, a.rows.seg_offset = seg_len, seg_stride, seg_offset
     a._keep = (x, dst_rows)
     return a
+
+
+def _check_append(a: Optional[tq_append], name: str, qz: Optional[Quantizer], dev) -> None:
+    if a is None:
+        return
+    if qz is None:
+        raise ValueError(f"{name} needs its quantizer")
+    x, dst_rows = getattr(a, "_keep", (None, None))
+    if x is None:
+        raise ValueError(f"{name} must come from append_spec")
+    _x_rows(x, f"{name}.x", int(qz.layout.d), dev)
+    _rows_ptr(dst_rows, int(x.shape[0]), dev)
 
 
 def tq_attn_decode_append(kq: Quantizer, vq: Optional[Quantizer], shape: tq_decode_shape, q,
@@ -431,23 +561,12 @@ def tq_attn_decode_append(kq: Quantizer, vq: Optional[Quantizer], shape: tq_deco
     """Appends k_new / v_new (append_spec structs, or None) to the caches and
     runs the decode step over them, as one launch for the appends and the
     query preparation followed by the split-K pass and the combine."""
-    torch = _torch()
-    if not q.is_contiguous():
-        raise ValueError("q must be contiguous")
-    dt = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}[q.dtype]
-    if workspace is None:
-        workspace = torch.empty(tq_attn_decode_workspace_bytes(kq, vq, shape), dtype=torch.uint8,
-                                device=q.device)
-    kqs = kq.struct()
-    vqs = vq.struct() if vq is not None else None
-    kc = k_cache.struct()
-    vc = v_cache.struct() if v_cache is not None else None
-    _check(lib().tq_attn_decode_append(C.byref(kqs), C.byref(vqs) if vqs is not None else None,
-                                       C.byref(shape), C.byref(k_new) if k_new is not None else None,
-                                       C.byref(v_new) if v_new is not None else None, _ptr(q), dt,
-                                       C.byref(kc), C.byref(vc) if vc is not None else None,
-                                       _ptr(logits), _ptr(out), _ptr(workspace), workspace.numel(),
-                                       _stream(stream)),
+    dev, qp, dt, kqs, vqs, kc, vc, lp, op = _decode_args(kq, vq, shape, q, k_cache, v_cache, logits, out)
+    _check_append(k_new, "k_new", kq, dev)
+    _check_append(v_new, "v_new", vq, dev)
+    wp, wn = _workspace(workspace, kq, vq, shape, dev)
+    _check(lib().tq_attn_decode_append(C.byref(kqs), _ref(vqs), C.byref(shape), _ref(k_new), _ref(v_new), qp, dt,
+                                       C.byref(kc), _ref(vc), lp, op, wp, wn, _stream(stream)),
            "tq_attn_decode_append")
 
 
@@ -464,15 +583,20 @@ def tq_attn_decode_bf16(shape: tq_decode_shape, q, k, v, out, logits=None, works
     v bf16 [batch*n_kv_heads*capacity/32, d, 32]; out / logits float32 device
     tensors; workspace: uint8 device tensor (allocated here if None)."""
     torch = _torch()
-    for t in (q, k, v, out):
-        if not t.is_contiguous():
-            raise ValueError("q, k, v and out must be contiguous")
-    dt = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}[q.dtype]
+    dev = _call_device(q, "q")
     d = int(q.shape[-1])
+    B, HQ, H, cap = int(shape.batch), int(shape.n_q_heads), int(shape.n_kv_heads), int(shape.cache_capacity)
+    dt = _qdtype(q, "q")
+    qp = _dev(q, "q", (torch.float32, torch.bfloat16), dev, numel=B * HQ * d)
+    kp = _dev(k, "k", torch.bfloat16, dev, min_numel=B * H * cap * d)
+    vp = _dev(v, "v", torch.bfloat16, dev, min_numel=B * H * cap * d)
+    op = _dev(out, "out", torch.float32, dev, numel=B * HQ * d)
+    lp = _dev(logits, "logits", torch.float32, dev, numel=B * HQ * int(shape.n_ctx), optional=True)
     if workspace is None:
-        workspace = torch.empty(tq_attn_decode_bf16_workspace_bytes(shape, d), dtype=torch.uint8, device=q.device)
-    _check(lib().tq_attn_decode_bf16(C.byref(shape), d, _ptr(q), dt, _ptr(k), _ptr(v), _ptr(logits), _ptr(out),
-                                     _ptr(workspace), workspace.numel(), _stream(stream)),
+        workspace = torch.empty(tq_attn_decode_bf16_workspace_bytes(shape, d), dtype=torch.uint8, device=dev)
+    wp = _dev(workspace, "workspace", torch.uint8, dev)
+    _check(lib().tq_attn_decode_bf16(C.byref(shape), d, qp, dt, kp, vp, lp, op, wp, workspace.numel(),
+                                     _stream(stream)),
            "tq_attn_decode_bf16")
 
 
@@ -483,24 +607,19 @@ def tq_attn_decode_paged(kq: Quantizer, vq: Optional[Quantizer], shape: tq_decod
     block_table int32 device tensor [batch, max_blocks]; seq_lens int32
     device tensor [batch] or None."""
     torch = _torch()
-    if not q.is_contiguous() or not block_table.is_contiguous() or block_table.dtype != torch.int32:
-        raise ValueError("q and block_table must be contiguous; block_table int32")
-    dt = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}[q.dtype]
-    if workspace is None:
-        workspace = torch.empty(tq_attn_decode_workspace_bytes(kq, vq, shape), dtype=torch.uint8,
-                                device=q.device)
+    dev, qp, dt, kqs, vqs, kc, vc, lp, op = _decode_args(kq, vq, shape, q, k_cache, v_cache, logits, out)
+    B = int(shape.batch)
+    if not isinstance(block_table, torch.Tensor) or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be an int32 tensor [batch, max_blocks]")
+    bp = _dev(block_table, "block_table", torch.int32, dev)
+    sp = _dev(seq_lens, "seq_lens", torch.int32, dev, numel=B, optional=True)
+    wp, wn = _workspace(workspace, kq, vq, shape, dev)
     pg = tq_paging()
-    pg.block_table = _ptr(block_table)
-    pg.seq_lens = _ptr(seq_lens)
+    pg.block_table = bp
+    pg.seq_lens = sp
     pg.max_blocks = int(block_table.shape[-1])
-    kqs = kq.struct()
-    vqs = vq.struct() if vq is not None else None
-    kc = k_cache.struct()
-    vc = v_cache.struct() if v_cache is not None else None
-    _check(lib().tq_attn_decode_paged(C.byref(kqs), C.byref(vqs) if vqs is not None else None, C.byref(shape),
-                                      C.byref(pg), _ptr(q), dt, C.byref(kc),
-                                      C.byref(vc) if vc is not None else None, _ptr(logits), _ptr(out),
-                                      _ptr(workspace), workspace.numel(), _stream(stream)),
+    _check(lib().tq_attn_decode_paged(C.byref(kqs), _ref(vqs), C.byref(shape), C.byref(pg), qp, dt, C.byref(kc),
+                                      _ref(vc), lp, op, wp, wn, _stream(stream)),
            "tq_attn_decode_paged")
 
 
@@ -517,21 +636,27 @@ def tq_search(quantizer: Quantizer, db: Cache, n_db: int, q, k: int, out_idx=Non
     float32/bfloat16 device tensor; db a token-major Cache; returns
     (out_idx int64 [n_q, k], out_score float32 [n_q, k]) device tensors."""
     torch = _torch()
-    if not q.is_contiguous() or q.dim() != 2:
+    dev = _call_device(q, "q")
+    if q.dim() != 2 or q.shape[1] != quantizer.layout.d:
         raise ValueError("q must be a contiguous [n_q, d] tensor")
-    dt = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}[q.dtype]
+    dt = _qdtype(q, "q")
     n_q = int(q.shape[0])
+    qp = _dev(q, "q", (torch.float32, torch.bfloat16), dev)
+    if db.fmt != TQ_TOKEN_MAJOR:
+        raise ValueError("db must be a TQ_TOKEN_MAJOR cache")
     if out_idx is None:
-        out_idx = torch.empty((n_q, k), dtype=torch.int64, device=q.device)
+        out_idx = torch.empty((n_q, k), dtype=torch.int64, device=dev)
     if out_score is None:
-        out_score = torch.empty((n_q, k), dtype=torch.float32, device=q.device)
+        out_score = torch.empty((n_q, k), dtype=torch.float32, device=dev)
+    ip = _dev(out_idx, "out_idx", torch.int64, dev, numel=n_q * k)
+    scp = _dev(out_score, "out_score", torch.float32, dev, numel=n_q * k)
     if workspace is None:
-        workspace = torch.empty(tq_search_workspace_bytes(quantizer, n_db, n_q, k), dtype=torch.uint8,
-                                device=q.device)
-    qs = quantizer.struct()
-    c = db.struct()
-    _check(lib().tq_search(C.byref(qs), C.byref(c), n_db, _ptr(q), dt, n_q, k, _ptr(out_idx), _ptr(out_score),
-                           _ptr(workspace), workspace.numel(), _stream(stream)), "tq_search")
+        workspace = torch.empty(tq_search_workspace_bytes(quantizer, n_db, n_q, k), dtype=torch.uint8, device=dev)
+    wp = _dev(workspace, "workspace", torch.uint8, dev)
+    qs = quantizer.struct(dev)
+    c = db.struct(quantizer, dev)
+    _check(lib().tq_search(C.byref(qs), C.byref(c), n_db, qp, dt, n_q, k, ip, scp, wp, workspace.numel(),
+                           _stream(stream)), "tq_search")
     return out_idx, out_score
 
 

@@ -8,6 +8,7 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -23,9 +24,9 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
 def build(verbose: bool = False) -> str:
-    objs = []
     tmp = os.path.join(HERE, "_build")
     os.makedirs(tmp, exist_ok=True)
+    cmds, objs = [], []
     for src in SOURCES:
         obj = os.path.join(tmp, src + ".o")
         cmd = [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -34,8 +35,12 @@ def build(verbose: bool = False) -> str:
             cmd[1:1] = DEVICE_FLAGS
         else:
             cmd += ["-x", "c++"]
-        _run(cmd, verbose)
+        cmds.append(cmd)
         objs.append(obj)
+    # the translation units are independent: compile them side by side
+    jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(jobs) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
     out_tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out_tmp] + objs, verbose)
     os.replace(out_tmp, LIB)
