@@ -334,7 +334,9 @@ typedef struct {
  * arithmetic is that of tq_attn_decode). shape->n_ctx is the longest
  * sequence: logits rows keep that length and entries past a sequence's own
  * length are not written; n_q_tokens chunks take their causal limits from
- * each sequence's length. Block ids outside the caches are clamped into them
+ * each sequence's length (a query token of a chunk that sees no cached token,
+ * when a sequence is shorter than the chunk, gets a zero output row and -inf
+ * logits). Block ids outside the caches are clamped into them
  * (the caller keeps the table valid; nothing is read outside the caches).
  * Workspace: tq_attn_decode_workspace_bytes(shape). Errors as
  * tq_attn_decode, plus TQ_ERR_INVALID for a missing or misaligned table or

@@ -12,23 +12,23 @@
 //              q_rot stored as an fp16 hi/lo pair, q_sk as fp16), both
 //              scaled by scale * log2(e) and q_sk also by alpha_g.
 //  2. split:   split-K over the context. A workgroup takes one (batch, KV
-//              head, 16-query-head block) and a range of 32-token tiles; its
-//              four waves take alternate tiles. Per tile a wave
-//              - expands the K codes through LDS tables (two fp16 centroids
-//                and, from a second table, their fp16 rounding remainders
-//                per lookup) and the K sign bits through a nibble table into
-//                fp16 +-1,
+//              head, block of query heads) and a range of 32-token tiles;
+//              its four waves take alternate tiles. Per tile a wave
+//              - expands the K codes through an LDS table of pairs of fp16
+//                scaled centroids fp16(s c) (one scale s per codebook, its
+//                1/s applied with the token's norm) and the K sign bits
+//                through a nibble table into fp16 +-1,
 //              - forms both logit parts on v_mfma_f32_16x16x32_f16 (tokens x
-//                channels times channels x heads); the MSE part uses the
-//                hi/lo splits of centroids and queries so its products keep
-//                fp32 accuracy; scales them by the tokens' norms and runs
-//                the online softmax (accumulators are rescaled only when a
+//                channels times channels x heads), with the rotated query
+//                as an fp16 hi/lo pair so the MSE part keeps fp32-grade
+//                accuracy; scales them by the tokens' norms and runs the
+//                online softmax (accumulators are rescaled only when a
 //                head's running maximum moves),
-//              - expands the V codes four at a time and the V signs, and
-//                accumulates sum_t p_t n_t c[idx_t] and sum_t p_t gamma_t z_t
-//                on MFMA (channels x tokens times tokens x heads): V is
-//                summed in the rotated and sketch domains, never
-//                dequantized per token.
+//              - expands the V codes and signs the same way and accumulates
+//                sum_t p_t n_t c[idx_t] and sum_t p_t gamma_t z_t on MFMA
+//                (channels x tokens times tokens x heads): V is summed in
+//                the rotated and sketch domains, never dequantized per
+//                token.
 //              The MFMA output layout of the logits (lane = head, 8 tokens)
 //              is exactly the operand layout the V product needs, so the
 //              softmax weights never leave registers. The four waves merge
@@ -1025,7 +1025,9 @@ __global__ __launch_bounds__(NTHR) void combine_kernel(const float* part, int n_
 #pragma unroll 8
     for (int r = 0; r < RP; ++r) o += s_out[r][t];
     const int64_t orow = T <= 1 ? head : ((int64_t)(head / T / hq) * T + head % T) * hq + (head / T) % hq;
-    out[orow * D + cs * OC + t] = o / L;
+    // (a query token that sees no key at all -- a paged sequence shorter
+    // than the chunk -- has L = 0 and gets a zero output)
+    out[orow * D + cs * OC + t] = L > 0.f ? o / L : 0.f;
   }
 }
 
@@ -1450,3 +1452,4 @@ extern "C" tq_status tq_attn_decode(const tq_quantizer* kq, const tq_quantizer* 
   return tq_attn_decode_phases(TQ_PHASE_ALL, kq, vq, shape, q, q_dtype, k_cache, v_cache, logits, out,
                                workspace, workspace_bytes, stream);
 }
+

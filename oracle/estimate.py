@@ -91,6 +91,9 @@ def attention_prefill(q: np.ndarray, k_tilde: np.ndarray, v_tilde: np.ndarray | 
     already hold the chunk's own T tokens as their last rows). Query token i
     sits at position N - T + i and sees tokens 0 .. N - T + i (reading: a
     prefill chunk attends to the cached prefix and causally within itself).
+    A token with no visible key (N - T + i < 0: a sequence shorter than the
+    chunk) keeps -inf logits and gets a zero output, the empty sum (reading:
+    the pages say nothing of this case).
     Returns (logits [H_q, T, N] with -inf past each token's limit,
     out [T, H_q, d] or None)."""
     T, hq, d = q.shape
@@ -100,6 +103,10 @@ def attention_prefill(q: np.ndarray, k_tilde: np.ndarray, v_tilde: np.ndarray | 
     out = None if v_tilde is None else np.empty((T, hq, d), dtype=np.float64)
     for i in range(T):
         lim = n - T + i + 1
+        if lim <= 0:
+            if out is not None:
+                out[i] = 0.0
+            continue
         for h in range(hq):
             kv = h // group
             row = estimate_logits(q[i, h][None, :], k_tilde[kv, :lim], scale)[0]

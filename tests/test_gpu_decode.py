@@ -486,6 +486,38 @@ def test_paged_cache_per_sequence_lengths(tq, T):
         assert np.all(np.isnan(lgn[b, :, :, n:]))  # past the sequence: not written
 
 
+def test_paged_sequence_shorter_than_chunk(tq):
+    # a chunk of 5 query tokens over sequences of 3 and 40 tokens: in the
+    # first sequence two query tokens see no key (zero output, -inf logits)
+    import torch
+    wl = synth.workload("llama8b_decode", batch=3, n_q_heads=8, n_kv_heads=2)
+    n_ctx, cap, T = 1000, 1024, 5
+    lens = np.array([3, 40, 1000], np.int32)
+    o, kq, vq, kc, vc, table = _paged_setup(tq, wl, n_ctx, cap, seed=9)
+    q = _chunk_queries(wl, T)
+    qt = torch.from_numpy(q).cuda().to(torch.bfloat16)
+    shape = tq.decode_shape(3, 8, 2, n_ctx, cap, wl.scale, n_q_tokens=T)
+    lg = torch.full((3, 8, T, n_ctx), float("nan"), device="cuda")
+    out = torch.full((3, T, 8, 128), float("nan"), device="cuda")
+    print("paged chunk T=5 over sequences of 3, 40, 1000 tokens", flush=True)
+    tq.tq_attn_decode_paged(kq, vq, shape, torch.from_numpy(table).cuda(), qt, kc, vc,
+                            seq_lens=torch.from_numpy(lens).cuda(), logits=lg, out=out)
+    torch.cuda.synchronize()
+    lgn, otn = lg.cpu().numpy().astype(np.float64), out.cpu().numpy().astype(np.float64)
+    for b in range(3):
+        n = int(lens[b])
+        rl, ro = oracle.attention_prefill(q[b].astype(np.float64), o["k_t"][b][:, :n], o["v_t"][b][:, :n],
+                                          wl.scale)
+        for i in range(T):
+            lim = n - T + i + 1
+            if lim <= 0:
+                assert np.all(otn[b, i] == 0.0), (b, i)
+                assert np.all(np.isneginf(lgn[b, :, i, :n])), (b, i)
+            else:
+                assert gc.normwise_close(otn[b, i], ro[i])[0], (b, i)
+                assert gc.normwise_close(lgn[b, :, i, :lim], rl[:, i, :lim])[0], (b, i)
+
+
 # MSE-only V records (codes and norms, no sign words; the values are
 # dequantized as n Pi^T c[idx]) under two-stage K: the packed layout (at most
 # 4 query heads per KV head), 16-head blocks, two groups, ragged lengths.

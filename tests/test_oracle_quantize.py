@@ -323,6 +323,26 @@ def test_attention_prefill_causal_chunk():
             assert np.allclose(out[i, h], ref, atol=1e-12)
 
 
+def test_attention_prefill_tokens_without_keys():
+    # a chunk longer than the sequence: the first T - n tokens see no key,
+    # keep -inf logits and get the empty sum (zero); the others equal the
+    # decode step over their own visible prefix
+    rng = np.random.default_rng(8)
+    hkv, g, n, d, T = 1, 3, 3, 4, 5
+    k = rng.standard_normal((hkv, n, d))
+    v = rng.standard_normal((hkv, n, d))
+    q = rng.standard_normal((T, hkv * g, d))
+    lg, out = oracle.attention_prefill(q, k, v, 0.5)
+    for i in range(T):
+        lim = n - T + i + 1
+        if lim <= 0:
+            assert np.all(out[i] == 0.0) and np.all(np.isneginf(lg[:, i]))
+        else:
+            lgd, od = oracle.attention_decode(q[i], k[:, :lim], v[:, :lim], 0.5)
+            assert np.allclose(out[i], od, atol=1e-14) and np.allclose(lg[:, i, :lim], lgd, atol=1e-14)
+            assert np.all(np.isneginf(lg[:, i, lim:]))
+
+
 def test_legal_variants_cover_near_boundary_choices():
     d = 16
     qz = _quantizer(d, ((d, 2),), seed=41)
