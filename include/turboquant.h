@@ -47,7 +47,8 @@
  *  - Device pointers are plain device addresses (e.g. from hipMalloc or a
  *    torch tensor) and must be 16-byte aligned. The caller owns every
  *    buffer, including the decode workspace; the library allocates nothing,
- *    keeps no mutable global state and never synchronizes: kernels are
+ *    keeps no mutable global state (apart from the static workspace of
+ *    tq_attn_decode_scratch) and never synchronizes: kernels are
  *    enqueued on `stream` (a hipStream_t passed as void*, NULL = the null
  *    stream) and results are visible after the caller's own sync.
  *  - Inputs and outputs must not alias.
@@ -64,7 +65,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 4
+#define TQ_ABI_VERSION 5
 
 typedef enum {
   TQ_OK = 0,
@@ -374,6 +375,23 @@ tq_status tq_attn_decode_append(const tq_quantizer* kq, const tq_quantizer* vq,
                                 const tq_append* v_new, const void* q, tq_dtype q_dtype,
                                 const tq_cache* k_cache, const tq_cache* v_cache, float* logits,
                                 float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* tq_attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). The workspace is a static device array
+ * of the library (16 MiB on each GPU the library runs on, held until the
+ * process ends); its per-device address is looked up on the first call on
+ * each device. Arguments, results and errors as tq_attn_decode, plus
+ * TQ_ERR_WORKSPACE when the shape needs more than 16 MiB of workspace
+ * (tq_attn_decode_workspace_bytes) and TQ_ERR_DEVICE when the array's
+ * address cannot be obtained. Nothing in the array needs to start at zero.
+ * Every call on one GPU uses the same array: calls that overlap in time on
+ * one GPU (on different streams, or from different threads) race and give
+ * undefined results; calls in order on one stream are safe. */
+tq_status tq_attn_decode_scratch(const tq_quantizer* kq, const tq_quantizer* vq,
+                                 const tq_decode_shape* shape, const void* q, tq_dtype q_dtype,
+                                 const tq_cache* k_cache, const tq_cache* v_cache, float* logits,
+                                 float* out, void* stream);
 
 /* Uncompressed decode baseline: the same decode step over bf16 K/V caches,
  * for comparison with tq_attn_decode ([WD] "Os numeros que importam": the

@@ -43,7 +43,8 @@ TQ_PHASE_ALL = 7
 SYMBOLS = ("tq_abi_version", "tq_status_string", "tq_build_codebook", "tq_record_layout",
            "tq_fold_sketch", "tq_quantize", "tq_attn_decode_workspace_bytes", "tq_attn_decode",
            "tq_attn_decode_phases", "tq_attn_decode_append", "tq_attn_decode_bf16_workspace_bytes",
-           "tq_attn_decode_bf16", "tq_search_workspace_bytes", "tq_search", "tq_attn_decode_paged")
+           "tq_attn_decode_bf16", "tq_search_workspace_bytes", "tq_search", "tq_attn_decode_paged",
+           "tq_attn_decode_scratch")
 
 
 class TQError(RuntimeError):
@@ -151,6 +152,8 @@ def lib() -> C.CDLL:
         L.tq_attn_decode_paged.restype = C.c_int
         L.tq_attn_decode_paged.argtypes = (L.tq_attn_decode.argtypes[:3] + [C.POINTER(tq_paging)] +
                                            L.tq_attn_decode.argtypes[3:])
+        L.tq_attn_decode_scratch.restype = C.c_int
+        L.tq_attn_decode_scratch.argtypes = (L.tq_attn_decode.argtypes[:9] + [C.c_void_p])
         L.tq_search_workspace_bytes.restype = C.c_int
         L.tq_search_workspace_bytes.argtypes = [C.POINTER(tq_quantizer), C.c_int64, C.c_int64, C.c_int,
                                                 C.POINTER(C.c_size_t)]
@@ -523,6 +526,18 @@ def tq_attn_decode_phases(phases: int, kq: Quantizer, vq: Optional[Quantizer], s
            "tq_attn_decode")
 
 
+def tq_attn_decode_scratch(kq: Quantizer, vq: Optional[Quantizer], shape: tq_decode_shape, q,
+                           k_cache: Cache, v_cache: Optional[Cache], logits=None, out=None,
+                           stream=None) -> None:
+    """tq_attn_decode with the library's static device workspace (no workspace
+    argument, nothing allocated; see include/turboquant.h). Calls that overlap
+    in time on one GPU race."""
+    dev, qp, dt, kqs, vqs, kc, vc, lp, op = _decode_args(kq, vq, shape, q, k_cache, v_cache, logits, out)
+    _check(lib().tq_attn_decode_scratch(C.byref(kqs), _ref(vqs), C.byref(shape), qp, dt, C.byref(kc),
+                                        _ref(vc), lp, op, _stream(stream)),
+           "tq_attn_decode_scratch")
+
+
 def append_spec(x, dst_rows=None, seg_len: int = 1, seg_stride: int = 1, seg_offset: int = 0) -> tq_append:
     """Vectors to append within tq_attn_decode_append: the rows of x ([n_vec,
     >= d] float32/bfloat16 on the GPU) go to dst_rows (int64 [n_vec]), or by
@@ -666,6 +681,7 @@ __all__ = [
     "tq_quantize", "tq_attn_decode_workspace_bytes", "tq_attn_decode", "tq_attn_decode_phases",
     "tq_attn_decode_append", "append_spec", "tq_append", "tq_attn_decode_bf16_workspace_bytes",
     "tq_attn_decode_bf16", "tq_search_workspace_bytes", "tq_search", "tq_attn_decode_paged", "tq_paging",
+    "tq_attn_decode_scratch",
     "TQ_PHASE_PREP", "TQ_PHASE_SPLIT", "TQ_PHASE_COMBINE", "TQ_PHASE_ALL",
     "TQ_OK", "TQ_ERR_INVALID", "TQ_ERR_UNSUPPORTED", "TQ_ERR_NOCONVERGE", "TQ_ERR_WORKSPACE",
     "TQ_ERR_DEVICE", "TQ_F32", "TQ_BF16", "TQ_TOKEN_MAJOR", "TQ_BLOCK32",

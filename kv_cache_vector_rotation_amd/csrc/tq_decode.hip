@@ -45,6 +45,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 
 #include "tq_internal.h"
@@ -1453,3 +1454,55 @@ extern "C" tq_status tq_attn_decode(const tq_quantizer* kq, const tq_quantizer* 
                                workspace, workspace_bytes, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Decode without a caller-supplied workspace, for callers that cannot
+// allocate device memory (code under graph capture, tight serving loops,
+// harnesses that forbid allocation). The workspace lives in a file-scope
+// device array; each device holds its own copy at its own address, looked up
+// once per device (with that device current) and kept for the process.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+constexpr int kScratchMaxDevices = 64;
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchMaxDevices] = {};
+
+// Device address of `scratch` on the current device (null on failure).
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" tq_status tq_attn_decode_scratch(const tq_quantizer* kq, const tq_quantizer* vq,
+                                            const tq_decode_shape* shape, const void* q, tq_dtype q_dtype,
+                                            const tq_cache* k_cache, const tq_cache* v_cache, float* logits,
+                                            float* out, void* stream) {
+  size_t need = 0;
+  tq_status st = tq_attn_decode_workspace_bytes(kq, vq, shape, &need);
+  if (st != TQ_OK) return st;
+  if (need > kScratchBytes) return TQ_ERR_WORKSPACE;
+  // full validation on the host before any HIP call (an aligned stand-in for
+  // the workspace address; the real address is looked up afterwards)
+  Plan pl;
+  void* const stand_in = reinterpret_cast<void*>((uintptr_t)256);
+  st = plan_decode(kq, vq, shape, q, q_dtype, k_cache, v_cache, logits, out, stand_in, kScratchBytes, &pl);
+  if (st != TQ_OK) return st;
+  void* ws = scratch_address();
+  if (!ws) return TQ_ERR_DEVICE;
+  st = plan_decode(kq, vq, shape, q, q_dtype, k_cache, v_cache, logits, out, ws, kScratchBytes, &pl);
+  if (st != TQ_OK) return st;
+  return run_phases(pl, TQ_PHASE_ALL, reinterpret_cast<hipStream_t>(stream));
+}

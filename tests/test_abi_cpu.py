@@ -30,7 +30,7 @@ def tq():
 def test_header_symbols_exported(tq):
     text = open(HEADER).read()
     declared = sorted(set(re.findall(r"^\s*(?:tq_status|int|const char\*)\s+(tq_\w+)\s*\(", text, re.M)))
-    assert len(declared) == 15
+    assert len(declared) == 16
     lib = C.CDLL(tq.LIB_PATH)
     for name in declared:
         assert hasattr(lib, name), name
@@ -180,6 +180,32 @@ def test_decode_validation(tq):
     need = C.c_size_t()
     assert lib.tq_attn_decode_workspace_bytes(C.byref(kq), C.byref(vq), C.byref(good), C.byref(need)) == 0
     assert call(good, wsb=need.value - 1) == tq.TQ_ERR_WORKSPACE
+
+
+def test_decode_scratch_validation(tq):
+    # the static-workspace decode validates like tq_attn_decode and rejects
+    # shapes whose workspace exceeds its 16 MiB array, before any HIP call
+    lib = tq.lib()
+    kq, vq = _fake_quantizer(tq), _fake_quantizer(tq)
+    kc = _fake_cache(tq, 2 * 8 * 1024)
+    vc = _fake_cache(tq, 2 * 8 * 1024)
+
+    def call(shape, **kw):
+        return lib.tq_attn_decode_scratch(C.byref(kq), kw.get("vq", C.byref(vq)), C.byref(shape),
+                                          kw.get("q", FAKE), kw.get("dt", 1), C.byref(kw.get("kc", kc)),
+                                          C.byref(vc), kw.get("logits", None), kw.get("out", FAKE), None)
+
+    good = tq.decode_shape(2, 32, 8, 1000, 1024, 0.088)
+    assert call(tq.decode_shape(2, 30, 8, 1000, 1024, 0.1)) == tq.TQ_ERR_INVALID
+    assert call(good, dt=5) == tq.TQ_ERR_INVALID
+    assert call(good, out=None) == tq.TQ_ERR_INVALID
+    assert call(good, q=FAKE + 8) == tq.TQ_ERR_INVALID
+    assert call(good, kc=_fake_cache(tq, 100)) == tq.TQ_ERR_INVALID
+    big = tq.decode_shape(2, 32, 8, 131072, 131072, 0.088, n_split=1024)
+    need = C.c_size_t()
+    assert lib.tq_attn_decode_workspace_bytes(C.byref(kq), C.byref(vq), C.byref(big), C.byref(need)) == 0
+    assert need.value > 16 << 20
+    assert call(big) == tq.TQ_ERR_WORKSPACE
 
 
 def test_phase_mask_validation(tq):

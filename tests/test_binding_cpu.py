@@ -56,6 +56,8 @@ def test_entry_points_reject_host_inputs():
     out = torch.zeros((1, 4, 128), dtype=torch.float32)
     with pytest.raises(ValueError, match="GPU"):
         tq.tq_attn_decode(kq, kq, shape, q, kc, vc, out=out)
+    with pytest.raises(ValueError, match="GPU"):
+        tq.tq_attn_decode_scratch(kq, kq, shape, q, kc, vc, out=out)
     with pytest.raises(ValueError):
         tq.tq_quantize(kq, tq.TQ_TOKEN_MAJOR, torch.zeros((8, 128)), kc)
     with pytest.raises(ValueError):
