@@ -1,10 +1,13 @@
 #!/usr/bin/env python3
-"""Throughput of the TurboQuant compressed-KV decode step on one MI355X.
+"""Throughput of the TurboQuant compressed-KV hot path on one MI355X.
 
-One step = quantize-on-append of the new token(s) of every (batch, KV head)
+One step = quantize-on-append of the new tokens of every (batch, KV head)
 for K (token-major records) and V (32-token block records), then one decode
 step over the whole compressed cache: tq_attn_decode_append, i.e. one launch
 for both appends and the query prep, then the split-K pass and the combine.
+The default workload is the 70B-shaped long context (batch 4, 64 query / 8
+KV heads, 131072 tokens, 3 bits): an 8192-token chunk is quantized per head
+(524,288 vectors), then one decode step attends over all 131072 tokens.
 Inputs are seeded synthetic tensors already resident in HBM; the cache is
 built (untimed) by the library's own quantize kernel from synthetic K/V.
 
@@ -13,24 +16,44 @@ next of several copies of the compressed cache (at least 1 GiB in total).
 
 Prints one JSON line: cached tokens/s (batch * context / step time), the
 split-K kernel against the HBM roofline (HIP events around that kernel on
-its stream), the same decode over uncompressed bf16 K/V caches for
-comparison, a secondary quantize throughput on a 524,288-vector chunk, the
-nearest-neighbour search workload (10,000 queries over 1,000,000 compressed
-vectors, top 10, with its recall), and the CPU oracle timed on a bounded
+its stream), the same decode for the other decode workloads, quantize
+throughput, the decode over uncompressed bf16 K/V for comparison, the
+nearest-neighbour search workload, and the CPU oracle timed on a bounded
 sample as a baseline.
 """
 from __future__ import annotations
 
-import argparse
-import hashlib
-import json
-import math
 import os
 import sys
-import time
-from concurrent.futures import ThreadPoolExecutor
 
-import numpy as np
+
+def _host_cores() -> int:
+    """Host threads the oracle may use: the process's CPU affinity, capped by
+    OMP_NUM_THREADS when the environment sets it."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    lim = os.environ.get("OMP_NUM_THREADS", "")
+    if lim.isdigit() and int(lim) > 0:
+        n = min(n, int(lim))
+    return max(1, n)
+
+
+# BLAS and OpenMP pools size themselves when numpy is first imported, so the
+# thread count is fixed here, before any import that loads numpy.
+HOST_CORES = _host_cores()
+for _var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS"):
+    os.environ[_var] = str(HOST_CORES)
+
+import argparse  # noqa: E402
+import hashlib  # noqa: E402
+import json  # noqa: E402
+import math  # noqa: E402
+import time  # noqa: E402
+from concurrent.futures import ThreadPoolExecutor  # noqa: E402
+
+import numpy as np  # noqa: E402
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -55,21 +78,22 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="llama8b_decode", choices=DECODE_WORKLOADS)
+    ap.add_argument("--workload", default="llama70b_long", choices=DECODE_WORKLOADS)
     ap.add_argument("--copies", type=int, default=0, help="cache copies (0: enough for 1 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quantize-bench", action="store_true")
+    ap.add_argument("--no-decode-legs", action="store_true",
+                    help="skip the other decode workloads (llama8b_decode, mixed_3p5, mixed_2p5)")
     ap.add_argument("--no-bf16-baseline", action="store_true")
     ap.add_argument("--no-search", action="store_true")
     ap.add_argument("--no-chunk", action="store_true", help="skip the prefill-chunk and paged-cache legs")
-    ap.add_argument("--no-mixed", action="store_true", help="skip the fractional-width (batch 16) legs")
+    ap.add_argument("--no-mixed", action="store_true", help="(same as --no-decode-legs)")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the record-variant legs (MSE-only V, fp16 norms)")
     ap.add_argument("--ctx-sweep", default="",
                     help="comma-separated context lengths: also time the compressed step and the bf16 "
                          "decode of the llama8b_decode shape at each (reported under ctx_sweep)")
-    ap.add_argument("--no-graph", action="store_true", help="launch every step from Python")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (the reference for scaling "
                          "the FETCH_SIZE / WRITE_SIZE counters of a profiled run)")
@@ -81,10 +105,8 @@ def record_bytes(dims, bits):
 
 
 def _threads():
-    try:
-        return max(1, min(16, len(os.sched_getaffinity(0))))
-    except AttributeError:
-        return 8
+    """Worker threads for drawing synthetic slabs on the host."""
+    return max(1, min(16, HOST_CORES))
 
 
 def build_caches(tq, torch, wl, kq, vq, prefix, cap, device_fill=False):
@@ -134,37 +156,80 @@ def new_tokens(torch, wl, prefix):
     return k, v
 
 
-def traffic_record():
-    """HBM traffic of the split-K kernel from rocprofv3 counters, if they were
-    taken on the current kernel source (else None)."""
+def traffic_record(workload):
+    """HBM bytes per launch of the split-K kernel on ``workload`` from
+    rocprofv3 FETCH_SIZE / WRITE_SIZE counters, if they were taken on the
+    current kernel source (else None)."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     rec = json.load(open(TRAFFIC_FILE))
     sha = hashlib.sha256(open(DECODE_SOURCE, "rb").read()).hexdigest()
-    return rec if rec.get("source_sha256") == sha else None
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec.get("workloads", {}).get(workload)
 
 
-def quantize_bench(tq, torch, wl, kq, n_vec=524288, launches=20):
-    """Secondary figure: vectors/s of one quantize launch over a chunk of
-    n_vec vectors (the 70B-shaped prefill chunk: 4 x 8 heads x 8192 tokens x K,V)."""
-    rng_x = synth.standard_normal(synth.rng_for(wl.seed, 99), (n_vec, wl.d))
-    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
-    x = torch.from_numpy(synth.to_bf16_exact(rng_x) if wl.dtype == "bf16" else rng_x).cuda().to(dt)
-    cache = tq.Cache.empty(kq, n_vec, tq.TQ_TOKEN_MAJOR)
+def _quantize_timed(tq, torch, calls, launches):
+    """Mean seconds per round of ``calls`` (quantize launches), HIP events."""
     for _ in range(3):
-        tq.tq_quantize(kq, tq.TQ_TOKEN_MAJOR, x, cache, seg_len=n_vec, seg_stride=n_vec)
+        for c in calls:
+            c()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(launches):
-        tq.tq_quantize(kq, tq.TQ_TOKEN_MAJOR, x, cache, seg_len=n_vec, seg_stride=n_vec)
+        for c in calls:
+            c()
     e1.record()
     torch.cuda.synchronize()
-    s = e0.elapsed_time(e1) / 1e3 / launches
+    return e0.elapsed_time(e1) / 1e3 / launches
+
+
+def quantize_chunk_bench(tq, torch, launches=20):
+    """The prefill-chunk quantize of the llama70b_long step on its own: the
+    8192-token chunk of every (batch, KV head), K into token-major records
+    and V into 32-token block records at the step's rows (524,288 vectors,
+    3 bits), as two tq_quantize launches."""
+    wl = synth.workload("llama70b_long")
+    ks, vs = synth.draw_quantizer(wl, "K"), synth.draw_quantizer(wl, "V")
+    bits = [g.mse_bits for g in ks.groups]
+    kq = tq.Quantizer.from_parts(ks.rotations, ks.sketches, bits, perm=ks.perm)
+    vq = tq.Quantizer.from_parts(vs.rotations, vs.sketches, bits, perm=vs.perm)
+    B, H, cap = wl.batch, wl.n_kv_heads, wl.capacity
+    prefix = wl.n_ctx - wl.n_new
+    k_new, v_new = new_tokens(torch, wl, prefix)
+    kc = tq.Cache.empty(kq, B * H * cap, tq.TQ_TOKEN_MAJOR)
+    vc = tq.Cache.empty(vq, B * H * cap, tq.TQ_BLOCK32)
+    kw = dict(seg_len=wl.n_new, seg_stride=cap, seg_offset=prefix)
+    calls = [lambda: tq.tq_quantize(kq, tq.TQ_TOKEN_MAJOR, k_new, kc, **kw),
+             lambda: tq.tq_quantize(vq, tq.TQ_BLOCK32, v_new, vc, **kw)]
+    s = _quantize_timed(tq, torch, calls, launches)
+    n_vec = 2 * B * H * wl.n_new
     flops = 4.0 * wl.d * wl.d * n_vec  # two d x d products per vector
-    return {"vectors": n_vec, "us_per_launch": round(s * 1e6, 2), "vectors_per_s": n_vec / s,
-            "bound": "mfma", "achieved_tflops": flops / s / 1e12, "peak_tflops": PEAK_FP32_MFMA_TFLOPS,
-            "frac": flops / s / 1e12 / PEAK_FP32_MFMA_TFLOPS, "dtype": "f32"}
+    del kc, vc, k_new, v_new
+    return {"workload": "llama70b_long", "vectors": n_vec, "formats": "K token-major + V block32",
+            "bits_per_channel": [m + 1 for m in bits], "input_dtype": wl.dtype,
+            "us_per_chunk": round(s * 1e6, 2), "vectors_per_s": n_vec / s,
+            "bound": "mfma", "achieved_tflops": round(flops / s / 1e12, 2), "peak_tflops": PEAK_FP32_MFMA_TFLOPS,
+            "peak_kind": "fp32 MFMA", "frac": round(flops / s / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4)}
+
+
+def quantize_nn_bench(tq, torch, launches=5):
+    """The nearest-neighbour database quantize: 1,000,000 fp32 vectors of
+    d = 200 at 4 bits (3 + 1) into token-major records, one launch."""
+    wl = synth.workload("nn_search")
+    spec = synth.draw_quantizer(wl, "K")
+    qz = tq.Quantizer.from_parts(spec.rotations, spec.sketches, [g.mse_bits for g in spec.groups], perm=spec.perm)
+    x = torch.from_numpy(synth.draw_mixture_vectors(wl, wl.n_ctx, "db")).cuda()
+    db = tq.Cache.empty(qz, wl.n_ctx, tq.TQ_TOKEN_MAJOR)
+    calls = [lambda: tq.tq_quantize(qz, tq.TQ_TOKEN_MAJOR, x, db, seg_len=wl.n_ctx, seg_stride=wl.n_ctx)]
+    s = _quantize_timed(tq, torch, calls, launches)
+    flops = 4.0 * wl.d * wl.d * wl.n_ctx
+    del x, db
+    return {"workload": "nn_search", "vectors": wl.n_ctx, "d": wl.d, "bits_per_channel": 4, "input_dtype": "f32",
+            "us_per_launch": round(s * 1e6, 2), "vectors_per_s": wl.n_ctx / s,
+            "bound": "mfma", "achieved_tflops": round(flops / s / 1e12, 2), "peak_tflops": PEAK_FP32_MFMA_TFLOPS,
+            "peak_kind": "fp32 MFMA", "frac": round(flops / s / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4)}
 
 
 def bf16_baseline(tq, torch, wl, q, step_ms, launches=200, min_bytes=1 << 30, max_copies=None):
@@ -343,29 +408,120 @@ def variants_bench(tq, torch):
     return out
 
 
-def mixed_bench(tq, torch):
-    """Secondary figures: the fused decode step of the fractional-width
-    workloads (batch 16, 32 query / 8 KV heads, 32768 tokens, two channel
-    groups of 64 with their own codebooks), over at least 1 GiB of cache
-    copies; the step's algorithmic bytes (every K and V record once) over its
-    time, against the HBM peak."""
+def decode_leg(tq, torch, wl, steps, warmup=3, copies=0, device_fill=False, split_launches=200):
+    """The fused step (appends + decode) of workload ``wl`` and its split-K
+    kernel alone. Every step uses the next of several cache copies (at least
+    1 GiB in total). Exactly ``steps`` steps are timed: one HIP graph holds a
+    cycle of one step per copy and is replayed steps // copies times, and a
+    second graph holds the remaining steps % copies steps. The split-K pass is
+    timed alone from replays of a graph of split-K launches, one per copy,
+    between HIP events on the launch stream."""
+    B, HQ, H, d, N = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.d, wl.n_ctx
+    cap = wl.capacity
+    prefix = N - wl.n_new
+    ks, vs = synth.draw_quantizer(wl, "K"), synth.draw_quantizer(wl, "V")
+    bits = [g.mse_bits for g in ks.groups]
+    dims = [g.dim for g in ks.groups]
+    kq = tq.Quantizer.from_parts(ks.rotations, ks.sketches, bits, perm=ks.perm)
+    vq = tq.Quantizer.from_parts(vs.rotations, vs.sketches, bits, perm=vs.perm)
+    t0 = time.perf_counter()
+    kc0, vc0 = build_caches(tq, torch, wl, kq, vq, prefix, cap, device_fill)
+    k_new, v_new = new_tokens(torch, wl, prefix)
+    rb = record_bytes(dims, bits)
+    cache_bytes = B * H * cap * 2 * rb
+    n_copies = copies or max(1, math.ceil((1 << 30) / cache_bytes))
+    caches = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(n_copies - 1)]
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    q = torch.from_numpy(synth.draw_queries(wl)).cuda().to(dt)
+    shape = tq.decode_shape(B, HQ, H, N, cap, wl.scale)
+    ws = torch.empty(tq.tq_attn_decode_workspace_bytes(kq, vq, shape), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, HQ, d), dtype=torch.float32, device="cuda")
+    k_app = tq.append_spec(k_new, seg_len=wl.n_new, seg_stride=cap, seg_offset=prefix)
+    v_app = tq.append_spec(v_new, seg_len=wl.n_new, seg_stride=cap, seg_offset=prefix)
+    torch.cuda.synchronize()
+    log(f"{wl.name}: setup {time.perf_counter() - t0:.1f}s B={B} Hq={HQ} Hkv={H} d={d} N={N} bits={bits} "
+        f"dims={dims} copies={n_copies} ({n_copies * cache_bytes / 2**30:.2f} GiB)")
+
+    def step(i):
+        kc, vc = caches[i % n_copies]
+        tq.tq_attn_decode_append(kq, vq, shape, q, kc, vc, k_new=k_app, v_new=v_app, out=out, workspace=ws)
+
+    for i in range(max(warmup, 1)):
+        step(i)
+    torch.cuda.synchronize()
+    full, rem = divmod(steps, n_copies)
+    g_full = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_full):
+        for i in range(n_copies):
+            step(i)
+    g_rem = None
+    if rem:
+        g_rem = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_rem):
+            for i in range(rem):
+                step(i)
+    g_full.replay()
+    if g_rem is not None:
+        g_rem.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record()
+    for _ in range(full):
+        g_full.replay()
+    if g_rem is not None:
+        g_rem.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = e0.elapsed_time(e1) / steps
+    # the split-K pass alone (the prepared queries in the workspace are the
+    # same for every copy)
+    g_split = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_split):
+        for i in range(n_copies):
+            kc, vc = caches[i]
+            tq.tq_attn_decode_phases(tq.TQ_PHASE_SPLIT, kq, vq, shape, q, kc, vc, out=out, workspace=ws)
+    g_split.replay()
+    torch.cuda.synchronize()
+    reps = max(1, math.ceil(split_launches / n_copies))
+    split_ms = []
+    for _ in range(5):
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        for _ in range(reps):
+            g_split.replay()
+        a1.record()
+        torch.cuda.synchronize()
+        split_ms.append(a0.elapsed_time(a1) / (reps * n_copies))
+    split_s = float(np.mean(split_ms)) / 1e3
+    algo = B * H * N * 2 * rb  # every K and V record read once by the split-K pass
+    gbs = algo / split_s / 1e9
+    log(f"{wl.name}: step {ms_step * 1e3:.2f} us over {steps} steps (wall {wall / steps * 1e6:.2f} us); split-K "
+        f"mean {split_s * 1e6:.2f} us (median {np.median(split_ms) * 1e3:.2f}, min {np.min(split_ms) * 1e3:.2f}) "
+        f"-> {gbs:.0f} GB/s, {gbs / PEAK_HBM_GBS:.3f} of peak")
+    res = {"workload": wl.name, "steps": steps, "us_per_step": round(ms_step * 1e3, 3),
+           "cached_tokens_per_s": B * N / (ms_step / 1e3), "record_bytes_per_token": rb,
+           "cache_copies": n_copies, "split_kernel_us": round(split_s * 1e6, 3),
+           "split_algorithmic_bytes": int(algo), "split_achieved_gbs": round(gbs, 1),
+           "split_frac": round(gbs / PEAK_HBM_GBS, 4),
+           "step_frac_of_hbm_peak": round(algo / (ms_step / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
+    if device_fill:
+        res["cache_fill"] = "device-drawn N(0,1) bf16 tokens"
+    state = dict(q=q, ms_step=ms_step, kq=kq, vq=vq)
+    del caches, kc0, vc0, g_full, g_rem, g_split, ws
+    torch.cuda.empty_cache()
+    return res, state
+
+
+def decode_legs(tq, torch, names):
+    """Secondary decode workloads: each one's fused step and split-K kernel."""
     out = {}
-    for name in ("mixed_3p5", "mixed_2p5"):
+    for name in names:
         wl = synth.workload(name)
-        ks, vs = synth.draw_quantizer(wl, "K"), synth.draw_quantizer(wl, "V")
-        bits = [g.mse_bits for g in ks.groups]
-        dims = [g.dim for g in ks.groups]
-        kq = tq.Quantizer.from_parts(ks.rotations, ks.sketches, bits, perm=ks.perm)
-        vq = tq.Quantizer.from_parts(vs.rotations, vs.sketches, bits, perm=vs.perm)
-        rb = record_bytes(dims, bits)
-        step_bytes = wl.batch * wl.n_kv_heads * wl.n_ctx * 2 * rb
-        copies = max(1, math.ceil((1 << 30) / (wl.batch * wl.n_kv_heads * wl.capacity * 2 * rb)))
-        us = compressed_step_us(tq, torch, wl, kq, vq, copies, device_fill=True)
-        out[name] = {"us_per_step": round(us, 2), "cached_tokens_per_s": wl.batch * wl.n_ctx / (us / 1e6),
-                     "record_bytes_per_token": rb, "step_gbs": round(step_bytes / us / 1e3, 1),
-                     "frac_of_hbm_peak": round(step_bytes / us / 1e3 / PEAK_HBM_GBS, 4), "cache_copies": copies,
-                     "cache_fill": "device-drawn N(0,1) bf16 tokens"}
-        torch.cuda.empty_cache()
+        fill = wl.batch * wl.n_kv_heads * wl.n_ctx > 8 * 32768  # large caches: device-drawn tokens
+        steps = 40 if fill else 290
+        out[name], _ = decode_leg(tq, torch, wl, steps, device_fill=fill)
     return out
 
 
@@ -474,17 +630,32 @@ def ctx_sweep(tq, torch, contexts):
     return rows
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        return HOST_CORES
+
+
 def cpu_baseline(wl, budget_s):
     """The oracle (plain float64 numpy) on a bounded sample of the same step:
     for (b, h) pairs in order, untimed: quantize the prefix; timed: quantize
     the appended token(s), dequantize the K and V caches and attend with the
-    pair's query heads. The mean time per pair is scaled to the whole step."""
+    pair's query heads. The mean time per pair is scaled to the whole step.
+    Also the tiny workload's oracle (quantize 4096 keys, 64 x 4096 logits)
+    with all host threads and with one thread."""
     import oracle  # the baseline leg is the only bench code that uses the oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = 1
     okq = oracle.Quantizer.from_spec(synth.draw_quantizer(wl, "K"))
     ovq = oracle.Quantizer.from_spec(synth.draw_quantizer(wl, "V"))
     q = synth.draw_queries(wl).astype(np.float64)
@@ -512,12 +683,35 @@ def cpu_baseline(wl, budget_s):
             continue
         break
     per_step = float(np.mean(times)) * wl.batch * wl.n_kv_heads
-    return {"value": wl.batch * wl.n_ctx / per_step, "unit": "cached tokens/s", "cores": int(cores),
+    # the tiny workload with every host thread and with one
+    tiny = synth.workload("tiny")
+    tspec = synth.draw_quantizer(tiny, "K")
+    tq_o = oracle.Quantizer.from_spec(tspec)
+    tk = synth.draw_kv_slab(tiny, "K", 0, 0, 0, tiny.n_ctx)
+    tqr = synth.draw_queries(tiny)[0].astype(np.float64)
+
+    def tiny_run():
+        t0 = time.perf_counter()
+        qv = oracle.quantize(tk, tq_o)
+        kt = oracle.dequantize(qv.idx, qv.bits, qv.norm, qv.gamma, tq_o)
+        oracle.estimate_logits(tqr, kt, tiny.scale)
+        return time.perf_counter() - t0
+    tiny_all = min(tiny_run() for _ in range(3))
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            tiny_one = min(tiny_run() for _ in range(3))
+    except Exception:  # pragma: no cover
+        tiny_one = None
+    return {"value": wl.batch * wl.n_ctx / per_step, "unit": "cached tokens/s", "cores": int(_blas_threads()),
             "kind": "oracle",
-            "sample": f"{pairs_done} of {wl.batch * wl.n_kv_heads} (batch, KV head) pairs: append "
+            "sample": f"{pairs_done} of {wl.batch * wl.n_kv_heads} (batch, KV head) pairs of {wl.name}: append "
                       f"{wl.n_new} token(s) K+V, dequantize {wl.n_ctx} K+V records, attend with {G} "
                       f"query heads; {sum(times):.1f} s timed, scaled to the full step",
-            "seconds_per_step": per_step}
+            "seconds_per_step": per_step, "cpu_model": cpu_model(), "host_threads": HOST_CORES,
+            "tiny_logits_s": {"all_threads": round(tiny_all, 4),
+                              "one_thread": None if tiny_one is None else round(tiny_one, 4),
+                              "what": "quantize 4096 fp32 keys (d=128, 3 bits) and the 64 x 4096 logits"}}
 
 
 def main():
@@ -525,6 +719,9 @@ def main():
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU layout "
               "(head-sharded decode, no collective) is not built here.")
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0")
         sys.exit(2)
     import torch
     import kv_cache_vector_rotation_amd as tq
@@ -534,139 +731,30 @@ def main():
     tq.lib()
     wl = synth.workload(args.workload)
     B, HQ, H, d, N = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.d, wl.n_ctx
-    cap = wl.capacity
-    prefix = N - wl.n_new
-    ks, vs = synth.draw_quantizer(wl, "K"), synth.draw_quantizer(wl, "V")
-    bits = [g.mse_bits for g in ks.groups]
-    dims = [g.dim for g in ks.groups]
-    kq = tq.Quantizer.from_parts(ks.rotations, ks.sketches, bits, perm=ks.perm)
-    vq = tq.Quantizer.from_parts(vs.rotations, vs.sketches, bits, perm=vs.perm)
 
-    t_setup = time.perf_counter()
-    kc0, vc0 = build_caches(tq, torch, wl, kq, vq, prefix, cap)
-    k_new, v_new = new_tokens(torch, wl, prefix)
-    rb = record_bytes(dims, bits)
-    cache_bytes = B * H * cap * 2 * rb
-    n_copies = args.copies or max(1, math.ceil((1 << 30) / cache_bytes))
-    caches = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(n_copies - 1)]
-    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
-    q = torch.from_numpy(synth.draw_queries(wl)).cuda().to(dt)
-    shape = tq.decode_shape(B, HQ, H, N, cap, wl.scale)
-    ws = torch.empty(tq.tq_attn_decode_workspace_bytes(kq, vq, shape), dtype=torch.uint8, device="cuda")
-    out = torch.empty((B, HQ, d), dtype=torch.float32, device="cuda")
-    torch.cuda.synchronize()
-    log(f"setup {time.perf_counter() - t_setup:.1f}s: {args.workload} B={B} Hq={HQ} Hkv={H} d={d} "
-        f"N={N} bits={bits} dims={dims} copies={n_copies} ({n_copies * cache_bytes / 2**30:.2f} GiB)")
-
-    k_app = tq.append_spec(k_new, seg_len=wl.n_new, seg_stride=cap, seg_offset=prefix)
-    v_app = tq.append_spec(v_new, seg_len=wl.n_new, seg_stride=cap, seg_offset=prefix)
-
-    def step(i, ev=None):
-        # append the new K/V tokens and decode over the whole cache: one
-        # launch for both appends and the query preparation, then the
-        # split-K pass and the combine
-        kc, vc = caches[i % n_copies]
-        if ev is None:
-            tq.tq_attn_decode_append(kq, vq, shape, q, kc, vc, k_new=k_app, v_new=v_app, out=out,
-                                     workspace=ws)
-            return
-        # (the per-phase form, to put events around the split-K pass)
-        tq.tq_quantize(kq, tq.TQ_TOKEN_MAJOR, k_new, kc, seg_len=wl.n_new, seg_stride=cap, seg_offset=prefix)
-        tq.tq_quantize(vq, tq.TQ_BLOCK32, v_new, vc, seg_len=wl.n_new, seg_stride=cap, seg_offset=prefix)
-        tq.tq_attn_decode_phases(tq.TQ_PHASE_PREP, kq, vq, shape, q, kc, vc, out=out, workspace=ws)
-        ev[0].record()
-        tq.tq_attn_decode_phases(tq.TQ_PHASE_SPLIT, kq, vq, shape, q, kc, vc, out=out, workspace=ws)
-        ev[1].record()
-        tq.tq_attn_decode_phases(tq.TQ_PHASE_COMBINE, kq, vq, shape, q, kc, vc, out=out, workspace=ws)
-
-    for i in range(max(args.warmup, n_copies)):
-        step(i)
-    torch.cuda.synchronize()
-
-    # One graph holds a full cycle of steps (one per cache copy); replaying it
-    # removes the host launch cost from the step time. (Event timestamps are
-    # not available inside a captured graph on ROCm, so the split-K kernel is
-    # then timed in its own event-bracketed loop right after.)
-    graph, evs = None, None
-    if not args.no_graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(n_copies):
-                step(i)
-        for _ in range(max(1, args.warmup // n_copies)):
-            graph.replay()
-        torch.cuda.synchronize()
-    t_begin, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = max(1, math.ceil(args.steps / n_copies)) if graph is not None else 0
-    n_steps = reps * n_copies if graph is not None else args.steps
-    split_ms = []
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_begin.record()
-    if graph is not None:
-        for _ in range(reps):
-            graph.replay()
-    else:
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(n_steps)]
-        for i in range(n_steps):
-            step(args.warmup + i, evs[i])
-    t_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_step = t_begin.elapsed_time(t_end) / n_steps
-    if evs is not None:
-        timing_source = "events around the split-K launch in the timed steps"
-        split_ms = [a.elapsed_time(b) for a, b in evs]
-    else:
-        # The split-K pass alone: a graph of one launch per cache copy (the
-        # prepared query in the workspace is the same for every copy), replayed
-        # between two events on the launch stream; the mean is per launch.
-        timing_source = "events around replays of a graph of split-K launches, one per cache copy"
-        split_graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(split_graph):
-            for i in range(n_copies):
-                kc, vc = caches[i]
-                tq.tq_attn_decode_phases(tq.TQ_PHASE_SPLIT, kq, vq, shape, q, kc, vc, out=out, workspace=ws)
-        split_graph.replay()
-        torch.cuda.synchronize()
-        split_reps = max(1, math.ceil(200 / n_copies))
-        for _ in range(5):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(split_reps):
-                split_graph.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            split_ms.append(e0.elapsed_time(e1) / (split_reps * n_copies))
-    split_s = float(np.mean(split_ms)) / 1e3
-    log(f"step {ms_step * 1e3:.2f} us over {n_steps} steps (wall {wall / n_steps * 1e6:.2f} us); "
-        f"split-K kernel mean {split_s * 1e6:.2f} us, median {np.median(split_ms) * 1e3:.2f} us, "
-        f"min {np.min(split_ms) * 1e3:.2f} us "
-        f"[{timing_source}]")
-
-    algo_bytes = B * H * N * 2 * rb  # K and V records of every cached token read by the split-K pass
-    achieved = algo_bytes / split_s / 1e9
-    tr = traffic_record()
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": tr["bytes_per_launch"] if tr and tr.get("workload") == args.workload else None,
-                "kernel": "decode_kernel (split-K pass)", "kernel_us": round(split_s * 1e6, 2),
-                "kernel_timing": timing_source,
-                "algorithmic_bytes": int(algo_bytes)}
+    head, state = decode_leg(tq, torch, wl, args.steps, warmup=args.warmup, copies=args.copies)
+    ms_step = state["ms_step"]
+    tr = traffic_record(args.workload)
+    roofline = {"bound": "hbm", "achieved": head["split_achieved_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": head["split_frac"], "traffic": tr["bytes_per_launch"] if tr else None,
+                "kernel": "decode_kernel (split-K pass)", "kernel_us": head["split_kernel_us"],
+                "kernel_timing": "events around replays of a graph of split-K launches, one per cache copy",
+                "algorithmic_bytes": head["split_algorithmic_bytes"]}
+    dims = [g for g, _ in wl.groups]
+    bits = [m for _, m in wl.groups]
     result = {
         "metric": "compressed-KV decode throughput (cached tokens/s; split-K kernel vs HBM roofline)",
         "value": B * N / (ms_step / 1e3),
         "unit": "cached tokens/s",
-        "n_gpus": 1, "steps": n_steps, "warmup": args.warmup,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": B, "n_q_heads": HQ, "n_kv_heads": H, "d": d,
                    "n_ctx": N, "appended_tokens": wl.n_new, "bits_per_channel": [m + 1 for m in bits],
-                   "group_dims": dims, "record_bytes_per_token": rb, "cache_copies": n_copies,
-                   "input_dtype": wl.dtype, "hip_graph": graph is not None},
+                   "group_dims": dims, "record_bytes_per_token": head["record_bytes_per_token"],
+                   "cache_copies": head["cache_copies"], "input_dtype": wl.dtype, "hip_graph": True},
         "roofline": roofline,
     }
     if args.copy_probe:
@@ -677,20 +765,19 @@ def main():
         torch.cuda.synchronize()
         log(f"copy probe: 3 device copies of {COPY_PROBE_BYTES} bytes")
         del src, dst
-    if not args.no_bf16_baseline:
-        result["bf16_baseline"] = bf16_baseline(tq, torch, wl, q, ms_step)
-        log(f"bf16 baseline: {result['bf16_baseline']}")
     if not args.no_quantize_bench:
-        result["quantize"] = quantize_bench(tq, torch, wl, kq)
+        result["quantize"] = {"chunk": quantize_chunk_bench(tq, torch), "nn_database": quantize_nn_bench(tq, torch)}
         log(f"quantize: {result['quantize']}")
+    if not (args.no_decode_legs or args.no_mixed):
+        result["decode_legs"] = decode_legs(tq, torch, [w for w in DECODE_WORKLOADS if w != args.workload])
+    if not args.no_bf16_baseline:
+        result["bf16_baseline"] = bf16_baseline(tq, torch, wl, state["q"], ms_step)
+        log(f"bf16 baseline: {result['bf16_baseline']}")
     if not args.no_chunk:
         result["chunk"] = chunk_bench(tq, torch)
         log(f"chunk: {result['chunk']}")
         result["paged"] = paged_bench(tq, torch)
         log(f"paged: {result['paged']}")
-    if not args.no_mixed:
-        result["mixed"] = mixed_bench(tq, torch)
-        log(f"mixed: {result['mixed']}")
     if not args.no_variants:
         result["variants"] = variants_bench(tq, torch)
         log(f"variants: {result['variants']}")
