@@ -906,6 +906,455 @@ __global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel
 }
 
 // ---------------------------------------------------------------------------
+// Byte-table split-K kernel: one quantizer group whose code width m divides
+// 8 (m = 1, 2, 4), d = 128. One 512-thread workgroup per compute unit holds
+// two 64 KB LDS tables of 256 rows x 256 bytes, indexed by one byte of a
+// record:
+//   code table  row e: the 8 / m fp16 scaled centroids fp16(s c[code]) of
+//               the codes packed in byte e (K centroids in bytes [0, 128),
+//               V centroids in [128, 256)), each entry replicated across
+//               its half row;
+//   sign table  row e: eight fp16 +-1 for the bits of e (bit 1 -> +1),
+//               replicated 16 times.
+// A lane reads the replica at its own offset within the row, so any mix of
+// rows is read without bank conflicts between the lanes served together,
+// and the LDS address of a lookup is one v_perm_b32: the record byte
+// becomes address bits 8..15, the lane's replica offset bits 0..7 and the
+// table base bit 16. A lane's 8 MFMA operand values of one token (K) or one
+// channel (V) are m lookups of codes and one of signs.
+//
+// Column packing of the 16 MFMA columns:
+//   HB = 8 (KV groups of more than 4 query heads, in blocks of 8 heads):
+//     K codes x [q_rot hi | q_rot lo * 2^11] (8 heads each), K signs x
+//     [q_sk | q_sk]; V codes x [w_n hi | w_n lo * 2^11] and V signs x
+//     [w_g hi | w_g lo * 2^11], with w_n = p n and w_g = p gamma the softmax
+//     weights times the token's norms, split into an fp16 part and its
+//     remainder so that the weights keep about 21 bits;
+//   HB = 4 (at most 4 query heads per KV head): column 4 h + r, role r =
+//     0 q_rot hi / w_n hi, 1 q_rot lo / w_n lo, 2 q_sk / w_g hi, 3 - / w_g lo;
+//     codes and signs accumulate into the same accumulator (their B columns
+//     are disjoint).
+// Each column's lanes form their head's logit (exchanging the hi / lo / sketch
+// parts by DPP), so every lane runs its head's online softmax.
+// ---------------------------------------------------------------------------
+constexpr int kBW = 8;                       // waves per workgroup
+constexpr int kBThreads = 64 * kBW;
+constexpr uint32_t kBSignBase = 1u << 16;    // LDS byte offset of the sign table
+constexpr int kBTabBytes = 2 << 16;          // both tables
+constexpr int kBMerge = 4 * 2 * (128 * 16 + 64) * 4;  // merge regions (reuse the table space)
+constexpr int kBNrm = kBTabBytes;                     // per-wave norm staging [kBW][2][64] floats
+constexpr int kBMisc = kBNrm + kBW * 2 * 64 * 4;      // s_m, s_lw [kBW][8] floats, centroids [2][16]
+constexpr int kBLds = kBMisc + (2 * kBW * 8 + 32) * 4;
+static_assert(kBMerge <= kBTabBytes, "merge regions fit in the table space");
+
+template <int M>
+struct BTab {
+  static constexpr int CPB = 8 / M;     // codes per record byte
+  static constexpr int EB = 2 * CPB;    // entry bytes: CPB fp16 centroids
+  static constexpr int REP = 128 / EB;  // replicas per half row
+};
+
+// LDS byte address of the table row selected by byte k of w, at the lane's
+// replica offset `off` (bits 0..7) and table base (bit 16 of off).
+__device__ __forceinline__ uint32_t baddr(uint32_t w, uint32_t off, int k) {
+  return __builtin_amdgcn_perm(w, off, 0x0C020000u | ((4u + (uint32_t)k) << 8));
+}
+
+// Loads at an absolute LDS byte address (the kernel's dynamic LDS starts at
+// address 0; the launch checks that it has no static LDS).
+template <typename T>
+__device__ __forceinline__ T lds_at(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) T*>((size_t)addr);
+}
+
+// 8 codes of M bits starting at byte b of the word array w -> 8 fp16 (the A
+// operand slots 0..7 in code order)
+template <int M>
+__device__ __forceinline__ u32x4 bcodes8(const uint32_t* w, int b, uint32_t off) {
+  if constexpr (M == 1) {
+    return lds_at<u32x4>(baddr(w[b >> 2], off, b & 3));
+  } else if constexpr (M == 2) {
+    const u32x2 x = lds_at<u32x2>(baddr(w[b >> 2], off, b & 3));
+    const u32x2 y = lds_at<u32x2>(baddr(w[(b + 1) >> 2], off, (b + 1) & 3));
+    return u32x4{x[0], x[1], y[0], y[1]};
+  } else {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = lds_at<uint32_t>(baddr(w[(b + i) >> 2], off, (b + i) & 3));
+    return r;
+  }
+}
+
+// 8 sign bits in byte b of w -> 8 fp16 +-1
+__device__ __forceinline__ u32x4 bsigns8(const uint32_t* w, int b, uint32_t off) {
+  return lds_at<u32x4>(baddr(w[b >> 2], off, b & 3));
+}
+
+// DPP move whose pattern sends every lane a value from inside its row
+// (rotations, quad permutations): no lane keeps its old value.
+template <int CTRL>
+__device__ __forceinline__ float dpp_full(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Weight operand of a column: w split into an fp16 part (its leading 11
+// bits, exact in fp16 for normal magnitudes) and the remainder times 2^11;
+// (bsel, csel) = (0, 1) gives the leading part, (2^11, -2^11) the remainder.
+__device__ __forceinline__ float wsplit(float w, float bsel, float csel) {
+  const float hi = __uint_as_float(__float_as_uint(w) & 0xFFFFE000u);
+  return fmaf(bsel, w, csel * hi);
+}
+
+template <int M, int WV, int HB>
+__global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
+  using G = Geo<128, 1, M, M>;
+  using BT = BTab<M>;
+  constexpr int D = 128, NC = 4, NMT = 8;
+  constexpr bool P8 = HB == 8;
+  // (the kernel has no static LDS: the dynamic area starts at LDS address 0,
+  // so the table addresses formed in registers are used as they are)
+  extern __shared__ __align__(16) unsigned char lds[];
+  float* s_nrm = reinterpret_cast<float*>(lds + kBNrm);
+  float* s_m = reinterpret_cast<float*>(lds + kBMisc);
+  float* s_lw = s_m + kBW * 8;
+  float* s_cent = s_lw + kBW * 8;  // [0, 16) K, [16, 32) V
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ln = lane & 15;
+  const int lg = lane >> 4;
+  const int split = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int hblk = blockIdx.z;
+  const int b = bh / a.hkv;
+  const int kvh = bh % a.hkv;
+  const uint32_t koff = BT::EB * (lane % BT::REP);
+  const uint32_t voff = 128u + BT::EB * (lane % BT::REP);
+  const uint32_t soff = kBSignBase | (16u * (lane & 15));
+
+  int64_t N = a.n_ctx;
+  if (a.seq_lens) {
+    const int64_t n = a.seq_lens[b];
+    N = n < 1 ? 1 : (n > a.n_ctx ? a.n_ctx : n);
+  }
+  const int64_t n_tiles = (N + kTile - 1) / kTile;
+  const int64_t tps = (n_tiles + a.n_split - 1) / a.n_split;
+  const int64_t t_begin = split * tps;
+  const int64_t t_end = t_begin + tps < n_tiles ? t_begin + tps : n_tiles;
+  const int64_t rowbase = (int64_t)bh * a.cap;
+  auto tile_row = [&](int64_t t) __attribute__((always_inline)) -> int64_t {
+    if (!a.block_table) return rowbase + t * kTile;
+    int64_t pb = a.block_table[(int64_t)b * a.max_blocks + t];
+    pb = pb < 0 ? 0 : (pb >= a.n_pblocks ? a.n_pblocks - 1 : pb);
+    return (pb * a.hkv + kvh) * kTile;
+  };
+  const LaneOff<D, 1, M, M> lo = lane_offsets<D, 1, M, M>(ln, lg);
+  NormOff<1> no;
+  no.kb[0] = a.kn_f16 ? 4 * (lane >> 1) : 4 * lane;
+  no.ksh[0] = a.kn_f16 ? 16 * (lane & 1) : 0;
+  no.vb[0] = a.vn_f16 ? 4 * (lane >> 1) : 4 * lane;
+  no.vsh[0] = a.vn_f16 ? 16 * (lane & 1) : 0;
+  // lane l stages float l of a tile's K norms [32][n, gamma]: n / s_K
+  const float kn_mul = (lane & 1) ? 1.0f : 1.0f / a.kscale[0];
+
+  // ---- this lane's column: head and role ----
+  const int hcol = P8 ? (ln & 7) : (ln >> 2);  // head within the block
+  const int role = P8 ? (ln >> 3) : (ln & 3);  // P8: 0 hi, 1 lo; else see above
+  const int hloc = hblk * HB + hcol;
+  const bool hvalid = hloc < a.group;
+  const int hq = kvh * a.group + hloc;
+  u32x4 bq[NC], bs[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const _Float16* qp = a.qprep + ((int64_t)b * a.hq + (hvalid ? hq : 0)) * (3 * D) + 32 * lg + 8 * c;
+    const u32x4 z{0, 0, 0, 0};
+    const u32x4 vh = *reinterpret_cast<const u32x4*>(qp);
+    const u32x4 vl = *reinterpret_cast<const u32x4*>(qp + D);
+    const u32x4 vs = *reinterpret_cast<const u32x4*>(qp + 2 * D);
+    if constexpr (P8) {
+      bq[c] = hvalid ? (role ? vl : vh) : z;
+      bs[c] = hvalid ? vs : z;
+    } else {
+      bq[c] = hvalid && role < 2 ? (role ? vl : vh) : z;
+      bs[c] = hvalid && role == 2 ? vs : z;
+    }
+  }
+  // logit combine factors (P8): hi + 2^-11 lo from this lane's value v and
+  // its partner's o (lane ln ^ 8): fma(ca, o, cb v)
+  const float ca = role ? 1.0f : kLoInv, cb = role ? kLoInv : 1.0f;
+  // weight split factors of this lane's column
+  const bool wlo = P8 ? role != 0 : (role & 1) != 0;
+  const float bsel = wlo ? 2048.0f : 0.0f, csel = wlo ? -2048.0f : 1.0f;
+
+  // ---- first tile in flight while the tables are built ----
+  Raw<D, 1, M, M> rb0, rb1;
+  int64_t tile = t_begin + wv;
+  load_tile<D, 1, M, M, WV>(a, tile_row(tile < t_end ? tile : 0), lane, lo, no, rb0);
+  if (tid < 16) {
+    const int L = 1 << M;
+    const int tc = tid < L ? tid : L - 1;
+    s_cent[tid] = a.kcent[tc] * a.kscale[0];
+    if constexpr (WV != 0) s_cent[16 + tid] = a.vcent[tc] * a.kscale[2];
+  }
+  __syncthreads();
+  {
+    // code table: 256 rows x 16 stores of 16 bytes (8 K, then 8 V)
+    constexpr uint32_t MASK = (1u << M) - 1;
+    for (int i = tid; i < 256 * 16; i += kBThreads) {
+      const int e = i >> 4, k = i & 15;
+      const float* cen = s_cent + (k < 8 ? 0 : 16);
+      uint32_t wd[4];
+      if constexpr (M == 1) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wd[j] = h2bits(cen[(e >> (2 * j)) & 1], cen[(e >> (2 * j + 1)) & 1]);
+      } else if constexpr (M == 2) {
+        wd[0] = wd[2] = h2bits(cen[e & MASK], cen[(e >> 2) & MASK]);
+        wd[1] = wd[3] = h2bits(cen[(e >> 4) & MASK], cen[(e >> 6) & MASK]);
+      } else {
+        wd[0] = wd[1] = wd[2] = wd[3] = h2bits(cen[e & MASK], cen[(e >> 4) & MASK]);
+      }
+      *reinterpret_cast<u32x4*>(lds + e * 256 + 16 * k) = u32x4{wd[0], wd[1], wd[2], wd[3]};
+    }
+    // sign table: 256 rows x 16 replicas of eight fp16 +-1
+    for (int i = tid; i < 256 * 16; i += kBThreads) {
+      const int e = i >> 4, k = i & 15;
+      uint32_t wd[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        wd[j] = (((e >> (2 * j)) & 1) ? 0x3C00u : 0xBC00u) | (((e >> (2 * j + 1)) & 1) ? 0x3C000000u : 0xBC000000u);
+      *reinterpret_cast<u32x4*>(lds + kBSignBase + e * 256 + 16 * k) = u32x4{wd[0], wd[1], wd[2], wd[3]};
+    }
+  }
+  __syncthreads();
+
+  float m_run = -INFINITY, l_run = 0.f;
+  constexpr int NVA = WV ? NMT : 1;
+  f32x4 avr[NVA], avs[WV && P8 ? NMT : 1];
+#pragma unroll
+  for (int v = 0; v < NVA; ++v) avr[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int v = 0; v < (WV && P8 ? NMT : 1); ++v) avs[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float* nrm_k = s_nrm + wv * 128;
+  float* nrm_v = nrm_k + 64;
+
+  auto compute = [&](const Raw<D, 1, M, M>& r, int64_t T0) __attribute__((always_inline)) {
+    const bool full = T0 + kTile <= N;
+    {
+      const bool nok = full || T0 + (lane >> 1) < N;
+      nrm_k[lane] = nok ? norm_value(r.kn[0], no.ksh[0], a.kn_f16) * kn_mul : 0.f;
+      if constexpr (WV != 0) nrm_v[lane] = nok ? norm_value(r.vn[0], no.vsh[0], a.vn_f16) : 0.f;
+    }
+    __builtin_amdgcn_wave_barrier();
+    // ---------------- K: logits ----------------
+    f32x4 ak[2], as[P8 ? 2 : 1];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      ak[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (P8) as[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const u32x4 kc = bcodes8<M>(r.kc[tau], M * c, koff);
+        const u32x4 ks = bsigns8(r.ks[tau], c, soff);
+        ak[tau] = mfma16(kc, bq[c], ak[tau]);
+        if constexpr (P8)
+          as[tau] = mfma16(ks, bs[c], as[tau]);
+        else
+          ak[tau] = mfma16(ks, bs[c], ak[tau]);
+      }
+    }
+    const int64_t tok0 = T0 + 8 * lg;
+    float kn[8][2];
+    load_norms<1>(nrm_k + 16 * lg, kn);
+    float l2[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int tau = j >> 2, i = j & 3;
+      const float v = ak[tau][i];
+      if constexpr (P8) {
+        const float o = dpp_full<0x128>(v);  // row_ror:8: the partner column ln ^ 8
+        l2[j] = fmaf(kn[j][1], as[tau][i], kn[j][0] * fmaf(ca, o, cb * v));
+      } else {
+        // quad_perm broadcasts of the quad's role 0, 1 and 2 columns
+        const float v0 = dpp_full<0x00>(v), v1 = dpp_full<0x55>(v), v2 = dpp_full<0xAA>(v);
+        l2[j] = fmaf(kn[j][1], v2, kn[j][0] * fmaf(kLoInv, v1, v0));
+      }
+    }
+    const int nvt = full ? kTile : (int)(N - T0);
+    if (a.T > 1) {
+      const int64_t lim = N - a.T + hloc % a.T + 1;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) l2[j] = tok0 + j < lim ? l2[j] : -INFINITY;
+    }
+    if (a.logits) {
+      if (hvalid && role == 0) {
+        float* lp = a.logits + ((int64_t)b * a.hq + hq) * a.n_ctx + tok0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (8 * lg + j < nvt) lp[j] = l2[j] * kLn2;
+      }
+    }
+    if (!full) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) l2[j] = 8 * lg + j < nvt ? l2[j] : -INFINITY;
+    }
+    if constexpr (WV != 0) {
+      // ---------------- online softmax (every lane: its column's head) ----------------
+      float mx = l2[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) mx = fmaxf(mx, l2[j]);
+      mx = rows4_max(mx);
+      // integer log2-domain reference: weights and rescales are exact powers
+      // of two times the same mantissa, independent of the split count
+      const float m_new = fmaxf(m_run, ceilf(mx));
+      if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+        const float corr = m_new == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= corr;
+#pragma unroll
+        for (int v = 0; v < NMT; ++v) avr[v] *= corr;
+        if constexpr (P8) {
+#pragma unroll
+          for (int v = 0; v < NMT; ++v) avs[v] *= corr;
+        }
+        m_run = m_new;
+      }
+      float p[8], psum;
+      const float m_ref = m_run == -INFINITY ? 0.f : m_run;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        p[j] = __builtin_amdgcn_exp2f(l2[j] - m_ref);
+        psum = j == 0 ? p[j] : psum + p[j];
+      }
+      l_run += psum;
+      float vn[8][2];
+      load_norms<1>(nrm_v + 16 * lg, vn);
+      u32x4 bvc, bvs;
+      if constexpr (P8) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int j0 = 2 * q, j1 = 2 * q + 1;
+          bvc[q] = h2bits(wsplit(p[j0] * vn[j0][0], bsel, csel), wsplit(p[j1] * vn[j1][0], bsel, csel));
+          bvs[q] = h2bits(wsplit(p[j0] * vn[j0][1], bsel, csel), wsplit(p[j1] * vn[j1][1], bsel, csel));
+        }
+      } else {
+        const bool gsel = role >= 2;
+        u32x4 w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int j0 = 2 * q, j1 = 2 * q + 1;
+          const float n0 = gsel ? vn[j0][1] : vn[j0][0], n1 = gsel ? vn[j1][1] : vn[j1][0];
+          w[q] = h2bits(wsplit(p[j0] * n0, bsel, csel), wsplit(p[j1] * n1, bsel, csel));
+        }
+        const u32x4 z{0, 0, 0, 0};
+        bvc = gsel ? z : w;
+        bvs = gsel ? w : z;
+      }
+      // ---------------- V: accumulate in the rotated / sketch domains ----------------
+#pragma unroll
+      for (int u = 0; u < NMT; ++u) {
+        const u32x4 vc = bcodes8<M>(r.vc, M * u, voff);
+        avr[u] = mfma16(vc, bvc, avr[u]);
+        if constexpr (WV == 1) {
+          const u32x4 vs = bsigns8(r.vs, u, soff);
+          if constexpr (P8)
+            avs[u] = mfma16(vs, bvs, avs[u]);
+          else
+            avr[u] = mfma16(vs, bvs, avr[u]);
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  if (tile < t_end) {
+    const int64_t last = t_end - 1 - ((t_end - 1 - tile) % kBW);
+    auto next = [&](int64_t t) { return t + kBW <= last ? t + kBW : last; };
+    for (;;) {
+      load_tile<D, 1, M, M, WV>(a, tile_row(next(tile)), lane, lo, no, rb1);
+      compute(rb0, tile * kTile);
+      if (tile == last) break;
+      tile += kBW;
+      load_tile<D, 1, M, M, WV>(a, tile_row(next(tile)), lane, lo, no, rb0);
+      compute(rb1, tile * kTile);
+      if (tile == last) break;
+      tile += kBW;
+    }
+  }
+
+  if constexpr (WV != 0) {
+    // ---- merge the eight waves into one partial per head ----
+    // Region r (0..3) holds, per part (code / sign accumulator) and channel,
+    // the 16 columns of waves r and r + 4 scaled to the workgroup maximum:
+    // float (part, ch, col) at part (128 16 + 64) + 16 ch + col + 16 (ch / 32),
+    // so the 64 lanes of one store fall in 64 different banks.
+    constexpr int PS = 128 * 16 + 64, RS = 2 * PS;
+    float* s_red = reinterpret_cast<float*>(lds);
+    __syncthreads();  // tables are no longer read
+    l_run = rows4_sum(l_run);
+    if (lg == 0 && role == 0) s_m[wv * 8 + hcol] = m_run;
+    __syncthreads();
+    float Mh = s_m[hcol];
+#pragma unroll
+    for (int w = 1; w < kBW; ++w) Mh = fmaxf(Mh, s_m[w * 8 + hcol]);
+    const float e = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - Mh);
+    if (lg == 0 && role == 0) s_lw[wv * 8 + hcol] = l_run * e;
+    float* reg = s_red + (wv & 3) * RS;
+    auto put = [&](bool add) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < NMT; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ch = 8 * (4 * lg + i) + u;
+          const int idx = 16 * ch + ln + 16 * (ch >> 5);
+          if (add) {
+            reg[idx] += avr[u][i] * e;
+            if constexpr (P8) reg[PS + idx] += avs[u][i] * e;
+          } else {
+            reg[idx] = avr[u][i] * e;
+            if constexpr (P8) reg[PS + idx] = avs[u][i] * e;
+          }
+        }
+    };
+    if (wv < 4) put(false);
+    __syncthreads();
+    if (wv >= 4) put(true);
+    __syncthreads();
+    // partial of every valid head: [max (log2 domain), sum, acc_rot[D] / s_V, acc_sk[D]]
+    const int nh = a.group - hblk * HB < HB ? a.group - hblk * HB : HB;
+    const float vinv = 1.0f / a.kscale[2];
+    for (int e2 = tid; e2 < nh * (2 + 2 * D); e2 += kBThreads) {
+      const int h = e2 / (2 + 2 * D), k = e2 % (2 + 2 * D);
+      float val;
+      if (k < 2) {
+        float Mx = s_m[h];
+#pragma unroll
+        for (int w = 1; w < kBW; ++w) Mx = fmaxf(Mx, s_m[w * 8 + h]);
+        float L = 0.f;
+#pragma unroll
+        for (int w = 0; w < kBW; ++w) L += s_lw[w * 8 + h];
+        val = k == 0 ? Mx : L;
+      } else {
+        const int pt = (k - 2) / D, ch = (k - 2) % D;
+        // columns of the leading and remainder parts
+        const int part = P8 ? pt : 0;
+        const int chi = P8 ? h : 4 * h + 2 * pt, clo = P8 ? h + 8 : 4 * h + 2 * pt + 1;
+        const int base = part * PS + 16 * ch + 16 * (ch >> 5);
+        float hi = 0.f, lo = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          hi += s_red[r * RS + base + chi];
+          lo += s_red[r * RS + base + clo];
+        }
+        val = fmaf(kLoInv, lo, hi);
+        if (pt == 0) val *= vinv;
+      }
+      const int hq2 = kvh * a.group + hblk * HB + h;
+      a.part[(((int64_t)b * a.hq + hq2) * a.n_split + split) * (2 + 2 * D) + k] = val;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Query preparation (see tq_prep_dev.h), 256 threads per block.
 // ---------------------------------------------------------------------------
 template <int D>
@@ -1093,6 +1542,77 @@ size_t workspace_for(const tq_decode_shape* s, int d, bool with_v, int n_split) 
 // heads with V, else 16
 inline int heads_per_block(int group, bool with_v) { return with_v && group <= 4 ? 4 : 16; }
 
+// The byte-table kernel takes one quantizer group of d = 128 whose code
+// width divides 8.
+inline bool byte_kernel_ok(const tq_layout& l) {
+  const int m = l.mse_bits[0];
+  return l.d == 128 && l.n_groups == 1 && (m == 1 || m == 2 || m == 4);
+}
+
+// Kernel, head block and split count of a decode call (the workspace size
+// and the launch both follow from it).
+struct DecodeCfg {
+  bool byte;
+  int hb, n_hblk, n_split;
+};
+
+DecodeCfg decode_cfg(const tq_layout& l, bool with_v, const tq_decode_shape* s) {
+  DecodeCfg c{};
+  const int T = s->n_q_tokens < 1 ? 1 : s->n_q_tokens;
+  const int group = s->n_q_heads / s->n_kv_heads * T;
+  c.byte = byte_kernel_ok(l);
+  c.hb = c.byte ? (group <= 4 ? 4 : 8) : heads_per_block(group, with_v);
+  c.n_hblk = (group + c.hb - 1) / c.hb;
+  if (!c.byte) {
+    c.n_split = choose_split(s, c.n_hblk);
+    return c;
+  }
+  // one workgroup per compute unit; at least one tile per wave
+  const int64_t n_tiles = (s->n_ctx + kTile - 1) / kTile;
+  int64_t max_split = (n_tiles + kBW - 1) / kBW;
+  if (max_split > kMaxSplit) max_split = kMaxSplit;
+  if (max_split < 1) max_split = 1;
+  if (s->n_split > 0) {
+    c.n_split = (int)(s->n_split < max_split ? s->n_split : max_split);
+    return c;
+  }
+  const int64_t per = (int64_t)s->batch * s->n_kv_heads * c.n_hblk;
+  int64_t want = (256 + per - 1) / per;
+  if (want > max_split) want = max_split;
+  if (want < 1) want = 1;
+  c.n_split = (int)want;
+  return c;
+}
+
+template <int M, int WV, int HB>
+hipError_t launch_byte(const DArgs& a, int n_hblk, hipStream_t st) {
+  const void* fn = reinterpret_cast<const void*>(&decode_byte_kernel<M, WV, HB>);
+  // the table addresses are absolute LDS addresses: the kernel must have no
+  // static LDS, so that its dynamic LDS starts at address 0
+  hipFuncAttributes fa;
+  if (hipFuncGetAttributes(&fa, fn) != hipSuccess || fa.sharedSizeBytes != 0) return hipErrorInvalidValue;
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kBLds) != hipSuccess)
+    return hipErrorInvalidValue;
+  (void)hipGetLastError();  // a launch error is reported below, not an older one
+  const dim3 grid((unsigned)a.n_split, (unsigned)(a.batch * a.hkv), (unsigned)n_hblk);
+  hipLaunchKernelGGL((decode_byte_kernel<M, WV, HB>), grid, dim3(kBThreads), kBLds, st, a);
+  return hipGetLastError();
+}
+
+template <int M, int WV>
+hipError_t dispatch_byte_hb(const DArgs& a, int hb, int n_hblk, hipStream_t st) {
+  return hb == 4 ? launch_byte<M, WV, 4>(a, n_hblk, st) : launch_byte<M, WV, 8>(a, n_hblk, st);
+}
+
+template <int WV>
+hipError_t dispatch_byte(const DArgs& a, int m, int hb, int n_hblk, hipStream_t st) {
+  switch (m) {
+    case 1: return dispatch_byte_hb<1, WV>(a, hb, n_hblk, st);
+    case 2: return dispatch_byte_hb<2, WV>(a, hb, n_hblk, st);
+    default: return dispatch_byte_hb<4, WV>(a, hb, n_hblk, st);
+  }
+}
+
 template <int D, int NG, int M0, int M1, int WV>
 hipError_t launch_decode(const DArgs& a, int n_hblk, hipStream_t st) {
   (void)hipGetLastError();  // a launch error is reported below, not an older one
@@ -1143,10 +1663,8 @@ extern "C" tq_status tq_attn_decode_workspace_bytes(const tq_quantizer* kq, cons
                                                     const tq_decode_shape* shape, size_t* bytes) {
   if (!kq || !tq::layout_valid(&kq->layout) || !shape_valid(shape) || !bytes) return TQ_ERR_INVALID;
   if (vq && !tq::layout_valid(&vq->layout)) return TQ_ERR_INVALID;
-  const int grp = shape->n_q_heads / shape->n_kv_heads * q_tokens(shape);
-  const int hb = heads_per_block(grp, vq != nullptr);
-  const int n_hblk = (grp + hb - 1) / hb;
-  *bytes = workspace_for(shape, kq->layout.d, vq != nullptr, choose_split(shape, n_hblk));
+  const DecodeCfg cfg = decode_cfg(kq->layout, vq != nullptr, shape);
+  *bytes = workspace_for(shape, kq->layout.d, vq != nullptr, cfg.n_split);
   return TQ_OK;
 }
 
@@ -1156,8 +1674,9 @@ namespace {
 struct Plan {
   DArgs a;
   tqp::PrepArgs prep;
-  int n_hblk, prep_grid_y, n_heads, n_groups, m0, m1, group_dim0, T, hq_orig;
+  int n_hblk, hb, prep_grid_y, n_heads, n_groups, m0, m1, group_dim0, T, hq_orig;
   bool with_v, v_mse;  // V records present; V records without sign bits
+  bool byte;           // the byte-table split-K kernel
   const float* vrot;
   const float* vsketch;
   float* out;
@@ -1204,9 +1723,10 @@ tq_status plan_decode(const tq_quantizer* kq, const tq_quantizer* vq, const tq_d
   const tq_layout& l = kq->layout;
   const int T = q_tokens(shape);
   const int group = shape->n_q_heads / shape->n_kv_heads * T;  // (q head, query token) columns per KV head
-  const int hb = heads_per_block(group, with_v);
-  const int n_hblk = (group + hb - 1) / hb;
-  const int n_split = choose_split(shape, n_hblk);
+  (void)group;
+  const DecodeCfg cfg = decode_cfg(l, with_v, shape);
+  const int n_hblk = cfg.n_hblk;
+  const int n_split = cfg.n_split;
   const size_t need = workspace_for(shape, l.d, with_v, n_split);
   if (!workspace || workspace_bytes < need) return TQ_ERR_WORKSPACE;
 
@@ -1219,6 +1739,8 @@ tq_status plan_decode(const tq_quantizer* kq, const tq_quantizer* vq, const tq_d
 
   *pl = Plan{};
   pl->n_hblk = n_hblk;
+  pl->hb = cfg.hb;
+  pl->byte = cfg.byte;
   pl->n_heads = n_heads;
   pl->n_groups = l.n_groups;
   pl->m0 = l.mse_bits[0];
@@ -1242,6 +1764,7 @@ tq_status plan_decode(const tq_quantizer* kq, const tq_quantizer* vq, const tq_d
   pp.m0 = pl->m0;
   pp.m1 = pl->m1;
   pp.kscale = kscale;
+  pp.vcent = with_v ? vq->centroids : nullptr;
   pp.T = T;
   pp.hq = shape->n_q_heads;
   pl->T = T;
@@ -1301,7 +1824,11 @@ tq_status run_phases(const Plan& pl, unsigned phases, hipStream_t st) {
   }
   if (phases & TQ_PHASE_SPLIT) {
     hipError_t e;
-    if (pl.n_groups == 1)
+    if (pl.byte)
+      e = !pl.with_v  ? dispatch_byte<0>(pl.a, pl.m0, pl.hb, pl.n_hblk, st)
+          : pl.v_mse ? dispatch_byte<2>(pl.a, pl.m0, pl.hb, pl.n_hblk, st)
+                     : dispatch_byte<1>(pl.a, pl.m0, pl.hb, pl.n_hblk, st);
+    else if (pl.n_groups == 1)
       e = !pl.with_v  ? dispatch_m0<D, 1, 0>(pl.a, pl.m0, 0, pl.n_hblk, st)
           : pl.v_mse ? dispatch_m0<D, 1, 2>(pl.a, pl.m0, 0, pl.n_hblk, st)
                      : dispatch_m0<D, 1, 1>(pl.a, pl.m0, 0, pl.n_hblk, st);

@@ -7,7 +7,8 @@
 // scaled after the sum. A block takes kPrepRows rows of the stacked
 // [rot; sketch] matrix and kPrepHeads heads; both are staged in LDS by
 // coalesced 16-byte loads, then each thread forms dot products of one row
-// with several heads. One extra block searches the K codebook scales.
+// with several heads. One extra block searches the K (and V) codebook
+// scales.
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -34,7 +35,8 @@ struct PrepArgs {
   _Float16* qprep;
   const float* kcent;
   int n_groups, m0, m1;
-  float* kscale;  // out: one scale per K group
+  float* kscale;  // out: one scale per K group, then (when vcent is set) one per V group at kscale + 2
+  const float* vcent;  // V centroids (same layout as K), or null
   // query tokens per head (T > 1: heads are ordered (batch, q head, token)
   // while q rows are (batch, token, q head)), and the q heads per batch
   int T, hq;
@@ -120,6 +122,10 @@ __device__ void prep_block(const PrepArgs& p, int bx, int by, int t, unsigned ch
     if (by == 0) {
       search_fp16_scale<NTHR>(p.kcent, 1 << p.m0, p.kscale, t, smem);
       if (p.n_groups > 1) search_fp16_scale<NTHR>(p.kcent + (1 << p.m0), 1 << p.m1, p.kscale + 1, t, smem);
+      if (p.vcent) {
+        search_fp16_scale<NTHR>(p.vcent, 1 << p.m0, p.kscale + 2, t, smem);
+        if (p.n_groups > 1) search_fp16_scale<NTHR>(p.vcent + (1 << p.m0), 1 << p.m1, p.kscale + 3, t, smem);
+      }
     }
     return;
   }
