@@ -937,6 +937,9 @@ __global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel
 // Each column's lanes form their head's logit (exchanging the hi / lo / sketch
 // parts by DPP), so every lane runs its head's online softmax.
 // ---------------------------------------------------------------------------
+#ifndef TQ_BYTE_NBUF
+#define TQ_BYTE_NBUF 2
+#endif
 constexpr int kBW = 8;                       // waves per workgroup
 constexpr int kBThreads = 64 * kBW;
 constexpr uint32_t kBSignBase = 1u << 16;    // LDS byte offset of the sign table
@@ -1005,9 +1008,20 @@ __device__ __forceinline__ float wsplit(float w, float bsel, float csel) {
   return fmaf(bsel, w, csel * hi);
 }
 
+// Record words of one 32-token tile held by one lane of the byte-table
+// kernel (the K rows of token rows r and r + 4, the lane's share of the
+// tile's norms, and the lane's V block fields).
+template <int M>
+struct BRaw {
+  uint32_t kc[2][M];    // K codes of the lane's 32 channels, token rows r, r + 4
+  uint32_t ks[2];       // K sign words, same rows
+  uint32_t kn, vn;      // word holding norm value `lane` of the tile's [32][n, gamma] (K, V)
+  uint32_t vc[2 * M];   // V codes: octet lg, channels 8 ln .. 8 ln + 7
+  uint32_t vs[2];       // V signs, same channels
+};
+
 template <int M, int WV, int HB>
 __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
-  using G = Geo<128, 1, M, M>;
   using BT = BTab<M>;
   constexpr int D = 128, NC = 4, NMT = 8;
   constexpr bool P8 = HB == 8;
@@ -1029,8 +1043,6 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
   const int hblk = blockIdx.z;
   const int b = bh / a.hkv;
   const int kvh = bh % a.hkv;
-  const uint32_t koff = BT::EB * (lane % BT::REP);
-  const uint32_t voff = 128u + BT::EB * (lane % BT::REP);
   const uint32_t soff = kBSignBase | (16u * (lane & 15));
 
   int64_t N = a.n_ctx;
@@ -1049,18 +1061,83 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
     pb = pb < 0 ? 0 : (pb >= a.n_pblocks ? a.n_pblocks - 1 : pb);
     return (pb * a.hkv + kvh) * kTile;
   };
-  const LaneOff<D, 1, M, M> lo = lane_offsets<D, 1, M, M>(ln, lg);
-  NormOff<1> no;
-  no.kb[0] = a.kn_f16 ? 4 * (lane >> 1) : 4 * lane;
-  no.ksh[0] = a.kn_f16 ? 16 * (lane & 1) : 0;
-  no.vb[0] = a.vn_f16 ? 4 * (lane >> 1) : 4 * lane;
-  no.vsh[0] = a.vn_f16 ? 16 * (lane & 1) : 0;
+  // Code table rows: when the K and V scaled codebooks are equal (equal
+  // layouts have equal Lloyd-Max codebooks), a row holds one entry
+  // replicated across all 256 bytes and K and V read the same replica;
+  // otherwise K entries fill bytes [0, 128) and V entries [128, 256).
+  // (The b64 reads of m = 2 serve 32 lanes together: a full-row replica per
+  // lane keeps them free of bank conflicts.)
+  bool shared_tab = true;
+  if constexpr (WV != 0) {
+    const int L = 1 << M;
+    for (int i = 0; i < L; ++i)
+      shared_tab = shared_tab && a.kcent[i] * a.kscale[0] == a.vcent[i] * a.kscale[2];
+  }
+  const uint32_t koff = shared_tab ? BT::EB * (lane % (2 * BT::REP)) : BT::EB * (lane % BT::REP);
+  const uint32_t voff = shared_tab ? koff : 128u + BT::EB * (lane % BT::REP);
+  // Per-lane byte offsets inside a tile (32-bit; the tile's base addresses
+  // are wave-uniform). MFMA row ln of the logit products is token row
+  // 8 (ln / 4) + ln % 4 (tau = 0) or that + 4 (tau = 1), lane group lg takes
+  // channels 32 lg .. 32 lg + 31, so a lane's K words of a row are M code
+  // words and one sign word; its V fields are octet lg, channels 8 ln ...
+  const uint32_t r0 = 8u * (ln >> 2) + (ln & 3);
+  const uint32_t okc = r0 * (16u * M) + 4u * M * lg, oks = r0 * 16u + 4u * lg;
+  const uint32_t okn = a.kn_f16 ? 4u * (lane >> 1) : 4u * lane;
+  const uint32_t ovn = a.vn_f16 ? 4u * (lane >> 1) : 4u * lane;
+  const uint32_t kn_sh = a.kn_f16 ? 16u * (lane & 1) : 0u, vn_sh = a.vn_f16 ? 16u * (lane & 1) : 0u;
+  const uint32_t ovc = M * (128u * lg + 8u * ln), ovs = 4u * (32u * lg + 2u * ln);
+  auto load = [&](int64_t row0, BRaw<M>& r) __attribute__((always_inline)) {
+    const char* kc = reinterpret_cast<const char*>(a.kc) + row0 * (16 * M);
+    const char* ks = reinterpret_cast<const char*>(a.ks) + row0 * 16;
+    const char* kn = reinterpret_cast<const char*>(a.kn) + (row0 << a.kn_shift);
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      const uint32_t ok = okc + tau * (64u * M);
+      if constexpr (M == 1) {
+        r.kc[tau][0] = *reinterpret_cast<const uint32_t*>(kc + ok);
+      } else if constexpr (M == 2) {
+        const u32x2a4 v = *reinterpret_cast<const u32x2a4*>(kc + ok);
+        r.kc[tau][0] = v[0];
+        r.kc[tau][1] = v[1];
+      } else {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(kc + ok);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r.kc[tau][i] = v[i];
+      }
+      r.ks[tau] = *reinterpret_cast<const uint32_t*>(ks + oks + tau * 64u);
+    }
+    r.kn = *reinterpret_cast<const uint32_t*>(kn + okn);
+    if constexpr (WV != 0) {
+      const int64_t blk = row0 >> 5;
+      const char* vc = reinterpret_cast<const char*>(a.vc) + blk * (512 * M);
+      const char* vn = reinterpret_cast<const char*>(a.vn) + (row0 << a.vn_shift);
+      if constexpr (M == 1) {
+        const u32x2a4 v = *reinterpret_cast<const u32x2a4*>(vc + ovc);
+        r.vc[0] = v[0];
+        r.vc[1] = v[1];
+      } else {
+#pragma unroll
+        for (int h = 0; h < M / 2; ++h) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(vc + ovc + 16u * h);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) r.vc[4 * h + i] = v[i];
+        }
+      }
+      if constexpr (WV == 1) {
+        const char* vs = reinterpret_cast<const char*>(a.vs) + blk * 512;
+        const u32x2a4 v = *reinterpret_cast<const u32x2a4*>(vs + ovs);
+        r.vs[0] = v[0];
+        r.vs[1] = v[1];
+      }
+      r.vn = *reinterpret_cast<const uint32_t*>(vn + ovn);
+    }
+  };
   // lane l stages float l of a tile's K norms [32][n, gamma]: n / s_K
   const float kn_mul = (lane & 1) ? 1.0f : 1.0f / a.kscale[0];
 
   // ---- this lane's column: head and role ----
   const int hcol = P8 ? (ln & 7) : (ln >> 2);  // head within the block
-  const int role = P8 ? (ln >> 3) : (ln & 3);  // P8: 0 hi, 1 lo; else see above
+  const int role = P8 ? (ln >> 3) : (ln & 3);  // P8: 0 hi, 1 lo; else 0 n hi, 1 n lo, 2 gamma hi, 3 gamma lo
   const int hloc = hblk * HB + hcol;
   const bool hvalid = hloc < a.group;
   const int hq = kvh * a.group + hloc;
@@ -1083,14 +1160,34 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
   // logit combine factors (P8): hi + 2^-11 lo from this lane's value v and
   // its partner's o (lane ln ^ 8): fma(ca, o, cb v)
   const float ca = role ? 1.0f : kLoInv, cb = role ? kLoInv : 1.0f;
-  // weight split factors of this lane's column
+  // weight split factors of this lane's column (the code-part weights p n
+  // always; P8 gives the sign-part weights p gamma in plain fp16)
   const bool wlo = P8 ? role != 0 : (role & 1) != 0;
   const float bsel = wlo ? 2048.0f : 0.0f, csel = wlo ? -2048.0f : 1.0f;
 
-  // ---- first tile in flight while the tables are built ----
-  Raw<D, 1, M, M> rb0, rb1;
+  // ---- the first NB - 1 tiles in flight while the tables are built ----
+  // Tile i of this wave uses buffer i mod NB; the load of tile i + NB - 1
+  // reuses the buffer of tile i - 1.
+  constexpr int NB = TQ_BYTE_NBUF;
+  BRaw<M> rb0, rb1, rb2, rb3;
+  auto rbuf = [&](auto kc) __attribute__((always_inline)) -> BRaw<M>& {
+    constexpr int k = decltype(kc)::value % NB;
+    if constexpr (k == 0) return rb0;
+    else if constexpr (k == 1) return rb1;
+    else if constexpr (k == 2) return rb2;
+    else return rb3;
+  };
   int64_t tile = t_begin + wv;
-  load_tile<D, 1, M, M, WV>(a, tile_row(tile < t_end ? tile : 0), lane, lo, no, rb0);
+  const int64_t last = tile < t_end ? t_end - 1 - ((t_end - 1 - tile) % kBW) : 0;  // this wave's last tile
+  // (a wave without tiles loads tile 0, which always exists, and drops it;
+  // past the last tile the prefetch reloads it)
+  auto ahead = [&](int k) __attribute__((always_inline)) -> int64_t {
+    if (tile >= t_end) return 0;
+    return tile + k * kBW <= last ? tile + k * kBW : last;
+  };
+  load(tile_row(ahead(0)), rb0);
+  if constexpr (NB > 2) load(tile_row(ahead(1)), rb1);
+  if constexpr (NB > 3) load(tile_row(ahead(2)), rb2);
   if (tid < 16) {
     const int L = 1 << M;
     const int tc = tid < L ? tid : L - 1;
@@ -1103,7 +1200,7 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
     constexpr uint32_t MASK = (1u << M) - 1;
     for (int i = tid; i < 256 * 16; i += kBThreads) {
       const int e = i >> 4, k = i & 15;
-      const float* cen = s_cent + (k < 8 ? 0 : 16);
+      const float* cen = s_cent + (k < 8 || shared_tab ? 0 : 16);
       uint32_t wd[4];
       if constexpr (M == 1) {
 #pragma unroll
@@ -1138,15 +1235,16 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
   float* nrm_k = s_nrm + wv * 128;
   float* nrm_v = nrm_k + 64;
 
-  auto compute = [&](const Raw<D, 1, M, M>& r, int64_t T0) __attribute__((always_inline)) {
+  // K part of a tile: logits, online softmax, and the V weight operands
+  // (bvc: code product, bvs: sign product) of its tokens.
+  auto kpart = [&](const BRaw<M>& r, int64_t T0, u32x4& bvc, u32x4& bvs) __attribute__((always_inline)) {
     const bool full = T0 + kTile <= N;
     {
       const bool nok = full || T0 + (lane >> 1) < N;
-      nrm_k[lane] = nok ? norm_value(r.kn[0], no.ksh[0], a.kn_f16) * kn_mul : 0.f;
-      if constexpr (WV != 0) nrm_v[lane] = nok ? norm_value(r.vn[0], no.vsh[0], a.vn_f16) : 0.f;
+      nrm_k[lane] = nok ? norm_value(r.kn, kn_sh, a.kn_f16) * kn_mul : 0.f;
+      if constexpr (WV != 0) nrm_v[lane] = nok ? norm_value(r.vn, vn_sh, a.vn_f16) : 0.f;
     }
     __builtin_amdgcn_wave_barrier();
-    // ---------------- K: logits ----------------
     f32x4 ak[2], as[P8 ? 2 : 1];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
@@ -1155,7 +1253,7 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         const u32x4 kc = bcodes8<M>(r.kc[tau], M * c, koff);
-        const u32x4 ks = bsigns8(r.ks[tau], c, soff);
+        const u32x4 ks = bsigns8(&r.ks[tau], c, soff);
         ak[tau] = mfma16(kc, bq[c], ak[tau]);
         if constexpr (P8)
           as[tau] = mfma16(ks, bs[c], as[tau]);
@@ -1166,48 +1264,54 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
     const int64_t tok0 = T0 + 8 * lg;
     float kn[8][2];
     load_norms<1>(nrm_k + 16 * lg, kn);
-    float l2[8];
+    // logits relative to the running integer reference (log2 domain):
+    // t = logit - m_ref, folded into the last fma
+    const float m_ref = m_run == -INFINITY ? 0.f : m_run;
+    float t2[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int tau = j >> 2, i = j & 3;
       const float v = ak[tau][i];
       if constexpr (P8) {
         const float o = dpp_full<0x128>(v);  // row_ror:8: the partner column ln ^ 8
-        l2[j] = fmaf(kn[j][1], as[tau][i], kn[j][0] * fmaf(ca, o, cb * v));
+        t2[j] = fmaf(kn[j][1], as[tau][i], fmaf(kn[j][0], fmaf(ca, o, cb * v), -m_ref));
       } else {
         // quad_perm broadcasts of the quad's role 0, 1 and 2 columns
         const float v0 = dpp_full<0x00>(v), v1 = dpp_full<0x55>(v), v2 = dpp_full<0xAA>(v);
-        l2[j] = fmaf(kn[j][1], v2, kn[j][0] * fmaf(kLoInv, v1, v0));
+        t2[j] = fmaf(kn[j][1], v2, fmaf(kn[j][0], fmaf(kLoInv, v1, v0), -m_ref));
       }
     }
     const int nvt = full ? kTile : (int)(N - T0);
     if (a.T > 1) {
       const int64_t lim = N - a.T + hloc % a.T + 1;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) l2[j] = tok0 + j < lim ? l2[j] : -INFINITY;
+      for (int j = 0; j < 8; ++j) t2[j] = tok0 + j < lim ? t2[j] : -INFINITY;
     }
     if (a.logits) {
       if (hvalid && role == 0) {
         float* lp = a.logits + ((int64_t)b * a.hq + hq) * a.n_ctx + tok0;
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-          if (8 * lg + j < nvt) lp[j] = l2[j] * kLn2;
+          if (8 * lg + j < nvt) lp[j] = (t2[j] + m_ref) * kLn2;
       }
     }
     if (!full) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) l2[j] = 8 * lg + j < nvt ? l2[j] : -INFINITY;
+      for (int j = 0; j < 8; ++j) t2[j] = 8 * lg + j < nvt ? t2[j] : -INFINITY;
     }
     if constexpr (WV != 0) {
       // ---------------- online softmax (every lane: its column's head) ----------------
-      float mx = l2[0];
+      float mx = t2[0];
 #pragma unroll
-      for (int j = 1; j < 8; ++j) mx = fmaxf(mx, l2[j]);
+      for (int j = 1; j < 8; ++j) mx = fmaxf(mx, t2[j]);
       mx = rows4_max(mx);
       // integer log2-domain reference: weights and rescales are exact powers
       // of two times the same mantissa, independent of the split count
-      const float m_new = fmaxf(m_run, ceilf(mx));
-      if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+      const float m_cand = m_ref + ceilf(mx);
+      if (__builtin_amdgcn_ballot_w64(m_cand > m_run) != 0) {
+        // some head's maximum moved: rescale (factor 1 for the others; a
+        // head that has seen only masked tokens keeps -inf and factor 1)
+        const float m_new = fmaxf(m_run, m_cand);
         const float corr = m_new == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= corr;
 #pragma unroll
@@ -1218,23 +1322,23 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
         }
         m_run = m_new;
       }
+      // (m_run is -inf only while every token seen is masked: then p = 0)
+      const float delta = m_run == -INFINITY ? 0.f : m_run - m_ref;
       float p[8], psum;
-      const float m_ref = m_run == -INFINITY ? 0.f : m_run;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        p[j] = __builtin_amdgcn_exp2f(l2[j] - m_ref);
-        psum = j == 0 ? p[j] : psum + p[j];
-      }
+      for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(t2[j] - delta);
+      psum = p[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) psum += p[j];
       l_run += psum;
       float vn[8][2];
       load_norms<1>(nrm_v + 16 * lg, vn);
-      u32x4 bvc, bvs;
       if constexpr (P8) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int j0 = 2 * q, j1 = 2 * q + 1;
           bvc[q] = h2bits(wsplit(p[j0] * vn[j0][0], bsel, csel), wsplit(p[j1] * vn[j1][0], bsel, csel));
-          bvs[q] = h2bits(wsplit(p[j0] * vn[j0][1], bsel, csel), wsplit(p[j1] * vn[j1][1], bsel, csel));
+          bvs[q] = h2bits(p[j0] * vn[j0][1], p[j1] * vn[j1][1]);
         }
       } else {
         const bool gsel = role >= 2;
@@ -1249,35 +1353,52 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
         bvc = gsel ? z : w;
         bvs = gsel ? w : z;
       }
-      // ---------------- V: accumulate in the rotated / sketch domains ----------------
-#pragma unroll
-      for (int u = 0; u < NMT; ++u) {
-        const u32x4 vc = bcodes8<M>(r.vc, M * u, voff);
-        avr[u] = mfma16(vc, bvc, avr[u]);
-        if constexpr (WV == 1) {
-          const u32x4 vs = bsigns8(r.vs, u, soff);
-          if constexpr (P8)
-            avs[u] = mfma16(vs, bvs, avs[u]);
-          else
-            avr[u] = mfma16(vs, bvs, avr[u]);
-        }
-      }
     }
     __builtin_amdgcn_wave_barrier();
   };
 
+  // V part of a tile: accumulate its weighted codes and signs in the rotated
+  // and sketch domains
+  auto vpart = [&](const BRaw<M>& r, const u32x4& bvc, const u32x4& bvs) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < NMT; ++u) {
+      const u32x4 vc = bcodes8<M>(r.vc, M * u, voff);
+      avr[u] = mfma16(vc, bvc, avr[u]);
+      if constexpr (WV == 1) {
+        const u32x4 vs = bsigns8(r.vs, u, soff);
+        if constexpr (P8)
+          avs[u] = mfma16(vs, bvs, avs[u]);
+        else
+          avr[u] = mfma16(vs, bvs, avr[u]);
+      }
+    }
+  };
+
   if (tile < t_end) {
-    const int64_t last = t_end - 1 - ((t_end - 1 - tile) % kBW);
-    auto next = [&](int64_t t) { return t + kBW <= last ? t + kBW : last; };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    // stage of tile i (buffer i mod NB): the load of tile i + NB - 1 into
+    // the buffer of tile i - 1, then this tile's K part and V part; true
+    // after the wave's last tile
+    auto stage = [&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      load(tile_row(ahead(NB - 1)), rbuf(std::integral_constant<int, k + NB - 1>{}));
+      u32x4 bvc, bvs;
+      kpart(rbuf(kc), tile * kTile, bvc, bvs);
+      if constexpr (WV != 0) vpart(rbuf(kc), bvc, bvs);
+      if (tile == last) return true;
+      tile += kBW;
+      return false;
+    };
     for (;;) {
-      load_tile<D, 1, M, M, WV>(a, tile_row(next(tile)), lane, lo, no, rb1);
-      compute(rb0, tile * kTile);
-      if (tile == last) break;
-      tile += kBW;
-      load_tile<D, 1, M, M, WV>(a, tile_row(next(tile)), lane, lo, no, rb0);
-      compute(rb1, tile * kTile);
-      if (tile == last) break;
-      tile += kBW;
+      if (stage(I0{})) break;
+      if (stage(I1{})) break;
+      if constexpr (NB > 2)
+        if (stage(I2{})) break;
+      if constexpr (NB > 3)
+        if (stage(I3{})) break;
     }
   }
 
@@ -1335,7 +1456,8 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
         val = k == 0 ? Mx : L;
       } else {
         const int pt = (k - 2) / D, ch = (k - 2) % D;
-        // columns of the leading and remainder parts
+        // columns of the leading and remainder parts (P8: the sign part's
+        // weights are plain fp16 in both halves; its leading column is read)
         const int part = P8 ? pt : 0;
         const int chi = P8 ? h : 4 * h + 2 * pt, clo = P8 ? h + 8 : 4 * h + 2 * pt + 1;
         const int base = part * PS + 16 * ch + 16 * (ch >> 5);
@@ -1345,7 +1467,7 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
           hi += s_red[r * RS + base + chi];
           lo += s_red[r * RS + base + clo];
         }
-        val = fmaf(kLoInv, lo, hi);
+        val = (P8 && pt == 1) ? hi : fmaf(kLoInv, lo, hi);
         if (pt == 0) val *= vinv;
       }
       const int hq2 = kvh * a.group + hblk * HB + h;
