@@ -51,6 +51,7 @@
 #include "tq_internal.h"
 #include "tq_prep_dev.h"
 #include "tq_quantize_dev.h"
+#include "tq_quantize_t_dev.h"
 #include "turboquant.h"
 
 namespace {
@@ -1989,8 +1990,9 @@ struct StepArgs {
 };
 
 // SMALL: every append takes the few-vector path (a smaller kernel without the
-// tile path, which is the usual decode step of one token per head).
-template <bool SMALL>
+// tile path, which is the usual decode step of one token per head). H: the
+// tile path takes its transposed half-precision variant (both appends qualify).
+template <bool SMALL, bool H>
 __global__ __launch_bounds__(kStepNT * 64) void step_kernel(StepArgs s) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int b = blockIdx.x;
@@ -1999,7 +2001,12 @@ __global__ __launch_bounds__(kStepNT * 64) void step_kernel(StepArgs s) {
     if (SMALL || (is_k ? s.k_small : s.v_small))
       tqq::quantize_small<kStepNT * 64>(is_k ? s.k : s.v, is_k ? b : b - s.nk, smem);
     else if constexpr (!SMALL)
-      tqq::quantize_tiles<kStepKP, kStepNT>(is_k ? s.k : s.v, is_k ? b : b - s.nk, is_k ? s.nk : s.nv, smem);
+    {
+      if constexpr (H)
+        tqq::quantize_tiles_t<kStepKP, kStepNT>(is_k ? s.k : s.v, is_k ? b : b - s.nk, is_k ? s.nk : s.nv, smem);
+      else
+        tqq::quantize_tiles<kStepKP, kStepNT>(is_k ? s.k : s.v, is_k ? b : b - s.nk, is_k ? s.nk : s.nv, smem);
+    }
   } else {
     const int pb = b - s.nk - s.nv;
     tqp::prep_block<kD, kStepNT * 64>(s.prep, pb % s.prep_x, pb / s.prep_x, threadIdx.x, smem);
@@ -2061,22 +2068,27 @@ extern "C" tq_status tq_attn_decode_append(const tq_quantizer* kq, const tq_quan
   sa.prep = pl.prep;
   sa.prep_x = tqp::prep_blocks_x<kD>();
   const int grid = sa.nk + sa.nv + sa.prep_x * pl.prep_grid_y;
-  using L = tqq::Lds<kStepKP, kStepNT>;
   constexpr int lds_small = tqp::prep_lds_bytes<kD>() > tqq::SmallLds<kStepNT * 64>::bytes
                                 ? tqp::prep_lds_bytes<kD>()
                                 : tqq::SmallLds<kStepNT * 64>::bytes;
-  constexpr int lds = L::bytes > lds_small ? L::bytes : lds_small;
+  constexpr int lds_f = tqq::Lds<kStepKP, kStepNT, false>::bytes;
+  constexpr int lds_h = tqq::LdsT<kStepKP, kStepNT>::bytes;
   const bool all_small = (k_empty || sa.k_small) && (v_empty || sa.v_small);
-  const void* fn = all_small ? reinterpret_cast<const void*>(&step_kernel<true>)
-                             : reinterpret_cast<const void*>(&step_kernel<false>);
-  const int lds_use = all_small ? lds_small : lds;
+  const bool h = (k_empty || sa.k_small || tqq::t_path_ok(sa.k)) && (v_empty || sa.v_small || tqq::t_path_ok(sa.v));
+  const void* fn = all_small ? reinterpret_cast<const void*>(&step_kernel<true, false>)
+                   : h       ? reinterpret_cast<const void*>(&step_kernel<false, true>)
+                             : reinterpret_cast<const void*>(&step_kernel<false, false>);
+  const int lds_tiles = h ? lds_h : lds_f;
+  const int lds_use = all_small ? lds_small : lds_tiles > lds_small ? lds_tiles : lds_small;
   if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds_use) != hipSuccess)
     return TQ_ERR_DEVICE;
   (void)hipGetLastError();  // a launch error is reported below, not an older one
   if (all_small)
-    hipLaunchKernelGGL(step_kernel<true>, dim3(grid), dim3(kStepNT * 64), lds_use, hs, sa);
+    hipLaunchKernelGGL((step_kernel<true, false>), dim3(grid), dim3(kStepNT * 64), lds_use, hs, sa);
+  else if (h)
+    hipLaunchKernelGGL((step_kernel<false, true>), dim3(grid), dim3(kStepNT * 64), lds_use, hs, sa);
   else
-    hipLaunchKernelGGL(step_kernel<false>, dim3(grid), dim3(kStepNT * 64), lds_use, hs, sa);
+    hipLaunchKernelGGL((step_kernel<false, false>), dim3(grid), dim3(kStepNT * 64), lds_use, hs, sa);
   if (hipGetLastError() != hipSuccess) return TQ_ERR_DEVICE;
   return run_phases(pl, TQ_PHASE_SPLIT | TQ_PHASE_COMBINE, hs);
 }

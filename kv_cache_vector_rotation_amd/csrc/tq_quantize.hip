@@ -26,6 +26,7 @@
 
 #include "tq_internal.h"
 #include "tq_quantize_dev.h"
+#include "tq_quantize_t_dev.h"
 #include "turboquant.h"
 
 namespace {
@@ -33,10 +34,16 @@ namespace {
 using tqq::Lds;
 using tqq::QArgs;
 
-template <int KP, int NT>
+template <int KP, int NT, bool H>
 __global__ __launch_bounds__(NT * 64) void quantize_kernel(QArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  tqq::quantize_tiles<KP, NT>(a, blockIdx.x, gridDim.x, smem);
+  tqq::quantize_tiles<KP, NT, H>(a, blockIdx.x, gridDim.x, smem);
+}
+
+template <int KP, int NT>
+__global__ __launch_bounds__(NT * 64) void quantize_t_kernel(QArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  tqq::quantize_tiles_t<KP, NT>(a, blockIdx.x, gridDim.x, smem);
 }
 
 __global__ __launch_bounds__(tqq::kSmallThreads) void quantize_small_kernel(QArgs a) {
@@ -51,12 +58,19 @@ tq_status launch_quantize_small(const QArgs& a, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_DEVICE;
 }
 
-template <int KP, int NT>
+// The tile kernel loops over tiles (grid-stride), so the grid is one round
+// of resident workgroups: compute units times the workgroups that fit on one
+// at once (registers and LDS, from the occupancy query).
+template <int KP, int NT, bool H, bool T = false>
 tq_status launch_quantize(const QArgs& a, hipStream_t stream) {
-  using L = Lds<KP, NT>;
-  static_assert(L::bytes <= 160 * 1024, "LDS budget");
-  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&quantize_kernel<KP, NT>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, L::bytes) != hipSuccess)
+  constexpr int lds = T ? tqq::LdsT<KP, NT>::bytes : Lds<KP, NT, H>::bytes;
+  static_assert(lds <= 160 * 1024, "LDS budget");
+  const void* fn;
+  if constexpr (T)
+    fn = reinterpret_cast<const void*>(&quantize_t_kernel<KP, NT>);
+  else
+    fn = reinterpret_cast<const void*>(&quantize_kernel<KP, NT, H>);
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
     return TQ_ERR_DEVICE;
   const int64_t n_tiles = a.n_tiles;
   int dev = 0, n_cu = 256;
@@ -65,11 +79,15 @@ tq_status launch_quantize(const QArgs& a, hipStream_t stream) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
       n_cu = v;
   }
-  const int64_t per_cu = L::bytes <= 80 * 1024 ? 2 : 1;
-  const int64_t grid = n_tiles < per_cu * n_cu ? n_tiles : per_cu * n_cu;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NT * 64, lds) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  const int64_t grid = n_tiles < (int64_t)per_cu * n_cu ? n_tiles : (int64_t)per_cu * n_cu;
   (void)hipGetLastError();  // a launch error is reported below, not an older one
-  hipLaunchKernelGGL((quantize_kernel<KP, NT>), dim3((unsigned)grid), dim3(NT * 64), L::bytes, stream,
-                     a);
+  if constexpr (T)
+    hipLaunchKernelGGL((quantize_t_kernel<KP, NT>), dim3((unsigned)grid), dim3(NT * 64), lds, stream, a);
+  else
+    hipLaunchKernelGGL((quantize_kernel<KP, NT, H>), dim3((unsigned)grid), dim3(NT * 64), lds, stream, a);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_DEVICE;
 }
 
@@ -85,10 +103,15 @@ extern "C" tq_status tq_quantize(const tq_quantizer* qz, tq_format fmt, const vo
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   // a few vectors (an append): one workgroup per vector, for latency
   if (tqq::small_path_ok(a)) return launch_quantize_small(a, s);
+  const bool h = tqq::h_path_ok(a), t = tqq::t_path_ok(a);
   switch (tqq::quantize_kp(a.d)) {
-    case 64: return launch_quantize<64, 4>(a, s);
-    case 128: return launch_quantize<128, 8>(a, s);
-    case 208: return launch_quantize<208, 13>(a, s);
-    default: return launch_quantize<256, 16>(a, s);
+    case 64:
+      return t ? launch_quantize<64, 4, true, true>(a, s)
+               : h ? launch_quantize<64, 4, true>(a, s) : launch_quantize<64, 4, false>(a, s);
+    case 128:
+      return t ? launch_quantize<128, 8, true, true>(a, s)
+               : h ? launch_quantize<128, 8, true>(a, s) : launch_quantize<128, 8, false>(a, s);
+    case 208: return launch_quantize<208, 13, false>(a, s);
+    default: return launch_quantize<256, 16, false>(a, s);
   }
 }

@@ -174,15 +174,24 @@ __device__ __forceinline__ void mfma_tiles(const float* xr, const float (&b)[KPG
 }
 
 // LDS layout (bytes), KP = padded K, NT = number of 16-wide coordinate tiles.
-template <int KP, int NT>
+// H: the half-precision MFMA variant (bf16 input tile, fp16 residual parts):
+// the input tile is bf16 [QT][XH]; once the rotation has read it, the same
+// bytes hold the high fp16 part of the scaled residual, and off_rl its low
+// part (both [QT][XH]).
+template <int KP, int NT, bool H = false>
 struct Lds {
   static constexpr int XS = KP + 4;  // row stride of the fp32 tile, in floats
+  // row stride of the 16-bit tiles: 16 bytes of padding shift consecutive
+  // rows by four banks, so the 16 rows one 16-byte operand read spans fall
+  // in disjoint banks
+  static constexpr int XH = KP + 8;
   // row stride of the code and sign bytes: 4 bytes of padding put the rows
   // that one byte store spans (four vectors, 4 DP bytes apart) in different
   // LDS banks
   static constexpr int DP = NT * 16 + 4;
-  static constexpr int off_x = 0;                                   // float [QT][XS]
-  static constexpr int off_code = off_x + QT * XS * 4;              // u8 [QT][DP]
+  static constexpr int off_x = 0;                                   // float [QT][XS] (H: u16 [QT][XH])
+  static constexpr int off_rl = off_x + (H ? QT * XH * 2 : 0);      // H: u16 [QT][XH]
+  static constexpr int off_code = off_rl + (H ? QT * XH * 2 : QT * XS * 4);  // u8 [QT][DP]
   static constexpr int off_sign = off_code + QT * DP;               // u8 [QT][DP]
   static constexpr int off_npart = off_sign + QT * DP;              // float [NT][QT]
   static constexpr int off_gpart = off_npart + NT * QT * 4;         // float [NT][QT]
@@ -196,7 +205,7 @@ struct Lds {
   static constexpr int off_pk = off_flags + 16;                     // u32 [QT][PKW]
   // every wave's slice of sketch_rot, in MFMA operand order: [NT][KP/16][64 lanes]
   // f32x4 (d <= 128; larger d keeps it in registers)
-  static constexpr bool SKR_LDS = KP <= 128;
+  static constexpr bool SKR_LDS = KP <= 128 && !H;
   static constexpr int off_skr = (off_pk + QT * PKW * 4 + 15) / 16 * 16;
   static constexpr int bytes = off_skr + (SKR_LDS ? NT * KP * 64 : 0);
 };
@@ -337,6 +346,90 @@ __device__ __forceinline__ void store_x(const QArgs& a, const XStage& st, int ti
   }
 }
 
+// The tile as bf16 in LDS (row stride XH, 16-bit units), zero padded: the
+// half-precision variant takes bf16 rows that load_x read as 16-byte chunks.
+template <int KP, int NT, int XH>
+__device__ __forceinline__ void store_xh(const XStage& st, int tid, uint16_t* xh) {
+  constexpr int CPR = KP / 8, NCH = QT * CPR / (NT * 64);
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = tid + i * NT * 64, v = c / CPR, k = (c % CPR) * 8;
+    *reinterpret_cast<u32x4*>(xh + v * XH + k) = st.v[i];
+  }
+}
+
+// Round to nearest even of an fp32 value to bf16, as the bits of the bf16
+// value (finite inputs), and the fp32 value of bf16 bits.
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ float bf16_val(uint32_t b) { return __uint_as_float(b << 16); }
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                0, 0);
+}
+
+// acc[mt] = A[16 mt .. 16 mt + 15][:] x B on v_mfma_f32_16x16x32_bf16 for the
+// first NMT 16-vector tiles, B = BH + BM + BL (three bf16 parts of an fp32
+// matrix). A is the bf16 tile in LDS (row stride XH). Step s of lane group lg
+// takes k = 32 s + 8 lg + j, j = 0 .. 7: one 16-byte read per operand. The
+// small parts go first in each step.
+template <int NMT, int KS, int XH>
+__device__ __forceinline__ void mfma_tiles_bf16x3(const uint16_t* xh, const u32x4 (&bh)[KS], const u32x4 (&bm)[KS],
+                                                  const u32x4 (&bl)[KS], int ln, int lg, f32x4 (&acc)[4]) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    u32x4 a[NMT];
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+      a[mt] = *reinterpret_cast<const u32x4*>(xh + (mt * 16 + ln) * XH + 32 * s + 8 * lg);
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) acc[mt] = mfma_bf16(a[mt], bl[s], acc[mt]);
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) acc[mt] = mfma_bf16(a[mt], bm[s], acc[mt]);
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) acc[mt] = mfma_bf16(a[mt], bh[s], acc[mt]);
+  }
+}
+
+// The same shape on v_mfma_f32_16x16x32_f16 with both operands in two fp16
+// parts, A = AH + AL (tiles ah, al in LDS) and B = BH + BL: the products
+// AL BH, AH BL and AH BH (AL BL, below 2^-22 of a term, is dropped).
+template <int NMT, int KS, int XH>
+__device__ __forceinline__ void mfma_tiles_f16x2(const uint16_t* ah, const uint16_t* al, const u32x4 (&bh)[KS],
+                                                 const u32x4 (&bl)[KS], int ln, int lg, f32x4 (&acc)[4]) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    u32x4 a_h[NMT], a_l[NMT];
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+      const int off = (mt * 16 + ln) * XH + 32 * s + 8 * lg;
+      a_h[mt] = *reinterpret_cast<const u32x4*>(ah + off);
+      a_l[mt] = *reinterpret_cast<const u32x4*>(al + off);
+    }
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) acc[mt] = mfma_f16(a_l[mt], bh[s], acc[mt]);
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) acc[mt] = mfma_f16(a_h[mt], bl[s], acc[mt]);
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) acc[mt] = mfma_f16(a_h[mt], bh[s], acc[mt]);
+  }
+}
+
 // Code word wd of block blk = block h of a block-owned tile's pair: the
 // fields of the pair's rows [vlo, vhi) (row t is the tile's vector
 // t - slot_lo; its codes are LDS bytes [vector][DP]). A word that also holds
@@ -405,16 +498,36 @@ __device__ __forceinline__ void store_blk_sign_word(const QArgs& a, const uint8_
 
 // The kernel body: this workgroup quantizes tiles first_tile,
 // first_tile + tile_stride, ... of `a`, with NT * 64 threads and the dynamic
-// LDS block `smem` (Lds<KP, NT>::bytes).
-template <int KP, int NT>
+// LDS block `smem` (Lds<KP, NT, H>::bytes).
+//
+// H selects the half-precision MFMA variant (bf16 inputs with 16-byte rows,
+// d a multiple of 8, KP <= 128; h_path_ok). Both products still reach
+// fp32-grade results:
+//  - y = rot x: x is exact in bf16 and rot = RH + RM + RL (three bf16 parts,
+//    together within 2^-27 of rot), so the three v_mfma_f32_16x16x32_bf16
+//    products are exact term by term and only the fp32 accumulation rounds.
+//  - s = sketch_rot r: the sign of s is what is kept, and it does not change
+//    when a row of sketch_rot or the residual of one (vector, group) is
+//    scaled by a power of two. Each row of sketch_rot is scaled so that its
+//    largest entry lies in [2^13, 2^14), each residual so that its group
+//    norm lies in [2^9, 2^10) (|r_k| < 2 n_g, so every scaled value fits
+//    fp16), and both are split into fp16 high and low parts (22 bits); the
+//    products AL BH + AH BL + AH BH on v_mfma_f32_16x16x32_f16 leave out
+//    AL BL, below 2^-22 of each term.
+template <int KP, int NT, bool H = false>
 __device__ __forceinline__ void quantize_tiles(const QArgs& a, int64_t first_tile, int64_t tile_stride,
                                                unsigned char* smem) {
-  using L = Lds<KP, NT>;
+  using L = Lds<KP, NT, H>;
   constexpr int XS = L::XS;
+  constexpr int XH = L::XH;
   constexpr int DP = L::DP;
   constexpr int KPG = KP / 4;  // k values per lane group
+  constexpr int KS = KP / 32;  // k steps of the half-precision products
   static_assert(KP == NT * 16 && KPG % 4 == 0, "tile shape");
+  static_assert(!H || (KP % 32 == 0 && KP <= 128), "half-precision variant: KP in {64, 128}");
   float* xr = reinterpret_cast<float*>(smem + L::off_x);
+  uint16_t* xh = reinterpret_cast<uint16_t*>(smem + L::off_x);   // H: bf16 tile, then the residual's high part
+  uint16_t* rl = reinterpret_cast<uint16_t*>(smem + L::off_rl);  // H: the residual's low part
   uint8_t* code_b = smem + L::off_code;
   uint8_t* sign_b = smem + L::off_sign;
   float* npart = reinterpret_cast<float*>(smem + L::off_npart);
@@ -459,10 +572,73 @@ __device__ __forceinline__ void quantize_tiles(const QArgs& a, int64_t first_til
   // For d <= 128 the sketch slice lives in LDS (read once per product), which
   // leaves the register file to the rotation slice and the tile's values;
   // larger d keeps both slices in registers.
-  float brot[KPG];
-  float bskr[SKR_LDS ? 1 : KPG];
+  float brot[H ? 1 : KPG];
+  float bskr[SKR_LDS || H ? 1 : KPG];
   f32x4* skr_lds = reinterpret_cast<f32x4*>(smem + L::off_skr);
-  {
+  // H: the same slices as B operands of the 16x16x32 products, lane (ln, lg)
+  // holding M[16 w + ln][32 s + 8 lg + j], j = 0 .. 7, as 16-bit pairs:
+  // rot in three bf16 parts, sketch_rot (row-scaled) in two fp16 parts
+  u32x4 rh[H ? KS : 1], rm[H ? KS : 1], rlo[H ? KS : 1], sh[H ? KS : 1], sl[H ? KS : 1];
+  if constexpr (H) {
+    const bool row_ok = ocoord < a.d;
+    const int64_t rb = (int64_t)(row_ok ? ocoord : a.d - 1) * a.d;
+    f32x4 mr[KS][2], ms[KS][2];
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2)
+#pragma unroll
+      for (int hlf = 0; hlf < 2; ++hlf) {
+        // (d is a multiple of 8: a lane's 8 entries are all inside the row or all past it)
+        const int k = 32 * s2 + 8 * lg + 4 * hlf;
+        const int kc = k < a.d ? k : 0;
+        mr[s2][hlf] = *reinterpret_cast<const f32x4*>(a.rot + rb + kc);
+        ms[s2][hlf] = *reinterpret_cast<const f32x4*>(a.skr + rb + kc);
+        if (!row_ok || 32 * s2 + 8 * lg >= a.d) {
+          mr[s2][hlf] = f32x4{0.f, 0.f, 0.f, 0.f};
+          ms[s2][hlf] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    // largest |entry| of the sketch row: the lane's 8 KS entries, then the
+    // four lane groups of the row
+    float mx = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(ms[s2][e / 4][e % 4]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float ssc = mx > 0.f ? __builtin_amdgcn_ldexpf(1.0f, 14 - __builtin_amdgcn_frexp_expf(mx)) : 1.0f;
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) {
+      uint32_t wh[4], wm[4], wl[4], vh[4], vl[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        uint32_t h2[2], m2[2], l2[2];
+        f16x2 sh2, sl2;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float v = mr[s2][p / 2][2 * (p % 2) + e];
+          h2[e] = bf16_rne(v);
+          const float r1 = v - bf16_val(h2[e]);
+          m2[e] = bf16_rne(r1);
+          l2[e] = bf16_rne(r1 - bf16_val(m2[e]));
+          const float u = ms[s2][p / 2][2 * (p % 2) + e] * ssc;
+          const _Float16 uh = (_Float16)u;
+          sh2[e] = uh;
+          sl2[e] = (_Float16)(u - (float)uh);
+        }
+        wh[p] = h2[0] | (h2[1] << 16);
+        wm[p] = m2[0] | (m2[1] << 16);
+        wl[p] = l2[0] | (l2[1] << 16);
+        vh[p] = __builtin_bit_cast(uint32_t, sh2);
+        vl[p] = __builtin_bit_cast(uint32_t, sl2);
+      }
+      rh[s2] = u32x4{wh[0], wh[1], wh[2], wh[3]};
+      rm[s2] = u32x4{wm[0], wm[1], wm[2], wm[3]};
+      rlo[s2] = u32x4{wl[0], wl[1], wl[2], wl[3]};
+      sh[s2] = u32x4{vh[0], vh[1], vh[2], vh[3]};
+      sl[s2] = u32x4{vl[0], vl[1], vl[2], vl[3]};
+    }
+  } else {
     float bs[KPG];
     const int64_t rb = (int64_t)(ocoord < d ? ocoord : d - 1) * d;
     if (a.m_vec) {
@@ -531,7 +707,10 @@ __device__ __forceinline__ void quantize_tiles(const QArgs& a, int64_t first_til
     // ---- stage the input tile (fp32, zero padded) and destination rows ----
     if (tok && a.pk_zero)
       for (int e = tid; e < QT * PKW; e += NT * 64) pk[e] = 0u;
-    store_x<KP, NT, XS>(a, st, tid, xr);
+    if constexpr (H)
+      store_xh<KP, NT, XH>(st, tid, xh);
+    else
+      store_x<KP, NT, XS>(a, st, tid, xr);
     if (tid < QT) rows[tid] = (st.row < 0 || st.row >= a.n_rows) ? -1 : st.row;
     if (tid < 32) {
       cbk[tid] = cent_reg;
@@ -544,10 +723,17 @@ __device__ __forceinline__ void quantize_tiles(const QArgs& a, int64_t first_til
     // 16-vector tile)
     const int n_mt = (nvalid + 15) / 16;
     f32x4 yacc[4];
-    if (n_mt == 1)
-      mfma_tiles<1, KPG, XS>(xr, brot, ln, lg, yacc);
-    else
-      mfma_tiles<4, KPG, XS>(xr, brot, ln, lg, yacc);
+    if constexpr (H) {
+      if (n_mt == 1)
+        mfma_tiles_bf16x3<1, KS, XH>(xh, rh, rm, rlo, ln, lg, yacc);
+      else
+        mfma_tiles_bf16x3<4, KS, XH>(xh, rh, rm, rlo, ln, lg, yacc);
+    } else {
+      if (n_mt == 1)
+        mfma_tiles<1, KPG, XS>(xr, brot, ln, lg, yacc);
+      else
+        mfma_tiles<4, KPG, XS>(xr, brot, ln, lg, yacc);
+    }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       if (mt >= n_mt) break;
@@ -612,7 +798,17 @@ __device__ __forceinline__ void quantize_tiles(const QArgs& a, int64_t first_til
       for (int i = 0; i < 4; ++i) {
         const int v = mt * 16 + lg * 4 + i;
         code_b[v * DP + ocoord] = (uint8_t)idx[i];
-        xr[v * XS + ocoord] = rr[i];  // A operand of the sketch product (k = rotated coordinate)
+        // A operand of the sketch product (k = rotated coordinate)
+        if constexpr (H) {
+          // scaled so that the group norm lies in [2^9, 2^10), in two fp16 parts
+          const float sc = nv[i] > 0.f ? __builtin_amdgcn_ldexpf(1.0f, 10 - __builtin_amdgcn_frexp_expf(nv[i])) : 1.0f;
+          const float u = rr[i] * sc;
+          const _Float16 uh = (_Float16)u;
+          xh[v * XH + ocoord] = __builtin_bit_cast(uint16_t, uh);
+          rl[v * XH + ocoord] = __builtin_bit_cast(uint16_t, (_Float16)(u - (float)uh));
+        } else {
+          xr[v * XS + ocoord] = rr[i];
+        }
       }
       if (tok) {
         // the row's 16 codes of this wave, OR-combined across the row of
@@ -649,7 +845,12 @@ __device__ __forceinline__ void quantize_tiles(const QArgs& a, int64_t first_til
     // ---- s = (S Pi^T) r (fp32 MFMA); sign bit = [s >= 0] (not for MSE-only records) ----
     if (!a.mse_only) {
       f32x4 sacc[4];
-      if constexpr (SKR_LDS) {
+      if constexpr (H) {
+        if (n_mt == 1)
+          mfma_tiles_f16x2<1, KS, XH>(xh, rl, sh, sl, ln, lg, sacc);
+        else
+          mfma_tiles_f16x2<4, KS, XH>(xh, rl, sh, sl, ln, lg, sacc);
+      } else if constexpr (SKR_LDS) {
         if (n_mt == 1)
           mfma_tiles_lds<1, KPG, XS>(xr, skr_lds + w * (KPG / 4) * 64 + lane, ln, lg, sacc);
         else
@@ -1194,6 +1395,13 @@ inline tq_status make_qargs(const tq_quantizer* qz, tq_format fmt, const void* x
   a.signs = cache->signs;
   a.norms = cache->norms;
   return TQ_OK;
+}
+
+// Whether a call (already validated by make_qargs) can take the
+// half-precision MFMA variant of the tile path: bf16 rows read as 16-byte
+// chunks (so d is a multiple of 8), 16-byte aligned matrices, d <= 128.
+inline bool h_path_ok(const QArgs& a) {
+  return a.x_bf16 && a.x_vec && a.m_vec && a.d % 8 == 0 && a.d <= 128;
 }
 
 // Kernel shape for a dimension: KP = d rounded up to 16, NT = KP / 16 waves.

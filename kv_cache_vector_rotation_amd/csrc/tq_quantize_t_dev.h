@@ -1,0 +1,607 @@
+// Transposed tile path of the quantize kernel: bf16 inputs, d <= 128.
+//
+// [ZB] paragraph 2 and [WD] "Como o TurboQuant funciona": rotate each vector,
+// give every rotated coordinate its Lloyd-Max cell, take the residual of that
+// MSE quantizer, keep the signs of a Gaussian sketch of the residual, store
+// codes, sign bits and the norms. The values this path produces follow the
+// same rules as the general tile path; only the work layout differs.
+//
+// Both products are formed as (matrix slice) x (tile)^T: a wave's 16 rows of
+// the d x d matrix are the A operand of v_mfma_f32_16x16x32_{bf16,f16} (held
+// in registers for the whole kernel) and 16 vectors of the tile in LDS are
+// the B operand. The result lane (ln, lg) of 16-vector tile mt then holds
+// coordinates 16 w + 4 lg + i (i = 0 .. 3) of the single vector 16 mt + ln,
+// so every per-vector quantity (norm, its reciprocal, the residual scale) is
+// one value per lane, sums over a wave's 16 coordinates take one in-lane sum
+// and two lane swaps, and the four codes, residual values and sign bits of a
+// lane are adjacent in every output layout (8-byte LDS stores of the
+// residual parts, packed code and sign fields).
+//
+// Precision is that of the general path's half-precision variant:
+//  - y = rot x: x is exact in bf16 and rot = RH + RM + RL (three bf16 parts
+//    within 2^-27 of rot), so the products are exact term by term and only
+//    the fp32 accumulation rounds.
+//  - s = sketch_rot r: only the sign of s is kept, and it does not change when
+//    a row of sketch_rot or the residual of one (vector, group) is scaled by a
+//    power of two: rows are scaled so their largest entry lies in
+//    [2^13, 2^14), residuals so their group norm lies in [2^9, 2^10)
+//    (|r_k| < 2 n_g, so every scaled value fits fp16), both are split into
+//    fp16 high and low parts, and AL BH + AH BL + AH BH leaves out AL BL,
+//    below 2^-22 of each term.
+//
+// Tiles: token-major records take 64 consecutive vectors; block records
+// take one aligned pair of 32-row blocks of one segment (block-owned tiling)
+// with tile row = slot in the pair, so the 8 tokens of an octet field sit in
+// 8 adjacent lanes. The next tile's input is loaded while the current one is
+// processed.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "tq_quantize_dev.h"
+
+namespace tqq {
+
+template <int KP, int NT>
+struct LdsT {
+  static constexpr int XH = KP + 8;  // row stride (16-bit units) of the bf16 tile and the residual parts
+  static constexpr int off_x = 0;                             // u16 [QT][XH]: bf16 tile, then the residual's high part
+  static constexpr int off_rl = off_x + QT * XH * 2;          // u16 [QT][XH]: the residual's low part
+  static constexpr int off_npart = off_rl + QT * XH * 2;      // float [NT][QT]: sums of y^2 per wave
+  static constexpr int off_gpart = off_npart + NT * QT * 4;   // float [NT][QT]: sums of r^2 per wave
+  static constexpr int off_nrm = off_gpart + NT * QT * 4;     // f32x4 [2][QT]: (n_g, 1 / n_g or 0, residual scale, 0)
+  static constexpr int off_cb = off_nrm + 2 * QT * 16;        // float [64]: centroids [0, 32), boundaries [32, 64)
+  static constexpr int off_rows = off_cb + 64 * 4;            // int64 [QT]: destination rows (token-major)
+  static constexpr int PKW = KP * 4 / 32 + KP / 32 + 4;       // token-major staging row, words
+  static constexpr int BKW = KP * 5;                          // block staging: code + sign words of one block
+  static constexpr int off_pk = off_rows + QT * 8;            // u32: token-major [QT][PKW]; block [2][BKW] + masks [2][BKW]
+  static constexpr int PK_WORDS = QT * PKW > 4 * BKW ? QT * PKW : 4 * BKW;
+  static constexpr int bytes = off_pk + PK_WORDS * 4;
+};
+
+// Whether a call (validated by make_qargs) takes the transposed tile path.
+inline bool t_path_ok(const QArgs& a) {
+  return h_path_ok(a) && (a.fmt == TQ_TOKEN_MAJOR || a.blk_owned);
+}
+
+// Sum / OR over the four lane groups (lanes ln, ln + 16, ln + 32, ln + 48),
+// the result in all four.
+__device__ __forceinline__ float lg_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ uint32_t lg_or(uint32_t v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = a[0] | a[1];
+  const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return b[0] | b[1];
+}
+// OR over each aligned group of 8 lanes, the result in all 8.
+__device__ __forceinline__ uint32_t oct_or(uint32_t s) {
+  s |= dpp_u<0xB1>(s);   // quad_perm [1, 0, 3, 2]
+  s |= dpp_u<0x4E>(s);   // quad_perm [2, 3, 0, 1]
+  s |= dpp_u<0x141>(s);  // row_half_mirror
+  return s;
+}
+
+// acc[mt] = (B = RH + RM + RL slice) x (tile rows 16 mt .. 16 mt + 15)^T for
+// the first NMT 16-vector tiles (the rest zero): the matrix parts are the A
+// operand, the bf16 tile (row stride XH) the B operand. Step s of lane group
+// lg takes k = 32 s + 8 lg + j, j = 0 .. 7; the small parts go first.
+template <int NMT, int KS, int XH>
+__device__ __forceinline__ void mfma_t_bf16x3(const uint16_t* xh, const u32x4 (&mh)[KS], const u32x4 (&mm)[KS],
+                                              const u32x4 (&ml)[KS], int ln, int lg, f32x4 (&acc)[4]) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    u32x4 b[NMT];
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+      b[mt] = *reinterpret_cast<const u32x4*>(xh + (mt * 16 + ln) * XH + 32 * s + 8 * lg);
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) acc[mt] = mfma_bf16(ml[s], b[mt], acc[mt]);
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) acc[mt] = mfma_bf16(mm[s], b[mt], acc[mt]);
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) acc[mt] = mfma_bf16(mh[s], b[mt], acc[mt]);
+  }
+}
+
+// The same with two fp16 parts on both sides: (SL RH^T) + (SH RL^T) + (SH RH^T).
+template <int NMT, int KS, int XH>
+__device__ __forceinline__ void mfma_t_f16x2(const uint16_t* rh, const uint16_t* rl, const u32x4 (&sh)[KS],
+                                             const u32x4 (&sl)[KS], int ln, int lg, f32x4 (&acc)[4]) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    u32x4 bh[NMT], bl[NMT];
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+      const int off = (mt * 16 + ln) * XH + 32 * s + 8 * lg;
+      bh[mt] = *reinterpret_cast<const u32x4*>(rh + off);
+      bl[mt] = *reinterpret_cast<const u32x4*>(rl + off);
+    }
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) acc[mt] = mfma_f16(sl[s], bh[mt], acc[mt]);
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) acc[mt] = mfma_f16(sh[s], bl[mt], acc[mt]);
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) acc[mt] = mfma_f16(sh[s], bh[mt], acc[mt]);
+  }
+}
+
+// Cells of four unit coordinates: the number of the NB boundaries below each.
+template <int NB>
+__device__ __forceinline__ void cells4(const float (&u)[4], const float (&tb)[15], int (&c)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int n = 0;
+#pragma unroll
+    for (int k = 0; k < NB; ++k) n += u[i] > tb[k] ? 1 : 0;
+    c[i] = n;
+  }
+}
+
+// The tile's bf16 input, two 16-byte chunks per thread, held in registers
+// from the load to the LDS store (one tile ahead).
+struct TStage {
+  u32x4 c[2];
+};
+
+// Chunk i of thread tid: tile row v = c / (KP / 8), columns k .. k + 7. A
+// block tile's row is the slot in its block pair: slot t holds vector
+// v0 + t - slot_lo when that lies in [0, nvalid), else zeros.
+template <int KP, int NT>
+__device__ __forceinline__ void load_t(const QArgs& a, const TileGeo& g, bool blk, int tid, TStage& st) {
+  constexpr int CPR = KP / 8;
+  static_assert(QT * CPR == 2 * NT * 64, "two chunks per thread");
+  const uint16_t* x = reinterpret_cast<const uint16_t*>(a.x);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + i * NT * 64, v = c / CPR, k = (c % CPR) * 8;
+    const int src = blk ? v - g.slot_lo : v;
+    st.c[i] = (src >= 0 && src < g.nvalid && k < a.d)
+                  ? *reinterpret_cast<const u32x4*>(x + (g.v0 + src) * a.x_stride + k)
+                  : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// Block staging word of the fields of block h, o, channel j0 .. j0 + 3 of
+// group g: the code words (m of them) start at word m (o dg + j0) / 4 of the
+// group's code area, the sign word at word (o dg + j0) / 4 of its sign area.
+
+// The kernel body: this workgroup quantizes tiles first_tile,
+// first_tile + tile_stride, ... of `a` (t_path_ok), with NT * 64 threads and
+// the dynamic LDS block `smem` (LdsT<KP, NT>::bytes).
+template <int KP, int NT>
+__device__ __forceinline__ void quantize_tiles_t(const QArgs& a, int64_t first_tile, int64_t tile_stride,
+                                                 unsigned char* smem) {
+  using L = LdsT<KP, NT>;
+  constexpr int XH = L::XH;
+  constexpr int KS = KP / 32;
+  constexpr int PKW = L::PKW;
+  constexpr int BKW = L::BKW;
+  static_assert(KP == NT * 16 && KP % 32 == 0 && KP <= 128, "tile shape");
+  uint16_t* xh = reinterpret_cast<uint16_t*>(smem + L::off_x);
+  uint16_t* rlo = reinterpret_cast<uint16_t*>(smem + L::off_rl);
+  float* npart = reinterpret_cast<float*>(smem + L::off_npart);
+  float* gpart = reinterpret_cast<float*>(smem + L::off_gpart);
+  f32x4* nrm4 = reinterpret_cast<f32x4*>(smem + L::off_nrm);
+  float* cbk = reinterpret_cast<float*>(smem + L::off_cb);
+  int64_t* rows = reinterpret_cast<int64_t*>(smem + L::off_rows);
+  uint32_t* pk = reinterpret_cast<uint32_t*>(smem + L::off_pk);
+  uint16_t* pk16 = reinterpret_cast<uint16_t*>(smem + L::off_pk);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave = 16 output coordinates
+  const int ln = lane & 15;
+  const int lg = lane >> 4;
+  const int d = a.d;
+  const bool blk = a.fmt == TQ_BLOCK32;  // (then blk_owned)
+
+  float cent_reg = 0.f, bnd_reg = 0.f;
+  {
+    const int ncent = (1 << a.gbits[0]) + (a.n_groups > 1 ? (1 << a.gbits[1]) : 0);
+    cent_reg = a.centroids[tid < ncent ? tid : ncent - 1];
+    const int nbt = ((1 << a.gbits[0]) - 1) + (a.n_groups > 1 ? (1 << a.gbits[1]) - 1 : 0);
+    bnd_reg = a.boundaries[tid < nbt ? tid : nbt - 1];
+  }
+  TileGeo g;
+  int64_t tile = next_live_tile(a, first_tile, tile_stride, g);
+  TStage st;
+  if (tile < a.n_tiles) load_t<KP, NT>(a, g, blk, tid, st);
+
+  // This wave's rows of rot (three bf16 parts) and sketch_rot (row-scaled,
+  // two fp16 parts), lane (ln, lg) holding M[16 w + ln][32 s + 8 lg + j].
+  u32x4 rh[KS], rm[KS], rl3[KS], sh[KS], sl[KS];
+  {
+    const int orow = 16 * w + ln;
+    const bool row_ok = orow < d;
+    const int64_t rb = (int64_t)(row_ok ? orow : d - 1) * d;
+    f32x4 mr[KS][2], ms[KS][2];
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2)
+#pragma unroll
+      for (int hlf = 0; hlf < 2; ++hlf) {
+        // (d is a multiple of 8: a lane's 8 entries are all inside the row or all past it)
+        const int k = 32 * s2 + 8 * lg + 4 * hlf;
+        const int kc = k < d ? k : 0;
+        mr[s2][hlf] = *reinterpret_cast<const f32x4*>(a.rot + rb + kc);
+        ms[s2][hlf] = *reinterpret_cast<const f32x4*>(a.skr + rb + kc);
+        if (!row_ok || 32 * s2 + 8 * lg >= d) {
+          mr[s2][hlf] = f32x4{0.f, 0.f, 0.f, 0.f};
+          ms[s2][hlf] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    float mx = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(ms[s2][e / 4][e % 4]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float ssc = mx > 0.f ? __builtin_amdgcn_ldexpf(1.0f, 14 - __builtin_amdgcn_frexp_expf(mx)) : 1.0f;
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) {
+      uint32_t wh[4], wm[4], wl[4], vh[4], vl[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        uint32_t h2[2], m2[2], l2[2];
+        f16x2 sh2, sl2;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float v = mr[s2][p / 2][2 * (p % 2) + e];
+          h2[e] = bf16_rne(v);
+          const float r1 = v - bf16_val(h2[e]);
+          m2[e] = bf16_rne(r1);
+          l2[e] = bf16_rne(r1 - bf16_val(m2[e]));
+          const float u = ms[s2][p / 2][2 * (p % 2) + e] * ssc;
+          const _Float16 uh = (_Float16)u;
+          sh2[e] = uh;
+          sl2[e] = (_Float16)(u - (float)uh);
+        }
+        wh[p] = h2[0] | (h2[1] << 16);
+        wm[p] = m2[0] | (m2[1] << 16);
+        wl[p] = l2[0] | (l2[1] << 16);
+        vh[p] = __builtin_bit_cast(uint32_t, sh2);
+        vl[p] = __builtin_bit_cast(uint32_t, sl2);
+      }
+      rh[s2] = u32x4{wh[0], wh[1], wh[2], wh[3]};
+      rm[s2] = u32x4{wm[0], wm[1], wm[2], wm[3]};
+      rl3[s2] = u32x4{wl[0], wl[1], wl[2], wl[3]};
+      sh[s2] = u32x4{vh[0], vh[1], vh[2], vh[3]};
+      sl[s2] = u32x4{vl[0], vl[1], vl[2], vl[3]};
+    }
+  }
+
+  // wave-uniform group parameters (group boundaries are multiples of 16)
+  const int grp = (a.n_groups > 1 && w * 16 >= a.choff[1]) ? 1 : 0;
+  const int mg = a.gbits[grp];
+  const int nb = (1 << mg) - 1;
+  const int coff = a.coff[grp];
+  const int boff = a.boff[grp];
+  const int choff = a.choff[grp];
+  const int dg = a.gdim[grp];
+  const int wig = w - choff / 16;          // wave index within its group
+  const int j0 = 16 * wig + 4 * lg;        // the lane's first channel within the group
+  const bool lane_ok = 16 * w + 4 * lg < d;  // the lane's four coordinates exist (d % 4 == 0)
+  const bool tail = 16 * w + 16 > d;       // (uniform) the wave has coordinates past d
+  const int mid = (nb + 1) / 2 - 1;        // the cell of a zero vector
+  const bool tok = !blk;
+  const int pk_code_h = 2 * a.cwoff[grp] + mg * wig;
+  const int pk_sign_h = 2 * (a.code_words + a.swoff[grp]) + wig;
+  const int bcw = a.blk_code_words, bsw = a.blk_sign_words;
+  const int bc_g = a.bcwoff[grp], bs_g = bcw + a.bswoff[grp];  // block staging offsets of the group
+  const bool signs_on = !a.mse_only;
+
+  while (tile < a.n_tiles) {
+    const TileGeo cg = g;
+    // ---- stage the tile: input, destination rows, codebook ----
+    if (tok && a.pk_zero)
+      for (int e = tid; e < QT * PKW; e += NT * 64) pk[e] = 0u;
+    {
+      constexpr int CPR = KP / 8;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int c = tid + i * NT * 64, v = c / CPR, k = (c % CPR) * 8;
+        *reinterpret_cast<u32x4*>(xh + v * XH + k) = st.c[i];
+      }
+    }
+    if (tok && tid < QT) {
+      int64_t row = -1;
+      if (tid < cg.nvalid) {
+        const int64_t i = cg.v0 + tid;
+        row = a.dst_rows ? a.dst_rows[i] : dest_row(a, i);
+        if (row < 0 || row >= a.n_rows) row = -1;
+      }
+      rows[tid] = row;
+    }
+    if (tid < 32) {
+      cbk[tid] = cent_reg;
+      cbk[32 + tid] = bnd_reg;
+    }
+    __syncthreads();
+    // the next tile's input, in flight while this one is processed
+    tile = next_live_tile(a, tile + tile_stride, tile_stride, g);
+    if (tile < a.n_tiles) load_t<KP, NT>(a, g, blk, tid, st);
+
+    // ---- y = rot x ----
+    // (a token-major tile of at most 16 vectors runs its first 16-vector
+    // tile only; rows past the tile's vectors are zero)
+    const int n_mt = (!blk && cg.nvalid <= 16) ? 1 : 4;
+    f32x4 y[4];
+    if (n_mt == 1)
+      mfma_t_bf16x3<1, KS, XH>(xh, rh, rm, rl3, ln, lg, y);
+    else
+      mfma_t_bf16x3<4, KS, XH>(xh, rh, rm, rl3, ln, lg, y);
+    // lane (ln, lg): y[mt][i] = coordinate 16 w + 4 lg + i of tile row 16 mt + ln
+    {
+      float sq[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const float s = fmaf(y[mt][3], y[mt][3], fmaf(y[mt][2], y[mt][2], fmaf(y[mt][1], y[mt][1], y[mt][0] * y[mt][0])));
+        sq[mt] = lg_sum(s);
+      }
+      // lane group lg writes the sums of tile lg
+      const float mine = lg == 0 ? sq[0] : lg == 1 ? sq[1] : lg == 2 ? sq[2] : sq[3];
+      npart[w * QT + 16 * lg + ln] = mine;
+    }
+    __syncthreads();
+    // group norms, their reciprocals and the residual scale
+    if (tid < QT * a.n_groups) {
+      const int gg = tid / QT, v = tid % QT;
+      const int w0 = a.choff[gg] / 16, w1 = (a.choff[gg] + a.gdim[gg] + 15) / 16;
+      float s = 0.f;
+      for (int ww = w0; ww < w1; ++ww) s += npart[ww * QT + v];
+      const float n = sqrtf(s);
+      const float inv = n > 0.f ? 1.0f / n : 0.f;
+      const float sc = n > 0.f ? __builtin_amdgcn_ldexpf(1.0f, 10 - __builtin_amdgcn_frexp_expf(n)) : 1.0f;
+      nrm4[gg * QT + v] = f32x4{n, inv, sc, 0.f};
+    }
+    __syncthreads();
+
+    // ---- cells, residual, residual norm partials, packed codes ----
+    float tb[15];
+#pragma unroll
+    for (int k = 0; k < 15; ++k)
+      tb[k] = k < nb ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(cbk[32 + boff + k]))) : INFINITY;
+    int idx[4][4];
+    float rr[4][4];
+    {
+      float gq[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const f32x4 nq = nrm4[grp * QT + 16 * mt + ln];
+        float u[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) u[i] = y[mt][i] * nq[1];
+        int c[4];
+        if (nb == 3)
+          cells4<3>(u, tb, c);
+        else if (nb == 7)
+          cells4<7>(u, tb, c);
+        else if (nb == 1)
+          cells4<1>(u, tb, c);
+        else
+          cells4<15>(u, tb, c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          idx[mt][i] = nq[0] > 0.f ? c[i] : mid;
+          if (tail && !lane_ok) idx[mt][i] = 0;
+        }
+        float cv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cv[i] = cbk[coff + idx[mt][i]];
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          rr[mt][i] = fmaf(-nq[0], cv[i], y[mt][i]);
+          if (tail && !lane_ok) rr[mt][i] = 0.f;
+          s = fmaf(rr[mt][i], rr[mt][i], s);
+        }
+        gq[mt] = lg_sum(s);
+        // the residual, scaled, as fp16 high and low parts (the B operand of
+        // the sketch product; the rotation has read the tile: two barriers
+        // lie between)
+        if (signs_on) {
+          f16x2 h01, h23, l01, l23;
+          const float u0 = rr[mt][0] * nq[2], u1 = rr[mt][1] * nq[2], u2 = rr[mt][2] * nq[2],
+                      u3 = rr[mt][3] * nq[2];
+          h01[0] = (_Float16)u0;
+          h01[1] = (_Float16)u1;
+          h23[0] = (_Float16)u2;
+          h23[1] = (_Float16)u3;
+          l01[0] = (_Float16)(u0 - (float)h01[0]);
+          l01[1] = (_Float16)(u1 - (float)h01[1]);
+          l23[0] = (_Float16)(u2 - (float)h23[0]);
+          l23[1] = (_Float16)(u3 - (float)h23[1]);
+          const int off = (16 * mt + ln) * XH + 16 * w + 4 * lg;
+          *reinterpret_cast<uint2*>(xh + off) =
+              uint2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
+          *reinterpret_cast<uint2*>(rlo + off) =
+              uint2{__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)};
+        }
+      }
+      const float mine = lg == 0 ? gq[0] : lg == 1 ? gq[1] : lg == 2 ? gq[2] : gq[3];
+      gpart[w * QT + 16 * lg + ln] = mine;
+    }
+    if (tok) {
+      // the wave's 16 codes of a row (16 mg bits), assembled across the lane
+      // groups, stored by lane group 0 as mg halfwords
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const uint32_t f4 = (uint32_t)idx[mt][0] | ((uint32_t)idx[mt][1] << mg) | ((uint32_t)idx[mt][2] << (2 * mg)) |
+                            ((uint32_t)idx[mt][3] << (3 * mg));
+        const uint64_t f = (uint64_t)f4 << (4 * mg * lg);
+        const uint32_t lo = lg_or((uint32_t)f);
+        const uint32_t hi = mg > 2 ? lg_or((uint32_t)(f >> 32)) : 0u;
+        if (lg == 0 && mt < n_mt) {
+          uint16_t* row = pk16 + (16 * mt + ln) * 2 * PKW + pk_code_h;
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            if (k < mg) row[k] = (uint16_t)((k < 2 ? lo : hi) >> (16 * (k & 1)));
+        }
+      }
+    } else {
+      // octet fields: channel j0 + i of the 8 tokens of octet o at bits
+      // 8 mg (o dg + j0 + i) + mg s; the 8 lanes of an octet OR their fields
+      // (lane moves outside any branch), lane s = 0 stores the mg words
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int s = ln & 7, h = mt >> 1, o = 2 * (mt & 1) + (ln >> 3);
+        uint32_t wv[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int bit = 8 * mg * i + mg * s;  // < 32 mg
+          const uint64_t f = (uint64_t)(uint32_t)idx[mt][i] << (bit & 31);
+          const int wi = bit >> 5;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (q == wi) wv[q] |= (uint32_t)f;
+            if (q == wi + 1) wv[q] |= (uint32_t)(f >> 32);
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (q < mg) wv[q] = oct_or(wv[q]);
+        if (s == 0 && lane_ok) {
+          uint32_t* dst = pk + h * BKW + bc_g + mg * (o * dg + j0) / 4;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (q < mg) dst[q] = wv[q];
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- s = sketch_rot r; sign bit = [s >= 0] ----
+    if (signs_on) {
+      f32x4 sacc[4];
+      if (n_mt == 1)
+        mfma_t_f16x2<1, KS, XH>(xh, rlo, sh, sl, ln, lg, sacc);
+      else
+        mfma_t_f16x2<4, KS, XH>(xh, rlo, sh, sl, ln, lg, sacc);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        uint32_t nib = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) nib |= (sacc[mt][i] >= 0.f ? 1u : 0u) << i;
+        if (!lane_ok) nib = 0u;
+        if (tok) {
+          const uint32_t bits16 = lg_or(nib << (4 * lg));
+          if (lg == 0 && mt < n_mt) pk16[(16 * mt + ln) * 2 * PKW + pk_sign_h] = (uint16_t)bits16;
+        } else {
+          const int s = ln & 7, h = mt >> 1, o = 2 * (mt & 1) + (ln >> 3);
+          uint32_t wv = 0u;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) wv |= ((nib >> i) & 1u) << (8 * i + s);
+          wv = oct_or(wv);
+          if (s == 0 && lane_ok) pk[h * BKW + bs_g + (o * dg + j0) / 4] = wv;
+        }
+      }
+    }
+    // partial block tiles: masks of the staged words (the same fields with
+    // every code bit and sign bit of a row inside the tile set)
+    const bool partial = blk && (cg.slot_lo > 0 || cg.slot_lo + cg.nvalid < 64);
+    if (partial) {
+      const uint32_t fm = (1u << mg) - 1u;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int s = ln & 7, h = mt >> 1, o = 2 * (mt & 1) + (ln >> 3);
+        const int t = 16 * mt + ln;
+        const bool in = t >= cg.slot_lo && t < cg.slot_lo + cg.nvalid;
+        uint32_t wv[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int bit = 8 * mg * i + mg * s;
+          const uint64_t f = (uint64_t)(in ? fm : 0u) << (bit & 31);
+          const int wi = bit >> 5;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (q == wi) wv[q] |= (uint32_t)f;
+            if (q == wi + 1) wv[q] |= (uint32_t)(f >> 32);
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (q < mg) wv[q] = oct_or(wv[q]);
+        uint32_t sv = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv |= (in ? 1u : 0u) << (8 * i + s);
+        sv = oct_or(sv);
+        if (s == 0 && lane_ok) {
+          uint32_t* dst = pk + (2 + h) * BKW + bc_g + mg * (o * dg + j0) / 4;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (q < mg) dst[q] = wv[q];
+          if (signs_on) pk[(2 + h) * BKW + bs_g + (o * dg + j0) / 4] = sv;
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- store: norms, then the records ----
+    if (tid < QT * a.n_groups) {
+      const int gg = tid / QT, v = tid % QT;
+      int64_t row = -1;
+      if (tok)
+        row = rows[v];
+      else if (v >= cg.slot_lo && v < cg.slot_lo + cg.nvalid)
+        row = cg.rowbase + v;
+      if (row >= 0) {
+        const int w0 = a.choff[gg] / 16, w1 = (a.choff[gg] + a.gdim[gg] + 15) / 16;
+        float s = 0.f;
+        for (int ww = w0; ww < w1; ++ww) s += gpart[ww * QT + v];
+        store_norms(a.norms, a.norm_f16, row * a.n_groups + gg, nrm4[gg * QT + v][0], sqrtf(s));
+      }
+    }
+    if (tok) {
+      // 16 threads per row, the row's code words then its sign words
+      const int cw = a.code_words, sw = a.sign_words, rw = cw + sw;
+      for (int v = tid >> 4; v < cg.nvalid; v += NT * 4) {
+        const int64_t row = rows[v];
+        if (row < 0) continue;
+        for (int wd = tid & 15; wd < rw; wd += 16) {
+          const uint32_t val = pk[v * PKW + wd];
+          if (wd < cw)
+            a.codes[row * cw + wd] = val;
+          else
+            a.signs[row * sw + wd - cw] = val;
+        }
+      }
+    } else {
+      const int nw = bcw + (signs_on ? bsw : 0);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int vlo = cg.slot_lo > 32 * h ? cg.slot_lo : 32 * h;
+        const int vhi = cg.slot_lo + cg.nvalid < 32 * h + 32 ? cg.slot_lo + cg.nvalid : 32 * h + 32;
+        if (vhi <= vlo) continue;
+        const int64_t blkrow = cg.rowbase / 32 + h;
+        for (int wd = tid; wd < nw; wd += NT * 64) {
+          const uint32_t val = pk[h * BKW + wd];
+          uint32_t* dst = wd < bcw ? a.codes + blkrow * bcw + wd : a.signs + blkrow * bsw + (wd - bcw);
+          if (!partial) {
+            *dst = val;
+          } else {
+            const uint32_t m = pk[(2 + h) * BKW + wd];
+            if (m == 0xFFFFFFFFu) {
+              *dst = val;
+            } else if (m != 0u) {
+              atomicAnd(dst, ~m);
+              atomicOr(dst, val & m);
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace tqq

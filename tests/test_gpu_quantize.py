@@ -83,6 +83,73 @@ def test_every_bit_width_d64(tq, m):
     _check(tq, spec, x, tq.TQ_TOKEN_MAJOR, 256, np.arange(256), dtype="bf16")
 
 
+# Tile path (more than SMALL_MAX vectors) with bf16 rows of d a multiple of 8
+# and d <= 128: the half-precision MFMA variants (bf16 rotation in three parts,
+# fp16 sketch product in two parts) must meet the same record rule. Rows given
+# by segments take the transposed variant for both formats; an explicit row
+# list takes it for token-major records only.
+@pytest.mark.parametrize("m", [1, 2, 3, 4])
+@pytest.mark.parametrize("fmt_name", ["TQ_TOKEN_MAJOR", "TQ_BLOCK32"])
+@pytest.mark.parametrize("by_segments", [True, False])
+def test_tile_path_d64_every_bit_width(tq, m, fmt_name, by_segments):
+    wl = synth.workload("llama8b_decode", d=64, groups=((64, m),), n_outliers=0)
+    spec = synth.draw_quantizer(wl, "K")
+    x = synth.draw_kv_slab(wl, "K", 0, 1, 0, 1500)
+    _check(tq, spec, x, getattr(tq, fmt_name), 1536, np.arange(1500), dtype="bf16",
+           seg=(1500, 1536, 0), pass_rows=not by_segments)
+
+
+@pytest.mark.parametrize("name", ["mixed_3p5", "mixed_2p5"])
+def test_tile_path_two_groups(tq, name):
+    wl = synth.workload(name)
+    spec = synth.draw_quantizer(wl, "K")
+    x = synth.draw_kv_slab(wl, "K", 1, 2, 0, 1300)
+    for fmt in (tq.TQ_TOKEN_MAJOR, tq.TQ_BLOCK32):
+        _check(tq, spec, x, fmt, 1312, np.arange(1300), dtype="bf16", seg=(1300, 1312, 0), pass_rows=False)
+
+
+@pytest.mark.parametrize("scale_exp", [-40, -20, 20, 40])
+def test_tile_path_input_scale(tq, scale_exp):
+    # inputs scaled by a power of two (exact in bf16): far from unit norm the
+    # scaled fp16 residual parts must neither overflow nor lose their bits
+    wl = synth.workload("llama8b_decode")
+    spec = synth.draw_quantizer(wl, "K")
+    x = synth.draw_kv_slab(wl, "K", 0, 5, 0, 700) * np.float32(2.0 ** scale_exp)
+    x[3] = 0.0
+    x[4, :] = 0.0
+    x[4, 7] = np.float32(2.0 ** scale_exp)  # a one-hot vector
+    for fmt in (tq.TQ_TOKEN_MAJOR, tq.TQ_BLOCK32):
+        _check(tq, spec, x, fmt, 704, np.arange(700), dtype="bf16", seg=(700, 704, 0), pass_rows=False)
+
+
+@pytest.mark.parametrize("seg_len,offset,n_vec", [(1000, 5, 2000), (777, 37, 777), (600, 32, 1800), (520, 63, 1040)])
+def test_tile_path_block_segments_partial_pairs(tq, seg_len, offset, n_vec):
+    # block records by segments whose first and last 64-row block pairs are
+    # partly covered: the transposed path merges those words bit by bit into a
+    # cache pre-filled with ones; rows outside the segments keep every bit
+    import torch
+    wl = synth.workload("llama8b_decode")
+    spec = synth.draw_quantizer(wl, "V")
+    cap = 1152
+    n_seg = (n_vec + seg_len - 1) // seg_len
+    x = synth.draw_kv_slab(wl, "V", 1, 3, 0, n_vec)
+    i = np.arange(n_vec)
+    rows = (i // seg_len) * cap + offset + i % seg_len
+    oq, dq = gc.quantizers(spec)
+    qv = oracle.quantize(x.astype(np.float64), oq)
+    cache = tq.Cache.empty(dq, n_seg * cap, tq.TQ_BLOCK32)
+    cache.codes.fill_(-1)
+    cache.signs.fill_(-1)
+    xt = torch.from_numpy(x).cuda().to(torch.bfloat16)
+    tq.tq_quantize(dq, tq.TQ_BLOCK32, xt, cache, seg_len=seg_len, seg_stride=cap, seg_offset=offset)
+    torch.cuda.synchronize()
+    got_all = gc.read_cache(cache, dq)
+    gc.compare_records(x.astype(np.float64), oq, qv, gc.select_rows(got_all, rows))
+    untouched = np.setdiff1d(np.arange(n_seg * cap), rows)
+    L = 2 ** dq.mse_bits[0] - 1
+    assert np.all(got_all[0][0][untouched] == L) and np.all(got_all[1][0][untouched])
+
+
 def test_d200_unit_vectors(tq):
     # nearest-neighbour database shape: d = 200, L2-normalised mixture vectors, 4 bits
     wl = synth.workload("nn_search")
