@@ -50,10 +50,10 @@ struct LdsT {
   static constexpr int off_rl = off_x + QT * XH * 2;          // u16 [QT][XH]: the residual's low part
   static constexpr int off_npart = off_rl + QT * XH * 2;      // float [NT][QT]: sums of y^2 per wave
   static constexpr int off_gpart = off_npart + NT * QT * 4;   // float [NT][QT]: sums of r^2 per wave
-  static constexpr int off_nrm = off_gpart + NT * QT * 4;     // f32x4 [2][QT]: (n_g, 1 / n_g or 0, residual scale, 0)
-  static constexpr int off_cb = off_nrm + 2 * QT * 16;        // float [64]: centroids [0, 32), boundaries [32, 64)
+  static constexpr int off_nrm = off_gpart + NT * QT * 4;     // float [2][QT]: group norms n_g
+  static constexpr int off_cb = off_nrm + 2 * QT * 4;         // float [64]: centroids [0, 32), boundaries [32, 64)
   static constexpr int off_rows = off_cb + 64 * 4;            // int64 [QT]: destination rows (token-major)
-  static constexpr int PKW = KP * 4 / 32 + KP / 32 + 4;       // token-major staging row, words
+  static constexpr int PKW = (KP * 4 / 32 + KP / 32 + 4 + 3) / 4 * 4;  // token-major staging row, words (16-byte rows)
   static constexpr int BKW = KP * 5;                          // block staging: code + sign words of one block
   static constexpr int off_pk = off_rows + QT * 8;            // u32: token-major [QT][PKW]; block [2][BKW] + masks [2][BKW]
   static constexpr int PK_WORDS = QT * PKW > 4 * BKW ? QT * PKW : 4 * BKW;
@@ -65,20 +65,38 @@ inline bool t_path_ok(const QArgs& a) {
   return h_path_ok(a) && (a.fmt == TQ_TOKEN_MAJOR || a.blk_owned);
 }
 
-// Sum / OR over the four lane groups (lanes ln, ln + 16, ln + 32, ln + 48),
-// the result in all four.
-__device__ __forceinline__ float lg_sum(float v) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+// Reduce-scatter over the four lane groups: given one value per 16-vector
+// tile mt, lane group lg returns the sum (OR) over the four lane groups of
+// the value of tile lg. The 32-lane swap pairs tiles (0, 2) and (1, 3), the
+// 16-lane swap then pairs the two partial results.
+__device__ __forceinline__ float lg_sum4(float v0, float v1, float v2, float v3) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v0), __float_as_uint(v2), false, false);
+  const float s02 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v1), __float_as_uint(v3), false, false);
+  const float s13 = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(s02), __float_as_uint(s13), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
-__device__ __forceinline__ uint32_t lg_or(uint32_t v) {
-  const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  v = a[0] | a[1];
-  const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  return b[0] | b[1];
+__device__ __forceinline__ uint32_t lg_or4(uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3) {
+  const auto a = __builtin_amdgcn_permlane32_swap(v0, v2, false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(v1, v3, false, false);
+  const auto c = __builtin_amdgcn_permlane16_swap(a[0] | a[1], b[0] | b[1], false, false);
+  return c[0] | c[1];
 }
+
+// All-gather over the four lane groups: out[mt] = the value of lane
+// (ln, mt). The 16-lane swap gives every row the values of its row pair, the
+// 32-lane swaps of those give rows 0 and 2, then rows 1 and 3.
+__device__ __forceinline__ void lg_gather4(float v, float (&out)[4]) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const auto e = __builtin_amdgcn_permlane32_swap(p[0], p[0], false, false);
+  const auto o = __builtin_amdgcn_permlane32_swap(p[1], p[1], false, false);
+  out[0] = __uint_as_float(e[0]);
+  out[1] = __uint_as_float(o[0]);
+  out[2] = __uint_as_float(e[1]);
+  out[3] = __uint_as_float(o[1]);
+}
+
 // OR over each aligned group of 8 lanes, the result in all 8.
 __device__ __forceinline__ uint32_t oct_or(uint32_t s) {
   s |= dpp_u<0xB1>(s);   // quad_perm [1, 0, 3, 2]
@@ -135,15 +153,18 @@ __device__ __forceinline__ void mfma_t_f16x2(const uint16_t* rh, const uint16_t*
   }
 }
 
-// Cells of four unit coordinates: the number of the NB boundaries below each.
+// Cells of four unit coordinates: the number of the NB boundaries below each,
+// plus corr. b_k - u has its sign bit set exactly when u > b_k (a difference
+// of zero is +0 unless b_k = -0 and u = +0, a tie that either cell may take),
+// so the count is a sum of sign bits (no lane masks).
 template <int NB>
-__device__ __forceinline__ void cells4(const float (&u)[4], const float (&tb)[15], int (&c)[4]) {
+__device__ __forceinline__ void cells4(const float (&u)[4], const float (&tb)[15], int corr, int (&c)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    int n = 0;
+    uint32_t n = (uint32_t)corr;
 #pragma unroll
-    for (int k = 0; k < NB; ++k) n += u[i] > tb[k] ? 1 : 0;
-    c[i] = n;
+    for (int k = 0; k < NB; ++k) n += __float_as_uint(tb[k] - u[i]) >> 31;
+    c[i] = (int)n;
   }
 }
 
@@ -171,16 +192,35 @@ __device__ __forceinline__ void load_t(const QArgs& a, const TileGeo& g, bool bl
   }
 }
 
-// Block staging word of the fields of block h, o, channel j0 .. j0 + 3 of
-// group g: the code words (m of them) start at word m (o dg + j0) / 4 of the
-// group's code area, the sign word at word (o dg + j0) / 4 of its sign area.
+// The octet-field words of a lane's four channels: code idx[i] of channel i
+// (token s of the octet) at bit 8 MG i + MG s of an MG-word string. The word
+// of each channel is a constant; MG = 3 fields may straddle two words.
+template <int MG>
+__device__ __forceinline__ void octet_words(const int (&idx)[4], int s, uint32_t (&wv)[4]) {
+  wv[0] = wv[1] = wv[2] = wv[3] = 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int bit0 = 8 * MG * i;  // (a constant once unrolled)
+    const int wi = bit0 >> 5;
+    const uint64_t f = (uint64_t)(uint32_t)idx[i] << ((bit0 & 31) + MG * s);
+    wv[wi] |= (uint32_t)f;
+    if (wi + 1 < MG) wv[wi + 1] |= (uint32_t)(f >> 32);
+  }
+}
+template <int MG>
+__device__ __forceinline__ void octet_or_words(const int (&idx)[4], int s, uint32_t (&wv)[4]) {
+  octet_words<MG>(idx, s, wv);
+#pragma unroll
+  for (int q = 0; q < MG; ++q) wv[q] = oct_or(wv[q]);
+}
+
 
 // The kernel body: this workgroup quantizes tiles first_tile,
 // first_tile + tile_stride, ... of `a` (t_path_ok), with NT * 64 threads and
 // the dynamic LDS block `smem` (LdsT<KP, NT>::bytes).
-template <int KP, int NT>
-__device__ __forceinline__ void quantize_tiles_t(const QArgs& a, int64_t first_tile, int64_t tile_stride,
-                                                 unsigned char* smem) {
+template <int KP, int NT, bool BLK>
+__device__ __forceinline__ void quantize_tiles_t_fmt(const QArgs& a, int64_t first_tile, int64_t tile_stride,
+                                                     unsigned char* smem) {
   using L = LdsT<KP, NT>;
   constexpr int XH = L::XH;
   constexpr int KS = KP / 32;
@@ -191,7 +231,7 @@ __device__ __forceinline__ void quantize_tiles_t(const QArgs& a, int64_t first_t
   uint16_t* rlo = reinterpret_cast<uint16_t*>(smem + L::off_rl);
   float* npart = reinterpret_cast<float*>(smem + L::off_npart);
   float* gpart = reinterpret_cast<float*>(smem + L::off_gpart);
-  f32x4* nrm4 = reinterpret_cast<f32x4*>(smem + L::off_nrm);
+  float* nrmv = reinterpret_cast<float*>(smem + L::off_nrm);
   float* cbk = reinterpret_cast<float*>(smem + L::off_cb);
   int64_t* rows = reinterpret_cast<int64_t*>(smem + L::off_rows);
   uint32_t* pk = reinterpret_cast<uint32_t*>(smem + L::off_pk);
@@ -203,7 +243,7 @@ __device__ __forceinline__ void quantize_tiles_t(const QArgs& a, int64_t first_t
   const int ln = lane & 15;
   const int lg = lane >> 4;
   const int d = a.d;
-  const bool blk = a.fmt == TQ_BLOCK32;  // (then blk_owned)
+  constexpr bool blk = BLK;  // block records (then blk_owned), else token-major
 
   float cent_reg = 0.f, bnd_reg = 0.f;
   {
@@ -289,22 +329,47 @@ __device__ __forceinline__ void quantize_tiles_t(const QArgs& a, int64_t first_t
   const int choff = a.choff[grp];
   const int dg = a.gdim[grp];
   const int wig = w - choff / 16;          // wave index within its group
+  const int gw0 = choff / 16, gw1 = (choff + dg + 15) / 16;  // the group's waves
   const int j0 = 16 * wig + 4 * lg;        // the lane's first channel within the group
   const bool lane_ok = 16 * w + 4 * lg < d;  // the lane's four coordinates exist (d % 4 == 0)
   const bool tail = 16 * w + 16 > d;       // (uniform) the wave has coordinates past d
   const int mid = (nb + 1) / 2 - 1;        // the cell of a zero vector
-  const bool tok = !blk;
+  constexpr bool tok = !BLK;
   const int pk_code_h = 2 * a.cwoff[grp] + mg * wig;
   const int pk_sign_h = 2 * (a.code_words + a.swoff[grp]) + wig;
   const int bcw = a.blk_code_words, bsw = a.blk_sign_words;
   const int bc_g = a.bcwoff[grp], bs_g = bcw + a.bswoff[grp];  // block staging offsets of the group
   const bool signs_on = !a.mse_only;
 
+  // the codebook, once (the tile loop only reads it); boundaries of this
+  // wave's group in registers
+  if (tid < 32) {
+    cbk[tid] = cent_reg;
+    cbk[32 + tid] = bnd_reg;
+  }
+  __syncthreads();
+  float tb[15];
+#pragma unroll
+  for (int k = 0; k < 15; ++k) tb[k] = k < nb ? cbk[32 + boff + k] : INFINITY;
+  // A zero vector (n = 0, so u = 0) takes the middle cell: its count of
+  // boundaries below 0, zc, is corrected by mid - zc.
+  int zc = 0;
+#pragma unroll
+  for (int k = 0; k < 15; ++k) zc += k < nb ? (int)(__float_as_uint(tb[k] - 0.0f) >> 31) : 0;
+  const int zcorr = mid - zc;
+  // 16-byte record stores: every record row and block a multiple of 16 bytes
+  // on 16-byte aligned arrays
+  const bool vec_out = ((reinterpret_cast<uintptr_t>(a.codes) | reinterpret_cast<uintptr_t>(a.signs)) % 16 == 0) &&
+                       (blk ? (bcw % 4 == 0 && bsw % 4 == 0) : (a.code_words % 4 == 0 && a.sign_words % 4 == 0));
+
+  // Barriers per tile: (1) the input tile is staged; (2) the per-wave sums of
+  // y^2 are in; (4) the residual parts and the code fields are in; (5) the
+  // sign fields are in. No barrier ends the tile:
+  // what the next tile writes before its barrier (1) (the input tile) was last
+  // read before (5), and what the store phase reads (destination rows, norms,
+  // partial sums, staged records) is next written after the next (1).
   while (tile < a.n_tiles) {
     const TileGeo cg = g;
-    // ---- stage the tile: input, destination rows, codebook ----
-    if (tok && a.pk_zero)
-      for (int e = tid; e < QT * PKW; e += NT * 64) pk[e] = 0u;
     {
       constexpr int CPR = KP / 8;
 #pragma unroll
@@ -313,23 +378,37 @@ __device__ __forceinline__ void quantize_tiles_t(const QArgs& a, int64_t first_t
         *reinterpret_cast<u32x4*>(xh + v * XH + k) = st.c[i];
       }
     }
+    __syncthreads();  // (1)
+    // the next tile's input, in flight while this one is processed
+    tile = next_live_tile(a, tile + tile_stride, tile_stride, g);
+    if (tile < a.n_tiles) load_t<KP, NT>(a, g, blk, tid, st);
+    if (tok && a.pk_zero)
+      for (int e = tid; e < QT * PKW; e += NT * 64) pk[e] = 0u;
     if (tok && tid < QT) {
+      // destination rows: vector v0 + t of the call (segments of seg_len rows)
       int64_t row = -1;
       if (tid < cg.nvalid) {
-        const int64_t i = cg.v0 + tid;
-        row = a.dst_rows ? a.dst_rows[i] : dest_row(a, i);
+        if (a.dst_rows) {
+          row = a.dst_rows[cg.v0 + tid];
+        } else {
+          const int64_t q0 = cg.v0 / a.seg_len, r0 = cg.v0 - q0 * a.seg_len;  // (uniform)
+          int64_t q = q0, r = r0 + tid;
+          if (a.seg_len >= QT) {
+            if (r >= a.seg_len) {
+              q += 1;
+              r -= a.seg_len;
+            }
+          } else {
+            const uint32_t sl = (uint32_t)a.seg_len, rr32 = (uint32_t)r, dq = rr32 / sl;
+            q += dq;
+            r = rr32 - dq * sl;
+          }
+          row = q * a.seg_stride + a.seg_offset + r;
+        }
         if (row < 0 || row >= a.n_rows) row = -1;
       }
       rows[tid] = row;
     }
-    if (tid < 32) {
-      cbk[tid] = cent_reg;
-      cbk[32 + tid] = bnd_reg;
-    }
-    __syncthreads();
-    // the next tile's input, in flight while this one is processed
-    tile = next_live_tile(a, tile + tile_stride, tile_stride, g);
-    if (tile < a.n_tiles) load_t<KP, NT>(a, g, blk, tid, st);
 
     // ---- y = rot x ----
     // (a token-major tile of at most 16 vectors runs its first 16-vector
@@ -344,110 +423,103 @@ __device__ __forceinline__ void quantize_tiles_t(const QArgs& a, int64_t first_t
     {
       float sq[4];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const float s = fmaf(y[mt][3], y[mt][3], fmaf(y[mt][2], y[mt][2], fmaf(y[mt][1], y[mt][1], y[mt][0] * y[mt][0])));
-        sq[mt] = lg_sum(s);
-      }
-      // lane group lg writes the sums of tile lg
-      const float mine = lg == 0 ? sq[0] : lg == 1 ? sq[1] : lg == 2 ? sq[2] : sq[3];
-      npart[w * QT + 16 * lg + ln] = mine;
+      for (int mt = 0; mt < 4; ++mt)
+        sq[mt] = fmaf(y[mt][3], y[mt][3], fmaf(y[mt][2], y[mt][2], fmaf(y[mt][1], y[mt][1], y[mt][0] * y[mt][0])));
+      // lane l = 16 lg + ln holds the wave's sum for tile row l
+      npart[w * QT + lane] = lg_sum4(sq[0], sq[1], sq[2], sq[3]);
     }
-    __syncthreads();
-    // group norms, their reciprocals and the residual scale
-    if (tid < QT * a.n_groups) {
-      const int gg = tid / QT, v = tid % QT;
-      const int w0 = a.choff[gg] / 16, w1 = (a.choff[gg] + a.gdim[gg] + 15) / 16;
-      float s = 0.f;
-      for (int ww = w0; ww < w1; ++ww) s += npart[ww * QT + v];
-      const float n = sqrtf(s);
-      const float inv = n > 0.f ? 1.0f / n : 0.f;
+    __syncthreads();  // (2)
+    // the group norm of tile row l (lane l of every wave: the group's wave
+    // sums), its reciprocal and the residual scale, then gathered so that
+    // lane (ln, lg) holds those of rows 16 mt + ln, mt = 0 .. 3
+    float nv4[4], inv4[4], sc4[4];
+    {
+      float sum = 0.f;
+      for (int ww = gw0; ww < gw1; ++ww) sum += npart[ww * QT + lane];
+      const float n = sqrtf(sum);
+      const float inv = n > 0.f ? __builtin_amdgcn_rcpf(n) : 0.f;
       const float sc = n > 0.f ? __builtin_amdgcn_ldexpf(1.0f, 10 - __builtin_amdgcn_frexp_expf(n)) : 1.0f;
-      nrm4[gg * QT + v] = f32x4{n, inv, sc, 0.f};
+      if (wig == 0) nrmv[grp * QT + lane] = n;  // for the norm stores
+      lg_gather4(n, nv4);
+      lg_gather4(inv, inv4);
+      lg_gather4(sc, sc4);
     }
-    __syncthreads();
 
     // ---- cells, residual, residual norm partials, packed codes ----
-    float tb[15];
-#pragma unroll
-    for (int k = 0; k < 15; ++k)
-      tb[k] = k < nb ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(cbk[32 + boff + k]))) : INFINITY;
     int idx[4][4];
-    float rr[4][4];
     {
       float gq[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const f32x4 nq = nrm4[grp * QT + 16 * mt + ln];
+        const float nq[3] = {nv4[mt], inv4[mt], sc4[mt]};
         float u[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) u[i] = y[mt][i] * nq[1];
+        const int corr = nq[0] > 0.f ? 0 : zcorr;
         int c[4];
         if (nb == 3)
-          cells4<3>(u, tb, c);
+          cells4<3>(u, tb, corr, c);
         else if (nb == 7)
-          cells4<7>(u, tb, c);
+          cells4<7>(u, tb, corr, c);
         else if (nb == 1)
-          cells4<1>(u, tb, c);
+          cells4<1>(u, tb, corr, c);
         else
-          cells4<15>(u, tb, c);
+          cells4<15>(u, tb, corr, c);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          idx[mt][i] = nq[0] > 0.f ? c[i] : mid;
+          idx[mt][i] = c[i];
           if (tail && !lane_ok) idx[mt][i] = 0;
         }
         float cv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) cv[i] = cbk[coff + idx[mt][i]];
+        float rr[4];
         float s = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          rr[mt][i] = fmaf(-nq[0], cv[i], y[mt][i]);
-          if (tail && !lane_ok) rr[mt][i] = 0.f;
-          s = fmaf(rr[mt][i], rr[mt][i], s);
+          rr[i] = fmaf(-nq[0], cv[i], y[mt][i]);
+          if (tail && !lane_ok) rr[i] = 0.f;
+          s = fmaf(rr[i], rr[i], s);
         }
-        gq[mt] = lg_sum(s);
-        // the residual, scaled, as fp16 high and low parts (the B operand of
-        // the sketch product; the rotation has read the tile: two barriers
-        // lie between)
+        gq[mt] = s;
+        // the residual, scaled by a power of two, as fp16 high and low parts
+        // (the B operand of the sketch product; the rotation read the tile
+        // before barrier (2))
         if (signs_on) {
-          f16x2 h01, h23, l01, l23;
-          const float u0 = rr[mt][0] * nq[2], u1 = rr[mt][1] * nq[2], u2 = rr[mt][2] * nq[2],
-                      u3 = rr[mt][3] * nq[2];
-          h01[0] = (_Float16)u0;
-          h01[1] = (_Float16)u1;
-          h23[0] = (_Float16)u2;
-          h23[1] = (_Float16)u3;
-          l01[0] = (_Float16)(u0 - (float)h01[0]);
-          l01[1] = (_Float16)(u1 - (float)h01[1]);
-          l23[0] = (_Float16)(u2 - (float)h23[0]);
-          l23[1] = (_Float16)(u3 - (float)h23[1]);
+          f16x2 hv[2], lv[2];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const _Float16 h = (_Float16)(rr[i] * nq[2]);
+            hv[i / 2][i % 2] = h;
+            lv[i / 2][i % 2] = (_Float16)fmaf(rr[i], nq[2], -(float)h);
+          }
           const int off = (16 * mt + ln) * XH + 16 * w + 4 * lg;
           *reinterpret_cast<uint2*>(xh + off) =
-              uint2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
+              uint2{__builtin_bit_cast(uint32_t, hv[0]), __builtin_bit_cast(uint32_t, hv[1])};
           *reinterpret_cast<uint2*>(rlo + off) =
-              uint2{__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)};
+              uint2{__builtin_bit_cast(uint32_t, lv[0]), __builtin_bit_cast(uint32_t, lv[1])};
         }
       }
-      const float mine = lg == 0 ? gq[0] : lg == 1 ? gq[1] : lg == 2 ? gq[2] : gq[3];
-      gpart[w * QT + 16 * lg + ln] = mine;
+      gpart[w * QT + lane] = lg_sum4(gq[0], gq[1], gq[2], gq[3]);
     }
     if (tok) {
       // the wave's 16 codes of a row (16 mg bits), assembled across the lane
-      // groups, stored by lane group 0 as mg halfwords
+      // groups: lane l stores the mg halfwords of tile row l
+      uint32_t flo[4], fhi[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const uint32_t f4 = (uint32_t)idx[mt][0] | ((uint32_t)idx[mt][1] << mg) | ((uint32_t)idx[mt][2] << (2 * mg)) |
                             ((uint32_t)idx[mt][3] << (3 * mg));
         const uint64_t f = (uint64_t)f4 << (4 * mg * lg);
-        const uint32_t lo = lg_or((uint32_t)f);
-        const uint32_t hi = mg > 2 ? lg_or((uint32_t)(f >> 32)) : 0u;
-        if (lg == 0 && mt < n_mt) {
-          uint16_t* row = pk16 + (16 * mt + ln) * 2 * PKW + pk_code_h;
-#pragma unroll
-          for (int k = 0; k < 4; ++k)
-            if (k < mg) row[k] = (uint16_t)((k < 2 ? lo : hi) >> (16 * (k & 1)));
-        }
+        flo[mt] = (uint32_t)f;
+        fhi[mt] = (uint32_t)(f >> 32);
       }
+      const uint32_t lo = lg_or4(flo[0], flo[1], flo[2], flo[3]);
+      const uint32_t hi = mg > 2 ? lg_or4(fhi[0], fhi[1], fhi[2], fhi[3]) : 0u;
+      uint16_t* row = pk16 + lane * 2 * PKW + pk_code_h;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (k < mg) row[k] = (uint16_t)((k < 2 ? lo : hi) >> (16 * (k & 1)));
     } else {
       // octet fields: channel j0 + i of the 8 tokens of octet o at bits
       // 8 mg (o dg + j0 + i) + mg s; the 8 lanes of an octet OR their fields
@@ -455,21 +527,15 @@ __device__ __forceinline__ void quantize_tiles_t(const QArgs& a, int64_t first_t
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const int s = ln & 7, h = mt >> 1, o = 2 * (mt & 1) + (ln >> 3);
-        uint32_t wv[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int bit = 8 * mg * i + mg * s;  // < 32 mg
-          const uint64_t f = (uint64_t)(uint32_t)idx[mt][i] << (bit & 31);
-          const int wi = bit >> 5;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (q == wi) wv[q] |= (uint32_t)f;
-            if (q == wi + 1) wv[q] |= (uint32_t)(f >> 32);
-          }
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (q < mg) wv[q] = oct_or(wv[q]);
+        uint32_t wv[4];
+        if (mg == 2)
+          octet_or_words<2>(idx[mt], s, wv);
+        else if (mg == 3)
+          octet_or_words<3>(idx[mt], s, wv);
+        else if (mg == 1)
+          octet_or_words<1>(idx[mt], s, wv);
+        else
+          octet_or_words<4>(idx[mt], s, wv);
         if (s == 0 && lane_ok) {
           uint32_t* dst = pk + h * BKW + bc_g + mg * (o * dg + j0) / 4;
 #pragma unroll
@@ -478,7 +544,7 @@ __device__ __forceinline__ void quantize_tiles_t(const QArgs& a, int64_t first_t
         }
       }
     }
-    __syncthreads();
+    __syncthreads();  // (4)
 
     // ---- s = sketch_rot r; sign bit = [s >= 0] ----
     if (signs_on) {
@@ -487,16 +553,25 @@ __device__ __forceinline__ void quantize_tiles_t(const QArgs& a, int64_t first_t
         mfma_t_f16x2<1, KS, XH>(xh, rlo, sh, sl, ln, lg, sacc);
       else
         mfma_t_f16x2<4, KS, XH>(xh, rlo, sh, sl, ln, lg, sacc);
+      // sign bit i of a lane: [s >= 0] = NOT the sign bit of s (s = -0 is a
+      // tie that either bit may take)
+      uint32_t nibs[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         uint32_t nib = 0u;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) nib |= (sacc[mt][i] >= 0.f ? 1u : 0u) << i;
-        if (!lane_ok) nib = 0u;
-        if (tok) {
-          const uint32_t bits16 = lg_or(nib << (4 * lg));
-          if (lg == 0 && mt < n_mt) pk16[(16 * mt + ln) * 2 * PKW + pk_sign_h] = (uint16_t)bits16;
-        } else {
+        for (int i = 0; i < 4; ++i) nib |= (~__float_as_uint(sacc[mt][i]) >> 31) << i;
+        nibs[mt] = lane_ok ? nib : 0u;
+      }
+      if (tok) {
+        const uint32_t bits16 =
+            lg_or4(nibs[0] << (4 * lg), nibs[1] << (4 * lg), nibs[2] << (4 * lg), nibs[3] << (4 * lg));
+        pk16[lane * 2 * PKW + pk_sign_h] = (uint16_t)bits16;
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const uint32_t nib = nibs[mt];
+        if (!tok) {
           const int s = ln & 7, h = mt >> 1, o = 2 * (mt & 1) + (ln >> 3);
           uint32_t wv = 0u;
 #pragma unroll
@@ -516,21 +591,17 @@ __device__ __forceinline__ void quantize_tiles_t(const QArgs& a, int64_t first_t
         const int s = ln & 7, h = mt >> 1, o = 2 * (mt & 1) + (ln >> 3);
         const int t = 16 * mt + ln;
         const bool in = t >= cg.slot_lo && t < cg.slot_lo + cg.nvalid;
-        uint32_t wv[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int bit = 8 * mg * i + mg * s;
-          const uint64_t f = (uint64_t)(in ? fm : 0u) << (bit & 31);
-          const int wi = bit >> 5;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (q == wi) wv[q] |= (uint32_t)f;
-            if (q == wi + 1) wv[q] |= (uint32_t)(f >> 32);
-          }
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (q < mg) wv[q] = oct_or(wv[q]);
+        const int fi = in ? (int)fm : 0;
+        const int fl[4] = {fi, fi, fi, fi};
+        uint32_t wv[4];
+        if (mg == 2)
+          octet_or_words<2>(fl, s, wv);
+        else if (mg == 3)
+          octet_or_words<3>(fl, s, wv);
+        else if (mg == 1)
+          octet_or_words<1>(fl, s, wv);
+        else
+          octet_or_words<4>(fl, s, wv);
         uint32_t sv = 0u;
 #pragma unroll
         for (int i = 0; i < 4; ++i) sv |= (in ? 1u : 0u) << (8 * i + s);
@@ -544,7 +615,7 @@ __device__ __forceinline__ void quantize_tiles_t(const QArgs& a, int64_t first_t
         }
       }
     }
-    __syncthreads();
+    __syncthreads();  // (5)
 
     // ---- store: norms, then the records ----
     if (tid < QT * a.n_groups) {
@@ -558,38 +629,61 @@ __device__ __forceinline__ void quantize_tiles_t(const QArgs& a, int64_t first_t
         const int w0 = a.choff[gg] / 16, w1 = (a.choff[gg] + a.gdim[gg] + 15) / 16;
         float s = 0.f;
         for (int ww = w0; ww < w1; ++ww) s += gpart[ww * QT + v];
-        store_norms(a.norms, a.norm_f16, row * a.n_groups + gg, nrm4[gg * QT + v][0], sqrtf(s));
+        store_norms(a.norms, a.norm_f16, row * a.n_groups + gg, nrmv[gg * QT + v], sqrtf(s));
       }
     }
     if (tok) {
-      // 16 threads per row, the row's code words then its sign words
-      const int cw = a.code_words, sw = a.sign_words, rw = cw + sw;
-      for (int v = tid >> 4; v < cg.nvalid; v += NT * 4) {
-        const int64_t row = rows[v];
-        if (row < 0) continue;
-        for (int wd = tid & 15; wd < rw; wd += 16) {
-          const uint32_t val = pk[v * PKW + wd];
-          if (wd < cw)
-            a.codes[row * cw + wd] = val;
+      const int cw = a.code_words, sw = a.sign_words;
+      if (vec_out) {
+        // 8 threads per row: 16-byte chunks, the row's code chunks then its sign chunks
+        const int v = tid >> 3, c = tid & 7, cc = cw / 4, sc4 = sw / 4;
+        for (int vv = v; vv < cg.nvalid; vv += NT * 8) {
+          const int64_t row = rows[vv];
+          if (row < 0 || c >= cc + sc4) continue;
+          const u32x4 val = *reinterpret_cast<const u32x4*>(pk + vv * PKW + 4 * c);
+          if (c < cc)
+            *reinterpret_cast<u32x4*>(a.codes + row * cw + 4 * c) = val;
           else
-            a.signs[row * sw + wd - cw] = val;
+            *reinterpret_cast<u32x4*>(a.signs + row * sw + 4 * (c - cc)) = val;
+        }
+      } else {
+        // 16 threads per row, word by word
+        const int rw = cw + sw;
+        for (int v = tid >> 4; v < cg.nvalid; v += NT * 4) {
+          const int64_t row = rows[v];
+          if (row < 0) continue;
+          for (int wd = tid & 15; wd < rw; wd += 16) {
+            const uint32_t val = pk[v * PKW + wd];
+            if (wd < cw)
+              a.codes[row * cw + wd] = val;
+            else
+              a.signs[row * sw + wd - cw] = val;
+          }
         }
       }
     } else {
       const int nw = bcw + (signs_on ? bsw : 0);
+      if (!partial && vec_out) {
+        // both blocks whole: 16-byte chunks
+        const int nc = nw / 4;
+        for (int e = tid; e < 2 * nc; e += NT * 64) {
+          const int h = e >= nc ? 1 : 0, c = e - h * nc;
+          const int64_t blkrow = cg.rowbase / 32 + h;
+          const u32x4 val = *reinterpret_cast<const u32x4*>(pk + h * BKW + 4 * c);
+          uint32_t* dst = 4 * c < bcw ? a.codes + blkrow * bcw + 4 * c : a.signs + blkrow * bsw + (4 * c - bcw);
+          *reinterpret_cast<u32x4*>(dst) = val;
+        }
+      } else {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int vlo = cg.slot_lo > 32 * h ? cg.slot_lo : 32 * h;
-        const int vhi = cg.slot_lo + cg.nvalid < 32 * h + 32 ? cg.slot_lo + cg.nvalid : 32 * h + 32;
-        if (vhi <= vlo) continue;
-        const int64_t blkrow = cg.rowbase / 32 + h;
-        for (int wd = tid; wd < nw; wd += NT * 64) {
-          const uint32_t val = pk[h * BKW + wd];
-          uint32_t* dst = wd < bcw ? a.codes + blkrow * bcw + wd : a.signs + blkrow * bsw + (wd - bcw);
-          if (!partial) {
-            *dst = val;
-          } else {
-            const uint32_t m = pk[(2 + h) * BKW + wd];
+        for (int h = 0; h < 2; ++h) {
+          const int vlo = cg.slot_lo > 32 * h ? cg.slot_lo : 32 * h;
+          const int vhi = cg.slot_lo + cg.nvalid < 32 * h + 32 ? cg.slot_lo + cg.nvalid : 32 * h + 32;
+          if (vhi <= vlo) continue;
+          const int64_t blkrow = cg.rowbase / 32 + h;
+          for (int wd = tid; wd < nw; wd += NT * 64) {
+            const uint32_t val = pk[h * BKW + wd];
+            uint32_t* dst = wd < bcw ? a.codes + blkrow * bcw + wd : a.signs + blkrow * bsw + (wd - bcw);
+            const uint32_t m = partial ? pk[(2 + h) * BKW + wd] : 0xFFFFFFFFu;
             if (m == 0xFFFFFFFFu) {
               *dst = val;
             } else if (m != 0u) {
@@ -600,8 +694,16 @@ __device__ __forceinline__ void quantize_tiles_t(const QArgs& a, int64_t first_t
         }
       }
     }
-    __syncthreads();
   }
+}
+
+template <int KP, int NT>
+__device__ __forceinline__ void quantize_tiles_t(const QArgs& a, int64_t first_tile, int64_t tile_stride,
+                                                 unsigned char* smem) {
+  if (a.fmt == TQ_BLOCK32)
+    quantize_tiles_t_fmt<KP, NT, true>(a, first_tile, tile_stride, smem);
+  else
+    quantize_tiles_t_fmt<KP, NT, false>(a, first_tile, tile_stride, smem);
 }
 
 }  // namespace tqq
