@@ -232,11 +232,19 @@ const char* tq_status_string(int status);
 tq_status tq_build_codebook(int32_t d, int32_t mse_bits, int32_t max_iter, double tol,
                             double* centroids, double* boundaries, double* mse_per_coord);
 
-/* Record sizes for a layout (host-only). Errors: TQ_ERR_INVALID. */
+/* Record sizes for a layout (host-only): the words of one token's stored
+ * form, which [ZB] paragraph 2 names as the quantization indices, the sign
+ * bits of the residual sketch and the norm (two norms per group here, n_g
+ * and gamma_g, as read above). Per group g: d_g m_g code bits and d_g sign
+ * bits (none for MSE-only records), each group's fields starting on a 32-bit
+ * word; TQ_BLOCK32 sizes are those of 32 tokens. Errors: TQ_ERR_INVALID. */
 tq_status tq_record_layout(const tq_layout* layout, tq_record_info* info);
 
 /* sketch_rot = sketch * rot^T for d x d row-major host matrices, accumulated
- * in double and rounded once to float. Host-only. Errors: TQ_ERR_INVALID. */
+ * in double and rounded once to float. Host-only. The sketch of [WD] "2. QJL
+ * Residual" acts on the residual r = x_g - n Pi^T c[idx]; with the residual
+ * kept in the rotated domain (Pi r = y n - n c[idx]) the sketch it needs is
+ * S Pi^T, which this folds once per quantizer. Errors: TQ_ERR_INVALID. */
 tq_status tq_fold_sketch(int32_t d, const float* rot, const float* sketch, float* sketch_rot);
 
 /* Quantize-on-append ([ZB] paragraph 2; [WD] "1. PolarQuant" and "2. QJL

@@ -995,10 +995,19 @@ __device__ __forceinline__ u32x4 bsigns8(const uint32_t* w, int b, uint32_t off)
 }
 
 // DPP move whose pattern sends every lane a value from inside its row
-// (rotations, quad permutations): no lane keeps its old value.
+// (rotations, quad permutations, row broadcasts): no lane keeps its old value.
 template <int CTRL>
 __device__ __forceinline__ float dpp_full(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// out[j][c] = v of lane 2 j + c of this lane's row of 16 (DPP row_newbcast).
+template <int K = 0>
+__device__ __forceinline__ void row_bcast16(float v, float (&out)[8][2]) {
+  if constexpr (K < 16) {
+    out[K / 2][K % 2] = dpp_full<0x150 + K>(v);
+    row_bcast16<K + 1>(v, out);
+  }
 }
 
 // Weight operand of a column: w split into an fp16 part (its leading 11
@@ -1029,7 +1038,6 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
   // (the kernel has no static LDS: the dynamic area starts at LDS address 0,
   // so the table addresses formed in registers are used as they are)
   extern __shared__ __align__(16) unsigned char lds[];
-  float* s_nrm = reinterpret_cast<float*>(lds + kBNrm);
   float* s_m = reinterpret_cast<float*>(lds + kBMisc);
   float* s_lw = s_m + kBW * 8;
   float* s_cent = s_lw + kBW * 8;  // [0, 16) K, [16, 32) V
@@ -1233,19 +1241,16 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
   for (int v = 0; v < NVA; ++v) avr[v] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int v = 0; v < (WV && P8 ? NMT : 1); ++v) avs[v] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float* nrm_k = s_nrm + wv * 128;
-  float* nrm_v = nrm_k + 64;
 
   // K part of a tile: logits, online softmax, and the V weight operands
   // (bvc: code product, bvs: sign product) of its tokens.
   auto kpart = [&](const BRaw<M>& r, int64_t T0, u32x4& bvc, u32x4& bvs) __attribute__((always_inline)) {
     const bool full = T0 + kTile <= N;
-    {
-      const bool nok = full || T0 + (lane >> 1) < N;
-      nrm_k[lane] = nok ? norm_value(r.kn, kn_sh, a.kn_f16) * kn_mul : 0.f;
-      if constexpr (WV != 0) nrm_v[lane] = nok ? norm_value(r.vn, vn_sh, a.vn_f16) : 0.f;
-    }
-    __builtin_amdgcn_wave_barrier();
+    // this lane's norm value (float `lane` of the tile's [32][n, gamma]);
+    // token 8 lg + j, component c is lane 2 j + c of row lg, read by a DPP
+    // row broadcast
+    const bool nok = full || T0 + (lane >> 1) < N;
+    const float kn_l = nok ? norm_value(r.kn, kn_sh, a.kn_f16) * kn_mul : 0.f;
     f32x4 ak[2], as[P8 ? 2 : 1];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
@@ -1264,7 +1269,7 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
     }
     const int64_t tok0 = T0 + 8 * lg;
     float kn[8][2];
-    load_norms<1>(nrm_k + 16 * lg, kn);
+    row_bcast16(kn_l, kn);
     // logits relative to the running integer reference (log2 domain):
     // t = logit - m_ref, folded into the last fma
     const float m_ref = m_run == -INFINITY ? 0.f : m_run;
@@ -1333,7 +1338,7 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
       for (int j = 1; j < 8; ++j) psum += p[j];
       l_run += psum;
       float vn[8][2];
-      load_norms<1>(nrm_v + 16 * lg, vn);
+      row_bcast16(nok ? norm_value(r.vn, vn_sh, a.vn_f16) : 0.f, vn);
       if constexpr (P8) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -1355,7 +1360,6 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
         bvs = gsel ? w : z;
       }
     }
-    __builtin_amdgcn_wave_barrier();
   };
 
   // V part of a tile: accumulate its weighted codes and signs in the rotated

@@ -186,7 +186,10 @@ def test_qjl_wrong_constant_would_be_caught():
     qjl_mean = est.mean() - (q @ x - q @ r)
     wrong = (q @ x - q @ r) + qjl_mean * (2 / math.pi)
     var = (math.pi / (2 * d)) * (r @ r) * (q @ q) - (q @ r) ** 2 / d
-    assert abs(wrong - q @ x) / math.sqrt(var / est.size) > 5 or abs(q @ r) < 1e-3
+    # the seeded draw has a residual inner product far from zero (the slip's
+    # bias is (2/pi - 1) <q, r>), so the comparison below has a signal to see
+    assert abs(q @ r) > 0.1
+    assert abs(wrong - q @ x) / math.sqrt(var / est.size) > 5
 
 
 def test_grouped_vector_unbiased_through_permutation():
