@@ -77,7 +77,7 @@ struct DArgs {
   int T;  // query tokens per head: column hloc is token hloc % T, causal past n_ctx - T + t
   int64_t n_ctx, cap;
   float scale;
-  const _Float16* qprep;  // [batch*hq][3d]: q_rot hi, q_rot lo * 2^11, q_sk
+  const _Float16* qprep;  // [batch*hq][4d]: q_rot hi, q_rot lo * 2^11, q_sk hi, q_sk lo * 2^11
   const float* kscale;    // per K group: the fp16 table holds c * kscale
   const uint32_t* kc;
   const uint32_t* ks;
@@ -106,6 +106,14 @@ __device__ __forceinline__ uint32_t h2bits(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Weight operand of a column: w split into an fp16 part (its leading 11
+// bits, exact in fp16 for normal magnitudes) and the remainder times 2^11;
+// (bsel, csel) = (0, 1) gives the leading part, (2^11, -2^11) the remainder.
+__device__ __forceinline__ float wsplit(float w, float bsel, float csel) {
+  const float hi = __uint_as_float(__float_as_uint(w) & 0xFFFFE000u);
+  return fmaf(bsel, w, csel * hi);
+}
+
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
@@ -129,6 +137,13 @@ __device__ __forceinline__ float dpp_row_z(float v) {
 
 // max over the four 16-lane rows (lanes l, l ^ 16, l ^ 32, l ^ 48): swap the
 // 32-lane halves, then odd and even rows, with v_permlane{32,16}_swap
+// DPP move whose pattern sends every lane a value from inside its row
+// (rotations, quad permutations, row broadcasts): no lane keeps its old value.
+template <int CTRL>
+__device__ __forceinline__ float dpp_full(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
 __device__ __forceinline__ float rows4_max(float v) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
@@ -418,8 +433,14 @@ __device__ __forceinline__ void load_tile(const DArgs& a, int64_t row0, int lane
 // serves all three logit parts and one serves both V parts.
 // WV = 0: logits only; 1: V records with sign bits; 2: MSE-only V records
 // (codes and norms alone; the sign product is skipped).
+// (at least two workgroups of 256 threads per compute unit: a register
+// budget of 256 per lane, which the packed mode's hi / lo columns need
+// without spills)
+#ifndef TQ_PK_MINB
+#define TQ_PK_MINB 2
+#endif
 template <int D, int NG, int M0, int M1, int WV, int HB>
-__global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel(DArgs a) {
+__global__ __launch_bounds__(256, TQ_PK_MINB) void decode_kernel(DArgs a) {
   using G = Geo<D, NG, M0, M1>;
   constexpr bool PK = HB == 4;
   constexpr int NC = G::NC, CPG = G::CPG, NMT = G::NMT, MTPG = G::MTPG, RUN = G::RUN, DG = G::DG;
@@ -493,15 +514,18 @@ __global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel
     const int nc = (1 << M0) + (NG > 1 ? (1 << M1) : 0);
     const int tc = tid < nc ? tid : nc - 1;
     cent_k = a.kcent[tc] * a.kscale[NG > 1 && tc >= (1 << M0) ? 1 : 0];
-    if constexpr (WV != 0) cent_v = a.vcent[tc];
+    // V centroids likewise as fp16(s_g c) with the V group's scale (divided
+    // out when the partial is written)
+    if constexpr (WV != 0) cent_v = a.vcent[tc] * a.kscale[2 + (NG > 1 && tc >= (1 << M0) ? 1 : 0)];
   }
   // ---- this lane's head and its query operands (B operand: channels x heads) ----
   // (loaded before the first tile: loads complete in issue order, so using
   // them then does not wait for the tile)
-  // packed: column ln = (role, head) with role = ln / 4: 0 q_rot hi / rot
-  // weights, 1 q_rot lo / sketch weights, 2 q_sk, 3 unused
-  const int role = PK ? ln >> 2 : 0;
-  const int hcol = PK ? ln & 3 : ln;  // head of this lane's column within the block
+  // packed: column ln = 4 head + role, the four columns of a head in one
+  // lane quad; K roles 0 q_rot hi, 1 q_rot lo, 2 q_sk hi, 3 q_sk lo; V roles
+  // 0 p n hi, 1 p gamma hi (sign product), 2 p n lo, 3 p gamma lo
+  const int role = PK ? ln & 3 : 0;
+  const int hcol = PK ? ln >> 2 : ln;  // head of this lane's column within the block
   const int hloc = hblk * HB + hcol;  // head index within the KV group
   const bool hvalid = hloc < a.group;
   const int hq = kvh * a.group + hloc;
@@ -509,12 +533,12 @@ __global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int g = c / CPG, cl = c % CPG;
-    const _Float16* qp = a.qprep + ((int64_t)b * a.hq + (hvalid ? hq : 0)) * (3 * D) + g * DG + 8 * CPG * lg + 8 * cl;
+    const _Float16* qp = a.qprep + ((int64_t)b * a.hq + (hvalid ? hq : 0)) * (4 * D) + g * DG + 8 * CPG * lg + 8 * cl;
     if constexpr (PK) {
       const u32x4 z{0, 0, 0, 0};
-      const u32x4 v = *reinterpret_cast<const u32x4*>(qp + (role == 0 ? 0 : role == 1 ? D : 2 * D));
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qp + role * D);
       qr[c] = hvalid && role < 2 ? v : z;
-      qs[c] = hvalid && role == 2 ? v : z;
+      qs[c] = hvalid && role >= 2 ? v : z;
     } else {
       const u32x4 z{0, 0, 0, 0};
       const u32x4 vr = *reinterpret_cast<const u32x4*>(qp);
@@ -658,10 +682,12 @@ __global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel
       for (int g = 0; g < NG; ++g) {
         float t;
         if constexpr (PK) {
-          // this lane's column is q_rot hi; q_rot lo and q_sk are 4 and 8 lanes up
+          // quad_perm broadcasts of the head's four columns: every lane
+          // forms its head's logit
           const float v = lr[tau][g][i];
-          const float vl = dpp_row_z<0x104>(v), vs = dpp_row_z<0x108>(v);  // row_shl:4, row_shl:8
-          t = kn[j][2 * g] * fmaf(kLoInv, vl, v) + kn[j][2 * g + 1] * vs;
+          const float v0 = dpp_full<0x00>(v), v1 = dpp_full<0x55>(v), v2 = dpp_full<0xAA>(v),
+                      v3 = dpp_full<0xFF>(v);
+          t = kn[j][2 * g] * fmaf(kLoInv, v1, v0) + kn[j][2 * g + 1] * fmaf(kLoInv, v3, v2);
         } else {
           t = kn[j][2 * g] * fmaf(kLoInv, lrl[tau][g][i], lr[tau][g][i]) + kn[j][2 * g + 1] * ls[tau][g][i];
         }
@@ -677,8 +703,8 @@ __global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel
 #pragma unroll
       for (int j = 0; j < 8; ++j) l2[j] = tok0 + j < lim ? l2[j] : -INFINITY;
     }
-    // (packed: only the role-0 columns are logits; the other columns carry
-    // finite values that no result uses)
+    // (packed: the four lanes of a head's quad hold the same logits; the
+    // role-0 lane stores them)
     if (a.logits) {
       if (hvalid && role == 0) {
         float* lp = a.logits + ((int64_t)b * a.hq + hq) * a.n_ctx + tok0;
@@ -708,11 +734,8 @@ __global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel
         const float corr = m_new == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= corr;
         if constexpr (PK) {
-          // the sketch column of a head (role 1) takes its head's factor
-          // from 4 lanes down; the role 2 and 3 columns are zero
-          const float cc = dpp_row<0x114>(corr);  // row_shr:4
 #pragma unroll
-          for (int v = 0; v < NMT; ++v) acc_r[v] *= cc;
+          for (int v = 0; v < NMT; ++v) acc_r[v] *= corr;
         } else {
 #pragma unroll
           for (int v = 0; v < NMT; ++v) {
@@ -736,26 +759,27 @@ __global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel
       load_norms<NG>(&s_nrm[wv][1][8 * lg * 2 * NG], vn);
       u32x4 pr[NG], pz[NG];
       if constexpr (PK) {
-        // column role 0 carries p n (code product), role 1 carries p gamma of
-        // the head 4 lanes down (sign product); the other columns are 0
-        float pp[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pp[j] = dpp_row<0x114>(p[j]);  // row_shr:4; role 0 keeps its own
+        // column roles of the V products: the leading fp16 part of p n (0)
+        // and its remainder times 2^11 (2) for the code product, the same
+        // of p gamma (1, 3) for the sign product
+        const float* pp = p;
+        const bool rem = role >= 2;
+        const float bsel = rem ? 2048.0f : 0.0f, csel = rem ? -2048.0f : 1.0f;
         const u32x4 z{0, 0, 0, 0};
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
           u32x4 w;
           // (a select of two constant indices: an index that depends on the
           // lane would be lowered to a search over the whole array)
-          const bool r1 = role == 1;
+          const bool r1 = (role & 1) != 0;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float n0 = r1 ? vn[2 * q][2 * g + 1] : vn[2 * q][2 * g];
             const float n1 = r1 ? vn[2 * q + 1][2 * g + 1] : vn[2 * q + 1][2 * g];
-            w[q] = h2bits(pp[2 * q] * n0, pp[2 * q + 1] * n1);
+            w[q] = h2bits(wsplit(pp[2 * q] * n0, bsel, csel), wsplit(pp[2 * q + 1] * n1, bsel, csel));
           }
-          pr[g] = role == 0 ? w : z;
-          pz[g] = role == 1 ? w : z;
+          pr[g] = r1 ? z : w;
+          pz[g] = r1 ? w : z;
         }
       } else {
 #pragma unroll
@@ -841,15 +865,14 @@ __global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel
     float* s_red = reinterpret_cast<float*>(s_tab);
     __syncthreads();  // tables are no longer read
     l_run = rows4_sum(l_run);
-    // (packed: the role-0 lanes own a head's maximum and sum; the role-1
-    // lanes, which hold its sketch sums, read the maximum back from LDS)
+    // (packed: every lane of a head's quad has run its softmax; the role-0
+    // lane stores its maximum and sum)
     if (lg == 0 && role == 0) s_m[wv][hcol] = m_run;
     __syncthreads();
     float M = s_m[0][hcol];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][hcol]);
-    const float m_own = PK ? s_m[wv][hcol] : m_run;
-    const float e = (m_own == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_own - M);
+    const float e = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
     if (lg == 0 && role == 0) s_lw[wv][hcol] = l_run * e;
     float* reg = s_red + (wv & 1) * REG + hcol * HS;
     auto slot = [&](int pt, int v, int i) {
@@ -857,6 +880,17 @@ __global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel
       const int ch = g * DG + RUN * (4 * lg + i) + u;
       return pt * DP + ch + 16 * (ch >> 6);
     };
+    if constexpr (PK) {
+      // a head's remainder columns (roles 2, 3) join their leading columns
+      // (roles 0, 1), two lanes down in the quad
+#pragma unroll
+      for (int v = 0; v < NMT; ++v)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float rem = dpp_full<0xEE>(acc_r[v][i]);  // quad_perm [2, 3, 2, 3]
+          acc_r[v][i] = role < 2 ? fmaf(kLoInv, rem, acc_r[v][i]) : acc_r[v][i];
+        }
+    }
     if (wv < 2) {
 #pragma unroll
       for (int v = 0; v < NMT; ++v)
@@ -885,8 +919,10 @@ __global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel
         }
     }
     __syncthreads();
-    // write the partial of every valid head: [max (log2 domain), sum, acc_rot[D], acc_sk[D]]
+    // write the partial of every valid head: [max (log2 domain), sum,
+    // acc_rot[D] / s_V,g, acc_sk[D]]
     const int nh = a.group - hblk * HB < HB ? a.group - hblk * HB : HB;
+    const float vinv[2] = {1.0f / a.kscale[2], NG > 1 ? 1.0f / a.kscale[3] : 1.0f};
     for (int e2 = tid; e2 < nh * (2 + 2 * D); e2 += 256) {
       const int h = e2 / (2 + 2 * D), k = e2 % (2 + 2 * D);
       float val;
@@ -899,6 +935,7 @@ __global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel
         const int pt = (k - 2) / D, ch = (k - 2) % D;
         const int idx = h * HS + pt * DP + ch + 16 * (ch >> 6);
         val = s_red[idx] + s_red[REG + idx];
+        if (pt == 0) val *= vinv[NG > 1 && ch >= DG ? 1 : 0];
       }
       const int hq2 = kvh * a.group + hblk * HB + h;
       a.part[(((int64_t)b * a.hq + hq2) * a.n_split + split) * (2 + 2 * D) + k] = val;
@@ -928,9 +965,9 @@ __global__ __launch_bounds__(256, HB == 4 && NG == 1 ? 3 : 2) void decode_kernel
 //   HB = 8 (KV groups of more than 4 query heads, in blocks of 8 heads):
 //     K codes x [q_rot hi | q_rot lo * 2^11] (8 heads each), K signs x
 //     [q_sk | q_sk]; V codes x [w_n hi | w_n lo * 2^11] and V signs x
-//     [w_g hi | w_g lo * 2^11], with w_n = p n and w_g = p gamma the softmax
-//     weights times the token's norms, split into an fp16 part and its
-//     remainder so that the weights keep about 21 bits;
+//     [w_g | w_g], with w_n = p n and w_g = p gamma the softmax weights
+//     times the token's norms; w_n is split into an fp16 part and its
+//     remainder so that it keeps about 21 bits, w_g is plain fp16;
 //   HB = 4 (at most 4 query heads per KV head): column 4 h + r, role r =
 //     0 q_rot hi / w_n hi, 1 q_rot lo / w_n lo, 2 q_sk / w_g hi, 3 - / w_g lo;
 //     codes and signs accumulate into the same accumulator (their B columns
@@ -994,12 +1031,6 @@ __device__ __forceinline__ u32x4 bsigns8(const uint32_t* w, int b, uint32_t off)
   return lds_at<u32x4>(baddr(w[b >> 2], off, b & 3));
 }
 
-// DPP move whose pattern sends every lane a value from inside its row
-// (rotations, quad permutations, row broadcasts): no lane keeps its old value.
-template <int CTRL>
-__device__ __forceinline__ float dpp_full(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
-}
 
 // out[j][c] = v of lane 2 j + c of this lane's row of 16 (DPP row_newbcast).
 template <int K = 0>
@@ -1010,13 +1041,6 @@ __device__ __forceinline__ void row_bcast16(float v, float (&out)[8][2]) {
   }
 }
 
-// Weight operand of a column: w split into an fp16 part (its leading 11
-// bits, exact in fp16 for normal magnitudes) and the remainder times 2^11;
-// (bsel, csel) = (0, 1) gives the leading part, (2^11, -2^11) the remainder.
-__device__ __forceinline__ float wsplit(float w, float bsel, float csel) {
-  const float hi = __uint_as_float(__float_as_uint(w) & 0xFFFFE000u);
-  return fmaf(bsel, w, csel * hi);
-}
 
 // Record words of one 32-token tile held by one lane of the byte-table
 // kernel (the K rows of token rows r and r + 4, the lane's share of the
@@ -1153,7 +1177,7 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
   u32x4 bq[NC], bs[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    const _Float16* qp = a.qprep + ((int64_t)b * a.hq + (hvalid ? hq : 0)) * (3 * D) + 32 * lg + 8 * c;
+    const _Float16* qp = a.qprep + ((int64_t)b * a.hq + (hvalid ? hq : 0)) * (4 * D) + 32 * lg + 8 * c;
     const u32x4 z{0, 0, 0, 0};
     const u32x4 vh = *reinterpret_cast<const u32x4*>(qp);
     const u32x4 vl = *reinterpret_cast<const u32x4*>(qp + D);
@@ -1660,7 +1684,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // workspace: [prepared queries][K codebook scales, 2 floats][split partials]
 size_t workspace_for(const tq_decode_shape* s, int d, bool with_v, int n_split) {
   const size_t heads = (size_t)s->batch * s->n_q_heads * q_tokens(s);
-  size_t bytes = align256(heads * 3 * d * sizeof(_Float16)) + 256;
+  size_t bytes = align256(heads * 4 * d * sizeof(_Float16)) + 256;
   if (with_v) bytes += align256(heads * (size_t)n_split * (2 + 2 * d) * sizeof(float));
   return bytes;
 }
@@ -1861,7 +1885,7 @@ tq_status plan_decode(const tq_quantizer* kq, const tq_quantizer* vq, const tq_d
   const int n_heads = shape->batch * shape->n_q_heads * T;
   _Float16* qprep = reinterpret_cast<_Float16*>(workspace);
   float* kscale = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
-                                           align256((size_t)n_heads * 3 * D * sizeof(_Float16)));
+                                           align256((size_t)n_heads * 4 * D * sizeof(_Float16)));
   float* part = kscale + 64;
 
   *pl = Plan{};

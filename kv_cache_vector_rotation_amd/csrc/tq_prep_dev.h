@@ -1,8 +1,8 @@
 // Query preparation of a decode step, shared by the decode entry points and
 // the fused append + prep launch.
 //
-// q_rot = f rot q (stored as fp16 hi and (q - hi) * 2^11) and
-// q_sk = f alpha_g sketch q (fp16), with f = scale * log2(e) so that the
+// q_rot = f rot q and q_sk = f alpha_g sketch q, each stored as fp16 hi and
+// (q - hi) * 2^11 (about 22 bits), with f = scale * log2(e) so that the
 // split pass forms log2-domain logits directly; fp32 sums in ascending k,
 // scaled after the sum. A block takes kPrepRows rows of the stacked
 // [rot; sketch] matrix and kPrepHeads heads; both are staged in LDS by
@@ -223,15 +223,13 @@ __device__ void prep_block(const PrepArgs& p, int bx, int by, int t, unsigned ch
   for (int r = 0; r < HPT; ++r) {
     const int h = h0 + hq + TPR * r;
     if (h >= p.n_heads) continue;
-    _Float16* dst = p.qprep + (int64_t)h * 3 * D;
+    // [q_rot hi | q_rot lo | q_sk hi | q_sk lo], D each: row r of [rot;
+    // sketch] goes to r (hi) and D + r (lo) of its half
+    _Float16* dst = p.qprep + (int64_t)h * 4 * D + (row < D ? 0 : D);
     acc[r] *= f;
     const _Float16 hi = (_Float16)acc[r];
-    if (row < D) {
-      dst[row] = hi;
-      dst[D + row] = (_Float16)((acc[r] - (float)hi) * kLoScale);
-    } else {
-      dst[D + row] = hi;  // q_sk at [2 D, 3 D)
-    }
+    dst[row] = hi;
+    dst[D + row] = (_Float16)((acc[r] - (float)hi) * kLoScale);
   }
 }
 

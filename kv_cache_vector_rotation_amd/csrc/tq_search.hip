@@ -61,7 +61,7 @@ struct SArgs {
   const uint32_t* signs;
   const float* norms;
   int norm_f16;  // norm pairs stored as float16 (one word per row)
-  const _Float16* qprep;  // [n_q][3 D]: q_rot hi, q_rot lo * 2^11 (unused here), q_sk
+  const _Float16* qprep;  // [n_q][4 D]: q_rot hi, q_rot lo * 2^11 (unused here), q_sk hi, q_sk lo (unused)
   const float* kscale;    // fp16 codebook scale s
   const float* centroids;
   float* part_score;      // [n_q][n_slices][kKL]
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(256, 3) void search_kernel(SArgs a) {
     const int h = qb * kQB + cb * 16 + (l & 15);
     const int k = 32 * c + 8 * (l >> 4);
     u32x4 v = u32x4{0u, 0u, 0u, 0u};
-    if (h < a.n_q && k < D) v = *reinterpret_cast<const u32x4*>(a.qprep + (int64_t)h * 3 * D + 2 * pt * D + k);
+    if (h < a.n_q && k < D) v = *reinterpret_cast<const u32x4*>(a.qprep + (int64_t)h * 4 * D + 2 * pt * D + k);
     s_b[e] = v;
   }
   __syncthreads();
@@ -364,7 +364,7 @@ bool plan_search(const tq_quantizer* qz, int64_t n_db, int64_t n_q, int k, Plan*
   if (ns < 1) ns = 1;
   pl->tiles_per_slice = (n_tiles + ns - 1) / ns;
   pl->n_slices = (int)((n_tiles + pl->tiles_per_slice - 1) / pl->tiles_per_slice);
-  pl->qprep_bytes = ((size_t)n_q * 3 * pl->d * 2 + 255) / 256 * 256;
+  pl->qprep_bytes = ((size_t)n_q * 4 * pl->d * 2 + 255) / 256 * 256;
   pl->part_bytes = (size_t)n_q * pl->n_slices * kKL * 4;
   pl->total = pl->qprep_bytes + 256 + 2 * pl->part_bytes;
   return true;

@@ -346,7 +346,10 @@ def test_causal_chunk_last_token_equals_decode(tq):
                       out=out1)
     torch.cuda.synchronize()
     a, b1 = out[0, -1].cpu().numpy(), out1[0].cpu().numpy()
-    assert np.max(np.abs(a - b1)) <= 1e-4 * np.max(np.abs(b1))
+    # (the decode of a 4-head group carries each softmax weight as an fp16
+    # part and its remainder; the chunk's 24 columns take the weights as
+    # plain fp16, 2^-11 relative, so the two agree to that rounding)
+    assert np.max(np.abs(a - b1)) <= 5e-4 * np.max(np.abs(b1))
 
 
 def test_causal_chunk_append_step_equals_separate_calls(tq):

@@ -8,10 +8,11 @@
 - llama70b_long (batch 4, 64 query heads over 8 KV heads, 131072 tokens,
   3 bits): the 8192-token prefill chunk of every head quantized at once
   (sampled rows against the oracle), then a decode step over the full cache,
-  checked on sampled (batch, KV head) pairs.
+  checked on (batch, KV head) pairs that include every batch index and every
+  KV head (interior ones included).
 - mixed_3p5 / mixed_2p5 (batch 16, two channel groups with their own
-  codebooks): a fused decode step over 32768 tokens, checked on sampled
-  pairs.
+  codebooks): a fused decode step over 32768 tokens, checked on pairs that
+  include every batch index and every KV head.
 
 The records of every checked pair are the oracle's own quantization of the
 synthetic tokens, uploaded to the device; pairs that are not checked hold
@@ -204,8 +205,9 @@ def test_llama70b_long_full_size_sampled(tq):
         rows = np.array([(i // chunk) * cap + t0 + i % chunk for i in sel])
         xs = x[sel].astype(np.float64)
         gc.compare_records(xs, oq, oracle.quantize(xs, oq), _read_rows(tq, cache, dq, rows))
-    # a decode step over the full cache; sampled pairs hold the oracle's records
-    sampled = [(0, 0), (3, 7)]
+    # a decode step over the full cache; the checked pairs (every KV head, each
+    # batch index twice) hold the oracle's records
+    sampled = [(h % B, h) for h in range(H)]
     deq = {}
     for b, h in sampled:
         r0 = (b * H + h) * cap
@@ -245,7 +247,7 @@ def test_mixed_bits_step_full_size_sampled(tq, name):
     vc = tq.Cache.empty(dvq, n_rows, tq.TQ_BLOCK32)
     _random_fill(tq, kc, dkq, n_rows, 35)
     _random_fill(tq, vc, dvq, n_rows, 36)
-    sampled = [(0, 0), (15, 7)]
+    sampled = [(b, (3 * b) % H) for b in range(B)]  # every batch index, every KV head twice
     deq = {}
     for b, h in sampled:
         r0 = (b * H + h) * cap
