@@ -150,7 +150,12 @@ def test_full_size_sampled_queries(tq):
     ref = oracle.estimated_scores(q[sample], *rec, oq)
     _check(gi[sample], gs[sample], ref, 10)
     ex, _ = oracle.exact_search(q[sample], x, 10)
-    print("recall@10 on the sampled queries:", oracle.recall_at_k(gi[sample], ex))
+    # the device's recall equals the oracle estimator's own recall on the same
+    # queries (the top-k check above leaves only ties free: allow two swaps)
+    oi = np.argsort(-ref, axis=1, kind="stable")[:, :10]
+    r_dev, r_orc = oracle.recall_at_k(gi[sample], ex), oracle.recall_at_k(oi, ex)
+    print("recall@10 on the sampled queries: device", r_dev, "oracle estimator", r_orc)
+    assert abs(r_dev - r_orc) <= 2 / (len(sample) * 10)
 
 
 test_full_size_sampled_queries = pytest.mark.timeout(900)(test_full_size_sampled_queries)
