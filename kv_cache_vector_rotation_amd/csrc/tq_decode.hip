@@ -1032,14 +1032,6 @@ __device__ __forceinline__ u32x4 bsigns8(const uint32_t* w, int b, uint32_t off)
 }
 
 
-// out[j][c] = v of lane 2 j + c of this lane's row of 16 (DPP row_newbcast).
-template <int K = 0>
-__device__ __forceinline__ void row_bcast16(float v, float (&out)[8][2]) {
-  if constexpr (K < 16) {
-    out[K / 2][K % 2] = dpp_full<0x150 + K>(v);
-    row_bcast16<K + 1>(v, out);
-  }
-}
 
 
 // Record words of one 32-token tile held by one lane of the byte-table
@@ -1062,6 +1054,7 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
   // (the kernel has no static LDS: the dynamic area starts at LDS address 0,
   // so the table addresses formed in registers are used as they are)
   extern __shared__ __align__(16) unsigned char lds[];
+  float* s_nrm = reinterpret_cast<float*>(lds + kBNrm);
   float* s_m = reinterpret_cast<float*>(lds + kBMisc);
   float* s_lw = s_m + kBW * 8;
   float* s_cent = s_lw + kBW * 8;  // [0, 16) K, [16, 32) V
@@ -1259,6 +1252,8 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
   __syncthreads();
 
   float m_run = -INFINITY, l_run = 0.f;
+  float* nrm_k = s_nrm + wv * 128;
+  float* nrm_v = nrm_k + 64;
   constexpr int NVA = WV ? NMT : 1;
   f32x4 avr[NVA], avs[WV && P8 ? NMT : 1];
 #pragma unroll
@@ -1270,11 +1265,12 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
   // (bvc: code product, bvs: sign product) of its tokens.
   auto kpart = [&](const BRaw<M>& r, int64_t T0, u32x4& bvc, u32x4& bvs) __attribute__((always_inline)) {
     const bool full = T0 + kTile <= N;
-    // this lane's norm value (float `lane` of the tile's [32][n, gamma]);
-    // token 8 lg + j, component c is lane 2 j + c of row lg, read by a DPP
-    // row broadcast
-    const bool nok = full || T0 + (lane >> 1) < N;
-    const float kn_l = nok ? norm_value(r.kn, kn_sh, a.kn_f16) * kn_mul : 0.f;
+    {
+      const bool nok = full || T0 + (lane >> 1) < N;
+      nrm_k[lane] = nok ? norm_value(r.kn, kn_sh, a.kn_f16) * kn_mul : 0.f;
+      if constexpr (WV != 0) nrm_v[lane] = nok ? norm_value(r.vn, vn_sh, a.vn_f16) : 0.f;
+    }
+    __builtin_amdgcn_wave_barrier();
     f32x4 ak[2], as[P8 ? 2 : 1];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
@@ -1293,7 +1289,7 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
     }
     const int64_t tok0 = T0 + 8 * lg;
     float kn[8][2];
-    row_bcast16(kn_l, kn);
+    load_norms<1>(nrm_k + 16 * lg, kn);
     // logits relative to the running integer reference (log2 domain):
     // t = logit - m_ref, folded into the last fma
     const float m_ref = m_run == -INFINITY ? 0.f : m_run;
@@ -1362,7 +1358,7 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
       for (int j = 1; j < 8; ++j) psum += p[j];
       l_run += psum;
       float vn[8][2];
-      row_bcast16(nok ? norm_value(r.vn, vn_sh, a.vn_f16) : 0.f, vn);
+      load_norms<1>(nrm_v + 16 * lg, vn);
       if constexpr (P8) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -1384,6 +1380,7 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
         bvs = gsel ? w : z;
       }
     }
+    __builtin_amdgcn_wave_barrier();
   };
 
   // V part of a tile: accumulate its weighted codes and signs in the rotated
@@ -2003,8 +2000,8 @@ tq_status run_phases(const Plan& pl, unsigned phases, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
-// Fused appends + query preparation: the blocks of one launch quantize the
-// new K vectors, then the new V vectors, then run the query preparation (the
+// Fused appends + query preparation: the blocks of one launch run the query
+// preparation, then quantize the new K vectors, then the new V vectors (the
 // three are independent, so their latencies overlap).
 // ---------------------------------------------------------------------------
 constexpr int kStepKP = 128, kStepNT = 8;  // quantize shape for d = 128
@@ -2015,6 +2012,8 @@ struct StepArgs {
   int k_small, v_small;  // append takes the one-block-per-vector path
   tqp::PrepArgs prep;
   int prep_x;  // prep blocks along x; the prep blocks are laid out x-major
+  int n_prep;  // prep blocks (the first blocks of the grid: they are short and
+               // then leave every compute unit to the appends)
 };
 
 // SMALL: every append takes the few-vector path (a smaller kernel without the
@@ -2023,8 +2022,13 @@ struct StepArgs {
 template <bool SMALL, bool H>
 __global__ __launch_bounds__(kStepNT * 64) void step_kernel(StepArgs s) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int b = blockIdx.x;
-  if (b < s.nk + s.nv) {
+  if ((int)blockIdx.x < s.n_prep) {
+    const int pb = blockIdx.x;
+    tqp::prep_block<kD, kStepNT * 64>(s.prep, pb % s.prep_x, pb / s.prep_x, threadIdx.x, smem);
+    return;
+  }
+  const int b = blockIdx.x - s.n_prep;
+  {
     const bool is_k = b < s.nk;
     if (SMALL || (is_k ? s.k_small : s.v_small))
       tqq::quantize_small<kStepNT * 64>(is_k ? s.k : s.v, is_k ? b : b - s.nk, smem);
@@ -2035,9 +2039,6 @@ __global__ __launch_bounds__(kStepNT * 64) void step_kernel(StepArgs s) {
       else
         tqq::quantize_tiles<kStepKP, kStepNT>(is_k ? s.k : s.v, is_k ? b : b - s.nk, is_k ? s.nk : s.nv, smem);
     }
-  } else {
-    const int pb = b - s.nk - s.nv;
-    tqp::prep_block<kD, kStepNT * 64>(s.prep, pb % s.prep_x, pb / s.prep_x, threadIdx.x, smem);
   }
 }
 
@@ -2095,7 +2096,8 @@ extern "C" tq_status tq_attn_decode_append(const tq_quantizer* kq, const tq_quan
   sa.nv = v_empty ? 0 : sa.v_small ? (int)sa.v.n_vec : (int)(sa.v.n_tiles < n_cu ? sa.v.n_tiles : n_cu);
   sa.prep = pl.prep;
   sa.prep_x = tqp::prep_blocks_x<kD>();
-  const int grid = sa.nk + sa.nv + sa.prep_x * pl.prep_grid_y;
+  sa.n_prep = sa.prep_x * pl.prep_grid_y;
+  const int grid = sa.n_prep + sa.nk + sa.nv;
   constexpr int lds_small = tqp::prep_lds_bytes<kD>() > tqq::SmallLds<kStepNT * 64>::bytes
                                 ? tqp::prep_lds_bytes<kD>()
                                 : tqq::SmallLds<kStepNT * 64>::bytes;
