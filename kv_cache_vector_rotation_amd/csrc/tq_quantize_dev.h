@@ -173,6 +173,49 @@ __device__ __forceinline__ void mfma_tiles(const float* xr, const float (&b)[KPG
   }
 }
 
+// The same product with the B fragment read from global memory (the
+// row-major d x d matrix m, rows past d and entries past a row's end as
+// zeros), one step ahead of its use: for d > 128 the matrix slices are not
+// kept in registers (with 13 or 16 waves per workgroup they would not fit
+// without spills); a wave's 16 rows stay in the caches across tiles.
+template <int NMT, int KPG, int XS>
+__device__ __forceinline__ void mfma_tiles_gmem(const float* xr, const float* m, int d, int m_vec, int orow, int ln,
+                                                int lg, f32x4 (&acc)[4]) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bool row_ok = orow < d;
+  const float* rowp = m + (int64_t)(row_ok ? orow : d - 1) * d;
+  auto ld = [&](int q) __attribute__((always_inline)) -> f32x4 {
+    const int k = 16 * q + 4 * lg;
+    f32x4 v;
+    if (m_vec) {
+      v = *reinterpret_cast<const f32x4*>(rowp + (k < d ? k : d - 4));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = rowp[k + j < d ? k + j : d - 1];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (!row_ok || k + j >= d) v[j] = 0.f;
+    return v;
+  };
+  f32x4 b = ld(0);
+#pragma unroll 1
+  for (int q = 0; q < KPG / 4; ++q) {
+    const f32x4 bn = ld(q + 1 < KPG / 4 ? q + 1 : q);
+    f32x4 a4[NMT];
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+      a4[mt] = *reinterpret_cast<const f32x4*>(xr + (mt * 16 + ln) * XS + 16 * q + 4 * lg);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[mt][j], b[j], acc[mt], 0, 0, 0);
+    b = bn;
+  }
+}
+
 // LDS layout (bytes), KP = padded K, NT = number of 16-wide coordinate tiles.
 // H: the half-precision MFMA variant (bf16 input tile, fp16 residual parts):
 // the input tile is bf16 [QT][XH]; once the rotation has read it, the same
@@ -572,8 +615,11 @@ __device__ __forceinline__ void quantize_tiles(const QArgs& a, int64_t first_til
   // For d <= 128 the sketch slice lives in LDS (read once per product), which
   // leaves the register file to the rotation slice and the tile's values;
   // larger d keeps both slices in registers.
-  float brot[H ? 1 : KPG];
-  float bskr[SKR_LDS || H ? 1 : KPG];
+  // (for KP > 128 both slices are read from global memory in the products)
+  constexpr bool GMEM = KP > 128 && !H;
+  float brot[H || GMEM ? 1 : KPG];
+  constexpr bool SKR_GMEM = GMEM;
+  static_assert(SKR_LDS || H || GMEM, "the sketch slice is in LDS, registers or global memory");
   f32x4* skr_lds = reinterpret_cast<f32x4*>(smem + L::off_skr);
   // H: the same slices as B operands of the 16x16x32 products, lane (ln, lg)
   // holding M[16 w + ln][32 s + 8 lg + j], j = 0 .. 7, as 16-bit pairs:
@@ -638,8 +684,8 @@ __device__ __forceinline__ void quantize_tiles(const QArgs& a, int64_t first_til
       sh[s2] = u32x4{vh[0], vh[1], vh[2], vh[3]};
       sl[s2] = u32x4{vl[0], vl[1], vl[2], vl[3]};
     }
-  } else {
-    float bs[KPG];
+  } else if constexpr (!GMEM) {
+    float bs[SKR_LDS ? KPG : 1];
     const int64_t rb = (int64_t)(ocoord < d ? ocoord : d - 1) * d;
     if (a.m_vec) {
       // d is a multiple of 4 and the matrices are 16-byte aligned
@@ -648,11 +694,12 @@ __device__ __forceinline__ void quantize_tiles(const QArgs& a, int64_t first_til
         const int k = 16 * q + 4 * lg;
         const int kc = k < d ? k : d - 4;
         const f32x4 r4 = *reinterpret_cast<const f32x4*>(a.rot + rb + kc);
-        const f32x4 s4 = *reinterpret_cast<const f32x4*>(a.skr + rb + kc);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          brot[4 * q + j] = r4[j];
-          bs[4 * q + j] = s4[j];
+        for (int j = 0; j < 4; ++j) brot[4 * q + j] = r4[j];
+        if constexpr (SKR_LDS) {
+          const f32x4 s4 = *reinterpret_cast<const f32x4*>(a.skr + rb + kc);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bs[4 * q + j] = s4[j];
         }
       }
     } else {
@@ -661,22 +708,19 @@ __device__ __forceinline__ void quantize_tiles(const QArgs& a, int64_t first_til
         const int k = 16 * (kk / 4) + 4 * lg + kk % 4;
         const int kc = k < d ? k : d - 1;
         brot[kk] = a.rot[rb + kc];
-        bs[kk] = a.skr[rb + kc];
+        if constexpr (SKR_LDS) bs[kk] = a.skr[rb + kc];
       }
     }
 #pragma unroll
     for (int kk = 0; kk < KPG; ++kk) {
       const bool ok = ocoord < d && 16 * (kk / 4) + 4 * lg + kk % 4 < d;
       brot[kk] = ok ? brot[kk] : 0.f;
-      bs[kk] = ok ? bs[kk] : 0.f;
+      if constexpr (SKR_LDS) bs[kk] = ok ? bs[kk] : 0.f;
     }
     if constexpr (SKR_LDS) {
 #pragma unroll
       for (int q = 0; q < KPG / 4; ++q)
         skr_lds[(w * (KPG / 4) + q) * 64 + lane] = f32x4{bs[4 * q], bs[4 * q + 1], bs[4 * q + 2], bs[4 * q + 3]};
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < KPG; ++kk) bskr[kk] = bs[kk];
     }
   }
   // group of this wave's coordinates (group boundaries are multiples of 16);
@@ -728,6 +772,11 @@ __device__ __forceinline__ void quantize_tiles(const QArgs& a, int64_t first_til
         mfma_tiles_bf16x3<1, KS, XH>(xh, rh, rm, rlo, ln, lg, yacc);
       else
         mfma_tiles_bf16x3<4, KS, XH>(xh, rh, rm, rlo, ln, lg, yacc);
+    } else if constexpr (GMEM) {
+      if (n_mt == 1)
+        mfma_tiles_gmem<1, KPG, XS>(xr, a.rot, d, a.m_vec, ocoord, ln, lg, yacc);
+      else
+        mfma_tiles_gmem<4, KPG, XS>(xr, a.rot, d, a.m_vec, ocoord, ln, lg, yacc);
     } else {
       if (n_mt == 1)
         mfma_tiles<1, KPG, XS>(xr, brot, ln, lg, yacc);
@@ -857,9 +906,9 @@ __device__ __forceinline__ void quantize_tiles(const QArgs& a, int64_t first_til
           mfma_tiles_lds<4, KPG, XS>(xr, skr_lds + w * (KPG / 4) * 64 + lane, ln, lg, sacc);
       } else {
         if (n_mt == 1)
-          mfma_tiles<1, KPG, XS>(xr, bskr, ln, lg, sacc);
+          mfma_tiles_gmem<1, KPG, XS>(xr, a.skr, d, a.m_vec, ocoord, ln, lg, sacc);
         else
-          mfma_tiles<4, KPG, XS>(xr, bskr, ln, lg, sacc);
+          mfma_tiles_gmem<4, KPG, XS>(xr, a.skr, d, a.m_vec, ocoord, ln, lg, sacc);
       }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
