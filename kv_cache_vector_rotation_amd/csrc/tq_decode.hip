@@ -1503,6 +1503,337 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Chunk kernel: the split-K pass when a KV head has many query columns (a
+// causal chunk of T query tokens gives G T columns), for one quantizer group
+// of d = 128. The 16-column kernel would decode every tile once per 16
+// columns; here a workgroup of 8 waves decodes each 32-token tile of its
+// split once into LDS as fp16 MFMA operands, and each wave then runs the
+// logits, softmax and V products of one 16-column block from them:
+//   K tile  [32 rows][128 channels]: fp16(s c[code]) and fp16 +-1 signs, row
+//           16 tau + r holding the token that MFMA row r of half tau takes
+//           (8 (r / 4) + r % 4 + 4 tau), so the 16 rows one operand read
+//           spans fall in disjoint banks;
+//   V tile  [128 channels][32 tokens]: the same for V;
+//   norms   [32][n, gamma] for K (n / s_K) and V.
+// Decoding: thread t takes 8 K codes and 8 K sign bits of token t / 16
+// (channels 8 (t mod 16) ...), and 8 V codes and sign bits of channel t / 4
+// (octet t mod 4), turns code pairs into fp16 pairs through a 2^(2m)-entry
+// LDS table, and stores 16 bytes per operand. Two tile buffers: tile t + 1 is
+// decoded (and tile t + 2 loaded) while tile t is computed, one barrier per
+// tile. Columns, weights and partials
+// are those of the 16-column kernel (q_rot hi / lo and q_sk; plain fp16
+// weights), so the combine reads the same partial layout.
+// ---------------------------------------------------------------------------
+constexpr int kCW = 8;                // waves (16-column blocks) per workgroup
+constexpr int kCThreads = 64 * kCW;
+constexpr int kCKS = 128 + 8;         // row stride (fp16) of the K operand tiles
+constexpr int kCVS = 32 + 8;          // row stride (fp16) of the V operand tiles
+
+struct ChunkTile {
+  _Float16 ka[32 * kCKS], ks[32 * kCKS];
+  _Float16 va[128 * kCVS], vs[128 * kCVS];
+  float kn[64], vn[64];
+};
+// pair tables: entry e = (fp16(s c[e & mask]), fp16(s c[e >> m])) for a pair
+// of codes, 16 replicas side by side (a lane reads replica lane mod 16, so
+// lanes that look up different entries mostly hit different banks)
+constexpr int kCRep = 16;
+struct ChunkLds {
+  ChunkTile tile[2];  // tile t in tile[t % 2]: one decoded while the other is computed
+  uint32_t kpair[256 * kCRep], vpair[256 * kCRep];
+};
+
+// Raw record words of one tile held by one thread between load and decode.
+struct ChunkRaw {
+  uint32_t kc0, kc1, ks, vc0, vc1, vs, nrm;
+};
+
+// eight fp16 +-1 of the bits of byte b (bit 1 -> +1), as four words
+__device__ __forceinline__ u32x4 sign_operand(uint32_t b) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = (b >> (2 * i)) & 1u, hi = (b >> (2 * i + 1)) & 1u;
+    r[i] = 0xBC00BC00u ^ (lo << 15) ^ (hi << 31);
+  }
+  return r;
+}
+
+template <int M, int WV>
+__global__ __launch_bounds__(kCThreads, 1) void chunk_kernel(DArgs a) {
+  constexpr int D = 128, NC = 4, NMT = 8;
+  constexpr uint32_t PMASK = (1u << (2 * M)) - 1u;
+  constexpr int CW = 4 * M;    // K code words per row
+  constexpr int BCW = 128 * M; // V code words per 32-row block
+  __shared__ __align__(16) ChunkLds L;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ln = lane & 15;
+  const int lg = lane >> 4;
+  const int split = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int b = bh / a.hkv;
+  const int kvh = bh % a.hkv;
+
+  int64_t N = a.n_ctx;
+  if (a.seq_lens) {
+    const int64_t n = a.seq_lens[b];
+    N = n < 1 ? 1 : (n > a.n_ctx ? a.n_ctx : n);
+  }
+  const int64_t n_tiles = (N + kTile - 1) / kTile;
+  const int64_t tps = (n_tiles + a.n_split - 1) / a.n_split;
+  const int64_t t_begin = split * tps;
+  const int64_t t_end = t_begin + tps < n_tiles ? t_begin + tps : n_tiles;
+  const int64_t rowbase = (int64_t)bh * a.cap;
+  auto tile_row = [&](int64_t t) __attribute__((always_inline)) -> int64_t {
+    if (!a.block_table) return rowbase + t * kTile;
+    int64_t pb = a.block_table[(int64_t)b * a.max_blocks + t];
+    pb = pb < 0 ? 0 : (pb >= a.n_pblocks ? a.n_pblocks - 1 : pb);
+    return (pb * a.hkv + kvh) * kTile;
+  };
+
+  // ---- what this thread decodes ----
+  const int kr = tid >> 4, kch = (tid & 15) * 8;  // K: token kr, channels kch ..
+  const int krow = 16 * ((kr >> 2) & 1) + 4 * (kr >> 3) + (kr & 3);  // its LDS row
+  const int kbit = M * kch;                       // first code bit in the row
+  const int vj = tid >> 2, vo = tid & 3;          // V: channel vj, octet vo
+  const int vbit = 8 * M * (vo * D + vj);         // first code bit in the block
+  auto load = [&](int64_t t, ChunkRaw& r) __attribute__((always_inline)) {
+    const int64_t row0 = tile_row(t);
+    const uint32_t* kcp = a.kc + (row0 + kr) * CW;
+    const int kw = kbit >> 5;
+    r.kc0 = kcp[kw];
+    r.kc1 = kcp[kw + 1 < CW ? kw + 1 : CW - 1];
+    r.ks = a.ks[(row0 + kr) * 4 + (kch >> 5)];
+    r.nrm = 0u;
+    if (tid < 64) {
+      const char* kn = reinterpret_cast<const char*>(a.kn) + (row0 << a.kn_shift);
+      r.nrm = *reinterpret_cast<const uint32_t*>(kn + (a.kn_f16 ? 4 * (tid >> 1) : 4 * tid));
+    }
+    if constexpr (WV != 0) {
+      const uint32_t* vcp = a.vc + (row0 >> 5) * BCW;
+      const int vw = vbit >> 5;
+      r.vc0 = vcp[vw];
+      r.vc1 = vcp[vw + 1 < BCW ? vw + 1 : BCW - 1];
+      if constexpr (WV == 1) r.vs = a.vs[(row0 >> 5) * D + ((vo * D + vj) >> 2)];
+      if (tid >= 64 && tid < 128) {
+        const char* vn = reinterpret_cast<const char*>(a.vn) + (row0 << a.vn_shift);
+        const int e = tid - 64;
+        r.nrm = *reinterpret_cast<const uint32_t*>(vn + (a.vn_f16 ? 4 * (e >> 1) : 4 * e));
+      }
+    }
+  };
+  const float kinv = 1.0f / a.kscale[0];
+  auto decode = [&](const ChunkRaw& r, int64_t T0, ChunkTile& B) __attribute__((always_inline)) {
+    {
+      const uint32_t f = __builtin_amdgcn_alignbit(r.kc1, r.kc0, kbit & 31);  // 8 M code bits
+      u32x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = L.kpair[((f >> (2 * M * i)) & PMASK) * kCRep + (lane & (kCRep - 1))];
+      *reinterpret_cast<u32x4*>(&B.ka[krow * kCKS + kch]) = w;
+      *reinterpret_cast<u32x4*>(&B.ks[krow * kCKS + kch]) = sign_operand((r.ks >> (kch & 31)) & 0xFFu);
+    }
+    if constexpr (WV != 0) {
+      const uint32_t f = __builtin_amdgcn_alignbit(r.vc1, r.vc0, vbit & 31);
+      u32x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = L.vpair[((f >> (2 * M * i)) & PMASK) * kCRep + (lane & (kCRep - 1))];
+      *reinterpret_cast<u32x4*>(&B.va[vj * kCVS + 8 * vo]) = w;
+      if constexpr (WV == 1)
+        *reinterpret_cast<u32x4*>(&B.vs[vj * kCVS + 8 * vo]) =
+            sign_operand((r.vs >> (8 * ((vo * D + vj) & 3))) & 0xFFu);
+    }
+    // norms past the sequence read as 0 (their tokens are masked)
+    if (tid < 128) {
+      const int e = tid & 63;
+      const bool nok = T0 + (e >> 1) < N;
+      const bool is_k = tid < 64;
+      const int f16 = is_k ? a.kn_f16 : a.vn_f16;
+      const float v = nok ? norm_value(r.nrm, f16 ? 16u * (e & 1) : 0u, f16) : 0.f;
+      if (is_k)
+        B.kn[e] = (e & 1) ? v : v * kinv;
+      else if constexpr (WV != 0)
+        B.vn[e] = v;
+    }
+  };
+
+  // ---- pair tables of the scaled codebooks ----
+  {
+    const float ks0 = a.kscale[0];
+    for (int x = tid; x < (int)(PMASK + 1) * kCRep; x += kCThreads) {
+      const int e = x / kCRep, c0 = e & ((1 << M) - 1), c1 = e >> M;
+      L.kpair[x] = h2bits(a.kcent[c0] * ks0, a.kcent[c1] * ks0);
+      if constexpr (WV != 0) L.vpair[x] = h2bits(a.vcent[c0] * a.kscale[2], a.vcent[c1] * a.kscale[2]);
+    }
+  }
+
+  // ---- this wave's 16 columns and their query operands ----
+  const int hloc = (blockIdx.z * kCW + wv) * 16 + ln;
+  const bool hvalid = hloc < a.group;
+  const bool wave_on = __builtin_amdgcn_readfirstlane((blockIdx.z * kCW + wv) * 16 < a.group ? 1 : 0) != 0;
+  const int hq = kvh * a.group + hloc;
+  u32x4 qr[NC], qrl[NC], qs[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const _Float16* qp = a.qprep + ((int64_t)b * a.hq + (hvalid ? hq : 0)) * (4 * D) + 32 * c + 8 * lg;
+    const u32x4 z{0, 0, 0, 0};
+    qr[c] = hvalid ? *reinterpret_cast<const u32x4*>(qp) : z;
+    qrl[c] = hvalid ? *reinterpret_cast<const u32x4*>(qp + D) : z;
+    qs[c] = hvalid ? *reinterpret_cast<const u32x4*>(qp + 2 * D) : z;
+  }
+  const int64_t lim = a.T > 1 ? N - a.T + hloc % a.T + 1 : N;  // tokens this column sees
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 acc_r[WV ? NMT : 1], acc_s[WV == 1 ? NMT : 1];
+#pragma unroll
+  for (int u = 0; u < (WV ? NMT : 1); ++u) acc_r[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < (WV == 1 ? NMT : 1); ++u) acc_s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int64_t T0, const ChunkTile& B) __attribute__((always_inline)) {
+    // ---- logits: MFMA row ln of half tau is token 8 (ln / 4) + ln % 4 + 4 tau,
+    // so lane (ln, lg) ends with tokens 8 lg + j, j = 4 tau + i, of column ln
+    f32x4 lr[2], lrl[2], ls[2];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      lr[tau] = lrl[tau] = ls[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int row = 16 * tau + ln;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const u32x4 ak = *reinterpret_cast<const u32x4*>(&B.ka[row * kCKS + 32 * c + 8 * lg]);
+        const u32x4 az = *reinterpret_cast<const u32x4*>(&B.ks[row * kCKS + 32 * c + 8 * lg]);
+        lr[tau] = mfma16(ak, qr[c], lr[tau]);
+        lrl[tau] = mfma16(ak, qrl[c], lrl[tau]);
+        ls[tau] = mfma16(az, qs[c], ls[tau]);
+      }
+    }
+    float kn[8][2];
+    load_norms<1>(&B.kn[16 * lg], kn);
+    const int64_t tok0 = T0 + 8 * lg;
+    float l2[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int tau = j >> 2, i = j & 3;
+      l2[j] = kn[j][0] * fmaf(kLoInv, lrl[tau][i], lr[tau][i]) + kn[j][1] * ls[tau][i];
+      if (tok0 + j >= lim) l2[j] = -INFINITY;  // causal limit and the sequence end
+    }
+    if (a.logits && hvalid) {
+      float* lp = a.logits + ((int64_t)b * a.hq + hq) * a.n_ctx + tok0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (tok0 + j < N) lp[j] = l2[j] * kLn2;
+    }
+    if constexpr (WV != 0) {
+      float mx = l2[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) mx = fmaxf(mx, l2[j]);
+      mx = rows4_max(mx);
+      // integer log2-domain reference (as the other split-K kernels)
+      const float m_new = fmaxf(m_run, ceilf(mx));
+      if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+        const float corr = m_new == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= corr;
+#pragma unroll
+        for (int u = 0; u < NMT; ++u) acc_r[u] *= corr;
+        if constexpr (WV == 1) {
+#pragma unroll
+          for (int u = 0; u < NMT; ++u) acc_s[u] *= corr;
+        }
+        m_run = m_new;
+      }
+      const float m_ref = m_run == -INFINITY ? 0.f : m_run;
+      float p[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        p[j] = __builtin_amdgcn_exp2f(l2[j] - m_ref);
+        l_run += p[j];
+      }
+      float vn[8][2];
+      load_norms<1>(&B.vn[16 * lg], vn);
+      u32x4 pr, pz;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        pr[q] = h2bits(p[2 * q] * vn[2 * q][0], p[2 * q + 1] * vn[2 * q + 1][0]);
+        pz[q] = h2bits(p[2 * q] * vn[2 * q][1], p[2 * q + 1] * vn[2 * q + 1][1]);
+      }
+#pragma unroll
+      for (int u = 0; u < NMT; ++u) {
+        const u32x4 av = *reinterpret_cast<const u32x4*>(&B.va[(16 * u + ln) * kCVS + 8 * lg]);
+        acc_r[u] = mfma16(av, pr, acc_r[u]);
+        if constexpr (WV == 1) {
+          const u32x4 az = *reinterpret_cast<const u32x4*>(&B.vs[(16 * u + ln) * kCVS + 8 * lg]);
+          acc_s[u] = mfma16(az, pz, acc_s[u]);
+        }
+      }
+    }
+  };
+
+  // ---- tile loop: compute tile j from one buffer while tile j + 1 is
+  // decoded into the other; the records of tile i sit in register slot i mod 3
+  // from their load, three tiles ahead, to their decode ----
+  if (t_begin < t_end) {
+    ChunkRaw r0, r1, r2;
+    auto slot = [&](auto kc) __attribute__((always_inline)) -> ChunkRaw& {
+      constexpr int k = decltype(kc)::value;
+      if constexpr (k == 0) return r0;
+      else if constexpr (k == 1) return r1;
+      else return r2;
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    load(t_begin, r0);
+    if (t_begin + 1 < t_end) load(t_begin + 1, r1);
+    if (t_begin + 2 < t_end) load(t_begin + 2, r2);
+    __syncthreads();  // pair tables
+    decode(r0, t_begin * kTile, L.tile[0]);
+    if (t_begin + 3 < t_end) load(t_begin + 3, r0);
+    __syncthreads();
+    int64_t t = t_begin;
+    // stage of tile t = t_begin + j: slot k holds tile j + 1
+    auto stage = [&](auto kc) __attribute__((always_inline)) {
+      const int j = (int)(t - t_begin);
+      if (t + 1 < t_end) {
+        decode(slot(kc), (t + 1) * kTile, L.tile[(j + 1) & 1]);
+        if (t + 4 < t_end) load(t + 4, slot(kc));
+      }
+      if (wave_on) compute(t * kTile, L.tile[j & 1]);
+      __syncthreads();
+      ++t;
+      return t >= t_end;
+    };
+    for (;;) {
+      if (stage(I1{})) break;
+      if (stage(I2{})) break;
+      if (stage(I0{})) break;
+    }
+  }
+
+  // ---- partial of each of this wave's columns: [max, sum, acc_rot / s_V, acc_sk] ----
+  if constexpr (WV != 0) {
+    l_run = rows4_sum(l_run);
+    if (hvalid) {
+      float* pp = a.part + (((int64_t)b * a.hq + hq) * a.n_split + split) * (2 + 2 * D);
+      if (lg == 0) {
+        pp[0] = m_run;
+        pp[1] = l_run;
+      }
+      const float vinv = 1.0f / a.kscale[2];
+#pragma unroll
+      for (int u = 0; u < NMT; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ch = 16 * u + 4 * lg + i;
+          pp[2 + ch] = acc_r[u][i] * vinv;
+          pp[2 + D + ch] = WV == 1 ? acc_s[u][i] : 0.f;
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Query preparation (see tq_prep_dev.h), 256 threads per block.
 // ---------------------------------------------------------------------------
 template <int D>
@@ -1700,14 +2031,38 @@ inline bool byte_kernel_ok(const tq_layout& l) {
 // Kernel, head block and split count of a decode call (the workspace size
 // and the launch both follow from it).
 struct DecodeCfg {
-  bool byte;
+  bool byte, chunk;
   int hb, n_hblk, n_split;
 };
+
+// The chunk kernel serves a KV head's many columns from tiles decoded once:
+// one quantizer group of d = 128 and more than one 16-column block.
+inline bool chunk_kernel_ok(const tq_layout& l, int group) { return l.d == 128 && l.n_groups == 1 && group > 16; }
 
 DecodeCfg decode_cfg(const tq_layout& l, bool with_v, const tq_decode_shape* s) {
   DecodeCfg c{};
   const int T = s->n_q_tokens < 1 ? 1 : s->n_q_tokens;
   const int group = s->n_q_heads / s->n_kv_heads * T;
+  c.chunk = chunk_kernel_ok(l, group);
+  if (c.chunk) {
+    // 16-column blocks, kCW of them per workgroup (grid z); about one
+    // workgroup per compute unit, at least one tile per split
+    c.hb = 16;
+    c.n_hblk = (group + 15) / 16;
+    const int n_z = (c.n_hblk + kCW - 1) / kCW;
+    const int64_t n_tiles = (s->n_ctx + kTile - 1) / kTile;
+    int64_t max_split = n_tiles < kMaxSplit ? n_tiles : kMaxSplit;
+    if (max_split < 1) max_split = 1;
+    if (s->n_split > 0) {
+      c.n_split = (int)(s->n_split < max_split ? s->n_split : max_split);
+      return c;
+    }
+    const int64_t per = (int64_t)s->batch * s->n_kv_heads * n_z;
+    int64_t want = (256 + per - 1) / per;
+    if (want > max_split) want = max_split;
+    c.n_split = (int)(want < 1 ? 1 : want);
+    return c;
+  }
   c.byte = byte_kernel_ok(l);
   c.hb = c.byte ? (group <= 4 ? 4 : 8) : heads_per_block(group, with_v);
   c.n_hblk = (group + c.hb - 1) / c.hb;
@@ -1758,6 +2113,24 @@ hipError_t dispatch_byte(const DArgs& a, int m, int hb, int n_hblk, hipStream_t 
     case 1: return dispatch_byte_hb<1, WV>(a, hb, n_hblk, st);
     case 2: return dispatch_byte_hb<2, WV>(a, hb, n_hblk, st);
     default: return dispatch_byte_hb<4, WV>(a, hb, n_hblk, st);
+  }
+}
+
+template <int M, int WV>
+hipError_t launch_chunk(const DArgs& a, int n_hblk, hipStream_t st) {
+  (void)hipGetLastError();  // a launch error is reported below, not an older one
+  const dim3 grid((unsigned)a.n_split, (unsigned)(a.batch * a.hkv), (unsigned)((n_hblk + kCW - 1) / kCW));
+  hipLaunchKernelGGL((chunk_kernel<M, WV>), grid, dim3(kCThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int WV>
+hipError_t dispatch_chunk(const DArgs& a, int m, int n_hblk, hipStream_t st) {
+  switch (m) {
+    case 1: return launch_chunk<1, WV>(a, n_hblk, st);
+    case 2: return launch_chunk<2, WV>(a, n_hblk, st);
+    case 3: return launch_chunk<3, WV>(a, n_hblk, st);
+    default: return launch_chunk<4, WV>(a, n_hblk, st);
   }
 }
 
@@ -1825,6 +2198,7 @@ struct Plan {
   int n_hblk, hb, prep_grid_y, n_heads, n_groups, m0, m1, group_dim0, T, hq_orig;
   bool with_v, v_mse;  // V records present; V records without sign bits
   bool byte;           // the byte-table split-K kernel
+  bool chunk;          // the decode-once chunk kernel
   const float* vrot;
   const float* vsketch;
   float* out;
@@ -1889,6 +2263,7 @@ tq_status plan_decode(const tq_quantizer* kq, const tq_quantizer* vq, const tq_d
   pl->n_hblk = n_hblk;
   pl->hb = cfg.hb;
   pl->byte = cfg.byte;
+  pl->chunk = cfg.chunk;
   pl->n_heads = n_heads;
   pl->n_groups = l.n_groups;
   pl->m0 = l.mse_bits[0];
@@ -1972,7 +2347,11 @@ tq_status run_phases(const Plan& pl, unsigned phases, hipStream_t st) {
   }
   if (phases & TQ_PHASE_SPLIT) {
     hipError_t e;
-    if (pl.byte)
+    if (pl.chunk)
+      e = !pl.with_v  ? dispatch_chunk<0>(pl.a, pl.m0, pl.n_hblk, st)
+          : pl.v_mse ? dispatch_chunk<2>(pl.a, pl.m0, pl.n_hblk, st)
+                     : dispatch_chunk<1>(pl.a, pl.m0, pl.n_hblk, st);
+    else if (pl.byte)
       e = !pl.with_v  ? dispatch_byte<0>(pl.a, pl.m0, pl.hb, pl.n_hblk, st)
           : pl.v_mse ? dispatch_byte<2>(pl.a, pl.m0, pl.hb, pl.n_hblk, st)
                      : dispatch_byte<1>(pl.a, pl.m0, pl.hb, pl.n_hblk, st);

@@ -286,6 +286,9 @@ CHUNK_CASES = [
     ("llama8b_decode", dict(batch=1, n_q_heads=4, n_kv_heads=1), 40, 64, 40),    # the whole context
     ("mixed_3p5", dict(batch=1, n_q_heads=8, n_kv_heads=2), 777, 800, 8),
     ("llama70b_long", dict(batch=1, n_q_heads=16, n_kv_heads=2), 2000, 2048, 33),
+    # widths 1 and 4 bits per code, a ragged context, three column blocks
+    ("llama8b_decode", dict(batch=1, n_q_heads=8, n_kv_heads=2, groups=((128, 1),)), 333, 352, 12),
+    ("llama8b_decode", dict(batch=1, n_q_heads=8, n_kv_heads=2, groups=((128, 4),), n_outliers=0), 450, 480, 9),
 ]
 
 
@@ -326,6 +329,64 @@ def test_causal_chunk_matches_oracle(tq, name, over, n_ctx, cap, T):
         assert ok, ("out", b, w)
         worst_o = max(worst_o, w)
     print(name, over, n_ctx, T, "logits", worst_l, "out", worst_o)
+
+
+@pytest.mark.parametrize("v_mse,f16", [(True, False), (False, True), (True, True)])
+def test_causal_chunk_record_variants(tq, v_mse, f16):
+    # a chunk of 16 query tokens per head (64 columns per KV head: the
+    # decode-once chunk kernel) over MSE-only V records and / or fp16 norms
+    import torch
+    wl = synth.workload("llama8b_decode", batch=1, n_q_heads=8, n_kv_heads=2)
+    n_ctx, cap, T = 600, 640, 16
+    o = _oracle_side(wl, n_ctx, cap, v_mse=v_mse, k_f16=f16, v_f16=f16)
+    kq = tq.Quantizer.from_parts(o["ks"].rotations, o["ks"].sketches, o["bits"], perm=o["ks"].perm, norm_f16=f16)
+    vq = tq.Quantizer.from_parts(o["vs"].rotations, o["vs"].sketches, o["bits"], perm=o["vs"].perm,
+                                 mse_only=v_mse, norm_f16=f16)
+    kc = gc.to_device_cache(kq, tq.TQ_TOKEN_MAJOR, 2 * cap, o["karr"])
+    vc = gc.to_device_cache(vq, tq.TQ_BLOCK32, 2 * cap, o["varr"])
+    q = _chunk_queries(wl, T)
+    qt = torch.from_numpy(q).cuda().to(torch.bfloat16)
+    out = torch.full((1, T, 8, 128), float("nan"), device="cuda")
+    tq.tq_attn_decode(kq, vq, tq.decode_shape(1, 8, 2, n_ctx, cap, wl.scale, n_q_tokens=T), qt, kc, vc, out=out)
+    torch.cuda.synchronize()
+    _, ro = oracle.attention_prefill(q[0].astype(np.float64), o["k_t"][0], o["v_t"][0], wl.scale)
+    ok, w = gc.normwise_close(out[0].cpu().numpy().astype(np.float64), ro)
+    print("chunk variants", v_mse, f16, "out", w)
+    assert ok, w
+
+
+def test_causal_chunk_split_count_and_logits_only(tq):
+    # the chunk kernel's result does not depend on the split count beyond
+    # fp32 summation order, and a logits-only call gives the same logits
+    import torch
+    wl = synth.workload("llama8b_decode", batch=1, n_q_heads=8, n_kv_heads=2)
+    n_ctx, cap, T = 900, 928, 10
+    o = _oracle_side(wl, n_ctx, cap)
+    kq = tq.Quantizer.from_parts(o["ks"].rotations, o["ks"].sketches, o["bits"], perm=o["ks"].perm)
+    vq = tq.Quantizer.from_parts(o["vs"].rotations, o["vs"].sketches, o["bits"], perm=o["vs"].perm)
+    kc = gc.to_device_cache(kq, tq.TQ_TOKEN_MAJOR, 2 * cap, o["karr"])
+    vc = gc.to_device_cache(vq, tq.TQ_BLOCK32, 2 * cap, o["varr"])
+    qt = torch.from_numpy(_chunk_queries(wl, T)).cuda().to(torch.bfloat16)
+    outs, lgs = [], []
+    for n_split in (1, 5, 29):
+        shape = tq.decode_shape(1, 8, 2, n_ctx, cap, wl.scale, n_q_tokens=T, n_split=n_split)
+        lg = torch.full((1, 8, T, n_ctx), float("nan"), device="cuda")
+        out = torch.empty((1, T, 8, 128), device="cuda")
+        tq.tq_attn_decode(kq, vq, shape, qt, kc, vc, logits=lg, out=out)
+        outs.append(out.cpu().numpy())
+        lgs.append(lg.cpu().numpy())
+    lg_only = torch.full((1, 8, T, n_ctx), float("nan"), device="cuda")
+    tq.tq_attn_decode(kq, None, tq.decode_shape(1, 8, 2, n_ctx, cap, wl.scale, n_q_tokens=T), qt, kc, None,
+                      logits=lg_only)
+    torch.cuda.synchronize()
+    for o2 in outs[1:]:
+        assert np.max(np.abs(o2 - outs[0])) <= 5e-5 * np.max(np.abs(outs[0]))
+    for l2 in lgs[1:]:
+        assert np.array_equal(np.isnan(l2), np.isnan(lgs[0]))
+        fin = np.isfinite(lgs[0])
+        assert np.array_equal(l2[fin], lgs[0][fin])
+    fin = np.isfinite(lgs[0])
+    assert np.array_equal(lg_only.cpu().numpy()[fin], lgs[0][fin])
 
 
 def test_causal_chunk_last_token_equals_decode(tq):
