@@ -165,9 +165,9 @@ def traffic_record(workload):
         return None
     rec = json.load(open(TRAFFIC_FILE))
     sha = hashlib.sha256(open(DECODE_SOURCE, "rb").read()).hexdigest()
-    if rec.get("source_sha256") != sha:
+    if rec.get("source_sha256") != sha or workload not in rec.get("workloads", {}):
         return None
-    return rec.get("workloads", {}).get(workload)
+    return dict(rec["workloads"][workload], kernel=rec.get("kernel"))
 
 
 def _quantize_timed(tq, torch, calls, launches):
@@ -745,7 +745,8 @@ def main():
     tr = traffic_record(args.workload)
     roofline = {"bound": "hbm", "achieved": head["split_achieved_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": head["split_frac"], "traffic": tr["bytes_per_launch"] if tr else None,
-                "kernel": "decode_kernel (split-K pass)", "kernel_us": head["split_kernel_us"],
+                "kernel": "split-K pass" + (f" ({tr['kernel']})" if tr and tr.get("kernel") else ""),
+                "kernel_us": head["split_kernel_us"],
                 "kernel_timing": "events around replays of a graph of split-K launches, one per cache copy",
                 "algorithmic_bytes": head["split_algorithmic_bytes"]}
     dims = [g for g, _ in wl.groups]
