@@ -52,6 +52,7 @@
 #include "tq_prep_dev.h"
 #include "tq_quantize_dev.h"
 #include "tq_quantize_t_dev.h"
+#include "tq_quantize_p_dev.h"
 #include "turboquant.h"
 
 namespace {
@@ -978,7 +979,7 @@ __global__ __launch_bounds__(256, TQ_PK_MINB) void decode_kernel(DArgs a) {
 #ifndef TQ_BYTE_NBUF
 #define TQ_BYTE_NBUF 2
 #endif
-constexpr int kBW = 8;                       // waves per workgroup
+constexpr int kBW = 8;                       // waves per workgroup (a multiple of 4)
 constexpr int kBThreads = 64 * kBW;
 constexpr uint32_t kBSignBase = 1u << 16;    // LDS byte offset of the sign table
 constexpr int kBTabBytes = 2 << 16;          // both tables
@@ -1431,7 +1432,8 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
   if constexpr (WV != 0) {
     // ---- merge the eight waves into one partial per head ----
     // Region r (0..3) holds, per part (code / sign accumulator) and channel,
-    // the 16 columns of waves r and r + 4 scaled to the workgroup maximum:
+    // the sum of the 16 columns of waves r, r + 4, ... scaled to the
+    // workgroup maximum:
     // float (part, ch, col) at part (128 16 + 64) + 16 ch + col + 16 (ch / 32),
     // so the 64 lanes of one store fall in 64 different banks.
     constexpr int PS = 128 * 16 + 64, RS = 2 * PS;
@@ -1462,10 +1464,10 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
           }
         }
     };
-    if (wv < 4) put(false);
-    __syncthreads();
-    if (wv >= 4) put(true);
-    __syncthreads();
+    for (int pass = 0; pass < kBW / 4; ++pass) {
+      if (wv / 4 == pass) put(pass > 0);
+      __syncthreads();
+    }
     // partial of every valid head: [max (log2 domain), sum, acc_rot[D] / s_V, acc_sk[D]]
     const int nh = a.group - hblk * HB < HB ? a.group - hblk * HB : HB;
     const float vinv = 1.0f / a.kscale[2];
@@ -2421,6 +2423,32 @@ __global__ __launch_bounds__(kStepNT * 64) void step_kernel(StepArgs s) {
   }
 }
 
+// The same with the pipelined tile path for the bulk appends (both take it
+// with code width MG; V carries sign bits iff VSIGNS).
+template <int MG, bool VSIGNS>
+__global__ __launch_bounds__(kStepNT * 64) void step_kernel_p(StepArgs s) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  if ((int)blockIdx.x < s.n_prep) {
+    const int pb = blockIdx.x;
+    tqp::prep_block<kD, kStepNT * 64>(s.prep, pb % s.prep_x, pb / s.prep_x, threadIdx.x, smem);
+    return;
+  }
+  const int b = blockIdx.x - s.n_prep;
+  const bool is_k = b < s.nk;
+  if (is_k ? s.k_small : s.v_small)
+    tqq::quantize_small<kStepNT * 64>(is_k ? s.k : s.v, is_k ? b : b - s.nk, smem);
+  else if (is_k)
+    tqq::quantize_tiles_p<MG, false, true>(s.k, b, s.nk, smem);
+  else
+    tqq::quantize_tiles_p<MG, true, VSIGNS>(s.v, b - s.nk, s.nv, smem);
+}
+
+template <int MG>
+const void* step_kernel_p_fn(bool vsigns) {
+  return vsigns ? reinterpret_cast<const void*>(&step_kernel_p<MG, true>)
+                : reinterpret_cast<const void*>(&step_kernel_p<MG, false>);
+}
+
 }  // namespace
 
 extern "C" tq_status tq_attn_decode_phases(unsigned phases, const tq_quantizer* kq,
@@ -2487,12 +2515,30 @@ extern "C" tq_status tq_attn_decode_append(const tq_quantizer* kq, const tq_quan
   const void* fn = all_small ? reinterpret_cast<const void*>(&step_kernel<true, false>)
                    : h       ? reinterpret_cast<const void*>(&step_kernel<false, true>)
                              : reinterpret_cast<const void*>(&step_kernel<false, false>);
-  const int lds_tiles = h ? lds_h : lds_f;
+  // the pipelined tile path: every bulk append takes it with one code width
+  // (K with sign bits)
+  const bool kp = k_empty || sa.k_small || (tqq::p_path_ok(sa.k) && !sa.k.mse_only);
+  const bool vp = v_empty || sa.v_small || tqq::p_path_ok(sa.v);
+  const int kbits = (k_empty || sa.k_small) ? 0 : sa.k.gbits[0];
+  const int vbits = (v_empty || sa.v_small) ? 0 : sa.v.gbits[0];
+  const int pbits = kbits ? kbits : vbits;
+  const bool pipe = !all_small && kp && vp && (kbits == 0 || vbits == 0 || kbits == vbits);
+  const bool vsigns = v_empty || !sa.v.mse_only;
+  const int lds_tiles = pipe ? tqq::LdsP::bytes : h ? lds_h : lds_f;
   const int lds_use = all_small ? lds_small : lds_tiles > lds_small ? lds_tiles : lds_small;
+  if (pipe) {
+    fn = pbits == 1 ? step_kernel_p_fn<1>(vsigns)
+         : pbits == 2 ? step_kernel_p_fn<2>(vsigns)
+         : pbits == 3 ? step_kernel_p_fn<3>(vsigns)
+                      : step_kernel_p_fn<4>(vsigns);
+  }
   if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds_use) != hipSuccess)
     return TQ_ERR_DEVICE;
   (void)hipGetLastError();  // a launch error is reported below, not an older one
-  if (all_small)
+  if (pipe) {
+    void* args[] = {&sa};
+    if (hipLaunchKernel(fn, dim3(grid), dim3(kStepNT * 64), args, lds_use, hs) != hipSuccess) return TQ_ERR_DEVICE;
+  } else if (all_small)
     hipLaunchKernelGGL((step_kernel<true, false>), dim3(grid), dim3(kStepNT * 64), lds_use, hs, sa);
   else if (h)
     hipLaunchKernelGGL((step_kernel<false, true>), dim3(grid), dim3(kStepNT * 64), lds_use, hs, sa);

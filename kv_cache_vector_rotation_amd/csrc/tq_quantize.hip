@@ -27,6 +27,7 @@
 #include "tq_internal.h"
 #include "tq_quantize_dev.h"
 #include "tq_quantize_t_dev.h"
+#include "tq_quantize_p_dev.h"
 #include "turboquant.h"
 
 namespace {
@@ -44,6 +45,12 @@ template <int KP, int NT>
 __global__ __launch_bounds__(NT * 64) void quantize_t_kernel(QArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   tqq::quantize_tiles_t<KP, NT>(a, blockIdx.x, gridDim.x, smem);
+}
+
+template <int MG, bool BLK, bool SIGNS>
+__global__ __launch_bounds__(tqq::LdsP::NT * 64) void quantize_p_kernel(QArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  tqq::quantize_tiles_p<MG, BLK, SIGNS>(a, blockIdx.x, gridDim.x, smem);
 }
 
 __global__ __launch_bounds__(tqq::kSmallThreads) void quantize_small_kernel(QArgs a) {
@@ -91,6 +98,41 @@ tq_status launch_quantize(const QArgs& a, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_DEVICE;
 }
 
+// The pipelined path: one resident workgroup round, as above.
+template <int MG, bool BLK, bool SIGNS>
+tq_status launch_quantize_p(const QArgs& a, hipStream_t stream) {
+  constexpr int lds = tqq::LdsP::bytes;
+  static_assert(lds <= 160 * 1024, "LDS budget");
+  const void* fn = reinterpret_cast<const void*>(&quantize_p_kernel<MG, BLK, SIGNS>);
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+    return TQ_ERR_DEVICE;
+  int dev = 0, n_cu = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n_cu = v;
+  }
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, tqq::LdsP::NT * 64, lds) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  const int64_t grid = a.n_tiles < (int64_t)per_cu * n_cu ? a.n_tiles : (int64_t)per_cu * n_cu;
+  (void)hipGetLastError();  // a launch error is reported below, not an older one
+  hipLaunchKernelGGL((quantize_p_kernel<MG, BLK, SIGNS>), dim3((unsigned)grid), dim3(tqq::LdsP::NT * 64), lds,
+                     stream, a);
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_DEVICE;
+}
+
+template <int MG>
+tq_status launch_quantize_p_fmt(const QArgs& a, hipStream_t stream) {
+  if (a.fmt == TQ_TOKEN_MAJOR) return launch_quantize_p<MG, false, true>(a, stream);
+  return a.mse_only ? launch_quantize_p<MG, true, false>(a, stream) : launch_quantize_p<MG, true, true>(a, stream);
+}
+
+// (p_path_ok) token-major records with sign bits, or block records
+inline bool p_launchable(const QArgs& a) {
+  return tqq::p_path_ok(a) && (a.fmt == TQ_BLOCK32 || !a.mse_only);
+}
+
 }  // namespace
 
 extern "C" tq_status tq_quantize(const tq_quantizer* qz, tq_format fmt, const void* x,
@@ -103,6 +145,14 @@ extern "C" tq_status tq_quantize(const tq_quantizer* qz, tq_format fmt, const vo
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   // a few vectors (an append): one workgroup per vector, for latency
   if (tqq::small_path_ok(a)) return launch_quantize_small(a, s);
+  if (p_launchable(a)) {
+    switch (a.gbits[0]) {
+      case 1: return launch_quantize_p_fmt<1>(a, s);
+      case 2: return launch_quantize_p_fmt<2>(a, s);
+      case 3: return launch_quantize_p_fmt<3>(a, s);
+      default: return launch_quantize_p_fmt<4>(a, s);
+    }
+  }
   const bool h = tqq::h_path_ok(a), t = tqq::t_path_ok(a);
   switch (tqq::quantize_kp(a.d)) {
     case 64:

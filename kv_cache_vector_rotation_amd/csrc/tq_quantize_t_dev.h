@@ -215,6 +215,193 @@ __device__ __forceinline__ void octet_or_words(const int (&idx)[4], int s, uint3
 }
 
 
+// This wave's rows of rot (three bf16 parts) and sketch_rot (row-scaled,
+// two fp16 parts), lane (ln, lg) holding M[16 w + ln][32 s + 8 lg + j]
+// (rows and columns past d are zero).
+template <int KS>
+__device__ __forceinline__ void t_matrix_regs(const QArgs& a, int w, int ln, int lg, u32x4 (&rh)[KS], u32x4 (&rm)[KS],
+                                              u32x4 (&rl3)[KS], u32x4 (&sh)[KS], u32x4 (&sl)[KS]) {
+  const int d = a.d;
+  const int orow = 16 * w + ln;
+  const bool row_ok = orow < d;
+  const int64_t rb = (int64_t)(row_ok ? orow : d - 1) * d;
+  f32x4 mr[KS][2], ms[KS][2];
+#pragma unroll
+  for (int s2 = 0; s2 < KS; ++s2)
+#pragma unroll
+    for (int hlf = 0; hlf < 2; ++hlf) {
+      // (d is a multiple of 8: a lane's 8 entries are all inside the row or all past it)
+      const int k = 32 * s2 + 8 * lg + 4 * hlf;
+      const int kc = k < d ? k : 0;
+      mr[s2][hlf] = *reinterpret_cast<const f32x4*>(a.rot + rb + kc);
+      ms[s2][hlf] = *reinterpret_cast<const f32x4*>(a.skr + rb + kc);
+      if (!row_ok || 32 * s2 + 8 * lg >= d) {
+        mr[s2][hlf] = f32x4{0.f, 0.f, 0.f, 0.f};
+        ms[s2][hlf] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  float mx = 0.f;
+#pragma unroll
+  for (int s2 = 0; s2 < KS; ++s2)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(ms[s2][e / 4][e % 4]));
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  const float ssc = mx > 0.f ? __builtin_amdgcn_ldexpf(1.0f, 14 - __builtin_amdgcn_frexp_expf(mx)) : 1.0f;
+#pragma unroll
+  for (int s2 = 0; s2 < KS; ++s2) {
+    uint32_t wh[4], wm[4], wl[4], vh[4], vl[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint32_t h2[2], m2[2], l2[2];
+      f16x2 sh2, sl2;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float v = mr[s2][p / 2][2 * (p % 2) + e];
+        h2[e] = bf16_rne(v);
+        const float r1 = v - bf16_val(h2[e]);
+        m2[e] = bf16_rne(r1);
+        l2[e] = bf16_rne(r1 - bf16_val(m2[e]));
+        const float u = ms[s2][p / 2][2 * (p % 2) + e] * ssc;
+        const _Float16 uh = (_Float16)u;
+        sh2[e] = uh;
+        sl2[e] = (_Float16)(u - (float)uh);
+      }
+      wh[p] = h2[0] | (h2[1] << 16);
+      wm[p] = m2[0] | (m2[1] << 16);
+      wl[p] = l2[0] | (l2[1] << 16);
+      vh[p] = __builtin_bit_cast(uint32_t, sh2);
+      vl[p] = __builtin_bit_cast(uint32_t, sl2);
+    }
+    rh[s2] = u32x4{wh[0], wh[1], wh[2], wh[3]};
+    rm[s2] = u32x4{wm[0], wm[1], wm[2], wm[3]};
+    rl3[s2] = u32x4{wl[0], wl[1], wl[2], wl[3]};
+    sh[s2] = u32x4{vh[0], vh[1], vh[2], vh[3]};
+    sl[s2] = u32x4{vl[0], vl[1], vl[2], vl[3]};
+  }
+}
+
+// Destination row of vector tid (< QT) of a token-major tile (-1: past the
+// tile or outside the cache), stored to rows[tid].
+__device__ __forceinline__ void t_tile_rows(const QArgs& a, const TileGeo& cg, int tid, int64_t* rows) {
+  // destination rows: vector v0 + t of the call (segments of seg_len rows)
+  int64_t row = -1;
+  if (tid < cg.nvalid) {
+    if (a.dst_rows) {
+      row = a.dst_rows[cg.v0 + tid];
+    } else {
+      const int64_t q0 = cg.v0 / a.seg_len, r0 = cg.v0 - q0 * a.seg_len;  // (uniform)
+      int64_t q = q0, r = r0 + tid;
+      if (a.seg_len >= QT) {
+        if (r >= a.seg_len) {
+          q += 1;
+          r -= a.seg_len;
+        }
+      } else {
+        const uint32_t sl = (uint32_t)a.seg_len, rr32 = (uint32_t)r, dq = rr32 / sl;
+        q += dq;
+        r = rr32 - dq * sl;
+      }
+      row = q * a.seg_stride + a.seg_offset + r;
+    }
+    if (row < 0 || row >= a.n_rows) row = -1;
+  }
+  rows[tid] = row;
+}
+
+// Store phase of a tile: the norms of its vectors (n_g staged in nrmv
+// [group][QT], gamma_g from the per-wave residual sums gpart [wave][QT]),
+// then the staged records pk (token-major rows of PKW words at the
+// destination rows `rows`; block records: the two blocks' words, with
+// per-word masks for partial blocks).
+template <int KP, int NT, bool BLK>
+__device__ __forceinline__ void t_store_tile(const QArgs& a, const TileGeo& cg, const int64_t* rows,
+                                             const float* nrmv, const float* gpart, const uint32_t* pk,
+                                             bool partial, bool vec_out, int tid) {
+  using L = LdsT<KP, NT>;
+  constexpr int PKW = L::PKW;
+  constexpr int BKW = L::BKW;
+  constexpr bool tok = !BLK;
+  const int bcw = a.blk_code_words, bsw = a.blk_sign_words;
+  const bool signs_on = !a.mse_only;
+  if (tid < QT * a.n_groups) {
+    const int gg = tid / QT, v = tid % QT;
+    int64_t row = -1;
+    if (tok)
+      row = rows[v];
+    else if (v >= cg.slot_lo && v < cg.slot_lo + cg.nvalid)
+      row = cg.rowbase + v;
+    if (row >= 0) {
+      const int w0 = a.choff[gg] / 16, w1 = (a.choff[gg] + a.gdim[gg] + 15) / 16;
+      float s = 0.f;
+      for (int ww = w0; ww < w1; ++ww) s += gpart[ww * QT + v];
+      store_norms(a.norms, a.norm_f16, row * a.n_groups + gg, nrmv[gg * QT + v], sqrtf(s));
+    }
+  }
+  if (tok) {
+    const int cw = a.code_words, sw = a.sign_words;
+    if (vec_out) {
+      // 8 threads per row: 16-byte chunks, the row's code chunks then its sign chunks
+      const int v = tid >> 3, c = tid & 7, cc = cw / 4, sc4 = sw / 4;
+      for (int vv = v; vv < cg.nvalid; vv += NT * 8) {
+        const int64_t row = rows[vv];
+        if (row < 0 || c >= cc + sc4) continue;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(pk + vv * PKW + 4 * c);
+        if (c < cc)
+          *reinterpret_cast<u32x4*>(a.codes + row * cw + 4 * c) = val;
+        else
+          *reinterpret_cast<u32x4*>(a.signs + row * sw + 4 * (c - cc)) = val;
+      }
+    } else {
+      // 16 threads per row, word by word
+      const int rw = cw + sw;
+      for (int v = tid >> 4; v < cg.nvalid; v += NT * 4) {
+        const int64_t row = rows[v];
+        if (row < 0) continue;
+        for (int wd = tid & 15; wd < rw; wd += 16) {
+          const uint32_t val = pk[v * PKW + wd];
+          if (wd < cw)
+            a.codes[row * cw + wd] = val;
+          else
+            a.signs[row * sw + wd - cw] = val;
+        }
+      }
+    }
+  } else {
+    const int nw = bcw + (signs_on ? bsw : 0);
+    if (!partial && vec_out) {
+      // both blocks whole: 16-byte chunks
+      const int nc = nw / 4;
+      for (int e = tid; e < 2 * nc; e += NT * 64) {
+        const int h = e >= nc ? 1 : 0, c = e - h * nc;
+        const int64_t blkrow = cg.rowbase / 32 + h;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(pk + h * BKW + 4 * c);
+        uint32_t* dst = 4 * c < bcw ? a.codes + blkrow * bcw + 4 * c : a.signs + blkrow * bsw + (4 * c - bcw);
+        *reinterpret_cast<u32x4*>(dst) = val;
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int vlo = cg.slot_lo > 32 * h ? cg.slot_lo : 32 * h;
+        const int vhi = cg.slot_lo + cg.nvalid < 32 * h + 32 ? cg.slot_lo + cg.nvalid : 32 * h + 32;
+        if (vhi <= vlo) continue;
+        const int64_t blkrow = cg.rowbase / 32 + h;
+        for (int wd = tid; wd < nw; wd += NT * 64) {
+          const uint32_t val = pk[h * BKW + wd];
+          uint32_t* dst = wd < bcw ? a.codes + blkrow * bcw + wd : a.signs + blkrow * bsw + (wd - bcw);
+          const uint32_t m = partial ? pk[(2 + h) * BKW + wd] : 0xFFFFFFFFu;
+          if (m == 0xFFFFFFFFu) {
+            *dst = val;
+          } else if (m != 0u) {
+            atomicAnd(dst, ~m);
+            atomicOr(dst, val & m);
+          }
+        }
+      }
+    }
+  }
+}
+
 // The kernel body: this workgroup quantizes tiles first_tile,
 // first_tile + tile_stride, ... of `a` (t_path_ok), with NT * 64 threads and
 // the dynamic LDS block `smem` (LdsT<KP, NT>::bytes).
@@ -257,68 +444,9 @@ __device__ __forceinline__ void quantize_tiles_t_fmt(const QArgs& a, int64_t fir
   TStage st;
   if (tile < a.n_tiles) load_t<KP, NT>(a, g, blk, tid, st);
 
-  // This wave's rows of rot (three bf16 parts) and sketch_rot (row-scaled,
-  // two fp16 parts), lane (ln, lg) holding M[16 w + ln][32 s + 8 lg + j].
+  // this wave's matrix rows
   u32x4 rh[KS], rm[KS], rl3[KS], sh[KS], sl[KS];
-  {
-    const int orow = 16 * w + ln;
-    const bool row_ok = orow < d;
-    const int64_t rb = (int64_t)(row_ok ? orow : d - 1) * d;
-    f32x4 mr[KS][2], ms[KS][2];
-#pragma unroll
-    for (int s2 = 0; s2 < KS; ++s2)
-#pragma unroll
-      for (int hlf = 0; hlf < 2; ++hlf) {
-        // (d is a multiple of 8: a lane's 8 entries are all inside the row or all past it)
-        const int k = 32 * s2 + 8 * lg + 4 * hlf;
-        const int kc = k < d ? k : 0;
-        mr[s2][hlf] = *reinterpret_cast<const f32x4*>(a.rot + rb + kc);
-        ms[s2][hlf] = *reinterpret_cast<const f32x4*>(a.skr + rb + kc);
-        if (!row_ok || 32 * s2 + 8 * lg >= d) {
-          mr[s2][hlf] = f32x4{0.f, 0.f, 0.f, 0.f};
-          ms[s2][hlf] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-      }
-    float mx = 0.f;
-#pragma unroll
-    for (int s2 = 0; s2 < KS; ++s2)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(ms[s2][e / 4][e % 4]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float ssc = mx > 0.f ? __builtin_amdgcn_ldexpf(1.0f, 14 - __builtin_amdgcn_frexp_expf(mx)) : 1.0f;
-#pragma unroll
-    for (int s2 = 0; s2 < KS; ++s2) {
-      uint32_t wh[4], wm[4], wl[4], vh[4], vl[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        uint32_t h2[2], m2[2], l2[2];
-        f16x2 sh2, sl2;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const float v = mr[s2][p / 2][2 * (p % 2) + e];
-          h2[e] = bf16_rne(v);
-          const float r1 = v - bf16_val(h2[e]);
-          m2[e] = bf16_rne(r1);
-          l2[e] = bf16_rne(r1 - bf16_val(m2[e]));
-          const float u = ms[s2][p / 2][2 * (p % 2) + e] * ssc;
-          const _Float16 uh = (_Float16)u;
-          sh2[e] = uh;
-          sl2[e] = (_Float16)(u - (float)uh);
-        }
-        wh[p] = h2[0] | (h2[1] << 16);
-        wm[p] = m2[0] | (m2[1] << 16);
-        wl[p] = l2[0] | (l2[1] << 16);
-        vh[p] = __builtin_bit_cast(uint32_t, sh2);
-        vl[p] = __builtin_bit_cast(uint32_t, sl2);
-      }
-      rh[s2] = u32x4{wh[0], wh[1], wh[2], wh[3]};
-      rm[s2] = u32x4{wm[0], wm[1], wm[2], wm[3]};
-      rl3[s2] = u32x4{wl[0], wl[1], wl[2], wl[3]};
-      sh[s2] = u32x4{vh[0], vh[1], vh[2], vh[3]};
-      sl[s2] = u32x4{vl[0], vl[1], vl[2], vl[3]};
-    }
-  }
+  t_matrix_regs<KS>(a, w, ln, lg, rh, rm, rl3, sh, sl);
 
   // wave-uniform group parameters (group boundaries are multiples of 16)
   const int grp = (a.n_groups > 1 && w * 16 >= a.choff[1]) ? 1 : 0;
@@ -384,31 +512,7 @@ __device__ __forceinline__ void quantize_tiles_t_fmt(const QArgs& a, int64_t fir
     if (tile < a.n_tiles) load_t<KP, NT>(a, g, blk, tid, st);
     if (tok && a.pk_zero)
       for (int e = tid; e < QT * PKW; e += NT * 64) pk[e] = 0u;
-    if (tok && tid < QT) {
-      // destination rows: vector v0 + t of the call (segments of seg_len rows)
-      int64_t row = -1;
-      if (tid < cg.nvalid) {
-        if (a.dst_rows) {
-          row = a.dst_rows[cg.v0 + tid];
-        } else {
-          const int64_t q0 = cg.v0 / a.seg_len, r0 = cg.v0 - q0 * a.seg_len;  // (uniform)
-          int64_t q = q0, r = r0 + tid;
-          if (a.seg_len >= QT) {
-            if (r >= a.seg_len) {
-              q += 1;
-              r -= a.seg_len;
-            }
-          } else {
-            const uint32_t sl = (uint32_t)a.seg_len, rr32 = (uint32_t)r, dq = rr32 / sl;
-            q += dq;
-            r = rr32 - dq * sl;
-          }
-          row = q * a.seg_stride + a.seg_offset + r;
-        }
-        if (row < 0 || row >= a.n_rows) row = -1;
-      }
-      rows[tid] = row;
-    }
+    if (tok && tid < QT) t_tile_rows(a, cg, tid, rows);
 
     // ---- y = rot x ----
     // (a token-major tile of at most 16 vectors runs its first 16-vector
@@ -618,82 +722,7 @@ __device__ __forceinline__ void quantize_tiles_t_fmt(const QArgs& a, int64_t fir
     __syncthreads();  // (5)
 
     // ---- store: norms, then the records ----
-    if (tid < QT * a.n_groups) {
-      const int gg = tid / QT, v = tid % QT;
-      int64_t row = -1;
-      if (tok)
-        row = rows[v];
-      else if (v >= cg.slot_lo && v < cg.slot_lo + cg.nvalid)
-        row = cg.rowbase + v;
-      if (row >= 0) {
-        const int w0 = a.choff[gg] / 16, w1 = (a.choff[gg] + a.gdim[gg] + 15) / 16;
-        float s = 0.f;
-        for (int ww = w0; ww < w1; ++ww) s += gpart[ww * QT + v];
-        store_norms(a.norms, a.norm_f16, row * a.n_groups + gg, nrmv[gg * QT + v], sqrtf(s));
-      }
-    }
-    if (tok) {
-      const int cw = a.code_words, sw = a.sign_words;
-      if (vec_out) {
-        // 8 threads per row: 16-byte chunks, the row's code chunks then its sign chunks
-        const int v = tid >> 3, c = tid & 7, cc = cw / 4, sc4 = sw / 4;
-        for (int vv = v; vv < cg.nvalid; vv += NT * 8) {
-          const int64_t row = rows[vv];
-          if (row < 0 || c >= cc + sc4) continue;
-          const u32x4 val = *reinterpret_cast<const u32x4*>(pk + vv * PKW + 4 * c);
-          if (c < cc)
-            *reinterpret_cast<u32x4*>(a.codes + row * cw + 4 * c) = val;
-          else
-            *reinterpret_cast<u32x4*>(a.signs + row * sw + 4 * (c - cc)) = val;
-        }
-      } else {
-        // 16 threads per row, word by word
-        const int rw = cw + sw;
-        for (int v = tid >> 4; v < cg.nvalid; v += NT * 4) {
-          const int64_t row = rows[v];
-          if (row < 0) continue;
-          for (int wd = tid & 15; wd < rw; wd += 16) {
-            const uint32_t val = pk[v * PKW + wd];
-            if (wd < cw)
-              a.codes[row * cw + wd] = val;
-            else
-              a.signs[row * sw + wd - cw] = val;
-          }
-        }
-      }
-    } else {
-      const int nw = bcw + (signs_on ? bsw : 0);
-      if (!partial && vec_out) {
-        // both blocks whole: 16-byte chunks
-        const int nc = nw / 4;
-        for (int e = tid; e < 2 * nc; e += NT * 64) {
-          const int h = e >= nc ? 1 : 0, c = e - h * nc;
-          const int64_t blkrow = cg.rowbase / 32 + h;
-          const u32x4 val = *reinterpret_cast<const u32x4*>(pk + h * BKW + 4 * c);
-          uint32_t* dst = 4 * c < bcw ? a.codes + blkrow * bcw + 4 * c : a.signs + blkrow * bsw + (4 * c - bcw);
-          *reinterpret_cast<u32x4*>(dst) = val;
-        }
-      } else {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int vlo = cg.slot_lo > 32 * h ? cg.slot_lo : 32 * h;
-          const int vhi = cg.slot_lo + cg.nvalid < 32 * h + 32 ? cg.slot_lo + cg.nvalid : 32 * h + 32;
-          if (vhi <= vlo) continue;
-          const int64_t blkrow = cg.rowbase / 32 + h;
-          for (int wd = tid; wd < nw; wd += NT * 64) {
-            const uint32_t val = pk[h * BKW + wd];
-            uint32_t* dst = wd < bcw ? a.codes + blkrow * bcw + wd : a.signs + blkrow * bsw + (wd - bcw);
-            const uint32_t m = partial ? pk[(2 + h) * BKW + wd] : 0xFFFFFFFFu;
-            if (m == 0xFFFFFFFFu) {
-              *dst = val;
-            } else if (m != 0u) {
-              atomicAnd(dst, ~m);
-              atomicOr(dst, val & m);
-            }
-          }
-        }
-      }
-    }
+    t_store_tile<KP, NT, BLK>(a, cg, rows, nrmv, gpart, pk, partial, vec_out, tid);
   }
 }
 

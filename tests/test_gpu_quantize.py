@@ -122,6 +122,45 @@ def test_tile_path_input_scale(tq, scale_exp):
         _check(tq, spec, x, fmt, 704, np.arange(700), dtype="bf16", seg=(700, 704, 0), pass_rows=False)
 
 
+# d = 128 with one group (bf16, at least one 64-vector tile) takes the
+# pipelined tile path, whose workgroups keep three tiles in flight: enough
+# vectors that every workgroup runs several tiles (more than 3 x 256), a
+# ragged last tile, segments whose block pairs are partly covered, every code
+# width, both formats, and MSE-only block records.
+@pytest.mark.parametrize("m", [1, 2, 3, 4])
+@pytest.mark.parametrize("fmt_name,mse_only", [("TQ_TOKEN_MAJOR", False), ("TQ_BLOCK32", False),
+                                                ("TQ_BLOCK32", True)])
+def test_pipelined_path_many_tiles_per_workgroup(tq, m, fmt_name, mse_only):
+    import torch
+    wl = synth.workload("llama8b_decode", groups=((128, m),))
+    spec = synth.draw_quantizer(wl, "V")
+    seg_len, cap, offset = 4100, 4224, 29
+    n_vec = 64 * 256 * 3 + 64 * 40 + 37
+    n_seg = (n_vec + seg_len - 1) // seg_len
+    x = np.concatenate([synth.draw_kv_slab(wl, "V", 0, h, 0, seg_len) for h in range(n_seg)])[:n_vec]
+    x[5] = 0.0  # a zero vector
+    i = np.arange(n_vec)
+    rows = (i // seg_len) * cap + offset + i % seg_len
+    oq, dq = gc.quantizers(spec, mse_only=mse_only)
+    fmt = getattr(tq, fmt_name)
+    cache = tq.Cache.empty(dq, n_seg * cap, fmt)
+    cache.codes.fill_(-1)
+    if cache.signs is not None and cache.signs.numel():
+        cache.signs.fill_(-1)
+    xt = torch.from_numpy(np.ascontiguousarray(x)).cuda().to(torch.bfloat16)
+    tq.tq_quantize(dq, fmt, xt, cache, seg_len=seg_len, seg_stride=cap, seg_offset=offset)
+    torch.cuda.synchronize()
+    qv = oracle.quantize(x.astype(np.float64), oq)
+    got_all = gc.read_cache(cache, dq)
+    gc.compare_records(x.astype(np.float64), oq, qv, gc.select_rows(got_all, rows))
+    # rows outside the segments keep every bit (block records share words
+    # with them)
+    untouched = np.setdiff1d(np.arange(n_seg * cap), rows)
+    assert np.all(got_all[0][0][untouched] == 2 ** m - 1)
+    if not mse_only:
+        assert np.all(got_all[1][0][untouched])
+
+
 @pytest.mark.parametrize("seg_len,offset,n_vec", [(1000, 5, 2000), (777, 37, 777), (600, 32, 1800), (520, 63, 1040)])
 def test_tile_path_block_segments_partial_pairs(tq, seg_len, offset, n_vec):
     # block records by segments whose first and last 64-row block pairs are
