@@ -282,8 +282,8 @@ tq_status tq_attn_decode_workspace_bytes(const tq_quantizer* kq, const tq_quanti
  * The estimate is evaluated in factored form: scale * sum_g (n_g <rot q,
  * c[idx]>_g + alpha_g gamma_g <sketch q, z>_g); V is accumulated in the
  * rotated and sketch domains and mapped back once per head with rot^T and
- * sketch^T. Operand precision: fp16 products, fp32 accumulation (queries
- * as an fp16 hi/lo pair; K centroids tabulated as fp16(s c) with a scale
+ * sketch^T. Operand precision: fp16 products, fp32 accumulation (the
+ * rotated and the sketched query each as an fp16 hi/lo pair; K centroids tabulated as fp16(s c) with a scale
  * s in [1, 2) chosen per codebook so that the rounding is far below fp16's
  * own, and 1/s applied with the norm); stored norms must be below 65504,
  * and scale * |rot q| below about 4.5e4.

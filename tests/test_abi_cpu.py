@@ -282,10 +282,11 @@ def test_search_validation(tq):
     db = _fake_cache(tq, 1000)
     need = C.c_size_t()
     assert lib.tq_search_workspace_bytes(C.byref(q), 1000, 50, 10, C.byref(need)) == 0
-    # prepared queries (50 x 3 x 200 fp16, rounded up to 256 B), the codebook
-    # scale (256 B) and two [50][slices][10] lists; 63 tiles of 16 rows give
-    # 16 slices of 4 tiles
-    qprep = (50 * 3 * 200 * 2 + 255) // 256 * 256
+    # prepared queries (50 x 4 x 200 fp16: the rotated and the sketched query,
+    # each as a high part and a scaled low part; rounded up to 256 B), the
+    # codebook scale (256 B) and two [50][slices][10] lists; 63 tiles of 16
+    # rows give 16 slices of 4 tiles
+    qprep = (50 * 4 * 200 * 2 + 255) // 256 * 256
     assert need.value == qprep + 256 + 2 * 50 * 16 * 10 * 4
     for args in ((0, 50, 10), (1000, 0, 10), (1000, 50, 0), (1000, 50, 11)):
         assert lib.tq_search_workspace_bytes(C.byref(q), *args, C.byref(need)) == tq.TQ_ERR_INVALID
@@ -320,7 +321,7 @@ def test_query_token_chunks_validation(tq):
     sT = tq.decode_shape(1, 8, 2, 1000, 1024, 0.088, n_split=4, n_q_tokens=16)
     assert lib.tq_attn_decode_workspace_bytes(C.byref(q), C.byref(q), C.byref(s1), C.byref(need1)) == 0
     assert lib.tq_attn_decode_workspace_bytes(C.byref(q), C.byref(q), C.byref(sT), C.byref(needT)) == 0
-    per_head = lambda heads: (heads * 3 * 128 * 2 + 255) // 256 * 256 + 256 + (heads * 4 * 258 * 4 + 255) // 256 * 256
+    per_head = lambda heads: (heads * 4 * 128 * 2 + 255) // 256 * 256 + 256 + (heads * 4 * 258 * 4 + 255) // 256 * 256
     assert need1.value == per_head(8) and needT.value == per_head(8 * 16)
     bad = tq.decode_shape(1, 8, 2, 10, 32, 0.088, n_q_tokens=11)
     assert lib.tq_attn_decode_workspace_bytes(C.byref(q), C.byref(q), C.byref(bad), C.byref(needT)) == \
