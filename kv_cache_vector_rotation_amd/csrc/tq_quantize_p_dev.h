@@ -14,11 +14,12 @@
 // is in the same step at once: its matrix-core products and its VALU work
 // (cells, residuals, packing) never overlap. Here a workgroup has three
 // tiles in flight and two phases per tile:
-//   X(k): the cells, residual, residual norm partials and codes of tile k,
-//         and the rotation of tile k + 1 with its per-wave sums of y^2;
-//   Y(k): the sketch of tile k's residual and its sign bits, the staging of
-//         tile k + 2's input into LDS (its loads were issued one phase Y
-//         earlier), and the stores of tile k - 1.
+//   X(k): the stores of tile k - 1, the cells, residual, residual norm
+//         partials and codes of tile k, and the rotation of tile k + 1 with
+//         its per-wave sums of y^2;
+//   Y(k): the sketch of tile k's residual and its sign bits, and the staging
+//         of tile k + 2's input into LDS (its loads were issued one phase Y
+//         earlier).
 // Tile k's norms are the sums of the per-wave partials written in X(k - 1).
 // What one phase writes and a later phase of another tile still reads (the
 // per-wave partials, norms, staged records, destination rows) is
@@ -262,6 +263,11 @@ __device__ __forceinline__ void quantize_tiles_p(const QArgs& a, int64_t first_t
         }
       }
     };
+    // tile k - 1's stores (its records were completed in Y(k - 1)), issued
+    // first so that their latency overlaps this phase's work
+    if (have_prev)
+      t_store_tile<KP, NT, BLK>(a, gp, rows + (1 - P) * QT, nrmv + (1 - P) * QT, gpart + (1 - P) * NT * QT,
+                                pk + (1 - P) * PKN, partial_prev, vec_out, tid);
     rotate(yn, 1 - P);
     cpart();
     __syncthreads();  // end of X(k)
@@ -273,8 +279,7 @@ __device__ __forceinline__ void quantize_tiles_p(const QArgs& a, int64_t first_t
     // (wave 1: wave 0 stores the norms below)
     if (tok && tid >= QT && tid < 2 * QT) t_tile_rows(a, g0, tid - QT, rows + P * QT);
     const bool partial = BLK && (g0.slot_lo > 0 || g0.slot_lo + g0.nvalid < 64);
-    // tile k's sketch and sign bits (matrix cores, then VALU), then tile
-    // k - 1's stores
+    // tile k's sketch and sign bits (matrix cores, then VALU)
     auto spart = [&]() __attribute__((always_inline)) {
       if constexpr (SIGNS) {
         f32x4 sacc[4];
@@ -329,13 +334,7 @@ __device__ __forceinline__ void quantize_tiles_p(const QArgs& a, int64_t first_t
         }
       }
     };
-    auto wpart = [&]() __attribute__((always_inline)) {
-      if (have_prev)
-        t_store_tile<KP, NT, BLK>(a, gp, rows + (1 - P) * QT, nrmv + (1 - P) * QT, gpart + (1 - P) * NT * QT,
-                                  pk + (1 - P) * PKN, partial_prev, vec_out, tid);
-    };
     spart();
-    wpart();
     __syncthreads();  // end of Y(k)
     if (t1 >= n_tiles) {
       // the workgroup's last tile: its stores
