@@ -542,9 +542,22 @@ def chunk_bench(tq, torch, T=64):
     rb = record_bytes([g for g, _ in wl.groups], [m for _, m in wl.groups])
     copies = max(1, math.ceil((1 << 30) / (wl.batch * wl.n_kv_heads * wl.capacity * 2 * rb)))
     us = compressed_step_us(tq, torch, wl, kq, vq, copies, T=T)
+    # the split-K pass decodes each 32-token tile once per workgroup and runs
+    # 16-column blocks of the G T columns of a KV head on it: per (tile,
+    # block) three K products (q_rot hi, q_rot lo, q_sk) of 32 x 128 x 16 and
+    # two V products (codes, signs) of 128 x 32 x 16
+    cache_bytes = wl.batch * wl.n_kv_heads * wl.n_ctx * 2 * rb
+    cols = wl.n_q_heads // wl.n_kv_heads * T
+    flop = wl.batch * wl.n_kv_heads * (wl.n_ctx // 32) * (cols // 16) * 2 * 16 * 32 * wl.d * (3 + 2)
     return {"workload": "llama8b_decode", "query_tokens_per_head": T, "n_ctx": wl.n_ctx,
             "us_per_chunk": round(us, 2), "query_tokens_per_s": wl.batch * T / (us / 1e6),
-            "cache_copies": copies}
+            "cache_copies": copies, "split_kernel": "chunk_kernel (each tile decoded once per workgroup)",
+            "cache_bytes_read": cache_bytes, "hbm_gbs": round(cache_bytes / us / 1e3, 1),
+            "hbm_frac": round(cache_bytes / us / 1e3 / PEAK_HBM_GBS, 4),
+            "mfma_issued_tflops": round(flop / us / 1e6, 1), "mfma_peak_tflops": PEAK_FP16_MFMA_TFLOPS,
+            "mfma_frac": round(flop / us / 1e6 / PEAK_FP16_MFMA_TFLOPS, 4),
+            "bound": "per-column logit, softmax and V work with two waves per SIMD (neither HBM nor the "
+                     "matrix cores near their peaks); times are of the whole chunk step"}
 
 
 def paged_bench(tq, torch, n_copies=8, reps=20):
