@@ -9,11 +9,15 @@
 //
 // Three kernels on the caller's stream:
 //  1. prep:    q_rot = rot q and q_sk = sketch q per query head (fp32 sums;
-//              q_rot stored as an fp16 hi/lo pair, q_sk as fp16), both
-//              scaled by scale * log2(e) and q_sk also by alpha_g.
+//              each stored as an fp16 hi/lo pair), both scaled by
+//              scale * log2(e) and q_sk also by alpha_g.
 //  2. split:   split-K over the context. A workgroup takes one (batch, KV
 //              head, block of query heads) and a range of 32-token tiles;
-//              its four waves take alternate tiles. Per tile a wave
+//              its waves take alternate tiles. Three kernels share this
+//              structure: the byte-table kernel (one group of code width
+//              1, 2 or 4, d = 128; 8 waves), the general kernel below (4
+//              waves; described here) and the chunk kernel for many query
+//              columns per KV head. Per tile a wave of the general kernel
 //              - expands the K codes through an LDS table of pairs of fp16
 //                scaled centroids fp16(s c) (one scale s per codebook, its
 //                1/s applied with the token's norm) and the K sign bits
@@ -33,6 +37,9 @@
 //              is exactly the operand layout the V product needs, so the
 //              softmax weights never leave registers. The four waves merge
 //              through LDS into one partial (max, sum, accumulators).
+//              In the packed mode (at most 4 query heads per KV head) the
+//              softmax weights, like the queries, are an fp16 part and its
+//              remainder; the 16-head mode takes plain fp16 weights.
 //  3. combine: log-sum-exp merge of the splits, then out = (rot^T acc_rot +
 //              sketch^T (alpha_g acc_sk)) / sum: the back-transform runs once
 //              per head, which is valid because dequantization is linear.
