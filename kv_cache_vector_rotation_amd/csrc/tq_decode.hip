@@ -953,7 +953,8 @@ __global__ __launch_bounds__(256, TQ_PK_MINB) void decode_kernel(DArgs a) {
 
 // ---------------------------------------------------------------------------
 // Byte-table split-K kernel: one quantizer group whose code width m divides
-// 8 (m = 1, 2, 4), d = 128. One 512-thread workgroup per compute unit holds
+// 8 (m = 1, 2, 4), d = 128. One workgroup per compute unit (12 waves for
+// m <= 2, 8 for m = 4, whose wider code words would spill at 12) holds
 // two 64 KB LDS tables of 256 rows x 256 bytes, indexed by one byte of a
 // record:
 //   code table  row e: the 8 / m fp16 scaled centroids fp16(s c[code]) of
@@ -972,10 +973,11 @@ __global__ __launch_bounds__(256, TQ_PK_MINB) void decode_kernel(DArgs a) {
 // Column packing of the 16 MFMA columns:
 //   HB = 8 (KV groups of more than 4 query heads, in blocks of 8 heads):
 //     K codes x [q_rot hi | q_rot lo * 2^11] (8 heads each), K signs x
-//     [q_sk | q_sk]; V codes x [w_n hi | w_n lo * 2^11] and V signs x
-//     [w_g | w_g], with w_n = p n and w_g = p gamma the softmax weights
-//     times the token's norms; w_n is split into an fp16 part and its
-//     remainder so that it keeps about 21 bits, w_g is plain fp16;
+//     [q_sk | q_sk]; V codes x [w_n | 0] and V signs x [0 | w_g] into one
+//     accumulator set, with w_n = p n and w_g = p gamma the softmax weights
+//     times the token's norms, both plain fp16 (relative rounding 2^-11 per
+//     weight; a hi / lo split of w_n took 32 more accumulator registers,
+//     which kept the kernel at 8 waves);
 //   HB = 4 (at most 4 query heads per KV head): column 4 h + r, role r =
 //     0 q_rot hi / w_n hi, 1 q_rot lo / w_n lo, 2 q_sk / w_g hi, 3 - / w_g lo;
 //     codes and signs accumulate into the same accumulator (their B columns
@@ -986,15 +988,20 @@ __global__ __launch_bounds__(256, TQ_PK_MINB) void decode_kernel(DArgs a) {
 #ifndef TQ_BYTE_NBUF
 #define TQ_BYTE_NBUF 2
 #endif
-constexpr int kBW = 8;                       // waves per workgroup (a multiple of 4)
-constexpr int kBThreads = 64 * kBW;
+// waves per workgroup for code width m (a multiple of 4)
+constexpr int byte_waves(int m) { return m == 4 ? 8 : 12; }
 constexpr uint32_t kBSignBase = 1u << 16;    // LDS byte offset of the sign table
 constexpr int kBTabBytes = 2 << 16;          // both tables
-constexpr int kBMerge = 4 * 2 * (128 * 16 + 64) * 4;  // merge regions (reuse the table space)
-constexpr int kBNrm = kBTabBytes;                     // per-wave norm staging [kBW][2][64] floats
-constexpr int kBMisc = kBNrm + kBW * 2 * 64 * 4;      // s_m, s_lw [kBW][8] floats, centroids [2][16]
-constexpr int kBLds = kBMisc + (2 * kBW * 8 + 32) * 4;
+constexpr int kBMerge = 4 * (128 * 16 + 64) * 4;  // merge regions (reuse the table space)
 static_assert(kBMerge <= kBTabBytes, "merge regions fit in the table space");
+// LDS layout past the tables for BW waves: per-wave norm staging [BW][2][64]
+// floats, then s_m, s_lw [BW][8] floats and the centroids [2][16]
+template <int BW>
+struct BLds {
+  static constexpr int nrm = kBTabBytes;
+  static constexpr int misc = nrm + BW * 2 * 64 * 4;
+  static constexpr int bytes = misc + (2 * BW * 8 + 32) * 4;
+};
 
 template <int M>
 struct BTab {
@@ -1055,15 +1062,17 @@ struct BRaw {
 };
 
 template <int M, int WV, int HB>
-__global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
+__global__ __launch_bounds__(64 * byte_waves(M), 1) void decode_byte_kernel(DArgs a) {
   using BT = BTab<M>;
   constexpr int D = 128, NC = 4, NMT = 8;
   constexpr bool P8 = HB == 8;
+  constexpr int kBW = byte_waves(M), kBThreads = 64 * kBW;
+  using BL = BLds<kBW>;
   // (the kernel has no static LDS: the dynamic area starts at LDS address 0,
   // so the table addresses formed in registers are used as they are)
   extern __shared__ __align__(16) unsigned char lds[];
-  float* s_nrm = reinterpret_cast<float*>(lds + kBNrm);
-  float* s_m = reinterpret_cast<float*>(lds + kBMisc);
+  float* s_nrm = reinterpret_cast<float*>(lds + BL::nrm);
+  float* s_m = reinterpret_cast<float*>(lds + BL::misc);
   float* s_lw = s_m + kBW * 8;
   float* s_cent = s_lw + kBW * 8;  // [0, 16) K, [16, 32) V
 
@@ -1194,9 +1203,8 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
   // logit combine factors (P8): hi + 2^-11 lo from this lane's value v and
   // its partner's o (lane ln ^ 8): fma(ca, o, cb v)
   const float ca = role ? 1.0f : kLoInv, cb = role ? kLoInv : 1.0f;
-  // weight split factors of this lane's column (the code-part weights p n
-  // always; P8 gives the sign-part weights p gamma in plain fp16)
-  const bool wlo = P8 ? role != 0 : (role & 1) != 0;
+  // weight split factors of this lane's column (HB = 4: remainder columns)
+  const bool wlo = (role & 1) != 0;
   const float bsel = wlo ? 2048.0f : 0.0f, csel = wlo ? -2048.0f : 1.0f;
 
   // ---- the first NB - 1 tiles in flight while the tables are built ----
@@ -1263,11 +1271,9 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
   float* nrm_k = s_nrm + wv * 128;
   float* nrm_v = nrm_k + 64;
   constexpr int NVA = WV ? NMT : 1;
-  f32x4 avr[NVA], avs[WV && P8 ? NMT : 1];
+  f32x4 avr[NVA];
 #pragma unroll
   for (int v = 0; v < NVA; ++v) avr[v] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int v = 0; v < (WV && P8 ? NMT : 1); ++v) avs[v] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // K part of a tile: logits, online softmax, and the V weight operands
   // (bvc: code product, bvs: sign product) of its tokens.
@@ -1350,10 +1356,6 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
         l_run *= corr;
 #pragma unroll
         for (int v = 0; v < NMT; ++v) avr[v] *= corr;
-        if constexpr (P8) {
-#pragma unroll
-          for (int v = 0; v < NMT; ++v) avs[v] *= corr;
-        }
         m_run = m_new;
       }
       // (m_run is -inf only while every token seen is masked: then p = 0)
@@ -1368,12 +1370,18 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
       float vn[8][2];
       load_norms<1>(nrm_v + 16 * lg, vn);
       if constexpr (P8) {
+        // columns h: w_n = p n (code product), columns h + 8: w_g = p gamma
+        // (sign product), plain fp16, one accumulator set
+        u32x4 w;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int j0 = 2 * q, j1 = 2 * q + 1;
-          bvc[q] = h2bits(wsplit(p[j0] * vn[j0][0], bsel, csel), wsplit(p[j1] * vn[j1][0], bsel, csel));
-          bvs[q] = h2bits(p[j0] * vn[j0][1], p[j1] * vn[j1][1]);
+          const float n0 = role ? vn[j0][1] : vn[j0][0], n1 = role ? vn[j1][1] : vn[j1][0];
+          w[q] = h2bits(p[j0] * n0, p[j1] * n1);
         }
+        const u32x4 z{0, 0, 0, 0};
+        bvc = role ? z : w;
+        bvs = role ? w : z;
       } else {
         const bool gsel = role >= 2;
         u32x4 w;
@@ -1400,10 +1408,7 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
       avr[u] = mfma16(vc, bvc, avr[u]);
       if constexpr (WV == 1) {
         const u32x4 vs = bsigns8(r.vs, u, soff);
-        if constexpr (P8)
-          avs[u] = mfma16(vs, bvs, avs[u]);
-        else
-          avr[u] = mfma16(vs, bvs, avr[u]);
+        avr[u] = mfma16(vs, bvs, avr[u]);
       }
     }
   };
@@ -1437,13 +1442,12 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
   }
 
   if constexpr (WV != 0) {
-    // ---- merge the eight waves into one partial per head ----
-    // Region r (0..3) holds, per part (code / sign accumulator) and channel,
-    // the sum of the 16 columns of waves r, r + 4, ... scaled to the
-    // workgroup maximum:
-    // float (part, ch, col) at part (128 16 + 64) + 16 ch + col + 16 (ch / 32),
-    // so the 64 lanes of one store fall in 64 different banks.
-    constexpr int PS = 128 * 16 + 64, RS = 2 * PS;
+    // ---- merge the workgroup's waves into one partial per head ----
+    // Region r (0..3) holds, per channel, the sum of the 16 accumulator
+    // columns of waves r, r + 4, ... scaled to the workgroup maximum:
+    // float (ch, col) at 16 ch + col + 16 (ch / 32), so the 64 lanes of one
+    // store fall in 64 different banks.
+    constexpr int RS = 128 * 16 + 64;
     float* s_red = reinterpret_cast<float*>(lds);
     __syncthreads();  // tables are no longer read
     l_run = rows4_sum(l_run);
@@ -1464,10 +1468,8 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
           const int idx = 16 * ch + ln + 16 * (ch >> 5);
           if (add) {
             reg[idx] += avr[u][i] * e;
-            if constexpr (P8) reg[PS + idx] += avs[u][i] * e;
           } else {
             reg[idx] = avr[u][i] * e;
-            if constexpr (P8) reg[PS + idx] = avs[u][i] * e;
           }
         }
     };
@@ -1491,18 +1493,18 @@ __global__ __launch_bounds__(kBThreads, 1) void decode_byte_kernel(DArgs a) {
         val = k == 0 ? Mx : L;
       } else {
         const int pt = (k - 2) / D, ch = (k - 2) % D;
-        // columns of the leading and remainder parts (P8: the sign part's
-        // weights are plain fp16 in both halves; its leading column is read)
-        const int part = P8 ? pt : 0;
-        const int chi = P8 ? h : 4 * h + 2 * pt, clo = P8 ? h + 8 : 4 * h + 2 * pt + 1;
-        const int base = part * PS + 16 * ch + 16 * (ch >> 5);
+        // columns (P8: the code product in column h, the sign product in
+        // column h + 8, both plain; HB = 4: the leading and remainder
+        // columns of each part)
+        const int chi = P8 ? h + 8 * pt : 4 * h + 2 * pt, clo = P8 ? chi : 4 * h + 2 * pt + 1;
+        const int base = 16 * ch + 16 * (ch >> 5);
         float hi = 0.f, lo = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           hi += s_red[r * RS + base + chi];
           lo += s_red[r * RS + base + clo];
         }
-        val = (P8 && pt == 1) ? hi : fmaf(kLoInv, lo, hi);
+        val = P8 ? hi : fmaf(kLoInv, lo, hi);
         if (pt == 0) val *= vinv;
       }
       const int hq2 = kvh * a.group + hblk * HB + h;
@@ -2081,7 +2083,8 @@ DecodeCfg decode_cfg(const tq_layout& l, bool with_v, const tq_decode_shape* s) 
   }
   // one workgroup per compute unit; at least one tile per wave
   const int64_t n_tiles = (s->n_ctx + kTile - 1) / kTile;
-  int64_t max_split = (n_tiles + kBW - 1) / kBW;
+  const int bw = byte_waves(l.mse_bits[0]);
+  int64_t max_split = (n_tiles + bw - 1) / bw;
   if (max_split > kMaxSplit) max_split = kMaxSplit;
   if (max_split < 1) max_split = 1;
   if (s->n_split > 0) {
@@ -2103,11 +2106,12 @@ hipError_t launch_byte(const DArgs& a, int n_hblk, hipStream_t st) {
   // static LDS, so that its dynamic LDS starts at address 0
   hipFuncAttributes fa;
   if (hipFuncGetAttributes(&fa, fn) != hipSuccess || fa.sharedSizeBytes != 0) return hipErrorInvalidValue;
-  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kBLds) != hipSuccess)
+  constexpr int lds = BLds<byte_waves(M)>::bytes;
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
     return hipErrorInvalidValue;
   (void)hipGetLastError();  // a launch error is reported below, not an older one
   const dim3 grid((unsigned)a.n_split, (unsigned)(a.batch * a.hkv), (unsigned)n_hblk);
-  hipLaunchKernelGGL((decode_byte_kernel<M, WV, HB>), grid, dim3(kBThreads), kBLds, st, a);
+  hipLaunchKernelGGL((decode_byte_kernel<M, WV, HB>), grid, dim3(64 * byte_waves(M)), lds, st, a);
   return hipGetLastError();
 }
 
