@@ -158,6 +158,14 @@ __device__ __forceinline__ float rows4_max(float v) {
   const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
+// the same with IEEE maximum (v_maximum3_f32 on gfx950: no canonicalizing
+// moves); for values that are never NaN
+__device__ __forceinline__ float rows4_maximum(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 __device__ __forceinline__ float rows4_sum(float v) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
@@ -991,6 +999,9 @@ __global__ __launch_bounds__(256, TQ_PK_MINB) void decode_kernel(DArgs a) {
 // waves per workgroup for code width m (a multiple of 4)
 constexpr int byte_waves(int m) { return m == 4 ? 8 : 12; }
 constexpr uint32_t kBSignBase = 1u << 16;    // LDS byte offset of the sign table
+// offset of the byte kernel's log2-domain softmax argument: its weights are
+// exp2(logit - reference + kTOff), and its V norms carry 2^-kTOff
+constexpr float kTOff = 96.0f;
 constexpr int kBTabBytes = 2 << 16;          // both tables
 constexpr int kBMerge = 4 * (128 * 16 + 64) * 4;  // merge regions (reuse the table space)
 static_assert(kBMerge <= kBTabBytes, "merge regions fit in the table space");
@@ -1093,16 +1104,24 @@ __global__ __launch_bounds__(64 * byte_waves(M), 1) void decode_byte_kernel(DArg
     const int64_t n = a.seq_lens[b];
     N = n < 1 ? 1 : (n > a.n_ctx ? a.n_ctx : n);
   }
-  const int64_t n_tiles = (N + kTile - 1) / kTile;
-  const int64_t tps = (n_tiles + a.n_split - 1) / a.n_split;
-  const int64_t t_begin = split * tps;
-  const int64_t t_end = t_begin + tps < n_tiles ? t_begin + tps : n_tiles;
+  // tile indices are 32-bit (wave-uniform, so their compares stay scalar)
+  const int n_tiles = (int)((N + kTile - 1) / kTile);
+  const int n_full = (int)(N / kTile);  // tiles whose 32 tokens all exist
+  const int tps = (n_tiles + a.n_split - 1) / a.n_split;
+  const int t_begin = split * tps;
+  const int t_end = t_begin + tps < n_tiles ? t_begin + tps : n_tiles;
   const int64_t rowbase = (int64_t)bh * a.cap;
-  auto tile_row = [&](int64_t t) __attribute__((always_inline)) -> int64_t {
-    if (!a.block_table) return rowbase + t * kTile;
-    int64_t pb = a.block_table[(int64_t)b * a.max_blocks + t];
-    pb = pb < 0 ? 0 : (pb >= a.n_pblocks ? a.n_pblocks - 1 : pb);
-    return (pb * a.hkv + kvh) * kTile;
+  const int npb = a.n_pblocks < INT32_MAX ? (int)a.n_pblocks : INT32_MAX;  // entries clamp into [0, npb)
+  auto tile_row = [&](int t) __attribute__((always_inline)) -> int64_t {
+    if (!a.block_table) return rowbase + (int64_t)t * kTile;
+    // the block table is read-only during the launch: read it through the
+    // constant address space, so the wave-uniform entry comes from a scalar
+    // load (a vector load would make the wave wait for its prefetched tiles)
+    const __attribute__((address_space(4))) int32_t* bt =
+        (const __attribute__((address_space(4))) int32_t*)(uintptr_t)a.block_table;
+    int pb = bt[(int64_t)b * a.max_blocks + t];
+    pb = pb < 0 ? 0 : (pb >= npb ? npb - 1 : pb);
+    return ((int64_t)pb * a.hkv + kvh) * kTile;
   };
   // Code table rows: when the K and V scaled codebooks are equal (equal
   // layouts have equal Lloyd-Max codebooks), a row holds one entry
@@ -1127,56 +1146,76 @@ __global__ __launch_bounds__(64 * byte_waves(M), 1) void decode_byte_kernel(DArg
   const uint32_t okc = r0 * (16u * M) + 4u * M * lg, oks = r0 * 16u + 4u * lg;
   const uint32_t okn = a.kn_f16 ? 4u * (lane >> 1) : 4u * lane;
   const uint32_t ovn = a.vn_f16 ? 4u * (lane >> 1) : 4u * lane;
-  const uint32_t kn_sh = a.kn_f16 ? 16u * (lane & 1) : 0u, vn_sh = a.vn_f16 ? 16u * (lane & 1) : 0u;
+  // odd lanes stage gamma (K: n / s_K on even lanes); with fp16 norms they
+  // take the upper half of the shared word (a wave-constant lane mask, kept
+  // in scalar registers rather than per-lane values)
+  const bool odd = (lane & 1) != 0;
+  auto bnorm = [&](uint32_t w, int f16) __attribute__((always_inline)) -> float {
+    if (!f16) return __uint_as_float(w);
+    // both halves converted, then a select on the lane mask (written so
+    // that the compiler does not fold it into a per-lane shift amount,
+    // which would hold one more vector register through the tile loop)
+    const float lo = (float)__builtin_bit_cast(_Float16, (uint16_t)w);
+    float hi;
+    asm("v_cvt_f32_f16_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_1" : "=v"(hi) : "v"(w));
+    return odd ? hi : lo;
+  };
   const uint32_t ovc = M * (128u * lg + 8u * ln), ovs = 4u * (32u * lg + 2u * ln);
+  // Record loads go through buffer resources based at the tile's first row
+  // (wave-uniform, built in scalar registers), so a load's address is the
+  // lane's constant 32-bit offset above plus an immediate: no per-tile
+  // vector address arithmetic.
+  auto rsrc = [](const void* base) __attribute__((always_inline)) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+  };
   auto load = [&](int64_t row0, BRaw<M>& r) __attribute__((always_inline)) {
-    const char* kc = reinterpret_cast<const char*>(a.kc) + row0 * (16 * M);
-    const char* ks = reinterpret_cast<const char*>(a.ks) + row0 * 16;
-    const char* kn = reinterpret_cast<const char*>(a.kn) + (row0 << a.kn_shift);
+    const auto kc = rsrc(reinterpret_cast<const char*>(a.kc) + row0 * (16 * M));
+    const auto ks = rsrc(reinterpret_cast<const char*>(a.ks) + row0 * 16);
+    const auto kn = rsrc(reinterpret_cast<const char*>(a.kn) + (row0 << a.kn_shift));
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
       const uint32_t ok = okc + tau * (64u * M);
       if constexpr (M == 1) {
-        r.kc[tau][0] = *reinterpret_cast<const uint32_t*>(kc + ok);
+        r.kc[tau][0] = __builtin_amdgcn_raw_buffer_load_b32(kc, ok, 0, 0);
       } else if constexpr (M == 2) {
-        const u32x2a4 v = *reinterpret_cast<const u32x2a4*>(kc + ok);
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(kc, ok, 0, 0);
         r.kc[tau][0] = v[0];
         r.kc[tau][1] = v[1];
       } else {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(kc + ok);
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(kc, ok, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) r.kc[tau][i] = v[i];
       }
-      r.ks[tau] = *reinterpret_cast<const uint32_t*>(ks + oks + tau * 64u);
+      r.ks[tau] = __builtin_amdgcn_raw_buffer_load_b32(ks, oks + tau * 64u, 0, 0);
     }
-    r.kn = *reinterpret_cast<const uint32_t*>(kn + okn);
+    r.kn = __builtin_amdgcn_raw_buffer_load_b32(kn, okn, 0, 0);
     if constexpr (WV != 0) {
       const int64_t blk = row0 >> 5;
-      const char* vc = reinterpret_cast<const char*>(a.vc) + blk * (512 * M);
-      const char* vn = reinterpret_cast<const char*>(a.vn) + (row0 << a.vn_shift);
+      const auto vc = rsrc(reinterpret_cast<const char*>(a.vc) + blk * (512 * M));
+      const auto vn = rsrc(reinterpret_cast<const char*>(a.vn) + (row0 << a.vn_shift));
       if constexpr (M == 1) {
-        const u32x2a4 v = *reinterpret_cast<const u32x2a4*>(vc + ovc);
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(vc, ovc, 0, 0);
         r.vc[0] = v[0];
         r.vc[1] = v[1];
       } else {
 #pragma unroll
         for (int h = 0; h < M / 2; ++h) {
-          const u32x4 v = *reinterpret_cast<const u32x4*>(vc + ovc + 16u * h);
+          const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(vc, ovc + 16u * h, 0, 0);
 #pragma unroll
           for (int i = 0; i < 4; ++i) r.vc[4 * h + i] = v[i];
         }
       }
       if constexpr (WV == 1) {
-        const char* vs = reinterpret_cast<const char*>(a.vs) + blk * 512;
-        const u32x2a4 v = *reinterpret_cast<const u32x2a4*>(vs + ovs);
+        const auto vs = rsrc(reinterpret_cast<const char*>(a.vs) + blk * 512);
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(vs, ovs, 0, 0);
         r.vs[0] = v[0];
         r.vs[1] = v[1];
       }
-      r.vn = *reinterpret_cast<const uint32_t*>(vn + ovn);
+      r.vn = __builtin_amdgcn_raw_buffer_load_b32(vn, ovn, 0, 0);
     }
   };
   // lane l stages float l of a tile's K norms [32][n, gamma]: n / s_K
-  const float kn_mul = (lane & 1) ? 1.0f : 1.0f / a.kscale[0];
+  const float kinv = 1.0f / a.kscale[0];
 
   // ---- this lane's column: head and role ----
   const int hcol = P8 ? (ln & 7) : (ln >> 2);  // head within the block
@@ -1193,16 +1232,17 @@ __global__ __launch_bounds__(64 * byte_waves(M), 1) void decode_byte_kernel(DArg
     const u32x4 vl = *reinterpret_cast<const u32x4*>(qp + D);
     const u32x4 vs = *reinterpret_cast<const u32x4*>(qp + 2 * D);
     if constexpr (P8) {
-      bq[c] = hvalid ? (role ? vl : vh) : z;
+      // the lo column takes the remainder at its own scale (lo * 2^11 times
+      // 2^-11; small remainders become fp16 subnormals, exact to 2^-25), so
+      // the two columns' sums add without a factor
+      const f16x8 lo = __builtin_bit_cast(f16x8, vl) * (_Float16)0x1p-11f;
+      bq[c] = hvalid ? (role ? __builtin_bit_cast(u32x4, lo) : vh) : z;
       bs[c] = hvalid ? vs : z;
     } else {
       bq[c] = hvalid && role < 2 ? (role ? vl : vh) : z;
       bs[c] = hvalid && role == 2 ? vs : z;
     }
   }
-  // logit combine factors (P8): hi + 2^-11 lo from this lane's value v and
-  // its partner's o (lane ln ^ 8): fma(ca, o, cb v)
-  const float ca = role ? 1.0f : kLoInv, cb = role ? kLoInv : 1.0f;
   // weight split factors of this lane's column (HB = 4: remainder columns)
   const bool wlo = (role & 1) != 0;
   const float bsel = wlo ? 2048.0f : 0.0f, csel = wlo ? -2048.0f : 1.0f;
@@ -1219,11 +1259,11 @@ __global__ __launch_bounds__(64 * byte_waves(M), 1) void decode_byte_kernel(DArg
     else if constexpr (k == 2) return rb2;
     else return rb3;
   };
-  int64_t tile = t_begin + wv;
-  const int64_t last = tile < t_end ? t_end - 1 - ((t_end - 1 - tile) % kBW) : 0;  // this wave's last tile
+  int tile = t_begin + wv;
+  const int last = tile < t_end ? t_end - 1 - ((t_end - 1 - tile) % kBW) : 0;  // this wave's last tile
   // (a wave without tiles loads tile 0, which always exists, and drops it;
   // past the last tile the prefetch reloads it)
-  auto ahead = [&](int k) __attribute__((always_inline)) -> int64_t {
+  auto ahead = [&](int k) __attribute__((always_inline)) -> int {
     if (tile >= t_end) return 0;
     return tile + k * kBW <= last ? tile + k * kBW : last;
   };
@@ -1275,14 +1315,24 @@ __global__ __launch_bounds__(64 * byte_waves(M), 1) void decode_byte_kernel(DArg
 #pragma unroll
   for (int v = 0; v < NVA; ++v) avr[v] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // V norms of a wave's tile are staged as [2][32] (all n, then all gamma),
+  // so a lane reads the 8 values its column takes (n for code columns,
+  // gamma for sign columns) as two 16-byte words.
+  const int vpart_sel = P8 ? role : (role >= 2 ? 1 : 0);
+  const uint32_t vst = 32u * (lane & 1) + (lane >> 1);
+
   // K part of a tile: logits, online softmax, and the V weight operands
   // (bvc: code product, bvs: sign product) of its tokens.
-  auto kpart = [&](const BRaw<M>& r, int64_t T0, u32x4& bvc, u32x4& bvs) __attribute__((always_inline)) {
-    const bool full = T0 + kTile <= N;
+  auto kpart = [&](const BRaw<M>& r, int t, u32x4& bvc, u32x4& bvs) __attribute__((always_inline)) {
+    const bool full = t < n_full;
+    const int nvt = full ? kTile : (int)(N - (int64_t)t * kTile);  // valid tokens of the tile
+    const int nvl = nvt - 8 * lg;  // valid tokens among the lane's 8 (j < nvl)
     {
-      const bool nok = full || T0 + (lane >> 1) < N;
-      nrm_k[lane] = nok ? norm_value(r.kn, kn_sh, a.kn_f16) * kn_mul : 0.f;
-      if constexpr (WV != 0) nrm_v[lane] = nok ? norm_value(r.vn, vn_sh, a.vn_f16) : 0.f;
+      const bool nok = full || (int)(lane >> 1) < nvt;
+      const float x = bnorm(r.kn, a.kn_f16);
+      nrm_k[lane] = nok ? (odd ? x : x * kinv) : 0.f;
+      // (V norms times 2^-kTOff: the weights exp2(t) carry 2^kTOff)
+      if constexpr (WV != 0) nrm_v[vst] = nok ? bnorm(r.vn, a.vn_f16) * 0x1p-96f : 0.f;
     }
     __builtin_amdgcn_wave_barrier();
     f32x4 ak[2], as[P8 ? 2 : 1];
@@ -1301,53 +1351,66 @@ __global__ __launch_bounds__(64 * byte_waves(M), 1) void decode_byte_kernel(DArg
           ak[tau] = mfma16(ks, bs[c], ak[tau]);
       }
     }
-    const int64_t tok0 = T0 + 8 * lg;
     float kn[8][2];
     load_norms<1>(nrm_k + 16 * lg, kn);
     // logits relative to the running integer reference (log2 domain):
-    // t = logit - m_ref, folded into the last fma
+    // t = logit - m_ref + kTOff, the offset folded into the inner fma. For
+    // |logit - m_ref| < 32 both fma results lie in [64, 128), where fp32
+    // values sit on the fixed grid 2^-17: their roundings commute with the
+    // integer reference, so a weight is the same power-of-two multiple for
+    // any split (or wave) whose reference differs
     const float m_ref = m_run == -INFINITY ? 0.f : m_run;
+    const float t_off = (WV != 0 ? kTOff : 0.f) - m_ref;  // (logits only: no offset)
     float t2[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int tau = j >> 2, i = j & 3;
       const float v = ak[tau][i];
       if constexpr (P8) {
-        const float o = dpp_full<0x128>(v);  // row_ror:8: the partner column ln ^ 8
-        t2[j] = fmaf(kn[j][1], as[tau][i], fmaf(kn[j][0], fmaf(ca, o, cb * v), -m_ref));
+        // the hi and lo columns hold the two parts of the same product at
+        // the same scale: their sum (with the partner column ln ^ 8, one DPP
+        // row rotation) is the MSE dot product
+        const float hl = v + dpp_full<0x128>(v);
+        t2[j] = fmaf(kn[j][1], as[tau][i], fmaf(kn[j][0], hl, t_off));
       } else {
         // quad_perm broadcasts of the quad's role 0, 1 and 2 columns
         const float v0 = dpp_full<0x00>(v), v1 = dpp_full<0x55>(v), v2 = dpp_full<0xAA>(v);
-        t2[j] = fmaf(kn[j][1], v2, fmaf(kn[j][0], fmaf(kLoInv, v1, v0), -m_ref));
+        t2[j] = fmaf(kn[j][1], v2, fmaf(kn[j][0], fmaf(kLoInv, v1, v0), t_off));
       }
     }
-    const int nvt = full ? kTile : (int)(N - T0);
     if (a.T > 1) {
       const int64_t lim = N - a.T + hloc % a.T + 1;
+      const int64_t tok0 = (int64_t)t * kTile + 8 * lg;
 #pragma unroll
       for (int j = 0; j < 8; ++j) t2[j] = tok0 + j < lim ? t2[j] : -INFINITY;
     }
     if (a.logits) {
       if (hvalid && role == 0) {
-        float* lp = a.logits + ((int64_t)b * a.hq + hq) * a.n_ctx + tok0;
+        // the block's logits from the tile's first token on; the lane's head
+        // and tokens as a 32-bit offset (contexts of up to 2^26 tokens)
+        const auto lr = rsrc(a.logits + ((int64_t)b * a.hq + kvh * a.group + hblk * HB) * a.n_ctx + (int64_t)t * kTile);
+        const uint32_t lo = 4u * ((uint32_t)hcol * (uint32_t)a.n_ctx + 8u * lg);
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-          if (8 * lg + j < nvt) lp[j] = (t2[j] + m_ref) * kLn2;
+          if (j < nvl)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((t2[j] - t_off) * kLn2), lr, lo, 4 * j, 0);
       }
     }
     if (!full) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) t2[j] = 8 * lg + j < nvt ? t2[j] : -INFINITY;
+      for (int j = 0; j < 8; ++j) t2[j] = j < nvl ? t2[j] : -INFINITY;
     }
     if constexpr (WV != 0) {
       // ---------------- online softmax (every lane: its column's head) ----------------
-      float mx = t2[0];
-#pragma unroll
-      for (int j = 1; j < 8; ++j) mx = fmaxf(mx, t2[j]);
-      mx = rows4_max(mx);
+      // (IEEE maximum: no NaN arises here, and it takes no canonicalizing moves)
+      float mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(t2[0], t2[1]),
+                                               __builtin_elementwise_maximum(t2[2], t2[3]));
+      mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(t2[4], t2[5]));
+      mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(t2[6], t2[7]));
+      mx = rows4_maximum(mx);
       // integer log2-domain reference: weights and rescales are exact powers
       // of two times the same mantissa, independent of the split count
-      const float m_cand = m_ref + ceilf(mx);
+      const float m_cand = m_ref + (ceilf(mx) - kTOff);
       if (__builtin_amdgcn_ballot_w64(m_cand > m_run) != 0) {
         // some head's maximum moved: rescale (factor 1 for the others; a
         // head that has seen only masked tokens keeps -inf and factor 1)
@@ -1357,28 +1420,39 @@ __global__ __launch_bounds__(64 * byte_waves(M), 1) void decode_byte_kernel(DArg
 #pragma unroll
         for (int v = 0; v < NMT; ++v) avr[v] *= corr;
         m_run = m_new;
-      }
-      // (m_run is -inf only while every token seen is masked: then p = 0)
-      const float delta = m_run == -INFINITY ? 0.f : m_run - m_ref;
-      float p[8], psum;
+        // t relative to the new reference (m_run is -inf only while every
+        // token seen is masked: then t stays -inf and p = 0)
+        const float delta = m_run == -INFINITY ? 0.f : m_run - m_ref;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(t2[j] - delta);
-      psum = p[0];
+        for (int j = 0; j < 8; ++j) t2[j] -= delta;
+      }
+      // (when no reference moved, m_ref is this lane's m_run, or 0 while
+      // every token seen is masked, so t is already relative to it;
+      // exp2(t) <= 2^kTOff)
+      float p[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(t2[j]);
+      float psum = p[0];
 #pragma unroll
       for (int j = 1; j < 8; ++j) psum += p[j];
-      l_run += psum;
-      float vn[8][2];
-      load_norms<1>(nrm_v + 16 * lg, vn);
+      l_run += psum;  // (in units of 2^kTOff)
+      // this column's V norms (n or gamma) of the lane's 8 tokens
+      float vn[8];
+      {
+        const f32x4* vp = reinterpret_cast<const f32x4*>(nrm_v + 32 * vpart_sel + 8 * lg);
+        const f32x4 x0 = vp[0], x1 = vp[1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vn[e] = x0[e];
+          vn[4 + e] = x1[e];
+        }
+      }
       if constexpr (P8) {
         // columns h: w_n = p n (code product), columns h + 8: w_g = p gamma
         // (sign product), plain fp16, one accumulator set
         u32x4 w;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int j0 = 2 * q, j1 = 2 * q + 1;
-          const float n0 = role ? vn[j0][1] : vn[j0][0], n1 = role ? vn[j1][1] : vn[j1][0];
-          w[q] = h2bits(p[j0] * n0, p[j1] * n1);
-        }
+        for (int q = 0; q < 4; ++q) w[q] = h2bits(p[2 * q] * vn[2 * q], p[2 * q + 1] * vn[2 * q + 1]);
         const u32x4 z{0, 0, 0, 0};
         bvc = role ? z : w;
         bvs = role ? w : z;
@@ -1386,11 +1460,8 @@ __global__ __launch_bounds__(64 * byte_waves(M), 1) void decode_byte_kernel(DArg
         const bool gsel = role >= 2;
         u32x4 w;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int j0 = 2 * q, j1 = 2 * q + 1;
-          const float n0 = gsel ? vn[j0][1] : vn[j0][0], n1 = gsel ? vn[j1][1] : vn[j1][0];
-          w[q] = h2bits(wsplit(p[j0] * n0, bsel, csel), wsplit(p[j1] * n1, bsel, csel));
-        }
+        for (int q = 0; q < 4; ++q)
+          w[q] = h2bits(wsplit(p[2 * q] * vn[2 * q], bsel, csel), wsplit(p[2 * q + 1] * vn[2 * q + 1], bsel, csel));
         const u32x4 z{0, 0, 0, 0};
         bvc = gsel ? z : w;
         bvs = gsel ? w : z;
@@ -1425,7 +1496,7 @@ __global__ __launch_bounds__(64 * byte_waves(M), 1) void decode_byte_kernel(DArg
       constexpr int k = decltype(kc)::value;
       load(tile_row(ahead(NB - 1)), rbuf(std::integral_constant<int, k + NB - 1>{}));
       u32x4 bvc, bvs;
-      kpart(rbuf(kc), tile * kTile, bvc, bvs);
+      kpart(rbuf(kc), tile, bvc, bvs);
       if constexpr (WV != 0) vpart(rbuf(kc), bvc, bvs);
       if (tile == last) return true;
       tile += kBW;
@@ -1450,7 +1521,7 @@ __global__ __launch_bounds__(64 * byte_waves(M), 1) void decode_byte_kernel(DArg
     constexpr int RS = 128 * 16 + 64;
     float* s_red = reinterpret_cast<float*>(lds);
     __syncthreads();  // tables are no longer read
-    l_run = rows4_sum(l_run);
+    l_run = rows4_sum(l_run) * 0x1p-96f;  // back from units of 2^kTOff
     if (lg == 0 && role == 0) s_m[wv * 8 + hcol] = m_run;
     __syncthreads();
     float Mh = s_m[hcol];
@@ -2074,7 +2145,9 @@ DecodeCfg decode_cfg(const tq_layout& l, bool with_v, const tq_decode_shape* s) 
     c.n_split = (int)(want < 1 ? 1 : want);
     return c;
   }
-  c.byte = byte_kernel_ok(l);
+  // (the byte kernel keeps tile indices and per-lane logit offsets in 32
+  // bits: contexts of up to 2^26 tokens)
+  c.byte = byte_kernel_ok(l) && s->n_ctx <= (int64_t(1) << 26);
   c.hb = c.byte ? (group <= 4 ? 4 : 8) : heads_per_block(group, with_v);
   c.n_hblk = (group + c.hb - 1) / c.hb;
   if (!c.byte) {

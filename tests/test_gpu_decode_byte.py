@@ -61,8 +61,11 @@ def test_byte_kernel_matches_oracle(tq, over, n_ctx, cap, v_mse, f16, with_v):
 
 
 def test_byte_kernel_split_count_invariance(tq):
-    # the integer log2 softmax reference makes every split weight the same
-    # power-of-two-scaled fp16 split, so only the fp32 summation order changes
+    # the integer log2 softmax reference, with the softmax argument held on a
+    # fixed fp32 grid (offset into [64, 128)), makes every split's weights the
+    # same power-of-two multiples, so only the fp32 summation order changes
+    # (observed ~4e-7; a weight whose fp16 rounding depended on the split
+    # would move the output by up to 2^-11 of its share)
     wl = synth.workload("llama70b_long", batch=1, n_q_heads=16, n_kv_heads=2)
     o = _oracle_side(wl, 3000, 3008)
     outs = []
@@ -72,9 +75,13 @@ def test_byte_kernel_split_count_invariance(tq):
         outs.append(out)
     _, ro = _reference(wl, o, q)
     for out in outs:
-        assert gc.normwise_close(out, ro)[0]
+        ok, err = gc.normwise_close(out, ro)
+        print("  vs oracle", err, flush=True)
+        assert ok, err
     for out in outs[1:]:
-        assert gc.normwise_close(out, outs[0], tol=5e-5)[0]
+        ok, err = gc.normwise_close(out, outs[0], tol=5e-6)
+        print("  vs one split", err, flush=True)
+        assert ok, err
 
 
 @pytest.mark.parametrize("G", [4, 8])
