@@ -993,8 +993,11 @@ __global__ __launch_bounds__(256, TQ_PK_MINB) void decode_kernel(DArgs a) {
 // Each column's lanes form their head's logit (exchanging the hi / lo / sketch
 // parts by DPP), so every lane runs its head's online softmax.
 // ---------------------------------------------------------------------------
-#ifndef TQ_BYTE_NBUF
-#define TQ_BYTE_NBUF 2
+#ifndef TQ_BYTE_NBK
+#define TQ_BYTE_NBK 3
+#endif
+#ifndef TQ_BYTE_NBV
+#define TQ_BYTE_NBV 2
 #endif
 // waves per workgroup for code width m (a multiple of 4)
 constexpr int byte_waves(int m) { return m == 4 ? 8 : 12; }
@@ -1168,27 +1171,33 @@ __global__ __launch_bounds__(64 * byte_waves(M), 1) void decode_byte_kernel(DArg
   auto rsrc = [](const void* base) __attribute__((always_inline)) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
   };
-  auto load = [&](int64_t row0, BRaw<M>& r) __attribute__((always_inline)) {
+  // K words of a tile (codes, signs, norms)
+  auto load_k = [&](int64_t row0, BRaw<M>& r) __attribute__((always_inline)) {
     const auto kc = rsrc(reinterpret_cast<const char*>(a.kc) + row0 * (16 * M));
     const auto ks = rsrc(reinterpret_cast<const char*>(a.ks) + row0 * 16);
     const auto kn = rsrc(reinterpret_cast<const char*>(a.kn) + (row0 << a.kn_shift));
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
-      const uint32_t ok = okc + tau * (64u * M);
+      // (the second row set's constant offset goes in the scalar offset, so
+      // that no per-lane register holds the sum)
+      const int so = tau * 64 * M;
       if constexpr (M == 1) {
-        r.kc[tau][0] = __builtin_amdgcn_raw_buffer_load_b32(kc, ok, 0, 0);
+        r.kc[tau][0] = __builtin_amdgcn_raw_buffer_load_b32(kc, okc, so, 0);
       } else if constexpr (M == 2) {
-        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(kc, ok, 0, 0);
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(kc, okc, so, 0);
         r.kc[tau][0] = v[0];
         r.kc[tau][1] = v[1];
       } else {
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(kc, ok, 0, 0);
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(kc, okc, so, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) r.kc[tau][i] = v[i];
       }
-      r.ks[tau] = __builtin_amdgcn_raw_buffer_load_b32(ks, oks + tau * 64u, 0, 0);
+      r.ks[tau] = __builtin_amdgcn_raw_buffer_load_b32(ks, oks, tau * 64, 0);
     }
     r.kn = __builtin_amdgcn_raw_buffer_load_b32(kn, okn, 0, 0);
+  };
+  // V words of a tile (block fields and norms)
+  auto load_v = [&](int64_t row0, BRaw<M>& r) __attribute__((always_inline)) {
     if constexpr (WV != 0) {
       const int64_t blk = row0 >> 5;
       const auto vc = rsrc(reinterpret_cast<const char*>(a.vc) + blk * (512 * M));
@@ -1200,7 +1209,7 @@ __global__ __launch_bounds__(64 * byte_waves(M), 1) void decode_byte_kernel(DArg
       } else {
 #pragma unroll
         for (int h = 0; h < M / 2; ++h) {
-          const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(vc, ovc + 16u * h, 0, 0);
+          const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(vc, ovc, 16 * h, 0);
 #pragma unroll
           for (int i = 0; i < 4; ++i) r.vc[4 * h + i] = v[i];
         }
@@ -1247,17 +1256,25 @@ __global__ __launch_bounds__(64 * byte_waves(M), 1) void decode_byte_kernel(DArg
   const bool wlo = (role & 1) != 0;
   const float bsel = wlo ? 2048.0f : 0.0f, csel = wlo ? -2048.0f : 1.0f;
 
-  // ---- the first NB - 1 tiles in flight while the tables are built ----
-  // Tile i of this wave uses buffer i mod NB; the load of tile i + NB - 1
-  // reuses the buffer of tile i - 1.
-  constexpr int NB = TQ_BYTE_NBUF;
-  BRaw<M> rb0, rb1, rb2, rb3;
-  auto rbuf = [&](auto kc) __attribute__((always_inline)) -> BRaw<M>& {
-    constexpr int k = decltype(kc)::value % NB;
-    if constexpr (k == 0) return rb0;
-    else if constexpr (k == 1) return rb1;
-    else if constexpr (k == 2) return rb2;
-    else return rb3;
+  // ---- the first tiles in flight while the tables are built ----
+  // K words are loaded NBK - 1 tiles ahead (ring of NBK buffers), V words
+  // NBV - 1 tiles ahead (ring of NBV): the K part of a tile is consumed
+  // first, so its words get the longer lead. Tile i of this wave uses K
+  // buffer i mod NBK and V buffer i mod NBV.
+  constexpr int NBK = TQ_BYTE_NBK, NBV = TQ_BYTE_NBV;
+  static_assert(NBK >= 2 && NBK <= 3 && NBV >= 2 && NBV <= 3, "buffer rings of 2 or 3");
+  BRaw<M> kb0, kb1, kb2, vb0, vb1, vb2;
+  auto kbuf = [&](auto kc) __attribute__((always_inline)) -> BRaw<M>& {
+    constexpr int k = decltype(kc)::value % NBK;
+    if constexpr (k == 0) return kb0;
+    else if constexpr (k == 1) return kb1;
+    else return kb2;
+  };
+  auto vbuf = [&](auto kc) __attribute__((always_inline)) -> BRaw<M>& {
+    constexpr int k = decltype(kc)::value % NBV;
+    if constexpr (k == 0) return vb0;
+    else if constexpr (k == 1) return vb1;
+    else return vb2;
   };
   int tile = t_begin + wv;
   const int last = tile < t_end ? t_end - 1 - ((t_end - 1 - tile) % kBW) : 0;  // this wave's last tile
@@ -1267,9 +1284,13 @@ __global__ __launch_bounds__(64 * byte_waves(M), 1) void decode_byte_kernel(DArg
     if (tile >= t_end) return 0;
     return tile + k * kBW <= last ? tile + k * kBW : last;
   };
-  load(tile_row(ahead(0)), rb0);
-  if constexpr (NB > 2) load(tile_row(ahead(1)), rb1);
-  if constexpr (NB > 3) load(tile_row(ahead(2)), rb2);
+  {
+    const int64_t r0 = tile_row(ahead(0));
+    load_k(r0, kb0);
+    load_v(r0, vb0);
+    if constexpr (NBK > 2) load_k(tile_row(ahead(1)), kb1);
+    if constexpr (NBV > 2) load_v(tile_row(ahead(1)), vb1);
+  }
   if (tid < 16) {
     const int L = 1 << M;
     const int tc = tid < L ? tid : L - 1;
@@ -1323,7 +1344,7 @@ __global__ __launch_bounds__(64 * byte_waves(M), 1) void decode_byte_kernel(DArg
 
   // K part of a tile: logits, online softmax, and the V weight operands
   // (bvc: code product, bvs: sign product) of its tokens.
-  auto kpart = [&](const BRaw<M>& r, int t, u32x4& bvc, u32x4& bvs) __attribute__((always_inline)) {
+  auto kpart = [&](const BRaw<M>& r, const BRaw<M>& rv, int t, u32x4& bvc, u32x4& bvs) __attribute__((always_inline)) {
     const bool full = t < n_full;
     const int nvt = full ? kTile : (int)(N - (int64_t)t * kTile);  // valid tokens of the tile
     const int nvl = nvt - 8 * lg;  // valid tokens among the lane's 8 (j < nvl)
@@ -1332,7 +1353,7 @@ __global__ __launch_bounds__(64 * byte_waves(M), 1) void decode_byte_kernel(DArg
       const float x = bnorm(r.kn, a.kn_f16);
       nrm_k[lane] = nok ? (odd ? x : x * kinv) : 0.f;
       // (V norms times 2^-kTOff: the weights exp2(t) carry 2^kTOff)
-      if constexpr (WV != 0) nrm_v[vst] = nok ? bnorm(r.vn, a.vn_f16) * 0x1p-96f : 0.f;
+      if constexpr (WV != 0) nrm_v[vst] = nok ? bnorm(rv.vn, a.vn_f16) * 0x1p-96f : 0.f;
     }
     __builtin_amdgcn_wave_barrier();
     f32x4 ak[2], as[P8 ? 2 : 1];
@@ -1485,30 +1506,35 @@ __global__ __launch_bounds__(64 * byte_waves(M), 1) void decode_byte_kernel(DArg
   };
 
   if (tile < t_end) {
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    using I3 = std::integral_constant<int, 3>;
-    // stage of tile i (buffer i mod NB): the load of tile i + NB - 1 into
-    // the buffer of tile i - 1, then this tile's K part and V part; true
-    // after the wave's last tile
+    // stage of tile i: the loads of tile i + NBV - 1 (V words, into the V
+    // buffer of tile i - 1) and tile i + NBK - 1 (K words), then this tile's
+    // K part and V part; true after the wave's last tile
     auto stage = [&](auto kc) __attribute__((always_inline)) {
       constexpr int k = decltype(kc)::value;
-      load(tile_row(ahead(NB - 1)), rbuf(std::integral_constant<int, k + NB - 1>{}));
+      // (V first: loads complete in issue order, so waiting for this tile's
+      // V words then leaves the later tiles' K words in flight)
+      if constexpr (WV != 0) load_v(tile_row(ahead(NBV - 1)), vbuf(std::integral_constant<int, k + NBV - 1>{}));
+      load_k(tile_row(ahead(NBK - 1)), kbuf(std::integral_constant<int, k + NBK - 1>{}));
       u32x4 bvc, bvs;
-      kpart(rbuf(kc), tile, bvc, bvs);
-      if constexpr (WV != 0) vpart(rbuf(kc), bvc, bvs);
+      kpart(kbuf(kc), vbuf(kc), tile, bvc, bvs);
+      if constexpr (WV != 0) vpart(vbuf(kc), bvc, bvs);
       if (tile == last) return true;
       tile += kBW;
       return false;
     };
-    for (;;) {
-      if (stage(I0{})) break;
-      if (stage(I1{})) break;
-      if constexpr (NB > 2)
-        if (stage(I2{})) break;
-      if constexpr (NB > 3)
-        if (stage(I3{})) break;
+    // the loop body runs lcm(NBK, NBV) stages, so every stage's buffers are
+    // fixed registers
+    constexpr int NS = NBK == NBV ? NBK : NBK * NBV;
+    auto run = [&](auto self, auto kc) __attribute__((always_inline)) -> bool {
+      constexpr int k = decltype(kc)::value;
+      if constexpr (k == NS) {
+        return false;
+      } else {
+        if (stage(kc)) return true;
+        return self(self, std::integral_constant<int, k + 1>{});
+      }
+    };
+    while (!run(run, std::integral_constant<int, 0>{})) {
     }
   }
 
