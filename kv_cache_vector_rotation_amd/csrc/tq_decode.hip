@@ -143,8 +143,6 @@ __device__ __forceinline__ float dpp_row_z(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
-// max over the four 16-lane rows (lanes l, l ^ 16, l ^ 32, l ^ 48): swap the
-// 32-lane halves, then odd and even rows, with v_permlane{32,16}_swap
 // DPP move whose pattern sends every lane a value from inside its row
 // (rotations, quad permutations, row broadcasts): no lane keeps its old value.
 template <int CTRL>
@@ -152,20 +150,17 @@ __device__ __forceinline__ float dpp_full(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
-__device__ __forceinline__ float rows4_max(float v) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-// the same with IEEE maximum (v_maximum3_f32 on gfx950: no canonicalizing
-// moves); for values that are never NaN
+// max over the four 16-lane rows (lanes l, l ^ 16, l ^ 32, l ^ 48): swap the
+// 32-lane halves, then odd and even rows, with v_permlane{32,16}_swap. IEEE
+// maximum (v_maximum3_f32 on gfx950: no canonicalizing moves), for values
+// that are never NaN.
 __device__ __forceinline__ float rows4_maximum(float v) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   v = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
+// sum over the four 16-lane rows (the same exchange)
 __device__ __forceinline__ float rows4_sum(float v) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
@@ -552,7 +547,11 @@ __global__ __launch_bounds__(256, TQ_PK_MINB) void decode_kernel(DArgs a) {
     const _Float16* qp = a.qprep + ((int64_t)b * a.hq + (hvalid ? hq : 0)) * (4 * D) + g * DG + 8 * CPG * lg + 8 * cl;
     if constexpr (PK) {
       const u32x4 z{0, 0, 0, 0};
-      const u32x4 v = *reinterpret_cast<const u32x4*>(qp + role * D);
+      u32x4 v = *reinterpret_cast<const u32x4*>(qp + role * D);
+      // the lo roles take the remainder at its own scale (lo * 2^11 times
+      // 2^-11; small remainders become fp16 subnormals, exact to 2^-25), so
+      // a head's four columns add without factors
+      if (role & 1) v = __builtin_bit_cast(u32x4, __builtin_bit_cast(f16x8, v) * (_Float16)0x1p-11f);
       qr[c] = hvalid && role < 2 ? v : z;
       qs[c] = hvalid && role >= 2 ? v : z;
     } else {
@@ -633,9 +632,12 @@ __global__ __launch_bounds__(256, TQ_PK_MINB) void decode_kernel(DArgs a) {
       const bool nok = full || T0 + (lane * NG) / (2 * NG) < N;
 #pragma unroll
       for (int e = 0; e < NG; ++e) {
-        s_nrm[wv][0][lane * NG + e] = nok ? norm_value(r.kn[e], no.ksh[e], a.kn_f16) * kn_mul[e] : 0.f;
-        if constexpr (WV != 0)
-          s_nrm[wv][1][lane * NG + e] = nok ? norm_value(r.vn[e], no.vsh[e], a.vn_f16) : 0.f;
+        // (packed: K norms as [2 NG][32], part-major, so a lane reads the
+        // 8 values of its column's part as two 16-byte words)
+        const int fk = lane * NG + e;
+        const int ik = PK ? (fk % (2 * NG)) * kTile + fk / (2 * NG) : fk;
+        s_nrm[wv][0][ik] = nok ? norm_value(r.kn[e], no.ksh[e], a.kn_f16) * kn_mul[e] : 0.f;
+        if constexpr (WV != 0) s_nrm[wv][1][ik] = nok ? norm_value(r.vn[e], no.vsh[e], a.vn_f16) : 0.f;
       }
     }
     // LDS operations of one wave execute in order; the wave barrier only keeps
@@ -685,31 +687,48 @@ __global__ __launch_bounds__(256, TQ_PK_MINB) void decode_kernel(DArgs a) {
     }
     // lane (head ln, lg) now holds tokens 8 lg + j, j = 4 tau + i
     const int64_t tok0 = T0 + 8 * lg;
-    float kn[8][2 * NG];
-    load_norms<NG>(&s_nrm[wv][0][8 * lg * 2 * NG], kn);
     float l2[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int tau = j >> 2, i = j & 3;
-      // (the prepared queries carry scale * log2(e), and alpha_g on the
-      // sketch part, so this is the logit in the log2 domain)
-      float s;
+    if constexpr (PK) {
+      // each lane scales its column by its part's norm (n for the code
+      // columns, gamma for the sign columns), sums the groups, and the quad
+      // adds its four columns by two DPP-folded adds: every lane of the quad
+      // forms the same logit (the sums only commute between lanes)
+      float kf[NG][8];
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        float t;
-        if constexpr (PK) {
-          // quad_perm broadcasts of the head's four columns: every lane
-          // forms its head's logit
-          const float v = lr[tau][g][i];
-          const float v0 = dpp_full<0x00>(v), v1 = dpp_full<0x55>(v), v2 = dpp_full<0xAA>(v),
-                      v3 = dpp_full<0xFF>(v);
-          t = kn[j][2 * g] * fmaf(kLoInv, v1, v0) + kn[j][2 * g + 1] * fmaf(kLoInv, v3, v2);
-        } else {
-          t = kn[j][2 * g] * fmaf(kLoInv, lrl[tau][g][i], lr[tau][g][i]) + kn[j][2 * g + 1] * ls[tau][g][i];
+        const f32x4* kp = reinterpret_cast<const f32x4*>(&s_nrm[wv][0][(2 * g + (role >> 1)) * kTile + 8 * lg]);
+        const f32x4 x0 = kp[0], x1 = kp[1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kf[g][e] = x0[e];
+          kf[g][4 + e] = x1[e];
         }
-        s = g == 0 ? t : s + t;
       }
-      l2[j] = s;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int tau = j >> 2, i = j & 3;
+        float c = lr[tau][0][i] * kf[0][j];
+#pragma unroll
+        for (int g = 1; g < NG; ++g) c = fmaf(lr[tau][g][i], kf[g][j], c);
+        c = c + dpp_full<0xB1>(c);  // quad_perm [1, 0, 3, 2]
+        l2[j] = c + dpp_full<0x4E>(c);  // quad_perm [2, 3, 0, 1]
+      }
+    } else {
+      float kn[8][2 * NG];
+      load_norms<NG>(&s_nrm[wv][0][8 * lg * 2 * NG], kn);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int tau = j >> 2, i = j & 3;
+        // (the prepared queries carry scale * log2(e), and alpha_g on the
+        // sketch part, so this is the logit in the log2 domain)
+        float s;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          const float t = kn[j][2 * g] * fmaf(kLoInv, lrl[tau][g][i], lr[tau][g][i]) + kn[j][2 * g + 1] * ls[tau][g][i];
+          s = g == 0 ? t : s + t;
+        }
+        l2[j] = s;
+      }
     }
     // tokens of the tile before n_ctx (32 except in the last tile)
     const int nvt = full ? kTile : (int)(N - T0);
@@ -735,10 +754,11 @@ __global__ __launch_bounds__(256, TQ_PK_MINB) void decode_kernel(DArgs a) {
     }
     if constexpr (WV != 0) {
       // ---------------- online softmax ----------------
+      // (IEEE maximum: no NaN arises here, and it takes no canonicalizing moves)
       float mx = l2[0];
 #pragma unroll
-      for (int j = 1; j < 8; ++j) mx = fmaxf(mx, l2[j]);
-      mx = rows4_max(mx);
+      for (int j = 1; j < 8; ++j) mx = __builtin_elementwise_maximum(mx, l2[j]);
+      mx = rows4_maximum(mx);
       // The reference is kept at an integer (log2 domain): every weight and
       // every rescale is then an exact power of two times the same mantissa,
       // so the fp16 weights, and hence the result, do not depend on how the
@@ -771,8 +791,6 @@ __global__ __launch_bounds__(256, TQ_PK_MINB) void decode_kernel(DArgs a) {
       }
       l_run += psum;
       // B operands of the V product: slot j <-> token 8 lg + j
-      float vn[8][2 * NG];
-      load_norms<NG>(&s_nrm[wv][1][8 * lg * 2 * NG], vn);
       u32x4 pr[NG], pz[NG];
       if constexpr (PK) {
         // column roles of the V products: the leading fp16 part of p n (0)
@@ -782,22 +800,26 @@ __global__ __launch_bounds__(256, TQ_PK_MINB) void decode_kernel(DArgs a) {
         const bool rem = role >= 2;
         const float bsel = rem ? 2048.0f : 0.0f, csel = rem ? -2048.0f : 1.0f;
         const u32x4 z{0, 0, 0, 0};
+        const bool r1 = (role & 1) != 0;
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
+          // this column's part (n or gamma) of the lane's 8 tokens, read
+          // directly from the part-major staging (a select between two
+          // register arrays would be folded into a lane-dependent index,
+          // which the compiler places in scratch memory)
+          const f32x4* vp = reinterpret_cast<const f32x4*>(&s_nrm[wv][1][(2 * g + (r1 ? 1 : 0)) * kTile + 8 * lg]);
+          const f32x4 x0 = vp[0], x1 = vp[1];
+          const float vs8[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
           u32x4 w;
-          // (a select of two constant indices: an index that depends on the
-          // lane would be lowered to a search over the whole array)
-          const bool r1 = (role & 1) != 0;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float n0 = r1 ? vn[2 * q][2 * g + 1] : vn[2 * q][2 * g];
-            const float n1 = r1 ? vn[2 * q + 1][2 * g + 1] : vn[2 * q + 1][2 * g];
-            w[q] = h2bits(wsplit(pp[2 * q] * n0, bsel, csel), wsplit(pp[2 * q + 1] * n1, bsel, csel));
-          }
+          for (int q = 0; q < 4; ++q)
+            w[q] = h2bits(wsplit(pp[2 * q] * vs8[2 * q], bsel, csel), wsplit(pp[2 * q + 1] * vs8[2 * q + 1], bsel, csel));
           pr[g] = r1 ? z : w;
           pz[g] = r1 ? w : z;
         }
       } else {
+        float vn[8][2 * NG];
+        load_norms<NG>(&s_nrm[wv][1][8 * lg * 2 * NG], vn);
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
 #pragma unroll
@@ -1164,6 +1186,9 @@ __global__ __launch_bounds__(64 * byte_waves(M), 1) void decode_byte_kernel(DArg
     return odd ? hi : lo;
   };
   const uint32_t ovc = M * (128u * lg + 8u * ln), ovs = 4u * (32u * lg + 2u * ln);
+  // (record words are read once: loads carry the non-temporal hint, aux
+  // bit 1, which measured ~1% faster on the 70B-shaped pass)
+  constexpr int kNT = 2;
   // Record loads go through buffer resources based at the tile's first row
   // (wave-uniform, built in scalar registers), so a load's address is the
   // lane's constant 32-bit offset above plus an immediate: no per-tile
@@ -1182,19 +1207,19 @@ __global__ __launch_bounds__(64 * byte_waves(M), 1) void decode_byte_kernel(DArg
       // that no per-lane register holds the sum)
       const int so = tau * 64 * M;
       if constexpr (M == 1) {
-        r.kc[tau][0] = __builtin_amdgcn_raw_buffer_load_b32(kc, okc, so, 0);
+        r.kc[tau][0] = __builtin_amdgcn_raw_buffer_load_b32(kc, okc, so, kNT);
       } else if constexpr (M == 2) {
-        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(kc, okc, so, 0);
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(kc, okc, so, kNT);
         r.kc[tau][0] = v[0];
         r.kc[tau][1] = v[1];
       } else {
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(kc, okc, so, 0);
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(kc, okc, so, kNT);
 #pragma unroll
         for (int i = 0; i < 4; ++i) r.kc[tau][i] = v[i];
       }
-      r.ks[tau] = __builtin_amdgcn_raw_buffer_load_b32(ks, oks, tau * 64, 0);
+      r.ks[tau] = __builtin_amdgcn_raw_buffer_load_b32(ks, oks, tau * 64, kNT);
     }
-    r.kn = __builtin_amdgcn_raw_buffer_load_b32(kn, okn, 0, 0);
+    r.kn = __builtin_amdgcn_raw_buffer_load_b32(kn, okn, 0, kNT);
   };
   // V words of a tile (block fields and norms)
   auto load_v = [&](int64_t row0, BRaw<M>& r) __attribute__((always_inline)) {
@@ -1203,24 +1228,24 @@ __global__ __launch_bounds__(64 * byte_waves(M), 1) void decode_byte_kernel(DArg
       const auto vc = rsrc(reinterpret_cast<const char*>(a.vc) + blk * (512 * M));
       const auto vn = rsrc(reinterpret_cast<const char*>(a.vn) + (row0 << a.vn_shift));
       if constexpr (M == 1) {
-        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(vc, ovc, 0, 0);
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(vc, ovc, 0, kNT);
         r.vc[0] = v[0];
         r.vc[1] = v[1];
       } else {
 #pragma unroll
         for (int h = 0; h < M / 2; ++h) {
-          const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(vc, ovc, 16 * h, 0);
+          const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(vc, ovc, 16 * h, kNT);
 #pragma unroll
           for (int i = 0; i < 4; ++i) r.vc[4 * h + i] = v[i];
         }
       }
       if constexpr (WV == 1) {
         const auto vs = rsrc(reinterpret_cast<const char*>(a.vs) + blk * 512);
-        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(vs, ovs, 0, 0);
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(vs, ovs, 0, kNT);
         r.vs[0] = v[0];
         r.vs[1] = v[1];
       }
-      r.vn = __builtin_amdgcn_raw_buffer_load_b32(vn, ovn, 0, 0);
+      r.vn = __builtin_amdgcn_raw_buffer_load_b32(vn, ovn, 0, kNT);
     }
   };
   // lane l stages float l of a tile's K norms [32][n, gamma]: n / s_K
@@ -1834,10 +1859,11 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_kernel(DArgs a) {
         if (tok0 + j < N) lp[j] = l2[j] * kLn2;
     }
     if constexpr (WV != 0) {
+      // (IEEE maximum: no NaN arises here, and it takes no canonicalizing moves)
       float mx = l2[0];
 #pragma unroll
-      for (int j = 1; j < 8; ++j) mx = fmaxf(mx, l2[j]);
-      mx = rows4_max(mx);
+      for (int j = 1; j < 8; ++j) mx = __builtin_elementwise_maximum(mx, l2[j]);
+      mx = rows4_maximum(mx);
       // integer log2-domain reference (as the other split-K kernels)
       const float m_new = fmaxf(m_run, ceilf(mx));
       if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
