@@ -1186,8 +1186,11 @@ __global__ __launch_bounds__(64 * byte_waves(M), 1) void decode_byte_kernel(DArg
     return odd ? hi : lo;
   };
   const uint32_t ovc = M * (128u * lg + 8u * ln), ovs = 4u * (32u * lg + 2u * ln);
-  // (record words are read once: loads carry the non-temporal hint, aux
-  // bit 1, which measured ~1% faster on the 70B-shaped pass)
+  // Record loads carry the non-temporal hint (aux bit 1): the words are read
+  // once. Measured on the 70B-shaped pass: 1.7% faster than plain loads,
+  // although HBM reads rise from 100.4% to 102.7% of the algorithmic bytes
+  // (the two row sets of a tile, tau 0 and 1, each take half of every K
+  // line, and the second request sometimes finds the line gone).
   constexpr int kNT = 2;
   // Record loads go through buffer resources based at the tile's first row
   // (wave-uniform, built in scalar registers), so a load's address is the
