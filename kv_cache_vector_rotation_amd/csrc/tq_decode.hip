@@ -1002,14 +1002,16 @@ __global__ __launch_bounds__(256, TQ_PK_MINB) void decode_kernel(DArgs a) {
 //
 // Column packing of the 16 MFMA columns:
 //   HB = 8 (KV groups of more than 4 query heads, in blocks of 8 heads):
-//     K codes x [q_rot hi | q_rot lo * 2^11] (8 heads each), K signs x
-//     [q_sk | q_sk]; V codes x [w_n | 0] and V signs x [0 | w_g] into one
+//     K codes x [q_rot hi | q_rot lo] (8 heads each; the lo parts at their
+//     own scale), K signs x [q_sk hi | q_sk lo]; V codes x [w_n | 0] and
+//     V signs x [0 | w_g] into one
 //     accumulator set, with w_n = p n and w_g = p gamma the softmax weights
 //     times the token's norms, both plain fp16 (relative rounding 2^-11 per
 //     weight; a hi / lo split of w_n took 32 more accumulator registers,
 //     which kept the kernel at 8 waves);
 //   HB = 4 (at most 4 query heads per KV head): column 4 h + r, role r =
-//     0 q_rot hi / w_n hi, 1 q_rot lo / w_n lo, 2 q_sk / w_g hi, 3 - / w_g lo;
+//     0 q_rot hi / w_n hi, 1 q_rot lo / w_n lo, 2 q_sk hi / w_g hi, 3 q_sk lo
+//     / w_g lo;
 //     codes and signs accumulate into the same accumulator (their B columns
 //     are disjoint).
 // Each column's lanes form their head's logit (exchanging the hi / lo / sketch
@@ -1268,16 +1270,19 @@ __global__ __launch_bounds__(64 * byte_waves(M), 1) void decode_byte_kernel(DArg
     const u32x4 vh = *reinterpret_cast<const u32x4*>(qp);
     const u32x4 vl = *reinterpret_cast<const u32x4*>(qp + D);
     const u32x4 vs = *reinterpret_cast<const u32x4*>(qp + 2 * D);
+    const u32x4 vsl = *reinterpret_cast<const u32x4*>(qp + 3 * D);
+    // lo parts at their own scale (lo * 2^11 times 2^-11; small remainders
+    // become fp16 subnormals, exact to 2^-25), so a hi and a lo column's
+    // sums add without a factor
+    const u32x4 slo = __builtin_bit_cast(u32x4, __builtin_bit_cast(f16x8, vsl) * (_Float16)0x1p-11f);
     if constexpr (P8) {
-      // the lo column takes the remainder at its own scale (lo * 2^11 times
-      // 2^-11; small remainders become fp16 subnormals, exact to 2^-25), so
-      // the two columns' sums add without a factor
-      const f16x8 lo = __builtin_bit_cast(f16x8, vl) * (_Float16)0x1p-11f;
-      bq[c] = hvalid ? (role ? __builtin_bit_cast(u32x4, lo) : vh) : z;
-      bs[c] = hvalid ? vs : z;
+      // K codes x [q_rot hi | q_rot lo], K signs x [q_sk hi | q_sk lo]
+      const u32x4 lo = __builtin_bit_cast(u32x4, __builtin_bit_cast(f16x8, vl) * (_Float16)0x1p-11f);
+      bq[c] = hvalid ? (role ? lo : vh) : z;
+      bs[c] = hvalid ? (role ? slo : vs) : z;
     } else {
       bq[c] = hvalid && role < 2 ? (role ? vl : vh) : z;
-      bs[c] = hvalid && role == 2 ? vs : z;
+      bs[c] = hvalid && role >= 2 ? (role == 3 ? slo : vs) : z;
     }
   }
   // weight split factors of this lane's column (HB = 4: remainder columns)
@@ -1420,11 +1425,15 @@ __global__ __launch_bounds__(64 * byte_waves(M), 1) void decode_byte_kernel(DArg
         // the same scale: their sum (with the partner column ln ^ 8, one DPP
         // row rotation) is the MSE dot product
         const float hl = v + dpp_full<0x128>(v);
-        t2[j] = fmaf(kn[j][1], as[tau][i], fmaf(kn[j][0], hl, t_off));
+        const float sv = as[tau][i];
+        const float sk = sv + dpp_full<0x128>(sv);  // sketch part: hi + lo
+        t2[j] = fmaf(kn[j][1], sk, fmaf(kn[j][0], hl, t_off));
       } else {
-        // quad_perm broadcasts of the quad's role 0, 1 and 2 columns
-        const float v0 = dpp_full<0x00>(v), v1 = dpp_full<0x55>(v), v2 = dpp_full<0xAA>(v);
-        t2[j] = fmaf(kn[j][1], v2, fmaf(kn[j][0], fmaf(kLoInv, v1, v0), t_off));
+        // quad_perm broadcasts of the quad's columns: q_rot hi, q_rot lo
+        // (times 2^11), q_sk hi, q_sk lo (own scale)
+        const float v0 = dpp_full<0x00>(v), v1 = dpp_full<0x55>(v), v2 = dpp_full<0xAA>(v),
+                    v3 = dpp_full<0xFF>(v);
+        t2[j] = fmaf(kn[j][1], v2 + v3, fmaf(kn[j][0], fmaf(kLoInv, v1, v0), t_off));
       }
     }
     if (a.T > 1) {
