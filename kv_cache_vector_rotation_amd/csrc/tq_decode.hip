@@ -15,8 +15,8 @@
 //              head, block of query heads) and a range of 32-token tiles;
 //              its waves take alternate tiles. Three kernels share this
 //              structure: the byte-table kernel (one group of code width
-//              1, 2 or 4, d = 128; 8 waves), the general kernel below (4
-//              waves; described here) and the chunk kernel for many query
+//              1, 2 or 4, d = 128; 12 waves, 8 for width 4), the general
+//              kernel below (4 waves; described here) and the chunk kernel for many query
 //              columns per KV head. Per tile a wave of the general kernel
 //              - expands the K codes through an LDS table of pairs of fp16
 //                scaled centroids fp16(s c) (one scale s per codebook, its
