@@ -1409,25 +1409,29 @@ __global__ __launch_bounds__(64 * byte_waves(M), 1) void decode_byte_kernel(DArg
     load_norms<1>(nrm_k + 16 * lg, kn);
     // logits relative to the running integer reference (log2 domain):
     // t = logit - m_ref + kTOff, the offset folded into the inner fma. For
-    // |logit - m_ref| < 32 both fma results lie in [64, 128), where fp32
-    // values sit on the fixed grid 2^-17: their roundings commute with the
-    // integer reference, so a weight is the same power-of-two multiple for
-    // any split (or wave) whose reference differs
+    // |logit - m_ref| < 32 the offset sums (both fma results; in 8-head
+    // blocks the hi lane's and the final sum, the lo lane's part not
+    // depending on the reference) lie in [64, 128), where fp32 values sit on
+    // the fixed grid 2^-17: their roundings commute with the integer
+    // reference, so a weight is the same power-of-two multiple for any split
+    // (or wave) whose reference differs
     const float m_ref = m_run == -INFINITY ? 0.f : m_run;
     const float t_off = (WV != 0 ? kTOff : 0.f) - m_ref;  // (logits only: no offset)
+    // (8-head blocks: the hi lane carries the offset, the lo lane none)
+    const float t_off_l = role ? 0.f : t_off;
     float t2[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int tau = j >> 2, i = j & 3;
       const float v = ak[tau][i];
       if constexpr (P8) {
-        // the hi and lo columns hold the two parts of the same product at
-        // the same scale: their sum (with the partner column ln ^ 8, one DPP
-        // row rotation) is the MSE dot product
-        const float hl = v + dpp_full<0x128>(v);
-        const float sv = as[tau][i];
-        const float sk = sv + dpp_full<0x128>(sv);  // sketch part: hi + lo
-        t2[j] = fmaf(kn[j][1], sk, fmaf(kn[j][0], hl, t_off));
+        // the hi and lo columns hold the two parts of the same products at
+        // the same scale: each lane forms its part of the logit (codes times
+        // n, signs times gamma; the hi lane with the offset, in [64, 128)),
+        // and the partner column ln ^ 8 (one DPP row rotation) adds the
+        // other part; the sum commutes, so both lanes hold the same value
+        const float u = fmaf(kn[j][1], as[tau][i], fmaf(kn[j][0], v, t_off_l));
+        t2[j] = u + dpp_full<0x128>(u);
       } else {
         // quad_perm broadcasts of the quad's columns: q_rot hi, q_rot lo
         // (times 2^11), q_sk hi, q_sk lo (own scale)
