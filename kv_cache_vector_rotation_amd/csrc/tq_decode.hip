@@ -1362,6 +1362,18 @@ __global__ __launch_bounds__(64 * byte_waves(M), 1) void decode_byte_kernel(DArg
   __syncthreads();
 
   float m_run = -INFINITY, l_run = 0.f;
+  // values that follow from the running reference, recomputed only when it
+  // moves: the softmax offset this lane folds into its logit part (8-head
+  // blocks: the hi lane only) and the running-max threshold above which the
+  // reference moves (ceil(max t) > kTOff, or any token while all were masked)
+  float t_offc = 0.f, thr = -INFINITY;
+  auto ref_vals = [&]() __attribute__((always_inline)) {
+    const float m_ref = m_run == -INFINITY ? 0.f : m_run;
+    const float t_off = (WV != 0 ? kTOff : 0.f) - m_ref;
+    t_offc = (P8 && role) ? 0.f : t_off;
+    thr = m_run == -INFINITY ? -INFINITY : kTOff;
+  };
+  ref_vals();
   float* nrm_k = s_nrm + wv * 128;
   float* nrm_v = nrm_k + 64;
   constexpr int NVA = WV ? NMT : 1;
@@ -1415,10 +1427,8 @@ __global__ __launch_bounds__(64 * byte_waves(M), 1) void decode_byte_kernel(DArg
     // the fixed grid 2^-17: their roundings commute with the integer
     // reference, so a weight is the same power-of-two multiple for any split
     // (or wave) whose reference differs
-    const float m_ref = m_run == -INFINITY ? 0.f : m_run;
-    const float t_off = (WV != 0 ? kTOff : 0.f) - m_ref;  // (logits only: no offset)
-    // (8-head blocks: the hi lane carries the offset, the lo lane none)
-    const float t_off_l = role ? 0.f : t_off;
+    // (logits only: no offset; 8-head blocks: the hi lane carries it, the
+    // lo lane none)
     float t2[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -1430,14 +1440,14 @@ __global__ __launch_bounds__(64 * byte_waves(M), 1) void decode_byte_kernel(DArg
         // n, signs times gamma; the hi lane with the offset, in [64, 128)),
         // and the partner column ln ^ 8 (one DPP row rotation) adds the
         // other part; the sum commutes, so both lanes hold the same value
-        const float u = fmaf(kn[j][1], as[tau][i], fmaf(kn[j][0], v, t_off_l));
+        const float u = fmaf(kn[j][1], as[tau][i], fmaf(kn[j][0], v, t_offc));
         t2[j] = u + dpp_full<0x128>(u);
       } else {
         // quad_perm broadcasts of the quad's columns: q_rot hi, q_rot lo
         // (times 2^11), q_sk hi, q_sk lo (own scale)
         const float v0 = dpp_full<0x00>(v), v1 = dpp_full<0x55>(v), v2 = dpp_full<0xAA>(v),
                     v3 = dpp_full<0xFF>(v);
-        t2[j] = fmaf(kn[j][1], v2 + v3, fmaf(kn[j][0], fmaf(kLoInv, v1, v0), t_off));
+        t2[j] = fmaf(kn[j][1], v2 + v3, fmaf(kn[j][0], fmaf(kLoInv, v1, v0), t_offc));
       }
     }
     if (a.T > 1) {
@@ -1448,6 +1458,7 @@ __global__ __launch_bounds__(64 * byte_waves(M), 1) void decode_byte_kernel(DArg
     }
     if (a.logits) {
       if (hvalid && role == 0) {
+        const float t_off = (WV != 0 ? kTOff : 0.f) - (m_run == -INFINITY ? 0.f : m_run);
         // the block's logits from the tile's first token on; the lane's head
         // and tokens as a 32-bit offset (contexts of up to 2^26 tokens)
         const auto lr = rsrc(a.logits + ((int64_t)b * a.hq + kvh * a.group + hblk * HB) * a.n_ctx + (int64_t)t * kTile);
@@ -1471,11 +1482,14 @@ __global__ __launch_bounds__(64 * byte_waves(M), 1) void decode_byte_kernel(DArg
       mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(t2[6], t2[7]));
       mx = rows4_maximum(mx);
       // integer log2-domain reference: weights and rescales are exact powers
-      // of two times the same mantissa, independent of the split count
-      const float m_cand = m_ref + (ceilf(mx) - kTOff);
-      if (__builtin_amdgcn_ballot_w64(m_cand > m_run) != 0) {
+      // of two times the same mantissa, independent of the split count; a
+      // head's candidate m_ref + ceil(mx) - kTOff exceeds m_run exactly when
+      // mx exceeds the threshold
+      if (__builtin_amdgcn_ballot_w64(mx > thr) != 0) {
         // some head's maximum moved: rescale (factor 1 for the others; a
         // head that has seen only masked tokens keeps -inf and factor 1)
+        const float m_ref = m_run == -INFINITY ? 0.f : m_run;
+        const float m_cand = m_ref + (ceilf(mx) - kTOff);
         const float m_new = fmaxf(m_run, m_cand);
         const float corr = m_new == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= corr;
@@ -1487,6 +1501,7 @@ __global__ __launch_bounds__(64 * byte_waves(M), 1) void decode_byte_kernel(DArg
         const float delta = m_run == -INFINITY ? 0.f : m_run - m_ref;
 #pragma unroll
         for (int j = 0; j < 8; ++j) t2[j] -= delta;
+        ref_vals();
       }
       // (when no reference moved, m_ref is this lane's m_run, or 0 while
       // every token seen is masked, so t is already relative to it;
