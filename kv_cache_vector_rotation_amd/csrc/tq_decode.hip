@@ -76,6 +76,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 // Low parts of the split fp16 operands are stored times 2^11 so they stay in
 // the normal fp16 range; their products are scaled back by 2^-11.
 constexpr float kLoInv = 1.0f / 2048.0f;
+// offset of the split-K kernels' log2-domain softmax argument: their weights
+// are exp2(logit - reference + kTOff), and their V norms carry 2^-kTOff
+constexpr float kTOff = 96.0f;
 constexpr int kWaves = 4;
 constexpr int kTile = 32;
 
@@ -616,6 +619,18 @@ __global__ __launch_bounds__(256, TQ_PK_MINB) void decode_kernel(DArgs a) {
   const unsigned char* stab = s_tab + ST;
 
   float m_run = -INFINITY, l_run = 0.f;
+  // values that follow from the running reference, recomputed only when it
+  // moves: the softmax offset this lane folds into its logit sum (packed:
+  // the role-0 lane only, the quad adding its four parts) and the
+  // running-max threshold above which the reference moves
+  float t_offc = 0.f, thr = -INFINITY;
+  auto ref_vals = [&]() __attribute__((always_inline)) {
+    const float m_ref = m_run == -INFINITY ? 0.f : m_run;
+    const float t_off = (WV != 0 ? kTOff : 0.f) - m_ref;
+    t_offc = (PK && role != 0) ? 0.f : t_off;
+    thr = m_run == -INFINITY ? -INFINITY : kTOff;
+  };
+  ref_vals();
   f32x4 acc_r[WV ? NMT : 1], acc_s[WV && !PK ? NMT : 1];  // packed: acc_r holds both
 #pragma unroll
   for (int v = 0; v < (WV ? NMT : 1); ++v) acc_r[v] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -637,7 +652,8 @@ __global__ __launch_bounds__(256, TQ_PK_MINB) void decode_kernel(DArgs a) {
         const int fk = lane * NG + e;
         const int ik = PK ? (fk % (2 * NG)) * kTile + fk / (2 * NG) : fk;
         s_nrm[wv][0][ik] = nok ? norm_value(r.kn[e], no.ksh[e], a.kn_f16) * kn_mul[e] : 0.f;
-        if constexpr (WV != 0) s_nrm[wv][1][ik] = nok ? norm_value(r.vn[e], no.vsh[e], a.vn_f16) : 0.f;
+        // (V norms times 2^-kTOff: the weights exp2(t) carry 2^kTOff)
+        if constexpr (WV != 0) s_nrm[wv][1][ik] = nok ? norm_value(r.vn[e], no.vsh[e], a.vn_f16) * 0x1p-96f : 0.f;
       }
     }
     // LDS operations of one wave execute in order; the wave barrier only keeps
@@ -707,7 +723,7 @@ __global__ __launch_bounds__(256, TQ_PK_MINB) void decode_kernel(DArgs a) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int tau = j >> 2, i = j & 3;
-        float c = lr[tau][0][i] * kf[0][j];
+        float c = fmaf(lr[tau][0][i], kf[0][j], t_offc);
 #pragma unroll
         for (int g = 1; g < NG; ++g) c = fmaf(lr[tau][g][i], kf[g][j], c);
         c = c + dpp_full<0xB1>(c);  // quad_perm [1, 0, 3, 2]
@@ -721,12 +737,10 @@ __global__ __launch_bounds__(256, TQ_PK_MINB) void decode_kernel(DArgs a) {
         const int tau = j >> 2, i = j & 3;
         // (the prepared queries carry scale * log2(e), and alpha_g on the
         // sketch part, so this is the logit in the log2 domain)
-        float s;
+        float s = t_offc;
 #pragma unroll
-        for (int g = 0; g < NG; ++g) {
-          const float t = kn[j][2 * g] * fmaf(kLoInv, lrl[tau][g][i], lr[tau][g][i]) + kn[j][2 * g + 1] * ls[tau][g][i];
-          s = g == 0 ? t : s + t;
-        }
+        for (int g = 0; g < NG; ++g)
+          s = fmaf(kn[j][2 * g + 1], ls[tau][g][i], fmaf(kn[j][2 * g], fmaf(kLoInv, lrl[tau][g][i], lr[tau][g][i]), s));
         l2[j] = s;
       }
     }
@@ -742,10 +756,11 @@ __global__ __launch_bounds__(256, TQ_PK_MINB) void decode_kernel(DArgs a) {
     // role-0 lane stores them)
     if (a.logits) {
       if (hvalid && role == 0) {
+        const float t_off = (WV != 0 ? kTOff : 0.f) - (m_run == -INFINITY ? 0.f : m_run);
         float* lp = a.logits + ((int64_t)b * a.hq + hq) * a.n_ctx + tok0;
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-          if (8 * lg + j < nvt) lp[j] = l2[j] * kLn2;
+          if (8 * lg + j < nvt) lp[j] = (l2[j] - t_off) * kLn2;
       }
     }
     if (!full) {
@@ -759,14 +774,19 @@ __global__ __launch_bounds__(256, TQ_PK_MINB) void decode_kernel(DArgs a) {
 #pragma unroll
       for (int j = 1; j < 8; ++j) mx = __builtin_elementwise_maximum(mx, l2[j]);
       mx = rows4_maximum(mx);
-      // The reference is kept at an integer (log2 domain): every weight and
-      // every rescale is then an exact power of two times the same mantissa,
-      // so the fp16 weights, and hence the result, do not depend on how the
-      // context is split.
-      const float m_new = fmaxf(m_run, ceilf(mx));
-      if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+      // The reference is kept at an integer (log2 domain), and the logit sums
+      // carry the offset kTOff - m_ref (l2 = logit - m_ref + kTOff, in
+      // [64, 128) for |logit - m_ref| < 32, where fp32 values sit on the
+      // fixed grid 2^-17): every weight and every rescale is then an exact
+      // power of two times the same mantissa, so the fp16 weights, and hence
+      // the result, do not depend on how the context is split. A head's
+      // candidate m_ref + ceil(mx) - kTOff exceeds m_run exactly when mx
+      // exceeds the threshold.
+      if (__builtin_amdgcn_ballot_w64(mx > thr) != 0) {
         // some head's maximum moved: rescale (factor 1 for the others; a
         // head that has seen only masked tokens keeps -inf and factor 1)
+        const float m_ref0 = m_run == -INFINITY ? 0.f : m_run;
+        const float m_new = fmaxf(m_run, m_ref0 + (ceilf(mx) - kTOff));
         const float corr = m_new == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= corr;
         if constexpr (PK) {
@@ -780,16 +800,21 @@ __global__ __launch_bounds__(256, TQ_PK_MINB) void decode_kernel(DArgs a) {
           }
         }
         m_run = m_new;
+        // the sums relative to the new reference (m_run is -inf only while
+        // every token seen is masked: then they stay -inf and p = 0)
+        const float delta = m_run == -INFINITY ? 0.f : m_run - m_ref0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) l2[j] -= delta;
+        ref_vals();
       }
       float p[8], psum;
-      // (m_run is -inf only while every token seen is masked: then p = 0)
-      const float m_ref = m_run == -INFINITY ? 0.f : m_run;
+      // (exp2(l2) <= 2^kTOff)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        p[j] = __builtin_amdgcn_exp2f(l2[j] - m_ref);
+        p[j] = __builtin_amdgcn_exp2f(l2[j]);
         psum = j == 0 ? p[j] : psum + p[j];
       }
-      l_run += psum;
+      l_run += psum;  // (in units of 2^kTOff)
       // B operands of the V product: slot j <-> token 8 lg + j
       u32x4 pr[NG], pz[NG];
       if constexpr (PK) {
@@ -902,7 +927,7 @@ __global__ __launch_bounds__(256, TQ_PK_MINB) void decode_kernel(DArgs a) {
     constexpr int DP = D + 16 * (D / 64), HS = 2 * DP + 1, REG = 16 * HS;
     float* s_red = reinterpret_cast<float*>(s_tab);
     __syncthreads();  // tables are no longer read
-    l_run = rows4_sum(l_run);
+    l_run = rows4_sum(l_run) * 0x1p-96f;  // back from units of 2^kTOff
     // (packed: every lane of a head's quad has run its softmax; the role-0
     // lane stores its maximum and sum)
     if (lg == 0 && role == 0) s_m[wv][hcol] = m_run;
@@ -1026,9 +1051,6 @@ __global__ __launch_bounds__(256, TQ_PK_MINB) void decode_kernel(DArgs a) {
 // waves per workgroup for code width m (a multiple of 4)
 constexpr int byte_waves(int m) { return m == 4 ? 8 : 12; }
 constexpr uint32_t kBSignBase = 1u << 16;    // LDS byte offset of the sign table
-// offset of the byte kernel's log2-domain softmax argument: its weights are
-// exp2(logit - reference + kTOff), and its V norms carry 2^-kTOff
-constexpr float kTOff = 96.0f;
 constexpr int kBTabBytes = 2 << 16;          // both tables
 constexpr int kBMerge = 4 * (128 * 16 + 64) * 4;  // merge regions (reuse the table space)
 static_assert(kBMerge <= kBTabBytes, "merge regions fit in the table space");
