@@ -136,12 +136,17 @@ def test_split_count_does_not_change_result(tq):
         outs.append(out)
     _, ro = _reference(wl, o, q)
     for out in outs:
-        assert gc.normwise_close(out, ro)[0]
-    # the softmax reference is an integer in the log2 domain, so a token's
-    # fp16 weight is the same whatever the split (up to a power of two); only
-    # the order of the fp32 sums changes
+        ok, err = gc.normwise_close(out, ro)
+        print("  vs oracle", err, flush=True)
+        assert ok, err
+    # the softmax reference is an integer in the log2 domain and the softmax
+    # argument sits on a fixed fp32 grid, so a token's fp16 weight is the same
+    # whatever the split (up to a power of two); only the order of the fp32
+    # sums changes (observed ~3e-7)
     for out in outs[1:]:
-        assert gc.normwise_close(out, outs[0], tol=5e-5)[0]
+        ok, err = gc.normwise_close(out, outs[0], tol=5e-6)
+        print("  vs one split", err, flush=True)
+        assert ok, err
 
 
 def test_gqa_equals_repeated_heads(tq):
