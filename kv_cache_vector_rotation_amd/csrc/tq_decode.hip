@@ -1043,7 +1043,7 @@ __global__ __launch_bounds__(256, TQ_PK_MINB) void decode_kernel(DArgs a) {
 // parts by DPP), so every lane runs its head's online softmax.
 // ---------------------------------------------------------------------------
 #ifndef TQ_BYTE_NBK
-#define TQ_BYTE_NBK 3
+#define TQ_BYTE_NBK 2
 #endif
 #ifndef TQ_BYTE_NBV
 #define TQ_BYTE_NBV 2
